@@ -1,0 +1,33 @@
+"""Marshalling helpers shared by the tests (no layer arithmetic here)."""
+import numpy as np
+
+
+def oracle_kwargs(inst, **extra):
+    """Keyword arguments of ``oracle.layer.layer_forward`` for a drawn instance."""
+    wl = inst.wl
+    kw = dict(hidden=wl.hidden, n_q_heads=wl.n_q_heads, n_kv_heads=wl.n_kv_heads,
+              head_dim=wl.head_dim, ffn_dim=wl.ffn_dim, page_size=wl.page_size,
+              rms_eps=wl.rms_eps, rope_base=wl.rope_base, dtype=wl.dtype, x=inst.x,
+              weights=inst.weights, dec_ctx=inst.dec_ctx, dec_pages=inst.dec_pages,
+              chunk_len=wl.chunk_len, prior_len=wl.prior_len, sp_degree=wl.sp_degree,
+              sp_rank=wl.sp_rank, n_prefill_local=wl.n_prefill_local,
+              local_row_offset=wl.local_row_offset, pre_pages=inst.pre_pages,
+              peer_qkv_in=inst.peer_qkv_in, peer_attn_in=inst.peer_attn_in, pool=inst.pool)
+    kw.update(extra)
+    return kw
+
+
+def rel_fro(a, b):
+    a = np.asarray(a, dtype=np.float64)
+    b = np.asarray(b, dtype=np.float64)
+    return float(np.linalg.norm(a - b) / max(np.linalg.norm(b), 1e-300))
+
+
+class ArrayPool:
+    """``pool[ids]`` over a plain stored array (for tests that build their own pool)."""
+
+    def __init__(self, array):
+        self.array = array
+
+    def __getitem__(self, ids):
+        return self.array[np.asarray(ids, dtype=np.int64)]
