@@ -1,0 +1,313 @@
+"""ctypes binding of libxp.so: the same entry points as include/xp.h, argument
+marshalling only (device buffers are passed as torch tensors or raw addresses).
+
+Every call raises ``XpError`` when the library returns a negative status.  The
+library must be built (``python -m mixed_prefill_decode_amd.build``); there is
+no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+
+import numpy as np
+
+__all__ = ["XpError", "lib", "XP_F32", "XP_BF16", "XP_EPI_F32", "XP_EPI_ADD_T", "XP_EPI_ADD_F32",
+           "XP_EPI_SWIGLU", "XP_DEV_BAD_PAGE", "LayerShape", "LayerWeights", "KvPages", "BatchDesc",
+           "WsLayout", "LatencyModel", "Ctx", "EXPORTED",
+           "xp_ctx_create", "xp_layer_workspace_layout", "xp_layer_forward", "xp_validate_batch",
+           "xp_layer_read_status", "xp_rmsnorm", "xp_gemm", "xp_kv_append", "xp_kv_gather",
+           "xp_decode_workspace_size", "xp_decode_attention", "xp_prefill_attention", "xp_probe_hw_ids",
+           "xp_waterfill", "xp_iteration_latency", "xp_build_info", "xp_last_error"]
+
+XP_F32, XP_BF16 = 0, 1
+XP_EPI_F32, XP_EPI_ADD_T, XP_EPI_ADD_F32, XP_EPI_SWIGLU = 0, 1, 2, 3
+XP_DEV_BAD_PAGE = 1
+STATUS_NAMES = {0: "XP_OK", -1: "XP_EINVAL", -2: "XP_ESHAPE", -3: "XP_EPAGE", -4: "XP_EHIP",
+                -5: "XP_EUNSUPPORTED", -6: "XP_EWORKSPACE"}
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libxp.so")
+
+# every symbol include/xp.h declares
+EXPORTED = ["xp_last_error", "xp_build_info", "xp_ctx_create", "xp_ctx_destroy", "xp_ctx_cu_masks",
+            "xp_layer_workspace_layout", "xp_layer_forward", "xp_validate_batch", "xp_layer_read_status",
+            "xp_rmsnorm", "xp_gemm", "xp_kv_append", "xp_kv_gather", "xp_decode_workspace_size",
+            "xp_decode_attention", "xp_prefill_attention", "xp_probe_hw_ids", "xp_waterfill",
+            "xp_iteration_latency"]
+
+
+class XpError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"{STATUS_NAMES.get(status, status)}: {msg}")
+        self.status = status
+
+
+class LayerShape(C.Structure):
+    _fields_ = [("hidden", C.c_int32), ("n_q_heads", C.c_int32), ("n_kv_heads", C.c_int32),
+                ("head_dim", C.c_int32), ("ffn_dim", C.c_int32), ("page_size", C.c_int32),
+                ("rms_eps", C.c_float), ("rope_base", C.c_double), ("dtype", C.c_int32)]
+
+
+class LayerWeights(C.Structure):
+    _fields_ = [(n, C.c_void_p) for n in ("w_qkv", "w_o", "w_gate", "w_up", "w_down", "g_attn", "g_ffn")]
+
+
+class KvPages(C.Structure):
+    _fields_ = [("pool", C.c_void_p), ("n_pages", C.c_int32)]
+
+
+class BatchDesc(C.Structure):
+    _fields_ = [("x", C.c_void_p), ("n_prefill_local", C.c_int32), ("n_decode", C.c_int32),
+                ("dec_ctx", C.c_void_p), ("dec_pages", C.c_void_p), ("dec_max_blocks", C.c_int32),
+                ("chunk_len", C.c_int32), ("prior_len", C.c_int32), ("sp_degree", C.c_int32),
+                ("sp_rank", C.c_int32), ("local_row_offset", C.c_int32), ("pre_pages", C.c_void_p),
+                ("pre_max_blocks", C.c_int32), ("peer_qkv_in", C.c_void_p), ("peer_qkv_out", C.c_void_p),
+                ("peer_attn_in", C.c_void_p), ("peer_attn_out", C.c_void_p)]
+
+
+class WsLayout(C.Structure):
+    _fields_ = [(n, C.c_size_t) for n in ("status", "hn", "qkv", "q_dec", "q_pre", "attn", "dec_ml",
+                                          "dec_o", "h1", "act", "total")] + \
+               [("dec_splits", C.c_int32), ("dec_pages_per_split", C.c_int32)]
+
+    def as_dict(self):
+        return {f: getattr(self, f) for f, _ in self._fields_}
+
+
+class LatencyModel(C.Structure):
+    _fields_ = [(n, C.c_double) for n in ("gamma", "gamma0", "a_d", "a_d0", "a_p", "a_p0", "a_comm",
+                                          "a_comm0", "alpha", "beta")] + [("n_layers", C.c_int32)]
+
+
+class WaterfillIn(C.Structure):
+    _fields_ = [("n_ranks", C.c_int32), ("n_decode_tokens", C.c_void_p), ("decode_ctx_sum", C.c_void_p),
+                ("existing_assign", C.c_void_p), ("n_selected", C.c_int32), ("sel_len", C.c_void_p),
+                ("sel_ctx", C.c_void_p), ("has_candidate", C.c_int32), ("m_remaining", C.c_int32),
+                ("c_processed", C.c_int64), ("fixed_target", C.c_int32), ("level_hi", C.c_int32),
+                ("quantum", C.c_int32), ("tbt_slo", C.c_double), ("model", C.POINTER(LatencyModel))]
+
+
+class WaterfillOut(C.Structure):
+    _fields_ = [("n_target", C.c_int32), ("budget", C.c_int64), ("chunk_len", C.c_int32),
+                ("assign", C.c_void_p)]
+
+
+_LIB = None
+_vp, _i32, _sz, _f32, _f64 = C.c_void_p, C.c_int32, C.c_size_t, C.c_float, C.c_double
+
+
+def _declare(L):
+    S = _i32
+    sig = {
+        "xp_last_error": (C.c_char_p, []),
+        "xp_build_info": (C.c_char_p, []),
+        "xp_ctx_create": (S, [C.POINTER(_vp), _i32, _i32, _i32]),
+        "xp_ctx_destroy": (S, [_vp]),
+        "xp_ctx_cu_masks": (S, [_vp, _vp, _vp, _vp]),
+        "xp_layer_workspace_layout": (S, [_vp, C.POINTER(LayerShape), C.POINTER(BatchDesc), C.POINTER(WsLayout)]),
+        "xp_layer_forward": (S, [_vp, C.POINTER(LayerShape), C.POINTER(BatchDesc), C.POINTER(LayerWeights),
+                                 C.POINTER(KvPages), _vp, _vp, _sz, _vp]),
+        "xp_validate_batch": (S, [C.POINTER(LayerShape), C.POINTER(BatchDesc), _i32, _vp, _vp, _vp]),
+        "xp_layer_read_status": (S, [_vp, C.POINTER(WsLayout), _vp, _vp]),
+        "xp_rmsnorm": (S, [_i32, _vp, _i32, _vp, _vp, _i32, _i32, _f32, _vp]),
+        "xp_gemm": (S, [_i32, _i32, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _vp]),
+        "xp_kv_append": (S, [_i32, _vp, _i32, _i32, _i32, _vp, _i32, _vp, _vp, _vp, _vp, _i32, _vp]),
+        "xp_kv_gather": (S, [_i32, _vp, _i32, _i32, _i32, _vp, _i32, _vp, _i32, _i32, _vp, _vp, _vp]),
+        "xp_decode_workspace_size": (_sz, [_i32, _i32, _i32, _i32, _i32]),
+        "xp_decode_attention": (S, [_i32, _vp, _vp, _i32, _i32, _vp, _i32, _vp, _i32, _i32, _i32, _i32, _vp,
+                                    _i32, _vp, _i32, _vp]),
+        "xp_prefill_attention": (S, [_i32, _vp, _vp, _i32, _i32, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
+                                     _i32, _vp, _i32, _vp, _i32, _vp, _vp]),
+        "xp_probe_hw_ids": (S, [_i32, _vp, _vp]),
+        "xp_waterfill": (S, [C.POINTER(WaterfillIn), C.POINTER(WaterfillOut)]),
+        "xp_iteration_latency": (S, [C.POINTER(LatencyModel), _i32, _vp, _vp, _vp, _i32, _vp, _vp,
+                                     C.POINTER(_f64)]),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(L, name)
+        fn.restype = res
+        fn.argtypes = args
+
+
+def lib():
+    """The loaded library (raises if it has not been built)."""
+    global _LIB
+    if _LIB is None:
+        if not os.path.exists(LIB_PATH):
+            raise XpError(-4, f"{LIB_PATH} is missing: build it with `python -m mixed_prefill_decode_amd.build`")
+        L = C.CDLL(LIB_PATH)
+        _declare(L)
+        _LIB = L
+    return _LIB
+
+
+def _ptr(x) -> int:
+    if x is None:
+        return 0
+    if isinstance(x, int):
+        return x
+    if hasattr(x, "data_ptr"):
+        return x.data_ptr()
+    if isinstance(x, np.ndarray):
+        return x.ctypes.data
+    raise TypeError(type(x))
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _check(st: int):
+    if st != 0:
+        raise XpError(st, lib().xp_last_error().decode())
+
+
+def xp_last_error() -> str:
+    return lib().xp_last_error().decode()
+
+
+def xp_build_info() -> str:
+    return lib().xp_build_info().decode()
+
+
+class Ctx:
+    """Owns an xp_ctx (two attention streams + fork/join events)."""
+
+    def __init__(self, device: int = 0, decode_cus: int = 0, pages_per_split: int = 0):
+        h = _vp()
+        _check(lib().xp_ctx_create(C.byref(h), device, decode_cus, pages_per_split))
+        self.handle = h
+        self.device, self.decode_cus = device, decode_cus
+
+    def cu_masks(self):
+        dec = (C.c_uint32 * 8)()
+        pre = (C.c_uint32 * 8)()
+        n = _i32()
+        _check(lib().xp_ctx_cu_masks(self.handle, dec, pre, C.byref(n)))
+        return list(dec), list(pre), n.value
+
+    def close(self):
+        if getattr(self, "handle", None):
+            lib().xp_ctx_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def xp_ctx_create(device=0, decode_cus=0, pages_per_split=0) -> Ctx:
+    return Ctx(device, decode_cus, pages_per_split)
+
+
+def xp_layer_workspace_layout(ctx, shape: LayerShape, desc: BatchDesc) -> WsLayout:
+    L = WsLayout()
+    _check(lib().xp_layer_workspace_layout(ctx.handle if ctx else None, C.byref(shape), C.byref(desc), C.byref(L)))
+    return L
+
+
+def xp_layer_forward(ctx, shape, desc, weights, kv, out, workspace, workspace_bytes, stream=None):
+    _check(lib().xp_layer_forward(ctx.handle, C.byref(shape), C.byref(desc), C.byref(weights), C.byref(kv),
+                                  _ptr(out), _ptr(workspace), workspace_bytes, _stream(stream)))
+
+
+def xp_validate_batch(shape, desc, n_pages, dec_ctx_host, dec_pages_host, pre_pages_host):
+    arrs = [None if a is None else np.ascontiguousarray(a, dtype=np.int32)
+            for a in (dec_ctx_host, dec_pages_host, pre_pages_host)]
+    return lib().xp_validate_batch(C.byref(shape), C.byref(desc), n_pages, *[_ptr(a) for a in arrs])
+
+
+def xp_layer_read_status(workspace, layout: WsLayout, stream=None) -> int:
+    v = C.c_uint32()
+    _check(lib().xp_layer_read_status(_ptr(workspace), C.byref(layout), C.byref(v), _stream(stream)))
+    return v.value
+
+
+def xp_rmsnorm(dtype, x, x_is_f32, gamma, y, M, H, eps, stream=None):
+    _check(lib().xp_rmsnorm(dtype, _ptr(x), int(x_is_f32), _ptr(gamma), _ptr(y), M, H, eps, _stream(stream)))
+
+
+def xp_gemm(dtype, epilogue, A, B, B2, R, Cout, M, N, K, stream=None):
+    _check(lib().xp_gemm(dtype, epilogue, _ptr(A), _ptr(B), _ptr(B2), _ptr(R), _ptr(Cout), M, N, K,
+                         _stream(stream)))
+
+
+def xp_kv_append(dtype, pool, n_pages, page_size, head_dim, table, table_stride, seq, pos, k, v, n, stream=None):
+    _check(lib().xp_kv_append(dtype, _ptr(pool), n_pages, page_size, head_dim, _ptr(table), table_stride,
+                              _ptr(seq), _ptr(pos), _ptr(k), _ptr(v), n, _stream(stream)))
+
+
+def xp_kv_gather(dtype, pool, n_pages, page_size, head_dim, table, table_stride, lens, n_seq, max_len, k_out,
+                 v_out, stream=None):
+    _check(lib().xp_kv_gather(dtype, _ptr(pool), n_pages, page_size, head_dim, _ptr(table), table_stride,
+                              _ptr(lens), n_seq, max_len, _ptr(k_out), _ptr(v_out), _stream(stream)))
+
+
+def xp_decode_workspace_size(n_decode, n_q_heads, head_dim, dec_max_blocks, pages_per_split) -> int:
+    return int(lib().xp_decode_workspace_size(n_decode, n_q_heads, head_dim, dec_max_blocks, pages_per_split))
+
+
+def xp_decode_attention(dtype, q, pool, n_pages, page_size, dec_pages, dec_max_blocks, dec_ctx, n_decode,
+                        n_q_heads, n_kv_heads, head_dim, out, out_stride, workspace, pages_per_split,
+                        stream=None):
+    _check(lib().xp_decode_attention(dtype, _ptr(q), _ptr(pool), n_pages, page_size, _ptr(dec_pages),
+                                     dec_max_blocks, _ptr(dec_ctx), n_decode, n_q_heads, n_kv_heads, head_dim,
+                                     _ptr(out), out_stride, _ptr(workspace), pages_per_split, _stream(stream)))
+
+
+def xp_prefill_attention(dtype, q, pool, n_pages, page_size, pre_pages, pre_max_blocks, hq, hkv, head_dim,
+                         prior_len, chunk_len, off, n_local, out_local, out_local_stride, out_peer,
+                         out_peer_stride, status=None, stream=None):
+    _check(lib().xp_prefill_attention(dtype, _ptr(q), _ptr(pool), n_pages, page_size, _ptr(pre_pages),
+                                      pre_max_blocks, hq, hkv, head_dim, prior_len, chunk_len, off, n_local,
+                                      _ptr(out_local), out_local_stride, _ptr(out_peer), out_peer_stride,
+                                      _ptr(status), _stream(stream)))
+
+
+def xp_probe_hw_ids(n_blocks, out, stream=None):
+    _check(lib().xp_probe_hw_ids(n_blocks, _ptr(out), _stream(stream)))
+
+
+def _model(d: dict) -> LatencyModel:
+    return LatencyModel(*[float(d[k]) for k in ("gamma", "gamma0", "a_d", "a_d0", "a_p", "a_p0", "a_comm",
+                                                "a_comm0", "alpha", "beta")], int(d["n_layers"]))
+
+
+def xp_waterfill(*, tau, n_decode_tokens, decode_ctx_sum, existing=None, selected=(), candidate=None,
+                 quantum=1, model, fixed_target=-1, level_hi=0) -> dict:
+    N = len(n_decode_tokens)
+    nd = np.ascontiguousarray(n_decode_tokens, dtype=np.int32)
+    cs = np.ascontiguousarray(decode_ctx_sum, dtype=np.int64)
+    ex = None if existing is None else np.ascontiguousarray(existing, dtype=np.int32)
+    sl = np.ascontiguousarray([s[0] for s in selected] or [0], dtype=np.int32)
+    sc = np.ascontiguousarray([s[1] for s in selected] or [0], dtype=np.int64)
+    m = _model(model)
+    inp = WaterfillIn(N, _ptr(nd), _ptr(cs), _ptr(ex), len(selected), _ptr(sl), _ptr(sc),
+                      1 if candidate is not None else 0, int(candidate[0]) if candidate else 0,
+                      int(candidate[1]) if candidate else 0, int(fixed_target), int(level_hi), int(quantum),
+                      float(tau), C.pointer(m))
+    assign = np.zeros(N, dtype=np.int32)
+    out = WaterfillOut(0, 0, 0, _ptr(assign))
+    _check(lib().xp_waterfill(C.byref(inp), C.byref(out)))
+    return dict(n_target=out.n_target, budget=out.budget, chunk_len=out.chunk_len, assign=assign.tolist())
+
+
+def xp_iteration_latency(model: dict, n_decode_tokens, decode_ctx_sum, n_prefill_tokens, chunks) -> float:
+    N = len(n_decode_tokens)
+    nd = np.ascontiguousarray(n_decode_tokens, dtype=np.int32)
+    cs = np.ascontiguousarray(decode_ctx_sum, dtype=np.int64)
+    npf = np.ascontiguousarray(n_prefill_tokens, dtype=np.int32)
+    cl = np.ascontiguousarray([c[0] for c in chunks] or [0], dtype=np.int32)
+    cc = np.ascontiguousarray([c[1] for c in chunks] or [0], dtype=np.int64)
+    m = _model(model)
+    t = _f64()
+    _check(lib().xp_iteration_latency(C.byref(m), N, _ptr(nd), _ptr(cs), _ptr(npf), len(chunks), _ptr(cl),
+                                      _ptr(cc), C.byref(t)))
+    return t.value

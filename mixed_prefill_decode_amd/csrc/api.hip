@@ -1,0 +1,438 @@
+// C ABI: context, validation, workspace layout and the layer step.
+//
+// The layer step follows ConfluxServe §4 (Fig. 7): one co-batched QKV
+// projection over the rank-local [prefill-chunk || decode] rows, a split
+// attention region, then co-batched O projection and FFN.  The split region
+// follows §6.1 (coordinated attention overlap): prefill and decode attention
+// are enqueued on two streams between a fork and a join event, optionally on
+// disjoint CU sets (hipExtStreamCreateWithCUMask) with decode given the fewest
+// CUs that keep most of its standalone HBM bandwidth.
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <algorithm>
+#include <string>
+
+#include "xp_internal.h"
+
+namespace xp {
+
+static thread_local std::string g_err;
+
+xp_status fail(xp_status code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return code;
+}
+
+}  // namespace xp
+
+using namespace xp;
+
+struct xp_ctx {
+  int device = 0;
+  int n_cus = 0;
+  int decode_cus = 0;  // 0 serialized, -1 concurrent unmasked, k masked
+  int pps = 32;
+  hipStream_t s_dec = nullptr, s_pre = nullptr;
+  hipEvent_t e_fork = nullptr, e_dec = nullptr, e_pre = nullptr;
+  uint32_t mask_dec[8] = {}, mask_pre[8] = {};
+};
+
+extern "C" {
+
+const char* xp_last_error(void) { return g_err.c_str(); }
+
+const char* xp_build_info(void) {
+  return "xp: gfx950 HIP kernels (MFMA bf16/fp32), hipcc " __clang_version__;
+}
+
+}  // extern "C"
+
+namespace {
+
+struct ScopedDevice {
+  int prev = -1;
+  explicit ScopedDevice(int dev) {
+    if (hipGetDevice(&prev) != hipSuccess) prev = -1;
+    (void)hipSetDevice(dev);
+  }
+  ~ScopedDevice() {
+    if (prev >= 0) (void)hipSetDevice(prev);
+  }
+};
+
+// CU mask of `k` CUs spread evenly over the XCDs, assuming mask bit i lands on
+// XCD i % n_xcd (the interleaving the runtime applies on multi-XCD parts); the
+// hardware ids each mask reaches are checked with xp_probe_hw_ids.
+void spread_mask(int n_cus, int k, uint32_t* dec, uint32_t* pre) {
+  for (int w = 0; w < 8; ++w) dec[w] = pre[w] = 0;
+  const int n_xcd = 8;
+  for (int bit = 0; bit < n_cus && bit < 256; ++bit) {
+    const int slot = bit / n_xcd;  // position of this CU inside its XCD
+    const int xcd = bit % n_xcd;
+    // the first k CUs in (slot, xcd) order: slot-major so every XCD gains one before any gains two
+    const int order = slot * n_xcd + xcd;
+    if (order < k)
+      dec[bit / 32] |= 1u << (bit % 32);
+    else
+      pre[bit / 32] |= 1u << (bit % 32);
+  }
+}
+
+int rows_of(const xp_batch_desc* d) { return d->n_prefill_local + d->n_decode; }
+
+xp_status check_shape(const xp_layer_shape* sh) {
+  if (!sh) return fail(XP_EINVAL, "null shape");
+  if (sh->dtype != XP_BF16 && sh->dtype != XP_F32) return fail(XP_EINVAL, "dtype %d", sh->dtype);
+  if (sh->hidden <= 0 || sh->n_q_heads <= 0 || sh->n_kv_heads <= 0 || sh->head_dim <= 0 || sh->ffn_dim <= 0)
+    return fail(XP_ESHAPE, "non-positive layer dimension");
+  if (sh->head_dim != 64 && sh->head_dim != 128) return fail(XP_EUNSUPPORTED, "head_dim %d (64 or 128)", sh->head_dim);
+  if (sh->page_size != 16) return fail(XP_EUNSUPPORTED, "page_size %d (16)", sh->page_size);
+  if (sh->n_q_heads % sh->n_kv_heads) return fail(XP_ESHAPE, "Hq %d not a multiple of Hkv %d", sh->n_q_heads, sh->n_kv_heads);
+  if (sh->n_q_heads / sh->n_kv_heads > 16) return fail(XP_EUNSUPPORTED, "GQA group %d > 16", sh->n_q_heads / sh->n_kv_heads);
+  const int bk = 128 / dtype_bytes(sh->dtype);
+  if (sh->hidden % bk || sh->ffn_dim % bk || (sh->n_q_heads * sh->head_dim) % bk)
+    return fail(XP_EUNSUPPORTED, "hidden, ffn_dim and Hq*d must be multiples of %d", bk);
+  if (!(sh->rms_eps >= 0.f) || !(sh->rope_base > 0.0)) return fail(XP_EINVAL, "rms_eps / rope_base");
+  return XP_OK;
+}
+
+xp_status check_desc(const xp_layer_shape* sh, const xp_batch_desc* d) {
+  if (!d) return fail(XP_EINVAL, "null batch descriptor");
+  const int P = d->sp_degree;
+  if (d->n_prefill_local < 0 || d->n_decode < 0 || d->chunk_len < 0 || d->prior_len < 0)
+    return fail(XP_ESHAPE, "negative row count");
+  if (P < 1 || d->sp_rank < 0 || d->sp_rank >= P) return fail(XP_ESHAPE, "sp_degree %d / sp_rank %d", P, d->sp_rank);
+  if (sh->n_q_heads % P || sh->n_kv_heads % P)
+    return fail(XP_ESHAPE, "heads %d/%d not divisible by sp_degree %d", sh->n_q_heads, sh->n_kv_heads, P);
+  if (d->n_prefill_local > d->chunk_len) return fail(XP_ESHAPE, "n_prefill_local > chunk_len");
+  if (d->local_row_offset < 0 || d->local_row_offset + d->n_prefill_local > d->chunk_len)
+    return fail(XP_ESHAPE, "local rows [%d, %d) outside the chunk of %d", d->local_row_offset,
+                d->local_row_offset + d->n_prefill_local, d->chunk_len);
+  if (P == 1 && d->n_prefill_local != d->chunk_len) return fail(XP_ESHAPE, "sp_degree 1 needs every chunk row local");
+  if (rows_of(d) > 0 && !d->x) return fail(XP_EINVAL, "null x");
+  if (d->n_decode > 0) {
+    if (!d->dec_ctx || !d->dec_pages) return fail(XP_EINVAL, "null decode table");
+    if (d->dec_max_blocks < 1) return fail(XP_ESHAPE, "dec_max_blocks %d", d->dec_max_blocks);
+  }
+  if (d->chunk_len > 0) {
+    if (!d->pre_pages) return fail(XP_EINVAL, "null prefill table");
+    if (long(d->pre_max_blocks) * sh->page_size < long(d->prior_len) + d->chunk_len)
+      return fail(XP_EPAGE, "prefill table of %d blocks cannot hold %d positions", d->pre_max_blocks,
+                  d->prior_len + d->chunk_len);
+    const int n_peer = d->chunk_len - d->n_prefill_local;
+    if (n_peer > 0 && (!d->peer_qkv_in || !d->peer_attn_out)) return fail(XP_EINVAL, "null peer_qkv_in / peer_attn_out");
+    if (P > 1 && d->n_prefill_local > 0 && (!d->peer_qkv_out || !d->peer_attn_in))
+      return fail(XP_EINVAL, "null peer_qkv_out / peer_attn_in");
+  }
+  return XP_OK;
+}
+
+xp_ws_layout make_layout(const xp_ctx* ctx, const xp_layer_shape* sh, const xp_batch_desc* d) {
+  xp_ws_layout L;
+  memset(&L, 0, sizeof(L));
+  const size_t eb = dtype_bytes(sh->dtype);
+  const size_t M = rows_of(d), H = sh->hidden, F = sh->ffn_dim, Hq = sh->n_q_heads, Hkv = sh->n_kv_heads,
+               D = sh->head_dim;
+  const int pps = ctx ? ctx->pps : 32;
+  const int splits = d->n_decode > 0 ? decode_splits(d->dec_max_blocks, pps) : 0;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    size_t o = off;
+    off += align_up(std::max<size_t>(bytes, 1), 256);
+    return o;
+  };
+  L.status = take(sizeof(uint32_t));
+  L.hn = take(M * H * eb);
+  L.qkv = take(M * (Hq + 2 * Hkv) * D * 4);
+  L.q_dec = take(size_t(d->n_decode) * Hq * D * eb);
+  L.q_pre = take(size_t(Hq / d->sp_degree) * d->chunk_len * D * eb);
+  L.attn = take(M * Hq * D * eb);
+  const size_t units = size_t(d->n_decode) * Hq * splits;
+  L.dec_ml = take(units * 2 * sizeof(float));
+  L.dec_o = take(units * D * sizeof(float));
+  L.h1 = take(M * H * 4);
+  L.act = take(M * F * eb);
+  L.total = off;
+  L.dec_splits = splits;
+  L.dec_pages_per_split = pps;
+  return L;
+}
+
+}  // namespace
+
+extern "C" {
+
+xp_status xp_ctx_create(xp_ctx** out, int32_t device, int32_t decode_cus, int32_t pages_per_split) {
+  if (!out) return fail(XP_EINVAL, "null ctx out");
+  *out = nullptr;
+  int n_dev = 0;
+  XP_HIP_TRY(hipGetDeviceCount(&n_dev));
+  if (device < 0 || device >= n_dev) return fail(XP_EINVAL, "device %d of %d", device, n_dev);
+  if (pages_per_split < 0 || pages_per_split > 64) return fail(XP_EINVAL, "pages_per_split %d (0..64)", pages_per_split);
+  ScopedDevice sd(device);
+  hipDeviceProp_t prop;
+  XP_HIP_TRY(hipGetDeviceProperties(&prop, device));
+  xp_ctx* c = new xp_ctx();
+  c->device = device;
+  c->n_cus = prop.multiProcessorCount;
+  c->pps = pages_per_split ? pages_per_split : 32;
+  if (decode_cus < -1 || decode_cus >= c->n_cus) {
+    delete c;
+    return fail(XP_EINVAL, "decode_cus %d (valid: -1, 0, 1..%d)", decode_cus, c->n_cus - 1);
+  }
+  c->decode_cus = decode_cus;
+  hipError_t e = hipSuccess;
+  if (decode_cus > 0) {
+    spread_mask(c->n_cus, decode_cus, c->mask_dec, c->mask_pre);
+    e = hipExtStreamCreateWithCUMask(&c->s_dec, 8, c->mask_dec);
+    if (e == hipSuccess) e = hipExtStreamCreateWithCUMask(&c->s_pre, 8, c->mask_pre);
+  } else {
+    for (int w = 0; w < 8; ++w) c->mask_dec[w] = c->mask_pre[w] = 0xffffffffu;
+    if (decode_cus == -1) {
+      e = hipStreamCreateWithFlags(&c->s_dec, hipStreamNonBlocking);
+      if (e == hipSuccess) e = hipStreamCreateWithFlags(&c->s_pre, hipStreamNonBlocking);
+    }
+  }
+  if (e == hipSuccess) e = hipEventCreateWithFlags(&c->e_fork, hipEventDisableTiming);
+  if (e == hipSuccess) e = hipEventCreateWithFlags(&c->e_dec, hipEventDisableTiming);
+  if (e == hipSuccess) e = hipEventCreateWithFlags(&c->e_pre, hipEventDisableTiming);
+  if (e != hipSuccess) {
+    xp_ctx_destroy(c);
+    return fail(XP_EHIP, "xp_ctx_create: %s", hipGetErrorString(e));
+  }
+  *out = c;
+  return XP_OK;
+}
+
+xp_status xp_ctx_destroy(xp_ctx* c) {
+  if (!c) return XP_OK;
+  ScopedDevice sd(c->device);
+  if (c->s_dec) (void)hipStreamDestroy(c->s_dec);
+  if (c->s_pre) (void)hipStreamDestroy(c->s_pre);
+  if (c->e_fork) (void)hipEventDestroy(c->e_fork);
+  if (c->e_dec) (void)hipEventDestroy(c->e_dec);
+  if (c->e_pre) (void)hipEventDestroy(c->e_pre);
+  delete c;
+  return XP_OK;
+}
+
+xp_status xp_ctx_cu_masks(const xp_ctx* c, uint32_t* dec, uint32_t* pre, int32_t* n_cus) {
+  if (!c) return fail(XP_EINVAL, "null ctx");
+  for (int w = 0; w < 8; ++w) {
+    if (dec) dec[w] = c->mask_dec[w];
+    if (pre) pre[w] = c->mask_pre[w];
+  }
+  if (n_cus) *n_cus = c->n_cus;
+  return XP_OK;
+}
+
+xp_status xp_layer_workspace_layout(const xp_ctx* ctx, const xp_layer_shape* sh, const xp_batch_desc* d,
+                                    xp_ws_layout* out) {
+  if (!out) return fail(XP_EINVAL, "null layout out");
+  xp_status st = check_shape(sh);
+  if (st) return st;
+  if ((st = check_desc(sh, d))) return st;
+  *out = make_layout(ctx, sh, d);
+  return XP_OK;
+}
+
+xp_status xp_validate_batch(const xp_layer_shape* sh, const xp_batch_desc* d, int32_t n_pages,
+                            const int32_t* dec_ctx_h, const int32_t* dec_pages_h, const int32_t* pre_pages_h) {
+  xp_status st = check_shape(sh);
+  if (st) return st;
+  if ((st = check_desc(sh, d))) return st;
+  if (n_pages <= 0) return fail(XP_ESHAPE, "n_pages %d", n_pages);
+  std::string seen(size_t(n_pages), '\0');
+  const int S = sh->page_size, Hkv = sh->n_kv_heads;
+  auto use = [&](int p, const char* what) -> xp_status {
+    if (p < 0 || p >= n_pages) return fail(XP_EPAGE, "%s page id %d outside [0, %d)", what, p, n_pages);
+    if (seen[size_t(p)]) return fail(XP_EPAGE, "%s page id %d named twice", what, p);
+    seen[size_t(p)] = 1;
+    return XP_OK;
+  };
+  if (d->n_decode > 0) {
+    if (!dec_ctx_h || !dec_pages_h) return fail(XP_EINVAL, "null host decode tables");
+    for (int i = 0; i < d->n_decode; ++i) {
+      const int c = dec_ctx_h[i];
+      if (c < 0) return fail(XP_ESHAPE, "decode %d: context %d", i, c);
+      const int nb = c / S + 1;
+      if (nb > d->dec_max_blocks) return fail(XP_EPAGE, "decode %d: context %d needs %d blocks > %d", i, c, nb, d->dec_max_blocks);
+      for (int g = 0; g < Hkv; ++g)
+        for (int b = 0; b < nb; ++b)
+          if ((st = use(dec_pages_h[(long(i) * Hkv + g) * d->dec_max_blocks + b], "decode"))) return st;
+    }
+  }
+  if (d->chunk_len > 0) {
+    if (!pre_pages_h) return fail(XP_EINVAL, "null host prefill table");
+    const int nb = cdiv(long(d->prior_len) + d->chunk_len, S);
+    for (int g = 0; g < Hkv / d->sp_degree; ++g)
+      for (int b = 0; b < nb; ++b)
+        if ((st = use(pre_pages_h[long(g) * d->pre_max_blocks + b], "prefill"))) return st;
+  }
+  return XP_OK;
+}
+
+xp_status xp_layer_read_status(const void* ws, const xp_ws_layout* L, uint32_t* status, void* stream) {
+  if (!ws || !L || !status) return fail(XP_EINVAL, "null argument");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  XP_HIP_TRY(hipMemcpyAsync(status, static_cast<const char*>(ws) + L->status, sizeof(uint32_t),
+                            hipMemcpyDeviceToHost, s));
+  XP_HIP_TRY(hipStreamSynchronize(s));
+  return XP_OK;
+}
+
+xp_status xp_layer_forward(xp_ctx* ctx, const xp_layer_shape* sh, const xp_batch_desc* d, const xp_layer_weights* w,
+                           const xp_kv_pages* kv, float* out, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!ctx) return fail(XP_EINVAL, "null ctx");
+  xp_status st = check_shape(sh);
+  if (st) return st;
+  if ((st = check_desc(sh, d))) return st;
+  if (!w || !w->w_qkv || !w->w_o || !w->w_gate || !w->w_up || !w->w_down || !w->g_attn || !w->g_ffn)
+    return fail(XP_EINVAL, "null weight");
+  if (!kv || !kv->pool || kv->n_pages <= 0) return fail(XP_EINVAL, "null or empty KV pool");
+  const int M = rows_of(d);
+  if (M > 0 && !out) return fail(XP_EINVAL, "null out");
+  const xp_ws_layout L = make_layout(ctx, sh, d);
+  if (!workspace || workspace_bytes < L.total)
+    return fail(XP_EWORKSPACE, "workspace of %zu bytes < %zu required", workspace_bytes, L.total);
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int dt = sh->dtype;
+  const size_t eb = dtype_bytes(dt);
+  const int H = sh->hidden, Hq = sh->n_q_heads, Hkv = sh->n_kv_heads, D = sh->head_dim, F = sh->ffn_dim;
+  const int P = d->sp_degree, r = d->sp_rank, hq_loc = Hq / P, hkv_loc = Hkv / P;
+  const int n_pl = d->n_prefill_local, n_d = d->n_decode;
+  char* ws = static_cast<char*>(workspace);
+  uint32_t* status = reinterpret_cast<uint32_t*>(ws + L.status);
+  char* hn = ws + L.hn;
+  float* qkv = reinterpret_cast<float*>(ws + L.qkv);
+  char* attn = ws + L.attn;
+  float* h1 = reinterpret_cast<float*>(ws + L.h1);
+  char* act = ws + L.act;
+
+  // shared linear region (1): RMSNorm + QKV over all M rows
+  if ((st = launch_rmsnorm(dt, d->x, 0, w->g_attn, hn, M, H, sh->rms_eps, status, s))) return st;
+  if (M > 0 && (st = launch_gemm(dt, XP_EPI_F32, hn, w->w_qkv, nullptr, nullptr, qkv, M, (Hq + 2 * Hkv) * D, H, s)))
+    return st;
+  // RoPE + appends (+ the peer stand-ins)
+  PostQkvArgs pa{qkv, n_pl, n_d, Hq, Hkv, D, sh->page_size, sh->rope_base, d->dec_ctx, d->dec_pages,
+                 d->dec_max_blocks, d->prior_len, d->chunk_len, P, r, d->local_row_offset, d->pre_pages,
+                 d->pre_max_blocks, d->peer_qkv_in, d->peer_qkv_out, d->peer_attn_in, kv->pool, kv->n_pages,
+                 ws + L.q_dec, ws + L.q_pre, attn, status};
+  if ((st = launch_post_qkv(dt, pa, s))) return st;
+
+  // split attention region
+  auto decode = [&](hipStream_t q) {
+    return launch_decode(dt, ws + L.q_dec, kv->pool, kv->n_pages, sh->page_size, d->dec_pages, d->dec_max_blocks,
+                         d->dec_ctx, n_d, Hq, Hkv, D, attn + size_t(n_pl) * Hq * D * eb, Hq * D,
+                         reinterpret_cast<float*>(ws + L.dec_ml), reinterpret_cast<float*>(ws + L.dec_o), ctx->pps,
+                         status, q);
+  };
+  auto prefill = [&](hipStream_t q) {
+    return launch_prefill(dt, ws + L.q_pre, kv->pool, kv->n_pages, sh->page_size, d->pre_pages, d->pre_max_blocks,
+                          hq_loc, hkv_loc, D, d->prior_len, d->chunk_len, d->local_row_offset, n_pl,
+                          attn + size_t(r) * hq_loc * D * eb, Hq * D, d->peer_attn_out, hq_loc * D, status, q);
+  };
+  const bool concurrent = ctx->s_dec && n_d > 0 && d->chunk_len > 0;
+  if (!concurrent) {
+    if ((st = decode(s))) return st;
+    if ((st = prefill(s))) return st;
+  } else {
+    XP_HIP_TRY(hipEventRecord(ctx->e_fork, s));
+    XP_HIP_TRY(hipStreamWaitEvent(ctx->s_dec, ctx->e_fork, 0));
+    XP_HIP_TRY(hipStreamWaitEvent(ctx->s_pre, ctx->e_fork, 0));
+    if ((st = decode(ctx->s_dec))) return st;
+    XP_HIP_TRY(hipEventRecord(ctx->e_dec, ctx->s_dec));
+    if ((st = prefill(ctx->s_pre))) return st;
+    XP_HIP_TRY(hipEventRecord(ctx->e_pre, ctx->s_pre));
+    XP_HIP_TRY(hipStreamWaitEvent(s, ctx->e_dec, 0));
+    XP_HIP_TRY(hipStreamWaitEvent(s, ctx->e_pre, 0));
+  }
+  if (M == 0) return XP_OK;
+
+  // shared linear region (2): O projection + residual, RMSNorm, gate/up + SwiGLU, down + residual
+  if ((st = launch_gemm(dt, XP_EPI_ADD_T, attn, w->w_o, nullptr, d->x, h1, M, H, Hq * D, s))) return st;
+  if ((st = launch_rmsnorm(dt, h1, 1, w->g_ffn, hn, M, H, sh->rms_eps, nullptr, s))) return st;
+  if ((st = launch_gemm(dt, XP_EPI_SWIGLU, hn, w->w_gate, w->w_up, nullptr, act, M, F, H, s))) return st;
+  if ((st = launch_gemm(dt, XP_EPI_ADD_F32, act, w->w_down, nullptr, h1, out, M, H, F, s))) return st;
+  return XP_OK;
+}
+
+// ---- kernel-level entry points ------------------------------------------------
+
+xp_status xp_rmsnorm(int32_t dtype, const void* x, int32_t x_is_f32, const void* gamma, void* y, int32_t M,
+                     int32_t H, float eps, void* stream) {
+  return launch_rmsnorm(dtype, x, x_is_f32, gamma, y, M, H, eps, nullptr, static_cast<hipStream_t>(stream));
+}
+
+xp_status xp_gemm(int32_t dtype, int32_t epi, const void* A, const void* B, const void* B2, const void* R, void* C,
+                  int32_t M, int32_t N, int32_t K, void* stream) {
+  return launch_gemm(dtype, epi, A, B, B2, R, C, M, N, K, static_cast<hipStream_t>(stream));
+}
+
+xp_status xp_kv_append(int32_t dtype, void* pool, int32_t n_pages, int32_t S, int32_t d, const int32_t* table,
+                       int32_t table_stride, const int32_t* seq, const int32_t* pos, const void* k, const void* v,
+                       int32_t n, void* stream) {
+  if (dtype != XP_BF16 && dtype != XP_F32) return fail(XP_EINVAL, "xp_kv_append: dtype %d", dtype);
+  if (n < 0 || S <= 0 || d <= 0 || table_stride <= 0 || n_pages <= 0) return fail(XP_ESHAPE, "xp_kv_append: sizes");
+  if (n > 0 && (!pool || !table || !seq || !pos || !k || !v)) return fail(XP_EINVAL, "xp_kv_append: null pointer");
+  return launch_kv_append(dtype, pool, n_pages, S, d, table, table_stride, seq, pos, k, v, n, nullptr,
+                          static_cast<hipStream_t>(stream));
+}
+
+xp_status xp_kv_gather(int32_t dtype, const void* pool, int32_t n_pages, int32_t S, int32_t d, const int32_t* table,
+                       int32_t table_stride, const int32_t* len, int32_t n_seq, int32_t max_len, void* k_out,
+                       void* v_out, void* stream) {
+  if (dtype != XP_BF16 && dtype != XP_F32) return fail(XP_EINVAL, "xp_kv_gather: dtype %d", dtype);
+  if (n_seq < 0 || max_len < 0 || S <= 0 || d <= 0 || table_stride <= 0 || n_pages <= 0)
+    return fail(XP_ESHAPE, "xp_kv_gather: sizes");
+  if (n_seq > 0 && max_len > 0 && (!pool || !table || !len || !k_out || !v_out))
+    return fail(XP_EINVAL, "xp_kv_gather: null pointer");
+  return launch_kv_gather(dtype, pool, n_pages, S, d, table, table_stride, len, n_seq, max_len, k_out, v_out,
+                          static_cast<hipStream_t>(stream));
+}
+
+size_t xp_decode_workspace_size(int32_t n_d, int32_t Hq, int32_t d, int32_t max_blocks, int32_t pps) {
+  if (n_d <= 0 || Hq <= 0 || d <= 0 || max_blocks <= 0 || pps <= 0) return 0;
+  return decode_ws_bytes(n_d, Hq, d, decode_splits(max_blocks, pps));
+}
+
+xp_status xp_decode_attention(int32_t dtype, const void* q, const void* pool, int32_t n_pages, int32_t S,
+                              const int32_t* dec_pages, int32_t max_blocks, const int32_t* dec_ctx, int32_t n_d,
+                              int32_t Hq, int32_t Hkv, int32_t d, void* out, int32_t out_stride, void* workspace,
+                              int32_t pps, void* stream) {
+  if (n_d < 0) return fail(XP_ESHAPE, "xp_decode_attention: n_decode %d", n_d);
+  if (n_d == 0) return XP_OK;
+  if (!q || !pool || !dec_pages || !dec_ctx || !out || !workspace) return fail(XP_EINVAL, "xp_decode_attention: null pointer");
+  if (out_stride < Hq * d) return fail(XP_ESHAPE, "xp_decode_attention: out_stride %d < Hq*d", out_stride);
+  if (pps <= 0) pps = 32;
+  const int splits = decode_splits(max_blocks, pps);
+  const size_t ml_bytes = align_up(size_t(n_d) * Hq * splits * 2 * sizeof(float), 256);
+  float* ml = static_cast<float*>(workspace);
+  float* po = reinterpret_cast<float*>(static_cast<char*>(workspace) + ml_bytes);
+  return launch_decode(dtype, q, pool, n_pages, S, dec_pages, max_blocks, dec_ctx, n_d, Hq, Hkv, d, out, out_stride,
+                       ml, po, pps, nullptr, static_cast<hipStream_t>(stream));
+}
+
+xp_status xp_prefill_attention(int32_t dtype, const void* q, const void* pool, int32_t n_pages, int32_t S,
+                               const int32_t* pre_pages, int32_t pre_max_blocks, int32_t hq, int32_t hkv, int32_t d,
+                               int32_t prior, int32_t chunk, int32_t off, int32_t n_local, void* out_local,
+                               int32_t out_local_stride, void* out_peer, int32_t out_peer_stride, uint32_t* status,
+                               void* stream) {
+  if (chunk < 0 || prior < 0) return fail(XP_ESHAPE, "xp_prefill_attention: chunk/prior");
+  if (chunk == 0) return XP_OK;
+  if (!q || !pool || !pre_pages) return fail(XP_EINVAL, "xp_prefill_attention: null pointer");
+  if (n_local > 0 && (!out_local || out_local_stride < hq * d)) return fail(XP_EINVAL, "xp_prefill_attention: out_local");
+  if (chunk - n_local > 0 && (!out_peer || out_peer_stride < hq * d)) return fail(XP_EINVAL, "xp_prefill_attention: out_peer");
+  return launch_prefill(dtype, q, pool, n_pages, S, pre_pages, pre_max_blocks, hq, hkv, d, prior, chunk, off, n_local,
+                        out_local, out_local_stride, out_peer, out_peer_stride, status, static_cast<hipStream_t>(stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,228 @@
+// Paged GQA decode attention, split-K over the context, with an fp32
+// log-sum-exp merge of the partials.
+//
+// ConfluxServe §4: decode attention stays rank-local and each request reads
+// only its own KV, so the step is bound by HBM bandwidth (App. B, Table 7:
+// its arithmetic intensity does not grow with batch).  The merge of partial
+// results uses the (output, fp32 log-sum-exp) partial form of Decode Token
+// Parallelism Eq. 4.
+//
+// One wave handles one (request, KV head, split) and reads each page of the
+// split exactly once for all G query heads of the group:
+//   S^T[16 keys x 16 heads] = K_page[16 x d] . Q^T[d x 16]   (16x16 MFMA, 32-deep k)
+//   O^T[d x 16 heads]     += V^T_page[d x 16 keys] . P^T     (16x16 MFMA, 16-deep k)
+// Query heads are the MFMA columns (G <= 16, unused columns are zero), so lane
+// l owns head l % 16 for both the scores and the output, and the online-softmax
+// rescale needs no cross-lane traffic beyond the 16-key max.  The V plane of a
+// page is stored dim-major, so the V^T operand of lane l is 4 consecutive keys
+// of one dim row (8 contiguous bytes for bf16).  Scores are kept in the exp2
+// domain (scale * log2(e) folded in).  The next page's K/V fragments are loaded
+// before the current page is consumed.
+#include "xp_device.h"
+#include "xp_internal.h"
+
+namespace xp {
+
+namespace {
+
+constexpr int kPage = 16;
+
+__device__ __forceinline__ void zero_tail(Frag4<bf16_t>& f, int nvalid) {
+  uint32_t x = f.v.x, y = f.v.y;
+  if (nvalid <= 0) x = 0;
+  else if (nvalid == 1) x &= 0xffffu;
+  if (nvalid <= 2) y = 0;
+  else if (nvalid == 3) y &= 0xffffu;
+  f.v = make_uint2(x, y);
+}
+__device__ __forceinline__ void zero_tail(Frag4<float>& f, int nvalid) {
+  if (nvalid <= 0) f.v.x = 0.f;
+  if (nvalid <= 1) f.v.y = 0.f;
+  if (nvalid <= 2) f.v.z = 0.f;
+  if (nvalid <= 3) f.v.w = 0.f;
+}
+
+template <typename T, int D>
+struct PageFrags {
+  Frag8<T> k[D / 32];
+  Frag4<T> v[D / 16];
+};
+
+template <typename T, int D>
+__device__ __forceinline__ void load_page(PageFrags<T, D>& f, const char* page, int lane) {
+  constexpr int EB = St<T>::bytes;
+  const int key = lane & 15, grp = lane >> 4;
+#pragma unroll
+  for (int st = 0; st < D / 32; ++st) load_frag8(f.k[st], page + (key * D + 32 * st + 8 * grp) * EB);
+  const char* vp = page + kPage * D * EB;
+#pragma unroll
+  for (int n = 0; n < D / 16; ++n) load_frag4(f.v[n], vp + ((16 * n + key) * kPage + 4 * grp) * EB);
+}
+
+template <typename T, int D>
+__global__ __launch_bounds__(64) void decode_split_kernel(const void* __restrict__ q, const char* __restrict__ pool,
+                                                          int n_pages, const int32_t* __restrict__ dec_pages,
+                                                          int max_blocks, const int32_t* __restrict__ dec_ctx, int Hq,
+                                                          int Hkv, int pps, int n_splits, float* __restrict__ part_ml,
+                                                          float* __restrict__ part_o, float scale_log2,
+                                                          uint32_t* __restrict__ status) {
+  constexpr int EB = St<T>::bytes;
+  constexpr long PAGE_BYTES = 2L * kPage * D * EB;
+  const int s = blockIdx.x, g = blockIdx.y, i = blockIdx.z;
+  const int lane = threadIdx.x;
+  const int G = Hq / Hkv;
+  const int n_keys = dec_ctx[i] + 1;
+  const int nb_need = (n_keys + kPage - 1) / kPage;
+  const int nb = min(nb_need, max_blocks);
+  const int b0 = s * pps;
+  if (b0 >= nb_need && !(s == 0 && n_keys <= 0)) return;  // this split has no keys
+  const int b1 = min(nb, b0 + pps);
+  bool bad = nb_need > max_blocks || n_keys <= 0;
+
+  const int hh = lane & 15, grp = lane >> 4;
+  Frag8<T> qf[D / 32];
+#pragma unroll
+  for (int st = 0; st < D / 32; ++st) {
+    if (hh < G) {
+      load_frag8(qf[st], static_cast<const char*>(q) + ((long(i) * Hq + g * G + hh) * D + 32 * st + 8 * grp) * EB);
+    } else {
+      zero_frag(qf[st]);
+    }
+  }
+  const int32_t* tbl = dec_pages + (long(i) * Hkv + g) * max_blocks;
+  const int my_pid = (b0 + lane < b1) ? tbl[b0 + lane] : 0;
+
+  f32x4 o[D / 16];
+#pragma unroll
+  for (int n = 0; n < D / 16; ++n) o[n] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m = -__builtin_inff(), lsum = 0.f;
+
+  PageFrags<T, D> cur, nxt;
+  int pid = __builtin_amdgcn_readlane(my_pid, 0);
+  bool ok = b0 < b1 && pid >= 0 && pid < n_pages;
+  if (ok) load_page<T, D>(cur, pool + pid * PAGE_BYTES, lane);
+  for (int b = b0; b < b1; ++b) {
+    const bool ok_cur = ok;
+    if (b + 1 < b1) {
+      pid = __builtin_amdgcn_readlane(my_pid, b + 1 - b0);
+      ok = pid >= 0 && pid < n_pages;
+      if (ok) load_page<T, D>(nxt, pool + pid * PAGE_BYTES, lane);
+    }
+    if (!ok_cur) {
+      bad = true;
+    } else {
+      f32x4 sacc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int st = 0; st < D / 32; ++st) mma16x16_k32(sacc, cur.k[st], qf[st]);
+      // element r: key b*16 + 4*grp + r of head hh
+      const int k0 = b * kPage + 4 * grp;
+      float sv[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) sv[r] = (k0 + r < n_keys) ? sacc[r] * scale_log2 : -__builtin_inff();
+      if ((b + 1) * kPage > n_keys) {
+#pragma unroll
+        for (int n = 0; n < D / 16; ++n) zero_tail(cur.v[n], n_keys - k0);
+      }
+      float mb = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
+      mb = fmaxf(mb, shfl_xor(mb, 16));
+      mb = fmaxf(mb, shfl_xor(mb, 32));
+      const float mn = fmaxf(m, mb);  // finite: every visited page holds a visible key
+      const float alpha = fast_exp2(m - mn);
+      // the weights are rounded to the operand type first, so the normaliser sums
+      // exactly the weights the PV product uses
+      const float p0 = round_st<T>(fast_exp2(sv[0] - mn)), p1 = round_st<T>(fast_exp2(sv[1] - mn));
+      const float p2 = round_st<T>(fast_exp2(sv[2] - mn)), p3 = round_st<T>(fast_exp2(sv[3] - mn));
+      lsum = lsum * alpha + ((p0 + p1) + (p2 + p3));
+      Frag4<T> pf;
+      set_frag4(pf, p0, p1, p2, p3);
+#pragma unroll
+      for (int n = 0; n < D / 16; ++n) {
+        o[n] *= alpha;
+        mma16x16_k16(o[n], cur.v[n], pf);
+      }
+      m = mn;
+    }
+    cur = nxt;
+  }
+  lsum += shfl_xor(lsum, 16);
+  lsum += shfl_xor(lsum, 32);
+  if (bad && status && lane == 0) atomicOr(status, XP_DEV_BAD_PAGE);
+  if (hh < G) {
+    const long base = (long(i) * Hq + g * G + hh) * n_splits + s;
+    if (grp == 0) {
+      part_ml[2 * base] = bad ? __builtin_nanf("") : m;
+      part_ml[2 * base + 1] = lsum;
+    }
+    float* po = part_o + base * D;
+#pragma unroll
+    for (int n = 0; n < D / 16; ++n)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) po[16 * n + 4 * grp + r] = o[n][r];
+  }
+}
+
+// out[i, h*D + j] = sum_s 2^(m_s - m*) o_s[j] / sum_s 2^(m_s - m*) l_s
+template <typename T, int D>
+__global__ __launch_bounds__(D) void decode_combine_kernel(const float* __restrict__ part_ml,
+                                                           const float* __restrict__ part_o,
+                                                           const int32_t* __restrict__ dec_ctx, int Hq, int pps,
+                                                           int n_splits, void* __restrict__ out, int out_stride) {
+  const int h = blockIdx.x, i = blockIdx.y, j = threadIdx.x;
+  const int nb = (dec_ctx[i] + 1 + kPage - 1) / kPage;
+  const int ns = max(1, min(n_splits, (nb + pps - 1) / pps));
+  const long base = (long(i) * Hq + h) * n_splits;
+  float mx = -__builtin_inff();
+  for (int s = 0; s < ns; ++s) mx = fmaxf(mx, part_ml[2 * (base + s)]);
+  float L = 0.f, acc = 0.f;
+  for (int s = 0; s < ns; ++s) {
+    const float w = fast_exp2(part_ml[2 * (base + s)] - mx);
+    L += part_ml[2 * (base + s) + 1] * w;
+    acc += part_o[(base + s) * D + j] * w;
+  }
+  St<T>::store(out, long(i) * out_stride + long(h) * D + j, acc / L);
+}
+
+template <typename T, int D>
+xp_status launch_dec_t(const void* q, const void* pool, int n_pages, const int32_t* dec_pages, int max_blocks,
+                       const int32_t* dec_ctx, int n_d, int Hq, int Hkv, void* out, int out_stride, float* part_ml,
+                       float* part_o, int pps, uint32_t* status, hipStream_t s) {
+  const int n_splits = decode_splits(max_blocks, pps);
+  const float scale_log2 = float(1.4426950408889634 / __builtin_sqrt(double(D)));
+  hipLaunchKernelGGL((decode_split_kernel<T, D>), dim3(n_splits, Hkv, n_d), dim3(64), 0, s, q,
+                     static_cast<const char*>(pool), n_pages, dec_pages, max_blocks, dec_ctx, Hq, Hkv, pps, n_splits,
+                     part_ml, part_o, scale_log2, status);
+  XP_CHECK_LAUNCH();
+  hipLaunchKernelGGL((decode_combine_kernel<T, D>), dim3(Hq, n_d), dim3(D), 0, s, part_ml, part_o, dec_ctx, Hq, pps,
+                     n_splits, out, out_stride);
+  XP_CHECK_LAUNCH();
+  return XP_OK;
+}
+
+}  // namespace
+
+int decode_splits(int dec_max_blocks, int pps) { return std::max(1, cdiv(dec_max_blocks, pps)); }
+
+size_t decode_ws_bytes(int n_d, int Hq, int d, int n_splits) {
+  const size_t units = size_t(n_d) * Hq * n_splits;
+  return align_up(units * 2 * sizeof(float), 256) + align_up(units * d * sizeof(float), 256);
+}
+
+xp_status launch_decode(int dtype, const void* q, const void* pool, int n_pages, int S, const int32_t* dec_pages,
+                        int dec_max_blocks, const int32_t* dec_ctx, int n_d, int Hq, int Hkv, int d, void* out,
+                        int out_stride, float* part_ml, float* part_o, int pps, uint32_t* status, hipStream_t s) {
+  if (n_d == 0) return XP_OK;
+  if (S != kPage) return fail(XP_EUNSUPPORTED, "decode attention: page_size %d (supported: 16)", S);
+  if (Hkv <= 0 || Hq % Hkv || Hq / Hkv > 16) return fail(XP_EUNSUPPORTED, "decode attention: Hq=%d Hkv=%d", Hq, Hkv);
+  if (pps < 1 || pps > 64) return fail(XP_EINVAL, "decode attention: pages_per_split %d (1..64)", pps);
+  if (dec_max_blocks < 1) return fail(XP_ESHAPE, "decode attention: dec_max_blocks %d", dec_max_blocks);
+  if (dtype == XP_BF16) {
+    if (d == 128) return launch_dec_t<bf16_t, 128>(q, pool, n_pages, dec_pages, dec_max_blocks, dec_ctx, n_d, Hq, Hkv, out, out_stride, part_ml, part_o, pps, status, s);
+    if (d == 64) return launch_dec_t<bf16_t, 64>(q, pool, n_pages, dec_pages, dec_max_blocks, dec_ctx, n_d, Hq, Hkv, out, out_stride, part_ml, part_o, pps, status, s);
+  } else if (dtype == XP_F32) {
+    if (d == 128) return launch_dec_t<float, 128>(q, pool, n_pages, dec_pages, dec_max_blocks, dec_ctx, n_d, Hq, Hkv, out, out_stride, part_ml, part_o, pps, status, s);
+    if (d == 64) return launch_dec_t<float, 64>(q, pool, n_pages, dec_pages, dec_max_blocks, dec_ctx, n_d, Hq, Hkv, out, out_stride, part_ml, part_o, pps, status, s);
+  }
+  return fail(XP_EUNSUPPORTED, "decode attention: dtype %d head_dim %d", dtype, d);
+}
+
+}  // namespace xp

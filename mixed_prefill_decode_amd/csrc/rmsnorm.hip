@@ -1,0 +1,62 @@
+// RMSNorm of a row block: y = x / sqrt(mean(x^2) + eps) * gamma, written in the
+// storage type as the next projection's MFMA operand (pre-norm block; Decode
+// Token Parallelism §4.3 lists normalization between attention and the MLP).
+// One workgroup per row; the sum of squares is accumulated in fp32.
+#include "xp_device.h"
+#include "xp_internal.h"
+
+namespace xp {
+
+namespace {
+
+template <typename TI, typename TO>
+__global__ __launch_bounds__(256) void rmsnorm_kernel(const void* __restrict__ x, const void* __restrict__ gamma,
+                                                      void* __restrict__ y, int H, float eps,
+                                                      uint32_t* __restrict__ status_clear) {
+  __shared__ float red[4];
+  const int row = blockIdx.x, tid = threadIdx.x;
+  if (status_clear && row == 0 && tid == 0) *status_clear = 0u;
+  const long base = long(row) * H;
+  float ss = 0.f;
+  for (int i = tid; i < H; i += 256) {
+    const float v = St<TI>::load(x, base + i);
+    ss += v * v;
+  }
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) ss += shfl_xor(ss, m);
+  if ((tid & 63) == 0) red[tid >> 6] = ss;
+  __syncthreads();
+  const float tot = red[0] + red[1] + red[2] + red[3];
+  const float rstd = 1.0f / sqrtf(tot / float(H) + eps);
+  for (int i = tid; i < H; i += 256) St<TO>::store(y, base + i, St<TI>::load(x, base + i) * rstd * St<TO>::load(gamma, i));
+}
+
+__global__ void clear_status_kernel(uint32_t* status) { *status = 0u; }
+
+}  // namespace
+
+xp_status launch_rmsnorm(int dtype, const void* x, int x_is_f32, const void* gamma, void* y, int M, int H,
+                         float eps, uint32_t* status_clear, hipStream_t s) {
+  if (dtype != XP_BF16 && dtype != XP_F32) return fail(XP_EINVAL, "xp_rmsnorm: dtype %d", dtype);
+  if (M < 0 || H <= 0) return fail(XP_ESHAPE, "xp_rmsnorm: M=%d H=%d", M, H);
+  if (!x || !gamma || !y) return fail(XP_EINVAL, "xp_rmsnorm: null pointer");
+  if (M == 0) {
+    if (status_clear) {
+      hipLaunchKernelGGL(clear_status_kernel, dim3(1), dim3(1), 0, s, status_clear);
+      XP_CHECK_LAUNCH();
+    }
+    return XP_OK;
+  }
+  if (dtype == XP_BF16) {
+    if (x_is_f32)
+      hipLaunchKernelGGL((rmsnorm_kernel<float, bf16_t>), dim3(M), dim3(256), 0, s, x, gamma, y, H, eps, status_clear);
+    else
+      hipLaunchKernelGGL((rmsnorm_kernel<bf16_t, bf16_t>), dim3(M), dim3(256), 0, s, x, gamma, y, H, eps, status_clear);
+  } else {
+    hipLaunchKernelGGL((rmsnorm_kernel<float, float>), dim3(M), dim3(256), 0, s, x, gamma, y, H, eps, status_clear);
+  }
+  XP_CHECK_LAUNCH();
+  return XP_OK;
+}
+
+}  // namespace xp

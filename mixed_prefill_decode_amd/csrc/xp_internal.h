@@ -1,0 +1,80 @@
+// Host-side internals shared by the library's translation units.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <string>
+
+#include "../../include/xp.h"
+
+namespace xp {
+
+// Records the message of a failing call for xp_last_error() and returns `code`.
+xp_status fail(xp_status code, const char* fmt, ...);
+
+#define XP_HIP_TRY(expr)                                                        \
+  do {                                                                          \
+    hipError_t e_ = (expr);                                                     \
+    if (e_ != hipSuccess) return ::xp::fail(XP_EHIP, "%s: %s", #expr, hipGetErrorString(e_)); \
+  } while (0)
+
+#define XP_CHECK_LAUNCH()                                                       \
+  do {                                                                          \
+    hipError_t e_ = hipGetLastError();                                          \
+    if (e_ != hipSuccess) return ::xp::fail(XP_EHIP, "kernel launch: %s", hipGetErrorString(e_)); \
+  } while (0)
+
+inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+inline int cdiv(long a, long b) { return int((a + b - 1) / b); }
+inline int dtype_bytes(int dtype) { return dtype == XP_BF16 ? 2 : 4; }
+
+// ---- launchers (each validates its own arguments) ------------------------------
+xp_status launch_rmsnorm(int dtype, const void* x, int x_is_f32, const void* gamma, void* y, int M,
+                         int H, float eps, uint32_t* status_clear, hipStream_t s);
+
+xp_status launch_gemm(int dtype, int epi, const void* A, const void* B, const void* B2, const void* R,
+                      void* C, int M, int N, int K, hipStream_t s);
+
+struct PostQkvArgs {
+  const float* qkv;
+  int n_pl, n_d;
+  int Hq, Hkv, d, S;
+  double rope_base;
+  const int32_t* dec_ctx;
+  const int32_t* dec_pages;
+  int dec_max_blocks;
+  int prior, chunk, P, r, off;
+  const int32_t* pre_pages;
+  int pre_max_blocks;
+  const void* peer_qkv_in;
+  void* peer_qkv_out;
+  const void* peer_attn_in;
+  void* pool;
+  int n_pages;
+  void* q_dec;
+  void* q_pre;
+  void* attn;
+  uint32_t* status;
+};
+xp_status launch_post_qkv(int dtype, const PostQkvArgs& a, hipStream_t s);
+
+xp_status launch_kv_append(int dtype, void* pool, int n_pages, int S, int d, const int32_t* table,
+                           int table_stride, const int32_t* seq, const int32_t* pos, const void* k,
+                           const void* v, int n, uint32_t* status, hipStream_t s);
+xp_status launch_kv_gather(int dtype, const void* pool, int n_pages, int S, int d, const int32_t* table,
+                           int table_stride, const int32_t* len, int n_seq, int max_len, void* k_out,
+                           void* v_out, hipStream_t s);
+
+int decode_splits(int dec_max_blocks, int pages_per_split);
+size_t decode_ws_bytes(int n_d, int Hq, int d, int n_splits);
+xp_status launch_decode(int dtype, const void* q, const void* pool, int n_pages, int S,
+                        const int32_t* dec_pages, int dec_max_blocks, const int32_t* dec_ctx, int n_d,
+                        int Hq, int Hkv, int d, void* out, int out_stride, float* part_ml,
+                        float* part_o, int pages_per_split, uint32_t* status, hipStream_t s);
+
+xp_status launch_prefill(int dtype, const void* q, const void* pool, int n_pages, int S,
+                         const int32_t* pre_pages, int pre_max_blocks, int hq, int hkv, int d,
+                         int prior, int chunk, int off, int n_local, void* out_local,
+                         int out_local_stride, void* out_peer, int out_peer_stride, uint32_t* status,
+                         hipStream_t s);
+
+}  // namespace xp

@@ -1,0 +1,158 @@
+"""The C-ABI library on the host: it loads, exports every declared symbol, its host-only
+entry points (waterfill, latency model, validation) agree with the oracle -- CPU only."""
+import os
+import random
+import re
+
+import numpy as np
+import pytest
+
+import mixed_prefill_decode_amd as X
+from oracle import waterfill as wf
+from synth import get_workload, make_instance, waterfill_cases
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(__file__)), "include", "xp.h")
+
+
+def test_library_exports_every_declared_symbol():
+    decl = set(re.findall(r"^\s*(?:xp_status|const char\*|size_t)\s+(xp_\w+)\s*\(", open(HEADER).read(), re.M))
+    assert decl == set(X.EXPORTED)
+    L = X.lib()
+    for name in decl:
+        assert getattr(L, name) is not None
+    assert "gfx950" in X.xp_build_info()
+
+
+def test_waterfill_worked_example():
+    import json
+    g = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "waterfill_worked_example.json")))
+    m = dict(gamma=1.0, gamma0=0.0, a_d=0.0, a_d0=0.0, a_p=0.0, a_p0=0.0, a_comm=0.0, a_comm0=0.0,
+             alpha=1.0, beta=1.0, n_layers=1)
+    r = X.xp_waterfill(tau=1.0, n_decode_tokens=g["n_decode_tokens"], decode_ctx_sum=[0] * 4,
+                       candidate=(g["candidate_remaining"], 0), model=m, fixed_target=g["n_target"])
+    assert (r["budget"], r["chunk_len"], r["assign"]) == (g["budget"], g["chunk_len"], g["assign"])
+
+
+def _rand_model(rnd):
+    # arbitrary (non-dyadic) coefficients: both sides evaluate the same IEEE operations
+    return dict(gamma=rnd.uniform(0.1, 3), gamma0=rnd.uniform(0, 5), a_d=rnd.uniform(0, 0.3),
+                a_d0=rnd.uniform(0, 2), a_p=rnd.uniform(0, 0.1), a_p0=rnd.uniform(0, 2),
+                a_comm=rnd.uniform(0, 1), a_comm0=rnd.uniform(0, 3), alpha=rnd.uniform(1, 1.5),
+                beta=rnd.uniform(1, 2), n_layers=rnd.randint(1, 4))
+
+
+def test_waterfill_bit_exact_with_oracle_on_random_cases():
+    rnd = random.Random(5)
+    for _ in range(600):
+        n = rnd.randint(1, 8)
+        nd = [rnd.randint(0, 300) for _ in range(n)]
+        ctx = [rnd.randint(0, 100000) if nd[r] else 0 for r in range(n)]
+        ex = [rnd.randint(0, 50) for _ in range(n)] if rnd.random() < 0.5 else None
+        sel = [(rnd.randint(1, 400), rnd.randint(0, 5000)) for _ in range(rnd.randint(0, 2))]
+        cand = (rnd.randint(0, 5000), rnd.randint(0, 20000)) if rnd.random() < 0.8 else None
+        kw = dict(tau=rnd.uniform(50, 5000), n_decode_tokens=nd, decode_ctx_sum=ctx, existing=ex,
+                  selected=sel, candidate=cand, quantum=rnd.choice([1, 8, 16, 64]), model=_rand_model(rnd),
+                  fixed_target=rnd.choice([-1, -1, -1, rnd.randint(0, 1000)]),
+                  level_hi=0 if cand else rnd.randint(0, 3000))
+        assert X.xp_waterfill(**kw) == wf.dispatch(**kw)
+
+
+def test_waterfill_bit_exact_on_the_c5_cases():
+    for c in waterfill_cases():
+        kw = dict(tau=c.tbt_slo, n_decode_tokens=c.n_decode_tokens, decode_ctx_sum=c.decode_ctx_sum,
+                  existing=c.existing_assign, selected=c.selected, candidate=c.candidate, quantum=c.quantum,
+                  model=c.model, fixed_target=c.fixed_target, level_hi=c.level_hi)
+        r = X.xp_waterfill(**kw)
+        assert r == wf.dispatch(**kw), c.name
+        assert sum(r["assign"]) == r["chunk_len"]
+
+
+def test_iteration_latency_bit_exact_with_oracle():
+    rnd = random.Random(9)
+    for _ in range(300):
+        n = rnd.randint(1, 8)
+        nd = [rnd.randint(0, 100) for _ in range(n)]
+        cs = [rnd.randint(0, 10 ** 6) for _ in range(n)]
+        npf = [rnd.randint(0, 2000) * rnd.randint(0, 1) for _ in range(n)]
+        ch = [(rnd.randint(1, 4096), rnd.randint(0, 60000)) for _ in range(rnd.randint(0, 3))]
+        m = _rand_model(rnd)
+        assert X.xp_iteration_latency(m, nd, cs, npf, ch) == wf.iteration_latency(m, nd, cs, npf, ch)
+
+
+def test_waterfill_rejects_bad_arguments():
+    m = dict(gamma=1, gamma0=0, a_d=0, a_d0=0, a_p=0, a_p0=0, a_comm=0, a_comm0=0, alpha=1, beta=1, n_layers=1)
+    with pytest.raises(X.XpError) as e:
+        X.xp_waterfill(tau=1.0, n_decode_tokens=[1, 2], decode_ctx_sum=[0, 0], candidate=(10, 0), quantum=0, model=m)
+    assert e.value.status == -1
+    with pytest.raises(X.XpError):
+        X.xp_waterfill(tau=1.0, n_decode_tokens=[-1, 2], decode_ctx_sum=[0, 0], candidate=(10, 0), model=m)
+
+
+def _host_desc(inst, **over):
+    wl = inst.wl
+    fields = dict(x=1, n_prefill_local=wl.n_prefill_local, n_decode=wl.n_decode, dec_ctx=1, dec_pages=1,
+                  dec_max_blocks=inst.dec_max_blocks, chunk_len=wl.chunk_len, prior_len=wl.prior_len,
+                  sp_degree=wl.sp_degree, sp_rank=wl.sp_rank, local_row_offset=wl.local_row_offset,
+                  pre_pages=1, pre_max_blocks=inst.pre_max_blocks, peer_qkv_in=1, peer_qkv_out=1,
+                  peer_attn_in=1, peer_attn_out=1)
+    fields.update(over)
+    return X.BatchDesc(**fields)
+
+
+def _shape(wl, **over):
+    f = dict(hidden=wl.hidden, n_q_heads=wl.n_q_heads, n_kv_heads=wl.n_kv_heads, head_dim=wl.head_dim,
+             ffn_dim=wl.ffn_dim, page_size=wl.page_size, rms_eps=wl.rms_eps, rope_base=wl.rope_base,
+             dtype=X.XP_BF16 if wl.dtype == "bf16" else X.XP_F32)
+    f.update(over)
+    return X.LayerShape(**f)
+
+
+def test_host_validation_accepts_generated_batches_and_rejects_broken_ones():
+    inst = make_instance(get_workload("P1"))
+    wl = inst.wl
+    sh, d = _shape(wl), _host_desc(inst)
+    ok = X.xp_validate_batch(sh, d, inst.pool.n_pages, inst.dec_ctx, inst.dec_pages, inst.pre_pages)
+    assert ok == 0, X.xp_last_error()
+    bad = inst.dec_pages.copy(); bad[1, 0, 0] = inst.pool.n_pages            # out of range
+    assert X.xp_validate_batch(sh, d, inst.pool.n_pages, inst.dec_ctx, bad, inst.pre_pages) == -3
+    dup = inst.pre_pages.copy(); dup[0, 1] = dup[0, 0]                        # a page named twice
+    assert X.xp_validate_batch(sh, d, inst.pool.n_pages, inst.dec_ctx, inst.dec_pages, dup) == -3
+    long_ctx = inst.dec_ctx.copy(); long_ctx[0] = inst.dec_max_blocks * 16    # table too short
+    assert X.xp_validate_batch(sh, d, inst.pool.n_pages, long_ctx, inst.dec_pages, inst.pre_pages) == -3
+    assert X.xp_validate_batch(_shape(wl, n_kv_heads=3), d, inst.pool.n_pages, inst.dec_ctx,
+                               inst.dec_pages, inst.pre_pages) == -2          # Hq % Hkv != 0
+    assert X.xp_validate_batch(sh, _host_desc(inst, sp_degree=3, sp_rank=0), inst.pool.n_pages,
+                               inst.dec_ctx, inst.dec_pages, inst.pre_pages) == -2   # heads % P != 0
+    assert X.xp_validate_batch(sh, _host_desc(inst, local_row_offset=150), inst.pool.n_pages,
+                               inst.dec_ctx, inst.dec_pages, inst.pre_pages) == -2   # rows outside chunk
+    assert X.xp_validate_batch(sh, _host_desc(inst, pre_max_blocks=3), inst.pool.n_pages,
+                               inst.dec_ctx, inst.dec_pages, inst.pre_pages) == -3   # prefill table short
+    assert X.xp_validate_batch(_shape(wl, head_dim=96), d, inst.pool.n_pages, inst.dec_ctx,
+                               inst.dec_pages, inst.pre_pages) == -5
+    assert X.xp_validate_batch(_shape(wl, page_size=32), d, inst.pool.n_pages, inst.dec_ctx,
+                               inst.dec_pages, inst.pre_pages) == -5
+
+
+def test_workspace_layout_is_host_only_and_consistent():
+    for name in ("P1", "C2", "C5"):
+        wl = get_workload(name)
+        inst = make_instance(wl) if name == "P1" else None
+        dmb = inst.dec_max_blocks if inst is not None else 4097
+        d = X.BatchDesc(x=1, n_prefill_local=wl.n_prefill_local, n_decode=wl.n_decode, dec_ctx=1, dec_pages=1,
+                        dec_max_blocks=dmb, chunk_len=wl.chunk_len, prior_len=wl.prior_len,
+                        sp_degree=wl.sp_degree, sp_rank=wl.sp_rank, local_row_offset=wl.local_row_offset,
+                        pre_pages=1, pre_max_blocks=-(-(wl.prior_len + wl.chunk_len) // 16), peer_qkv_in=1,
+                        peer_qkv_out=1, peer_attn_in=1, peer_attn_out=1)
+        L = X.xp_layer_workspace_layout(None, _shape(wl), d).as_dict()
+        offs = sorted((v, k) for k, v in L.items() if k not in ("total", "dec_splits", "dec_pages_per_split"))
+        assert all(o % 256 == 0 for o, _ in offs)
+        assert offs[-1][0] < L["total"]
+        assert L["dec_splits"] == -(-dmb // 32)
+
+
+def test_gemm_rejects_unsupported_k_before_launching():
+    with pytest.raises(X.XpError) as e:
+        X.xp_gemm(X.XP_BF16, X.XP_EPI_F32, 16, 16, None, None, 16, 4, 4, 100, stream=0)
+    assert e.value.status == -5
+    with pytest.raises(X.XpError):
+        X.xp_gemm(X.XP_BF16, 9, 16, 16, None, None, 16, 4, 4, 64, stream=0)

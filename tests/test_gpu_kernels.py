@@ -1,0 +1,248 @@
+"""Kernel-level parity of the HIP path against the fp64 oracle, through the C ABI.
+
+Tolerances: integer addressing (KV append / gather) bit-exact; attention rel-Frobenius
+<= 5e-3 (bf16) / 1e-4 (fp32); GEMM outputs in fp32 rel-Frobenius <= 1e-5, in bf16 <= 5e-3.
+"""
+import numpy as np
+import pytest
+import torch
+
+import mixed_prefill_decode_amd as X
+from oracle import layer as L
+from oracle.numerics import to_f64
+from synth import f32_to_bf16_bits, get_workload, make_instance
+from synth.device import to_device, to_host_bits, upload_pool
+from tests.helpers import rel_fro
+
+pytestmark = pytest.mark.gpu
+
+DT = {"bf16": X.XP_BF16, "f32": X.XP_F32}
+ATTN_TOL = {"bf16": 5e-3, "f32": 1e-4}
+
+
+def _stored(a32: np.ndarray, dtype: str) -> np.ndarray:
+    return f32_to_bf16_bits(a32) if dtype == "bf16" else a32.astype(np.float32)
+
+
+def _rand(rng, shape, dtype, scale=1.0):
+    return _stored((rng.standard_normal(shape) * scale).astype(np.float32), dtype)
+
+
+def _sync():
+    torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("M,N,K", [(1, 64, 128), (67, 200, 256), (130, 257, 192), (300, 512, 1024)])
+def test_gemm_epilogues(dtype, M, N, K):
+    rng = np.random.default_rng(M * 7919 + N)
+    A, B, B2 = _rand(rng, (M, K), dtype), _rand(rng, (N, K), dtype, 0.05), _rand(rng, (N, K), dtype, 0.05)
+    Rt, Rf = _rand(rng, (M, N), dtype), rng.standard_normal((M, N)).astype(np.float32)
+    a64, b64, b264 = (to_f64(v, dtype) for v in (A, B, B2))
+    acc = a64 @ b64.T
+    dA, dB, dB2 = (to_device(v, dtype) for v in (A, B, B2))
+    dRt, dRf = to_device(Rt, dtype), torch.from_numpy(Rf).cuda()
+    C32 = torch.empty((M, N), dtype=torch.float32, device="cuda")
+    for epi, R, ref in ((X.XP_EPI_F32, None, acc), (X.XP_EPI_ADD_T, dRt, to_f64(Rt, dtype) + acc),
+                        (X.XP_EPI_ADD_F32, dRf, Rf.astype(np.float64) + acc)):
+        X.xp_gemm(DT[dtype], epi, dA, dB, None, R, C32, M, N, K)
+        _sync()
+        assert rel_fro(C32.cpu().numpy(), ref) < 1e-5, epi
+    Cs = torch.empty((M, N), dtype=torch.bfloat16 if dtype == "bf16" else torch.float32, device="cuda")
+    X.xp_gemm(DT[dtype], X.XP_EPI_SWIGLU, dA, dB, dB2, None, Cs, M, N, K)
+    _sync()
+    g, u = acc, a64 @ b264.T
+    ref = g / (1 + np.exp(-g)) * u
+    assert rel_fro(to_f64(to_host_bits(Cs), dtype), ref) < (5e-3 if dtype == "bf16" else 1e-5)
+
+
+def test_gemm_rows_do_not_depend_on_the_batch():
+    # the same rows inside batches of 40 (64-row tiles) and 300 (128-row tiles): bit-identical
+    rng = np.random.default_rng(3)
+    K, N = 512, 384
+    A = _rand(rng, (300, K), "bf16")
+    B = _rand(rng, (N, K), "bf16", 0.05)
+    dA, dB = to_device(A, "bf16"), to_device(B, "bf16")
+    full = torch.empty((300, N), dtype=torch.float32, device="cuda")
+    X.xp_gemm(X.XP_BF16, X.XP_EPI_F32, dA, dB, None, None, full, 300, N, K)
+    part = torch.empty((40, N), dtype=torch.float32, device="cuda")
+    X.xp_gemm(X.XP_BF16, X.XP_EPI_F32, dA[100:140].contiguous(), dB, None, None, part, 40, N, K)
+    _sync()
+    assert torch.equal(full[100:140], part)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_rmsnorm(dtype):
+    rng = np.random.default_rng(4)
+    M, H = 37, 640
+    x = _rand(rng, (M, H), dtype, 3.0)
+    g = _rand(rng, (H,), dtype)
+    y = torch.empty((M, H), dtype=torch.bfloat16 if dtype == "bf16" else torch.float32, device="cuda")
+    X.xp_rmsnorm(DT[dtype], to_device(x, dtype), 0, to_device(g, dtype), y, M, H, 1e-5)
+    xf = rng.standard_normal((M, H)).astype(np.float32) * 2
+    y2 = torch.empty_like(y)
+    X.xp_rmsnorm(DT[dtype], torch.from_numpy(xf).cuda(), 1, to_device(g, dtype), y2, M, H, 1e-5)
+    _sync()
+    tol = 3e-3 if dtype == "bf16" else 1e-6
+    ref = L.rmsnorm(to_f64(x, dtype), to_f64(g, dtype), 1e-5)
+    assert rel_fro(to_f64(to_host_bits(y), dtype), ref) < tol
+    ref2 = L.rmsnorm(xf.astype(np.float64), to_f64(g, dtype), 1e-5)
+    assert rel_fro(to_f64(to_host_bits(y2), dtype), ref2) < tol
+
+
+def _append_decode_tokens(inst, dpool, rng, kv):
+    """Append random K/V of every decode request's new position on both sides."""
+    wl, dt = inst.wl, inst.wl.dtype
+    n = wl.n_decode * wl.n_kv_heads
+    k = _rand(rng, (n, wl.head_dim), dt)
+    v = _rand(rng, (n, wl.head_dim), dt)
+    seq = np.arange(n, dtype=np.int32)
+    pos = np.repeat(inst.dec_ctx, wl.n_kv_heads).astype(np.int32)
+    table = inst.dec_pages.reshape(n, -1)
+    X.xp_kv_append(DT[dt], dpool, inst.pool.n_pages, wl.page_size, wl.head_dim, to_device(table, "i32"),
+                   table.shape[1], to_device(seq, "i32"), to_device(pos, "i32"), to_device(k, dt),
+                   to_device(v, dt), n)
+    k64, v64 = to_f64(k, dt), to_f64(v, dt)
+    for t in range(n):
+        kv.write(table[t], int(pos[t]), k64[t], v64[t])
+
+
+def _append_chunk_tokens(inst, dpool, rng, kv):
+    wl, dt = inst.wl, inst.wl.dtype
+    n = wl.chunk_len * wl.hkv_loc
+    k = _rand(rng, (n, wl.head_dim), dt)
+    v = _rand(rng, (n, wl.head_dim), dt)
+    seq = np.repeat(np.arange(wl.hkv_loc, dtype=np.int32), wl.chunk_len)
+    pos = np.tile(wl.prior_len + np.arange(wl.chunk_len, dtype=np.int32), wl.hkv_loc)
+    X.xp_kv_append(DT[dt], dpool, inst.pool.n_pages, wl.page_size, wl.head_dim, to_device(inst.pre_pages, "i32"),
+                   inst.pre_pages.shape[1], to_device(seq, "i32"), to_device(pos, "i32"), to_device(k, dt),
+                   to_device(v, dt), n)
+    k64, v64 = to_f64(k, dt), to_f64(v, dt)
+    for t in range(n):
+        kv.write(inst.pre_pages[seq[t]], int(pos[t]), k64[t], v64[t])
+
+
+@pytest.mark.parametrize("name", ["P1", "P2", "E1", "C1", "E3"])
+def test_kv_append_and_gather_bit_exact(name):
+    inst = make_instance(get_workload(name))
+    wl, dt = inst.wl, inst.wl.dtype
+    rng = np.random.default_rng(5)
+    dpool = upload_pool(inst)
+    kv = L.PagedKV(inst.pool, dt, wl.page_size, wl.head_dim)
+    _append_decode_tokens(inst, dpool, rng, kv)
+    _sync()
+    host = to_host_bits(dpool)
+    for p in range(inst.pool.n_pages):
+        assert np.array_equal(host[p], kv.stored_page(p), equal_nan=True) if dt == "f32" else \
+            np.array_equal(host[p], kv.stored_page(p)), p
+    n = wl.n_decode * wl.n_kv_heads
+    lens = np.repeat(inst.dec_ctx + 1, wl.n_kv_heads).astype(np.int32)
+    max_len = int(lens.max())
+    tdt = torch.bfloat16 if dt == "bf16" else torch.float32
+    ko = torch.zeros((n, max_len, wl.head_dim), dtype=tdt, device="cuda")
+    vo = torch.zeros_like(ko)
+    table = inst.dec_pages.reshape(n, -1)
+    X.xp_kv_gather(DT[dt], dpool, inst.pool.n_pages, wl.page_size, wl.head_dim, to_device(table, "i32"),
+                   table.shape[1], to_device(lens, "i32"), n, max_len, ko, vo)
+    _sync()
+    kh, vh = to_host_bits(ko), to_host_bits(vo)
+    for t in range(n):
+        K, V = kv.read(table[t], int(lens[t]))
+        from oracle.numerics import encode
+        assert np.array_equal(kh[t, :lens[t]], encode(K, dt)) and np.array_equal(vh[t, :lens[t]], encode(V, dt))
+
+
+@pytest.mark.parametrize("name", ["P1", "P2", "P3", "E1", "C1", "E3"])
+@pytest.mark.parametrize("pps", [1, 5, 32])
+def test_decode_attention(name, pps):
+    inst = make_instance(get_workload(name))
+    wl, dt = inst.wl, inst.wl.dtype
+    rng = np.random.default_rng(6)
+    dpool = upload_pool(inst)
+    kv = L.PagedKV(inst.pool, dt, wl.page_size, wl.head_dim)
+    _append_decode_tokens(inst, dpool, rng, kv)
+    q = _rand(rng, (wl.n_decode, wl.n_q_heads, wl.head_dim), dt)
+    tdt = torch.bfloat16 if dt == "bf16" else torch.float32
+    out = torch.full((wl.n_decode, wl.n_q_heads * wl.head_dim), float("nan"), dtype=tdt, device="cuda")
+    ws = torch.empty(X.xp_decode_workspace_size(wl.n_decode, wl.n_q_heads, wl.head_dim, inst.dec_max_blocks, pps),
+                     dtype=torch.uint8, device="cuda")
+    X.xp_decode_attention(DT[dt], to_device(q, dt), dpool, inst.pool.n_pages, wl.page_size,
+                          to_device(inst.dec_pages, "i32"), inst.dec_max_blocks, to_device(inst.dec_ctx, "i32"),
+                          wl.n_decode, wl.n_q_heads, wl.n_kv_heads, wl.head_dim, out, wl.n_q_heads * wl.head_dim,
+                          ws, pps)
+    _sync()
+    ref = L.decode_attention(to_f64(q, dt), kv, inst.dec_pages, inst.dec_ctx, wl.n_kv_heads)
+    got = to_f64(to_host_bits(out), dt).reshape(ref.shape)
+    assert np.isfinite(got).all()
+    assert rel_fro(got, ref) < ATTN_TOL[dt]
+    for i in range(wl.n_decode):      # per request as well (short contexts are not drowned out)
+        assert rel_fro(got[i], ref[i]) < 2 * ATTN_TOL[dt], i
+
+
+@pytest.mark.parametrize("name", ["P1", "P2", "P3", "E2", "C1", "E4"])
+def test_prefill_attention(name):
+    inst = make_instance(get_workload(name))
+    wl, dt = inst.wl, inst.wl.dtype
+    rng = np.random.default_rng(7)
+    dpool = upload_pool(inst)
+    kv = L.PagedKV(inst.pool, dt, wl.page_size, wl.head_dim)
+    _append_chunk_tokens(inst, dpool, rng, kv)
+    l, hq, d = wl.chunk_len, wl.hq_loc, wl.head_dim
+    q = _rand(rng, (hq, l, d), dt)
+    tdt = torch.bfloat16 if dt == "bf16" else torch.float32
+    n_loc, off = wl.n_prefill_local, wl.local_row_offset
+    out_l = torch.full((max(n_loc, 1), hq * d), float("nan"), dtype=tdt, device="cuda")
+    out_p = torch.full((max(l - n_loc, 1), hq * d), float("nan"), dtype=tdt, device="cuda")
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    X.xp_prefill_attention(DT[dt], to_device(q, dt), dpool, inst.pool.n_pages, wl.page_size,
+                           to_device(inst.pre_pages, "i32"), inst.pre_max_blocks, hq, wl.hkv_loc, d, wl.prior_len,
+                           l, off, n_loc, out_l, hq * d, out_p, hq * d, status)
+    _sync()
+    ref = L.prefill_attention(to_f64(q, dt).transpose(1, 0, 2), kv, inst.pre_pages, wl.prior_len, wl.group)
+    ref = ref.reshape(l, hq * d)
+    loc = [t for t in range(l) if off <= t < off + n_loc]
+    peer = [t for t in range(l) if not (off <= t < off + n_loc)]
+    got_l = to_f64(to_host_bits(out_l), dt)[:n_loc]
+    got_p = to_f64(to_host_bits(out_p), dt)[:len(peer)]
+    assert int(status.item()) == 0
+    if loc:
+        assert np.isfinite(got_l).all() and rel_fro(got_l, ref[loc]) < ATTN_TOL[dt]
+    if peer:
+        assert np.isfinite(got_p).all() and rel_fro(got_p, ref[peer]) < ATTN_TOL[dt]
+    # every row, including the first chunk rows that see only a few keys
+    full = np.zeros_like(ref)
+    full[loc], full[peer] = got_l, got_p
+    for t in (0, 1, l // 2, l - 1):
+        assert rel_fro(full[t], ref[t]) < 2 * ATTN_TOL[dt], t
+
+
+def test_decode_token_matches_prefill_row_on_gpu():
+    # decode attention of a query at position c+t over the chunk's own table equals prefill row t
+    inst = make_instance(get_workload("E2"))
+    wl, dt = inst.wl, inst.wl.dtype
+    rng = np.random.default_rng(8)
+    dpool = upload_pool(inst)
+    kv = L.PagedKV(inst.pool, dt, wl.page_size, wl.head_dim)
+    _append_chunk_tokens(inst, dpool, rng, kv)
+    l, hq, d, G = wl.chunk_len, wl.hq_loc, wl.head_dim, wl.group
+    q = _rand(rng, (hq, l, d), dt)
+    out_l = torch.empty((l, hq * d), dtype=torch.bfloat16, device="cuda")
+    X.xp_prefill_attention(DT[dt], to_device(q, dt), dpool, inst.pool.n_pages, wl.page_size,
+                           to_device(inst.pre_pages, "i32"), inst.pre_max_blocks, hq, wl.hkv_loc, d, wl.prior_len,
+                           l, 0, l, out_l, hq * d, None, hq * d)
+    # the same queries as decode requests: request t has context prior + t on kv head g's table
+    rows = [0, 5, l - 1]
+    for g in range(wl.hkv_loc):
+        qd = np.ascontiguousarray(q[g * G:(g + 1) * G].transpose(1, 0, 2)[rows])       # [n, G, d]
+        tables = np.repeat(inst.pre_pages[g:g + 1][None], len(rows), axis=0)           # [n, 1, blocks]
+        ctx = (wl.prior_len + np.array(rows)).astype(np.int32)
+        out_d = torch.empty((len(rows), G * d), dtype=torch.bfloat16, device="cuda")
+        ws = torch.empty(X.xp_decode_workspace_size(len(rows), G, d, tables.shape[2], 4), dtype=torch.uint8,
+                         device="cuda")
+        X.xp_decode_attention(DT[dt], to_device(qd, dt), dpool, inst.pool.n_pages, wl.page_size,
+                              to_device(tables, "i32"), tables.shape[2], to_device(ctx, "i32"), len(rows), G, 1, d,
+                              out_d, G * d, ws, 4)
+        _sync()
+        a = to_f64(to_host_bits(out_d), dt)
+        b = to_f64(to_host_bits(out_l), dt)[rows][:, g * G * d:(g + 1) * G * d]
+        assert rel_fro(a, b) < 5e-3
