@@ -1,0 +1,324 @@
+#!/usr/bin/env python3
+"""Benchmark of one GPU's share of a Conflux Parallelism layer step on MI355X.
+
+A timed step is one pass of the whole hot path over one batch: the waterfill
+dispatch of the iteration's chunk (host) and one xp_layer_forward (co-batched
+RMSNorm + QKV GEMM, RoPE + paged K/V append, decode attention || prefill
+attention on a CU partition, O-proj, RMSNorm, gate/up + SwiGLU, down), inputs
+resident in HBM.  Prints one JSON line (metric, value, roofline of the dominant
+kernel, the fp64 oracle timed on the host as a baseline) on stdout; details go
+to stderr.
+
+    python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--workload C2]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+METRIC = "mixed-layer tokens/s; decode-attn HBM GB/s and GEMM MFMA util as % of peak"
+PEAK_BF16_TFLOPS = 2500.0
+PEAK_HBM_GBS = 8000.0
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--workload", default="C2")
+    p.add_argument("--decode-cus", type=int, default=None,
+                   help="CUs for decode attention (default: calibrated, 0 = serialized, -1 = unmasked)")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-budget-s", type=float, default=25.0)
+    p.add_argument("--kernel-only", choices=["none", "swiglu", "decode", "prefill", "copy"], default="none",
+                   help="only launch one kernel repeatedly (for counter runs)")
+    p.add_argument("--repeats", type=int, default=20, help="launches per kernel timing")
+    return p.parse_args()
+
+
+class Timer:
+    """HIP-event timing on torch's current stream."""
+
+    def __init__(self, torch):
+        self.torch = torch
+
+    def __call__(self, fn, n):
+        t = self.torch
+        a, b = t.cuda.Event(enable_timing=True), t.cuda.Event(enable_timing=True)
+        fn()
+        t.cuda.synchronize()
+        a.record()
+        for _ in range(n):
+            fn()
+        b.record()
+        b.synchronize()
+        return a.elapsed_time(b) / n * 1e-3  # seconds per launch
+
+
+def decode_bytes(inst) -> int:
+    """Algorithmic bytes of decode attention: every K/V element of the visible context once
+    (for all G heads of a group), q in, o out, the table entries read."""
+    wl = inst.wl
+    eb = 2 if wl.dtype == "bf16" else 4
+    keys = int(np.sum(inst.dec_ctx.astype(np.int64) + 1))
+    kv = keys * 2 * wl.n_kv_heads * wl.head_dim * eb
+    qo = 2 * wl.n_decode * wl.n_q_heads * wl.head_dim * eb
+    tbl = int(np.sum(-(-(inst.dec_ctx.astype(np.int64) + 1) // wl.page_size))) * wl.n_kv_heads * 4
+    return kv + qo + tbl
+
+
+def prefill_flops(wl) -> int:
+    pairs = wl.chunk_len * wl.prior_len + wl.chunk_len * (wl.chunk_len + 1) // 2
+    return 4 * wl.head_dim * wl.hq_loc * pairs
+
+
+def gemm_list(wl):
+    M, H, F, d = wl.n_rows, wl.hidden, wl.ffn_dim, wl.head_dim
+    return {"qkv": (M, (wl.n_q_heads + 2 * wl.n_kv_heads) * d, H), "o": (M, H, wl.n_q_heads * d),
+            "gate_up": (M, 2 * F, H), "down": (M, H, F)}
+
+
+def cpu_baseline(inst, budget_s: float) -> dict:
+    """The fp64 oracle (as it stands) on the host: full layer steps until the budget is used."""
+    from oracle import layer as L
+    from tests.helpers import oracle_kwargs
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [os.cpu_count()])
+    except Exception:
+        cores = os.cpu_count()
+    t0 = time.perf_counter()
+    n = 0
+    while True:
+        L.layer_forward(**oracle_kwargs(inst))
+        n += 1
+        if time.perf_counter() - t0 > budget_s / 2 or n >= 3:
+            break
+    dt = (time.perf_counter() - t0) / n
+    return {"value": round(inst.wl.n_rows / dt, 2), "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"{n} full {inst.wl.name} layer step(s) of {inst.wl.n_rows} rows in fp64 on the host "
+                      f"({dt:.2f} s each)"}
+
+
+def calibrate_decode_cus(X, torch, step, inst, dev, timer, n_cus, repeats) -> tuple[int, dict]:
+    """Fewest CUs whose standalone decode-attention bandwidth is >= 90% of the all-CU figure
+    (the decode CU-allocation rule of the pages).  Candidates are multiples of 32: the mask
+    spreads CUs evenly over the 8 XCDs, and bandwidth only grows when every shader engine
+    (4 per XCD) gains a CU."""
+    wl = inst.wl
+    lay = step.layout
+    q = int(step.workspace.data_ptr()) + lay.q_dec
+    dws = torch.empty(X.xp_decode_workspace_size(wl.n_decode, wl.n_q_heads, wl.head_dim, inst.dec_max_blocks,
+                                                 lay.dec_pages_per_split), dtype=torch.uint8, device="cuda")
+    out = torch.empty((wl.n_decode, wl.n_q_heads * wl.head_dim), dtype=torch.bfloat16, device="cuda")
+    nbytes = decode_bytes(inst)
+
+    def run_on(stream):
+        return lambda: X.xp_decode_attention(X.XP_BF16, q, dev.pool, inst.pool.n_pages, wl.page_size,
+                                             dev.dec_pages, inst.dec_max_blocks, dev.dec_ctx, wl.n_decode,
+                                             wl.n_q_heads, wl.n_kv_heads, wl.head_dim, out,
+                                             wl.n_q_heads * wl.head_dim, dws, lay.dec_pages_per_split, stream)
+
+    full = nbytes / timer(run_on(None), repeats)
+    curve = {}
+    chosen = n_cus - 32
+    for k in range(32, n_cus, 32):
+        ctx = X.Ctx(0, k, lay.dec_pages_per_split)
+        s_dec, _ = ctx.streams()
+        ts = torch.cuda.ExternalStream(s_dec)
+        with torch.cuda.stream(ts):
+            bw = nbytes / timer(run_on(s_dec), repeats)
+        curve[k] = round(bw / 1e9, 1)
+        ctx.close()
+        if bw >= 0.9 * full:
+            chosen = k
+            break
+    return chosen, {"full_GBs": round(full / 1e9, 1), "curve_GBs": curve}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "bench.py measures one GPU's share of the layer; this build has no "
+                                   "multi-GPU path (run with --gpus 1)", "n_gpus": args.gpus}))
+        sys.exit(2)
+    import torch
+
+    import mixed_prefill_decode_amd as X
+    from synth import get_workload, make_instance
+    from synth.device import make_step, upload
+
+    torch.cuda.init()
+    props = torch.cuda.get_device_properties(0)
+    n_cus = props.multi_processor_count
+    wl = get_workload(args.workload)
+    t0 = time.time()
+    inst = make_instance(wl)
+    dev = upload(inst)
+    log(f"[bench] {wl.name}: {wl.description}; rows {wl.n_rows}; pool {inst.pool.nbytes / 2**30:.2f} GiB; "
+        f"inputs ready in {time.time() - t0:.1f} s on {props.name} ({n_cus} CUs)")
+    timer = Timer(torch)
+
+    # the iteration's dispatch: the chunk the waterfill gives this rank at the batch's level
+    model = dict(gamma=2.0 ** -17, gamma0=2.0 ** -12, a_d=2.0 ** -27, a_d0=2.0 ** -13, a_p=2.0 ** -31,
+                 a_p0=2.0 ** -13, a_comm=2.0 ** -20, a_comm0=2.0 ** -14, alpha=1.125, beta=1.25, n_layers=32)
+    ctx_sum = int(np.sum(inst.dec_ctx.astype(np.int64)))
+    wf_args = dict(tau=0.05, n_decode_tokens=[wl.n_decode], decode_ctx_sum=[ctx_sum],
+                   candidate=(wl.n_prefill_local, wl.prior_len), model=model, fixed_target=wl.n_rows)
+
+    ctx0 = X.Ctx(0, 0, 0)
+    step0, _ = make_step(inst, ctx0, dev)
+
+    if args.kernel_only != "none":
+        return kernel_only(args, X, torch, inst, step0, dev, timer)
+
+    step0.run()
+    torch.cuda.synchronize()
+    # decode CU partition
+    if args.decode_cus is None:
+        if wl.n_decode and wl.chunk_len:
+            k, calib = calibrate_decode_cus(X, torch, step0, inst, dev, timer, n_cus, args.repeats)
+        else:
+            k, calib = 0, {}
+    else:
+        k, calib = args.decode_cus, {}
+    ctx = X.Ctx(0, k, 0) if k != 0 else ctx0
+    step, _ = make_step(inst, ctx, dev)
+
+    def one_step():
+        r = X.xp_waterfill(**wf_args)
+        assert r["chunk_len"] == wl.n_prefill_local
+        step.run()
+
+    for _ in range(args.warmup):
+        one_step()
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    ev0.record()
+    for _ in range(args.steps):
+        one_step()
+    ev1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = ev0.elapsed_time(ev1) / args.steps
+    tokens_per_s = wl.n_rows * args.steps / wall
+    assert step.status() == 0
+
+    # per-kernel measurements (standalone, all CUs, caller stream)
+    lay = step0.layout
+    ws = int(step0.workspace.data_ptr())
+    w = dev.weights
+    M, H, F = wl.n_rows, wl.hidden, wl.ffn_dim
+    kern = {}
+    gl = gemm_list(wl)
+    gemm_calls = {
+        "qkv": lambda: X.xp_gemm(X.XP_BF16, X.XP_EPI_F32, ws + lay.hn, w["w_qkv"], None, None, ws + lay.qkv,
+                                 M, gl["qkv"][1], H),
+        "o": lambda: X.xp_gemm(X.XP_BF16, X.XP_EPI_ADD_T, ws + lay.attn, w["w_o"], None, dev.x, ws + lay.h1,
+                               M, H, gl["o"][2]),
+        "gate_up": lambda: X.xp_gemm(X.XP_BF16, X.XP_EPI_SWIGLU, ws + lay.hn, w["w_gate"], w["w_up"], None,
+                                     ws + lay.act, M, F, H),
+        "down": lambda: X.xp_gemm(X.XP_BF16, X.XP_EPI_ADD_F32, ws + lay.act, w["w_down"], None, ws + lay.h1,
+                                  step0.out, M, H, F),
+    }
+    for name, fn in gemm_calls.items():
+        m_, n_, k_ = gl[name]
+        t = timer(fn, args.repeats)
+        fl = 2.0 * m_ * n_ * k_
+        wbytes = n_ * k_ * 2
+        kern[name] = {"us": round(t * 1e6, 2), "TFLOPs": round(fl / t / 1e12, 1),
+                      "mfma_frac": round(fl / t / 1e12 / PEAK_BF16_TFLOPS, 4),
+                      "weight_GBs": round(wbytes / t / 1e9, 1)}
+    dws = torch.empty(X.xp_decode_workspace_size(wl.n_decode, wl.n_q_heads, wl.head_dim, max(inst.dec_max_blocks, 1),
+                                                 lay.dec_pages_per_split) or 256, dtype=torch.uint8, device="cuda")
+    if wl.n_decode:
+        dout = torch.empty((wl.n_decode, wl.n_q_heads * wl.head_dim), dtype=torch.bfloat16, device="cuda")
+        t = timer(lambda: X.xp_decode_attention(X.XP_BF16, ws + lay.q_dec, dev.pool, inst.pool.n_pages, 16,
+                                                dev.dec_pages, inst.dec_max_blocks, dev.dec_ctx, wl.n_decode,
+                                                wl.n_q_heads, wl.n_kv_heads, wl.head_dim, dout,
+                                                wl.n_q_heads * wl.head_dim, dws, lay.dec_pages_per_split), args.repeats)
+        nb = decode_bytes(inst)
+        kern["decode_attn"] = {"us": round(t * 1e6, 2), "GBs": round(nb / t / 1e9, 1),
+                               "hbm_frac": round(nb / t / 1e9 / PEAK_HBM_GBS, 4), "bytes": nb}
+    if wl.chunk_len:
+        hq, d = wl.hq_loc, wl.head_dim
+        pout = torch.empty((wl.chunk_len, hq * d), dtype=torch.bfloat16, device="cuda")
+        t = timer(lambda: X.xp_prefill_attention(X.XP_BF16, ws + lay.q_pre, dev.pool, inst.pool.n_pages, 16,
+                                                 dev.pre_pages, inst.pre_max_blocks, hq, wl.hkv_loc, d,
+                                                 wl.prior_len, wl.chunk_len, 0, wl.chunk_len, pout, hq * d,
+                                                 None, hq * d), args.repeats)
+        fl = prefill_flops(wl)
+        kern["prefill_attn"] = {"us": round(t * 1e6, 2), "TFLOPs": round(fl / t / 1e12, 1),
+                                "mfma_frac": round(fl / t / 1e12 / PEAK_BF16_TFLOPS, 4), "flops": fl}
+    # split attention segment: serialized vs the CU partition
+    seg = {}
+    if wl.n_decode and wl.chunk_len:
+        for mode, c in (("serialized", ctx0), ("overlapped", ctx)):
+            st, _ = make_step(inst, c, dev)
+            seg[mode + "_layer_us"] = round(timer(st.run, args.repeats) * 1e6, 1)
+        seg["decode_cus"] = k
+        seg["calibration"] = calib
+
+    dom = "gate_up"
+    m_, n_, k_ = gl[dom]
+    fl = 2.0 * m_ * n_ * k_
+    t_dom = kern[dom]["us"] * 1e-6
+    roofline = {"bound": "mfma", "achieved": round(fl / t_dom / 1e12, 2), "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(fl / t_dom / 1e12 / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                "kernel": "gemm_kernel<bf16,SwiGLU> (gate/up projection)", "flops_per_launch": fl}
+    log(f"[bench] layer {ms * 1e3:.1f} us/step, {tokens_per_s:.0f} tokens/s; kernels {json.dumps(kern)}")
+    log(f"[bench] split attention {json.dumps(seg)}")
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(inst, args.cpu_budget_s)
+        log(f"[bench] cpu baseline {cpu}")
+    line = {
+        "metric": METRIC, "value": round(tokens_per_s, 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": wl.dtype, "data": "synthetic (seeded, random-init weights)",
+        "config": {"workload": f"{wl.name}: {wl.description}", "rows": wl.n_rows, "hidden": wl.hidden,
+                   "q_heads": wl.n_q_heads, "kv_heads": wl.n_kv_heads, "head_dim": wl.head_dim,
+                   "ffn": wl.ffn_dim, "decodes": wl.n_decode, "decode_ctx": wl.ctx[1] if wl.ctx[0] == "fixed" else list(wl.ctx),
+                   "chunk": wl.chunk_len, "prior": wl.prior_len, "sp_degree": wl.sp_degree,
+                   "decode_cus": k, "page_size": wl.page_size},
+        "roofline": roofline, "cpu_baseline": cpu, "kernels": kern, "split_attention": seg,
+    }
+    print(json.dumps(line), flush=True)
+
+
+def kernel_only(args, X, torch, inst, step, dev, timer):
+    """Launch only one kernel repeatedly (input of counter-collection runs)."""
+    wl = inst.wl
+    step.run()
+    torch.cuda.synchronize()
+    lay, ws, w = step.layout, int(step.workspace.data_ptr()), dev.weights
+    if args.kernel_only == "swiglu":
+        fn = lambda: X.xp_gemm(X.XP_BF16, X.XP_EPI_SWIGLU, ws + lay.hn, w["w_gate"], w["w_up"], None, ws + lay.act,
+                               wl.n_rows, wl.ffn_dim, wl.hidden)
+    elif args.kernel_only == "copy":
+        src = torch.empty(1 << 28, dtype=torch.float32, device="cuda").fill_(1.0)   # 1 GiB
+        dst = torch.empty_like(src)
+        fn = lambda: dst.copy_(src)
+        log("[bench] copy kernel: 1 GiB read + 1 GiB written per launch")
+    else:
+        raise SystemExit(f"--kernel-only {args.kernel_only}: not wired")
+    t = timer(fn, args.repeats)
+    torch.cuda.synchronize()
+    log(f"[bench] {args.kernel_only}: {t * 1e6:.2f} us per launch over {args.repeats} launches")
+    print(json.dumps({"kernel_only": args.kernel_only, "us": round(t * 1e6, 3), "repeats": args.repeats}))
+
+
+if __name__ == "__main__":
+    main()

@@ -180,6 +180,11 @@ xp_status xp_ctx_destroy(xp_ctx* ctx);
 xp_status xp_ctx_cu_masks(const xp_ctx* ctx, uint32_t* decode_mask8, uint32_t* prefill_mask8,
                           int32_t* n_cus);
 
+/* The context's decode and prefill attention streams (hipStream_t as void*;
+ * NULL in serialized mode).  Owned by the context; for callers that time a
+ * kernel-level entry point on the same CU partition the layer step uses. */
+xp_status xp_ctx_streams(const xp_ctx* ctx, void** decode_stream, void** prefill_stream);
+
 xp_status xp_layer_workspace_layout(const xp_ctx* ctx, const xp_layer_shape* shape,
                                     const xp_batch_desc* desc, xp_ws_layout* layout);
 

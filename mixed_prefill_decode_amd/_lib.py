@@ -30,6 +30,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libxp.so")
 
 # every symbol include/xp.h declares
 EXPORTED = ["xp_last_error", "xp_build_info", "xp_ctx_create", "xp_ctx_destroy", "xp_ctx_cu_masks",
+            "xp_ctx_streams",
             "xp_layer_workspace_layout", "xp_layer_forward", "xp_validate_batch", "xp_layer_read_status",
             "xp_rmsnorm", "xp_gemm", "xp_kv_append", "xp_kv_gather", "xp_decode_workspace_size",
             "xp_decode_attention", "xp_prefill_attention", "xp_probe_hw_ids", "xp_waterfill",
@@ -104,6 +105,7 @@ def _declare(L):
         "xp_ctx_create": (S, [C.POINTER(_vp), _i32, _i32, _i32]),
         "xp_ctx_destroy": (S, [_vp]),
         "xp_ctx_cu_masks": (S, [_vp, _vp, _vp, _vp]),
+        "xp_ctx_streams": (S, [_vp, C.POINTER(_vp), C.POINTER(_vp)]),
         "xp_layer_workspace_layout": (S, [_vp, C.POINTER(LayerShape), C.POINTER(BatchDesc), C.POINTER(WsLayout)]),
         "xp_layer_forward": (S, [_vp, C.POINTER(LayerShape), C.POINTER(BatchDesc), C.POINTER(LayerWeights),
                                  C.POINTER(KvPages), _vp, _vp, _sz, _vp]),
@@ -190,6 +192,12 @@ class Ctx:
         n = _i32()
         _check(lib().xp_ctx_cu_masks(self.handle, dec, pre, C.byref(n)))
         return list(dec), list(pre), n.value
+
+    def streams(self):
+        """(decode stream, prefill stream) raw handles; 0 in serialized mode."""
+        d, p = _vp(), _vp()
+        _check(lib().xp_ctx_streams(self.handle, C.byref(d), C.byref(p)))
+        return d.value or 0, p.value or 0
 
     def close(self):
         if getattr(self, "handle", None):

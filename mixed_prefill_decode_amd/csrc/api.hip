@@ -233,6 +233,13 @@ xp_status xp_ctx_cu_masks(const xp_ctx* c, uint32_t* dec, uint32_t* pre, int32_t
   return XP_OK;
 }
 
+xp_status xp_ctx_streams(const xp_ctx* c, void** dec, void** pre) {
+  if (!c) return fail(XP_EINVAL, "null ctx");
+  if (dec) *dec = c->s_dec;
+  if (pre) *pre = c->s_pre;
+  return XP_OK;
+}
+
 xp_status xp_layer_workspace_layout(const xp_ctx* ctx, const xp_layer_shape* sh, const xp_batch_desc* d,
                                     xp_ws_layout* out) {
   if (!out) return fail(XP_EINVAL, "null layout out");
