@@ -1,0 +1,224 @@
+// The MFMA GEMM, as a template over block tile, wave grid and LDS ring depth.
+//
+// C = epilogue(A B^T): A [M, K] and B [N, K] (K contiguous), fp32 accumulation.
+// Block tile BM x BN, WGM x WGN waves, wave tile (BM/WGM) x (BN/WGN) made of
+// 32x32 MFMA blocks.  Each stage is a 128-byte slice of K per row (64 bf16 or 32
+// fp32), copied from HBM straight into an LDS ring (buffer_load ... lds: no staging
+// registers, no LDS store instructions) whose 16-byte chunks are XOR-swizzled by
+// (row & 7), so the eight lanes an LDS fragment read serves together hit eight
+// different bank groups.  The SwiGLU epilogue reads two weight tiles (gate, up)
+// against the same A tile and keeps both accumulators, so silu(g) * u is formed in
+// registers.
+//
+// Block order is XCD-aware: workgroups are dealt to the 8 XCDs round-robin, so
+// block b is remapped to tile (b % 8) * per_xcd + b / 8 with tiles ordered
+// M-fastest; the M tiles that share one weight tile then run on one XCD and
+// share its L2.
+//
+// The K loop order (128-byte stages, 16-deep MFMA steps, in order) is the same for
+// every M and every tile shape, so a row's result does not depend on which other
+// rows are co-batched with it.
+#pragma once
+#include "xp_device.h"
+#include "../../include/xp.h"
+
+namespace xp {
+namespace gemm {
+
+constexpr int kRowBytes = 128;
+constexpr int kChunks = 8;  // 16-byte chunks per LDS row
+
+__device__ __forceinline__ int swz(int row, int chunk) { return row * kChunks + (chunk ^ (row & 7)); }
+
+template <typename T>
+__device__ __forceinline__ void lds_frag(Frag8<T>& f, const uint4* buf, int row, int chunk);
+template <>
+__device__ __forceinline__ void lds_frag(Frag8<bf16_t>& f, const uint4* buf, int row, int chunk) {
+  f.v = buf[swz(row, chunk)];
+}
+template <>
+__device__ __forceinline__ void lds_frag(Frag8<float>& f, const uint4* buf, int row, int chunk) {
+  uint4 a = buf[swz(row, chunk)], b = buf[swz(row, chunk + 1)];
+  f.lo = __builtin_bit_cast(float4, a);
+  f.hi = __builtin_bit_cast(float4, b);
+}
+
+template <typename T, int BM, int BN, int WGM, int WGN, int EPI>
+struct Cfg {
+  static constexpr int THREADS = 64 * WGM * WGN;
+  static constexpr int EB = St<T>::bytes;
+  static constexpr int BK = kRowBytes / EB;
+  static constexpr int NB = (EPI == XP_EPI_SWIGLU) ? 2 : 1;
+  static constexpr int WM = BM / WGM, WN = BN / WGN;
+  static constexpr int FM = WM / 32, FN = WN / 32;
+  static constexpr int ROWS = BM + NB * BN;
+  static constexpr int CPK = 16 * EB / 16;       // 16-byte chunks per 16-deep k step
+  static_assert(WM % 32 == 0 && WN % 32 == 0, "wave tile must be made of 32x32 blocks");
+};
+
+// ---------------------------------------------------------------------------
+// Loads: a wave instruction fills 8 consecutive LDS rows (64 lanes x 16 B,
+// lane-contiguous); lane l fetches global chunk (l % 8) ^ (l / 8) of its row so the
+// LDS image is the XOR-swizzled layout the fragment reads expect.  Each operand's
+// buffer resource starts at the tile's first row and covers only its valid rows, so
+// rows past M or N read as zero without any per-load check.  STAGES-deep ring:
+// stage kt + STAGES - 1 is issued right after the barrier that ends the reads of the
+// buffer it overwrites.
+// ---------------------------------------------------------------------------
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
+
+// Buffer resource over `rows` rows of `row_bytes` starting at `base` (gfx9 layout: 48-bit
+// base, stride 0, num_records in bytes, default format word); reads past it return 0.
+__device__ __forceinline__ i32x4 rsrc_rows(const char* base, long rows, long row_bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  const long n = rows > 0 ? rows * row_bytes : 0;
+  i32x4 r;
+  r.x = __builtin_amdgcn_readfirstlane(int32_t(a & 0xffffffffu));
+  r.y = __builtin_amdgcn_readfirstlane(int32_t((a >> 32) & 0xffffu));
+  r.z = __builtin_amdgcn_readfirstlane(int32_t(n));
+  r.w = 0x00020000;
+  return r;
+}
+
+// 16 bytes per lane from buffer `r` at byte offset `voff` into LDS at `lds_addr` + 16 * lane.
+// Issued as inline asm so the compiler's wait-count pass does not see an LDS write it cannot
+// disambiguate (it would otherwise drain every load in flight before each LDS read); the
+// caller waits on vmcnt itself.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void load_lds16(i32x4 r, uint32_t lds_addr, int voff) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+               :
+               : "s"(lds_addr), "v"(voff), "s"(r)
+               : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+template <typename T, int BM, int BN, int WGM, int WGN, int EPI, int STAGES>
+__global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(const char* __restrict__ A, const char* __restrict__ B,
+                                                                 const char* __restrict__ B2, const void* __restrict__ R,
+                                                                 void* __restrict__ C, int M, int N, int K, int tiles_m,
+                                                                 int tiles_n) {
+  using G = Cfg<T, BM, BN, WGM, WGN, EPI>;
+  constexpr int NB = G::NB, FM = G::FM, FN = G::FN, CPK = G::CPK;
+  constexpr int ROWS = G::ROWS, BK = G::BK, WM = G::WM, WN = G::WN;
+  constexpr int W = WGM * WGN;
+  constexpr int INSTR = ROWS / 8;        // wave instructions per stage
+  static_assert(INSTR % W == 0, "stage rows must split evenly over the waves");
+  constexpr int IPW = INSTR / W;
+  __shared__ uint4 lds[STAGES][ROWS * kChunks];
+
+  const int n_tiles = tiles_m * tiles_n;
+  const int b = blockIdx.x;
+  const int q = n_tiles / 8, rem = n_tiles % 8, x = b % 8;
+  const int t = x * q + min(x, rem) + b / 8;
+  const int m0 = (t % tiles_m) * BM, n0 = (t / tiles_m) * BN;
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: scalar branches below
+  const int wm = wave / WGN, wn = wave % WGN;
+  const long kbytes = long(K) * G::EB;
+  const auto ra = rsrc_rows(A + m0 * kbytes, min(BM, M - m0), kbytes);
+  const auto rb = rsrc_rows(B + n0 * kbytes, min(BN, N - n0), kbytes);
+  const auto rb2 = rsrc_rows((NB == 2 ? B2 : B) + n0 * kbytes, min(BN, N - n0), kbytes);
+  const int lrow = lane >> 3;
+  const int lchunk = (lane & 7) ^ lrow;  // 8-row groups start at multiples of 8
+
+  auto issue = [&](int kt, int buf) {
+#pragma unroll
+    for (int i = 0; i < IPW; ++i) {
+      const int row0 = (i * W + wave) * 8;   // wave-uniform
+      const int off = kt * kRowBytes + lchunk * 16;
+      const uint32_t dst = __builtin_amdgcn_readfirstlane(
+          uint32_t(reinterpret_cast<uintptr_t>(&lds[buf][row0 * kChunks])));
+      if (row0 < BM) {
+        load_lds16(ra, dst, int((row0 + lrow) * kbytes) + off);
+      } else if (NB == 1 || row0 < BM + BN) {
+        load_lds16(rb, dst, int((row0 - BM + lrow) * kbytes) + off);
+      } else {
+        load_lds16(rb2, dst, int((row0 - BM - BN + lrow) * kbytes) + off);
+      }
+    }
+  };
+
+  f32x16 acc[NB][FM][FN];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j) acc[nb][i][j] = f32x16{};
+
+  const int lr = lane & 31, kg = lane >> 5;
+  const int nk = K / BK;
+#pragma unroll
+  for (int s = 0; s < STAGES - 1; ++s)
+    if (s < nk) issue(s, s);
+  for (int kt = 0; kt < nk; ++kt) {
+    // stage kt must have landed: the stages issued after it may stay in flight
+    const int after = min(STAGES - 2, nk - 1 - kt);
+    if constexpr (STAGES >= 3) {
+      if (after >= 1) wait_vmcnt<IPW>();
+      else wait_vmcnt<0>();
+    } else {
+      wait_vmcnt<0>();
+    }
+    // A bare barrier: every wave has waited for its own loads of stage kt above, and
+    // its reads of the buffer being refilled next were consumed by MFMAs before it
+    // arrived.  (A fence here would also drain the stages still in flight.)
+    __builtin_amdgcn_s_barrier();
+    if (kt + STAGES - 1 < nk) issue(kt + STAGES - 1, (kt + STAGES - 1) % STAGES);
+    const uint4* buf = lds[kt % STAGES];
+#pragma unroll
+    for (int ks = 0; ks < BK / 16; ++ks) {
+      const int chunk = ks * CPK + kg * (CPK / 2);
+      Frag8<T> fa[FM], fb[NB][FN];
+#pragma unroll
+      for (int i = 0; i < FM; ++i) lds_frag<T>(fa[i], buf, wm * WM + i * 32 + lr, chunk);
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+        for (int j = 0; j < FN; ++j) lds_frag<T>(fb[nb][j], buf, BM + nb * BN + wn * WN + j * 32 + lr, chunk);
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+          for (int j = 0; j < FN; ++j) mma32x32_k16(acc[nb][i][j], fa[i], fb[nb][j]);
+    }
+  }
+
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+      const int col = n0 + wn * WN + j * 32 + lr;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int row = m0 + wm * WM + i * 32 + 8 * (r >> 2) + 4 * kg + (r & 3);
+        if (row >= M || col >= N) continue;
+        const long idx = long(row) * N + col;
+        const float v = acc[0][i][j][r];
+        if constexpr (EPI == XP_EPI_F32) {
+          reinterpret_cast<float*>(C)[idx] = v;
+        } else if constexpr (EPI == XP_EPI_ADD_T) {
+          reinterpret_cast<float*>(C)[idx] = St<T>::load(R, idx) + v;
+        } else if constexpr (EPI == XP_EPI_ADD_F32) {
+          reinterpret_cast<float*>(C)[idx] = reinterpret_cast<const float*>(R)[idx] + v;
+        } else {
+          const float u = acc[NB - 1][i][j][r];
+          St<T>::store(C, idx, v / (1.0f + __expf(-v)) * u);
+        }
+      }
+    }
+}
+
+}  // namespace gemm
+}  // namespace xp
