@@ -257,7 +257,7 @@ def main():
         t = timer(lambda: X.xp_prefill_attention(X.XP_BF16, ws + lay.q_pre, dev.pool, inst.pool.n_pages, 16,
                                                  dev.pre_pages, inst.pre_max_blocks, hq, wl.hkv_loc, d,
                                                  wl.prior_len, wl.chunk_len, 0, wl.chunk_len, pout, hq * d,
-                                                 None, hq * d), args.repeats)
+                                                 None, hq * d, ws + lay.pre_part), args.repeats)
         fl = prefill_flops(wl)
         kern["prefill_attn"] = {"us": round(t * 1e6, 2), "TFLOPs": round(fl / t / 1e12, 1),
                                 "mfma_frac": round(fl / t / 1e12 / PEAK_BF16_TFLOPS, 4), "flops": fl}

@@ -17,7 +17,8 @@ __all__ = ["XpError", "lib", "XP_F32", "XP_BF16", "XP_EPI_F32", "XP_EPI_ADD_T", 
            "WsLayout", "LatencyModel", "Ctx", "EXPORTED",
            "xp_ctx_create", "xp_layer_workspace_layout", "xp_layer_forward", "xp_validate_batch",
            "xp_layer_read_status", "xp_rmsnorm", "xp_gemm", "xp_kv_append", "xp_kv_gather",
-           "xp_decode_workspace_size", "xp_decode_attention", "xp_prefill_attention", "xp_probe_hw_ids",
+           "xp_decode_workspace_size", "xp_decode_attention", "xp_prefill_workspace_size", "xp_prefill_attention",
+           "xp_probe_hw_ids",
            "xp_waterfill", "xp_iteration_latency", "xp_build_info", "xp_last_error"]
 
 XP_F32, XP_BF16 = 0, 1
@@ -33,7 +34,8 @@ EXPORTED = ["xp_last_error", "xp_build_info", "xp_ctx_create", "xp_ctx_destroy",
             "xp_ctx_streams",
             "xp_layer_workspace_layout", "xp_layer_forward", "xp_validate_batch", "xp_layer_read_status",
             "xp_rmsnorm", "xp_gemm", "xp_kv_append", "xp_kv_gather", "xp_decode_workspace_size",
-            "xp_decode_attention", "xp_prefill_attention", "xp_probe_hw_ids", "xp_waterfill",
+            "xp_decode_attention", "xp_prefill_workspace_size", "xp_prefill_attention", "xp_probe_hw_ids",
+            "xp_waterfill",
             "xp_iteration_latency"]
 
 
@@ -68,7 +70,7 @@ class BatchDesc(C.Structure):
 
 class WsLayout(C.Structure):
     _fields_ = [(n, C.c_size_t) for n in ("status", "hn", "qkv", "q_dec", "q_pre", "attn", "dec_ml",
-                                          "dec_o", "h1", "act", "total")] + \
+                                          "dec_o", "pre_part", "h1", "act", "total")] + \
                [("dec_splits", C.c_int32), ("dec_pages_per_split", C.c_int32)]
 
     def as_dict(self):
@@ -118,8 +120,9 @@ def _declare(L):
         "xp_decode_workspace_size": (_sz, [_i32, _i32, _i32, _i32, _i32]),
         "xp_decode_attention": (S, [_i32, _vp, _vp, _i32, _i32, _vp, _i32, _vp, _i32, _i32, _i32, _i32, _vp,
                                     _i32, _vp, _i32, _vp]),
+        "xp_prefill_workspace_size": (_sz, [_i32, _i32, _i32, _i32, _i32]),
         "xp_prefill_attention": (S, [_i32, _vp, _vp, _i32, _i32, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
-                                     _i32, _vp, _i32, _vp, _i32, _vp, _vp]),
+                                     _i32, _vp, _i32, _vp, _i32, _vp, _vp, _vp]),
         "xp_probe_hw_ids": (S, [_i32, _vp, _vp]),
         "xp_waterfill": (S, [C.POINTER(WaterfillIn), C.POINTER(WaterfillOut)]),
         "xp_iteration_latency": (S, [C.POINTER(LatencyModel), _i32, _vp, _vp, _vp, _i32, _vp, _vp,
@@ -270,13 +273,17 @@ def xp_decode_attention(dtype, q, pool, n_pages, page_size, dec_pages, dec_max_b
                                      _ptr(out), out_stride, _ptr(workspace), pages_per_split, _stream(stream)))
 
 
+def xp_prefill_workspace_size(hq, hkv, head_dim, prior_len, chunk_len) -> int:
+    return int(lib().xp_prefill_workspace_size(hq, hkv, head_dim, prior_len, chunk_len))
+
+
 def xp_prefill_attention(dtype, q, pool, n_pages, page_size, pre_pages, pre_max_blocks, hq, hkv, head_dim,
                          prior_len, chunk_len, off, n_local, out_local, out_local_stride, out_peer,
-                         out_peer_stride, status=None, stream=None):
+                         out_peer_stride, workspace=None, status=None, stream=None):
     _check(lib().xp_prefill_attention(dtype, _ptr(q), _ptr(pool), n_pages, page_size, _ptr(pre_pages),
                                       pre_max_blocks, hq, hkv, head_dim, prior_len, chunk_len, off, n_local,
                                       _ptr(out_local), out_local_stride, _ptr(out_peer), out_peer_stride,
-                                      _ptr(status), _stream(stream)))
+                                      _ptr(workspace), _ptr(status), _stream(stream)))
 
 
 def xp_probe_hw_ids(n_blocks, out, stream=None):

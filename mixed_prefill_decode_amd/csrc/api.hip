@@ -157,6 +157,8 @@ xp_ws_layout make_layout(const xp_ctx* ctx, const xp_layer_shape* sh, const xp_b
   const size_t units = size_t(d->n_decode) * Hq * splits;
   L.dec_ml = take(units * 2 * sizeof(float));
   L.dec_o = take(units * D * sizeof(float));
+  L.pre_part = take(prefill_ws_bytes(int(Hq) / d->sp_degree, int(Hkv) / d->sp_degree, int(D), d->prior_len,
+                                     d->chunk_len));
   L.h1 = take(M * H * 4);
   L.act = take(M * F * eb);
   L.total = off;
@@ -345,7 +347,8 @@ xp_status xp_layer_forward(xp_ctx* ctx, const xp_layer_shape* sh, const xp_batch
   auto prefill = [&](hipStream_t q) {
     return launch_prefill(dt, ws + L.q_pre, kv->pool, kv->n_pages, sh->page_size, d->pre_pages, d->pre_max_blocks,
                           hq_loc, hkv_loc, D, d->prior_len, d->chunk_len, d->local_row_offset, n_pl,
-                          attn + size_t(r) * hq_loc * D * eb, Hq * D, d->peer_attn_out, hq_loc * D, status, q);
+                          attn + size_t(r) * hq_loc * D * eb, Hq * D, d->peer_attn_out, hq_loc * D,
+                          ws + L.pre_part, status, q);
   };
   const bool concurrent = ctx->s_dec && n_d > 0 && d->chunk_len > 0;
   if (!concurrent) {
@@ -428,18 +431,24 @@ xp_status xp_decode_attention(int32_t dtype, const void* q, const void* pool, in
                        ml, po, pps, nullptr, static_cast<hipStream_t>(stream));
 }
 
+size_t xp_prefill_workspace_size(int32_t hq, int32_t hkv, int32_t d, int32_t prior, int32_t chunk) {
+  if (hq <= 0 || hkv <= 0 || hq % hkv || d <= 0 || prior < 0 || chunk <= 0) return 0;
+  return prefill_ws_bytes(hq, hkv, d, prior, chunk);
+}
+
 xp_status xp_prefill_attention(int32_t dtype, const void* q, const void* pool, int32_t n_pages, int32_t S,
                                const int32_t* pre_pages, int32_t pre_max_blocks, int32_t hq, int32_t hkv, int32_t d,
                                int32_t prior, int32_t chunk, int32_t off, int32_t n_local, void* out_local,
-                               int32_t out_local_stride, void* out_peer, int32_t out_peer_stride, uint32_t* status,
-                               void* stream) {
+                               int32_t out_local_stride, void* out_peer, int32_t out_peer_stride, void* workspace,
+                               uint32_t* status, void* stream) {
   if (chunk < 0 || prior < 0) return fail(XP_ESHAPE, "xp_prefill_attention: chunk/prior");
   if (chunk == 0) return XP_OK;
   if (!q || !pool || !pre_pages) return fail(XP_EINVAL, "xp_prefill_attention: null pointer");
   if (n_local > 0 && (!out_local || out_local_stride < hq * d)) return fail(XP_EINVAL, "xp_prefill_attention: out_local");
   if (chunk - n_local > 0 && (!out_peer || out_peer_stride < hq * d)) return fail(XP_EINVAL, "xp_prefill_attention: out_peer");
   return launch_prefill(dtype, q, pool, n_pages, S, pre_pages, pre_max_blocks, hq, hkv, d, prior, chunk, off, n_local,
-                        out_local, out_local_stride, out_peer, out_peer_stride, status, static_cast<hipStream_t>(stream));
+                        out_local, out_local_stride, out_peer, out_peer_stride, workspace, status,
+                        static_cast<hipStream_t>(stream));
 }
 
 }  // extern "C"

@@ -13,14 +13,21 @@ template <typename TI, typename TO>
 __global__ __launch_bounds__(256) void rmsnorm_kernel(const void* __restrict__ x, const void* __restrict__ gamma,
                                                       void* __restrict__ y, int H, float eps,
                                                       uint32_t* __restrict__ status_clear) {
+  // 16-byte vectors of the input; the row is read twice (the second pass hits L2)
+  constexpr int V = 16 / St<TI>::bytes;
   __shared__ float red[4];
   const int row = blockIdx.x, tid = threadIdx.x;
   if (status_clear && row == 0 && tid == 0) *status_clear = 0u;
-  const long base = long(row) * H;
+  const char* xr = static_cast<const char*>(x) + long(row) * H * St<TI>::bytes;
+  const int nv = H / V;
   float ss = 0.f;
-  for (int i = tid; i < H; i += 256) {
-    const float v = St<TI>::load(x, base + i);
-    ss += v * v;
+  for (int v = tid; v < nv; v += 256) {
+    const uint4 u = reinterpret_cast<const uint4*>(xr)[v];
+#pragma unroll
+    for (int e = 0; e < V; ++e) {
+      const float f = St<TI>::load(&u, e);
+      ss += f * f;
+    }
   }
 #pragma unroll
   for (int m = 32; m >= 1; m >>= 1) ss += shfl_xor(ss, m);
@@ -28,7 +35,25 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(const void* __restrict__ x
   __syncthreads();
   const float tot = red[0] + red[1] + red[2] + red[3];
   const float rstd = 1.0f / sqrtf(tot / float(H) + eps);
-  for (int i = tid; i < H; i += 256) St<TO>::store(y, base + i, St<TI>::load(x, base + i) * rstd * St<TO>::load(gamma, i));
+  char* yr = static_cast<char*>(y) + long(row) * H * St<TO>::bytes;
+  for (int v = tid; v < nv; v += 256) {
+    const uint4 u = reinterpret_cast<const uint4*>(xr)[v];
+    float f[V];
+#pragma unroll
+    for (int e = 0; e < V; ++e) f[e] = St<TI>::load(&u, e) * rstd * St<TO>::load(gamma, long(v) * V + e);
+    if constexpr (St<TO>::bytes == 2) {
+      uint32_t w[V / 2];
+#pragma unroll
+      for (int e = 0; e < V / 2; ++e) w[e] = pack_bf16x2(f[2 * e], f[2 * e + 1]);
+      if constexpr (V == 8)
+        reinterpret_cast<uint4*>(yr)[v] = make_uint4(w[0], w[1], w[2], w[3]);
+      else
+        reinterpret_cast<uint2*>(yr)[v] = make_uint2(w[0], w[1]);
+    } else {
+#pragma unroll
+      for (int e = 0; e < V; ++e) reinterpret_cast<float*>(yr)[long(v) * V + e] = f[e];
+    }
+  }
 }
 
 __global__ void clear_status_kernel(uint32_t* status) { *status = 0u; }
@@ -38,7 +63,7 @@ __global__ void clear_status_kernel(uint32_t* status) { *status = 0u; }
 xp_status launch_rmsnorm(int dtype, const void* x, int x_is_f32, const void* gamma, void* y, int M, int H,
                          float eps, uint32_t* status_clear, hipStream_t s) {
   if (dtype != XP_BF16 && dtype != XP_F32) return fail(XP_EINVAL, "xp_rmsnorm: dtype %d", dtype);
-  if (M < 0 || H <= 0) return fail(XP_ESHAPE, "xp_rmsnorm: M=%d H=%d", M, H);
+  if (M < 0 || H <= 0 || H % 8) return fail(XP_ESHAPE, "xp_rmsnorm: M=%d H=%d (H a multiple of 8)", M, H);
   if (!x || !gamma || !y) return fail(XP_EINVAL, "xp_rmsnorm: null pointer");
   if (M == 0) {
     if (status_clear) {

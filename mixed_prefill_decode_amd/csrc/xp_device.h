@@ -32,13 +32,11 @@ struct bf16_t { uint16_t bits; };
 
 __device__ __forceinline__ float bf2f(uint16_t b) { return __uint_as_float(uint32_t(b) << 16); }
 
-// fp32 -> bf16, round to nearest even; NaN stays a quiet NaN.
-__device__ __forceinline__ uint16_t f2bf(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return uint16_t((u >> 16) | 0x40u);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return uint16_t(u >> 16);
-}
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+
+// fp32 -> bf16, round to nearest even (NaN stays NaN): gfx950's v_cvt_pk_bf16_f32.
+__device__ __forceinline__ uint16_t f2bf(float f) { return __builtin_bit_cast(uint16_t, (__bf16)f); }
 
 // ---- storage-type traits ---------------------------------------------------
 template <typename T> struct St;
@@ -105,7 +103,7 @@ __device__ __forceinline__ float frag_get(const Frag8<float>& f, int e) {
 }
 
 __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
-  return uint32_t(f2bf(a)) | (uint32_t(f2bf(b)) << 16);
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){a, b}, bf16x2_t));
 }
 __device__ __forceinline__ void set_frag4(Frag4<bf16_t>& f, float a, float b, float c, float d) {
   f.v = make_uint2(pack_bf16x2(a, b), pack_bf16x2(c, d));

@@ -71,10 +71,11 @@ xp_status launch_decode(int dtype, const void* q, const void* pool, int n_pages,
                         int Hq, int Hkv, int d, void* out, int out_stride, float* part_ml,
                         float* part_o, int pages_per_split, uint32_t* status, hipStream_t s);
 
+size_t prefill_ws_bytes(int hq, int hkv, int d, int prior, int chunk);
 xp_status launch_prefill(int dtype, const void* q, const void* pool, int n_pages, int S,
                          const int32_t* pre_pages, int pre_max_blocks, int hq, int hkv, int d,
                          int prior, int chunk, int off, int n_local, void* out_local,
-                         int out_local_stride, void* out_peer, int out_peer_stride, uint32_t* status,
-                         hipStream_t s);
+                         int out_local_stride, void* out_peer, int out_peer_stride, void* ws,
+                         uint32_t* status, hipStream_t s);
 
 }  // namespace xp

@@ -362,6 +362,10 @@ PARITY_WORKLOADS = {
     "P3": Workload("P3", 103, "bf16", 1024, 64, 8, 128, 2048, n_decode=3, ctx=("uniform", 100, 900),
                    chunk_len=256, prior_len=130, sp_degree=8, sp_rank=0,
                    description="small bf16 layer, 8 q heads on one kv head per rank"),
+    # long prior context: many key splits per query tile (the merge path), G=8 on one kv head, rank 1
+    "P4": Workload("P4", 104, "bf16", 1024, 16, 2, 128, 2048, n_decode=2, ctx=("list", [37, 2500]),
+                   chunk_len=320, prior_len=2000, sp_degree=2, sp_rank=1,
+                   description="small bf16 layer, 2000 prior keys, SP2 rank 1"),
     # decode only
     "E1": Workload("E1", 111, "bf16", 512, 8, 2, 128, 1024, n_decode=9, ctx=("uniform", 1, 2000),
                    chunk_len=0, prior_len=0, description="decode only"),

@@ -179,7 +179,7 @@ def test_decode_attention(name, pps):
         assert rel_fro(got[i], ref[i]) < 2 * ATTN_TOL[dt], i
 
 
-@pytest.mark.parametrize("name", ["P1", "P2", "P3", "E2", "C1", "E4"])
+@pytest.mark.parametrize("name", ["P1", "P2", "P3", "P4", "E2", "C1", "E4"])
 def test_prefill_attention(name):
     inst = make_instance(get_workload(name))
     wl, dt = inst.wl, inst.wl.dtype
@@ -194,9 +194,11 @@ def test_prefill_attention(name):
     out_l = torch.full((max(n_loc, 1), hq * d), float("nan"), dtype=tdt, device="cuda")
     out_p = torch.full((max(l - n_loc, 1), hq * d), float("nan"), dtype=tdt, device="cuda")
     status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    ws = torch.empty(max(X.xp_prefill_workspace_size(hq, wl.hkv_loc, d, wl.prior_len, l), 1), dtype=torch.uint8,
+                     device="cuda")
     X.xp_prefill_attention(DT[dt], to_device(q, dt), dpool, inst.pool.n_pages, wl.page_size,
                            to_device(inst.pre_pages, "i32"), inst.pre_max_blocks, hq, wl.hkv_loc, d, wl.prior_len,
-                           l, off, n_loc, out_l, hq * d, out_p, hq * d, status)
+                           l, off, n_loc, out_l, hq * d, out_p, hq * d, ws, status)
     _sync()
     ref = L.prefill_attention(to_f64(q, dt).transpose(1, 0, 2), kv, inst.pre_pages, wl.prior_len, wl.group)
     ref = ref.reshape(l, hq * d)
@@ -227,9 +229,11 @@ def test_decode_token_matches_prefill_row_on_gpu():
     l, hq, d, G = wl.chunk_len, wl.hq_loc, wl.head_dim, wl.group
     q = _rand(rng, (hq, l, d), dt)
     out_l = torch.empty((l, hq * d), dtype=torch.bfloat16, device="cuda")
+    pws = torch.empty(max(X.xp_prefill_workspace_size(hq, wl.hkv_loc, d, wl.prior_len, l), 1), dtype=torch.uint8,
+                      device="cuda")
     X.xp_prefill_attention(DT[dt], to_device(q, dt), dpool, inst.pool.n_pages, wl.page_size,
                            to_device(inst.pre_pages, "i32"), inst.pre_max_blocks, hq, wl.hkv_loc, d, wl.prior_len,
-                           l, 0, l, out_l, hq * d, None, hq * d)
+                           l, 0, l, out_l, hq * d, None, hq * d, pws)
     # the same queries as decode requests: request t has context prior + t on kv head g's table
     rows = [0, 5, l - 1]
     for g in range(wl.hkv_loc):
