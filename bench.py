@@ -118,7 +118,7 @@ def calibrate_decode_cus(X, torch, step, inst, dev, timer, n_cus, repeats) -> tu
     wl = inst.wl
     lay = step.layout
     q = int(step.workspace.data_ptr()) + lay.q_dec
-    dws = torch.empty(X.xp_decode_workspace_size(wl.n_decode, wl.n_q_heads, wl.head_dim, inst.dec_max_blocks,
+    dws = torch.empty(X.xp_decode_workspace_size(wl.n_decode, wl.n_q_heads, wl.n_kv_heads, wl.head_dim, inst.dec_max_blocks,
                                                  lay.dec_pages_per_split), dtype=torch.uint8, device="cuda")
     out = torch.empty((wl.n_decode, wl.n_q_heads * wl.head_dim), dtype=torch.bfloat16, device="cuda")
     nbytes = decode_bytes(inst)
@@ -159,6 +159,10 @@ def main():
     from synth.device import make_step, upload
 
     torch.cuda.init()
+    # Everything runs on a non-blocking stream: the context's CU-masked side
+    # streams are blocking HIP streams, which the null stream would otherwise
+    # wait on at every launch.
+    torch.cuda.set_stream(torch.cuda.Stream())
     props = torch.cuda.get_device_properties(0)
     n_cus = props.multi_processor_count
     wl = get_workload(args.workload)
@@ -240,7 +244,7 @@ def main():
         kern[name] = {"us": round(t * 1e6, 2), "TFLOPs": round(fl / t / 1e12, 1),
                       "mfma_frac": round(fl / t / 1e12 / PEAK_BF16_TFLOPS, 4),
                       "weight_GBs": round(wbytes / t / 1e9, 1)}
-    dws = torch.empty(X.xp_decode_workspace_size(wl.n_decode, wl.n_q_heads, wl.head_dim, max(inst.dec_max_blocks, 1),
+    dws = torch.empty(X.xp_decode_workspace_size(wl.n_decode, wl.n_q_heads, wl.n_kv_heads, wl.head_dim, max(inst.dec_max_blocks, 1),
                                                  lay.dec_pages_per_split) or 256, dtype=torch.uint8, device="cuda")
     if wl.n_decode:
         dout = torch.empty((wl.n_decode, wl.n_q_heads * wl.head_dim), dtype=torch.bfloat16, device="cuda")

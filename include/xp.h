@@ -173,7 +173,12 @@ typedef struct xp_ctx xp_ctx;
  *         the rest for prefill ([CS] §6.1: decode gets the fewest CUs that keep
  *         90% of its standalone HBM bandwidth).  The k CUs are spread evenly
  *         over the XCDs.
- * decode_pages_per_split: KV pages per decode split-K partition (0 = 32). */
+ * decode_pages_per_split: KV pages per decode split-K partition, 1..64, or 0
+ *   to choose per batch from the decode shape (about 1600 split waves, 8..64
+ *   pages each; the layout's dec_pages_per_split reports the choice).
+ * The two side streams are ordinary blocking HIP streams, so on the null
+ * stream every launch also waits on them: run xp_layer_forward on a
+ * non-blocking stream when decode_cus != 0. */
 xp_status xp_ctx_create(xp_ctx** ctx, int32_t device, int32_t decode_cus,
                         int32_t decode_pages_per_split);
 xp_status xp_ctx_destroy(xp_ctx* ctx);
@@ -256,9 +261,12 @@ xp_status xp_kv_gather(int32_t dtype, const void* pool, int32_t n_pages, int32_t
  * follows [TKNP] Eq. 4's (output, fp32 LSE) partials).  q [n_d, Hq, d] T;
  * request i, head h reads kv head h / (Hq/Hkv) over positions 0..dec_ctx[i];
  * out row i at out + i*out_stride (elements), [Hq d] T.
- * workspace: >= xp_decode_workspace_size bytes of device memory. */
-size_t xp_decode_workspace_size(int32_t n_decode, int32_t n_q_heads, int32_t head_dim,
-                                int32_t dec_max_blocks, int32_t pages_per_split);
+ * pages_per_split: 1..64 KV pages per split, or 0 to choose from the shape as
+ * xp_ctx_create describes.
+ * workspace: >= xp_decode_workspace_size bytes of device memory, computed with
+ * the same sizes and pages_per_split. */
+size_t xp_decode_workspace_size(int32_t n_decode, int32_t n_q_heads, int32_t n_kv_heads,
+                                int32_t head_dim, int32_t dec_max_blocks, int32_t pages_per_split);
 xp_status xp_decode_attention(int32_t dtype, const void* q, const void* pool, int32_t n_pages,
                               int32_t page_size, const int32_t* dec_pages, int32_t dec_max_blocks,
                               const int32_t* dec_ctx, int32_t n_decode, int32_t n_q_heads,

@@ -117,7 +117,7 @@ def _declare(L):
         "xp_gemm": (S, [_i32, _i32, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _vp]),
         "xp_kv_append": (S, [_i32, _vp, _i32, _i32, _i32, _vp, _i32, _vp, _vp, _vp, _vp, _i32, _vp]),
         "xp_kv_gather": (S, [_i32, _vp, _i32, _i32, _i32, _vp, _i32, _vp, _i32, _i32, _vp, _vp, _vp]),
-        "xp_decode_workspace_size": (_sz, [_i32, _i32, _i32, _i32, _i32]),
+        "xp_decode_workspace_size": (_sz, [_i32, _i32, _i32, _i32, _i32, _i32]),
         "xp_decode_attention": (S, [_i32, _vp, _vp, _i32, _i32, _vp, _i32, _vp, _i32, _i32, _i32, _i32, _vp,
                                     _i32, _vp, _i32, _vp]),
         "xp_prefill_workspace_size": (_sz, [_i32, _i32, _i32, _i32, _i32]),
@@ -261,8 +261,9 @@ def xp_kv_gather(dtype, pool, n_pages, page_size, head_dim, table, table_stride,
                               _ptr(lens), n_seq, max_len, _ptr(k_out), _ptr(v_out), _stream(stream)))
 
 
-def xp_decode_workspace_size(n_decode, n_q_heads, head_dim, dec_max_blocks, pages_per_split) -> int:
-    return int(lib().xp_decode_workspace_size(n_decode, n_q_heads, head_dim, dec_max_blocks, pages_per_split))
+def xp_decode_workspace_size(n_decode, n_q_heads, n_kv_heads, head_dim, dec_max_blocks, pages_per_split) -> int:
+    return int(lib().xp_decode_workspace_size(n_decode, n_q_heads, n_kv_heads, head_dim, dec_max_blocks,
+                                              pages_per_split))
 
 
 def xp_decode_attention(dtype, q, pool, n_pages, page_size, dec_pages, dec_max_blocks, dec_ctx, n_decode,

@@ -38,7 +38,7 @@ struct xp_ctx {
   int device = 0;
   int n_cus = 0;
   int decode_cus = 0;  // 0 serialized, -1 concurrent unmasked, k masked
-  int pps = 32;
+  int pps = 0;
   hipStream_t s_dec = nullptr, s_pre = nullptr;
   hipEvent_t e_fork = nullptr, e_dec = nullptr, e_pre = nullptr;
   uint32_t mask_dec[8] = {}, mask_pre[8] = {};
@@ -140,7 +140,7 @@ xp_ws_layout make_layout(const xp_ctx* ctx, const xp_layer_shape* sh, const xp_b
   const size_t eb = dtype_bytes(sh->dtype);
   const size_t M = rows_of(d), H = sh->hidden, F = sh->ffn_dim, Hq = sh->n_q_heads, Hkv = sh->n_kv_heads,
                D = sh->head_dim;
-  const int pps = ctx ? ctx->pps : 32;
+  const int pps = decode_pick_pps(ctx ? ctx->pps : 0, d->n_decode, int(Hkv), d->dec_max_blocks);
   const int splits = d->n_decode > 0 ? decode_splits(d->dec_max_blocks, pps) : 0;
   size_t off = 0;
   auto take = [&](size_t bytes) {
@@ -184,7 +184,7 @@ xp_status xp_ctx_create(xp_ctx** out, int32_t device, int32_t decode_cus, int32_
   xp_ctx* c = new xp_ctx();
   c->device = device;
   c->n_cus = prop.multiProcessorCount;
-  c->pps = pages_per_split ? pages_per_split : 32;
+  c->pps = pages_per_split;  // 0: chosen per batch
   if (decode_cus < -1 || decode_cus >= c->n_cus) {
     delete c;
     return fail(XP_EINVAL, "decode_cus %d (valid: -1, 0, 1..%d)", decode_cus, c->n_cus - 1);
@@ -341,7 +341,7 @@ xp_status xp_layer_forward(xp_ctx* ctx, const xp_layer_shape* sh, const xp_batch
   auto decode = [&](hipStream_t q) {
     return launch_decode(dt, ws + L.q_dec, kv->pool, kv->n_pages, sh->page_size, d->dec_pages, d->dec_max_blocks,
                          d->dec_ctx, n_d, Hq, Hkv, D, attn + size_t(n_pl) * Hq * D * eb, Hq * D,
-                         reinterpret_cast<float*>(ws + L.dec_ml), reinterpret_cast<float*>(ws + L.dec_o), ctx->pps,
+                         reinterpret_cast<float*>(ws + L.dec_ml), reinterpret_cast<float*>(ws + L.dec_o), L.dec_pages_per_split,
                          status, q);
   };
   auto prefill = [&](hipStream_t q) {
@@ -409,9 +409,9 @@ xp_status xp_kv_gather(int32_t dtype, const void* pool, int32_t n_pages, int32_t
                           static_cast<hipStream_t>(stream));
 }
 
-size_t xp_decode_workspace_size(int32_t n_d, int32_t Hq, int32_t d, int32_t max_blocks, int32_t pps) {
-  if (n_d <= 0 || Hq <= 0 || d <= 0 || max_blocks <= 0 || pps <= 0) return 0;
-  return decode_ws_bytes(n_d, Hq, d, decode_splits(max_blocks, pps));
+size_t xp_decode_workspace_size(int32_t n_d, int32_t Hq, int32_t Hkv, int32_t d, int32_t max_blocks, int32_t pps) {
+  if (n_d <= 0 || Hq <= 0 || Hkv <= 0 || d <= 0 || max_blocks <= 0 || pps < 0) return 0;
+  return decode_ws_bytes(n_d, Hq, d, decode_splits(max_blocks, decode_pick_pps(pps, n_d, Hkv, max_blocks)));
 }
 
 xp_status xp_decode_attention(int32_t dtype, const void* q, const void* pool, int32_t n_pages, int32_t S,
@@ -422,7 +422,9 @@ xp_status xp_decode_attention(int32_t dtype, const void* q, const void* pool, in
   if (n_d == 0) return XP_OK;
   if (!q || !pool || !dec_pages || !dec_ctx || !out || !workspace) return fail(XP_EINVAL, "xp_decode_attention: null pointer");
   if (out_stride < Hq * d) return fail(XP_ESHAPE, "xp_decode_attention: out_stride %d < Hq*d", out_stride);
-  if (pps <= 0) pps = 32;
+  if (pps < 0) return fail(XP_EINVAL, "xp_decode_attention: pages_per_split %d", pps);
+  if (Hkv <= 0 || max_blocks <= 0) return fail(XP_ESHAPE, "xp_decode_attention: Hkv %d max_blocks %d", Hkv, max_blocks);
+  pps = decode_pick_pps(pps, n_d, Hkv, max_blocks);
   const int splits = decode_splits(max_blocks, pps);
   const size_t ml_bytes = align_up(size_t(n_d) * Hq * splits * 2 * sizeof(float), 256);
   float* ml = static_cast<float*>(workspace);

@@ -16,8 +16,8 @@
 // rescale needs no cross-lane traffic beyond the 16-key max.  The V plane of a
 // page is stored dim-major, so the V^T operand of lane l is 4 consecutive keys
 // of one dim row (8 contiguous bytes for bf16).  Scores are kept in the exp2
-// domain (scale * log2(e) folded in).  The next page's K/V fragments are loaded
-// before the current page is consumed.
+// domain (scale * log2(e) folded in).  Each wave keeps a few pages of K/V
+// fragments in flight ahead of the page it consumes.
 #include "xp_device.h"
 #include "xp_internal.h"
 
@@ -26,6 +26,8 @@ namespace xp {
 namespace {
 
 constexpr int kPage = 16;
+// pages in flight per wave while one is consumed
+constexpr int kDepth = 1;
 
 __device__ __forceinline__ void zero_tail(Frag4<bf16_t>& f, int nvalid) {
   uint32_t x = f.v.x, y = f.v.y;
@@ -48,18 +50,43 @@ struct PageFrags {
   Frag4<T> v[D / 16];
 };
 
+// Buffer resource over one page: a page outside the split or with an id
+// outside the pool gets zero records, so its loads return zeros and touch no
+// memory.  The loads of the pipeline are therefore unconditional.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t page_rsrc(const char* page, int nbytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(page), (short)0, nbytes, 0x00020000);
+}
+
+__device__ __forceinline__ void bload(Frag8<bf16_t>& f, __amdgpu_buffer_rsrc_t r, int off) {
+  f.v = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+__device__ __forceinline__ void bload(Frag8<float>& f, __amdgpu_buffer_rsrc_t r, int off) {
+  f.lo = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+  f.hi = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(r, off + 16, 0, 0));
+}
+__device__ __forceinline__ void bload(Frag4<bf16_t>& f, __amdgpu_buffer_rsrc_t r, int off) {
+  f.v = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0));
+}
+__device__ __forceinline__ void bload(Frag4<float>& f, __amdgpu_buffer_rsrc_t r, int off) {
+  f.v = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+
+// K plane token-major [16][D]: lane l reads key l%16, dims [32*st + 8*(l/16), +8).
+// V plane dim-major [D][16]: lane l reads dim 16*n + l%16, keys [4*(l/16), +4).
 template <typename T, int D>
-__device__ __forceinline__ void load_page(PageFrags<T, D>& f, const char* page, int lane) {
+__device__ __forceinline__ void load_page(PageFrags<T, D>& f, __amdgpu_buffer_rsrc_t r, int lane) {
   constexpr int EB = St<T>::bytes;
   const int key = lane & 15, grp = lane >> 4;
 #pragma unroll
-  for (int st = 0; st < D / 32; ++st) load_frag8(f.k[st], page + (key * D + 32 * st + 8 * grp) * EB);
-  const char* vp = page + kPage * D * EB;
+  for (int st = 0; st < D / 32; ++st) bload(f.k[st], r, (key * D + 32 * st + 8 * grp) * EB);
 #pragma unroll
-  for (int n = 0; n < D / 16; ++n) load_frag4(f.v[n], vp + ((16 * n + key) * kPage + 4 * grp) * EB);
+  for (int n = 0; n < D / 16; ++n) bload(f.v[n], r, (kPage * D + (16 * n + key) * kPage + 4 * grp) * EB);
 }
 
-template <typename T, int D>
+// One wave per (split s, KV head g, request i).  DEPTH pages are in flight
+// while one is consumed; the register ring has DEPTH + 1 page buffers and the
+// loop is unrolled over the ring so every buffer index is static.
+template <typename T, int D, int DEPTH>
 __global__ __launch_bounds__(64) void decode_split_kernel(const void* __restrict__ q, const char* __restrict__ pool,
                                                           int n_pages, const int32_t* __restrict__ dec_pages,
                                                           int max_blocks, const int32_t* __restrict__ dec_ctx, int Hq,
@@ -67,18 +94,15 @@ __global__ __launch_bounds__(64) void decode_split_kernel(const void* __restrict
                                                           float* __restrict__ part_o, float scale_log2,
                                                           uint32_t* __restrict__ status) {
   constexpr int EB = St<T>::bytes;
-  constexpr long PAGE_BYTES = 2L * kPage * D * EB;
+  constexpr int PAGE_BYTES = 2 * kPage * D * EB;
+  constexpr int NB = DEPTH + 1;
   const int s = blockIdx.x, g = blockIdx.y, i = blockIdx.z;
   const int lane = threadIdx.x;
   const int G = Hq / Hkv;
-  const int n_keys = dec_ctx[i] + 1;
-  const int nb_need = (n_keys + kPage - 1) / kPage;
-  const int nb = min(nb_need, max_blocks);
   const int b0 = s * pps;
-  if (b0 >= nb_need && !(s == 0 && n_keys <= 0)) return;  // this split has no keys
-  const int b1 = min(nb, b0 + pps);
-  bool bad = nb_need > max_blocks || n_keys <= 0;
-
+  // the table slice is read before anything that depends on the context length
+  const int32_t* tbl = dec_pages + (long(i) * Hkv + g) * max_blocks;
+  const int my_pid = (lane < pps && b0 + lane < max_blocks) ? tbl[b0 + lane] : -1;
   const int hh = lane & 15, grp = lane >> 4;
   Frag8<T> qf[D / 32];
 #pragma unroll
@@ -89,60 +113,73 @@ __global__ __launch_bounds__(64) void decode_split_kernel(const void* __restrict
       zero_frag(qf[st]);
     }
   }
-  const int32_t* tbl = dec_pages + (long(i) * Hkv + g) * max_blocks;
-  const int my_pid = (b0 + lane < b1) ? tbl[b0 + lane] : 0;
+  const int n_keys = dec_ctx[i] + 1;
+  const int nb_need = (n_keys + kPage - 1) / kPage;
+  const int nb = min(nb_need, max_blocks);
+  if (b0 >= nb_need && !(s == 0 && n_keys <= 0)) return;  // this split has no keys
+  const int b1 = min(nb, b0 + pps);
+  bool bad = nb_need > max_blocks || n_keys <= 0;
+
+  auto rsrc_of = [&](int b) {
+    const bool in = b < b1;
+    const int pid = __builtin_amdgcn_readlane(my_pid, in ? b - b0 : 0);
+    const bool ok = in && pid >= 0 && pid < n_pages;
+    bad |= in && !ok;
+    return page_rsrc(pool + (ok ? long(pid) : 0L) * PAGE_BYTES, ok ? PAGE_BYTES : 0);
+  };
 
   f32x4 o[D / 16];
 #pragma unroll
   for (int n = 0; n < D / 16; ++n) o[n] = f32x4{0.f, 0.f, 0.f, 0.f};
   float m = -__builtin_inff(), lsum = 0.f;
 
-  PageFrags<T, D> cur, nxt;
-  int pid = __builtin_amdgcn_readlane(my_pid, 0);
-  bool ok = b0 < b1 && pid >= 0 && pid < n_pages;
-  if (ok) load_page<T, D>(cur, pool + pid * PAGE_BYTES, lane);
-  for (int b = b0; b < b1; ++b) {
-    const bool ok_cur = ok;
-    if (b + 1 < b1) {
-      pid = __builtin_amdgcn_readlane(my_pid, b + 1 - b0);
-      ok = pid >= 0 && pid < n_pages;
-      if (ok) load_page<T, D>(nxt, pool + pid * PAGE_BYTES, lane);
-    }
-    if (!ok_cur) {
-      bad = true;
-    } else {
-      f32x4 sacc = {0.f, 0.f, 0.f, 0.f};
+  PageFrags<T, D> buf[NB];
 #pragma unroll
-      for (int st = 0; st < D / 32; ++st) mma16x16_k32(sacc, cur.k[st], qf[st]);
-      // element r: key b*16 + 4*grp + r of head hh
-      const int k0 = b * kPage + 4 * grp;
-      float sv[4];
+  for (int j = 0; j < DEPTH; ++j) {
+    load_page<T, D>(buf[j], rsrc_of(b0 + j), lane);
+    // keep the pages' loads in issue order: the waits below count on it
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  for (int bb = b0; bb < b1; bb += NB) {
 #pragma unroll
-      for (int r = 0; r < 4; ++r) sv[r] = (k0 + r < n_keys) ? sacc[r] * scale_log2 : -__builtin_inff();
-      if ((b + 1) * kPage > n_keys) {
+    for (int u = 0; u < NB; ++u) {
+      const int b = bb + u;
+      load_page<T, D>(buf[(u + DEPTH) % NB], rsrc_of(b + DEPTH), lane);
+      __builtin_amdgcn_sched_barrier(0);
+      if (b < b1) {
+        PageFrags<T, D>& cur = buf[u];
+        f32x4 sacc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int n = 0; n < D / 16; ++n) zero_tail(cur.v[n], n_keys - k0);
+        for (int st = 0; st < D / 32; ++st) mma16x16_k32(sacc, cur.k[st], qf[st]);
+        // element r: key b*16 + 4*grp + r of head hh
+        const int k0 = b * kPage + 4 * grp;
+        float sv[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) sv[r] = (k0 + r < n_keys) ? sacc[r] * scale_log2 : -__builtin_inff();
+        if ((b + 1) * kPage > n_keys) {
+#pragma unroll
+          for (int n = 0; n < D / 16; ++n) zero_tail(cur.v[n], n_keys - k0);
+        }
+        float mb = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
+        mb = fmaxf(mb, shfl_xor(mb, 16));
+        mb = fmaxf(mb, shfl_xor(mb, 32));
+        const float mn = fmaxf(m, mb);  // finite: every visited page holds a visible key
+        const float alpha = fast_exp2(m - mn);
+        // the weights are rounded to the operand type first, so the normaliser sums
+        // exactly the weights the PV product uses
+        const float p0 = round_st<T>(fast_exp2(sv[0] - mn)), p1 = round_st<T>(fast_exp2(sv[1] - mn));
+        const float p2 = round_st<T>(fast_exp2(sv[2] - mn)), p3 = round_st<T>(fast_exp2(sv[3] - mn));
+        lsum = lsum * alpha + ((p0 + p1) + (p2 + p3));
+        Frag4<T> pf;
+        set_frag4(pf, p0, p1, p2, p3);
+#pragma unroll
+        for (int n = 0; n < D / 16; ++n) {
+          o[n] *= alpha;
+          mma16x16_k16(o[n], cur.v[n], pf);
+        }
+        m = mn;
       }
-      float mb = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
-      mb = fmaxf(mb, shfl_xor(mb, 16));
-      mb = fmaxf(mb, shfl_xor(mb, 32));
-      const float mn = fmaxf(m, mb);  // finite: every visited page holds a visible key
-      const float alpha = fast_exp2(m - mn);
-      // the weights are rounded to the operand type first, so the normaliser sums
-      // exactly the weights the PV product uses
-      const float p0 = round_st<T>(fast_exp2(sv[0] - mn)), p1 = round_st<T>(fast_exp2(sv[1] - mn));
-      const float p2 = round_st<T>(fast_exp2(sv[2] - mn)), p3 = round_st<T>(fast_exp2(sv[3] - mn));
-      lsum = lsum * alpha + ((p0 + p1) + (p2 + p3));
-      Frag4<T> pf;
-      set_frag4(pf, p0, p1, p2, p3);
-#pragma unroll
-      for (int n = 0; n < D / 16; ++n) {
-        o[n] *= alpha;
-        mma16x16_k16(o[n], cur.v[n], pf);
-      }
-      m = mn;
     }
-    cur = nxt;
   }
   lsum += shfl_xor(lsum, 16);
   lsum += shfl_xor(lsum, 32);
@@ -162,24 +199,72 @@ __global__ __launch_bounds__(64) void decode_split_kernel(const void* __restrict
 }
 
 // out[i, h*D + j] = sum_s 2^(m_s - m*) o_s[j] / sum_s 2^(m_s - m*) l_s
+// One 256-thread workgroup per (query head, request): thread t accumulates dim
+// t % D over every (256 / D)-th split with several partial loads in flight,
+// and the split groups are summed in LDS at the end.
+constexpr int kCombineThreads = 256;
+
 template <typename T, int D>
-__global__ __launch_bounds__(D) void decode_combine_kernel(const float* __restrict__ part_ml,
-                                                           const float* __restrict__ part_o,
-                                                           const int32_t* __restrict__ dec_ctx, int Hq, int pps,
-                                                           int n_splits, void* __restrict__ out, int out_stride) {
-  const int h = blockIdx.x, i = blockIdx.y, j = threadIdx.x;
+__global__ __launch_bounds__(kCombineThreads) void decode_combine_kernel(const float* __restrict__ part_ml,
+                                                                         const float* __restrict__ part_o,
+                                                                         const int32_t* __restrict__ dec_ctx, int Hq,
+                                                                         int pps, int n_splits, void* __restrict__ out,
+                                                                         int out_stride) {
+  constexpr int R = kCombineThreads / D;  // split groups
+  __shared__ float red[kCombineThreads / 64];
+  __shared__ float acc_s[R][D];
+  __shared__ float l_s[R];
+  const int h = blockIdx.x, i = blockIdx.y, t = threadIdx.x;
   const int nb = (dec_ctx[i] + 1 + kPage - 1) / kPage;
   const int ns = max(1, min(n_splits, (nb + pps - 1) / pps));
-  const long base = (long(i) * Hq + h) * n_splits;
+  const float* ml = part_ml + 2L * (long(i) * Hq + h) * n_splits;
+  const float* po = part_o + (long(i) * Hq + h) * n_splits * long(D);
+  // m* over the splits (a NaN maximum of a flagged split is ignored here and
+  // poisons the weights below)
   float mx = -__builtin_inff();
-  for (int s = 0; s < ns; ++s) mx = fmaxf(mx, part_ml[2 * (base + s)]);
-  float L = 0.f, acc = 0.f;
-  for (int s = 0; s < ns; ++s) {
-    const float w = fast_exp2(part_ml[2 * (base + s)] - mx);
-    L += part_ml[2 * (base + s) + 1] * w;
-    acc += part_o[(base + s) * D + j] * w;
+  for (int s = t; s < ns; s += kCombineThreads) mx = fmaxf(mx, ml[2 * s]);
+#pragma unroll
+  for (int w = 32; w >= 1; w >>= 1) mx = fmaxf(mx, shfl_xor(mx, w));
+  if ((t & 63) == 0) red[t >> 6] = mx;
+  __syncthreads();
+  mx = red[0];
+#pragma unroll
+  for (int w = 1; w < kCombineThreads / 64; ++w) mx = fmaxf(mx, red[w]);
+  const int j = t % D, r = t / D;
+  float acc = 0.f, L = 0.f;
+  constexpr int U = 4;
+  int s = r;
+  for (; s + (U - 1) * R < ns; s += U * R) {
+    float m4[U], l4[U], o4[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      m4[u] = ml[2 * (s + u * R)];
+      l4[u] = ml[2 * (s + u * R) + 1];
+      o4[u] = po[long(s + u * R) * D + j];
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const float w = fast_exp2(m4[u] - mx);
+      L += l4[u] * w;
+      acc += o4[u] * w;
+    }
   }
-  St<T>::store(out, long(i) * out_stride + long(h) * D + j, acc / L);
+  for (; s < ns; s += R) {
+    const float w = fast_exp2(ml[2 * s] - mx);
+    L += ml[2 * s + 1] * w;
+    acc += po[long(s) * D + j] * w;
+  }
+  acc_s[r][j] = acc;
+  if (j == 0) l_s[r] = L;
+  __syncthreads();
+  if (r == 0) {
+#pragma unroll
+    for (int q = 1; q < R; ++q) {
+      acc += acc_s[q][j];
+      L += l_s[q];
+    }
+    St<T>::store(out, long(i) * out_stride + long(h) * D + j, acc / L);
+  }
 }
 
 template <typename T, int D>
@@ -188,11 +273,11 @@ xp_status launch_dec_t(const void* q, const void* pool, int n_pages, const int32
                        float* part_o, int pps, uint32_t* status, hipStream_t s) {
   const int n_splits = decode_splits(max_blocks, pps);
   const float scale_log2 = float(1.4426950408889634 / __builtin_sqrt(double(D)));
-  hipLaunchKernelGGL((decode_split_kernel<T, D>), dim3(n_splits, Hkv, n_d), dim3(64), 0, s, q,
+  hipLaunchKernelGGL((decode_split_kernel<T, D, kDepth>), dim3(n_splits, Hkv, n_d), dim3(64), 0, s, q,
                      static_cast<const char*>(pool), n_pages, dec_pages, max_blocks, dec_ctx, Hq, Hkv, pps, n_splits,
                      part_ml, part_o, scale_log2, status);
   XP_CHECK_LAUNCH();
-  hipLaunchKernelGGL((decode_combine_kernel<T, D>), dim3(Hq, n_d), dim3(D), 0, s, part_ml, part_o, dec_ctx, Hq, pps,
+  hipLaunchKernelGGL((decode_combine_kernel<T, D>), dim3(Hq, n_d), dim3(kCombineThreads), 0, s, part_ml, part_o, dec_ctx, Hq, pps,
                      n_splits, out, out_stride);
   XP_CHECK_LAUNCH();
   return XP_OK;
@@ -201,6 +286,17 @@ xp_status launch_dec_t(const void* q, const void* pool, int n_pages, const int32
 }  // namespace
 
 int decode_splits(int dec_max_blocks, int pps) { return std::max(1, cdiv(dec_max_blocks, pps)); }
+
+// Pages per split when the caller leaves it open (0): about kTargetWaves split
+// waves over the batch's (request, KV head) pairs at their table width, i.e.
+// some six resident waves per CU, and between 8 and 64 pages per wave.  Fewer,
+// longer splits write fewer partials; more splits keep more pages in flight.
+constexpr long kTargetWaves = 1600;
+int decode_pick_pps(int requested, int n_d, int Hkv, int dec_max_blocks) {
+  if (requested > 0) return requested;
+  const long work = long(n_d) * Hkv * dec_max_blocks;
+  return int(std::min(64L, std::max(8L, work / kTargetWaves)));
+}
 
 size_t decode_ws_bytes(int n_d, int Hq, int d, int n_splits) {
   const size_t units = size_t(n_d) * Hq * n_splits;

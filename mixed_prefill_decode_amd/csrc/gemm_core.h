@@ -5,10 +5,12 @@
 // 32x32 MFMA blocks.  Each stage is a 128-byte slice of K per row (64 bf16 or 32
 // fp32), copied from HBM straight into an LDS ring (buffer_load ... lds: no staging
 // registers, no LDS store instructions) whose 16-byte chunks are XOR-swizzled by
-// (row & 7), so the eight lanes an LDS fragment read serves together hit eight
-// different bank groups.  The SwiGLU epilogue reads two weight tiles (gate, up)
-// against the same A tile and keeps both accumulators, so silu(g) * u is formed in
-// registers.
+// ((row >> 1) & 7).  gfx950's LDS serves a 16-byte-per-lane read 16 lanes at a time
+// across 64 four-byte banks (256 bytes): the 16 rows such a group reads are 8
+// row pairs, and a pair spans the 64 banks once, so the swizzle gives the 8 pairs
+// 8 different chunk positions and the group hits every bank exactly once.  The
+// SwiGLU epilogue reads two weight tiles (gate, up) against the same A tile and
+// keeps both accumulators, so silu(g) * u is formed in registers.
 //
 // Block order is XCD-aware: workgroups are dealt to the 8 XCDs round-robin, so
 // block b is remapped to tile (b % 8) * per_xcd + b / 8 with tiles ordered
@@ -28,7 +30,8 @@ namespace gemm {
 constexpr int kRowBytes = 128;
 constexpr int kChunks = 8;  // 16-byte chunks per LDS row
 
-__device__ __forceinline__ int swz(int row, int chunk) { return row * kChunks + (chunk ^ (row & 7)); }
+__device__ __forceinline__ int swz_of(int row) { return (row >> 1) & 7; }
+__device__ __forceinline__ int swz(int row, int chunk) { return row * kChunks + (chunk ^ swz_of(row)); }
 
 template <typename T>
 __device__ __forceinline__ void lds_frag(Frag8<T>& f, const uint4* buf, int row, int chunk);
@@ -58,8 +61,8 @@ struct Cfg {
 
 // ---------------------------------------------------------------------------
 // Loads: a wave instruction fills 8 consecutive LDS rows (64 lanes x 16 B,
-// lane-contiguous); lane l fetches global chunk (l % 8) ^ (l / 8) of its row so the
-// LDS image is the XOR-swizzled layout the fragment reads expect.  Each operand's
+// lane-contiguous); lane l fetches global chunk (l % 8) ^ swz_of(row) of its row so
+// the LDS image is the XOR-swizzled layout the fragment reads expect.  Each operand's
 // buffer resource starts at the tile's first row and covers only its valid rows, so
 // rows past M or N read as zero without any per-load check.  STAGES-deep ring:
 // stage kt + STAGES - 1 is issued right after the barrier that ends the reads of the
@@ -129,13 +132,12 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(const char* __rest
   const auto rb = rsrc_rows(B + n0 * kbytes, min(BN, N - n0), kbytes);
   const auto rb2 = rsrc_rows((NB == 2 ? B2 : B) + n0 * kbytes, min(BN, N - n0), kbytes);
   const int lrow = lane >> 3;
-  const int lchunk = (lane & 7) ^ lrow;  // 8-row groups start at multiples of 8
 
   auto issue = [&](int kt, int buf) {
 #pragma unroll
     for (int i = 0; i < IPW; ++i) {
       const int row0 = (i * W + wave) * 8;   // wave-uniform
-      const int off = kt * kRowBytes + lchunk * 16;
+      const int off = kt * kRowBytes + (((lane & 7) ^ swz_of(row0 + lrow)) << 4);
       const uint32_t dst = __builtin_amdgcn_readfirstlane(
           uint32_t(reinterpret_cast<uintptr_t>(&lds[buf][row0 * kChunks])));
       if (row0 < BM) {

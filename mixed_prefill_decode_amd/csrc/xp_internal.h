@@ -65,6 +65,7 @@ xp_status launch_kv_gather(int dtype, const void* pool, int n_pages, int S, int 
                            void* v_out, hipStream_t s);
 
 int decode_splits(int dec_max_blocks, int pages_per_split);
+int decode_pick_pps(int requested, int n_d, int Hkv, int dec_max_blocks);
 size_t decode_ws_bytes(int n_d, int Hq, int d, int n_splits);
 xp_status launch_decode(int dtype, const void* q, const void* pool, int n_pages, int S,
                         const int32_t* dec_pages, int dec_max_blocks, const int32_t* dec_ctx, int n_d,

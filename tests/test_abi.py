@@ -147,7 +147,24 @@ def test_workspace_layout_is_host_only_and_consistent():
         offs = sorted((v, k) for k, v in L.items() if k not in ("total", "dec_splits", "dec_pages_per_split"))
         assert all(o % 256 == 0 for o, _ in offs)
         assert offs[-1][0] < L["total"]
-        assert L["dec_splits"] == -(-dmb // 32)
+        pps = L["dec_pages_per_split"]
+        assert 8 <= pps <= 64
+        assert L["dec_splits"] == -(-dmb // pps)
+        # the per-batch choice grows with the decode work and saturates at 64
+        expect = min(64, max(8, wl.n_decode * wl.n_kv_heads * dmb // 1600))
+        assert pps == expect, (name, pps, expect)
+
+
+def test_decode_workspace_size_matches_layer_layout():
+    # host-only: the kernel-level size for a split choice equals the layer layout's regions
+    wl = get_workload("C2")
+    for pps in (0, 1, 8, 64):
+        n = X.xp_decode_workspace_size(wl.n_decode, wl.n_q_heads, wl.n_kv_heads, wl.head_dim, 513, pps)
+        splits = -(-513 // (pps or min(64, max(8, wl.n_decode * wl.n_kv_heads * 513 // 1600))))
+        units = wl.n_decode * wl.n_q_heads * splits
+        assert n == -(-units * 8 // 256) * 256 + -(-units * wl.head_dim * 4 // 256) * 256
+    assert X.xp_decode_workspace_size(0, 8, 2, 128, 10, 0) == 0
+    assert X.xp_decode_workspace_size(4, 8, 2, 128, 10, -1) == 0
 
 
 def test_gemm_rejects_unsupported_k_before_launching():

@@ -153,7 +153,7 @@ def test_kv_append_and_gather_bit_exact(name):
 
 
 @pytest.mark.parametrize("name", ["P1", "P2", "P3", "E1", "C1", "E3"])
-@pytest.mark.parametrize("pps", [1, 5, 32])
+@pytest.mark.parametrize("pps", [0, 1, 5, 32, 64])
 def test_decode_attention(name, pps):
     inst = make_instance(get_workload(name))
     wl, dt = inst.wl, inst.wl.dtype
@@ -164,7 +164,7 @@ def test_decode_attention(name, pps):
     q = _rand(rng, (wl.n_decode, wl.n_q_heads, wl.head_dim), dt)
     tdt = torch.bfloat16 if dt == "bf16" else torch.float32
     out = torch.full((wl.n_decode, wl.n_q_heads * wl.head_dim), float("nan"), dtype=tdt, device="cuda")
-    ws = torch.empty(X.xp_decode_workspace_size(wl.n_decode, wl.n_q_heads, wl.head_dim, inst.dec_max_blocks, pps),
+    ws = torch.empty(X.xp_decode_workspace_size(wl.n_decode, wl.n_q_heads, wl.n_kv_heads, wl.head_dim, inst.dec_max_blocks, pps),
                      dtype=torch.uint8, device="cuda")
     X.xp_decode_attention(DT[dt], to_device(q, dt), dpool, inst.pool.n_pages, wl.page_size,
                           to_device(inst.dec_pages, "i32"), inst.dec_max_blocks, to_device(inst.dec_ctx, "i32"),
@@ -241,7 +241,7 @@ def test_decode_token_matches_prefill_row_on_gpu():
         tables = np.repeat(inst.pre_pages[g:g + 1][None], len(rows), axis=0)           # [n, 1, blocks]
         ctx = (wl.prior_len + np.array(rows)).astype(np.int32)
         out_d = torch.empty((len(rows), G * d), dtype=torch.bfloat16, device="cuda")
-        ws = torch.empty(X.xp_decode_workspace_size(len(rows), G, d, tables.shape[2], 4), dtype=torch.uint8,
+        ws = torch.empty(X.xp_decode_workspace_size(len(rows), G, 1, d, tables.shape[2], 4), dtype=torch.uint8,
                          device="cuda")
         X.xp_decode_attention(DT[dt], to_device(qd, dt), dpool, inst.pool.n_pages, wl.page_size,
                               to_device(tables, "i32"), tables.shape[2], to_device(ctx, "i32"), len(rows), G, 1, d,
