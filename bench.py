@@ -311,6 +311,22 @@ def kernel_only(args, X, torch, inst, step, dev, timer):
     if args.kernel_only == "swiglu":
         fn = lambda: X.xp_gemm(X.XP_BF16, X.XP_EPI_SWIGLU, ws + lay.hn, w["w_gate"], w["w_up"], None, ws + lay.act,
                                wl.n_rows, wl.ffn_dim, wl.hidden)
+    elif args.kernel_only == "prefill":
+        hq, d = wl.hq_loc, wl.head_dim
+        pout = torch.empty((wl.chunk_len, hq * d), dtype=torch.bfloat16, device="cuda")
+        fn = lambda: X.xp_prefill_attention(X.XP_BF16, ws + lay.q_pre, dev.pool, inst.pool.n_pages, wl.page_size,
+                                            dev.pre_pages, inst.pre_max_blocks, hq, wl.hkv_loc, d, wl.prior_len,
+                                            wl.chunk_len, 0, wl.chunk_len, pout, hq * d, None, hq * d,
+                                            ws + lay.pre_part)
+    elif args.kernel_only == "decode":
+        dws = torch.empty(X.xp_decode_workspace_size(wl.n_decode, wl.n_q_heads, wl.n_kv_heads, wl.head_dim,
+                                                     inst.dec_max_blocks, lay.dec_pages_per_split),
+                          dtype=torch.uint8, device="cuda")
+        dout = torch.empty((wl.n_decode, wl.n_q_heads * wl.head_dim), dtype=torch.bfloat16, device="cuda")
+        fn = lambda: X.xp_decode_attention(X.XP_BF16, ws + lay.q_dec, dev.pool, inst.pool.n_pages, wl.page_size,
+                                           dev.dec_pages, inst.dec_max_blocks, dev.dec_ctx, wl.n_decode,
+                                           wl.n_q_heads, wl.n_kv_heads, wl.head_dim, dout,
+                                           wl.n_q_heads * wl.head_dim, dws, lay.dec_pages_per_split)
     elif args.kernel_only == "copy":
         src = torch.empty(1 << 28, dtype=torch.float32, device="cuda").fill_(1.0)   # 1 GiB
         dst = torch.empty_like(src)

@@ -5,28 +5,32 @@
 // inclusive causal mask of Adaptive Context Parallelism §2.1).  All keys are
 // read from the paged pool: the chunk's own K/V were appended before.
 //
-// Work decomposition: a workgroup owns one KV head g, one 32-query tile and one
-// split of the tile's key range (`bps` 32-key blocks), with one wave per query
-// head of g's GQA group (up to 8), so each K/V block is read from HBM once for
-// the whole group.  Blocks (two pages: 8 KB of K rows + 8 KB of V^T rows for
-// d = 128) are copied straight into a 3-stage LDS ring with buffer_load ... lds;
-// K rows are stored with their 16-byte chunks XOR-swizzled by (key & 15) so the
-// eight keys an LDS read serves together hit different banks.  Splitting the key
-// range gives long prior contexts enough workgroups; a tile whose keys fit in one
-// split writes its output directly, the others write fp32 (max, sum, output)
-// partials that `prefill_combine_kernel` merges (the log-sum-exp merge of Decode
-// Token Parallelism Eq. 4).
+// Work decomposition: a workgroup owns one KV head g, one query tile of 32*NQ
+// chunk rows and one split of the tile's key range (`bps` 32-key blocks), with
+// one wave per query head of g's GQA group (up to 8), so each K/V block is read
+// from HBM once for the whole group.  A wave covers the whole query tile for its
+// head, as NQ 32-query MFMA column blocks: every K or V fragment it reads from
+// LDS feeds NQ MFMAs, and the NQ accumulation chains are independent.  Blocks
+// (two pages: 8 KB of K rows + 8 KB of V^T rows for d = 128 bf16) are copied
+// straight into a 3-stage LDS ring with buffer_load ... lds.  gfx950's LDS serves
+// 16-byte reads 16 lanes at a time over 64 banks (256 bytes), and both planes are
+// XOR-swizzled in 16-byte chunks so those 16 lanes -- 16 keys of a K read, 16 dim
+// rows of a V^T read -- land on distinct banks.  Splitting the key range gives
+// long prior contexts enough workgroups; a tile whose keys fit in one split
+// writes its output directly, the others write fp32 (max, sum, output) partials
+// that `prefill_combine_kernel` merges (the log-sum-exp merge of Decode Token
+// Parallelism Eq. 4).
 //
-// Per wave and block, 32x32 MFMA tiles:
-//   S^T[32 keys x 32 queries] = K[32 x d] . Q^T[d x 32]      (16-deep k steps)
-//   O^T[d x 32 queries]     += V^T[d x 32 keys] . P^T        (16-deep k steps)
-// Queries are the MFMA columns, so lane l owns query l % 32 for both the scores
-// and the output: the row max needs one exchange with lane l ^ 32 and the
-// rescale is per lane.  Row i of the K operand holds key kappa(i) of the block
-// (bits 2 and 3 of i swapped), which makes accumulator elements 0..7 of lane l
-// the keys 8*(l/32) .. +7 of the first page and elements 8..15 the same slots of
-// the second page -- exactly the k-slots the PV step's P operand supplies, and
-// the V^T operand is then 8 consecutive slots of one dim row (16 bytes for bf16).
+// Per wave, block and query column block j, 32x32 MFMA tiles:
+//   S^T[32 keys x 32 queries] = K[32 x d] . Q_j^T[d x 32]      (16-deep k steps)
+//   O_j^T[d x 32 queries]   += V^T[d x 32 keys] . P_j^T        (16-deep k steps)
+// Queries are the MFMA columns, so lane l owns query l % 32 of each column block
+// for both the scores and the output: the row max needs one exchange with lane
+// l ^ 32 and the rescale is per lane.  Row i of the K operand holds key kappa(i)
+// of the block (bits 2 and 3 of i swapped), which makes accumulator elements
+// 0..7 of lane l the keys 8*(l/32) .. +7 of the first page and elements 8..15 the
+// same slots of the second page -- exactly the k-slots the PV step's P operand
+// supplies, and the V^T operand is then 8 consecutive slots of one dim row.
 #include "gemm_core.h"
 #include "xp_device.h"
 #include "xp_internal.h"
@@ -36,8 +40,23 @@ namespace xp {
 namespace {
 
 constexpr int kPage = 16;
-constexpr int kMaxWaves = 8;
-constexpr int kStages = 3;
+#ifndef XP_PREFILL_NQ
+#define XP_PREFILL_NQ 1
+#endif
+#ifndef XP_PREFILL_TARGET_WAVES
+#define XP_PREFILL_TARGET_WAVES 8192
+#endif
+#ifndef XP_PREFILL_MAXW
+#define XP_PREFILL_MAXW 8
+#endif
+#ifndef XP_PREFILL_STAGES
+#define XP_PREFILL_STAGES 2
+#endif
+constexpr int kStages = XP_PREFILL_STAGES;
+#ifndef XP_PREFILL_SB
+#define XP_PREFILL_SB 2
+#endif
+constexpr int kBlocksPerStage = XP_PREFILL_SB;
 constexpr int kMaxBps = 256;   // key blocks per split (its page ids are staged in LDS)
 
 __device__ __forceinline__ int kappa(int i) { return (i & ~12) | ((i & 4) << 1) | ((i & 8) >> 1); }
@@ -60,10 +79,45 @@ __device__ __forceinline__ void zero_from(Frag8<float>& f, int nvalid) {
   if (nvalid <= 7) f.hi.w = 0.f;
 }
 
-// K rows are stored with 16-byte chunk c of key k at position c ^ (k & (chunks - 1)).
+// log2-domain margin by which a row maximum may exceed the softmax reference
+// before O and l are rescaled
+constexpr float kLazy = 8.0f;
+
+// Packs 8 weights into a PV operand fragment (rounding them to the operand type)
+// and returns the sum of the rounded weights, so the normaliser sums exactly the
+// weights the PV product uses.
+__device__ __forceinline__ float pack_and_sum(Frag8<bf16_t>& f, const float* p) {
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  set_frag8(f, p);
+  const bf16x2 one2 = __builtin_bit_cast(bf16x2, 0x3f803f80u);
+  float s = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, f.v.x), one2, 0.f, false);
+  s = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, f.v.y), one2, s, false);
+  s = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, f.v.z), one2, s, false);
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, f.v.w), one2, s, false);
+}
+__device__ __forceinline__ float pack_and_sum(Frag8<float>& f, const float* p) {
+  set_frag8(f, p);
+  return ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
+}
+
+// LDS plane swizzles (16-byte chunks).  K plane: rows of KROW_CH chunks, one per
+// key; key k's chunk c sits at c ^ kswz(k), where keys that share a 256-byte
+// bank line (two for 128-byte rows) get the same value and the next 16 keys
+// distinct ones.  V^T plane: rows of VROW_CH chunks, one per dim; dim row r's
+// chunk c sits at c ^ vswz(r), which alternates every 256 bytes of rows.
+template <int KROW_CH>
+__device__ __forceinline__ int kswz(int k) {
+  constexpr int ROWS256 = KROW_CH >= 16 ? 1 : 16 / KROW_CH;   // K rows per 256-byte bank line
+  return (k / ROWS256) & (KROW_CH - 1);
+}
+template <int VROW_CH>
+__device__ __forceinline__ int vswz(int r) {
+  constexpr int ROWS256 = 16 / VROW_CH;                       // V^T rows per 256-byte bank line
+  return (r / ROWS256) & (VROW_CH - 1);
+}
 template <int KROW_CH>
 __device__ __forceinline__ const uint4* kchunk(const char* plane, int k, int c, int row_bytes) {
-  return reinterpret_cast<const uint4*>(plane + k * row_bytes + ((c ^ (k & (KROW_CH - 1))) & (KROW_CH - 1)) * 16);
+  return reinterpret_cast<const uint4*>(plane + k * row_bytes + (c ^ kswz<KROW_CH>(k)) * 16);
 }
 template <int KROW_CH>
 __device__ __forceinline__ void kfrag(Frag8<bf16_t>& f, const char* plane, int k, int elem0, int row_bytes) {
@@ -74,6 +128,16 @@ __device__ __forceinline__ void kfrag(Frag8<float>& f, const char* plane, int k,
   const int c = elem0 * 4 / 16;
   f.lo = __builtin_bit_cast(float4, *kchunk<KROW_CH>(plane, k, c, row_bytes));
   f.hi = __builtin_bit_cast(float4, *kchunk<KROW_CH>(plane, k, c + 1, row_bytes));
+}
+// V^T fragment: 8 consecutive key slots [8*hf, 8*hf + 8) of dim row r
+template <int VROW_CH>
+__device__ __forceinline__ void vfrag(Frag8<bf16_t>& f, const char* plane, int r, int hf) {
+  f.v = *reinterpret_cast<const uint4*>(plane + (r * VROW_CH + (hf ^ vswz<VROW_CH>(r))) * 16);
+}
+template <int VROW_CH>
+__device__ __forceinline__ void vfrag(Frag8<float>& f, const char* plane, int r, int hf) {
+  f.lo = *reinterpret_cast<const float4*>(plane + (r * VROW_CH + ((2 * hf) ^ vswz<VROW_CH>(r))) * 16);
+  f.hi = *reinterpret_cast<const float4*>(plane + (r * VROW_CH + ((2 * hf + 1) ^ vswz<VROW_CH>(r))) * 16);
 }
 
 struct PrefillArgs {
@@ -92,22 +156,25 @@ struct PrefillArgs {
   int bps;        // 32-key blocks per split
   int n_split;    // splits in the grid (the longest tile's)
   int wpg;        // waves per workgroup (query heads of the group it covers)
-  float* part_ml; // [n_qt, hq, n_split, 32, 2]
-  float* part_o;  // [n_qt, hq, n_split, 32, D]
+  int qt_rows;    // queries per tile (32 * NQ)
+  float* part_ml; // [n_qt, hq, n_split, qt_rows, 2]
+  float* part_o;  // [n_qt, hq, n_split, qt_rows, D]
 };
 
-__device__ __forceinline__ void wait_vm_upto16(int n) {
-  switch (n) {
-    case 0: gemm::wait_vmcnt<0>(); break;
-    case 1: gemm::wait_vmcnt<1>(); break;
-    case 2: gemm::wait_vmcnt<2>(); break;
-    case 3: gemm::wait_vmcnt<3>(); break;
-    case 4: gemm::wait_vmcnt<4>(); break;
-    case 5: gemm::wait_vmcnt<5>(); break;
-    case 6: gemm::wait_vmcnt<6>(); break;
-    case 7: gemm::wait_vmcnt<7>(); break;
-    default: gemm::wait_vmcnt<8>(); break;
+// s_waitcnt vmcnt(min(n, 63)) for a wave-uniform n (gfx950's counter holds 6 bits;
+// a larger n waits for more than necessary, never less)
+__device__ __forceinline__ void wait_vm_le(int n) {
+#define XP_VM_CASE(k) \
+  case k: gemm::wait_vmcnt<k>(); break;
+#define XP_VM_CASE8(k) XP_VM_CASE(k) XP_VM_CASE(k + 1) XP_VM_CASE(k + 2) XP_VM_CASE(k + 3) \
+  XP_VM_CASE(k + 4) XP_VM_CASE(k + 5) XP_VM_CASE(k + 6) XP_VM_CASE(k + 7)
+  switch (n < 63 ? n : 63) {
+    XP_VM_CASE8(0) XP_VM_CASE8(8) XP_VM_CASE8(16) XP_VM_CASE8(24)
+    XP_VM_CASE8(32) XP_VM_CASE8(40) XP_VM_CASE8(48) XP_VM_CASE8(56)
+    default: gemm::wait_vmcnt<0>(); break;
   }
+#undef XP_VM_CASE8
+#undef XP_VM_CASE
 }
 
 // output row pointer of chunk row t (local rows and peer rows go to different buffers)
@@ -121,31 +188,40 @@ __device__ __forceinline__ void out_row(const PrefillArgs& a, int t, void*& dst,
   }
 }
 
-template <typename T, int D>
-__global__ __launch_bounds__(64 * kMaxWaves) void prefill_kernel(PrefillArgs a) {
+template <typename T, int D, int NQ, int MAXW>
+__global__ __launch_bounds__(64 * MAXW) void prefill_kernel(PrefillArgs a) {
   constexpr int EB = St<T>::bytes;
+  constexpr int QT = 32 * NQ;                     // queries per tile
   constexpr int PLANE = kPage * D * EB;           // bytes of one K or V plane of a page
   constexpr long PAGE_BYTES = 2L * PLANE;
-  constexpr int STAGE = 4 * PLANE;                // K_A | K_B | V_A | V_B
+  constexpr int BLK = 4 * PLANE;                  // one 32-key block: K_A | K_B | V_A | V_B
   constexpr int CH_PER_PLANE = PLANE / 16;        // 16-byte chunks per plane
-  constexpr int INSTR = 4 * CH_PER_PLANE / 64;    // 64-lane load instructions per stage
+  constexpr int INSTR_BLK = 4 * CH_PER_PLANE / 64;  // 64-lane load instructions per block
   constexpr int KROW_CH = D * EB / 16;            // 16-byte chunks per K row
-  constexpr int VROW_B = kPage * EB;              // bytes per V^T row of a page
-  __shared__ uint4 ring[kStages][STAGE / 16];
+  constexpr int VROW_CH = kPage * EB / 16;        // 16-byte chunks per V^T row
+  // blocks per stage and ring depth, within the LDS budget
+  constexpr int kBudget = 144 * 1024;
+  constexpr int SB = kBlocksPerStage * kStages * BLK <= kBudget
+                         ? kBlocksPerStage
+                         : (kBudget / (kStages * BLK) > 0 ? kBudget / (kStages * BLK) : 1);
+  constexpr int NST = kStages * SB * BLK <= kBudget ? kStages : (kBudget / (SB * BLK) > 2 ? kBudget / (SB * BLK) : 2);
+  constexpr int STAGE = SB * BLK;
+  constexpr int INSTR = SB * INSTR_BLK;           // load instructions per stage
+  __shared__ uint4 ring[NST][STAGE / 16];
   __shared__ int32_t pids[2 * kMaxBps];
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int G = a.hq / a.hkv;
-  const int n_qt = (a.chunk + 31) / 32;
+  const int n_qt = (a.chunk + QT - 1) / QT;
   const int qt = n_qt - 1 - int(blockIdx.x) / a.n_split;   // longest tiles first
   const int s = int(blockIdx.x) % a.n_split;
   const int groups_per_kv = (G + a.wpg - 1) / a.wpg;
   const int g = int(blockIdx.y) / groups_per_kv;
   const int h0 = g * G + (int(blockIdx.y) % groups_per_kv) * a.wpg;   // first query head of this workgroup
   const int waves = min(a.wpg, g * G + G - h0);
-  const int t0 = qt * 32;
-  const int q_last = min(t0 + 31, a.chunk - 1);
+  const int t0 = qt * QT;
+  const int q_last = min(t0 + QT - 1, a.chunk - 1);
   const int n_keys = a.prior + a.chunk;                     // keys in the table
   const int nkb = (a.prior + q_last + 1 + 31) / 32;         // key blocks this tile needs
   const int kb0 = s * a.bps;
@@ -156,191 +232,257 @@ __global__ __launch_bounds__(64 * kMaxWaves) void prefill_kernel(PrefillArgs a) 
   const int h = h0 + (active ? wave : 0);
   const int32_t* tbl = a.pre_pages + long(g) * a.pre_max_blocks;
 
-  // The split's page ids, staged once: table reads inside the pipeline would be vector
-  // loads, and waiting for one of them would also wait for every ring load before it.
+  // The split's page ids, staged once and validated: table reads inside the pipeline
+  // would be vector loads, and waiting for one of them would also wait for every
+  // ring load before it.  An id outside the pool is staged as -1 (its page then
+  // reads as zeros) and flags the workgroup.
+  __shared__ int bad_s;
+  if (threadIdx.x == 0) bad_s = 0;
+  __syncthreads();
   const int n_tbl = (n_keys + kPage - 1) / kPage;
   for (int i = int(threadIdx.x); i < 2 * (kb1 - kb0); i += int(blockDim.x)) {
     const int b = 2 * kb0 + i;
-    pids[i] = b < n_tbl ? tbl[b] : -1;
+    const int pid = b < n_tbl ? tbl[b] : -1;
+    const bool ok = pid >= 0 && pid < a.n_pages;
+    if (b < n_tbl && !ok) bad_s = 1;
+    pids[i] = ok ? pid : -1;
   }
   __syncthreads();
+  const bool bad = bad_s != 0;
 
-  // my load instructions per stage: i = wave, wave + waves, ...
-  const int my_instr = wave < waves ? (INSTR - wave + waves - 1) / waves : 0;
-  bool bad = false;
-  auto issue = [&](int kb, int buf) {
-    if (wave >= waves) return;
-    const int key0 = kb * 32;
-    const int pa = __builtin_amdgcn_readfirstlane(pids[2 * (kb - kb0)]);
-    const bool has_b = key0 + kPage < n_keys;
-    const int pb = has_b ? __builtin_amdgcn_readfirstlane(pids[2 * (kb - kb0) + 1]) : -1;
-    const bool ok_a = pa >= 0 && pa < a.n_pages;
-    const bool ok_b = pb >= 0 && pb < a.n_pages;
-    if (!ok_a || (has_b && !ok_b)) bad = true;
-    const gemm::i32x4 ra = gemm::rsrc_rows(a.pool + (ok_a ? long(pa) : 0L) * PAGE_BYTES, ok_a ? 1 : 0, PAGE_BYTES);
-    const gemm::i32x4 rb = gemm::rsrc_rows(a.pool + (ok_b ? long(pb) : 0L) * PAGE_BYTES, ok_b ? 1 : 0, PAGE_BYTES);
-    for (int i = wave; i < INSTR; i += waves) {
+  // Loads are issued a whole block at a time by one wave: block b of every stage by
+  // wave b % waves, so its page resources are set up once and its 64-lane load
+  // instructions have fixed LDS destinations.  Blocks past the split load through
+  // empty resources (moving no data), so each wave issues the same number of
+  // instructions for every stage and the wait counts below are exact.
+  int my_blocks = 0;
+  for (int b = wave; b < SB; b += waves) ++my_blocks;
+  const int my_instr = wave < waves ? my_blocks * INSTR_BLK : 0;   // per stage
+  auto issue_block = [&](int sg, int b, int buf) {
+    const int kb = kb0 + sg * SB + b;
+    const bool in = kb < kb1;
+    const int2 pp = in ? *reinterpret_cast<const int2*>(&pids[2 * (kb - kb0)]) : make_int2(-1, -1);
+    const int pa = __builtin_amdgcn_readfirstlane(pp.x), pb = __builtin_amdgcn_readfirstlane(pp.y);
+    const gemm::i32x4 ra = gemm::rsrc_rows(a.pool + (pa >= 0 ? long(pa) : 0L) * PAGE_BYTES, pa >= 0 ? 1 : 0, PAGE_BYTES);
+    const gemm::i32x4 rb = gemm::rsrc_rows(a.pool + (pb >= 0 ? long(pb) : 0L) * PAGE_BYTES, pb >= 0 ? 1 : 0, PAGE_BYTES);
+    const uint32_t dst0 = __builtin_amdgcn_readfirstlane(uint32_t(reinterpret_cast<uintptr_t>(&ring[buf][(b * BLK) / 16])));
+#pragma unroll
+    for (int i = 0; i < INSTR_BLK; ++i) {
       const int region = i / (CH_PER_PLANE / 64);         // 0 K_A, 1 K_B, 2 V_A, 3 V_B
       const int p = (i % (CH_PER_PLANE / 64)) * 64 + lane;  // chunk position inside the plane
       int src;
       if (region < 2) {
-        const int row = p / KROW_CH, c = (p % KROW_CH) ^ (row & (KROW_CH - 1));
+        const int row = p / KROW_CH, c = (p % KROW_CH) ^ kswz<KROW_CH>(row);
         src = row * (D * EB) + c * 16;
       } else {
-        src = PLANE + p * 16;
+        const int row = p / VROW_CH, c = (p % VROW_CH) ^ vswz<VROW_CH>(row);
+        src = PLANE + (row * VROW_CH + c) * 16;
       }
-      const uint32_t dst = __builtin_amdgcn_readfirstlane(
-          uint32_t(reinterpret_cast<uintptr_t>(&ring[buf][region * CH_PER_PLANE + (i % (CH_PER_PLANE / 64)) * 64])));
-      gemm::load_lds16((region & 1) ? rb : ra, dst, src);
+      gemm::load_lds16((region & 1) ? rb : ra, dst0 + (region * CH_PER_PLANE + (i % (CH_PER_PLANE / 64)) * 64) * 16, src);
     }
   };
 
   const int ql = lane & 31, hf = lane >> 5;
-  const int t = t0 + ql;
-  const bool qvalid = t < a.chunk;
-  const int qpos = a.prior + min(t, a.chunk - 1);
 
-  Frag8<T> qf[D / 16];
-  const char* qrow = static_cast<const char*>(a.q) + (long(h) * a.chunk + min(t, a.chunk - 1)) * D * EB;
+  Frag8<T> qf[NQ][D / 16];
 #pragma unroll
-  for (int st = 0; st < D / 16; ++st) load_frag8(qf[st], qrow + (16 * st + 8 * hf) * EB);
+  for (int j = 0; j < NQ; ++j) {
+    const char* qrow = static_cast<const char*>(a.q) + (long(h) * a.chunk + min(t0 + 32 * j + ql, a.chunk - 1)) * D * EB;
+#pragma unroll
+    for (int st = 0; st < D / 16; ++st) load_frag8(qf[j][st], qrow + (16 * st + 8 * hf) * EB);
+  }
   // Settle these loads before any ring load is issued: the compiler waits for them at
   // their first use inside the loop, and with in-order completion such a wait would
   // also drain the ring stages in flight.
   gemm::wait_vmcnt<0>();
 
-  f32x16 o[D / 32];
+  f32x16 o[NQ][D / 32];
+  float ms[NQ], lsum[NQ];
 #pragma unroll
-  for (int n = 0; n < D / 32; ++n) o[n] = f32x16{};
-  float m = -__builtin_inff(), lsum = 0.f;
+  for (int j = 0; j < NQ; ++j) {
+#pragma unroll
+    for (int n = 0; n < D / 32; ++n) o[j][n] = f32x16{};
+    ms[j] = -__builtin_inff();
+    lsum[j] = 0.f;
+  }
 
-  issue(kb0, 0);
-  if (kb0 + 1 < kb1) issue(kb0 + 1, 1);
+  // stages 0 .. NST - 2 in flight before the first one is consumed; stage
+  // sg + NST - 1 is then issued block by block while stage sg is consumed, into the
+  // ring slot every wave finished reading before the barrier that opened stage sg
+  const int n_sg = (kb1 - kb0 + SB - 1) / SB;
+#pragma unroll
+  for (int i = 0; i < NST - 1; ++i)
+    if (i < n_sg && wave < waves)
+      for (int b = wave; b < SB; b += waves) issue_block(i, b, i);
   const int krow = kappa(ql);
-  for (int kb = kb0; kb < kb1; ++kb) {
-    const int it = kb - kb0;
-    if (kb + 1 < kb1) wait_vm_upto16(my_instr);
-    else gemm::wait_vmcnt<0>();
+  for (int sg = 0; sg < n_sg; ++sg) {
+    // stage sg has landed once no more than the later stages' loads are outstanding
+    wait_vm_le(min(NST - 2, n_sg - 1 - sg) * my_instr);
     __builtin_amdgcn_s_barrier();
-    if (kb + 2 < kb1) issue(kb + 2, (it + 2) % kStages);
-    if (!active) continue;
-    const char* st_base = reinterpret_cast<const char*>(ring[it % kStages]);
-    const int key0 = kb * 32;
-    // S^T = K . Q^T; K operand row ql holds key kappa(ql) of the block
-    const char* kplane = st_base + (krow < kPage ? 0 : PLANE);
-    const int kr = krow & 15;
-    f32x16 sacc = f32x16{};
+    const bool refill = sg + NST - 1 < n_sg;
+#pragma unroll 1
+    for (int b = 0; b < SB; ++b) {
+      if (refill && b % waves == wave) issue_block(sg + NST - 1, b, (sg + NST - 1) % NST);
+      const int kb = kb0 + sg * SB + b;
+      if (!active || kb >= kb1) continue;
+      const char* st_base = reinterpret_cast<const char*>(ring[sg % NST]) + b * BLK;
+      const int key0 = kb * 32;
+      // All K fragments of the block are read up front, then the V^T fragments right
+      // after the QK MFMAs are issued, so the LDS latency hides behind MFMAs and the
+      // softmax instead of stalling each MFMA on its own read.
+      const char* kplane = st_base + (krow < kPage ? 0 : PLANE);
+      const int kr = krow & 15;
+      Frag8<T> kf[D / 16];
 #pragma unroll
-    for (int st = 0; st < D / 16; ++st) {
-      Frag8<T> kf;
-      kfrag<KROW_CH>(kf, kplane, kr, 16 * st + 8 * hf, D * EB);
-      mma32x32_k16(sacc, kf, qf[st]);
-    }
-    // element r: key key0 + 16*(r/8) + 8*hf + r%8
-    float sv[16];
-    float mb = -__builtin_inff();
+      for (int st = 0; st < D / 16; ++st) kfrag<KROW_CH>(kf[st], kplane, kr, 16 * st + 8 * hf, D * EB);
+      // S^T = K . Q^T; K operand row ql holds key kappa(ql) of the block
+      f32x16 sacc[NQ];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int kpos = key0 + 16 * (r >> 3) + 8 * hf + (r & 7);
-      sv[r] = (kpos <= qpos) ? sacc[r] * a.scale_log2 : -__builtin_inff();
-      mb = fmaxf(mb, sv[r]);
-    }
-    mb = fmaxf(mb, shfl_xor(mb, 32));
-    const float mn = fmaxf(m, mb);
-    const float mref = (mn == -__builtin_inff()) ? 0.f : mn;
-    const float alpha = fast_exp2(m - mref);
-    float p[16];
-    float ps = 0.f;
+      for (int j = 0; j < NQ; ++j) sacc[j] = f32x16{};
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      p[r] = round_st<T>(fast_exp2(sv[r] - mref));
-      ps += p[r];
-    }
-    lsum = lsum * alpha + ps;
-    m = mn;
+      for (int st = 0; st < D / 16; ++st)
 #pragma unroll
-    for (int n = 0; n < D / 32; ++n) o[n] *= alpha;
+        for (int j = 0; j < NQ; ++j) mma32x32_k16(sacc[j], kf[st], qf[j][st]);
+      Frag8<T> vf[2][D / 32];
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      Frag8<T> pf;
-      set_frag8(pf, &p[8 * u]);
-      const char* vplane = st_base + (2 + u) * PLANE;
-      const int nvalid = n_keys - (key0 + 16 * u + 8 * hf);   // slots at or past the table end hold no key
+      for (int u = 0; u < 2; ++u)
 #pragma unroll
-      for (int n = 0; n < D / 32; ++n) {
-        Frag8<T> vf;
-        load_frag8(vf, vplane + (32 * n + ql) * VROW_B + 8 * hf * EB);
-        if (nvalid < 8) zero_from(vf, nvalid);
-        mma32x32_k16(o[n], vf, pf);
+        for (int n = 0; n < D / 32; ++n) vfrag<VROW_CH>(vf[u][n], st_base + (2 + u) * PLANE, 32 * n + ql, hf);
+      // issue order: the K reads, the QK MFMAs, then the V^T reads
+      constexpr int KREADS = (D / 16) * (sizeof(Frag8<T>) / 16), VREADS = D / 16 * (sizeof(Frag8<T>) / 16);
+      __builtin_amdgcn_sched_group_barrier(0x100, KREADS, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, NQ * (D / 16) * (sizeof(Frag8<T>) / 16 == 2 ? 8 : 1), 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, VREADS, 0);
+
+      // Online softmax in the exp2 domain with a lazily moved reference: ms is the
+      // row maximum (scaled) a rescale last set, and the weights exp2(s c - ms) stay
+      // below 2^kLazy while no new score exceeds ms by more than kLazy, so O and l
+      // are rescaled only when some row of the wave crosses that margin (the result
+      // is the same function of the scores; only the rounding points move).  Only
+      // blocks that cross the causal diagonal are masked.
+      const bool masked = key0 + 31 > a.prior + t0;       // uniform over the wave
+      Frag8<T> pf[NQ][2];   // the weights as PV operands: slots 8u .. 8u + 7 of the block
+#pragma unroll
+      for (int j = 0; j < NQ; ++j) {
+        // element r: key key0 + 16*(r/8) + 8*hf + r%8 for query t0 + 32 j + ql
+        float sv[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sv[r] = sacc[j][r];
+        if (masked) {
+          const int lim = a.prior + min(t0 + 32 * j + ql, a.chunk - 1) - (key0 + 8 * hf);
+#pragma unroll
+          for (int r = 0; r < 16; ++r) sv[r] = (16 * (r >> 3) + (r & 7) > lim) ? -__builtin_inff() : sv[r];
+        }
+        float mb = fmaxf(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])), fmaxf(fmaxf(sv[4], sv[5]), fmaxf(sv[6], sv[7])));
+        mb = fmaxf(mb, fmaxf(fmaxf(fmaxf(sv[8], sv[9]), fmaxf(sv[10], sv[11])),
+                             fmaxf(fmaxf(sv[12], sv[13]), fmaxf(sv[14], sv[15]))));
+        mb = fmaxf(mb, shfl_xor(mb, 32)) * a.scale_log2;
+        if (__builtin_amdgcn_ballot_w64(mb > ms[j] + kLazy) != 0) {
+          const float mn = fmaxf(ms[j], mb);
+          const float alpha = ms[j] == -__builtin_inff() ? 0.f : fast_exp2(ms[j] - mn);
+          ms[j] = mn;
+          lsum[j] *= alpha;
+#pragma unroll
+          for (int n = 0; n < D / 32; ++n) o[j][n] *= alpha;
+        }
+        const float mref = ms[j] == -__builtin_inff() ? 0.f : ms[j];
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          float pu[8];
+#pragma unroll
+          for (int r = 0; r < 8; ++r) pu[r] = fast_exp2(__builtin_fmaf(sv[8 * u + r], a.scale_log2, -mref));
+          lsum[j] += pack_and_sum(pf[j][u], pu);
+        }
       }
+      // slots at or past the table end hold no key (their V^T columns may hold
+      // anything, including NaN): only the last block of the table has them
+      if (key0 + 32 > n_keys) {
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
+#pragma unroll
+          for (int n = 0; n < D / 32; ++n) zero_from(vf[u][n], n_keys - (key0 + 16 * u + 8 * hf));
+      }
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int n = 0; n < D / 32; ++n)
+#pragma unroll
+          for (int j = 0; j < NQ; ++j) mma32x32_k16(o[j][n], vf[u][n], pf[j][u]);
     }
   }
   if (bad && a.status && lane == 0 && wave == 0) atomicOr(a.status, XP_DEV_BAD_PAGE);
   if (!active) return;
-  lsum += shfl_xor(lsum, 32);
-  if (ns == 1) {
-    if (!qvalid) return;
-    const float inv = bad ? __builtin_nanf("") : 1.0f / lsum;
-    void* dst;
-    long row_off;
-    out_row(a, t, dst, row_off);
-    const long base = row_off + long(h) * D;
-    // element r of o[n]: dim 32*n + 8*(r/4) + 4*hf + r%4
+#pragma unroll
+  for (int j = 0; j < NQ; ++j) {
+    const int t = t0 + 32 * j + ql;
+    const float ls = lsum[j] + shfl_xor(lsum[j], 32);
+    if (ns == 1) {
+      if (t >= a.chunk) continue;
+      const float inv = bad ? __builtin_nanf("") : 1.0f / ls;
+      void* dst;
+      long row_off;
+      out_row(a, t, dst, row_off);
+      const long base = row_off + long(h) * D;
+      // element r of o[j][n]: dim 32*n + 8*(r/4) + 4*hf + r%4
+#pragma unroll
+      for (int n = 0; n < D / 32; ++n)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          St<T>::store(dst, base + 32 * n + 8 * (r >> 2) + 4 * hf + (r & 3), o[j][n][r] * inv);
+      continue;
+    }
+    const long unit = ((long(qt) * a.hq + h) * a.n_split + s) * QT + 32 * j + ql;
+    if (hf == 0) {
+      a.part_ml[2 * unit] = bad ? __builtin_nanf("") : ms[j];
+      a.part_ml[2 * unit + 1] = ls;
+    }
+    float* po = a.part_o + unit * D;
 #pragma unroll
     for (int n = 0; n < D / 32; ++n)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) St<T>::store(dst, base + 32 * n + 8 * (r >> 2) + 4 * hf + (r & 3), o[n][r] * inv);
-    return;
+      for (int r4 = 0; r4 < 4; ++r4)
+        *reinterpret_cast<float4*>(po + 32 * n + 8 * r4 + 4 * hf) =
+            make_float4(o[j][n][4 * r4], o[j][n][4 * r4 + 1], o[j][n][4 * r4 + 2], o[j][n][4 * r4 + 3]);
   }
-  const long unit = ((long(qt) * a.hq + h) * a.n_split + s) * 32 + ql;
-  if (hf == 0) {
-    a.part_ml[2 * unit] = bad ? __builtin_nanf("") : m;
-    a.part_ml[2 * unit + 1] = lsum;
-  }
-  float* po = a.part_o + unit * D;
-#pragma unroll
-  for (int n = 0; n < D / 32; ++n)
-#pragma unroll
-    for (int r4 = 0; r4 < 4; ++r4)
-      *reinterpret_cast<float4*>(po + 32 * n + 8 * r4 + 4 * hf) =
-          make_float4(o[n][4 * r4], o[n][4 * r4 + 1], o[n][4 * r4 + 2], o[n][4 * r4 + 3]);
 }
 
 // merges the split partials of the tiles that were split (scores in the exp2 domain):
 // the split weights of each query are formed once, then every thread sums float4
 // slices of the partial outputs with independent loads.
 constexpr int kMaxSplits = 64;
+constexpr int kMaxQT = 64;          // queries per tile, at most
 
 template <typename T, int D>
 __global__ __launch_bounds__(256) void prefill_combine_kernel(PrefillArgs a) {
-  __shared__ float wts[kMaxSplits][32];
+  __shared__ float wts[kMaxSplits][kMaxQT];
+  const int QT = a.qt_rows;
   const int qt = blockIdx.x, h = blockIdx.y;
-  const int q_last = min(qt * 32 + 31, a.chunk - 1);
+  const int q_last = min(qt * QT + QT - 1, a.chunk - 1);
   const int nkb = (a.prior + q_last + 1 + 31) / 32;
   const int ns = (nkb + a.bps - 1) / a.bps;
   if (ns <= 1) return;
-  const long u0 = ((long(qt) * a.hq + h) * a.n_split) * 32;   // unit of (split 0, query 0)
-  if (threadIdx.x < 32) {
+  const long u0 = ((long(qt) * a.hq + h) * a.n_split) * QT;   // unit of (split 0, query 0)
+  if (threadIdx.x < QT) {
     const int ql = threadIdx.x;
     float mx = -__builtin_inff();
-    for (int s = 0; s < ns; ++s) mx = fmaxf(mx, a.part_ml[2 * (u0 + s * 32 + ql)]);
+    for (int s = 0; s < ns; ++s) mx = fmaxf(mx, a.part_ml[2 * (u0 + s * QT + ql)]);
     float L = 0.f;
     for (int s = 0; s < ns; ++s) {
-      const float w = fast_exp2(a.part_ml[2 * (u0 + s * 32 + ql)] - mx);
+      const float w = fast_exp2(a.part_ml[2 * (u0 + s * QT + ql)] - mx);
       wts[s][ql] = w;
-      L += a.part_ml[2 * (u0 + s * 32 + ql) + 1] * w;
+      L += a.part_ml[2 * (u0 + s * QT + ql) + 1] * w;
     }
     const float inv = 1.0f / L;
     for (int s = 0; s < ns; ++s) wts[s][ql] *= inv;
   }
   __syncthreads();
-  for (int e = threadIdx.x; e < 32 * (D / 4); e += 256) {
+  for (int e = threadIdx.x; e < QT * (D / 4); e += 256) {
     const int ql = e / (D / 4), j4 = e % (D / 4);
-    const int t = qt * 32 + ql;
+    const int t = qt * QT + ql;
     if (t >= a.chunk) continue;
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
     for (int s = 0; s < ns; ++s) {
-      const float4 v = reinterpret_cast<const float4*>(a.part_o + (u0 + s * 32 + ql) * D)[j4];
+      const float4 v = reinterpret_cast<const float4*>(a.part_o + (u0 + s * QT + ql) * D)[j4];
       const float w = wts[s][ql];
       acc.x += w * v.x;
       acc.y += w * v.y;
@@ -359,20 +501,32 @@ __global__ __launch_bounds__(256) void prefill_combine_kernel(PrefillArgs a) {
 }
 
 struct Plan {
-  int bps, n_split, wpg;
+  int bps, n_split, wpg, nq, qt;
 };
 
-Plan plan(int hq, int hkv, int prior, int chunk) {
+// Query column blocks per wave and waves per workgroup.
+struct Shape {
+  int nq, maxw;
+};
+Shape pick_shape(int d, int G) {
+  (void)d;
+  (void)G;
+  return {XP_PREFILL_NQ, XP_PREFILL_MAXW};
+}
+
+Plan plan(int hq, int hkv, int d, int prior, int chunk) {
   const int G = hq / hkv;
-  const int n_qt = (chunk + 31) / 32;
+  const Shape sh = pick_shape(d, G);
+  const int kQT = 32 * sh.nq;
+  const int n_qt = (chunk + kQT - 1) / kQT;
   const int max_nkb = (prior + chunk + 31) / 32;
   long total = 0;  // key blocks over all tiles
-  for (int qt = 0; qt < n_qt; ++qt) total += (prior + std::min(qt * 32 + 31, chunk - 1) + 1 + 31) / 32;
-  const int wpg = std::min(G, kMaxWaves);
+  for (int qt = 0; qt < n_qt; ++qt) total += (prior + std::min(qt * kQT + kQT - 1, chunk - 1) + 1 + 31) / 32;
+  const int wpg = std::min(G, sh.maxw);
   const long wgs_per_tile = long(hkv) * ((G + wpg - 1) / wpg);
   // aim at about two waves per SIMD over the whole launch (more splits cost fp32 partial
   // traffic), splits of >= 8 blocks
-  const long target = std::max<long>(1, 2048 / wpg);
+  const long target = std::max<long>(1, XP_PREFILL_TARGET_WAVES / wpg);
   long bps = (total * wgs_per_tile + target - 1) / target;
   bps = std::max<long>(8, bps);
   bps = std::min<long>(bps, max_nkb);
@@ -382,16 +536,16 @@ Plan plan(int hq, int hkv, int prior, int chunk) {
     bps = (max_nkb + kMaxSplits - 1) / kMaxSplits;
     n_split = int((max_nkb + bps - 1) / bps);
   }
-  return {int(bps), n_split, wpg};
+  return {int(bps), n_split, wpg, sh.nq, kQT};
 }
 
 }  // namespace
 
 size_t prefill_ws_bytes(int hq, int hkv, int d, int prior, int chunk) {
   if (chunk <= 0) return 0;
-  const Plan p = plan(hq, hkv, prior, chunk);
+  const Plan p = plan(hq, hkv, d, prior, chunk);
   if (p.n_split <= 1) return 0;
-  const size_t units = size_t((chunk + 31) / 32) * hq * p.n_split * 32;
+  const size_t units = size_t((chunk + p.qt - 1) / p.qt) * hq * p.n_split * p.qt;
   return align_up(units * 2 * sizeof(float), 256) + align_up(units * d * sizeof(float), 256);
 }
 
@@ -407,36 +561,36 @@ xp_status launch_prefill(int dtype, const void* q, const void* pool, int n_pages
   if (off < 0 || n_local < 0 || off + n_local > chunk) return fail(XP_ESHAPE, "prefill attention: off/n_local");
   if ((long(prior) + chunk + 31) / 32 > long(kMaxBps) * kMaxSplits)
     return fail(XP_EUNSUPPORTED, "prefill attention: %d keys exceed %d", prior + chunk, 32 * kMaxBps * kMaxSplits);
-  const Plan p = plan(hq, hkv, prior, chunk);
+  const Plan p = plan(hq, hkv, d, prior, chunk);
   const size_t need = prefill_ws_bytes(hq, hkv, d, prior, chunk);
   if (need && !ws) return fail(XP_EWORKSPACE, "prefill attention: needs %zu bytes of workspace", need);
-  const size_t units = size_t((chunk + 31) / 32) * hq * p.n_split * 32;
+  const size_t units = size_t((chunk + p.qt - 1) / p.qt) * hq * p.n_split * p.qt;
   float* ml = static_cast<float*>(ws);
   float* po = ws ? reinterpret_cast<float*>(static_cast<char*>(ws) + align_up(units * 2 * sizeof(float), 256)) : nullptr;
   PrefillArgs a{q, static_cast<const char*>(pool), n_pages, pre_pages, pre_max_blocks, hq, hkv, prior, chunk, off,
                 n_local, out_local, out_local_stride, out_peer, out_peer_stride,
-                float(1.4426950408889634 / __builtin_sqrt(double(d))), status, p.bps, p.n_split, p.wpg, ml, po};
-  const int n_qt = (chunk + 31) / 32;
+                float(1.4426950408889634 / __builtin_sqrt(double(d))), status, p.bps, p.n_split, p.wpg, p.qt, ml, po};
+  const int n_qt = (chunk + p.qt - 1) / p.qt;
   const int G = hq / hkv;
   const dim3 grid(n_qt * p.n_split, hkv * ((G + p.wpg - 1) / p.wpg));
   const dim3 block(64 * p.wpg);
   const dim3 cgrid(n_qt, hq);
   if (dtype == XP_BF16) {
     if (d == 128) {
-      hipLaunchKernelGGL((prefill_kernel<bf16_t, 128>), grid, block, 0, s, a);
+      hipLaunchKernelGGL((prefill_kernel<bf16_t, 128, XP_PREFILL_NQ, XP_PREFILL_MAXW>), grid, block, 0, s, a);
       if (p.n_split > 1) hipLaunchKernelGGL((prefill_combine_kernel<bf16_t, 128>), cgrid, dim3(256), 0, s, a);
     } else if (d == 64) {
-      hipLaunchKernelGGL((prefill_kernel<bf16_t, 64>), grid, block, 0, s, a);
+      hipLaunchKernelGGL((prefill_kernel<bf16_t, 64, XP_PREFILL_NQ, XP_PREFILL_MAXW>), grid, block, 0, s, a);
       if (p.n_split > 1) hipLaunchKernelGGL((prefill_combine_kernel<bf16_t, 64>), cgrid, dim3(256), 0, s, a);
     } else {
       return fail(XP_EUNSUPPORTED, "prefill attention: head_dim %d", d);
     }
   } else if (dtype == XP_F32) {
     if (d == 128) {
-      hipLaunchKernelGGL((prefill_kernel<float, 128>), grid, block, 0, s, a);
+      hipLaunchKernelGGL((prefill_kernel<float, 128, XP_PREFILL_NQ, XP_PREFILL_MAXW>), grid, block, 0, s, a);
       if (p.n_split > 1) hipLaunchKernelGGL((prefill_combine_kernel<float, 128>), cgrid, dim3(256), 0, s, a);
     } else if (d == 64) {
-      hipLaunchKernelGGL((prefill_kernel<float, 64>), grid, block, 0, s, a);
+      hipLaunchKernelGGL((prefill_kernel<float, 64, XP_PREFILL_NQ, XP_PREFILL_MAXW>), grid, block, 0, s, a);
       if (p.n_split > 1) hipLaunchKernelGGL((prefill_combine_kernel<float, 64>), cgrid, dim3(256), 0, s, a);
     } else {
       return fail(XP_EUNSUPPORTED, "prefill attention: head_dim %d", d);
