@@ -29,20 +29,30 @@ xp_status launch_cfg(const void* A, const void* B, const void* B2, const void* R
 }
 
 struct Candidate {
-  int id, bm, bn, per_cu;   // tile, workgroups resident per CU
-  double tflops;            // measured rate when every CU is busy (bf16)
+  int id, bm, bn, per_cu;   // tile, workgroups resident per CU (LDS-limited)
+  double tflops;            // measured rate of one resident workgroup (bf16, TFLOP/s)
 };
 
-// per epilogue kind: single weight (plain / residual epilogues) and dual weight (SwiGLU)
+// Per epilogue kind: single weight (plain / residual epilogues) and dual weight
+// (SwiGLU).  Rates are per resident workgroup, fitted over the layer shapes' QKV, O,
+// gate/up and down projections at 128 to 1040 rows; a workgroup's time is then
+// rounds x (tile flops / rate).
 constexpr Candidate kSingle[] = {
-    {0, 128, 128, 2, 880.0},  // 2x4 waves, 2-stage ring (64 KB LDS)
-    {1, 128, 256, 1, 875.0},  // 2x4 waves, 3-stage ring (144 KB)
-    {2, 64, 128, 2, 760.0},   // 1x4 waves, 3-stage ring (72 KB)
+    {0, 128, 128, 2, 3.14},   // 2x4 waves, 2-stage ring (64 KB LDS)
+    {1, 128, 128, 1, 4.74},   // 2x4 waves, 3-stage ring (96 KB)
+    {2, 128, 256, 1, 5.19},   // 2x4 waves, 2-stage ring (96 KB)
+    {3, 64, 128, 2, 2.16},    // 1x4 waves, 3-stage ring (72 KB)
+    {4, 128, 256, 1, 6.12},   // 2x4 waves, 3-stage ring (144 KB)
+    {5, 64, 128, 1, 3.11},    // 1x4 waves, 4-stage ring (96 KB)
+    {6, 128, 64, 2, 2.24},    // 2x2 waves, 3-stage ring (72 KB)
 };
 constexpr Candidate kDual[] = {
-    {0, 128, 128, 1, 880.0},  // 2x4 waves, 2-stage ring (96 KB)
-    {1, 128, 256, 1, 960.0},  // 2x4 waves, 2-stage ring (160 KB)
-    {2, 64, 128, 1, 700.0},   // 1x4 waves, 3-stage ring (120 KB)
+    {0, 128, 128, 1, 3.62},   // 2x4 waves, 2-stage ring (96 KB)
+    {1, 128, 128, 1, 4.55},   // 2x4 waves, 3-stage ring (144 KB)
+    {2, 128, 256, 1, 4.39},   // 2x4 waves, 2-stage ring (160 KB)
+    {3, 64, 128, 1, 3.32},    // 1x4 waves, 3-stage ring (120 KB)
+    {4, 256, 128, 1, 5.73},   // 4x2 waves, 2-stage ring (128 KB)
+    {5, 128, 64, 1, 3.77},    // 2x2 waves, 3-stage ring (96 KB)
 };
 
 template <size_t NC>
@@ -53,8 +63,7 @@ int pick(const Candidate (&c)[NC], int M, int N, int K, int n_cus, int nb) {
     const long tiles = long(cdiv(M, x.bm)) * cdiv(N, x.bn);
     const long slots = long(n_cus) * x.per_cu;
     const double rounds = double((tiles + slots - 1) / slots);
-    const double t_tile = 2.0 * x.bm * x.bn * nb * K / (x.tflops * 1e12 / slots);
-    const double t = rounds * t_tile;
+    const double t = rounds * 2.0 * x.bm * x.bn * nb * K / (x.tflops * 1e12);
     if (t < best) {
       best = t;
       id = x.id;
@@ -81,14 +90,21 @@ xp_status launch_epi(const void* A, const void* B, const void* B2, const void* R
   const int cus = n_cus_of_current_device();
   if constexpr (EPI == XP_EPI_SWIGLU) {
     switch (pick(kDual, M, N, K, cus, 2)) {
-      case 1: return launch_cfg<T, 128, 256, 2, 4, EPI, 2>(A, B, B2, R, C, M, N, K, s);
-      case 2: return launch_cfg<T, 64, 128, 1, 4, EPI, 3>(A, B, B2, R, C, M, N, K, s);
+      case 1: return launch_cfg<T, 128, 128, 2, 4, EPI, 3>(A, B, B2, R, C, M, N, K, s);
+      case 2: return launch_cfg<T, 128, 256, 2, 4, EPI, 2>(A, B, B2, R, C, M, N, K, s);
+      case 3: return launch_cfg<T, 64, 128, 1, 4, EPI, 3>(A, B, B2, R, C, M, N, K, s);
+      case 4: return launch_cfg<T, 256, 128, 4, 2, EPI, 2>(A, B, B2, R, C, M, N, K, s);
+      case 5: return launch_cfg<T, 128, 64, 2, 2, EPI, 3>(A, B, B2, R, C, M, N, K, s);
       default: return launch_cfg<T, 128, 128, 2, 4, EPI, 2>(A, B, B2, R, C, M, N, K, s);
     }
   } else {
     switch (pick(kSingle, M, N, K, cus, 1)) {
-      case 1: return launch_cfg<T, 128, 256, 2, 4, EPI, 3>(A, B, B2, R, C, M, N, K, s);
-      case 2: return launch_cfg<T, 64, 128, 1, 4, EPI, 3>(A, B, B2, R, C, M, N, K, s);
+      case 1: return launch_cfg<T, 128, 128, 2, 4, EPI, 3>(A, B, B2, R, C, M, N, K, s);
+      case 2: return launch_cfg<T, 128, 256, 2, 4, EPI, 2>(A, B, B2, R, C, M, N, K, s);
+      case 3: return launch_cfg<T, 64, 128, 1, 4, EPI, 3>(A, B, B2, R, C, M, N, K, s);
+      case 4: return launch_cfg<T, 128, 256, 2, 4, EPI, 3>(A, B, B2, R, C, M, N, K, s);
+      case 5: return launch_cfg<T, 64, 128, 1, 4, EPI, 4>(A, B, B2, R, C, M, N, K, s);
+      case 6: return launch_cfg<T, 128, 64, 2, 2, EPI, 3>(A, B, B2, R, C, M, N, K, s);
       default: return launch_cfg<T, 128, 128, 2, 4, EPI, 2>(A, B, B2, R, C, M, N, K, s);
     }
   }

@@ -102,6 +102,13 @@ __device__ __forceinline__ void load_lds16(i32x4 r, uint32_t lds_addr, int voff)
                : "s"(lds_addr), "v"(voff), "s"(r)
                : "memory", "m0");
 }
+// as load_lds16, plus a wave-uniform byte offset `soff` added to the address
+__device__ __forceinline__ void load_lds16_so(i32x4 r, uint32_t lds_addr, int voff, int soff) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+               :
+               : "s"(lds_addr), "v"(voff), "s"(r), "s"(soff)
+               : "memory", "m0");
+}
 #pragma clang diagnostic pop
 
 template <typename T, int BM, int BN, int WGM, int WGN, int EPI, int STAGES>
@@ -133,20 +140,31 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(const char* __rest
   const auto rb2 = rsrc_rows((NB == 2 ? B2 : B) + n0 * kbytes, min(BN, N - n0), kbytes);
   const int lrow = lane >> 3;
 
-  auto issue = [&](int kt, int buf) {
+  // Load instruction i of a wave fills LDS rows (i * W + wave) * 8 .. + 7 of a stage.
+  // W * 8 divides BM and BN, so whether instruction i reads A, B or B2 depends on i
+  // alone; its per-lane byte offset inside the operand is fixed for the whole K loop
+  // and the stage's K position is added as a scalar offset.
+  constexpr int RPI = 8 * W;
+  static_assert(BM % RPI == 0 && BN % RPI == 0, "tile rows must split evenly over the waves");
+  int voff[IPW];
+#pragma unroll
+  for (int i = 0; i < IPW; ++i) {
+    const int row = i * RPI + wave * 8 + lrow;                 // LDS row of this lane's chunk
+    const int orow = (i * RPI < BM) ? row : (NB == 1 || i * RPI < BM + BN) ? row - BM : row - BM - BN;
+    voff[i] = int(orow * kbytes) + (((lane & 7) ^ swz_of(row)) << 4);
+  }
+  const uint32_t lds0 = __builtin_amdgcn_readfirstlane(uint32_t(reinterpret_cast<uintptr_t>(&lds[0][0])));
+  constexpr uint32_t SLOT = ROWS * kRowBytes;
+  // instructions [i0, i1) of stage kt into ring slot buf
+  auto issue = [&](int kt, int buf, int i0, int i1) {
+    const int soff = kt * kRowBytes;
 #pragma unroll
     for (int i = 0; i < IPW; ++i) {
-      const int row0 = (i * W + wave) * 8;   // wave-uniform
-      const int off = kt * kRowBytes + (((lane & 7) ^ swz_of(row0 + lrow)) << 4);
-      const uint32_t dst = __builtin_amdgcn_readfirstlane(
-          uint32_t(reinterpret_cast<uintptr_t>(&lds[buf][row0 * kChunks])));
-      if (row0 < BM) {
-        load_lds16(ra, dst, int((row0 + lrow) * kbytes) + off);
-      } else if (NB == 1 || row0 < BM + BN) {
-        load_lds16(rb, dst, int((row0 - BM + lrow) * kbytes) + off);
-      } else {
-        load_lds16(rb2, dst, int((row0 - BM - BN + lrow) * kbytes) + off);
-      }
+      if (i < i0 || i >= i1) continue;
+      const uint32_t dst = lds0 + buf * SLOT + uint32_t((i * RPI + wave * 8) * kRowBytes);
+      if (i * RPI < BM) load_lds16_so(ra, dst, voff[i], soff);
+      else if (NB == 1 || i * RPI < BM + BN) load_lds16_so(rb, dst, voff[i], soff);
+      else load_lds16_so(rb2, dst, voff[i], soff);
     }
   };
 
@@ -160,9 +178,10 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(const char* __rest
 
   const int lr = lane & 31, kg = lane >> 5;
   const int nk = K / BK;
+  constexpr int KS = BK / 16;     // 16-deep MFMA steps per stage
 #pragma unroll
   for (int s = 0; s < STAGES - 1; ++s)
-    if (s < nk) issue(s, s);
+    if (s < nk) issue(s, s, 0, IPW);
   for (int kt = 0; kt < nk; ++kt) {
     // stage kt must have landed: the stages issued after it may stay in flight
     const int after = min(STAGES - 2, nk - 1 - kt);
@@ -173,13 +192,14 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(const char* __rest
       wait_vmcnt<0>();
     }
     // A bare barrier: every wave has waited for its own loads of stage kt above, and
-    // its reads of the buffer being refilled next were consumed by MFMAs before it
-    // arrived.  (A fence here would also drain the stages still in flight.)
+    // its reads of the slot refilled during this stage were consumed by MFMAs before
+    // it arrived.  (A fence here would also drain the stages still in flight.)
     __builtin_amdgcn_s_barrier();
-    if (kt + STAGES - 1 < nk) issue(kt + STAGES - 1, (kt + STAGES - 1) % STAGES);
+    const bool refill = kt + STAGES - 1 < nk;
+    const int kn = kt + STAGES - 1, bn = (kt + STAGES - 1) % STAGES;
     const uint4* buf = lds[kt % STAGES];
 #pragma unroll
-    for (int ks = 0; ks < BK / 16; ++ks) {
+    for (int ks = 0; ks < KS; ++ks) {
       const int chunk = ks * CPK + kg * (CPK / 2);
       Frag8<T> fa[FM], fb[NB][FN];
 #pragma unroll
@@ -188,6 +208,11 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(const char* __rest
       for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
         for (int j = 0; j < FN; ++j) lds_frag<T>(fb[nb][j], buf, BM + nb * BN + wn * WN + j * 32 + lr, chunk);
+      // The next stage's loads, spread over the MFMA steps of this one.  With a
+      // two-slot ring they must land before the next barrier, so they go out in the
+      // first half of the steps; deeper rings spread them over all of them.
+      constexpr int SPREAD = STAGES == 2 ? (KS + 1) / 2 : KS;
+      if (refill && ks < SPREAD) issue(kn, bn, (IPW * ks) / SPREAD, (IPW * (ks + 1)) / SPREAD);
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
