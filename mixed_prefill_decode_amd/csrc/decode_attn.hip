@@ -28,6 +28,25 @@ namespace {
 constexpr int kPage = 16;
 // pages in flight per wave while one is consumed
 constexpr int kDepth = 1;
+// pages are read through plain pointers (true) or per-page buffer resources
+constexpr bool kPtrLoads = false;
+// log2-domain margin by which a head's maximum may exceed the softmax reference
+// before O and l are rescaled
+constexpr float kLazy = 8.0f;
+
+// Packs 4 weights into a PV operand fragment (rounding them to the operand type)
+// and returns the sum of the rounded weights.
+__device__ __forceinline__ float pack4_and_sum(Frag4<bf16_t>& f, const float* p) {
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  set_frag4(f, p[0], p[1], p[2], p[3]);
+  const bf16x2 one2 = __builtin_bit_cast(bf16x2, 0x3f803f80u);
+  const float s = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, f.v.x), one2, 0.f, false);
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, f.v.y), one2, s, false);
+}
+__device__ __forceinline__ float pack4_and_sum(Frag4<float>& f, const float* p) {
+  set_frag4(f, p[0], p[1], p[2], p[3]);
+  return (p[0] + p[1]) + (p[2] + p[3]);
+}
 
 __device__ __forceinline__ void zero_tail(Frag4<bf16_t>& f, int nvalid) {
   uint32_t x = f.v.x, y = f.v.y;
@@ -83,10 +102,21 @@ __device__ __forceinline__ void load_page(PageFrags<T, D>& f, __amdgpu_buffer_rs
   for (int n = 0; n < D / 16; ++n) bload(f.v[n], r, (kPage * D + (16 * n + key) * kPage + 4 * grp) * EB);
 }
 
+// the same fragments through a plain pointer to the page
+template <typename T, int D>
+__device__ __forceinline__ void load_page(PageFrags<T, D>& f, const char* page, int lane) {
+  constexpr int EB = St<T>::bytes;
+  const int key = lane & 15, grp = lane >> 4;
+#pragma unroll
+  for (int st = 0; st < D / 32; ++st) load_frag8(f.k[st], page + (key * D + 32 * st + 8 * grp) * EB);
+#pragma unroll
+  for (int n = 0; n < D / 16; ++n) load_frag4(f.v[n], page + (kPage * D + (16 * n + key) * kPage + 4 * grp) * EB);
+}
+
 // One wave per (split s, KV head g, request i).  DEPTH pages are in flight
 // while one is consumed; the register ring has DEPTH + 1 page buffers and the
 // loop is unrolled over the ring so every buffer index is static.
-template <typename T, int D, int DEPTH>
+template <typename T, int D, int DEPTH, bool PTR>
 __global__ __launch_bounds__(64) void decode_split_kernel(const void* __restrict__ q, const char* __restrict__ pool,
                                                           int n_pages, const int32_t* __restrict__ dec_pages,
                                                           int max_blocks, const int32_t* __restrict__ dec_ctx, int Hq,
@@ -127,6 +157,15 @@ __global__ __launch_bounds__(64) void decode_split_kernel(const void* __restrict
     bad |= in && !ok;
     return page_rsrc(pool + (ok ? long(pid) : 0L) * PAGE_BYTES, ok ? PAGE_BYTES : 0);
   };
+  // pointer form: a page outside the split or the pool reads page 0 instead (never
+  // consumed, or consumed only by a split whose output is flagged)
+  auto page_of = [&](int b) {
+    const bool in = b < b1;
+    const int pid = __builtin_amdgcn_readlane(my_pid, in ? b - b0 : 0);
+    const bool ok = in && pid >= 0 && pid < n_pages;
+    bad |= in && !ok;
+    return pool + (ok ? long(pid) : 0L) * PAGE_BYTES;
+  };
 
   f32x4 o[D / 16];
 #pragma unroll
@@ -136,7 +175,8 @@ __global__ __launch_bounds__(64) void decode_split_kernel(const void* __restrict
   PageFrags<T, D> buf[NB];
 #pragma unroll
   for (int j = 0; j < DEPTH; ++j) {
-    load_page<T, D>(buf[j], rsrc_of(b0 + j), lane);
+    if constexpr (PTR) load_page<T, D>(buf[j], page_of(b0 + j), lane);
+    else load_page<T, D>(buf[j], rsrc_of(b0 + j), lane);
     // keep the pages' loads in issue order: the waits below count on it
     __builtin_amdgcn_sched_barrier(0);
   }
@@ -144,40 +184,47 @@ __global__ __launch_bounds__(64) void decode_split_kernel(const void* __restrict
 #pragma unroll
     for (int u = 0; u < NB; ++u) {
       const int b = bb + u;
-      load_page<T, D>(buf[(u + DEPTH) % NB], rsrc_of(b + DEPTH), lane);
+      if constexpr (PTR) load_page<T, D>(buf[(u + DEPTH) % NB], page_of(b + DEPTH), lane);
+      else load_page<T, D>(buf[(u + DEPTH) % NB], rsrc_of(b + DEPTH), lane);
       __builtin_amdgcn_sched_barrier(0);
       if (b < b1) {
         PageFrags<T, D>& cur = buf[u];
         f32x4 sacc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int st = 0; st < D / 32; ++st) mma16x16_k32(sacc, cur.k[st], qf[st]);
-        // element r: key b*16 + 4*grp + r of head hh
-        const int k0 = b * kPage + 4 * grp;
-        float sv[4];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) sv[r] = (k0 + r < n_keys) ? sacc[r] * scale_log2 : -__builtin_inff();
+        // element r: key b*16 + 4*grp + r of head hh; only the context's last page
+        // has slots past the newest key (their V^T columns may hold anything)
+        float sv[4] = {sacc[0], sacc[1], sacc[2], sacc[3]};
         if ((b + 1) * kPage > n_keys) {
+          const int k0 = b * kPage + 4 * grp;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) sv[r] = (k0 + r < n_keys) ? sv[r] : -__builtin_inff();
 #pragma unroll
           for (int n = 0; n < D / 16; ++n) zero_tail(cur.v[n], n_keys - k0);
         }
         float mb = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
         mb = fmaxf(mb, shfl_xor(mb, 16));
-        mb = fmaxf(mb, shfl_xor(mb, 32));
-        const float mn = fmaxf(m, mb);  // finite: every visited page holds a visible key
-        const float alpha = fast_exp2(m - mn);
+        mb = fmaxf(mb, shfl_xor(mb, 32)) * scale_log2;   // finite: every visited page holds a key
+        // Lazily moved softmax reference (exp2 domain): O and l are rescaled only when
+        // some head's maximum exceeds the reference by more than kLazy, so the
+        // weights stay below 2^kLazy; the result is the same function of the scores.
+        if (__builtin_amdgcn_ballot_w64(mb > m + kLazy) != 0) {
+          const float mn = fmaxf(m, mb);
+          const float alpha = m == -__builtin_inff() ? 0.f : fast_exp2(m - mn);
+          m = mn;
+          lsum *= alpha;
+#pragma unroll
+          for (int n = 0; n < D / 16; ++n) o[n] *= alpha;
+        }
+        float p[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) p[r] = fast_exp2(__builtin_fmaf(sv[r], scale_log2, -m));
         // the weights are rounded to the operand type first, so the normaliser sums
         // exactly the weights the PV product uses
-        const float p0 = round_st<T>(fast_exp2(sv[0] - mn)), p1 = round_st<T>(fast_exp2(sv[1] - mn));
-        const float p2 = round_st<T>(fast_exp2(sv[2] - mn)), p3 = round_st<T>(fast_exp2(sv[3] - mn));
-        lsum = lsum * alpha + ((p0 + p1) + (p2 + p3));
         Frag4<T> pf;
-        set_frag4(pf, p0, p1, p2, p3);
+        lsum += pack4_and_sum(pf, p);
 #pragma unroll
-        for (int n = 0; n < D / 16; ++n) {
-          o[n] *= alpha;
-          mma16x16_k16(o[n], cur.v[n], pf);
-        }
-        m = mn;
+        for (int n = 0; n < D / 16; ++n) mma16x16_k16(o[n], cur.v[n], pf);
       }
     }
   }
@@ -273,7 +320,7 @@ xp_status launch_dec_t(const void* q, const void* pool, int n_pages, const int32
                        float* part_o, int pps, uint32_t* status, hipStream_t s) {
   const int n_splits = decode_splits(max_blocks, pps);
   const float scale_log2 = float(1.4426950408889634 / __builtin_sqrt(double(D)));
-  hipLaunchKernelGGL((decode_split_kernel<T, D, kDepth>), dim3(n_splits, Hkv, n_d), dim3(64), 0, s, q,
+  hipLaunchKernelGGL((decode_split_kernel<T, D, kDepth, kPtrLoads>), dim3(n_splits, Hkv, n_d), dim3(64), 0, s, q,
                      static_cast<const char*>(pool), n_pages, dec_pages, max_blocks, dec_ctx, Hq, Hkv, pps, n_splits,
                      part_ml, part_o, scale_log2, status);
   XP_CHECK_LAUNCH();
