@@ -14,6 +14,7 @@ to stderr.
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -86,6 +87,30 @@ def gemm_list(wl):
     M, H, F, d = wl.n_rows, wl.hidden, wl.ffn_dim, wl.head_dim
     return {"qkv": (M, (wl.n_q_heads + 2 * wl.n_kv_heads) * d, H), "o": (M, H, wl.n_q_heads * d),
             "gate_up": (M, 2 * F, H), "down": (M, H, F)}
+
+
+TRAFFIC_PROFILE = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles",
+                               "gate_up_swiglu_gemm_c2_traffic.md")
+GEMM_SOURCES = ("mixed_prefill_decode_amd/csrc/gemm_core.h", "mixed_prefill_decode_amd/csrc/gemm.hip")
+
+
+def recorded_traffic(workload: str):
+    """HBM bytes per launch of the dominant kernel from the committed counter summary
+    (FETCH_SIZE and WRITE_SIZE scaled by a copy kernel's readings), or None when the
+    summary is for another workload or the GEMM sources changed since it was taken."""
+    try:
+        text = open(TRAFFIC_PROFILE).read()
+        rec = json.loads(text[text.index("```json") + 7:text.rindex("```")])
+        h = hashlib.sha256()
+        root = os.path.dirname(os.path.abspath(__file__))
+        for f in GEMM_SOURCES:
+            with open(os.path.join(root, f), "rb") as fh:
+                h.update(fh.read())
+    except (OSError, ValueError):
+        return None
+    if rec.get("workload") != workload or rec.get("src_sha256_16") != h.hexdigest()[:16]:
+        return None
+    return rec["traffic_bytes"]
 
 
 def cpu_baseline(inst, budget_s: float) -> dict:
@@ -280,11 +305,12 @@ def main():
                                 "mfma_frac": round(fl / t / 1e12 / PEAK_BF16_TFLOPS, 4), "flops": fl}
 
     dom = "gate_up"
+    traffic = recorded_traffic(wl.name)
     m_, n_, k_ = gl[dom]
     fl = 2.0 * m_ * n_ * k_
     t_dom = kern[dom]["us"] * 1e-6
     roofline = {"bound": "mfma", "achieved": round(fl / t_dom / 1e12, 2), "peak": PEAK_BF16_TFLOPS,
-                "unit": "TFLOP/s", "frac": round(fl / t_dom / 1e12 / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                "unit": "TFLOP/s", "frac": round(fl / t_dom / 1e12 / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
                 "kernel": "gemm_kernel<bf16,SwiGLU> (gate/up projection)", "flops_per_launch": fl}
     log(f"[bench] layer {ms * 1e3:.1f} us/step, {tokens_per_s:.0f} tokens/s; kernels {json.dumps(kern)}")
     log(f"[bench] split attention {json.dumps(seg)}")
