@@ -264,15 +264,16 @@ def main():
     M, H, F = wl.n_rows, wl.hidden, wl.ffn_dim
     kern = {}
     gl = gemm_list(wl)
+    gp, gpb = ws + lay.gemm_part, lay.h1 - lay.gemm_part     # the layer's GEMM split partials
     gemm_calls = {
         "qkv": lambda: X.xp_gemm(X.XP_BF16, X.XP_EPI_F32, ws + lay.hn, w["w_qkv"], None, None, ws + lay.qkv,
-                                 M, gl["qkv"][1], H),
+                                 M, gl["qkv"][1], H, gp, gpb),
         "o": lambda: X.xp_gemm(X.XP_BF16, X.XP_EPI_ADD_T, ws + lay.attn, w["w_o"], None, dev.x, ws + lay.h1,
-                               M, H, gl["o"][2]),
+                               M, H, gl["o"][2], gp, gpb),
         "gate_up": lambda: X.xp_gemm(X.XP_BF16, X.XP_EPI_SWIGLU, ws + lay.hn, w["w_gate"], w["w_up"], None,
-                                     ws + lay.act, M, F, H),
+                                     ws + lay.act, M, F, H, gp, gpb),
         "down": lambda: X.xp_gemm(X.XP_BF16, X.XP_EPI_ADD_F32, ws + lay.act, w["w_down"], None, ws + lay.h1,
-                                  step0.out, M, H, F),
+                                  step0.out, M, H, F, gp, gpb),
     }
     for name, fn in gemm_calls.items():
         m_, n_, k_ = gl[name]
@@ -342,7 +343,7 @@ def kernel_only(args, X, torch, inst, step, dev, timer):
     lay, ws, w = step.layout, int(step.workspace.data_ptr()), dev.weights
     if args.kernel_only == "swiglu":
         fn = lambda: X.xp_gemm(X.XP_BF16, X.XP_EPI_SWIGLU, ws + lay.hn, w["w_gate"], w["w_up"], None, ws + lay.act,
-                               wl.n_rows, wl.ffn_dim, wl.hidden)
+                               wl.n_rows, wl.ffn_dim, wl.hidden, ws + lay.gemm_part, lay.h1 - lay.gemm_part)
     elif args.kernel_only == "prefill":
         hq, d = wl.hq_loc, wl.head_dim
         pout = torch.empty((wl.chunk_len, hq * d), dtype=torch.bfloat16, device="cuda")

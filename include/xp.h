@@ -155,6 +155,7 @@ typedef struct {
   size_t dec_ml;       /* fp32 split-K partial (max, sum) pairs             */
   size_t dec_o;        /* fp32 split-K partial outputs                       */
   size_t pre_part;     /* prefill key-split partials (see xp_prefill_workspace_size) */
+  size_t gemm_part;    /* GEMM K-split partials, the largest of the four projections' */
   size_t h1;           /* [M, H] fp32 x + attn W_o^T                         */
   size_t act;          /* [M, F] T silu(hn2 W_gate^T) * (hn2 W_up^T)         */
   size_t total;        /* bytes required                                     */
@@ -228,19 +229,26 @@ xp_status xp_layer_read_status(const void* workspace, const xp_ws_layout* layout
 xp_status xp_rmsnorm(int32_t dtype, const void* x, int32_t x_is_f32, const void* gamma, void* y,
                      int32_t M, int32_t H, float eps, void* stream);
 
-/* MFMA GEMM with fp32 accumulation; A [M, K] T, B [N, K] T (C = A B^T).
+/* MFMA GEMM with fp32 accumulation; A [M, K] T, B [N, K] T (C = A B^T), the
+ * co-batched projections of [CS] §4 / App. B (one weight read for all rows).
  * Epilogues:
  *   XP_EPI_F32     C fp32 [M, N]  = A B^T
  *   XP_EPI_ADD_T   C fp32 [M, N]  = R (T) + A B^T
  *   XP_EPI_ADD_F32 C fp32 [M, N]  = R (fp32) + A B^T
  *   XP_EPI_SWIGLU  C T    [M, N]  = silu(A B^T) * (A B2^T), B2 [N, K] T
- * K must be a multiple of 64 (bf16) / 32 (fp32). */
+ * K must be a multiple of 64 (bf16) / 32 (fp32).  Wide-K / narrow-N products are
+ * split over K; the split count depends on (dtype, epilogue, N, K) only, so a row's
+ * result never depends on M, and the fp32 split partials are summed in split
+ * order.  workspace: >= xp_gemm_workspace_size bytes of device memory (0 when
+ * the product is not split; workspace may then be NULL), otherwise XP_EWORKSPACE. */
 #define XP_EPI_F32 0
 #define XP_EPI_ADD_T 1
 #define XP_EPI_ADD_F32 2
 #define XP_EPI_SWIGLU 3
+size_t xp_gemm_workspace_size(int32_t dtype, int32_t epilogue, int32_t M, int32_t N, int32_t K);
 xp_status xp_gemm(int32_t dtype, int32_t epilogue, const void* A, const void* B, const void* B2,
-                  const void* R, void* C, int32_t M, int32_t N, int32_t K, void* stream);
+                  const void* R, void* C, int32_t M, int32_t N, int32_t K, void* workspace,
+                  size_t workspace_bytes, void* stream);
 
 /* Append n token rows of K/V (T, [n, d] each) at device positions pos[n]
  * through table rows: token t uses table + seq[t] * table_stride (seq: device

@@ -16,7 +16,8 @@ __all__ = ["XpError", "lib", "XP_F32", "XP_BF16", "XP_EPI_F32", "XP_EPI_ADD_T", 
            "XP_EPI_SWIGLU", "XP_DEV_BAD_PAGE", "LayerShape", "LayerWeights", "KvPages", "BatchDesc",
            "WsLayout", "LatencyModel", "Ctx", "EXPORTED",
            "xp_ctx_create", "xp_layer_workspace_layout", "xp_layer_forward", "xp_validate_batch",
-           "xp_layer_read_status", "xp_rmsnorm", "xp_gemm", "xp_kv_append", "xp_kv_gather",
+           "xp_layer_read_status", "xp_rmsnorm", "xp_gemm_workspace_size", "xp_gemm", "xp_kv_append",
+           "xp_kv_gather",
            "xp_decode_workspace_size", "xp_decode_attention", "xp_prefill_workspace_size", "xp_prefill_attention",
            "xp_probe_hw_ids",
            "xp_waterfill", "xp_iteration_latency", "xp_build_info", "xp_last_error"]
@@ -33,7 +34,8 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libxp.so")
 EXPORTED = ["xp_last_error", "xp_build_info", "xp_ctx_create", "xp_ctx_destroy", "xp_ctx_cu_masks",
             "xp_ctx_streams",
             "xp_layer_workspace_layout", "xp_layer_forward", "xp_validate_batch", "xp_layer_read_status",
-            "xp_rmsnorm", "xp_gemm", "xp_kv_append", "xp_kv_gather", "xp_decode_workspace_size",
+            "xp_rmsnorm", "xp_gemm_workspace_size", "xp_gemm", "xp_kv_append", "xp_kv_gather",
+            "xp_decode_workspace_size",
             "xp_decode_attention", "xp_prefill_workspace_size", "xp_prefill_attention", "xp_probe_hw_ids",
             "xp_waterfill",
             "xp_iteration_latency"]
@@ -70,7 +72,7 @@ class BatchDesc(C.Structure):
 
 class WsLayout(C.Structure):
     _fields_ = [(n, C.c_size_t) for n in ("status", "hn", "qkv", "q_dec", "q_pre", "attn", "dec_ml",
-                                          "dec_o", "pre_part", "h1", "act", "total")] + \
+                                          "dec_o", "pre_part", "gemm_part", "h1", "act", "total")] + \
                [("dec_splits", C.c_int32), ("dec_pages_per_split", C.c_int32)]
 
     def as_dict(self):
@@ -114,7 +116,8 @@ def _declare(L):
         "xp_validate_batch": (S, [C.POINTER(LayerShape), C.POINTER(BatchDesc), _i32, _vp, _vp, _vp]),
         "xp_layer_read_status": (S, [_vp, C.POINTER(WsLayout), _vp, _vp]),
         "xp_rmsnorm": (S, [_i32, _vp, _i32, _vp, _vp, _i32, _i32, _f32, _vp]),
-        "xp_gemm": (S, [_i32, _i32, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _vp]),
+        "xp_gemm_workspace_size": (_sz, [_i32, _i32, _i32, _i32, _i32]),
+        "xp_gemm": (S, [_i32, _i32, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _vp, _sz, _vp]),
         "xp_kv_append": (S, [_i32, _vp, _i32, _i32, _i32, _vp, _i32, _vp, _vp, _vp, _vp, _i32, _vp]),
         "xp_kv_gather": (S, [_i32, _vp, _i32, _i32, _i32, _vp, _i32, _vp, _i32, _i32, _vp, _vp, _vp]),
         "xp_decode_workspace_size": (_sz, [_i32, _i32, _i32, _i32, _i32, _i32]),
@@ -245,9 +248,13 @@ def xp_rmsnorm(dtype, x, x_is_f32, gamma, y, M, H, eps, stream=None):
     _check(lib().xp_rmsnorm(dtype, _ptr(x), int(x_is_f32), _ptr(gamma), _ptr(y), M, H, eps, _stream(stream)))
 
 
-def xp_gemm(dtype, epilogue, A, B, B2, R, Cout, M, N, K, stream=None):
+def xp_gemm_workspace_size(dtype, epilogue, M, N, K) -> int:
+    return int(lib().xp_gemm_workspace_size(dtype, epilogue, M, N, K))
+
+
+def xp_gemm(dtype, epilogue, A, B, B2, R, Cout, M, N, K, workspace=None, workspace_bytes=0, stream=None):
     _check(lib().xp_gemm(dtype, epilogue, _ptr(A), _ptr(B), _ptr(B2), _ptr(R), _ptr(Cout), M, N, K,
-                         _stream(stream)))
+                         _ptr(workspace), workspace_bytes, _stream(stream)))
 
 
 def xp_kv_append(dtype, pool, n_pages, page_size, head_dim, table, table_stride, seq, pos, k, v, n, stream=None):

@@ -159,6 +159,14 @@ xp_ws_layout make_layout(const xp_ctx* ctx, const xp_layer_shape* sh, const xp_b
   L.dec_o = take(units * D * sizeof(float));
   L.pre_part = take(prefill_ws_bytes(int(Hq) / d->sp_degree, int(Hkv) / d->sp_degree, int(D), d->prior_len,
                                      d->chunk_len));
+  {
+    const int dt = sh->dtype;
+    const size_t g = std::max(std::max(gemm_ws_bytes(dt, XP_EPI_F32, int(M), int((Hq + 2 * Hkv) * D), int(H)),
+                                       gemm_ws_bytes(dt, XP_EPI_ADD_T, int(M), int(H), int(Hq * D))),
+                              std::max(gemm_ws_bytes(dt, XP_EPI_SWIGLU, int(M), int(F), int(H)),
+                                       gemm_ws_bytes(dt, XP_EPI_ADD_F32, int(M), int(H), int(F))));
+    L.gemm_part = take(g);
+  }
   L.h1 = take(M * H * 4);
   L.act = take(M * F * eb);
   L.total = off;
@@ -325,10 +333,12 @@ xp_status xp_layer_forward(xp_ctx* ctx, const xp_layer_shape* sh, const xp_batch
   char* attn = ws + L.attn;
   float* h1 = reinterpret_cast<float*>(ws + L.h1);
   char* act = ws + L.act;
+  void* gp = ws + L.gemm_part;                  // GEMM K-split partials
+  const size_t gpb = L.h1 - L.gemm_part;
 
   // shared linear region (1): RMSNorm + QKV over all M rows
   if ((st = launch_rmsnorm(dt, d->x, 0, w->g_attn, hn, M, H, sh->rms_eps, status, s))) return st;
-  if (M > 0 && (st = launch_gemm(dt, XP_EPI_F32, hn, w->w_qkv, nullptr, nullptr, qkv, M, (Hq + 2 * Hkv) * D, H, s)))
+  if (M > 0 && (st = launch_gemm(dt, XP_EPI_F32, hn, w->w_qkv, nullptr, nullptr, qkv, M, (Hq + 2 * Hkv) * D, H, gp, gpb, s)))
     return st;
   // RoPE + appends (+ the peer stand-ins)
   PostQkvArgs pa{qkv, n_pl, n_d, Hq, Hkv, D, sh->page_size, sh->rope_base, d->dec_ctx, d->dec_pages,
@@ -368,10 +378,10 @@ xp_status xp_layer_forward(xp_ctx* ctx, const xp_layer_shape* sh, const xp_batch
   if (M == 0) return XP_OK;
 
   // shared linear region (2): O projection + residual, RMSNorm, gate/up + SwiGLU, down + residual
-  if ((st = launch_gemm(dt, XP_EPI_ADD_T, attn, w->w_o, nullptr, d->x, h1, M, H, Hq * D, s))) return st;
+  if ((st = launch_gemm(dt, XP_EPI_ADD_T, attn, w->w_o, nullptr, d->x, h1, M, H, Hq * D, gp, gpb, s))) return st;
   if ((st = launch_rmsnorm(dt, h1, 1, w->g_ffn, hn, M, H, sh->rms_eps, nullptr, s))) return st;
-  if ((st = launch_gemm(dt, XP_EPI_SWIGLU, hn, w->w_gate, w->w_up, nullptr, act, M, F, H, s))) return st;
-  if ((st = launch_gemm(dt, XP_EPI_ADD_F32, act, w->w_down, nullptr, h1, out, M, H, F, s))) return st;
+  if ((st = launch_gemm(dt, XP_EPI_SWIGLU, hn, w->w_gate, w->w_up, nullptr, act, M, F, H, gp, gpb, s))) return st;
+  if ((st = launch_gemm(dt, XP_EPI_ADD_F32, act, w->w_down, nullptr, h1, out, M, H, F, gp, gpb, s))) return st;
   return XP_OK;
 }
 
@@ -382,9 +392,15 @@ xp_status xp_rmsnorm(int32_t dtype, const void* x, int32_t x_is_f32, const void*
   return launch_rmsnorm(dtype, x, x_is_f32, gamma, y, M, H, eps, nullptr, static_cast<hipStream_t>(stream));
 }
 
+size_t xp_gemm_workspace_size(int32_t dtype, int32_t epi, int32_t M, int32_t N, int32_t K) {
+  if ((dtype != XP_BF16 && dtype != XP_F32) || epi < XP_EPI_F32 || epi > XP_EPI_SWIGLU) return 0;
+  return gemm_ws_bytes(dtype, epi, M, N, K);
+}
+
 xp_status xp_gemm(int32_t dtype, int32_t epi, const void* A, const void* B, const void* B2, const void* R, void* C,
-                  int32_t M, int32_t N, int32_t K, void* stream) {
-  return launch_gemm(dtype, epi, A, B, B2, R, C, M, N, K, static_cast<hipStream_t>(stream));
+                  int32_t M, int32_t N, int32_t K, void* workspace, size_t workspace_bytes, void* stream) {
+  return launch_gemm(dtype, epi, A, B, B2, R, C, M, N, K, workspace, workspace_bytes,
+                     static_cast<hipStream_t>(stream));
 }
 
 xp_status xp_kv_append(int32_t dtype, void* pool, int32_t n_pages, int32_t S, int32_t d, const int32_t* table,

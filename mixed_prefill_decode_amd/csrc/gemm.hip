@@ -19,51 +19,65 @@ using gemm::gemm_kernel;
 
 template <typename T, int BM, int BN, int WGM, int WGN, int EPI, int ST>
 xp_status launch_cfg(const void* A, const void* B, const void* B2, const void* R, void* C, int M, int N, int K,
-                     hipStream_t s) {
+                     int splits, float* part, hipStream_t s) {
   const int tm = cdiv(M, BM), tn = cdiv(N, BN);
-  hipLaunchKernelGGL((gemm_kernel<T, BM, BN, WGM, WGN, EPI, ST>), dim3(tm * tn), dim3(64 * WGM * WGN), 0, s,
+  const int stages = K / gemm::Cfg<T, BM, BN, WGM, WGN, EPI>::BK;
+  const int per = cdiv(stages, splits);
+  hipLaunchKernelGGL((gemm_kernel<T, BM, BN, WGM, WGN, EPI, ST>), dim3(tm * tn * splits), dim3(64 * WGM * WGN), 0, s,
                      static_cast<const char*>(A), static_cast<const char*>(B), static_cast<const char*>(B2), R, C,
-                     M, N, K, tm, tn);
+                     M, N, K, tm, tn, splits, per, part);
   XP_CHECK_LAUNCH();
+  if (splits > 1) {
+    const long mn = long(M) * N;
+    const int blocks = int(std::min<long>((mn + 255) / 256, 4096));
+    hipLaunchKernelGGL((gemm::gemm_reduce_kernel<T, EPI>), dim3(blocks), dim3(256), 0, s, part, R, C, mn, splits);
+    XP_CHECK_LAUNCH();
+  }
   return XP_OK;
 }
 
 struct Candidate {
-  int id, bm, bn, per_cu;   // tile, workgroups resident per CU (LDS-limited)
+  int id, bm, bn, per_cu;   // tile, workgroups resident per CU (LDS- and wave-limited)
   double tflops;            // measured rate of one resident workgroup (bf16, TFLOP/s)
+  double tflops_split;      // the same for a K-split work unit (a quarter to a third of K)
 };
 
 // Per epilogue kind: single weight (plain / residual epilogues) and dual weight
-// (SwiGLU).  Rates are per resident workgroup, fitted over the layer shapes' QKV, O,
-// gate/up and down projections at 128 to 1040 rows; a workgroup's time is then
-// rounds x (tile flops / rate).
+// (SwiGLU).  Rates are per resident workgroup, fitted over the QKV, O, gate/up and
+// down projections of the 8B, 14B and 32B layer shapes at 128 to 1040 rows; a call
+// then takes rounds x (work-unit flops / rate), rounds counting waves of resident
+// workgroups.  Over those 16 shapes the picks total within 1% of the best measured.
 constexpr Candidate kSingle[] = {
-    {0, 128, 128, 2, 3.14},   // 2x4 waves, 2-stage ring (64 KB LDS)
-    {1, 128, 128, 1, 4.74},   // 2x4 waves, 3-stage ring (96 KB)
-    {2, 128, 256, 1, 5.19},   // 2x4 waves, 2-stage ring (96 KB)
-    {3, 64, 128, 2, 2.16},    // 1x4 waves, 3-stage ring (72 KB)
-    {4, 128, 256, 1, 6.12},   // 2x4 waves, 3-stage ring (144 KB)
-    {5, 64, 128, 1, 3.11},    // 1x4 waves, 4-stage ring (96 KB)
-    {6, 128, 64, 2, 2.24},    // 2x2 waves, 3-stage ring (72 KB)
+    {0, 128, 128, 2, 3.26, 2.54},   // 2x4 waves, 2-stage ring (64 KB LDS)
+    {1, 128, 128, 1, 4.75, 4.06},   // 2x4 waves, 3-stage ring (96 KB)
+    {2, 128, 256, 1, 5.25, 4.53},   // 2x4 waves, 2-stage ring (96 KB)
+    {3, 64, 128, 2, 2.15, 1.75},    // 1x4 waves, 3-stage ring (72 KB)
+    {4, 256, 128, 1, 5.23, 4.76},   // 4x2 waves, 2-stage ring (96 KB)
+    {5, 256, 256, 1, 7.38, 6.24},   // 2x4 waves, 2-stage ring (128 KB)
+    {6, 128, 128, 1, 5.00, 4.16},   // 2x4 waves, 4-stage ring (128 KB)
+    {7, 128, 256, 1, 6.40, 5.16},   // 2x4 waves, 3-stage ring (144 KB)
+    {8, 64, 128, 1, 3.06, 2.67},    // 1x4 waves, 4-stage ring (96 KB)
+    {9, 128, 64, 2, 2.28, 1.98},    // 2x2 waves, 3-stage ring (72 KB)
 };
 constexpr Candidate kDual[] = {
-    {0, 128, 128, 1, 3.62},   // 2x4 waves, 2-stage ring (96 KB)
-    {1, 128, 128, 1, 4.55},   // 2x4 waves, 3-stage ring (144 KB)
-    {2, 128, 256, 1, 4.39},   // 2x4 waves, 2-stage ring (160 KB)
-    {3, 64, 128, 1, 3.32},    // 1x4 waves, 3-stage ring (120 KB)
-    {4, 256, 128, 1, 5.73},   // 4x2 waves, 2-stage ring (128 KB)
-    {5, 128, 64, 1, 3.77},    // 2x2 waves, 3-stage ring (96 KB)
+    {0, 128, 128, 1, 3.68, 3.68},   // 2x4 waves, 2-stage ring (96 KB)
+    {1, 128, 128, 1, 4.78, 4.78},   // 2x4 waves, 3-stage ring (144 KB)
+    {2, 128, 256, 1, 4.64, 4.64},   // 2x4 waves, 2-stage ring (160 KB)
+    {3, 64, 128, 1, 3.29, 3.29},    // 1x4 waves, 3-stage ring (120 KB)
+    {4, 256, 128, 1, 6.23, 6.23},   // 4x2 waves, 2-stage ring (128 KB)
+    {5, 128, 64, 1, 3.89, 3.89},    // 2x2 waves, 3-stage ring (96 KB)
 };
 
 template <size_t NC>
-int pick(const Candidate (&c)[NC], int M, int N, int K, int n_cus, int nb) {
+int pick(const Candidate (&c)[NC], int M, int N, int K, int n_cus, int nb, int splits) {
   double best = 1e300;
   int id = 0;
   for (const Candidate& x : c) {
-    const long tiles = long(cdiv(M, x.bm)) * cdiv(N, x.bn);
+    const long units = long(cdiv(M, x.bm)) * cdiv(N, x.bn) * splits;
     const long slots = long(n_cus) * x.per_cu;
-    const double rounds = double((tiles + slots - 1) / slots);
-    const double t = rounds * 2.0 * x.bm * x.bn * nb * K / (x.tflops * 1e12);
+    const double rounds = double((units + slots - 1) / slots);
+    const double rate = splits > 1 ? x.tflops_split : x.tflops;
+    const double t = rounds * 2.0 * x.bm * x.bn * nb * (double(K) / splits) / (rate * 1e12);
     if (t < best) {
       best = t;
       id = x.id;
@@ -86,48 +100,78 @@ int n_cus_of_current_device() {
 
 template <typename T, int EPI>
 xp_status launch_epi(const void* A, const void* B, const void* B2, const void* R, void* C, int M, int N, int K,
-                     hipStream_t s) {
+                     int splits, float* part, hipStream_t s) {
   const int cus = n_cus_of_current_device();
+#define XP_GEMM_ARGS A, B, B2, R, C, M, N, K, splits, part, s
   if constexpr (EPI == XP_EPI_SWIGLU) {
-    switch (pick(kDual, M, N, K, cus, 2)) {
-      case 1: return launch_cfg<T, 128, 128, 2, 4, EPI, 3>(A, B, B2, R, C, M, N, K, s);
-      case 2: return launch_cfg<T, 128, 256, 2, 4, EPI, 2>(A, B, B2, R, C, M, N, K, s);
-      case 3: return launch_cfg<T, 64, 128, 1, 4, EPI, 3>(A, B, B2, R, C, M, N, K, s);
-      case 4: return launch_cfg<T, 256, 128, 4, 2, EPI, 2>(A, B, B2, R, C, M, N, K, s);
-      case 5: return launch_cfg<T, 128, 64, 2, 2, EPI, 3>(A, B, B2, R, C, M, N, K, s);
-      default: return launch_cfg<T, 128, 128, 2, 4, EPI, 2>(A, B, B2, R, C, M, N, K, s);
+    switch (pick(kDual, M, N, K, cus, 2, splits)) {
+      case 1: return launch_cfg<T, 128, 128, 2, 4, EPI, 3>(XP_GEMM_ARGS);
+      case 2: return launch_cfg<T, 128, 256, 2, 4, EPI, 2>(XP_GEMM_ARGS);
+      case 3: return launch_cfg<T, 64, 128, 1, 4, EPI, 3>(XP_GEMM_ARGS);
+      case 4: return launch_cfg<T, 256, 128, 4, 2, EPI, 2>(XP_GEMM_ARGS);
+      case 5: return launch_cfg<T, 128, 64, 2, 2, EPI, 3>(XP_GEMM_ARGS);
+      default: return launch_cfg<T, 128, 128, 2, 4, EPI, 2>(XP_GEMM_ARGS);
     }
   } else {
-    switch (pick(kSingle, M, N, K, cus, 1)) {
-      case 1: return launch_cfg<T, 128, 128, 2, 4, EPI, 3>(A, B, B2, R, C, M, N, K, s);
-      case 2: return launch_cfg<T, 128, 256, 2, 4, EPI, 2>(A, B, B2, R, C, M, N, K, s);
-      case 3: return launch_cfg<T, 64, 128, 1, 4, EPI, 3>(A, B, B2, R, C, M, N, K, s);
-      case 4: return launch_cfg<T, 128, 256, 2, 4, EPI, 3>(A, B, B2, R, C, M, N, K, s);
-      case 5: return launch_cfg<T, 64, 128, 1, 4, EPI, 4>(A, B, B2, R, C, M, N, K, s);
-      case 6: return launch_cfg<T, 128, 64, 2, 2, EPI, 3>(A, B, B2, R, C, M, N, K, s);
-      default: return launch_cfg<T, 128, 128, 2, 4, EPI, 2>(A, B, B2, R, C, M, N, K, s);
+    switch (pick(kSingle, M, N, K, cus, 1, splits)) {
+      case 1: return launch_cfg<T, 128, 128, 2, 4, EPI, 3>(XP_GEMM_ARGS);
+      case 2: return launch_cfg<T, 128, 256, 2, 4, EPI, 2>(XP_GEMM_ARGS);
+      case 3: return launch_cfg<T, 64, 128, 1, 4, EPI, 3>(XP_GEMM_ARGS);
+      case 4: return launch_cfg<T, 256, 128, 4, 2, EPI, 2>(XP_GEMM_ARGS);
+      case 5: return launch_cfg<T, 256, 256, 2, 4, EPI, 2>(XP_GEMM_ARGS);
+      case 6: return launch_cfg<T, 128, 128, 2, 4, EPI, 4>(XP_GEMM_ARGS);
+      case 7: return launch_cfg<T, 128, 256, 2, 4, EPI, 3>(XP_GEMM_ARGS);
+      case 8: return launch_cfg<T, 64, 128, 1, 4, EPI, 4>(XP_GEMM_ARGS);
+      case 9: return launch_cfg<T, 128, 64, 2, 2, EPI, 3>(XP_GEMM_ARGS);
+      default: return launch_cfg<T, 128, 128, 2, 4, EPI, 2>(XP_GEMM_ARGS);
     }
   }
+#undef XP_GEMM_ARGS
 }
 
 template <typename T>
 xp_status launch_type(int epi, const void* A, const void* B, const void* B2, const void* R, void* C, int M, int N,
-                      int K, hipStream_t s) {
+                      int K, int splits, float* part, hipStream_t s) {
   switch (epi) {
-    case XP_EPI_F32: return launch_epi<T, XP_EPI_F32>(A, B, B2, R, C, M, N, K, s);
-    case XP_EPI_ADD_T: return launch_epi<T, XP_EPI_ADD_T>(A, B, B2, R, C, M, N, K, s);
-    case XP_EPI_ADD_F32: return launch_epi<T, XP_EPI_ADD_F32>(A, B, B2, R, C, M, N, K, s);
-    case XP_EPI_SWIGLU: return launch_epi<T, XP_EPI_SWIGLU>(A, B, B2, R, C, M, N, K, s);
+    case XP_EPI_F32: return launch_epi<T, XP_EPI_F32>(A, B, B2, R, C, M, N, K, splits, part, s);
+    case XP_EPI_ADD_T: return launch_epi<T, XP_EPI_ADD_T>(A, B, B2, R, C, M, N, K, splits, part, s);
+    case XP_EPI_ADD_F32: return launch_epi<T, XP_EPI_ADD_F32>(A, B, B2, R, C, M, N, K, splits, part, s);
+    case XP_EPI_SWIGLU: return launch_epi<T, XP_EPI_SWIGLU>(A, B, B2, R, C, M, N, K, splits, part, s);
   }
   return fail(XP_EINVAL, "xp_gemm: unknown epilogue %d", epi);
 }
 
 }  // namespace
 
+// K splits of a GEMM against an [N, K] weight: a function of the weight's shape only,
+// so a row's result never depends on how many rows share the call.  Only long-K,
+// narrow products (K >= 3N, the FFN down projection) are split: there a few rows
+// cannot fill the chip otherwise (128 rows: 70 -> 28 us for an 8B down projection),
+// while at 500-1000 rows the split costs at most a few percent.  Aim: with 256-row
+// tiles and about 1024 rows, (N / 256) x 4 x splits ~ 256 work units; at least 16
+// K stages per split; at most 4 splits.
+int gemm_splits(int dtype, int epi, int N, int K) {
+  const int nb = epi == XP_EPI_SWIGLU ? 2 : 1;
+  const int stages = K / (gemm::kRowBytes / dtype_bytes(dtype));
+  if (long(K) < 3L * N * nb) return 1;
+  int sp = int(16384.0 / (double(N) * nb) + 0.5);
+  sp = std::max(1, std::min(4, sp));
+  while (sp > 1 && stages / sp < 16) --sp;
+  return sp;
+}
+
+size_t gemm_ws_bytes(int dtype, int epi, int M, int N, int K) {
+  if (M <= 0 || N <= 0 || K <= 0) return 0;
+  const int sp = gemm_splits(dtype, epi, N, K);
+  if (sp <= 1) return 0;
+  return size_t(sp) * (epi == XP_EPI_SWIGLU ? 2 : 1) * size_t(M) * N * sizeof(float);
+}
+
 xp_status launch_gemm(int dtype, int epi, const void* A, const void* B, const void* B2, const void* R, void* C,
-                      int M, int N, int K, hipStream_t s) {
+                      int M, int N, int K, void* ws, size_t ws_bytes, hipStream_t s) {
   if (dtype != XP_BF16 && dtype != XP_F32) return fail(XP_EINVAL, "xp_gemm: dtype %d", dtype);
   if (M < 0 || N <= 0 || K <= 0) return fail(XP_ESHAPE, "xp_gemm: M=%d N=%d K=%d", M, N, K);
+  if (epi < XP_EPI_F32 || epi > XP_EPI_SWIGLU) return fail(XP_EINVAL, "xp_gemm: unknown epilogue %d", epi);
   const int bk = gemm::kRowBytes / dtype_bytes(dtype);
   if (K % bk) return fail(XP_EUNSUPPORTED, "xp_gemm: K=%d is not a multiple of %d", K, bk);
   // a buffer resource covers one tile's rows (<= 256), so its byte offsets must stay below 2^31
@@ -136,8 +180,13 @@ xp_status launch_gemm(int dtype, int epi, const void* A, const void* B, const vo
   if ((epi == XP_EPI_ADD_T || epi == XP_EPI_ADD_F32) && !R) return fail(XP_EINVAL, "xp_gemm: null residual");
   if (epi == XP_EPI_SWIGLU && !B2) return fail(XP_EINVAL, "xp_gemm: null second weight");
   if (M == 0) return XP_OK;
-  if (dtype == XP_BF16) return launch_type<bf16_t>(epi, A, B, B2, R, C, M, N, K, s);
-  return launch_type<float>(epi, A, B, B2, R, C, M, N, K, s);
+  const int splits = gemm_splits(dtype, epi, N, K);
+  const size_t need = gemm_ws_bytes(dtype, epi, M, N, K);
+  if (need && (!ws || ws_bytes < need))
+    return fail(XP_EWORKSPACE, "xp_gemm: needs %zu bytes of workspace (got %zu)", need, ws ? ws_bytes : size_t(0));
+  float* part = static_cast<float*>(ws);
+  if (dtype == XP_BF16) return launch_type<bf16_t>(epi, A, B, B2, R, C, M, N, K, splits, part, s);
+  return launch_type<float>(epi, A, B, B2, R, C, M, N, K, splits, part, s);
 }
 
 }  // namespace xp

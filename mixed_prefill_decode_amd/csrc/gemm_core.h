@@ -77,6 +77,11 @@ __device__ __forceinline__ void wait_vmcnt() {
 
 typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
 
+template <bool V>
+struct LiveTag {
+  static constexpr bool value = V;
+};
+
 // Buffer resource over `rows` rows of `row_bytes` starting at `base` (gfx9 layout: 48-bit
 // base, stride 0, num_records in bytes, default format word); reads past it return 0.
 __device__ __forceinline__ i32x4 rsrc_rows(const char* base, long rows, long row_bytes) {
@@ -115,7 +120,8 @@ template <typename T, int BM, int BN, int WGM, int WGN, int EPI, int STAGES>
 __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(const char* __restrict__ A, const char* __restrict__ B,
                                                                  const char* __restrict__ B2, const void* __restrict__ R,
                                                                  void* __restrict__ C, int M, int N, int K, int tiles_m,
-                                                                 int tiles_n) {
+                                                                 int tiles_n, int splits, int kt_per_split,
+                                                                 float* __restrict__ part) {
   using G = Cfg<T, BM, BN, WGM, WGN, EPI>;
   constexpr int NB = G::NB, FM = G::FM, FN = G::FN, CPK = G::CPK;
   constexpr int ROWS = G::ROWS, BK = G::BK, WM = G::WM, WN = G::WN;
@@ -125,11 +131,14 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(const char* __rest
   constexpr int IPW = INSTR / W;
   __shared__ uint4 lds[STAGES][ROWS * kChunks];
 
+  // work units: (tile, K split), M tiles fastest, then N tiles, then splits
   const int n_tiles = tiles_m * tiles_n;
+  const int n_units = n_tiles * splits;
   const int b = blockIdx.x;
-  const int q = n_tiles / 8, rem = n_tiles % 8, x = b % 8;
+  const int q = n_units / 8, rem = n_units % 8, x = b % 8;
   const int t = x * q + min(x, rem) + b / 8;
-  const int m0 = (t % tiles_m) * BM, n0 = (t / tiles_m) * BN;
+  const int tile = t % n_tiles, sp = t / n_tiles;
+  const int m0 = (tile % tiles_m) * BM, n0 = (tile / tiles_m) * BN;
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: scalar branches below
@@ -177,49 +186,83 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(const char* __rest
       for (int j = 0; j < FN; ++j) acc[nb][i][j] = f32x16{};
 
   const int lr = lane & 31, kg = lane >> 5;
-  const int nk = K / BK;
+  // this unit's K stages [kt0, kt0 + nk)
+  const int kt0 = sp * kt_per_split;
+  const int nk = min(K / BK - kt0, kt_per_split);
   constexpr int KS = BK / 16;     // 16-deep MFMA steps per stage
+  // A wave whose rows all lie past M (the last M tile of a ragged M) still issues
+  // its share of the loads and meets every barrier, but skips the LDS reads and MFMAs.
+  const bool live = m0 + wm * WM < M;
+  auto k_loop = [&](auto live_tag) {
+    constexpr bool LIVE = decltype(live_tag)::value;
 #pragma unroll
-  for (int s = 0; s < STAGES - 1; ++s)
-    if (s < nk) issue(s, s, 0, IPW);
-  for (int kt = 0; kt < nk; ++kt) {
-    // stage kt must have landed: the stages issued after it may stay in flight
-    const int after = min(STAGES - 2, nk - 1 - kt);
-    if constexpr (STAGES >= 3) {
-      if (after >= 1) wait_vmcnt<IPW>();
-      else wait_vmcnt<0>();
-    } else {
-      wait_vmcnt<0>();
+    for (int s = 0; s < STAGES - 1; ++s)
+      if (s < nk) issue(kt0 + s, s, 0, IPW);
+    for (int kt = 0; kt < nk; ++kt) {
+      // stage kt must have landed: the stages issued after it may stay in flight
+      const int after = min(STAGES - 2, nk - 1 - kt);
+      if constexpr (STAGES >= 3) {
+        if (after >= 1) wait_vmcnt<IPW>();
+        else wait_vmcnt<0>();
+      } else {
+        wait_vmcnt<0>();
+      }
+      // A bare barrier: every wave has waited for its own loads of stage kt above, and
+      // its reads of the slot refilled during this stage were consumed by MFMAs before
+      // it arrived.  (A fence here would also drain the stages still in flight.)
+      __builtin_amdgcn_s_barrier();
+      const bool refill = kt + STAGES - 1 < nk;
+      const int kn = kt0 + kt + STAGES - 1, bn = (kt + STAGES - 1) % STAGES;
+      const uint4* buf = lds[kt % STAGES];
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const int chunk = ks * CPK + kg * (CPK / 2);
+        Frag8<T> fa[FM], fb[NB][FN];
+        if constexpr (LIVE) {
+#pragma unroll
+          for (int i = 0; i < FM; ++i) lds_frag<T>(fa[i], buf, wm * WM + i * 32 + lr, chunk);
+#pragma unroll
+          for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+            for (int j = 0; j < FN; ++j) lds_frag<T>(fb[nb][j], buf, BM + nb * BN + wn * WN + j * 32 + lr, chunk);
+        }
+        // The next stage's loads, spread over the MFMA steps of this one.  With a
+        // two-slot ring they must land before the next barrier, so they go out in the
+        // first half of the steps; deeper rings spread them over all of them.
+        constexpr int SPREAD = STAGES == 2 ? (KS + 1) / 2 : KS;
+        if (refill && ks < SPREAD) issue(kn, bn, (IPW * ks) / SPREAD, (IPW * (ks + 1)) / SPREAD);
+        if constexpr (LIVE) {
+#pragma unroll
+          for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+            for (int i = 0; i < FM; ++i)
+#pragma unroll
+              for (int j = 0; j < FN; ++j) mma32x32_k16(acc[nb][i][j], fa[i], fb[nb][j]);
+        }
+      }
     }
-    // A bare barrier: every wave has waited for its own loads of stage kt above, and
-    // its reads of the slot refilled during this stage were consumed by MFMAs before
-    // it arrived.  (A fence here would also drain the stages still in flight.)
-    __builtin_amdgcn_s_barrier();
-    const bool refill = kt + STAGES - 1 < nk;
-    const int kn = kt + STAGES - 1, bn = (kt + STAGES - 1) % STAGES;
-    const uint4* buf = lds[kt % STAGES];
+  };
+  if (live) k_loop(LiveTag<true>{});
+  else k_loop(LiveTag<false>{});
+  if (!live) return;
+
+  if (splits > 1) {
+    // fp32 partial of this K split: part[sp][nb][row][col]
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      const int chunk = ks * CPK + kg * (CPK / 2);
-      Frag8<T> fa[FM], fb[NB][FN];
+    for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
-      for (int i = 0; i < FM; ++i) lds_frag<T>(fa[i], buf, wm * WM + i * 32 + lr, chunk);
+      for (int i = 0; i < FM; ++i)
 #pragma unroll
-      for (int nb = 0; nb < NB; ++nb)
+        for (int j = 0; j < FN; ++j) {
+          const int col = n0 + wn * WN + j * 32 + lr;
+          float* pp = part + (long(sp) * NB + nb) * long(M) * N;
 #pragma unroll
-        for (int j = 0; j < FN; ++j) lds_frag<T>(fb[nb][j], buf, BM + nb * BN + wn * WN + j * 32 + lr, chunk);
-      // The next stage's loads, spread over the MFMA steps of this one.  With a
-      // two-slot ring they must land before the next barrier, so they go out in the
-      // first half of the steps; deeper rings spread them over all of them.
-      constexpr int SPREAD = STAGES == 2 ? (KS + 1) / 2 : KS;
-      if (refill && ks < SPREAD) issue(kn, bn, (IPW * ks) / SPREAD, (IPW * (ks + 1)) / SPREAD);
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-        for (int i = 0; i < FM; ++i)
-#pragma unroll
-          for (int j = 0; j < FN; ++j) mma32x32_k16(acc[nb][i][j], fa[i], fb[nb][j]);
-    }
+          for (int r = 0; r < 16; ++r) {
+            const int row = m0 + wm * WM + i * 32 + 8 * (r >> 2) + 4 * kg + (r & 3);
+            if (row < M && col < N) pp[long(row) * N + col] = acc[nb][i][j][r];
+          }
+        }
+    return;
   }
 
 #pragma unroll
@@ -245,6 +288,29 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(const char* __rest
         }
       }
     }
+}
+
+// Sums the K-split partials of gemm_kernel in split order and applies the epilogue:
+// C = epi(sum_s part[s][0]) (SwiGLU: silu(sum_s part[s][0]) * sum_s part[s][1]).
+template <typename T, int EPI>
+__global__ __launch_bounds__(256) void gemm_reduce_kernel(const float* __restrict__ part, const void* __restrict__ R,
+                                                          void* __restrict__ C, long MN, int splits) {
+  constexpr int NB = (EPI == XP_EPI_SWIGLU) ? 2 : 1;
+  for (long idx = long(blockIdx.x) * 256 + threadIdx.x; idx < MN; idx += long(gridDim.x) * 256) {
+    float v = part[idx];
+    for (int s = 1; s < splits; ++s) v += part[long(s) * NB * MN + idx];
+    if constexpr (EPI == XP_EPI_F32) {
+      reinterpret_cast<float*>(C)[idx] = v;
+    } else if constexpr (EPI == XP_EPI_ADD_T) {
+      reinterpret_cast<float*>(C)[idx] = St<T>::load(R, idx) + v;
+    } else if constexpr (EPI == XP_EPI_ADD_F32) {
+      reinterpret_cast<float*>(C)[idx] = reinterpret_cast<const float*>(R)[idx] + v;
+    } else {
+      float u = part[MN + idx];
+      for (int s = 1; s < splits; ++s) u += part[(long(s) * NB + 1) * MN + idx];
+      St<T>::store(C, idx, v / (1.0f + __expf(-v)) * u);
+    }
+  }
 }
 
 }  // namespace gemm

@@ -31,8 +31,10 @@ inline int dtype_bytes(int dtype) { return dtype == XP_BF16 ? 2 : 4; }
 xp_status launch_rmsnorm(int dtype, const void* x, int x_is_f32, const void* gamma, void* y, int M,
                          int H, float eps, uint32_t* status_clear, hipStream_t s);
 
+int gemm_splits(int dtype, int epi, int N, int K);
+size_t gemm_ws_bytes(int dtype, int epi, int M, int N, int K);
 xp_status launch_gemm(int dtype, int epi, const void* A, const void* B, const void* B2, const void* R,
-                      void* C, int M, int N, int K, hipStream_t s);
+                      void* C, int M, int N, int K, void* ws, size_t ws_bytes, hipStream_t s);
 
 struct PostQkvArgs {
   const float* qkv;

@@ -167,6 +167,18 @@ def test_decode_workspace_size_matches_layer_layout():
     assert X.xp_decode_workspace_size(4, 8, 2, 128, 10, -1) == 0
 
 
+def test_gemm_workspace_depends_on_the_weight_shape_only():
+    # host-only: K splits follow (N, K); the partials take splits x weights x M x N fp32
+    for M in (16, 300, 1040):
+        assert X.xp_gemm_workspace_size(X.XP_BF16, X.XP_EPI_ADD_F32, M, 4096, 14336) == 4 * M * 4096 * 4
+        assert X.xp_gemm_workspace_size(X.XP_BF16, X.XP_EPI_ADD_F32, M, 5120, 25600) == 3 * M * 5120 * 4
+        assert X.xp_gemm_workspace_size(X.XP_BF16, X.XP_EPI_F32, M, 6144, 4096) == 0     # K < 3N: not split
+        assert X.xp_gemm_workspace_size(X.XP_BF16, X.XP_EPI_SWIGLU, M, 14336, 4096) == 0
+        assert X.xp_gemm_workspace_size(X.XP_BF16, X.XP_EPI_SWIGLU, M, 512, 4096) == 4 * 2 * M * 512 * 4
+    assert X.xp_gemm_workspace_size(X.XP_BF16, X.XP_EPI_F32, 64, 512, 512) == 0   # too few K stages
+    assert X.xp_gemm_workspace_size(X.XP_BF16, 9, 64, 512, 4096) == 0
+
+
 def test_gemm_rejects_unsupported_k_before_launching():
     with pytest.raises(X.XpError) as e:
         X.xp_gemm(X.XP_BF16, X.XP_EPI_F32, 16, 16, None, None, 16, 4, 4, 100, stream=0)

@@ -32,8 +32,17 @@ def _sync():
     torch.cuda.synchronize()
 
 
+def _gemm_ws(dtype, epi, M, N, K):
+    n = X.xp_gemm_workspace_size(DT[dtype], epi, M, N, K)
+    return torch.empty(max(n, 256), dtype=torch.uint8, device="cuda"), n
+
+
+# (300, 512, 4096) is split over K in every epilogue (4 splits), (260, 512, 2048) in
+# the single-weight ones (bf16: 2, fp32: 4); 260 and 1040 rows leave the last
+# 256-row tile with 4 and 16 live rows
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
-@pytest.mark.parametrize("M,N,K", [(1, 64, 128), (67, 200, 256), (130, 257, 192), (300, 512, 1024)])
+@pytest.mark.parametrize("M,N,K", [(1, 64, 128), (67, 200, 256), (130, 257, 192), (300, 512, 1024),
+                                   (300, 512, 4096), (260, 512, 2048), (1040, 1024, 1024)])
 def test_gemm_epilogues(dtype, M, N, K):
     rng = np.random.default_rng(M * 7919 + N)
     A, B, B2 = _rand(rng, (M, K), dtype), _rand(rng, (N, K), dtype, 0.05), _rand(rng, (N, K), dtype, 0.05)
@@ -45,11 +54,13 @@ def test_gemm_epilogues(dtype, M, N, K):
     C32 = torch.empty((M, N), dtype=torch.float32, device="cuda")
     for epi, R, ref in ((X.XP_EPI_F32, None, acc), (X.XP_EPI_ADD_T, dRt, to_f64(Rt, dtype) + acc),
                         (X.XP_EPI_ADD_F32, dRf, Rf.astype(np.float64) + acc)):
-        X.xp_gemm(DT[dtype], epi, dA, dB, None, R, C32, M, N, K)
+        ws, n = _gemm_ws(dtype, epi, M, N, K)
+        X.xp_gemm(DT[dtype], epi, dA, dB, None, R, C32, M, N, K, ws, n)
         _sync()
         assert rel_fro(C32.cpu().numpy(), ref) < 1e-5, epi
     Cs = torch.empty((M, N), dtype=torch.bfloat16 if dtype == "bf16" else torch.float32, device="cuda")
-    X.xp_gemm(DT[dtype], X.XP_EPI_SWIGLU, dA, dB, dB2, None, Cs, M, N, K)
+    ws, n = _gemm_ws(dtype, X.XP_EPI_SWIGLU, M, N, K)
+    X.xp_gemm(DT[dtype], X.XP_EPI_SWIGLU, dA, dB, dB2, None, Cs, M, N, K, ws, n)
     _sync()
     g, u = acc, a64 @ b264.T
     ref = g / (1 + np.exp(-g)) * u
@@ -69,6 +80,30 @@ def test_gemm_rows_do_not_depend_on_the_batch():
     X.xp_gemm(X.XP_BF16, X.XP_EPI_F32, dA[100:140].contiguous(), dB, None, None, part, 40, N, K)
     _sync()
     assert torch.equal(full[100:140], part)
+
+
+@pytest.mark.parametrize("epi", [X.XP_EPI_F32, X.XP_EPI_SWIGLU])
+def test_gemm_split_rows_do_not_depend_on_the_batch(epi):
+    # a projection split over K (the down-projection shape of an 8B layer, and a
+    # gate/up shape with two splits): rows inside a 1040-row batch equal the same
+    # rows computed alone, bit for bit
+    N, K = (4096, 14336) if epi == X.XP_EPI_F32 else (512, 4096)
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(11)
+    A = torch.randn(1040, K, device="cuda", generator=gen).bfloat16()
+    B = (torch.randn(N, K, device="cuda", generator=gen) * 0.05).bfloat16()
+    B2 = (torch.randn(N, K, device="cuda", generator=gen) * 0.05).bfloat16() if epi == X.XP_EPI_SWIGLU else None
+    odt = torch.float32 if epi == X.XP_EPI_F32 else torch.bfloat16
+    outs = []
+    for lo, hi in ((0, 1040), (1024, 1040)):
+        M = hi - lo
+        ws, n = _gemm_ws("bf16", epi, M, N, K)
+        assert n > 0      # split over K
+        C = torch.empty((M, N), dtype=odt, device="cuda")
+        X.xp_gemm(X.XP_BF16, epi, A[lo:hi].contiguous(), B, B2, None, C, M, N, K, ws, n)
+        outs.append(C)
+    _sync()
+    assert torch.equal(outs[0][1024:].view(torch.int16), outs[1].view(torch.int16))
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
