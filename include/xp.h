@@ -246,6 +246,13 @@ xp_status xp_rmsnorm(int32_t dtype, const void* x, int32_t x_is_f32, const void*
 #define XP_EPI_ADD_F32 2
 #define XP_EPI_SWIGLU 3
 size_t xp_gemm_workspace_size(int32_t dtype, int32_t epilogue, int32_t M, int32_t N, int32_t K);
+/* The work unit xp_gemm would use for this product on the current device (a
+ * 256-CU device when none is visible): *bm x *bn outputs and *splits K splits.  The
+ * tile follows from (dtype, epilogue, M, N, K) and the CU count only.  Host only: no
+ * device memory is touched and nothing is launched.  XP_EINVAL / XP_ESHAPE on bad
+ * arguments. */
+xp_status xp_gemm_tile(int32_t dtype, int32_t epilogue, int32_t M, int32_t N, int32_t K, int32_t* bm,
+                       int32_t* bn, int32_t* splits);
 xp_status xp_gemm(int32_t dtype, int32_t epilogue, const void* A, const void* B, const void* B2,
                   const void* R, void* C, int32_t M, int32_t N, int32_t K, void* workspace,
                   size_t workspace_bytes, void* stream);

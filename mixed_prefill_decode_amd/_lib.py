@@ -16,7 +16,7 @@ __all__ = ["XpError", "lib", "XP_F32", "XP_BF16", "XP_EPI_F32", "XP_EPI_ADD_T", 
            "XP_EPI_SWIGLU", "XP_DEV_BAD_PAGE", "LayerShape", "LayerWeights", "KvPages", "BatchDesc",
            "WsLayout", "LatencyModel", "Ctx", "EXPORTED",
            "xp_ctx_create", "xp_layer_workspace_layout", "xp_layer_forward", "xp_validate_batch",
-           "xp_layer_read_status", "xp_rmsnorm", "xp_gemm_workspace_size", "xp_gemm", "xp_kv_append",
+           "xp_layer_read_status", "xp_rmsnorm", "xp_gemm_workspace_size", "xp_gemm_tile", "xp_gemm", "xp_kv_append",
            "xp_kv_gather",
            "xp_decode_workspace_size", "xp_decode_attention", "xp_prefill_workspace_size", "xp_prefill_attention",
            "xp_probe_hw_ids",
@@ -34,7 +34,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libxp.so")
 EXPORTED = ["xp_last_error", "xp_build_info", "xp_ctx_create", "xp_ctx_destroy", "xp_ctx_cu_masks",
             "xp_ctx_streams",
             "xp_layer_workspace_layout", "xp_layer_forward", "xp_validate_batch", "xp_layer_read_status",
-            "xp_rmsnorm", "xp_gemm_workspace_size", "xp_gemm", "xp_kv_append", "xp_kv_gather",
+            "xp_rmsnorm", "xp_gemm_workspace_size", "xp_gemm_tile", "xp_gemm", "xp_kv_append", "xp_kv_gather",
             "xp_decode_workspace_size",
             "xp_decode_attention", "xp_prefill_workspace_size", "xp_prefill_attention", "xp_probe_hw_ids",
             "xp_waterfill",
@@ -117,6 +117,7 @@ def _declare(L):
         "xp_layer_read_status": (S, [_vp, C.POINTER(WsLayout), _vp, _vp]),
         "xp_rmsnorm": (S, [_i32, _vp, _i32, _vp, _vp, _i32, _i32, _f32, _vp]),
         "xp_gemm_workspace_size": (_sz, [_i32, _i32, _i32, _i32, _i32]),
+        "xp_gemm_tile": (S, [_i32, _i32, _i32, _i32, _i32, C.POINTER(_i32), C.POINTER(_i32), C.POINTER(_i32)]),
         "xp_gemm": (S, [_i32, _i32, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _vp, _sz, _vp]),
         "xp_kv_append": (S, [_i32, _vp, _i32, _i32, _i32, _vp, _i32, _vp, _vp, _vp, _vp, _i32, _vp]),
         "xp_kv_gather": (S, [_i32, _vp, _i32, _i32, _i32, _vp, _i32, _vp, _i32, _i32, _vp, _vp, _vp]),
@@ -250,6 +251,13 @@ def xp_rmsnorm(dtype, x, x_is_f32, gamma, y, M, H, eps, stream=None):
 
 def xp_gemm_workspace_size(dtype, epilogue, M, N, K) -> int:
     return int(lib().xp_gemm_workspace_size(dtype, epilogue, M, N, K))
+
+
+def xp_gemm_tile(dtype, epilogue, M, N, K) -> tuple:
+    """(rows, columns, K splits) of the work unit xp_gemm would use for this product."""
+    bm, bn, sp = _i32(), _i32(), _i32()
+    _check(lib().xp_gemm_tile(dtype, epilogue, M, N, K, C.byref(bm), C.byref(bn), C.byref(sp)))
+    return bm.value, bn.value, sp.value
 
 
 def xp_gemm(dtype, epilogue, A, B, B2, R, Cout, M, N, K, workspace=None, workspace_bytes=0, stream=None):

@@ -397,6 +397,20 @@ size_t xp_gemm_workspace_size(int32_t dtype, int32_t epi, int32_t M, int32_t N, 
   return gemm_ws_bytes(dtype, epi, M, N, K);
 }
 
+xp_status xp_gemm_tile(int32_t dtype, int32_t epi, int32_t M, int32_t N, int32_t K, int32_t* bm, int32_t* bn,
+                       int32_t* splits) {
+  if (dtype != XP_BF16 && dtype != XP_F32) return fail(XP_EINVAL, "xp_gemm_tile: dtype %d", dtype);
+  if (epi < XP_EPI_F32 || epi > XP_EPI_SWIGLU) return fail(XP_EINVAL, "xp_gemm_tile: unknown epilogue %d", epi);
+  if (M <= 0 || N <= 0 || K <= 0) return fail(XP_ESHAPE, "xp_gemm_tile: M=%d N=%d K=%d", M, N, K);
+  if (!bm || !bn || !splits) return fail(XP_EINVAL, "xp_gemm_tile: null output");
+  int a = 0, b = 0, sp = 0;
+  gemm_tile(dtype, epi, M, N, K, &a, &b, &sp);
+  *bm = a;
+  *bn = b;
+  *splits = sp;
+  return XP_OK;
+}
+
 xp_status xp_gemm(int32_t dtype, int32_t epi, const void* A, const void* B, const void* B2, const void* R, void* C,
                   int32_t M, int32_t N, int32_t K, void* workspace, size_t workspace_bytes, void* stream) {
   return launch_gemm(dtype, epi, A, B, B2, R, C, M, N, K, workspace, workspace_bytes,

@@ -38,34 +38,32 @@ xp_status launch_cfg(const void* A, const void* B, const void* B2, const void* R
 
 struct Candidate {
   int id, bm, bn, per_cu;   // tile, workgroups resident per CU (LDS- and wave-limited)
-  double tflops;            // measured rate of one resident workgroup (bf16, TFLOP/s)
-  double tflops_split;      // the same for a K-split work unit (a quarter to a third of K)
+  double tflops;            // fitted rate of one resident workgroup (bf16, TFLOP/s)
 };
 
 // Per epilogue kind: single weight (plain / residual epilogues) and dual weight
-// (SwiGLU).  Rates are per resident workgroup, fitted over the QKV, O, gate/up and
-// down projections of the 8B, 14B and 32B layer shapes at 128 to 1040 rows; a call
-// then takes rounds x (work-unit flops / rate), rounds counting waves of resident
-// workgroups.  Over those 16 shapes the picks total within 1% of the best measured.
+// (SwiGLU).  A call is modelled as rounds x (work-unit flops / rate), rounds counting
+// waves of resident workgroups (a grid of 1.1 rounds takes as long as 2).  The rates
+// are fitted so that the model's pick is the fastest measured candidate on the QKV,
+// O, gate/up and down projections of the 8B, 14B and 32B layer shapes at 128 to 1040
+// rows and the 14B shape at 8216 rows (all picks within 1% of the best measured); they
+// rank the candidates rather than describe them.  Tiles of 96 and 192 rows exist for
+// row counts such as 1040 = 1024 + 16, where 128-row tiles leave a nearly empty extra
+// tile row (and so a second round of workgroups).
 constexpr Candidate kSingle[] = {
-    {0, 128, 128, 2, 3.26, 2.54},   // 2x4 waves, 2-stage ring (64 KB LDS)
-    {1, 128, 128, 1, 4.75, 4.06},   // 2x4 waves, 3-stage ring (96 KB)
-    {2, 128, 256, 1, 5.25, 4.53},   // 2x4 waves, 2-stage ring (96 KB)
-    {3, 64, 128, 2, 2.15, 1.75},    // 1x4 waves, 3-stage ring (72 KB)
-    {4, 256, 128, 1, 5.23, 4.76},   // 4x2 waves, 2-stage ring (96 KB)
-    {5, 256, 256, 1, 7.38, 6.24},   // 2x4 waves, 2-stage ring (128 KB)
-    {6, 128, 128, 1, 5.00, 4.16},   // 2x4 waves, 4-stage ring (128 KB)
-    {7, 128, 256, 1, 6.40, 5.16},   // 2x4 waves, 3-stage ring (144 KB)
-    {8, 64, 128, 1, 3.06, 2.67},    // 1x4 waves, 4-stage ring (96 KB)
-    {9, 128, 64, 2, 2.28, 1.98},    // 2x2 waves, 3-stage ring (72 KB)
+    {0, 64, 128, 1, 4.59},    // 1x4 waves, 4-stage ring (96 KB LDS)
+    {1, 96, 128, 1, 5.50},    // 1x4 waves, 4-stage ring (112 KB)
+    {2, 128, 256, 1, 6.65},   // 2x4 waves, 3-stage ring (144 KB)
+    {3, 192, 128, 1, 7.03},   // 2x4 waves, 4-stage ring (160 KB)
+    {4, 192, 192, 1, 6.88},   // 2x2 waves, 3-stage ring (144 KB)
+    {5, 256, 256, 1, 11.61},  // 2x4 waves, 2-stage ring (128 KB)
 };
 constexpr Candidate kDual[] = {
-    {0, 128, 128, 1, 3.68, 3.68},   // 2x4 waves, 2-stage ring (96 KB)
-    {1, 128, 128, 1, 4.78, 4.78},   // 2x4 waves, 3-stage ring (144 KB)
-    {2, 128, 256, 1, 4.64, 4.64},   // 2x4 waves, 2-stage ring (160 KB)
-    {3, 64, 128, 1, 3.29, 3.29},    // 1x4 waves, 3-stage ring (120 KB)
-    {4, 256, 128, 1, 6.23, 6.23},   // 4x2 waves, 2-stage ring (128 KB)
-    {5, 128, 64, 1, 3.89, 3.89},    // 2x2 waves, 3-stage ring (96 KB)
+    {0, 128, 64, 1, 8.03},    // 2x2 waves, 3-stage ring (96 KB)
+    {4, 128, 128, 1, 10.32},  // 2x4 waves, 3-stage ring (144 KB)
+    {1, 192, 64, 1, 8.98},    // 2x2 waves, 3-stage ring (120 KB)
+    {2, 192, 128, 1, 10.32},  // 2x4 waves, 2-stage ring (112 KB)
+    {3, 256, 128, 1, 11.05},  // 4x2 waves, 2-stage ring (128 KB)
 };
 
 template <size_t NC>
@@ -76,8 +74,7 @@ int pick(const Candidate (&c)[NC], int M, int N, int K, int n_cus, int nb, int s
     const long units = long(cdiv(M, x.bm)) * cdiv(N, x.bn) * splits;
     const long slots = long(n_cus) * x.per_cu;
     const double rounds = double((units + slots - 1) / slots);
-    const double rate = splits > 1 ? x.tflops_split : x.tflops;
-    const double t = rounds * 2.0 * x.bm * x.bn * nb * (double(K) / splits) / (rate * 1e12);
+    const double t = rounds * 2.0 * x.bm * x.bn * nb * (double(K) / splits) / (x.tflops * 1e12);
     if (t < best) {
       best = t;
       id = x.id;
@@ -105,25 +102,20 @@ xp_status launch_epi(const void* A, const void* B, const void* B2, const void* R
 #define XP_GEMM_ARGS A, B, B2, R, C, M, N, K, splits, part, s
   if constexpr (EPI == XP_EPI_SWIGLU) {
     switch (pick(kDual, M, N, K, cus, 2, splits)) {
-      case 1: return launch_cfg<T, 128, 128, 2, 4, EPI, 3>(XP_GEMM_ARGS);
-      case 2: return launch_cfg<T, 128, 256, 2, 4, EPI, 2>(XP_GEMM_ARGS);
-      case 3: return launch_cfg<T, 64, 128, 1, 4, EPI, 3>(XP_GEMM_ARGS);
-      case 4: return launch_cfg<T, 256, 128, 4, 2, EPI, 2>(XP_GEMM_ARGS);
-      case 5: return launch_cfg<T, 128, 64, 2, 2, EPI, 3>(XP_GEMM_ARGS);
-      default: return launch_cfg<T, 128, 128, 2, 4, EPI, 2>(XP_GEMM_ARGS);
+      case 1: return launch_cfg<T, 192, 64, 2, 2, EPI, 3>(XP_GEMM_ARGS);
+      case 2: return launch_cfg<T, 192, 128, 2, 4, EPI, 2>(XP_GEMM_ARGS);
+      case 3: return launch_cfg<T, 256, 128, 4, 2, EPI, 2>(XP_GEMM_ARGS);
+      case 4: return launch_cfg<T, 128, 128, 2, 4, EPI, 3>(XP_GEMM_ARGS);
+      default: return launch_cfg<T, 128, 64, 2, 2, EPI, 3>(XP_GEMM_ARGS);
     }
   } else {
     switch (pick(kSingle, M, N, K, cus, 1, splits)) {
-      case 1: return launch_cfg<T, 128, 128, 2, 4, EPI, 3>(XP_GEMM_ARGS);
-      case 2: return launch_cfg<T, 128, 256, 2, 4, EPI, 2>(XP_GEMM_ARGS);
-      case 3: return launch_cfg<T, 64, 128, 1, 4, EPI, 3>(XP_GEMM_ARGS);
-      case 4: return launch_cfg<T, 256, 128, 4, 2, EPI, 2>(XP_GEMM_ARGS);
+      case 1: return launch_cfg<T, 96, 128, 1, 4, EPI, 4>(XP_GEMM_ARGS);
+      case 2: return launch_cfg<T, 128, 256, 2, 4, EPI, 3>(XP_GEMM_ARGS);
+      case 3: return launch_cfg<T, 192, 128, 2, 4, EPI, 4>(XP_GEMM_ARGS);
+      case 4: return launch_cfg<T, 192, 192, 2, 2, EPI, 3>(XP_GEMM_ARGS);
       case 5: return launch_cfg<T, 256, 256, 2, 4, EPI, 2>(XP_GEMM_ARGS);
-      case 6: return launch_cfg<T, 128, 128, 2, 4, EPI, 4>(XP_GEMM_ARGS);
-      case 7: return launch_cfg<T, 128, 256, 2, 4, EPI, 3>(XP_GEMM_ARGS);
-      case 8: return launch_cfg<T, 64, 128, 1, 4, EPI, 4>(XP_GEMM_ARGS);
-      case 9: return launch_cfg<T, 128, 64, 2, 2, EPI, 3>(XP_GEMM_ARGS);
-      default: return launch_cfg<T, 128, 128, 2, 4, EPI, 2>(XP_GEMM_ARGS);
+      default: return launch_cfg<T, 64, 128, 1, 4, EPI, 4>(XP_GEMM_ARGS);
     }
   }
 #undef XP_GEMM_ARGS
@@ -152,12 +144,28 @@ xp_status launch_type(int epi, const void* A, const void* B, const void* B2, con
 // K stages per split; at most 4 splits.
 int gemm_splits(int dtype, int epi, int N, int K) {
   const int nb = epi == XP_EPI_SWIGLU ? 2 : 1;
-  const int stages = K / (gemm::kRowBytes / dtype_bytes(dtype));
+  const int stages = K / (128 / dtype_bytes(dtype));
   if (long(K) < 3L * N * nb) return 1;
   int sp = int(16384.0 / (double(N) * nb) + 0.5);
   sp = std::max(1, std::min(4, sp));
   while (sp > 1 && stages / sp < 16) --sp;
   return sp;
+}
+
+void gemm_tile(int dtype, int epi, int M, int N, int K, int* bm, int* bn, int* splits) {
+  const int sp = gemm_splits(dtype, epi, N, K);
+  const int cus = n_cus_of_current_device();
+  const Candidate* c = nullptr;
+  if (epi == XP_EPI_SWIGLU) {
+    const int id = pick(kDual, M, N, K, cus, 2, sp);
+    for (const Candidate& x : kDual) if (x.id == id) c = &x;
+  } else {
+    const int id = pick(kSingle, M, N, K, cus, 1, sp);
+    for (const Candidate& x : kSingle) if (x.id == id) c = &x;
+  }
+  *bm = c ? c->bm : 0;
+  *bn = c ? c->bn : 0;
+  *splits = sp;
 }
 
 size_t gemm_ws_bytes(int dtype, int epi, int M, int N, int K) {
@@ -172,7 +180,7 @@ xp_status launch_gemm(int dtype, int epi, const void* A, const void* B, const vo
   if (dtype != XP_BF16 && dtype != XP_F32) return fail(XP_EINVAL, "xp_gemm: dtype %d", dtype);
   if (M < 0 || N <= 0 || K <= 0) return fail(XP_ESHAPE, "xp_gemm: M=%d N=%d K=%d", M, N, K);
   if (epi < XP_EPI_F32 || epi > XP_EPI_SWIGLU) return fail(XP_EINVAL, "xp_gemm: unknown epilogue %d", epi);
-  const int bk = gemm::kRowBytes / dtype_bytes(dtype);
+  const int bk = 128 / dtype_bytes(dtype);
   if (K % bk) return fail(XP_EUNSUPPORTED, "xp_gemm: K=%d is not a multiple of %d", K, bk);
   // a buffer resource covers one tile's rows (<= 256), so its byte offsets must stay below 2^31
   if (256L * K * dtype_bytes(dtype) >= (1L << 31)) return fail(XP_EUNSUPPORTED, "xp_gemm: K=%d too large", K);

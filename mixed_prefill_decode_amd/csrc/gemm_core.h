@@ -1,25 +1,29 @@
-// The MFMA GEMM, as a template over block tile, wave grid and LDS ring depth.
+// The MFMA GEMM, as a template over block tile, wave grid, LDS ring depth and stage
+// row size.
 //
 // C = epilogue(A B^T): A [M, K] and B [N, K] (K contiguous), fp32 accumulation.
 // Block tile BM x BN, WGM x WGN waves, wave tile (BM/WGM) x (BN/WGN) made of
-// 32x32 MFMA blocks.  Each stage is a 128-byte slice of K per row (64 bf16 or 32
-// fp32), copied from HBM straight into an LDS ring (buffer_load ... lds: no staging
-// registers, no LDS store instructions) whose 16-byte chunks are XOR-swizzled by
-// ((row >> 1) & 7).  gfx950's LDS serves a 16-byte-per-lane read 16 lanes at a time
-// across 64 four-byte banks (256 bytes): the 16 rows such a group reads are 8
-// row pairs, and a pair spans the 64 banks once, so the swizzle gives the 8 pairs
-// 8 different chunk positions and the group hits every bank exactly once.  The
-// SwiGLU epilogue reads two weight tiles (gate, up) against the same A tile and
-// keeps both accumulators, so silu(g) * u is formed in registers.
+// 32x32 MFMA blocks.  Each stage is an RB-byte slice of K per row (RB = 128: 64 bf16
+// or 32 fp32), copied from HBM straight into an LDS ring (buffer_load ... lds: no
+// staging registers, no LDS store instructions) whose 16-byte chunks are
+// XOR-swizzled per row (see Rows).  The SwiGLU epilogue reads two weight tiles
+// (gate, up) against the same A tile and keeps both accumulators, so silu(g) * u is
+// formed in registers.
+//
+// Inside a stage the fragments of the next 16-deep step are read from LDS while the
+// current step's MFMAs run.  Measured on MI355X, these kernels are bound by the vector
+// memory path that fills the ring (the address and data units are 85-90% busy, mostly
+// waiting on L2 reads of about 600 cycles), then by LDS reads; with both taken out the
+// same loop reaches 0.8 of the bf16 peak.
 //
 // Block order is XCD-aware: workgroups are dealt to the 8 XCDs round-robin, so
 // block b is remapped to tile (b % 8) * per_xcd + b / 8 with tiles ordered
 // M-fastest; the M tiles that share one weight tile then run on one XCD and
 // share its L2.
 //
-// The K loop order (128-byte stages, 16-deep MFMA steps, in order) is the same for
-// every M and every tile shape, so a row's result does not depend on which other
-// rows are co-batched with it.
+// The K loop order (16-deep MFMA steps, in order) is the same for every M and every
+// tile shape, so a row's result does not depend on which other rows are co-batched
+// with it.
 #pragma once
 #include "xp_device.h"
 #include "../../include/xp.h"
@@ -27,30 +31,36 @@
 namespace xp {
 namespace gemm {
 
-constexpr int kRowBytes = 128;
-constexpr int kChunks = 8;  // 16-byte chunks per LDS row
+// Stage rows are RB bytes of K: 128 (8 chunks of 16 bytes) or 64 (4 chunks).  The
+// chunk position of a row is XOR-swizzled so that the 16 consecutive rows one
+// 16-lane group of a fragment read touches cover the 64 banks once: with 128-byte
+// rows a row pair spans the banks and the 8 pairs get 8 positions ((row >> 1) & 7);
+// with 64-byte rows 4 rows span them and the 4 quads get 4 positions ((row >> 2) & 3).
+template <int RB>
+struct Rows {
+  static constexpr int chunks = RB / 16;
+  static_assert(RB == 64 || RB == 128, "stage rows are 64 or 128 bytes");
+  __device__ static __forceinline__ int swz_of(int row) { return RB == 128 ? (row >> 1) & 7 : (row >> 2) & 3; }
+  __device__ static __forceinline__ int swz(int row, int chunk) { return row * chunks + (chunk ^ swz_of(row)); }
+};
 
-__device__ __forceinline__ int swz_of(int row) { return (row >> 1) & 7; }
-__device__ __forceinline__ int swz(int row, int chunk) { return row * kChunks + (chunk ^ swz_of(row)); }
-
-template <typename T>
-__device__ __forceinline__ void lds_frag(Frag8<T>& f, const uint4* buf, int row, int chunk);
-template <>
-__device__ __forceinline__ void lds_frag(Frag8<bf16_t>& f, const uint4* buf, int row, int chunk) {
-  f.v = buf[swz(row, chunk)];
+template <typename T, int RB>
+__device__ __forceinline__ void lds_frag(Frag8<T>& f, const uint4* buf, int row, int chunk) {
+  using Rw = Rows<RB>;
+  if constexpr (sizeof(Frag8<T>) == 16) {
+    f.v = buf[Rw::swz(row, chunk)];
+  } else {
+    uint4 a = buf[Rw::swz(row, chunk)], b = buf[Rw::swz(row, chunk + 1)];
+    f.lo = __builtin_bit_cast(float4, a);
+    f.hi = __builtin_bit_cast(float4, b);
+  }
 }
-template <>
-__device__ __forceinline__ void lds_frag(Frag8<float>& f, const uint4* buf, int row, int chunk) {
-  uint4 a = buf[swz(row, chunk)], b = buf[swz(row, chunk + 1)];
-  f.lo = __builtin_bit_cast(float4, a);
-  f.hi = __builtin_bit_cast(float4, b);
-}
 
-template <typename T, int BM, int BN, int WGM, int WGN, int EPI>
+template <typename T, int BM, int BN, int WGM, int WGN, int EPI, int RB = 128>
 struct Cfg {
   static constexpr int THREADS = 64 * WGM * WGN;
   static constexpr int EB = St<T>::bytes;
-  static constexpr int BK = kRowBytes / EB;
+  static constexpr int BK = RB / EB;
   static constexpr int NB = (EPI == XP_EPI_SWIGLU) ? 2 : 1;
   static constexpr int WM = BM / WGM, WN = BN / WGN;
   static constexpr int FM = WM / 32, FN = WN / 32;
@@ -60,13 +70,13 @@ struct Cfg {
 };
 
 // ---------------------------------------------------------------------------
-// Loads: a wave instruction fills 8 consecutive LDS rows (64 lanes x 16 B,
-// lane-contiguous); lane l fetches global chunk (l % 8) ^ swz_of(row) of its row so
-// the LDS image is the XOR-swizzled layout the fragment reads expect.  Each operand's
-// buffer resource starts at the tile's first row and covers only its valid rows, so
-// rows past M or N read as zero without any per-load check.  STAGES-deep ring:
-// stage kt + STAGES - 1 is issued right after the barrier that ends the reads of the
-// buffer it overwrites.
+// Loads: a wave instruction fills 1024 bytes of consecutive LDS rows (64 lanes x 16 B,
+// lane-contiguous); lane l fetches global chunk (l % chunks) ^ swz_of(row) of its row
+// so the LDS image is the XOR-swizzled layout the fragment reads expect.  Each
+// operand's buffer resource starts at the tile's first row and covers only its valid
+// rows, so rows past M or N read as zero without any per-load check.  STAGES-deep
+// ring: stage kt + STAGES - 1 is issued after the barrier that ends the reads of the
+// slot it overwrites.
 // ---------------------------------------------------------------------------
 
 template <int N>
@@ -76,6 +86,15 @@ __device__ __forceinline__ void wait_vmcnt() {
 }
 
 typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ void wait_lgkmcnt0() { __builtin_amdgcn_s_waitcnt(0xc07f); }
+
+// s_barrier with compiler fences on both sides: no LDS access moves across it.
+__device__ __forceinline__ void barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
 
 template <bool V>
 struct LiveTag {
@@ -92,6 +111,12 @@ __device__ __forceinline__ i32x4 rsrc_rows(const char* base, long rows, long row
   r.y = __builtin_amdgcn_readfirstlane(int32_t((a >> 32) & 0xffffu));
   r.z = __builtin_amdgcn_readfirstlane(int32_t(n));
   r.w = 0x00020000;
+  return r;
+}
+
+// the resource itself (mask -1) or the same resource with no records (mask 0)
+__device__ __forceinline__ i32x4 gate(i32x4 r, int mask) {
+  r.z &= mask;
   return r;
 }
 
@@ -116,20 +141,23 @@ __device__ __forceinline__ void load_lds16_so(i32x4 r, uint32_t lds_addr, int vo
 }
 #pragma clang diagnostic pop
 
-template <typename T, int BM, int BN, int WGM, int WGN, int EPI, int STAGES>
+template <typename T, int BM, int BN, int WGM, int WGN, int EPI, int STAGES, int RB = 128>
 __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(const char* __restrict__ A, const char* __restrict__ B,
                                                                  const char* __restrict__ B2, const void* __restrict__ R,
                                                                  void* __restrict__ C, int M, int N, int K, int tiles_m,
                                                                  int tiles_n, int splits, int kt_per_split,
                                                                  float* __restrict__ part) {
-  using G = Cfg<T, BM, BN, WGM, WGN, EPI>;
+  using G = Cfg<T, BM, BN, WGM, WGN, EPI, RB>;
+  using Rw = Rows<RB>;
   constexpr int NB = G::NB, FM = G::FM, FN = G::FN, CPK = G::CPK;
   constexpr int ROWS = G::ROWS, BK = G::BK, WM = G::WM, WN = G::WN;
   constexpr int W = WGM * WGN;
-  constexpr int INSTR = ROWS / 8;        // wave instructions per stage
+  constexpr int CH = Rw::chunks;
+  constexpr int LR = 64 / CH;            // LDS rows one wave instruction fills
+  constexpr int INSTR = ROWS / LR;       // wave instructions per stage
   static_assert(INSTR % W == 0, "stage rows must split evenly over the waves");
   constexpr int IPW = INSTR / W;
-  __shared__ uint4 lds[STAGES][ROWS * kChunks];
+  __shared__ uint4 lds[STAGES][ROWS * CH];
 
   // work units: (tile, K split), M tiles fastest, then N tiles, then splits
   const int n_tiles = tiles_m * tiles_n;
@@ -147,33 +175,35 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(const char* __rest
   const auto ra = rsrc_rows(A + m0 * kbytes, min(BM, M - m0), kbytes);
   const auto rb = rsrc_rows(B + n0 * kbytes, min(BN, N - n0), kbytes);
   const auto rb2 = rsrc_rows((NB == 2 ? B2 : B) + n0 * kbytes, min(BN, N - n0), kbytes);
-  const int lrow = lane >> 3;
+  const int lrow = lane / CH;
 
-  // Load instruction i of a wave fills LDS rows (i * W + wave) * 8 .. + 7 of a stage.
-  // W * 8 divides BM and BN, so whether instruction i reads A, B or B2 depends on i
-  // alone; its per-lane byte offset inside the operand is fixed for the whole K loop
-  // and the stage's K position is added as a scalar offset.
-  constexpr int RPI = 8 * W;
+  // Load instruction i of a wave fills LDS rows (i * W + wave) * LR .. + LR - 1 of a
+  // stage.  W * LR divides BM and BN, so whether instruction i reads A, B or B2 depends
+  // on i alone; its per-lane byte offset inside the operand is fixed for the whole K
+  // loop and the stage's K position is added as a scalar offset.
+  constexpr int RPI = LR * W;
   static_assert(BM % RPI == 0 && BN % RPI == 0, "tile rows must split evenly over the waves");
   int voff[IPW];
 #pragma unroll
   for (int i = 0; i < IPW; ++i) {
-    const int row = i * RPI + wave * 8 + lrow;                 // LDS row of this lane's chunk
+    const int row = i * RPI + wave * LR + lrow;                // LDS row of this lane's chunk
     const int orow = (i * RPI < BM) ? row : (NB == 1 || i * RPI < BM + BN) ? row - BM : row - BM - BN;
-    voff[i] = int(orow * kbytes) + (((lane & 7) ^ swz_of(row)) << 4);
+    voff[i] = int(orow * kbytes) + (((lane % CH) ^ Rw::swz_of(row)) << 4);
   }
   const uint32_t lds0 = __builtin_amdgcn_readfirstlane(uint32_t(reinterpret_cast<uintptr_t>(&lds[0][0])));
-  constexpr uint32_t SLOT = ROWS * kRowBytes;
-  // instructions [i0, i1) of stage kt into ring slot buf
-  auto issue = [&](int kt, int buf, int i0, int i1) {
-    const int soff = kt * kRowBytes;
+  constexpr uint32_t SLOT = ROWS * RB;
+  // instructions [i0, i1) of stage kt into ring slot buf; with on == false the loads
+  // use zero-record resources (they return zeros and fetch nothing)
+  auto issue = [&](int kt, int buf, int i0, int i1, bool on) {
+    const int soff = kt * RB;
+    const int nr = on ? -1 : 0;
 #pragma unroll
     for (int i = 0; i < IPW; ++i) {
       if (i < i0 || i >= i1) continue;
-      const uint32_t dst = lds0 + buf * SLOT + uint32_t((i * RPI + wave * 8) * kRowBytes);
-      if (i * RPI < BM) load_lds16_so(ra, dst, voff[i], soff);
-      else if (NB == 1 || i * RPI < BM + BN) load_lds16_so(rb, dst, voff[i], soff);
-      else load_lds16_so(rb2, dst, voff[i], soff);
+      const uint32_t dst = lds0 + buf * SLOT + uint32_t((i * RPI + wave * LR) * RB);
+      if (i * RPI < BM) load_lds16_so(gate(ra, nr), dst, voff[i], soff);
+      else if (NB == 1 || i * RPI < BM + BN) load_lds16_so(gate(rb, nr), dst, voff[i], soff);
+      else load_lds16_so(gate(rb2, nr), dst, voff[i], soff);
     }
   };
 
@@ -190,78 +220,143 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(const char* __rest
   const int kt0 = sp * kt_per_split;
   const int nk = min(K / BK - kt0, kt_per_split);
   constexpr int KS = BK / 16;     // 16-deep MFMA steps per stage
+  static_assert(KS % 2 == 0, "fragment double buffer alternates over an even number of steps");
+  constexpr int NF = FM + NB * FN;                        // fragments per 16-deep step
+  // The refill of a stage is spread over the first SPREAD steps of the stage before it.
+  // With a two-slot ring it must land by the next stage's start, so it goes out early.
+  constexpr int SPREAD = STAGES == 2 ? KS / 2 : KS - 1;
   // A wave whose rows all lie past M (the last M tile of a ragged M) still issues
   // its share of the loads and meets every barrier, but skips the LDS reads and MFMAs.
   const bool live = m0 + wm * WM < M;
+  auto read = [&](Frag8<T>* dst, const uint4* buf, int ks) {
+    const int chunk = ks * CPK + kg * (CPK / 2);
+#pragma unroll
+    for (int i = 0; i < FM; ++i) lds_frag<T, RB>(dst[i], buf, wm * WM + i * 32 + lr, chunk);
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+      for (int j = 0; j < FN; ++j) lds_frag<T, RB>(dst[FM + nb * FN + j], buf, BM + nb * BN + wn * WN + j * 32 + lr, chunk);
+  };
+  // Software pipeline: the fragments of step ks + 1 are read while the MFMAs of step ks
+  // run (two register sets).  With a ring of three or more slots the barrier that hands
+  // the next stage over is taken in the last step of a stage, after this stage's reads
+  // have all returned, so the first fragments of the next stage are in flight during
+  // that step's MFMAs.  A two-slot ring keeps the barrier at the start of each stage
+  // instead: its refill then has the whole stage to land.  Refill loads are
+  // unconditional (the stages past the unit's range read nothing: their resource has no
+  // records), so each stage is one straight-line block.
+  constexpr bool EARLY = STAGES >= 3;
   auto k_loop = [&](auto live_tag) {
     constexpr bool LIVE = decltype(live_tag)::value;
+    Frag8<T> f[2][NF];
 #pragma unroll
-    for (int s = 0; s < STAGES - 1; ++s)
-      if (s < nk) issue(kt0 + s, s, 0, IPW);
+    for (int s = 0; s < STAGES - 1; ++s) issue(kt0 + s, s, 0, IPW, s < nk);
+    if constexpr (EARLY) {
+      wait_vmcnt<IPW * (STAGES - 2)>();
+      barrier();
+      if constexpr (LIVE) read(f[0], lds[0], 0);
+    }
     for (int kt = 0; kt < nk; ++kt) {
-      // stage kt must have landed: the stages issued after it may stay in flight
-      const int after = min(STAGES - 2, nk - 1 - kt);
-      if constexpr (STAGES >= 3) {
-        if (after >= 1) wait_vmcnt<IPW>();
-        else wait_vmcnt<0>();
-      } else {
-        wait_vmcnt<0>();
-      }
-      // A bare barrier: every wave has waited for its own loads of stage kt above, and
-      // its reads of the slot refilled during this stage were consumed by MFMAs before
-      // it arrived.  (A fence here would also drain the stages still in flight.)
-      __builtin_amdgcn_s_barrier();
-      const bool refill = kt + STAGES - 1 < nk;
-      const int kn = kt0 + kt + STAGES - 1, bn = (kt + STAGES - 1) % STAGES;
       const uint4* buf = lds[kt % STAGES];
+      const int kn = kt0 + kt + STAGES - 1, bn = (kt + STAGES - 1) % STAGES;
+      const bool refill = kt + STAGES - 1 < nk;
+      if constexpr (!EARLY) {
+        // stage kt has landed and every wave is done with the slot refilled below
+        wait_vmcnt<0>();
+        barrier();
+        if constexpr (LIVE) read(f[0], buf, 0);
+      }
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        const int chunk = ks * CPK + kg * (CPK / 2);
-        Frag8<T> fa[FM], fb[NB][FN];
-        if constexpr (LIVE) {
-#pragma unroll
-          for (int i = 0; i < FM; ++i) lds_frag<T>(fa[i], buf, wm * WM + i * 32 + lr, chunk);
-#pragma unroll
-          for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-            for (int j = 0; j < FN; ++j) lds_frag<T>(fb[nb][j], buf, BM + nb * BN + wn * WN + j * 32 + lr, chunk);
+        Frag8<T>* cur = f[ks & 1];
+        Frag8<T>* nxt = f[(ks + 1) & 1];
+        if (ks < KS - 1) {
+          if constexpr (LIVE) read(nxt, buf, ks + 1);
+          if (ks < SPREAD) issue(kn, bn, (IPW * ks) / SPREAD, (IPW * (ks + 1)) / SPREAD, refill);
+        } else if constexpr (EARLY) {
+          // this stage's fragments are all in registers before its slot is released;
+          // the next stage's own loads have landed (the later stages may stay in flight)
+          wait_lgkmcnt0();
+          wait_vmcnt<IPW * (STAGES - 2)>();
+          barrier();
+          if constexpr (LIVE) read(nxt, lds[(kt + 1) % STAGES], 0);
         }
-        // The next stage's loads, spread over the MFMA steps of this one.  With a
-        // two-slot ring they must land before the next barrier, so they go out in the
-        // first half of the steps; deeper rings spread them over all of them.
-        constexpr int SPREAD = STAGES == 2 ? (KS + 1) / 2 : KS;
-        if (refill && ks < SPREAD) issue(kn, bn, (IPW * ks) / SPREAD, (IPW * (ks + 1)) / SPREAD);
+        // the reads above go out before this step's MFMAs (no reordering across)
+        __builtin_amdgcn_sched_barrier(0);
         if constexpr (LIVE) {
 #pragma unroll
           for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
             for (int i = 0; i < FM; ++i)
 #pragma unroll
-              for (int j = 0; j < FN; ++j) mma32x32_k16(acc[nb][i][j], fa[i], fb[nb][j]);
+              for (int j = 0; j < FN; ++j) mma32x32_k16(acc[nb][i][j], cur[i], cur[FM + nb * FN + j]);
         }
       }
     }
+    // the loads of the stages past the range still write the ring: drain them
+    wait_vmcnt<0>();
   };
   if (live) k_loop(LiveTag<true>{});
   else k_loop(LiveTag<false>{});
+
+  // ---- epilogue ----
+  // Each 32x32 accumulator block goes through a wave-private LDS patch (the ring is
+  // free once every wave is past this barrier: all reads are consumed and all loads
+  // drained) and is read back as rows of 4 consecutive columns per lane, so the
+  // residual loads and the output stores move whole 16-byte (fp32) or 8-byte (bf16)
+  // pieces of a row instead of single elements.  Patch rows are 40 floats apart: the
+  // two rows one MFMA-layout store instruction writes (r and r + 4) then fall in
+  // opposite halves of the 64 banks, and each 16-lane group of a read takes rows r and
+  // r + 4 as well.  The arithmetic per element is unchanged.
+  barrier();
   if (!live) return;
+  constexpr int PS = 40;                                   // patch row stride (floats)
+  float* patch = reinterpret_cast<float*>(&lds[0][0]) + wave * (32 * PS);
+  const bool vec = (N & 3) == 0;
+  const int rsub = lane >> 3, c4 = (lane & 7) * 4;
+  const int rperm = (rsub >> 1) + 4 * (rsub & 1);          // 16-lane group: rows r, r + 4
+  // stores a 32x32 block `v` (MFMA layout) at rows r0.., cols c0.. through f(row, col, x4)
+  auto emit = [&](const f32x16& v, int r0, int c0, auto&& f) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) patch[(8 * (r >> 2) + 4 * kg + (r & 3)) * PS + lr] = v[r];
+#pragma unroll
+    for (int it = 0; it < 4; ++it) {
+      const int pr = it * 8 + rperm;
+      const float4 x = *reinterpret_cast<const float4*>(&patch[pr * PS + c4]);
+      const int row = r0 + pr, col = c0 + c4;
+      if (row < M) f(row, col, x);
+    }
+  };
+  // writes 4 consecutive values of row `row` from column `col` (vector when whole and
+  // aligned, else element by element inside N)
+  auto put4 = [&](auto* out, int row, int col, float4 x, auto&& g) {
+    const long idx = long(row) * N + col;
+    if (vec && col + 3 < N) {
+      g(out, idx, x, true);
+    } else {
+      const float e[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        if (col + q < N) g(out, idx + q, make_float4(e[q], 0.f, 0.f, 0.f), false);
+    }
+  };
+  auto store_f32 = [](float* out, long idx, float4 x, bool v4) {
+    if (v4) *reinterpret_cast<float4*>(out + idx) = x;
+    else out[idx] = x.x;
+  };
 
   if (splits > 1) {
     // fp32 partial of this K split: part[sp][nb][row][col]
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb)
+    for (int nb = 0; nb < NB; ++nb) {
+      float* pp = part + (long(sp) * NB + nb) * long(M) * N;
 #pragma unroll
       for (int i = 0; i < FM; ++i)
 #pragma unroll
-        for (int j = 0; j < FN; ++j) {
-          const int col = n0 + wn * WN + j * 32 + lr;
-          float* pp = part + (long(sp) * NB + nb) * long(M) * N;
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int row = m0 + wm * WM + i * 32 + 8 * (r >> 2) + 4 * kg + (r & 3);
-            if (row < M && col < N) pp[long(row) * N + col] = acc[nb][i][j][r];
-          }
-        }
+        for (int j = 0; j < FN; ++j)
+          emit(acc[nb][i][j], m0 + wm * WM + i * 32, n0 + wn * WN + j * 32,
+               [&](int row, int col, float4 x) { put4(pp, row, col, x, store_f32); });
+    }
     return;
   }
 
@@ -269,23 +364,35 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(const char* __rest
   for (int i = 0; i < FM; ++i)
 #pragma unroll
     for (int j = 0; j < FN; ++j) {
-      const int col = n0 + wn * WN + j * 32 + lr;
+      const int r0 = m0 + wm * WM + i * 32, c0 = n0 + wn * WN + j * 32;
+      if constexpr (EPI == XP_EPI_F32) {
+        emit(acc[0][i][j], r0, c0,
+             [&](int row, int col, float4 x) { put4(reinterpret_cast<float*>(C), row, col, x, store_f32); });
+      } else if constexpr (EPI == XP_EPI_ADD_T || EPI == XP_EPI_ADD_F32) {
+        emit(acc[0][i][j], r0, c0, [&](int row, int col, float4 x) {
+          put4(reinterpret_cast<float*>(C), row, col, x, [&](float* out, long idx, float4 y, bool v4) {
+            if (v4) {
+              const float4 rr = EPI == XP_EPI_ADD_F32 ? St4<float>::load(R, idx) : St4<T>::load(R, idx);
+              *reinterpret_cast<float4*>(out + idx) = make_float4(rr.x + y.x, rr.y + y.y, rr.z + y.z, rr.w + y.w);
+            } else {
+              const float rv = EPI == XP_EPI_ADD_F32 ? reinterpret_cast<const float*>(R)[idx] : St<T>::load(R, idx);
+              out[idx] = rv + y.x;
+            }
+          });
+        });
+      } else {
+        f32x16 h;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int row = m0 + wm * WM + i * 32 + 8 * (r >> 2) + 4 * kg + (r & 3);
-        if (row >= M || col >= N) continue;
-        const long idx = long(row) * N + col;
-        const float v = acc[0][i][j][r];
-        if constexpr (EPI == XP_EPI_F32) {
-          reinterpret_cast<float*>(C)[idx] = v;
-        } else if constexpr (EPI == XP_EPI_ADD_T) {
-          reinterpret_cast<float*>(C)[idx] = St<T>::load(R, idx) + v;
-        } else if constexpr (EPI == XP_EPI_ADD_F32) {
-          reinterpret_cast<float*>(C)[idx] = reinterpret_cast<const float*>(R)[idx] + v;
-        } else {
-          const float u = acc[NB - 1][i][j][r];
-          St<T>::store(C, idx, v / (1.0f + __expf(-v)) * u);
+        for (int r = 0; r < 16; ++r) {
+          const float v = acc[0][i][j][r], u = acc[NB - 1][i][j][r];
+          h[r] = v / (1.0f + __expf(-v)) * u;
         }
+        emit(h, r0, c0, [&](int row, int col, float4 x) {
+          put4(C, row, col, x, [&](void* out, long idx, float4 y, bool v4) {
+            if (v4) St4<T>::store(out, idx, y);
+            else St<T>::store(out, idx, y.x);
+          });
+        });
       }
     }
 }

@@ -59,6 +59,31 @@ template <> struct St<float> {
   }
 };
 
+// 4 consecutive elements at index i (i a multiple of 4, 4-element aligned storage)
+template <typename T> struct St4;
+template <> struct St4<bf16_t> {
+  __device__ static __forceinline__ float4 load(const void* p, long i) {
+    const uint2 w = *reinterpret_cast<const uint2*>(reinterpret_cast<const uint16_t*>(p) + i);
+    return make_float4(__uint_as_float(w.x << 16), __uint_as_float(w.x & 0xffff0000u), __uint_as_float(w.y << 16),
+                       __uint_as_float(w.y & 0xffff0000u));
+  }
+  __device__ static __forceinline__ void store(void* p, long i, float4 v) {
+    *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(p) + i) =
+        make_uint2(pack_bf16x2_(v.x, v.y), pack_bf16x2_(v.z, v.w));
+  }
+  __device__ static __forceinline__ uint32_t pack_bf16x2_(float a, float b) {
+    return uint32_t(f2bf(a)) | (uint32_t(f2bf(b)) << 16);
+  }
+};
+template <> struct St4<float> {
+  __device__ static __forceinline__ float4 load(const void* p, long i) {
+    return *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(p) + i);
+  }
+  __device__ static __forceinline__ void store(void* p, long i, float4 v) {
+    *reinterpret_cast<float4*>(reinterpret_cast<float*>(p) + i) = v;
+  }
+};
+
 // value after a round trip through the storage type
 template <typename T> __device__ __forceinline__ float round_st(float v);
 template <> __device__ __forceinline__ float round_st<bf16_t>(float v) { return bf2f(f2bf(v)); }

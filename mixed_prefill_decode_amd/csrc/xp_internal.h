@@ -33,6 +33,7 @@ xp_status launch_rmsnorm(int dtype, const void* x, int x_is_f32, const void* gam
 
 int gemm_splits(int dtype, int epi, int N, int K);
 size_t gemm_ws_bytes(int dtype, int epi, int M, int N, int K);
+void gemm_tile(int dtype, int epi, int M, int N, int K, int* bm, int* bn, int* splits);
 xp_status launch_gemm(int dtype, int epi, const void* A, const void* B, const void* B2, const void* R,
                       void* C, int M, int N, int K, void* ws, size_t ws_bytes, hipStream_t s);
 

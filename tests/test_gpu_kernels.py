@@ -67,6 +67,45 @@ def test_gemm_epilogues(dtype, M, N, K):
     assert rel_fro(to_f64(to_host_bits(Cs), dtype), ref) < (5e-3 if dtype == "bf16" else 1e-5)
 
 
+# (M, N) pairs whose unsplit products make the launcher take each of its work-unit
+# shapes (found with xp_gemm_tile; the choice does not depend on K when K is not split)
+GEMM_TILE_SHAPES = {"single": [(128, 6144), (536, 5120), (1040, 6144), (1040, 4096), (536, 14336), (8216, 7168)],
+                    "dual": [(128, 14336), (1040, 14336), (536, 5120), (536, 7168), (8216, 17408)]}
+
+
+@pytest.mark.parametrize("kind", ["single", "dual"])
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_gemm_every_tile_shape(kind, dtype):
+    # every work-unit shape of the launcher, against the fp64 product on sampled rows
+    K = 128
+    epi = X.XP_EPI_SWIGLU if kind == "dual" else X.XP_EPI_F32
+    seen = set()
+    for M, N in GEMM_TILE_SHAPES[kind]:
+        bm, bn, sp = X.xp_gemm_tile(DT[dtype], epi, M, N, K)
+        assert sp == 1
+        seen.add((bm, bn))
+        rng = np.random.default_rng(M + N)
+        A, B, B2 = _rand(rng, (M, K), dtype), _rand(rng, (N, K), dtype, 0.05), _rand(rng, (N, K), dtype, 0.05)
+        odt = torch.bfloat16 if (epi == X.XP_EPI_SWIGLU and dtype == "bf16") else torch.float32
+        C = torch.empty((M, N), dtype=odt, device="cuda")
+        X.xp_gemm(DT[dtype], epi, to_device(A, dtype), to_device(B, dtype), to_device(B2, dtype) if kind == "dual"
+                  else None, None, C, M, N, K)
+        _sync()
+        rows = np.unique(np.concatenate([np.arange(min(M, 40)), rng.integers(0, M, 200), np.arange(max(0, M - 40), M)]))
+        a64 = to_f64(A, dtype)[rows]
+        g = a64 @ to_f64(B, dtype).T
+        if kind == "dual":
+            ref = g / (1 + np.exp(-g)) * (a64 @ to_f64(B2, dtype).T)
+            got = to_f64(to_host_bits(C), dtype)[rows] if dtype == "bf16" else C.cpu().numpy()[rows].astype(np.float64)
+            tol = 5e-3 if dtype == "bf16" else 1e-5
+        else:
+            ref, got, tol = g, C.cpu().numpy()[rows].astype(np.float64), 1e-5
+        assert rel_fro(got, ref) < tol, (M, N, bm, bn)
+    want = {"single": {(64, 128), (96, 128), (128, 256), (192, 128), (192, 192), (256, 256)},
+            "dual": {(128, 64), (128, 128), (192, 64), (192, 128), (256, 128)}}[kind]
+    assert seen == want
+
+
 def test_gemm_rows_do_not_depend_on_the_batch():
     # the same rows inside batches of 40 (64-row tiles) and 300 (128-row tiles): bit-identical
     rng = np.random.default_rng(3)
