@@ -91,7 +91,8 @@ def gemm_list(wl):
 
 TRAFFIC_PROFILE = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles",
                                "gate_up_swiglu_gemm_c2_traffic.md")
-GEMM_SOURCES = ("mixed_prefill_decode_amd/csrc/gemm_core.h", "mixed_prefill_decode_amd/csrc/gemm.hip")
+GEMM_SOURCES = ("mixed_prefill_decode_amd/csrc/gemm_core.h", "mixed_prefill_decode_amd/csrc/gemm.hip",
+                "mixed_prefill_decode_amd/csrc/xp_device.h")
 
 
 def recorded_traffic(workload: str):
