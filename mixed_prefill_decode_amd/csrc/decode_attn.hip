@@ -113,20 +113,18 @@ __device__ __forceinline__ void load_page(PageFrags<T, D>& f, const char* page, 
   for (int n = 0; n < D / 16; ++n) load_frag4(f.v[n], page + (kPage * D + (16 * n + key) * kPage + 4 * grp) * EB);
 }
 
-// One wave per (split s, KV head g, request i).  DEPTH pages are in flight
-// while one is consumed; the register ring has DEPTH + 1 page buffers and the
-// loop is unrolled over the ring so every buffer index is static.
+// One unit of work: split s of request i's context on KV head g.  DEPTH pages
+// are in flight while one is consumed; the register ring has DEPTH + 1 page
+// buffers and the loop is unrolled over the ring so every buffer index is static.
 template <typename T, int D, int DEPTH, bool PTR>
-__global__ __launch_bounds__(64) void decode_split_kernel(const void* __restrict__ q, const char* __restrict__ pool,
-                                                          int n_pages, const int32_t* __restrict__ dec_pages,
-                                                          int max_blocks, const int32_t* __restrict__ dec_ctx, int Hq,
-                                                          int Hkv, int pps, int n_splits, float* __restrict__ part_ml,
-                                                          float* __restrict__ part_o, float scale_log2,
-                                                          uint32_t* __restrict__ status) {
+__device__ __forceinline__ void decode_unit(const void* __restrict__ q, const char* __restrict__ pool, int n_pages,
+                                            const int32_t* __restrict__ dec_pages, int max_blocks,
+                                            const int32_t* __restrict__ dec_ctx, int Hq, int Hkv, int pps,
+                                            int n_splits, float* __restrict__ part_ml, float* __restrict__ part_o,
+                                            float scale_log2, uint32_t* __restrict__ status, int i, int g, int s) {
   constexpr int EB = St<T>::bytes;
   constexpr int PAGE_BYTES = 2 * kPage * D * EB;
   constexpr int NB = DEPTH + 1;
-  const int s = blockIdx.x, g = blockIdx.y, i = blockIdx.z;
   const int lane = threadIdx.x;
   const int G = Hq / Hkv;
   const int b0 = s * pps;
@@ -245,6 +243,35 @@ __global__ __launch_bounds__(64) void decode_split_kernel(const void* __restrict
   }
 }
 
+// The split waves of a batch as one compact list: unit u enumerates (request i,
+// split s, KV head g) with i slowest and g fastest, over only the splits that hold
+// keys (a request of nb pages has ceil(nb / pps) of them), and workgroup w takes
+// units w, w + W, w + 2W, ... of the W workgroups launched.  Short requests then
+// cost nothing and the splits of long ones spread over the whole grid; the
+// partials keep their (i, h, s) layout for the combine.
+template <typename T, int D, int DEPTH, bool PTR>
+__global__ __launch_bounds__(64) void decode_split_kernel(const void* __restrict__ q, const char* __restrict__ pool,
+                                                          int n_pages, const int32_t* __restrict__ dec_pages,
+                                                          int max_blocks, const int32_t* __restrict__ dec_ctx, int n_d,
+                                                          int Hq, int Hkv, int pps, int n_splits,
+                                                          float* __restrict__ part_ml, float* __restrict__ part_o,
+                                                          float scale_log2, uint32_t* __restrict__ status) {
+  const int W = int(gridDim.x);
+  int u = int(blockIdx.x);
+  int base = 0;
+  for (int i = 0; i < n_d; ++i) {
+    const int nb_need = (dec_ctx[i] + kPage) / kPage;               // pages of ctx + 1 keys
+    const int ns = max(1, min(n_splits, (nb_need + pps - 1) / pps));
+    const int cnt = ns * Hkv;
+    for (; u < base + cnt; u += W) {
+      const int r = u - base;
+      decode_unit<T, D, DEPTH, PTR>(q, pool, n_pages, dec_pages, max_blocks, dec_ctx, Hq, Hkv, pps, n_splits,
+                                    part_ml, part_o, scale_log2, status, i, r % Hkv, r / Hkv);
+    }
+    base += cnt;
+  }
+}
+
 // out[i, h*D + j] = sum_s 2^(m_s - m*) o_s[j] / sum_s 2^(m_s - m*) l_s
 // One 256-thread workgroup per (query head, request): thread t accumulates dim
 // t % D over every (256 / D)-th split with several partial loads in flight,
@@ -320,9 +347,9 @@ xp_status launch_dec_t(const void* q, const void* pool, int n_pages, const int32
                        float* part_o, int pps, uint32_t* status, hipStream_t s) {
   const int n_splits = decode_splits(max_blocks, pps);
   const float scale_log2 = float(1.4426950408889634 / __builtin_sqrt(double(D)));
-  hipLaunchKernelGGL((decode_split_kernel<T, D, kDepth, kPtrLoads>), dim3(n_splits, Hkv, n_d), dim3(64), 0, s, q,
-                     static_cast<const char*>(pool), n_pages, dec_pages, max_blocks, dec_ctx, Hq, Hkv, pps, n_splits,
-                     part_ml, part_o, scale_log2, status);
+  hipLaunchKernelGGL((decode_split_kernel<T, D, kDepth, kPtrLoads>), dim3(decode_grid(n_d, Hkv, n_splits)), dim3(64), 0,
+                     s, q, static_cast<const char*>(pool), n_pages, dec_pages, max_blocks, dec_ctx, n_d, Hq, Hkv, pps,
+                     n_splits, part_ml, part_o, scale_log2, status);
   XP_CHECK_LAUNCH();
   hipLaunchKernelGGL((decode_combine_kernel<T, D>), dim3(Hq, n_d), dim3(kCombineThreads), 0, s, part_ml, part_o, dec_ctx, Hq, pps,
                      n_splits, out, out_stride);
@@ -334,11 +361,31 @@ xp_status launch_dec_t(const void* q, const void* pool, int n_pages, const int32
 
 int decode_splits(int dec_max_blocks, int pps) { return std::max(1, cdiv(dec_max_blocks, pps)); }
 
+// Workgroups of the split kernel.  Up to kGridWaves units (counting every request
+// as filling its table) each unit gets a workgroup of its own, so the hardware
+// dispatcher balances uniform batches; beyond that the count is the largest one
+// that gives every workgroup the same number of units.  Measured on MI355X over the
+// 8B, 14B and 32B decode batches: as fast as one workgroup per split for uniform
+// contexts, and 1.26x faster for the lognormal 32B batch, whose short requests no
+// longer leave most of a table-wide grid empty.
+#ifndef XP_DECODE_GRID_WAVES
+#define XP_DECODE_GRID_WAVES 16384
+#endif
+constexpr long kGridWaves = XP_DECODE_GRID_WAVES;
+int decode_grid(int n_d, int Hkv, int n_splits) {
+  const long units = long(n_d) * Hkv * n_splits;   // when every request fills its table
+  const long per = (units + kGridWaves - 1) / kGridWaves;
+  return int(std::max(1L, (units + per - 1) / per));
+}
+
 // Pages per split when the caller leaves it open (0): about kTargetWaves split
 // waves over the batch's (request, KV head) pairs at their table width, i.e.
 // some six resident waves per CU, and between 8 and 64 pages per wave.  Fewer,
 // longer splits write fewer partials; more splits keep more pages in flight.
-constexpr long kTargetWaves = 1600;
+#ifndef XP_DECODE_TARGET_UNITS
+#define XP_DECODE_TARGET_UNITS 1600
+#endif
+constexpr long kTargetWaves = XP_DECODE_TARGET_UNITS;
 int decode_pick_pps(int requested, int n_d, int Hkv, int dec_max_blocks) {
   if (requested > 0) return requested;
   const long work = long(n_d) * Hkv * dec_max_blocks;

@@ -68,6 +68,7 @@ xp_status launch_kv_gather(int dtype, const void* pool, int n_pages, int S, int 
                            void* v_out, hipStream_t s);
 
 int decode_splits(int dec_max_blocks, int pages_per_split);
+int decode_grid(int n_d, int Hkv, int n_splits);
 int decode_pick_pps(int requested, int n_d, int Hkv, int dec_max_blocks);
 size_t decode_ws_bytes(int n_d, int Hq, int d, int n_splits);
 xp_status launch_decode(int dtype, const void* q, const void* pool, int n_pages, int S,
