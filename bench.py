@@ -38,17 +38,23 @@ def parse():
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--workload", default="C2")
     p.add_argument("--decode-cus", type=int, default=None,
-                   help="CUs for decode attention (default: calibrated, 0 = serialized, -1 = unmasked)")
+                   help="CUs for decode attention (default: the fastest of serialized, unmasked and a sweep of "
+                        "partitions that includes the pages' 90%% rule; 0 = serialized, -1 = unmasked)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-budget-s", type=float, default=25.0)
     p.add_argument("--kernel-only", choices=["none", "swiglu", "decode", "prefill", "copy"], default="none",
                    help="only launch one kernel repeatedly (for counter runs)")
     p.add_argument("--repeats", type=int, default=20, help="launches per kernel timing")
+    p.add_argument("--probe", default=None,
+                   help="internal: time one split-attention mode in this fresh process ('rule' = the pages' "
+                        "decode-CU calibration, or a decode CU count) and print it as one JSON line")
     return p.parse_args()
 
 
 class Timer:
-    """HIP-event timing on torch's current stream."""
+    """HIP-event timing on torch's current stream.  The GPU's clock drops after a few
+    milliseconds idle and takes most of a 20-step window to recover (measured: the
+    first window after a 50 ms gap is ~9% slow), so n untimed calls run first."""
 
     def __init__(self, torch):
         self.torch = torch
@@ -56,8 +62,8 @@ class Timer:
     def __call__(self, fn, n):
         t = self.torch
         a, b = t.cuda.Event(enable_timing=True), t.cuda.Event(enable_timing=True)
-        fn()
-        t.cuda.synchronize()
+        for _ in range(n):
+            fn()
         a.record()
         for _ in range(n):
             fn()
@@ -206,6 +212,9 @@ def main():
     wf_args = dict(tau=0.05, n_decode_tokens=[wl.n_decode], decode_ctx_sum=[ctx_sum],
                    candidate=(wl.n_prefill_local, wl.prior_len), model=model, fixed_target=wl.n_rows)
 
+    if args.probe is not None:
+        return probe_mode(args, X, torch, inst, dev, timer, n_cus)
+
     ctx0 = X.Ctx(0, 0, 0)
     step0, _ = make_step(inst, ctx0, dev)
 
@@ -214,28 +223,44 @@ def main():
 
     step0.run()
     torch.cuda.synchronize()
-    # decode CU partition
-    if args.decode_cus is None:
-        if wl.n_decode and wl.chunk_len:
-            k, calib = calibrate_decode_cus(X, torch, step0, inst, dev, timer, n_cus, args.repeats)
-        else:
-            k, calib = 0, {}
-    else:
-        k, calib = args.decode_cus, {}
-    ctx = X.Ctx(0, k, 0) if k != 0 else ctx0
-    step, _ = make_step(inst, ctx, dev)
-    # The timed step runs the split attention CU-partitioned at the calibrated size
-    # unless serializing it is faster for this batch (the partition only pays when
-    # decode keeps its bandwidth on few CUs); both figures are reported.
+    # Split-attention mode.  The pages size the decode partition by their rule (the
+    # fewest CUs that keep 90% of decode's standalone bandwidth); on MI355X decode
+    # bandwidth grows almost linearly with CUs, so that rule hands decode most of the
+    # chip and starves prefill.  The step is therefore also timed serialized, with the
+    # two attention kernels concurrent on all CUs (no masks), and on a sweep of
+    # partitions; the timed steps use the fastest and every figure is reported.
+    # Each mode is timed in a fresh process whose first streams are that context's:
+    # a context created after others in one process can be slowed as a whole (its
+    # queues may share a hardware pipe with the main stream's), so this process
+    # creates no masked context before the chosen one.
     seg = {}
-    timed_mode = "serialized" if k == 0 else "overlapped"
-    if wl.n_decode and wl.chunk_len:
+    step, k, timed_mode = step0, 0, "serialized"
+    if args.decode_cus is not None:
+        k = args.decode_cus
+        if k != 0:
+            step, _ = make_step(inst, X.Ctx(0, k, 0), dev)
+            timed_mode = "unmasked" if k < 0 else "partitioned"
+    elif wl.n_decode and wl.chunk_len:
+        rule = run_probe(args, "rule")
+        k_rule = rule["rule_decode_cus"]
+        seg["rule_decode_cus"] = k_rule
+        seg["calibration"] = rule["calibration"]
         seg["serialized_layer_us"] = round(timer(step0.run, args.repeats) * 1e6, 1)
-        seg["overlapped_layer_us"] = round(timer(step.run, args.repeats) * 1e6, 1) if k != 0 else None
+        sweep = {}
+        best = (seg["serialized_layer_us"], 0)
+        for kk in sorted({-1, 64, 96, 128, 160, k_rule}):
+            t = run_probe(args, str(kk))["layer_us"]
+            sweep["unmasked" if kk < 0 else kk] = t
+            if t < best[0]:
+                best = (t, kk)
+        seg["rule_layer_us"] = sweep[k_rule]
+        seg["unmasked_layer_us"] = sweep["unmasked"]
+        seg["partition_layer_us"] = {kk: v for kk, v in sweep.items() if kk != "unmasked"}
+        k = best[1]
+        if k != 0:
+            step, _ = make_step(inst, X.Ctx(0, k, 0), dev)
+        timed_mode = "serialized" if k == 0 else "unmasked" if k < 0 else "partitioned"
         seg["decode_cus"] = k
-        seg["calibration"] = calib
-        if k != 0 and seg["serialized_layer_us"] < seg["overlapped_layer_us"]:
-            step, timed_mode = step0, "serialized"
         seg["timed_mode"] = timed_mode
 
     def one_step():
@@ -243,6 +268,11 @@ def main():
         assert r["chunk_len"] == wl.n_prefill_local
         step.run()
 
+    # untimed steps until the clock has settled (not part of the W warmup steps)
+    t_warm = time.perf_counter()
+    while time.perf_counter() - t_warm < 0.2:
+        step.run()
+        torch.cuda.synchronize()
     for _ in range(args.warmup):
         one_step()
     torch.cuda.synchronize()
@@ -334,6 +364,40 @@ def main():
         "roofline": roofline, "cpu_baseline": cpu, "kernels": kern, "split_attention": seg,
     }
     print(json.dumps(line), flush=True)
+
+
+def run_probe(args, what: str) -> dict:
+    """Runs this script with --probe in a child process and returns its JSON line."""
+    import subprocess
+    cmd = [sys.executable, os.path.abspath(__file__), "--workload", args.workload, "--repeats", str(args.repeats),
+           "--probe", what]
+    r = subprocess.run(cmd, capture_output=True, text=True, timeout=600)
+    if r.returncode != 0:
+        raise RuntimeError(f"probe {what} failed ({r.returncode}):\n{r.stderr[-2000:]}")
+    out = json.loads(r.stdout.strip().splitlines()[-1])
+    log(f"[bench] probe {what}: {json.dumps(out)}")
+    return out
+
+
+def probe_mode(args, X, torch, inst, dev, timer, n_cus):
+    """One split-attention mode in this fresh process: its context is the first one made."""
+    from synth.device import make_step
+    if args.probe == "rule":
+        ctx0 = X.Ctx(0, 0, 0)
+        step0, _ = make_step(inst, ctx0, dev)
+        step0.run()
+        torch.cuda.synchronize()
+        k_rule, calib = calibrate_decode_cus(X, torch, step0, inst, dev, timer, n_cus, args.repeats)
+        print(json.dumps({"rule_decode_cus": k_rule, "calibration": calib}), flush=True)
+        return
+    k = int(args.probe)
+    step, _ = make_step(inst, X.Ctx(0, k, 0), dev)
+    for _ in range(3):
+        step.run()
+    torch.cuda.synchronize()
+    t = timer(step.run, args.repeats)
+    assert step.status() == 0
+    print(json.dumps({"decode_cus": k, "layer_us": round(t * 1e6, 1)}), flush=True)
 
 
 def kernel_only(args, X, torch, inst, step, dev, timer):
