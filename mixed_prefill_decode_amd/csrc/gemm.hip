@@ -17,15 +17,15 @@ namespace {
 
 using gemm::gemm_kernel;
 
-template <typename T, int BM, int BN, int WGM, int WGN, int EPI, int ST>
+template <typename T, int BM, int BN, int WGM, int WGN, int EPI, int ST, bool FOLD = false>
 xp_status launch_cfg(const void* A, const void* B, const void* B2, const void* R, void* C, int M, int N, int K,
-                     int splits, float* part, hipStream_t s) {
+                     int splits, int chunks, float* part, hipStream_t s) {
   const int tm = cdiv(M, BM), tn = cdiv(N, BN);
   const int stages = K / gemm::Cfg<T, BM, BN, WGM, WGN, EPI>::BK;
-  const int per = cdiv(stages, splits);
-  hipLaunchKernelGGL((gemm_kernel<T, BM, BN, WGM, WGN, EPI, ST>), dim3(tm * tn * splits), dim3(64 * WGM * WGN), 0, s,
-                     static_cast<const char*>(A), static_cast<const char*>(B), static_cast<const char*>(B2), R, C,
-                     M, N, K, tm, tn, splits, per, part);
+  const int per = cdiv(stages, chunks);     // stages per K chunk
+  hipLaunchKernelGGL((gemm_kernel<T, BM, BN, WGM, WGN, EPI, ST, 128, FOLD>), dim3(tm * tn * splits),
+                     dim3(64 * WGM * WGN), 0, s, static_cast<const char*>(A), static_cast<const char*>(B),
+                     static_cast<const char*>(B2), R, C, M, N, K, tm, tn, splits, per, part);
   XP_CHECK_LAUNCH();
   if (splits > 1) {
     const long mn = long(M) * N;
@@ -57,6 +57,14 @@ constexpr Candidate kSingle[] = {
     {3, 192, 128, 1, 7.03},   // 2x4 waves, 4-stage ring (160 KB)
     {4, 192, 192, 1, 6.88},   // 2x2 waves, 3-stage ring (144 KB)
     {5, 256, 256, 1, 11.61},  // 2x4 waves, 2-stage ring (128 KB)
+};
+// Unsplit units that fold K chunks hold a second set of accumulators: the tiles
+// that keep it in registers.
+constexpr Candidate kSingleFold[] = {
+    {0, 64, 128, 1, 4.59},
+    {1, 96, 128, 1, 5.50},
+    {2, 128, 256, 1, 6.65},
+    {3, 192, 128, 1, 7.03},
 };
 constexpr Candidate kDual[] = {
     {0, 128, 64, 1, 8.03},    // 2x2 waves, 3-stage ring (96 KB)
@@ -97,9 +105,9 @@ int n_cus_of_current_device() {
 
 template <typename T, int EPI>
 xp_status launch_epi(const void* A, const void* B, const void* B2, const void* R, void* C, int M, int N, int K,
-                     int splits, float* part, hipStream_t s) {
+                     int splits, int chunks, float* part, hipStream_t s) {
   const int cus = n_cus_of_current_device();
-#define XP_GEMM_ARGS A, B, B2, R, C, M, N, K, splits, part, s
+#define XP_GEMM_ARGS A, B, B2, R, C, M, N, K, splits, chunks, part, s
   if constexpr (EPI == XP_EPI_SWIGLU) {
     switch (pick(kDual, M, N, K, cus, 2, splits)) {
       case 1: return launch_cfg<T, 192, 64, 2, 2, EPI, 3>(XP_GEMM_ARGS);
@@ -107,6 +115,13 @@ xp_status launch_epi(const void* A, const void* B, const void* B2, const void* R
       case 3: return launch_cfg<T, 256, 128, 4, 2, EPI, 2>(XP_GEMM_ARGS);
       case 4: return launch_cfg<T, 128, 128, 2, 4, EPI, 3>(XP_GEMM_ARGS);
       default: return launch_cfg<T, 128, 64, 2, 2, EPI, 3>(XP_GEMM_ARGS);
+    }
+  } else if (splits == 1 && chunks > 1) {
+    switch (pick(kSingleFold, M, N, K, cus, 1, splits)) {
+      case 1: return launch_cfg<T, 96, 128, 1, 4, EPI, 4, true>(XP_GEMM_ARGS);
+      case 2: return launch_cfg<T, 128, 256, 2, 4, EPI, 3, true>(XP_GEMM_ARGS);
+      case 3: return launch_cfg<T, 192, 128, 2, 4, EPI, 4, true>(XP_GEMM_ARGS);
+      default: return launch_cfg<T, 64, 128, 1, 4, EPI, 4, true>(XP_GEMM_ARGS);
     }
   } else {
     switch (pick(kSingle, M, N, K, cus, 1, splits)) {
@@ -123,26 +138,27 @@ xp_status launch_epi(const void* A, const void* B, const void* B2, const void* R
 
 template <typename T>
 xp_status launch_type(int epi, const void* A, const void* B, const void* B2, const void* R, void* C, int M, int N,
-                      int K, int splits, float* part, hipStream_t s) {
+                      int K, int splits, int chunks, float* part, hipStream_t s) {
   switch (epi) {
-    case XP_EPI_F32: return launch_epi<T, XP_EPI_F32>(A, B, B2, R, C, M, N, K, splits, part, s);
-    case XP_EPI_ADD_T: return launch_epi<T, XP_EPI_ADD_T>(A, B, B2, R, C, M, N, K, splits, part, s);
-    case XP_EPI_ADD_F32: return launch_epi<T, XP_EPI_ADD_F32>(A, B, B2, R, C, M, N, K, splits, part, s);
-    case XP_EPI_SWIGLU: return launch_epi<T, XP_EPI_SWIGLU>(A, B, B2, R, C, M, N, K, splits, part, s);
+    case XP_EPI_F32: return launch_epi<T, XP_EPI_F32>(A, B, B2, R, C, M, N, K, splits, chunks, part, s);
+    case XP_EPI_ADD_T: return launch_epi<T, XP_EPI_ADD_T>(A, B, B2, R, C, M, N, K, splits, chunks, part, s);
+    case XP_EPI_ADD_F32: return launch_epi<T, XP_EPI_ADD_F32>(A, B, B2, R, C, M, N, K, splits, chunks, part, s);
+    case XP_EPI_SWIGLU: return launch_epi<T, XP_EPI_SWIGLU>(A, B, B2, R, C, M, N, K, splits, chunks, part, s);
   }
   return fail(XP_EINVAL, "xp_gemm: unknown epilogue %d", epi);
 }
 
 }  // namespace
 
-// K splits of a GEMM against an [N, K] weight: a function of the weight's shape only,
-// so a row's result never depends on how many rows share the call.  Only long-K,
-// narrow products (K >= 3N, the FFN down projection) are split: there a few rows
-// cannot fill the chip otherwise (128 rows: 70 -> 28 us for an 8B down projection),
-// while at 500-1000 rows the split costs at most a few percent.  Aim: with 256-row
-// tiles and about 1024 rows, (N / 256) x 4 x splits ~ 256 work units; at least 16
-// K stages per split; at most 4 splits.
-int gemm_splits(int dtype, int epi, int N, int K) {
+// K chunks of a GEMM against an [N, K] weight: a function of the weight's shape only.
+// Only long-K, narrow products (K >= 3N, the FFN down projection) are chunked: their
+// sum runs over C fixed K ranges in order, whether the chunks are separate work units
+// (few rows cannot fill the chip otherwise: 128 rows of an 8B down projection take 27
+// us split, 61 unsplit) or one unit folds them (gemm_kernel's FOLD), so a row's result
+// never depends on how many rows share the call.  Aim: with 256-row tiles and about
+// 1024 rows, (N / 256) x 4 x C ~ 256 work units; at least 16 K stages per chunk; at
+// most 4 chunks.
+int gemm_chunks(int dtype, int epi, int N, int K) {
   const int nb = epi == XP_EPI_SWIGLU ? 2 : 1;
   const int stages = K / (128 / dtype_bytes(dtype));
   if (long(K) < 3L * N * nb) return 1;
@@ -152,13 +168,28 @@ int gemm_splits(int dtype, int epi, int N, int K) {
   return sp;
 }
 
+// Work units per chunked product: one per chunk (plus the reduction) when the unsplit
+// product would keep fewer than 70% of the CUs busy with 192 x 128 tiles, else one
+// folding unit per tile.  Measured on the down projections of the layer shapes: 1040
+// rows run unsplit in 127 us vs 145 split; 128 to 544 rows split in 27-154 us vs
+// 61-205 unsplit.  Chunked SwiGLU products always split.
+int gemm_split_count(int dtype, int epi, int M, int N, int K) {
+  const int c = gemm_chunks(dtype, epi, N, K);
+  if (c <= 1 || epi == XP_EPI_SWIGLU) return c;
+  const long tiles = long(cdiv(M, 192)) * cdiv(N, 128);
+  return tiles * 10 < long(n_cus_of_current_device()) * 7 ? c : 1;
+}
+
 void gemm_tile(int dtype, int epi, int M, int N, int K, int* bm, int* bn, int* splits) {
-  const int sp = gemm_splits(dtype, epi, N, K);
+  const int sp = gemm_split_count(dtype, epi, M, N, K);
   const int cus = n_cus_of_current_device();
   const Candidate* c = nullptr;
   if (epi == XP_EPI_SWIGLU) {
     const int id = pick(kDual, M, N, K, cus, 2, sp);
     for (const Candidate& x : kDual) if (x.id == id) c = &x;
+  } else if (sp == 1 && gemm_chunks(dtype, epi, N, K) > 1) {
+    const int id = pick(kSingleFold, M, N, K, cus, 1, sp);
+    for (const Candidate& x : kSingleFold) if (x.id == id) c = &x;
   } else {
     const int id = pick(kSingle, M, N, K, cus, 1, sp);
     for (const Candidate& x : kSingle) if (x.id == id) c = &x;
@@ -170,7 +201,7 @@ void gemm_tile(int dtype, int epi, int M, int N, int K, int* bm, int* bn, int* s
 
 size_t gemm_ws_bytes(int dtype, int epi, int M, int N, int K) {
   if (M <= 0 || N <= 0 || K <= 0) return 0;
-  const int sp = gemm_splits(dtype, epi, N, K);
+  const int sp = gemm_split_count(dtype, epi, M, N, K);
   if (sp <= 1) return 0;
   return size_t(sp) * (epi == XP_EPI_SWIGLU ? 2 : 1) * size_t(M) * N * sizeof(float);
 }
@@ -188,13 +219,13 @@ xp_status launch_gemm(int dtype, int epi, const void* A, const void* B, const vo
   if ((epi == XP_EPI_ADD_T || epi == XP_EPI_ADD_F32) && !R) return fail(XP_EINVAL, "xp_gemm: null residual");
   if (epi == XP_EPI_SWIGLU && !B2) return fail(XP_EINVAL, "xp_gemm: null second weight");
   if (M == 0) return XP_OK;
-  const int splits = gemm_splits(dtype, epi, N, K);
+  const int splits = gemm_split_count(dtype, epi, M, N, K), chunks = gemm_chunks(dtype, epi, N, K);
   const size_t need = gemm_ws_bytes(dtype, epi, M, N, K);
   if (need && (!ws || ws_bytes < need))
     return fail(XP_EWORKSPACE, "xp_gemm: needs %zu bytes of workspace (got %zu)", need, ws ? ws_bytes : size_t(0));
   float* part = static_cast<float*>(ws);
-  if (dtype == XP_BF16) return launch_type<bf16_t>(epi, A, B, B2, R, C, M, N, K, splits, part, s);
-  return launch_type<float>(epi, A, B, B2, R, C, M, N, K, splits, part, s);
+  if (dtype == XP_BF16) return launch_type<bf16_t>(epi, A, B, B2, R, C, M, N, K, splits, chunks, part, s);
+  return launch_type<float>(epi, A, B, B2, R, C, M, N, K, splits, chunks, part, s);
 }
 
 }  // namespace xp

@@ -141,7 +141,7 @@ __device__ __forceinline__ void load_lds16_so(i32x4 r, uint32_t lds_addr, int vo
 }
 #pragma clang diagnostic pop
 
-template <typename T, int BM, int BN, int WGM, int WGN, int EPI, int STAGES, int RB = 128>
+template <typename T, int BM, int BN, int WGM, int WGN, int EPI, int STAGES, int RB = 128, bool FOLD = false>
 __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(const char* __restrict__ A, const char* __restrict__ B,
                                                                  const char* __restrict__ B2, const void* __restrict__ R,
                                                                  void* __restrict__ C, int M, int N, int K, int tiles_m,
@@ -216,9 +216,10 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(const char* __rest
       for (int j = 0; j < FN; ++j) acc[nb][i][j] = f32x16{};
 
   const int lr = lane & 31, kg = lane >> 5;
-  // this unit's K stages [kt0, kt0 + nk)
-  const int kt0 = sp * kt_per_split;
-  const int nk = min(K / BK - kt0, kt_per_split);
+  // this unit's K stages [kt0, kt0 + nk); with FOLD the unit covers all of K as
+  // consecutive chunks of kt_per_split stages (see the fold below)
+  const int kt0 = FOLD ? 0 : sp * kt_per_split;
+  const int nk = FOLD ? K / BK : min(K / BK - kt0, kt_per_split);
   constexpr int KS = BK / 16;     // 16-deep MFMA steps per stage
   static_assert(KS % 2 == 0, "fragment double buffer alternates over an even number of steps");
   constexpr int NF = FM + NB * FN;                        // fragments per 16-deep step
@@ -246,8 +247,26 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(const char* __rest
   // unconditional (the stages past the unit's range read nothing: their resource has no
   // records), so each stage is one straight-line block.
   constexpr bool EARLY = STAGES >= 3;
+  // FOLD: a long-K product is summed over fixed K chunks in chunk order.  Split into
+  // units, each chunk is a unit and the reduction adds the chunk results in order;
+  // unsplit, one unit accumulates chunk by chunk and folds each finished chunk into a
+  // running total, in the same order: ((c0 + c1) + c2) + ...  Both give the same bits,
+  // so the launcher may choose either for any row count.
+  [[maybe_unused]] f32x16 tot[NB][FM][FN];
+  auto fold = [&](bool first) {
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+          tot[nb][i][j] = first ? acc[nb][i][j] : tot[nb][i][j] + acc[nb][i][j];
+          acc[nb][i][j] = f32x16{};
+        }
+  };
   auto k_loop = [&](auto live_tag) {
     constexpr bool LIVE = decltype(live_tag)::value;
+    [[maybe_unused]] int chunk_left = kt_per_split, chunks_done = 0;
     Frag8<T> f[2][NF];
 #pragma unroll
     for (int s = 0; s < STAGES - 1; ++s) issue(kt0 + s, s, 0, IPW, s < nk);
@@ -291,6 +310,23 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(const char* __rest
 #pragma unroll
               for (int j = 0; j < FN; ++j) mma32x32_k16(acc[nb][i][j], cur[i], cur[FM + nb * FN + j]);
         }
+      }
+      if constexpr (FOLD && LIVE) {
+        if (--chunk_left == 0 && kt + 1 < nk) {
+          fold(chunks_done == 0);
+          ++chunks_done;
+          chunk_left = kt_per_split;
+        }
+      }
+    }
+    if constexpr (FOLD && LIVE) {
+      if (chunks_done > 0) {
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+          for (int i = 0; i < FM; ++i)
+#pragma unroll
+            for (int j = 0; j < FN; ++j) acc[nb][i][j] = tot[nb][i][j] + acc[nb][i][j];
       }
     }
     // the loads of the stages past the range still write the ring: drain them

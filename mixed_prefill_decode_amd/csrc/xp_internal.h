@@ -31,7 +31,8 @@ inline int dtype_bytes(int dtype) { return dtype == XP_BF16 ? 2 : 4; }
 xp_status launch_rmsnorm(int dtype, const void* x, int x_is_f32, const void* gamma, void* y, int M,
                          int H, float eps, uint32_t* status_clear, hipStream_t s);
 
-int gemm_splits(int dtype, int epi, int N, int K);
+int gemm_chunks(int dtype, int epi, int N, int K);
+int gemm_split_count(int dtype, int epi, int M, int N, int K);
 size_t gemm_ws_bytes(int dtype, int epi, int M, int N, int K);
 void gemm_tile(int dtype, int epi, int M, int N, int K, int* bm, int* bn, int* splits);
 xp_status launch_gemm(int dtype, int epi, const void* A, const void* B, const void* B2, const void* R,

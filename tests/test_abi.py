@@ -173,7 +173,7 @@ def test_decode_workspace_size_matches_layer_layout():
 LAYER_TILES = [
     # (epilogue, M, N, K) -> (rows, cols, K splits)
     ((X.XP_EPI_F32, 1040, 6144, 4096), (128, 256, 1)), ((X.XP_EPI_ADD_T, 1040, 4096, 4096), (192, 128, 1)),
-    ((X.XP_EPI_SWIGLU, 1040, 14336, 4096), (128, 128, 1)), ((X.XP_EPI_ADD_F32, 1040, 4096, 14336), (192, 128, 4)),
+    ((X.XP_EPI_SWIGLU, 1040, 14336, 4096), (128, 128, 1)), ((X.XP_EPI_ADD_F32, 1040, 4096, 14336), (192, 128, 1)),
     ((X.XP_EPI_F32, 536, 7168, 5120), (192, 128, 1)), ((X.XP_EPI_ADD_T, 536, 5120, 5120), (96, 128, 1)),
     ((X.XP_EPI_SWIGLU, 536, 17408, 5120), (128, 128, 1)), ((X.XP_EPI_ADD_F32, 536, 5120, 17408), (192, 192, 3)),
     ((X.XP_EPI_F32, 128, 6144, 4096), (64, 128, 1)), ((X.XP_EPI_ADD_T, 128, 4096, 4096), (64, 128, 1)),
@@ -194,12 +194,17 @@ def test_gemm_tile_choice_on_the_layer_shapes():
         X.xp_gemm_tile(X.XP_BF16, X.XP_EPI_F32, 0, 64, 64)
 
 
-def test_gemm_workspace_depends_on_the_weight_shape_only():
-    # host-only: K splits follow (N, K); the partials take splits x weights x M x N fp32
-    for M in (16, 300, 1040):
+def test_gemm_workspace_follows_the_split_choice():
+    # host-only: long-K products are summed over K chunks that follow the weight shape
+    # (N, K); few rows run one unit per chunk, whose fp32 partials take chunks x weights
+    # x M x N, and many rows fold the chunks inside one unit per tile (no workspace)
+    for M in (16, 300):
         assert X.xp_gemm_workspace_size(X.XP_BF16, X.XP_EPI_ADD_F32, M, 4096, 14336) == 4 * M * 4096 * 4
         assert X.xp_gemm_workspace_size(X.XP_BF16, X.XP_EPI_ADD_F32, M, 5120, 25600) == 3 * M * 5120 * 4
-        assert X.xp_gemm_workspace_size(X.XP_BF16, X.XP_EPI_F32, M, 6144, 4096) == 0     # K < 3N: not split
+    assert X.xp_gemm_workspace_size(X.XP_BF16, X.XP_EPI_ADD_F32, 1040, 4096, 14336) == 0
+    assert X.xp_gemm_tile(X.XP_BF16, X.XP_EPI_ADD_F32, 1040, 4096, 14336)[2] == 1
+    for M in (16, 300, 1040):
+        assert X.xp_gemm_workspace_size(X.XP_BF16, X.XP_EPI_F32, M, 6144, 4096) == 0     # K < 3N: not chunked
         assert X.xp_gemm_workspace_size(X.XP_BF16, X.XP_EPI_SWIGLU, M, 14336, 4096) == 0
         assert X.xp_gemm_workspace_size(X.XP_BF16, X.XP_EPI_SWIGLU, M, 512, 4096) == 4 * 2 * M * 512 * 4
     assert X.xp_gemm_workspace_size(X.XP_BF16, X.XP_EPI_F32, 64, 512, 512) == 0   # too few K stages

@@ -121,28 +121,39 @@ def test_gemm_rows_do_not_depend_on_the_batch():
     assert torch.equal(full[100:140], part)
 
 
-@pytest.mark.parametrize("epi", [X.XP_EPI_F32, X.XP_EPI_SWIGLU])
+@pytest.mark.parametrize("epi", [X.XP_EPI_F32, X.XP_EPI_ADD_F32, X.XP_EPI_SWIGLU])
 def test_gemm_split_rows_do_not_depend_on_the_batch(epi):
-    # a projection split over K (the down-projection shape of an 8B layer, and a
-    # gate/up shape with two splits): rows inside a 1040-row batch equal the same
-    # rows computed alone, bit for bit
-    N, K = (4096, 14336) if epi == X.XP_EPI_F32 else (512, 4096)
+    # long-K products summed over K chunks (the down-projection shape of an 8B layer,
+    # and a gate/up shape with chunks): rows inside a 1040-row batch equal the same rows
+    # computed alone, bit for bit, whether the chunks ran as separate units (16 rows)
+    # or folded inside one unit per tile (1040 rows of the single-weight products)
+    N, K = (4096, 14336) if epi != X.XP_EPI_SWIGLU else (512, 4096)
     gen = torch.Generator(device="cuda")
     gen.manual_seed(11)
     A = torch.randn(1040, K, device="cuda", generator=gen).bfloat16()
     B = (torch.randn(N, K, device="cuda", generator=gen) * 0.05).bfloat16()
     B2 = (torch.randn(N, K, device="cuda", generator=gen) * 0.05).bfloat16() if epi == X.XP_EPI_SWIGLU else None
-    odt = torch.float32 if epi == X.XP_EPI_F32 else torch.bfloat16
+    R = torch.randn(1040, N, device="cuda", generator=gen)
+    odt = torch.bfloat16 if epi == X.XP_EPI_SWIGLU else torch.float32
     outs = []
     for lo, hi in ((0, 1040), (1024, 1040)):
         M = hi - lo
         ws, n = _gemm_ws("bf16", epi, M, N, K)
-        assert n > 0      # split over K
+        split = X.xp_gemm_tile(X.XP_BF16, epi, M, N, K)[2] > 1
+        assert split == (M == 16 or epi == X.XP_EPI_SWIGLU)
+        assert (n > 0) == split
         C = torch.empty((M, N), dtype=odt, device="cuda")
-        X.xp_gemm(X.XP_BF16, epi, A[lo:hi].contiguous(), B, B2, None, C, M, N, K, ws, n)
+        X.xp_gemm(X.XP_BF16, epi, A[lo:hi].contiguous(), B, B2, R[lo:hi].contiguous() if epi == X.XP_EPI_ADD_F32
+                  else None, C, M, N, K, ws, n)
         outs.append(C)
     _sync()
-    assert torch.equal(outs[0][1024:].view(torch.int16), outs[1].view(torch.int16))
+    view = torch.int16 if odt == torch.bfloat16 else torch.int32
+    assert torch.equal(outs[0][1024:].view(view), outs[1].view(view))
+    if epi != X.XP_EPI_SWIGLU:
+        # and against the fp64 product on a few rows (fp32 output)
+        rows = [0, 517, 1039]
+        ref = A[rows].double() @ B.double().T + (R[rows].double() if epi == X.XP_EPI_ADD_F32 else 0)
+        assert rel_fro(outs[0][rows].double().cpu().numpy(), ref.cpu().numpy()) < 1e-5
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
