@@ -134,6 +134,13 @@ xp_status check_desc(const xp_layer_shape* sh, const xp_batch_desc* d) {
   return XP_OK;
 }
 
+// CUs the step's prefill attention runs on: the context's prefill partition, else all
+// (a layout computed without a context assumes the whole current device)
+int prefill_cus(const xp_ctx* ctx) {
+  if (!ctx) return device_cus();
+  return ctx->decode_cus > 0 ? ctx->n_cus - ctx->decode_cus : ctx->n_cus;
+}
+
 xp_ws_layout make_layout(const xp_ctx* ctx, const xp_layer_shape* sh, const xp_batch_desc* d) {
   xp_ws_layout L;
   memset(&L, 0, sizeof(L));
@@ -158,7 +165,7 @@ xp_ws_layout make_layout(const xp_ctx* ctx, const xp_layer_shape* sh, const xp_b
   L.dec_ml = take(units * 2 * sizeof(float));
   L.dec_o = take(units * D * sizeof(float));
   L.pre_part = take(prefill_ws_bytes(int(Hq) / d->sp_degree, int(Hkv) / d->sp_degree, int(D), d->prior_len,
-                                     d->chunk_len));
+                                     d->chunk_len, prefill_cus(ctx)));
   {
     const int dt = sh->dtype;
     const size_t g = std::max(std::max(gemm_ws_bytes(dt, XP_EPI_F32, int(M), int((Hq + 2 * Hkv) * D), int(H)),
@@ -358,7 +365,7 @@ xp_status xp_layer_forward(xp_ctx* ctx, const xp_layer_shape* sh, const xp_batch
     return launch_prefill(dt, ws + L.q_pre, kv->pool, kv->n_pages, sh->page_size, d->pre_pages, d->pre_max_blocks,
                           hq_loc, hkv_loc, D, d->prior_len, d->chunk_len, d->local_row_offset, n_pl,
                           attn + size_t(r) * hq_loc * D * eb, Hq * D, d->peer_attn_out, hq_loc * D,
-                          ws + L.pre_part, status, q);
+                          ws + L.pre_part, status, prefill_cus(ctx), q);
   };
   const bool concurrent = ctx->s_dec && n_d > 0 && d->chunk_len > 0;
   if (!concurrent) {
@@ -465,7 +472,7 @@ xp_status xp_decode_attention(int32_t dtype, const void* q, const void* pool, in
 
 size_t xp_prefill_workspace_size(int32_t hq, int32_t hkv, int32_t d, int32_t prior, int32_t chunk) {
   if (hq <= 0 || hkv <= 0 || hq % hkv || d <= 0 || prior < 0 || chunk <= 0) return 0;
-  return prefill_ws_bytes(hq, hkv, d, prior, chunk);
+  return prefill_ws_bytes(hq, hkv, d, prior, chunk, device_cus());
 }
 
 xp_status xp_prefill_attention(int32_t dtype, const void* q, const void* pool, int32_t n_pages, int32_t S,
@@ -479,7 +486,7 @@ xp_status xp_prefill_attention(int32_t dtype, const void* q, const void* pool, i
   if (n_local > 0 && (!out_local || out_local_stride < hq * d)) return fail(XP_EINVAL, "xp_prefill_attention: out_local");
   if (chunk - n_local > 0 && (!out_peer || out_peer_stride < hq * d)) return fail(XP_EINVAL, "xp_prefill_attention: out_peer");
   return launch_prefill(dtype, q, pool, n_pages, S, pre_pages, pre_max_blocks, hq, hkv, d, prior, chunk, off, n_local,
-                        out_local, out_local_stride, out_peer, out_peer_stride, workspace, status,
+                        out_local, out_local_stride, out_peer, out_peer_stride, workspace, status, device_cus(),
                         static_cast<hipStream_t>(stream));
 }
 

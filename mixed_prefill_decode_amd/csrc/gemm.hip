@@ -91,22 +91,11 @@ int pick(const Candidate (&c)[NC], int M, int N, int K, int n_cus, int nb, int s
   return id;
 }
 
-int n_cus_of_current_device() {
-  static int cached[64] = {};
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (!cached[dev]) {
-    int n = 0;
-    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
-    cached[dev] = n;
-  }
-  return cached[dev];
-}
 
 template <typename T, int EPI>
 xp_status launch_epi(const void* A, const void* B, const void* B2, const void* R, void* C, int M, int N, int K,
                      int splits, int chunks, float* part, hipStream_t s) {
-  const int cus = n_cus_of_current_device();
+  const int cus = device_cus();
 #define XP_GEMM_ARGS A, B, B2, R, C, M, N, K, splits, chunks, part, s
   if constexpr (EPI == XP_EPI_SWIGLU) {
     switch (pick(kDual, M, N, K, cus, 2, splits)) {
@@ -150,6 +139,18 @@ xp_status launch_type(int epi, const void* A, const void* B, const void* B2, con
 
 }  // namespace
 
+int device_cus() {
+  static int cached[64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (!cached[dev]) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cached[dev] = n;
+  }
+  return cached[dev];
+}
+
 // K chunks of a GEMM against an [N, K] weight: a function of the weight's shape only.
 // Only long-K, narrow products (K >= 3N, the FFN down projection) are chunked: their
 // sum runs over C fixed K ranges in order, whether the chunks are separate work units
@@ -177,12 +178,12 @@ int gemm_split_count(int dtype, int epi, int M, int N, int K) {
   const int c = gemm_chunks(dtype, epi, N, K);
   if (c <= 1 || epi == XP_EPI_SWIGLU) return c;
   const long tiles = long(cdiv(M, 192)) * cdiv(N, 128);
-  return tiles * 10 < long(n_cus_of_current_device()) * 7 ? c : 1;
+  return tiles * 10 < long(device_cus()) * 7 ? c : 1;
 }
 
 void gemm_tile(int dtype, int epi, int M, int N, int K, int* bm, int* bn, int* splits) {
   const int sp = gemm_split_count(dtype, epi, M, N, K);
-  const int cus = n_cus_of_current_device();
+  const int cus = device_cus();
   const Candidate* c = nullptr;
   if (epi == XP_EPI_SWIGLU) {
     const int id = pick(kDual, M, N, K, cus, 2, sp);

@@ -514,36 +514,64 @@ Shape pick_shape(int d, int G) {
   return {XP_PREFILL_NQ, XP_PREFILL_MAXW};
 }
 
-Plan plan(int hq, int hkv, int d, int prior, int chunk) {
+// Key blocks per split.  A candidate split count gives work units of at most bps
+// 32-key blocks (a tile's key range cut into ceil(nkb / bps) pieces); the launch
+// takes about max(total work / CUs, longest unit) plus half a longest unit when units
+// outnumber the CUs, and every split unit adds its fp32 partials to the combine's
+// reads.  The estimate (microseconds, per-block and per-unit costs measured on
+// MI355X for d = 128 bf16) picks the candidate; on the 8B, 14B and 32B prefill
+// batches it matches the longest-first schedule of the units over the CUs and the
+// measured best split within a few percent (8B chunk: no split, 33 us vs 48 us at
+// the previous fixed target of 8192 waves; 14B: 2 splits, 154 vs 192 us).
+Plan plan(int hq, int hkv, int d, int prior, int chunk, int cus) {
   const int G = hq / hkv;
   const Shape sh = pick_shape(d, G);
   const int kQT = 32 * sh.nq;
   const int n_qt = (chunk + kQT - 1) / kQT;
   const int max_nkb = (prior + chunk + 31) / 32;
-  long total = 0;  // key blocks over all tiles
-  for (int qt = 0; qt < n_qt; ++qt) total += (prior + std::min(qt * kQT + kQT - 1, chunk - 1) + 1 + 31) / 32;
   const int wpg = std::min(G, sh.maxw);
-  const long wgs_per_tile = long(hkv) * ((G + wpg - 1) / wpg);
-  // aim at about two waves per SIMD over the whole launch (more splits cost fp32 partial
-  // traffic), splits of >= 8 blocks
-  const long target = std::max<long>(1, XP_PREFILL_TARGET_WAVES / wpg);
-  long bps = (total * wgs_per_tile + target - 1) / target;
-  bps = std::max<long>(8, bps);
-  bps = std::min<long>(bps, max_nkb);
-  bps = std::min<long>(bps, kMaxBps);
-  int n_split = int((max_nkb + bps - 1) / bps);
-  if (n_split > kMaxSplits) {
-    bps = (max_nkb + kMaxSplits - 1) / kMaxSplits;
-    n_split = int((max_nkb + bps - 1) / bps);
+  const long groups = long(hkv) * ((G + wpg - 1) / wpg);
+  const double t_blk = 0.75 + 0.065 * wpg, t_unit = 2.0;
+  cus = std::max(1, cus);
+  static constexpr int kCand[] = {1, 2, 3, 4, 6, 8, 12, 16, 24, 32, 48, 64};
+  double best = 1e300;
+  Plan out{std::min(max_nkb, kMaxBps), (max_nkb + kMaxBps - 1) / kMaxBps, wpg, sh.nq, kQT};
+  int last_bps = -1;
+  for (int ns : kCand) {
+    if (ns > kMaxSplits) break;
+    const int bps = (max_nkb + ns - 1) / ns;
+    if (bps > kMaxBps || bps == last_bps) continue;
+    last_bps = bps;
+    double total = 0.0, longest = 0.0;
+    long n_units = 0, split_units = 0;
+    for (int qt = 0; qt < n_qt; ++qt) {
+      const int nkb = (prior + std::min(qt * kQT + kQT - 1, chunk - 1) + 1 + 31) / 32;
+      const int n = (nkb + bps - 1) / bps;
+      total += nkb * t_blk + n * t_unit;
+      longest = std::max(longest, std::min(bps, nkb) * t_blk + t_unit);
+      n_units += n;
+      if (n > 1) split_units += n;
+    }
+    total *= double(groups);
+    n_units *= groups;
+    split_units *= groups;
+    double t = std::max(total / cus, longest);
+    if (n_units > cus) t = std::max(t, total / cus + 0.5 * longest);
+    if (split_units) t += 3.0 + double(split_units) * kQT * wpg * (d + 2) * 4.0 / 5e12 * 1e6;
+    if (t < best) {
+      best = t;
+      out.bps = bps;
+      out.n_split = (max_nkb + bps - 1) / bps;
+    }
   }
-  return {int(bps), n_split, wpg, sh.nq, kQT};
+  return out;
 }
 
 }  // namespace
 
-size_t prefill_ws_bytes(int hq, int hkv, int d, int prior, int chunk) {
+size_t prefill_ws_bytes(int hq, int hkv, int d, int prior, int chunk, int cus) {
   if (chunk <= 0) return 0;
-  const Plan p = plan(hq, hkv, d, prior, chunk);
+  const Plan p = plan(hq, hkv, d, prior, chunk, cus);
   if (p.n_split <= 1) return 0;
   const size_t units = size_t((chunk + p.qt - 1) / p.qt) * hq * p.n_split * p.qt;
   return align_up(units * 2 * sizeof(float), 256) + align_up(units * d * sizeof(float), 256);
@@ -552,7 +580,7 @@ size_t prefill_ws_bytes(int hq, int hkv, int d, int prior, int chunk) {
 xp_status launch_prefill(int dtype, const void* q, const void* pool, int n_pages, int S, const int32_t* pre_pages,
                          int pre_max_blocks, int hq, int hkv, int d, int prior, int chunk, int off, int n_local,
                          void* out_local, int out_local_stride, void* out_peer, int out_peer_stride, void* ws,
-                         uint32_t* status, hipStream_t s) {
+                         uint32_t* status, int cus, hipStream_t s) {
   if (chunk == 0) return XP_OK;
   if (S != kPage) return fail(XP_EUNSUPPORTED, "prefill attention: page_size %d (supported: 16)", S);
   if (hkv <= 0 || hq % hkv) return fail(XP_ESHAPE, "prefill attention: hq=%d hkv=%d", hq, hkv);
@@ -561,8 +589,8 @@ xp_status launch_prefill(int dtype, const void* q, const void* pool, int n_pages
   if (off < 0 || n_local < 0 || off + n_local > chunk) return fail(XP_ESHAPE, "prefill attention: off/n_local");
   if ((long(prior) + chunk + 31) / 32 > long(kMaxBps) * kMaxSplits)
     return fail(XP_EUNSUPPORTED, "prefill attention: %d keys exceed %d", prior + chunk, 32 * kMaxBps * kMaxSplits);
-  const Plan p = plan(hq, hkv, d, prior, chunk);
-  const size_t need = prefill_ws_bytes(hq, hkv, d, prior, chunk);
+  const Plan p = plan(hq, hkv, d, prior, chunk, cus);
+  const size_t need = prefill_ws_bytes(hq, hkv, d, prior, chunk, cus);
   if (need && !ws) return fail(XP_EWORKSPACE, "prefill attention: needs %zu bytes of workspace", need);
   const size_t units = size_t((chunk + p.qt - 1) / p.qt) * hq * p.n_split * p.qt;
   float* ml = static_cast<float*>(ws);

@@ -31,6 +31,7 @@ inline int dtype_bytes(int dtype) { return dtype == XP_BF16 ? 2 : 4; }
 xp_status launch_rmsnorm(int dtype, const void* x, int x_is_f32, const void* gamma, void* y, int M,
                          int H, float eps, uint32_t* status_clear, hipStream_t s);
 
+int device_cus();   // CUs of the current device (256 when none is visible)
 int gemm_chunks(int dtype, int epi, int N, int K);
 int gemm_split_count(int dtype, int epi, int M, int N, int K);
 size_t gemm_ws_bytes(int dtype, int epi, int M, int N, int K);
@@ -77,11 +78,11 @@ xp_status launch_decode(int dtype, const void* q, const void* pool, int n_pages,
                         int Hq, int Hkv, int d, void* out, int out_stride, float* part_ml,
                         float* part_o, int pages_per_split, uint32_t* status, hipStream_t s);
 
-size_t prefill_ws_bytes(int hq, int hkv, int d, int prior, int chunk);
+size_t prefill_ws_bytes(int hq, int hkv, int d, int prior, int chunk, int cus);
 xp_status launch_prefill(int dtype, const void* q, const void* pool, int n_pages, int S,
                          const int32_t* pre_pages, int pre_max_blocks, int hq, int hkv, int d,
                          int prior, int chunk, int off, int n_local, void* out_local,
                          int out_local_stride, void* out_peer, int out_peer_stride, void* ws,
-                         uint32_t* status, hipStream_t s);
+                         uint32_t* status, int cus, hipStream_t s);
 
 }  // namespace xp
