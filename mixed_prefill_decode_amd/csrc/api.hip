@@ -134,12 +134,10 @@ xp_status check_desc(const xp_layer_shape* sh, const xp_batch_desc* d) {
   return XP_OK;
 }
 
-// CUs the step's prefill attention runs on: the context's prefill partition, else all
-// (a layout computed without a context assumes the whole current device)
-int prefill_cus(const xp_ctx* ctx) {
-  if (!ctx) return device_cus();
-  return ctx->decode_cus > 0 ? ctx->n_cus - ctx->decode_cus : ctx->n_cus;
-}
+// CUs the prefill key-split plan assumes: the whole device in every split-attention
+// mode, so that the mode never changes which partials are summed (serialized,
+// concurrent and partitioned steps give bit-identical results)
+int prefill_cus(const xp_ctx* ctx) { return ctx ? ctx->n_cus : device_cus(); }
 
 xp_ws_layout make_layout(const xp_ctx* ctx, const xp_layer_shape* sh, const xp_batch_desc* d) {
   xp_ws_layout L;

@@ -514,7 +514,8 @@ Shape pick_shape(int d, int G) {
   return {XP_PREFILL_NQ, XP_PREFILL_MAXW};
 }
 
-// Key blocks per split.  A candidate split count gives work units of at most bps
+// Key blocks per split (planned for the whole device in every split-attention mode, so
+// the mode never changes the summation).  A candidate split count gives work units of at most bps
 // 32-key blocks (a tile's key range cut into ceil(nkb / bps) pieces); the launch
 // takes about max(total work / CUs, longest unit) plus half a longest unit when units
 // outnumber the CUs, and every split unit adds its fp32 partials to the combine's
