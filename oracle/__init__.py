@@ -10,8 +10,9 @@ Pages cited (by title; sections, equations, tables and figures as printed):
 * "ConfluxServe: Reconciling Resource Utilization and Parallelism Efficiency
   across Prefill and Decode in LLM Serving" -- the method: §4 (Conflux
   Parallelism execution flow, Fig. 7; KV residency, Fig. 8), §6.1 (coordinated
-  attention overlap), §6.2 (Eq. 2-6), §6.3 (waterfill dispatch), App. B
-  (Table 7), App. D (Eq. 7-12), App. E (Algorithm 2).
+  attention overlap), §6.2 (Eq. 2-6), §6.3 (waterfill dispatch, dual-mode
+  decode placement), §6.4 (Algorithm 1), App. B (Table 7), App. D (Eq. 7-12),
+  App. E (Algorithm 2), App. F (Algorithm 3), App. G (Algorithm 4).
 * "Adaptive Context Parallelism for Production LLM Serving" -- §2.1 (causal
   attention with mask M_ij = 0 for j <= i), §2.2 Eq. 1 (remaining attention
   workload R*P + R(R+1)/2).
@@ -32,6 +33,9 @@ Modules:
 * ``waterfill`` -- latency model (Eq. 2-11) and waterfill dispatch
   (Algorithm 2) in Python integers and doubles (pinned: the worked example,
   brute-force min-max enumeration, linear scan of levels, closed forms).
+* ``scheduler`` -- SLO-aware scheduler (Algorithm 1), dual-mode decode
+  placement (Algorithm 3) and Moore-Hodgson admission (Algorithm 4) (pinned:
+  brute-force largest on-time set, hand-worked cases, invariants).
 
 Parity status: every function here has at least one pin in
 ``tests/test_oracle_*.py``; none is "parity unpinned".

@@ -35,13 +35,13 @@ __all__ = [
     "TENSOR_IDS", "Workload", "Instance", "PagePool", "WaterfillCase",
     "WORKLOADS", "PARITY_WORKLOADS", "get_workload", "make_instance",
     "f32_to_bf16_bits", "bf16_bits_to_f32", "storage_to_f64",
-    "waterfill_cases", "make_latency_model",
+    "waterfill_cases", "make_latency_model", "SchedulerCase", "scheduler_case",
 ]
 
 TENSOR_IDS = {
     "x": 0, "w_qkv": 1, "w_o": 2, "w_gate": 3, "w_up": 4, "w_down": 5,
     "kv": 6, "peer_qkv_in": 7, "peer_attn_in": 8, "dec_ctx": 9,
-    "page_perm": 10, "kv_bank_idx": 11, "extra": 12,
+    "page_perm": 10, "kv_bank_idx": 11, "extra": 12, "sched_state": 13, "sched_queue": 14,
 }
 
 # Fixed draw granularity for the KV pool, so the drawn sequence is defined.
@@ -436,3 +436,60 @@ def waterfill_cases() -> list:
     cases.append(WaterfillCase("C5-4rank-B0", split, sums, [0, 0, 0, 0], [], None,
                                -1, 0.100, 16, 1 << 16, m0))
     return cases
+
+
+@dataclass
+class SchedulerCase:
+    """Decode state of one XP instance and a pending prefill queue (host values)."""
+    name: str
+    n_decode_tokens: list
+    decode_ctx_sum: list
+    kv_used: list
+    kv_capacity: list
+    m_remaining: list
+    c_processed: list
+    deadlines: list
+    now: float
+    tau: float
+    quantum: int
+    eta: float
+    headroom: int
+    model: dict
+
+
+# Mooncake-Toolagent prompt lengths (P50 6,346, P95 26,114 tokens), the stand-in for the
+# pages' traces: lognormal with mu = ln 6346 and sigma = ln(26114 / 6346) / 1.644854.
+_PROMPT_MU, _PROMPT_SIGMA = float(np.log(6346.0)), float(np.log(26114.0 / 6346.0) / 1.644854)
+
+
+def scheduler_case(depth: int, n_ranks: int = 8, seed: int = 0, kv_capacity: int = 1_600_000,
+                   tau: float = 0.100, quantum: int = 16, eta: float = 0.8, headroom: int = 4096) -> SchedulerCase:
+    """A scheduling iteration on ``n_ranks`` ranks with ``depth`` pending prefills.
+
+    Each rank holds 4..32 resident decodes whose contexts are drawn from the prompt
+    distribution; its KV use is their sum, against ``kv_capacity`` tokens (about
+    200 GB of 128 KiB-per-token KV, an 8B model on one MI355X).  Pending requests
+    draw a prompt from the same distribution; a quarter already have part of it
+    cached (c > 0).  They arrived in the last 2 s and their TTFT deadline is
+    arrival + 0.5 s + 0.1 ms per prompt token.  The latency model has the magnitudes of
+    an 8B layer on one MI355X (32 layers; about 0.5 us per shared-linear token, 1 ns per
+    decode context token, 60 ps per prefill attention pair), in dyadic coefficients.
+    """
+    rs = _rng(seed, "sched_state")
+    nd = rs.integers(4, 33, size=n_ranks)
+    ctx = [np.clip(np.rint(rs.lognormal(_PROMPT_MU, _PROMPT_SIGMA, size=int(n))), 1, 65536).astype(np.int64)
+           for n in nd]
+    ctx_sum = [int(c.sum()) for c in ctx]
+    rq = _rng(seed, "sched_queue")
+    prompt = np.clip(np.rint(rq.lognormal(_PROMPT_MU, _PROMPT_SIGMA, size=depth)), 16, 65536).astype(np.int64)
+    partial = rq.random(depth) < 0.25
+    done = np.where(partial, np.floor(prompt * rq.uniform(0.1, 0.9, size=depth)), 0).astype(np.int64)
+    now = 100.0
+    arrival = now - rq.uniform(0.0, 2.0, size=depth)
+    deadline = arrival + 0.5 + 1e-4 * prompt
+    return SchedulerCase(f"sched-N{n_ranks}-R{depth}-s{seed}", [int(v) for v in nd], ctx_sum, list(ctx_sum),
+                         [kv_capacity] * n_ranks, [int(v) for v in prompt - done], [int(v) for v in done],
+                         [float(v) for v in deadline], now, tau, quantum, eta, headroom,
+                         make_latency_model(gamma=2.0 ** -21, gamma0=2.0 ** -15, a_d=2.0 ** -30, a_d0=2.0 ** -16,
+                                            a_p=2.0 ** -34, a_p0=2.0 ** -16, a_comm=2.0 ** -24,
+                                            a_comm0=2.0 ** -16, n_layers=32))
