@@ -142,6 +142,33 @@ def cpu_baseline(inst, budget_s: float) -> dict:
                       f"({dt:.2f} s each)"}
 
 
+def scheduler_timing(X, repeats: int = 100) -> dict:
+    """Host time of one SLO-aware scheduling iteration (admission, ordering, one dispatch
+    per chosen chunk, decode placement) on 8 simulated ranks, at the pending-queue depths
+    the pages report (ConfluxServe §8.5, Table 5): mean and standard deviation over
+    ``repeats`` calls of the native entry point, arguments marshalled once."""
+    import dataclasses
+    import statistics
+    from synth import scheduler_case
+    out = {"unit": "us", "ranks": 8, "repeats": repeats, "depths": {}}
+    for depth in (10, 50, 100, 500):
+        c = dataclasses.asdict(scheduler_case(depth))
+        c.pop("name")
+        call = X.ScheduleCall(**c)
+        for _ in range(10):
+            call.call()
+        ts = []
+        for _ in range(repeats):
+            t0 = time.perf_counter()
+            call.call()
+            ts.append(time.perf_counter() - t0)
+        r = call.result()
+        out["depths"][depth] = {"mean": round(statistics.mean(ts) * 1e6, 1),
+                                "std": round(statistics.stdev(ts) * 1e6, 1), "chunks": r["n_selected"],
+                                "admitted": r["n_admitted"], "tokens": sum(r["prefill_assign"])}
+    return out
+
+
 def calibrate_decode_cus(X, torch, step, inst, dev, timer, n_cus, repeats) -> tuple[int, dict]:
     """Fewest CUs whose standalone decode-attention bandwidth is >= 90% of the all-CU figure
     (the decode CU-allocation rule of the pages).  Candidates are multiples of 32: the mask
@@ -347,6 +374,9 @@ def main():
     log(f"[bench] layer {ms * 1e3:.1f} us/step, {tokens_per_s:.0f} tokens/s; kernels {json.dumps(kern)}")
     log(f"[bench] split attention {json.dumps(seg)}")
 
+    sched = scheduler_timing(X)
+    log(f"[bench] scheduler {json.dumps(sched)}")
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(inst, args.cpu_budget_s)
@@ -362,6 +392,7 @@ def main():
                    "decode_cus": k, "split_attention": timed_mode if wl.n_decode and wl.chunk_len else None,
                    "page_size": wl.page_size},
         "roofline": roofline, "cpu_baseline": cpu, "kernels": kern, "split_attention": seg,
+        "scheduler": sched,
     }
     print(json.dumps(line), flush=True)
 

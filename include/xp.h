@@ -367,6 +367,93 @@ xp_status xp_iteration_latency(const xp_latency_model* model, int32_t n_ranks,
                                const int32_t* n_prefill_tokens, int32_t n_chunks,
                                const int32_t* chunk_len, const int64_t* chunk_ctx, double* t_iter);
 
+/* ------------------------------------------------------------------------ */
+/* SLO-aware scheduler around the dispatcher (host only, thread-safe)       */
+/* ------------------------------------------------------------------------ */
+
+/* Resident decode state D of one XP instance, per rank (host arrays). */
+typedef struct {
+  int32_t n_ranks;                 /* N >= 1                                       */
+  const int32_t* n_decode_tokens;  /* [N] n_d^r: resident decodes (one token each) */
+  const int64_t* decode_ctx_sum;   /* [N] aggregate decode context on rank r       */
+  const int64_t* kv_used;          /* [N] KV tokens resident on rank r (>= 0)      */
+  const int64_t* kv_capacity;      /* [N] KV token capacity of rank r (> 0)        */
+} xp_decode_state;
+
+/* Pending prefill requests R (host arrays, request index = position). */
+typedef struct {
+  int32_t n;                       /* R >= 0                                       */
+  const int32_t* m_remaining;      /* [R] m_i >= 1: prompt tokens still to prefill */
+  const int64_t* c_processed;      /* [R] c_i >= 0: prompt tokens already cached   */
+  const double* deadline;          /* [R] d_i: TTFT deadline (finite), same clock  */
+                                   /*      as `now` below                          */
+} xp_prefill_queue;
+
+/* Algorithm 4 ([CS] App. G): Moore-Hodgson admission under the fixed
+ * per-iteration budget `ref_budget` (B0 >= 0).  Requests are taken in EDF order
+ * (deadline, then index); request i brings the capacity
+ * K_i = max(0, floor((d_i - now) / tbt_slo)) * B0 (floor clamped at 2^40
+ * iterations); whenever the admitted total C exceeds K_i, the admitted request
+ * with the largest m (the later in EDF order among equal m) is removed.
+ * order: caller array [R], receives the admitted requests in EDF order followed
+ * by the removed ones in SJF order (m, then EDF order); *n_admitted their split.
+ * XP_EINVAL on null arrays, m < 1, c < 0, a non-finite deadline, tbt_slo <= 0
+ * or B0 < 0. */
+xp_status xp_admission(const xp_prefill_queue* queue, int64_t ref_budget, double now, double tbt_slo,
+                       int32_t* order, int32_t* n_admitted);
+
+/* Algorithm 3 ([CS] App. F): dual-mode decode placement of a request whose KV
+ * state is kv_need tokens.  Feasible ranks keep `kv_headroom` tokens free:
+ * kv_used + kv_need + kv_headroom <= kv_capacity.  Among feasible ranks whose
+ * utilization kv_used / kv_capacity (fp64) is below kv_util_threshold (eta),
+ * worst fit: the smallest decode_ctx_sum; if there is none, best fit: the
+ * highest utilization (compared exactly).  Ties go to the lowest rank index.
+ * *rank = -1 means Infeasible, which is a result, not an error.
+ * XP_EINVAL on null arrays, kv_need < 0, kv_headroom < 0 or a capacity <= 0. */
+xp_status xp_decode_placement(const xp_decode_state* state, int64_t kv_need, double kv_util_threshold,
+                              int64_t kv_headroom, int32_t* rank);
+
+typedef struct {
+  double now;                      /* t                                            */
+  double tbt_slo;                  /* tau (> 0)                                    */
+  int32_t quantum;                 /* alignment quantum q >= 1 of the dispatcher   */
+  double kv_util_threshold;        /* eta                                          */
+  int64_t kv_headroom;             /* h, KV tokens kept free on a host rank        */
+  const xp_latency_model* model;
+} xp_sched_params;
+
+#define XP_SCHED_DONE 0      /* every pending request was considered              */
+#define XP_SCHED_BUDGET 1    /* a dispatch returned l = 0: budget exhausted       */
+#define XP_SCHED_NO_HOST 2   /* a completing prefill had no feasible decode host  */
+
+typedef struct {
+  int64_t ref_budget;        /* B0, the dispatcher's budget with no candidate         */
+  int32_t n_admitted;        /* |R_adm|                                               */
+  int32_t n_selected;        /* chunks in the batch: the first n_selected of order    */
+  int32_t stop;              /* XP_SCHED_*                                             */
+  int32_t* order;            /* caller array [R]: consideration order (EDF admitted,  */
+                             /*   then SJF removed)                                   */
+  int32_t* chunk_len;        /* caller array [R]: l_i by request index, 0 if unchosen */
+  int32_t* decode_rank;      /* caller array [R]: g_i when the chunk completes the    */
+                             /*   prompt, else -1                                     */
+  int32_t* prefill_assign;   /* caller array [N]: A_p, prefill tokens per rank        */
+  int32_t* request_assign;   /* caller array [R, N] (may be NULL): A_i by request     */
+} xp_schedule_out;
+
+/* Algorithm 1 ([CS] §6.4): one iteration of the SLO-aware scheduler.  B0 is
+ * the dispatcher's budget for the current decode state with no chunk selected
+ * and no candidate (level bound max_r n_d^r + sum_i m_i); admission and
+ * ordering follow xp_admission; each request in turn gets the dispatcher's
+ * chunk and increment (xp_waterfill on the current decode state, the chunks
+ * selected so far and their cumulative assignment); l = 0 ends the
+ * iteration; a chunk that completes its prompt (l = m) needs a decode host from
+ * xp_decode_placement on the tentative state (which then carries the earlier
+ * placements of this iteration: +1 decode, +c+m context and KV tokens), and
+ * without one the chunk is discarded and the iteration ends.  Same argument
+ * errors as the three calls above. */
+xp_status xp_schedule(const xp_decode_state* state, const xp_prefill_queue* queue, const xp_sched_params* params,
+                      xp_schedule_out* out);
+
 #ifdef __cplusplus
 }
 #endif

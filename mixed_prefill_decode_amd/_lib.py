@@ -20,11 +20,13 @@ __all__ = ["XpError", "lib", "XP_F32", "XP_BF16", "XP_EPI_F32", "XP_EPI_ADD_T", 
            "xp_kv_gather",
            "xp_decode_workspace_size", "xp_decode_attention", "xp_prefill_workspace_size", "xp_prefill_attention",
            "xp_probe_hw_ids",
-           "xp_waterfill", "xp_iteration_latency", "xp_build_info", "xp_last_error"]
+           "xp_waterfill", "xp_iteration_latency", "xp_admission", "xp_decode_placement", "xp_schedule",
+           "ScheduleCall", "XP_SCHED_DONE", "XP_SCHED_BUDGET", "XP_SCHED_NO_HOST", "xp_build_info", "xp_last_error"]
 
 XP_F32, XP_BF16 = 0, 1
 XP_EPI_F32, XP_EPI_ADD_T, XP_EPI_ADD_F32, XP_EPI_SWIGLU = 0, 1, 2, 3
 XP_DEV_BAD_PAGE = 1
+XP_SCHED_DONE, XP_SCHED_BUDGET, XP_SCHED_NO_HOST = 0, 1, 2
 STATUS_NAMES = {0: "XP_OK", -1: "XP_EINVAL", -2: "XP_ESHAPE", -3: "XP_EPAGE", -4: "XP_EHIP",
                 -5: "XP_EUNSUPPORTED", -6: "XP_EWORKSPACE"}
 
@@ -38,7 +40,7 @@ EXPORTED = ["xp_last_error", "xp_build_info", "xp_ctx_create", "xp_ctx_destroy",
             "xp_decode_workspace_size",
             "xp_decode_attention", "xp_prefill_workspace_size", "xp_prefill_attention", "xp_probe_hw_ids",
             "xp_waterfill",
-            "xp_iteration_latency"]
+            "xp_iteration_latency", "xp_admission", "xp_decode_placement", "xp_schedule"]
 
 
 class XpError(RuntimeError):
@@ -97,6 +99,28 @@ class WaterfillOut(C.Structure):
                 ("assign", C.c_void_p)]
 
 
+class DecodeState(C.Structure):
+    _fields_ = [("n_ranks", C.c_int32), ("n_decode_tokens", C.c_void_p), ("decode_ctx_sum", C.c_void_p),
+                ("kv_used", C.c_void_p), ("kv_capacity", C.c_void_p)]
+
+
+class PrefillQueue(C.Structure):
+    _fields_ = [("n", C.c_int32), ("m_remaining", C.c_void_p), ("c_processed", C.c_void_p),
+                ("deadline", C.c_void_p)]
+
+
+class SchedParams(C.Structure):
+    _fields_ = [("now", C.c_double), ("tbt_slo", C.c_double), ("quantum", C.c_int32),
+                ("kv_util_threshold", C.c_double), ("kv_headroom", C.c_int64),
+                ("model", C.POINTER(LatencyModel))]
+
+
+class ScheduleOut(C.Structure):
+    _fields_ = [("ref_budget", C.c_int64), ("n_admitted", C.c_int32), ("n_selected", C.c_int32),
+                ("stop", C.c_int32), ("order", C.c_void_p), ("chunk_len", C.c_void_p),
+                ("decode_rank", C.c_void_p), ("prefill_assign", C.c_void_p), ("request_assign", C.c_void_p)]
+
+
 _LIB = None
 _vp, _i32, _sz, _f32, _f64 = C.c_void_p, C.c_int32, C.c_size_t, C.c_float, C.c_double
 
@@ -131,6 +155,10 @@ def _declare(L):
         "xp_waterfill": (S, [C.POINTER(WaterfillIn), C.POINTER(WaterfillOut)]),
         "xp_iteration_latency": (S, [C.POINTER(LatencyModel), _i32, _vp, _vp, _vp, _i32, _vp, _vp,
                                      C.POINTER(_f64)]),
+        "xp_admission": (S, [C.POINTER(PrefillQueue), C.c_int64, _f64, _f64, _vp, C.POINTER(_i32)]),
+        "xp_decode_placement": (S, [C.POINTER(DecodeState), C.c_int64, _f64, C.c_int64, C.POINTER(_i32)]),
+        "xp_schedule": (S, [C.POINTER(DecodeState), C.POINTER(PrefillQueue), C.POINTER(SchedParams),
+                            C.POINTER(ScheduleOut)]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(L, name)
@@ -342,3 +370,80 @@ def xp_iteration_latency(model: dict, n_decode_tokens, decode_ctx_sum, n_prefill
     _check(lib().xp_iteration_latency(C.byref(m), N, _ptr(nd), _ptr(cs), _ptr(npf), len(chunks), _ptr(cl),
                                       _ptr(cc), C.byref(t)))
     return t.value
+
+
+_STOP_NAMES = {XP_SCHED_DONE: "done", XP_SCHED_BUDGET: "budget", XP_SCHED_NO_HOST: "no_host"}
+
+
+def _queue(m_remaining, c_processed, deadlines):
+    m = np.ascontiguousarray(m_remaining, dtype=np.int32)
+    c = np.ascontiguousarray(c_processed, dtype=np.int64)
+    d = np.ascontiguousarray(deadlines, dtype=np.float64)
+    return PrefillQueue(len(m), _ptr(m), _ptr(c), _ptr(d)), (m, c, d)
+
+
+def _state(n_decode_tokens, decode_ctx_sum, kv_used, kv_capacity):
+    arrs = (np.ascontiguousarray(n_decode_tokens, dtype=np.int32),
+            np.ascontiguousarray(decode_ctx_sum, dtype=np.int64),
+            np.ascontiguousarray(kv_used, dtype=np.int64), np.ascontiguousarray(kv_capacity, dtype=np.int64))
+    return DecodeState(len(arrs[0]), *[_ptr(a) for a in arrs]), arrs
+
+
+def xp_admission(m_remaining, deadlines, ref_budget, now, tau, c_processed=None):
+    """(admitted in EDF order, removed in SJF order) -- Algorithm 4."""
+    q, keep = _queue(m_remaining, [0] * len(m_remaining) if c_processed is None else c_processed, deadlines)
+    order = np.zeros(max(1, q.n), dtype=np.int32)
+    n_adm = _i32()
+    _check(lib().xp_admission(C.byref(q), int(ref_budget), float(now), float(tau), _ptr(order), C.byref(n_adm)))
+    o = order[:q.n].tolist()
+    return o[:n_adm.value], o[n_adm.value:]
+
+
+def xp_decode_placement(decode_ctx_sum, kv_used, kv_capacity, need, eta, headroom, n_decode_tokens=None):
+    """Host rank of a request with ``need`` KV tokens, or None (Infeasible) -- Algorithm 3."""
+    nd = [0] * len(kv_used) if n_decode_tokens is None else n_decode_tokens
+    st, keep = _state(nd, decode_ctx_sum, kv_used, kv_capacity)
+    g = _i32()
+    _check(lib().xp_decode_placement(C.byref(st), int(need), float(eta), int(headroom), C.byref(g)))
+    return None if g.value < 0 else g.value
+
+
+class ScheduleCall:
+    """One xp_schedule call with its arguments marshalled once: ``call()`` runs the
+    scheduler on them (so a caller can time the native call alone), ``result()``
+    decodes the last call's outputs."""
+
+    def __init__(self, *, n_decode_tokens, decode_ctx_sum, kv_used, kv_capacity, m_remaining, c_processed,
+                 deadlines, now, tau, quantum, eta, headroom, model):
+        self.state, self._keep_s = _state(n_decode_tokens, decode_ctx_sum, kv_used, kv_capacity)
+        self.queue, self._keep_q = _queue(m_remaining, c_processed, deadlines)
+        N, R = self.state.n_ranks, self.queue.n
+        self._model = _model(model)
+        self.params = SchedParams(float(now), float(tau), int(quantum), float(eta), int(headroom),
+                                  C.pointer(self._model))
+        self.order = np.zeros(max(1, R), dtype=np.int32)
+        self.chunk = np.zeros(max(1, R), dtype=np.int32)
+        self.host = np.zeros(max(1, R), dtype=np.int32)
+        self.a_p = np.zeros(N, dtype=np.int32)
+        self.req = np.zeros((max(1, R), N), dtype=np.int32)
+        self.out = ScheduleOut(0, 0, 0, 0, _ptr(self.order), _ptr(self.chunk), _ptr(self.host), _ptr(self.a_p),
+                               _ptr(self.req))
+        self._fn = lib().xp_schedule
+        self._args = (C.byref(self.state), C.byref(self.queue), C.byref(self.params), C.byref(self.out))
+
+    def call(self):
+        _check(self._fn(*self._args))
+        return self
+
+    def result(self) -> dict:
+        R, o = self.queue.n, self.out
+        return dict(ref_budget=o.ref_budget, n_admitted=o.n_admitted, order=self.order[:R].tolist(),
+                    n_selected=o.n_selected, stop=_STOP_NAMES[o.stop], chunk_len=self.chunk[:R].tolist(),
+                    decode_rank=self.host[:R].tolist(), prefill_assign=self.a_p.tolist(),
+                    request_assign=self.req[:R].tolist())
+
+
+def xp_schedule(**kw) -> dict:
+    """One iteration of the SLO-aware scheduler (Algorithm 1); keyword arguments as
+    ScheduleCall."""
+    return ScheduleCall(**kw).call().result()

@@ -217,3 +217,85 @@ def test_gemm_rejects_unsupported_k_before_launching():
     assert e.value.status == -5
     with pytest.raises(X.XpError):
         X.xp_gemm(X.XP_BF16, 9, 16, 16, None, None, 16, 4, 4, 64, stream=0)
+
+
+# ---- SLO-aware scheduler (Algorithms 1, 3, 4) ---------------------------------------
+
+def _sched_case(rnd):
+    N, R = rnd.randint(1, 8), rnd.randint(0, 24)
+    nd = [rnd.randint(0, 64) for _ in range(N)]
+    return dict(n_decode_tokens=nd, decode_ctx_sum=[rnd.randint(0, 200000) * (n > 0) for n in nd],
+                kv_used=[rnd.randint(0, 400000) for _ in range(N)],
+                kv_capacity=[rnd.randint(300000, 600000) for _ in range(N)],
+                m_remaining=[rnd.randint(1, 20000) for _ in range(R)],
+                c_processed=[rnd.choice([0, 0, rnd.randint(1, 30000)]) for _ in range(R)],
+                deadlines=[rnd.uniform(-0.5, 3.0) for _ in range(R)], now=0.0,
+                tau=rnd.uniform(0.02, 0.3), quantum=rnd.choice([1, 8, 16, 64]), eta=rnd.uniform(0.2, 1.0),
+                headroom=rnd.choice([0, 1024, 8192]), model=_rand_model(rnd))
+
+
+def test_schedule_bit_exact_with_oracle_on_random_iterations():
+    from oracle import scheduler as sch
+    rnd = random.Random(21)
+    stops, selected = {}, 0
+    for _ in range(300):
+        c = _sched_case(rnd)
+        # keep the synthetic coefficients in a range where some chunks fit
+        c["model"] = dict(c["model"], gamma=c["model"]["gamma"] * 1e-6, gamma0=c["model"]["gamma0"] * 1e-4,
+                          a_d=c["model"]["a_d"] * 1e-8, a_d0=c["model"]["a_d0"] * 1e-4,
+                          a_p=c["model"]["a_p"] * 1e-10, a_p0=c["model"]["a_p0"] * 1e-4,
+                          a_comm=c["model"]["a_comm"] * 1e-7, a_comm0=c["model"]["a_comm0"] * 1e-4)
+        got = X.xp_schedule(**c)
+        assert got == sch.schedule(**c)
+        stops[got["stop"]] = stops.get(got["stop"], 0) + 1
+        selected += got["n_selected"] > 0
+    # the cases reach every way an iteration can end, and most select something
+    assert set(stops) == {"done", "budget", "no_host"} and selected > 150
+
+
+@pytest.mark.parametrize("depth", [10, 50, 100, 500])
+def test_schedule_bit_exact_on_synthetic_queues(depth):
+    import dataclasses
+    from oracle import scheduler as sch
+    from synth import scheduler_case
+    for seed in range(3):
+        c = dataclasses.asdict(scheduler_case(depth, seed=seed))
+        c.pop("name")
+        got = X.xp_schedule(**c)
+        assert got == sch.schedule(**c)
+        assert got["n_selected"] > 0
+
+
+def test_admission_and_placement_bit_exact_with_oracle():
+    from oracle import scheduler as sch
+    rnd = random.Random(8)
+    for _ in range(500):
+        R = rnd.randint(0, 30)
+        m = [rnd.randint(1, 50) for _ in range(R)]
+        d = [rnd.choice([rnd.uniform(-1, 10), float(rnd.randint(0, 6))]) for _ in range(R)]
+        b0, tau, now = rnd.randint(0, 60), rnd.choice([0.5, 1.0, 0.3]), rnd.choice([0.0, 0.7])
+        assert X.xp_admission(m, d, b0, now, tau) == sch.admission(m, d, b0, now, tau)
+        N = rnd.randint(1, 8)
+        cap = [rnd.randint(100, 2000) for _ in range(N)]
+        used = [rnd.randint(0, c) for c in cap]
+        ctx = [rnd.randint(0, 50) for _ in range(N)]
+        need, eta, h = rnd.randint(0, 400), rnd.uniform(0, 1), rnd.choice([0, 50])
+        assert X.xp_decode_placement(ctx, used, cap, need, eta, h) == sch.placement(ctx, used, cap, need, eta, h)
+
+
+def test_scheduler_rejects_bad_arguments():
+    good = dict(n_decode_tokens=[1, 2], decode_ctx_sum=[10, 20], kv_used=[0, 0], kv_capacity=[100, 100],
+                m_remaining=[5], c_processed=[0], deadlines=[1.0], now=0.0, tau=0.1, quantum=1, eta=0.5,
+                headroom=0, model=_rand_model(random.Random(0)))
+    X.xp_schedule(**good)
+    for bad in (dict(kv_capacity=[100, 0]), dict(m_remaining=[0]), dict(c_processed=[-1]),
+                dict(deadlines=[float("nan")]), dict(tau=0.0), dict(quantum=0), dict(headroom=-1),
+                dict(n_decode_tokens=[-1, 2])):
+        with pytest.raises(X.XpError) as e:
+            X.xp_schedule(**dict(good, **bad))
+        assert e.value.status == -1
+    with pytest.raises(X.XpError):
+        X.xp_admission([3], [1.0], -1, 0.0, 1.0)
+    with pytest.raises(X.XpError):
+        X.xp_decode_placement([0], [0], [10], -5, 0.5, 0)
+    assert X.xp_decode_placement([0], [95], [100], 10, 0.5, 0) is None      # Infeasible is a result
