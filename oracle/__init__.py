@@ -33,6 +33,9 @@ Modules:
 * ``waterfill`` -- latency model (Eq. 2-11) and waterfill dispatch
   (Algorithm 2) in Python integers and doubles (pinned: the worked example,
   brute-force min-max enumeration, linear scan of levels, closed forms).
+* ``estimator`` -- fitting the latency model's base functions (App. D) and the
+  contention factors of Eq. 4 from profiles (pinned: exact recovery from noiseless
+  data, closed forms, optimality of the relative-error loss).
 * ``scheduler`` -- SLO-aware scheduler (Algorithm 1), dual-mode decode
   placement (Algorithm 3) and Moore-Hodgson admission (Algorithm 4) (pinned:
   brute-force largest on-time set, hand-worked cases, invariants).
