@@ -16,6 +16,7 @@ from __future__ import annotations
 import argparse
 import hashlib
 import json
+import math
 import os
 import sys
 import time
@@ -45,6 +46,13 @@ def parse():
     p.add_argument("--kernel-only", choices=["none", "swiglu", "decode", "prefill", "copy"], default="none",
                    help="only launch one kernel repeatedly (for counter runs)")
     p.add_argument("--repeats", type=int, default=20, help="launches per kernel timing")
+    p.add_argument("--estimator", action="store_true",
+                   help="fit the iteration-latency estimator on this GPU from isolated profiles and report its "
+                        "error on random heterogeneous batches, instead of the layer benchmark")
+    p.add_argument("--estimator-decode-cus", type=int, default=128,
+                   help="decode CUs of the concurrent split attention the estimator models")
+    p.add_argument("--estimator-batches", type=int, default=200)
+    p.add_argument("--estimator-out", default=None, help="write every profiled and evaluated batch here (JSON)")
     p.add_argument("--probe", default=None,
                    help="internal: time one split-attention mode in this fresh process ('rule' = the pages' "
                         "decode-CU calibration, or a decode CU count) and print it as one JSON line")
@@ -142,6 +150,178 @@ def cpu_baseline(inst, budget_s: float) -> dict:
                       f"({dt:.2f} s each)"}
 
 
+class EstimatorRig:
+    """Device buffers for timing Llama-3.1-8B layer steps of arbitrary batch mixes: random
+    bf16 weights, a random KV pool large enough for 128 decodes at 16K context plus a
+    10K-token chunk after 16K cached tokens, and page tables cut from one random
+    permutation of the pool."""
+
+    H, HQ, HKV, D, F, PAGE = 4096, 32, 8, 128, 14336, 16
+    MAX_ROWS = 10240 + 128
+
+    def __init__(self, X, torch, ctx):
+        self.X, self.torch, self.ctx = X, torch, ctx
+        g = torch.Generator(device="cuda")
+        g.manual_seed(1234)
+        H, HQ, HKV, D, F = self.H, self.HQ, self.HKV, self.D, self.F
+
+        def rnd(*shape, scale=1.0):
+            out = torch.empty(shape, dtype=torch.bfloat16, device="cuda")
+            flat = out.view(-1)
+            step = 1 << 28
+            for o in range(0, flat.numel(), step):
+                n = min(step, flat.numel() - o)
+                flat[o:o + n] = (torch.randn(n, generator=g, device="cuda") * scale).to(torch.bfloat16)
+            return out
+
+        self.w = {"w_qkv": rnd((HQ + 2 * HKV) * D, H, scale=0.02), "w_o": rnd(H, HQ * D, scale=0.02),
+                  "w_gate": rnd(F, H, scale=0.02), "w_up": rnd(F, H, scale=0.02), "w_down": rnd(H, F, scale=0.02),
+                  "g_attn": torch.ones(H, dtype=torch.bfloat16, device="cuda"),
+                  "g_ffn": torch.ones(H, dtype=torch.bfloat16, device="cuda")}
+        self.n_pages = 128 * HKV * (16384 // self.PAGE + 1) + HKV * ((16384 + 10240) // self.PAGE + 1) + 1024
+        self.pool = rnd(self.n_pages, 2, self.PAGE * D)
+        self.perm = torch.randperm(self.n_pages, generator=g, device="cuda").to(torch.int32)
+        self.x = rnd(self.MAX_ROWS, H)
+        self.q = rnd(self.MAX_ROWS, HQ * D)
+        self.out = torch.empty(self.MAX_ROWS, HQ * D, dtype=torch.bfloat16, device="cuda")
+        self.shape = X.layer_shape(hidden=H, n_q_heads=HQ, n_kv_heads=HKV, head_dim=D, ffn_dim=F)
+        self.weights = X.layer_weights(self.w)
+
+    def tables(self, dec_ctx, chunk, prior):
+        t, HKV, P = self.torch, self.HKV, self.PAGE
+        n_d = len(dec_ctx)
+        dmb = max([(c + 1 + P - 1) // P for c in dec_ctx], default=0)
+        pmb = (prior + chunk + P - 1) // P if chunk else 0
+        nd_pages = n_d * HKV * dmb
+        dec_pages = self.perm[:nd_pages].view(n_d, HKV, dmb) if n_d else None
+        pre_pages = self.perm[nd_pages:nd_pages + HKV * pmb].view(HKV, pmb) if chunk else None
+        ctx = t.tensor(dec_ctx, dtype=t.int32, device="cuda") if n_d else None
+        return ctx, dec_pages, dmb, pre_pages, pmb
+
+    def layer_step(self, dec_ctx, chunk, prior):
+        X = self.X
+        ctx_t, dec_pages, _, pre_pages, _ = self.tables(dec_ctx, chunk, prior)
+        M = chunk + len(dec_ctx)
+        desc = X.batch_desc(x=self.x[:M], n_prefill_local=chunk, n_decode=len(dec_ctx), dec_ctx=ctx_t,
+                            dec_pages=dec_pages, chunk_len=chunk, prior_len=prior, pre_pages=pre_pages)
+        return X.LayerStep(self.ctx, self.shape, desc, self.weights, self.pool, self.n_pages,
+                           keep=(ctx_t, dec_pages, pre_pages))
+
+    def decode_call(self, dec_ctx):
+        X, t = self.X, self.torch
+        ctx_t, dec_pages, dmb, _, _ = self.tables(dec_ctx, 0, 0)
+        n_d = len(dec_ctx)
+        ws = t.empty(max(256, X.xp_decode_workspace_size(n_d, self.HQ, self.HKV, self.D, dmb, 0)),
+                     dtype=t.uint8, device="cuda")
+        keep = (ctx_t, dec_pages, ws)
+        return lambda: X.xp_decode_attention(X.XP_BF16, self.q, self.pool, self.n_pages, self.PAGE, dec_pages,
+                                             dmb, ctx_t, n_d, self.HQ, self.HKV, self.D, self.out, self.HQ * self.D,
+                                             ws, 0) or keep
+
+    def prefill_call(self, chunk, prior):
+        X, t = self.X, self.torch
+        _, _, _, pre_pages, pmb = self.tables([], chunk, prior)
+        ws = t.empty(max(256, X.xp_prefill_workspace_size(self.HQ, self.HKV, self.D, prior, chunk)),
+                     dtype=t.uint8, device="cuda")
+        keep = (pre_pages, ws)
+        return lambda: X.xp_prefill_attention(X.XP_BF16, self.q, self.pool, self.n_pages, self.PAGE, pre_pages,
+                                              pmb, self.HQ, self.HKV, self.D, prior, chunk, 0, chunk, self.out,
+                                              self.HQ * self.D, None, self.HQ * self.D, ws) or keep
+
+
+def _mixed_batch(rnd):
+    """A heterogeneous batch as the pages sample them for estimator accuracy (§8.5): a
+    prefill chunk of 32-10K tokens (log-uniform) after 0-16K cached tokens, and 1-128
+    decodes with contexts of 1K-16K tokens."""
+    chunk = int(round(math.exp(rnd.uniform(math.log(32), math.log(10240)))))
+    prior = rnd.randint(0, 16384)
+    dec = [rnd.randint(1024, 16384) for _ in range(rnd.randint(1, 128))]
+    return chunk, prior, dec
+
+
+def estimator_mode(args, X, torch, timer):
+    """Fit the latency model (ConfluxServe §6.2, App. D) from isolated profiles of this
+    build's kernels, calibrate alpha and beta on heterogeneous layer steps, then report
+    its mean absolute percentage error on fresh random heterogeneous batches (§8.5)."""
+    import random
+    t0 = time.time()
+    ctx = X.Ctx(0, args.estimator_decode_cus, 0)
+    rig = EstimatorRig(X, torch, ctx)
+    log(f"[estimator] rig ready in {time.time() - t0:.1f} s: {rig.n_pages} pages, "
+        f"decode CUs {args.estimator_decode_cus}")
+    rec = {"gemm": [], "decode": [], "prefill": [], "mixed": [], "eval": []}
+    n_rep = 8
+    # shared linear region: decode-only steps of n rows with one-page contexts, minus the
+    # standalone decode attention of the same rows
+    for n in (16, 32, 48, 64, 96, 128, 192, 256, 384, 512, 768, 1024, 1536, 2048, 3072, 4096, 6144, 8192,
+              10368):
+        dec = [15] * n
+        step = rig.layer_step(dec, 0, 0)
+        t_layer = timer(step.run, n_rep)
+        t_dec = timer(rig.decode_call(dec), n_rep)
+        assert step.status() == 0
+        rec["gemm"].append((n, t_layer - t_dec))
+    log(f"[estimator] shared-linear profile: {[(n, round(t * 1e6, 1)) for n, t in rec['gemm']]}")
+    rnd = random.Random(7)
+    for _ in range(32):
+        dec = [rnd.randint(1024, 16384) for _ in range(rnd.randint(1, 128))]
+        rec["decode"].append((sum(dec), timer(rig.decode_call(dec), n_rep)))
+    for _ in range(32):
+        chunk, prior = int(round(math.exp(rnd.uniform(math.log(32), math.log(10240))))), rnd.randint(0, 16384)
+        w = chunk * prior + chunk * (chunk + 1) // 2
+        rec["prefill"].append((w, timer(rig.prefill_call(chunk, prior), n_rep)))
+    log(f"[estimator] attention profiles done ({time.time() - t0:.0f} s)")
+
+    def run_mixed(rnd, n):
+        out = []
+        for _ in range(n):
+            chunk, prior, dec = _mixed_batch(rnd)
+            step = rig.layer_step(dec, chunk, prior)
+            t = timer(step.run, n_rep)
+            assert step.status() == 0
+            out.append((chunk, prior, dec, t))
+        return out
+
+    def reduce(b):
+        chunk, prior, dec, t = b
+        return (chunk + len(dec), float(sum(dec)), float(chunk * prior + chunk * (chunk + 1) // 2), float(chunk), t)
+
+    mixed = run_mixed(random.Random(11), 60)
+    rec["mixed"] = [reduce(b) for b in mixed]
+    model = X.xp_fit_latency_model(tuple(zip(*rec["gemm"])), tuple(zip(*rec["decode"])),
+                                   tuple(zip(*rec["prefill"])), ([], []), rec["mixed"], n_layers=1, ab_max=4.0)
+    log(f"[estimator] fitted {json.dumps(model)} ({time.time() - t0:.0f} s)")
+    ev = run_mixed(random.Random(12), args.estimator_batches)
+
+    def predict(b):
+        chunk, prior, dec, _ = b
+        return X.xp_iteration_latency(model, [len(dec)], [sum(dec)], [chunk], [(chunk, prior)])
+
+    errs = [abs(predict(b) - b[3]) / b[3] for b in ev]
+    cal = [abs(predict(b) - b[3]) / b[3] for b in mixed]
+    rec["eval"] = [(b[0], b[1], len(b[2]), sum(b[2]), b[3], predict(b)) for b in ev]
+    # the fitted model fed to the dispatcher: the TBT-safe chunk for the 8B decode batch
+    # of the layer benchmark (16 decodes at 8192) under a 32-layer, 100 ms iteration
+    m32 = dict(model, n_layers=32)
+    wf = X.xp_waterfill(tau=0.100, n_decode_tokens=[16], decode_ctx_sum=[16 * 8192], candidate=(65536, 0),
+                        model=m32)
+    srt = sorted(errs)
+    res = {"estimator": {
+        "model": model, "mode": f"split attention on {args.estimator_decode_cus} decode CUs",
+        "profiles": {k: len(rec[k]) for k in ("gemm", "decode", "prefill", "mixed")},
+        "calibration_mape": round(sum(cal) / len(cal), 4), "eval_batches": len(ev),
+        "eval_mape": round(sum(errs) / len(errs), 4), "eval_p50": round(srt[len(srt) // 2], 4),
+        "eval_p90": round(srt[int(len(srt) * 0.9)], 4), "eval_max": round(srt[-1], 4),
+        "dispatch_example": {"decodes": 16, "ctx": 8192, "tau_s": 0.100, "layers": 32,
+                             "chunk_len": wf["chunk_len"], "n_target": wf["n_target"]},
+        "seconds": round(time.time() - t0, 1)}}
+    if args.estimator_out:
+        with open(args.estimator_out, "w") as f:
+            json.dump(dict(res, records=rec), f)
+    print(json.dumps(res), flush=True)
+    ctx.close()
+
+
 def scheduler_timing(X, repeats: int = 100) -> dict:
     """Host time of one SLO-aware scheduling iteration (admission, ordering, one dispatch
     per chosen chunk, decode placement) on 8 simulated ranks, at the pending-queue depths
@@ -222,6 +402,8 @@ def main():
     # streams are blocking HIP streams, which the null stream would otherwise
     # wait on at every launch.
     torch.cuda.set_stream(torch.cuda.Stream())
+    if args.estimator:
+        return estimator_mode(args, X, torch, Timer(torch))
     props = torch.cuda.get_device_properties(0)
     n_cus = props.multi_processor_count
     wl = get_workload(args.workload)

@@ -368,6 +368,45 @@ xp_status xp_iteration_latency(const xp_latency_model* model, int32_t n_ranks,
                                const int32_t* chunk_len, const int64_t* chunk_ctx, double* t_iter);
 
 /* ------------------------------------------------------------------------ */
+/* Latency-estimator fitting (host only, thread-safe)                       */
+/* ------------------------------------------------------------------------ */
+
+/* Profile samples of one base function ([CS] App. D): x is its workload metric,
+ * t the measured latency (> 0, finite). */
+typedef struct {
+  int32_t n;           /* samples (>= 0)  */
+  const double* x;     /* [n] host        */
+  const double* t;     /* [n] host        */
+} xp_samples;
+
+/* Heterogeneous iterations, each reduced to the arguments of Eq. 3-6. */
+typedef struct {
+  int32_t n;                 /* iterations (>= 0)                                           */
+  const double* gemm_x;      /* [n] max_r (n_p^r + n_d^r)                                   */
+  const double* decode_x;    /* [n] max_r sum_{i on r} c_i, or < 0 when no decode runs      */
+  const double* prefill_x;   /* [n] (1/N) sum_i l_i (c_i + (l_i + 1)/2), or < 0: no prefill */
+  const double* comm_x;      /* [n] max_r n_p^r (read only when prefill_x >= 0)            */
+  const double* t;           /* [n] measured latency of the iteration                       */
+} xp_mixed_samples;
+
+/* Affine base function t ~ slope x + intercept (Eq. 7, 8, 10, 11) fitted to the
+ * samples by least squares on the relative error, sum ((slope x + intercept)/t - 1)^2.
+ * No samples: both 0 (an unprofiled path contributes nothing).  When every x is
+ * equal only the intercept is fitted.  XP_EINVAL on null arrays or t <= 0. */
+xp_status xp_fit_affine(const xp_samples* samples, double* slope, double* intercept);
+
+/* The whole estimator ([CS] §6.2 "Estimator construction"): the four base
+ * functions from their isolated profiles (xp_fit_affine), then the contention
+ * factors alpha, beta >= 1 of Eq. 4 from the heterogeneous iterations: the pair on
+ * the grid 1 + k/64 (k = 0 .. 64 (ab_max - 1)) that minimizes
+ * sum ((L (f_GEMM + max(beta T_P, alpha T_D)))/t - 1)^2, the smaller alpha, then
+ * beta, on ties.  n_layers is L of the profiled iterations and is stored in *out.
+ * XP_EINVAL on null arrays, t <= 0, n_layers < 1 or ab_max outside [1, 16]. */
+xp_status xp_fit_latency_model(const xp_samples* gemm, const xp_samples* decode, const xp_samples* prefill,
+                               const xp_samples* comm, const xp_mixed_samples* mixed, int32_t n_layers,
+                               double ab_max, xp_latency_model* out);
+
+/* ------------------------------------------------------------------------ */
 /* SLO-aware scheduler around the dispatcher (host only, thread-safe)       */
 /* ------------------------------------------------------------------------ */
 

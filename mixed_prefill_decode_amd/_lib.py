@@ -21,7 +21,7 @@ __all__ = ["XpError", "lib", "XP_F32", "XP_BF16", "XP_EPI_F32", "XP_EPI_ADD_T", 
            "xp_decode_workspace_size", "xp_decode_attention", "xp_prefill_workspace_size", "xp_prefill_attention",
            "xp_probe_hw_ids",
            "xp_waterfill", "xp_iteration_latency", "xp_admission", "xp_decode_placement", "xp_schedule",
-           "ScheduleCall", "XP_SCHED_DONE", "XP_SCHED_BUDGET", "XP_SCHED_NO_HOST", "xp_build_info", "xp_last_error"]
+           "ScheduleCall", "xp_fit_affine", "xp_fit_latency_model", "XP_SCHED_DONE", "XP_SCHED_BUDGET", "XP_SCHED_NO_HOST", "xp_build_info", "xp_last_error"]
 
 XP_F32, XP_BF16 = 0, 1
 XP_EPI_F32, XP_EPI_ADD_T, XP_EPI_ADD_F32, XP_EPI_SWIGLU = 0, 1, 2, 3
@@ -40,7 +40,8 @@ EXPORTED = ["xp_last_error", "xp_build_info", "xp_ctx_create", "xp_ctx_destroy",
             "xp_decode_workspace_size",
             "xp_decode_attention", "xp_prefill_workspace_size", "xp_prefill_attention", "xp_probe_hw_ids",
             "xp_waterfill",
-            "xp_iteration_latency", "xp_admission", "xp_decode_placement", "xp_schedule"]
+            "xp_iteration_latency", "xp_fit_affine", "xp_fit_latency_model", "xp_admission",
+            "xp_decode_placement", "xp_schedule"]
 
 
 class XpError(RuntimeError):
@@ -99,6 +100,15 @@ class WaterfillOut(C.Structure):
                 ("assign", C.c_void_p)]
 
 
+class Samples(C.Structure):
+    _fields_ = [("n", C.c_int32), ("x", C.c_void_p), ("t", C.c_void_p)]
+
+
+class MixedSamples(C.Structure):
+    _fields_ = [("n", C.c_int32), ("gemm_x", C.c_void_p), ("decode_x", C.c_void_p), ("prefill_x", C.c_void_p),
+                ("comm_x", C.c_void_p), ("t", C.c_void_p)]
+
+
 class DecodeState(C.Structure):
     _fields_ = [("n_ranks", C.c_int32), ("n_decode_tokens", C.c_void_p), ("decode_ctx_sum", C.c_void_p),
                 ("kv_used", C.c_void_p), ("kv_capacity", C.c_void_p)]
@@ -155,6 +165,9 @@ def _declare(L):
         "xp_waterfill": (S, [C.POINTER(WaterfillIn), C.POINTER(WaterfillOut)]),
         "xp_iteration_latency": (S, [C.POINTER(LatencyModel), _i32, _vp, _vp, _vp, _i32, _vp, _vp,
                                      C.POINTER(_f64)]),
+        "xp_fit_affine": (S, [C.POINTER(Samples), C.POINTER(_f64), C.POINTER(_f64)]),
+        "xp_fit_latency_model": (S, [C.POINTER(Samples)] * 4 + [C.POINTER(MixedSamples), _i32, _f64,
+                                                                C.POINTER(LatencyModel)]),
         "xp_admission": (S, [C.POINTER(PrefillQueue), C.c_int64, _f64, _f64, _vp, C.POINTER(_i32)]),
         "xp_decode_placement": (S, [C.POINTER(DecodeState), C.c_int64, _f64, C.c_int64, C.POINTER(_i32)]),
         "xp_schedule": (S, [C.POINTER(DecodeState), C.POINTER(PrefillQueue), C.POINTER(SchedParams),
@@ -447,3 +460,31 @@ def xp_schedule(**kw) -> dict:
     """One iteration of the SLO-aware scheduler (Algorithm 1); keyword arguments as
     ScheduleCall."""
     return ScheduleCall(**kw).call().result()
+
+
+def _samples(x, t):
+    xa = np.ascontiguousarray(x, dtype=np.float64)
+    ta = np.ascontiguousarray(t, dtype=np.float64)
+    if xa.shape != ta.shape:
+        raise ValueError("x and t differ in length")
+    return Samples(len(xa), _ptr(xa), _ptr(ta)), (xa, ta)
+
+
+def xp_fit_affine(x, t) -> tuple:
+    """(slope, intercept) of t ~ slope x + intercept on relative error (App. D base functions)."""
+    s, keep = _samples(x, t)
+    a, b = _f64(), _f64()
+    _check(lib().xp_fit_affine(C.byref(s), C.byref(a), C.byref(b)))
+    return a.value, b.value
+
+
+def xp_fit_latency_model(gemm, decode, prefill, comm, mixed, n_layers=1, ab_max=3.0) -> dict:
+    """The latency model from isolated profiles ((x, t) pairs) and heterogeneous iterations
+    [(gemm_x, decode_x, prefill_x, comm_x, t)]."""
+    parts = [_samples(*p) for p in (gemm, decode, prefill, comm)]
+    cols = [np.ascontiguousarray([m[k] for m in mixed], dtype=np.float64) for k in range(5)]
+    ms = MixedSamples(len(mixed), *[_ptr(c) for c in cols])
+    out = LatencyModel()
+    _check(lib().xp_fit_latency_model(*[C.byref(p[0]) for p in parts], C.byref(ms), int(n_layers), float(ab_max),
+                                      C.byref(out)))
+    return {f: getattr(out, f) for f, _ in LatencyModel._fields_}

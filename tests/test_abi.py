@@ -299,3 +299,54 @@ def test_scheduler_rejects_bad_arguments():
     with pytest.raises(X.XpError):
         X.xp_decode_placement([0], [0], [10], -5, 0.5, 0)
     assert X.xp_decode_placement([0], [95], [100], 10, 0.5, 0) is None      # Infeasible is a result
+
+
+# ---- latency-estimator fitting ---------------------------------------------------------
+
+def _noisy_profile(rnd, a, b, lo, hi, n):
+    x = [rnd.uniform(lo, hi) for _ in range(n)]
+    return x, [(a * v + b) * rnd.uniform(0.85, 1.2) for v in x]
+
+
+def test_fit_affine_agrees_with_oracle():
+    from oracle import estimator as est
+    rnd = random.Random(31)
+    for _ in range(300):
+        n = rnd.randint(0, 40)
+        scale = 10 ** rnd.uniform(0, 9)
+        x, t = _noisy_profile(rnd, rnd.uniform(1e-12, 1e-6), rnd.uniform(1e-6, 1e-3), 1, scale, n)
+        if rnd.random() < 0.1 and n:
+            x = [x[0]] * n
+        ga, gb = X.xp_fit_affine(x, t)
+        oa, ob = est.fit_affine(x, t)
+        assert ga == pytest.approx(oa, rel=1e-8, abs=1e-300) and gb == pytest.approx(ob, rel=1e-8, abs=1e-300)
+
+
+def test_fit_latency_model_agrees_with_oracle():
+    from oracle import estimator as est
+    rnd = random.Random(32)
+    for _ in range(20):
+        gemm = _noisy_profile(rnd, 2e-7, 3e-5, 16, 10000, 20)
+        dec = _noisy_profile(rnd, 8e-10, 1e-5, 1000, 2e6, 20)
+        pre = _noisy_profile(rnd, 6e-11, 9e-6, 500, 5e7, 20)
+        comm = _noisy_profile(rnd, 1e-8, 5e-6, 16, 5000, rnd.choice([0, 10]))
+        mixed = []
+        for _ in range(rnd.randint(0, 30)):
+            g, d, p = rnd.randint(64, 10000), rnd.choice([-1.0, rnd.uniform(1e3, 2e6)]), rnd.choice([-1.0, rnd.uniform(5e2, 5e7)])
+            tg = 2e-7 * g + 3e-5
+            t = tg + max(1.4 * (6e-11 * p + 9e-6) * (p >= 0), 1.2 * (8e-10 * d + 1e-5) * (d >= 0))
+            mixed.append((g, d, p, rnd.uniform(16, 5000), t * rnd.uniform(0.9, 1.1)))
+        got = X.xp_fit_latency_model(gemm, dec, pre, comm, mixed, n_layers=1, ab_max=2.5)
+        ref = est.fit_model(gemm, dec, pre, comm, mixed, n_layers=1, ab_max=2.5)
+        for k in ("gamma", "gamma0", "a_d", "a_d0", "a_p", "a_p0", "a_comm", "a_comm0"):
+            assert got[k] == pytest.approx(ref[k], rel=1e-8, abs=1e-300), k
+        assert (got["alpha"], got["beta"], got["n_layers"]) == (ref["alpha"], ref["beta"], 1)
+
+
+def test_fit_rejects_bad_samples():
+    with pytest.raises(X.XpError):
+        X.xp_fit_affine([1.0, 2.0], [1.0, 0.0])
+    with pytest.raises(X.XpError):
+        X.xp_fit_latency_model(([], []), ([], []), ([], []), ([], []), [], n_layers=0)
+    with pytest.raises(X.XpError):
+        X.xp_fit_latency_model(([], []), ([], []), ([], []), ([], []), [(1, 1, 1, 1, -1.0)])
