@@ -35,7 +35,7 @@ from .numerics import encode, round_f64, to_f64
 
 __all__ = [
     "rmsnorm", "rope", "silu", "attend", "PagedKV", "decode_attention",
-    "prefill_attention", "layer_forward", "causal_pair_count",
+    "prefill_attention", "layer_forward", "layer_forward_chunks", "causal_pair_count",
 ]
 
 
@@ -284,6 +284,72 @@ def layer_forward(*, hidden, n_q_heads, n_kv_heads, head_dim, ffn_dim, page_size
         out[rows] = h1[rows] + act[rows] @ W["w_down"].T
     return dict(out=out, h1=h1, act=act, attn=attn, q=q, k=k, v=v, q_pre=q_pre, positions=pos,
                 peer_qkv_out=peer_qkv_out, peer_attn_out=peer_attn_out, kv=kv, rows=rows)
+
+
+def layer_forward_chunks(*, hidden, n_q_heads, n_kv_heads, head_dim, ffn_dim, page_size, rms_eps, rope_base,
+                         dtype, x, weights, dec_ctx, dec_pages, chunks, pool, rows=None) -> dict:
+    """One layer step whose prefill side is a set of chunks (ConfluxServe §6.2 Eq. 6 and §6.4:
+    the scheduled prefills P are several requests' chunks), sp_degree 1.
+
+    ``chunks`` is a list of (chunk_len, prior_len, table[Hkv, blocks]); rows are ordered
+    [chunk 0 || chunk 1 || ... || decode].  Chunk j's row t is at position prior_j + t, its
+    K/V go to every kv head through its own table, and it attends keys 0..prior_j + t of
+    its own request.  Everything else is the step of ``layer_forward``.
+    """
+    H, Hq, Hkv, d = hidden, n_q_heads, n_kv_heads, head_dim
+    G = Hq // Hkv
+    n_d = len(dec_ctx)
+    starts = np.cumsum([0] + [l for l, _, _ in chunks])
+    n_pre = int(starts[-1])
+    M = n_pre + n_d
+    W = {k: to_f64(v, dtype) for k, v in weights.items()}
+    x64 = to_f64(x, dtype).reshape(M, H)
+    kv = PagedKV(pool, dtype, page_size, d)
+
+    # co-batched norm + QKV over every row
+    hn = rmsnorm(x64, W["g_attn"], rms_eps)
+    qkv = hn @ W["w_qkv"].T
+    q = qkv[:, :Hq * d].reshape(M, Hq, d)
+    k = qkv[:, Hq * d:(Hq + Hkv) * d].reshape(M, Hkv, d)
+    v = qkv[:, (Hq + Hkv) * d:].reshape(M, Hkv, d)
+
+    # RoPE at absolute positions, then the appends
+    pos = np.concatenate([c + np.arange(l) for l, c, _ in chunks] + [np.asarray(dec_ctx, dtype=np.int64)])
+    q = rope(q, pos, rope_base)
+    k = rope(k, pos, rope_base)
+    for i in range(n_d):
+        for g in range(Hkv):
+            kv.write(dec_pages[i, g], int(dec_ctx[i]), k[n_pre + i, g], v[n_pre + i, g])
+    for j, (l, c, table) in enumerate(chunks):
+        for t in range(l):
+            for g in range(Hkv):
+                kv.write(table[g], c + t, k[starts[j] + t, g], v[starts[j] + t, g])
+
+    # split attention: decodes, then each chunk over its own request's keys
+    rows = np.arange(M) if rows is None else np.asarray(sorted(set(int(i) for i in rows)), dtype=np.int64)
+    attn = np.full((M, Hq * d), np.nan)
+    dec_req = [int(i) - n_pre for i in rows if i >= n_pre]
+    o_dec = decode_attention(q[n_pre:], kv, dec_pages, dec_ctx, Hkv, requests=dec_req)
+    for i in dec_req:
+        attn[n_pre + i] = o_dec[i].reshape(-1)
+    for j, (l, c, table) in enumerate(chunks):
+        sel = [int(i) - int(starts[j]) for i in rows if starts[j] <= i < starts[j + 1]]
+        if not sel:
+            continue
+        o = prefill_attention(q[starts[j]:starts[j + 1]], kv, table, c, G, rows=sel)
+        for t in sel:
+            attn[starts[j] + t] = o[t].reshape(-1)
+
+    # co-batched O-proj, FFN and residuals on the requested rows
+    h1 = np.full((M, H), np.nan)
+    act = np.full((M, ffn_dim), np.nan)
+    out = np.full((M, H), np.nan)
+    if len(rows):
+        h1[rows] = x64[rows] + attn[rows] @ W["w_o"].T
+        hn2 = rmsnorm(h1[rows], W["g_ffn"], rms_eps)
+        act[rows] = silu(hn2 @ W["w_gate"].T) * (hn2 @ W["w_up"].T)
+        out[rows] = h1[rows] + act[rows] @ W["w_down"].T
+    return dict(out=out, h1=h1, act=act, attn=attn, q=q, k=k, v=v, positions=pos, kv=kv, rows=rows)
 
 
 def _peer_index(t: int, off: int, n_pl: int) -> int:

@@ -36,6 +36,7 @@ __all__ = [
     "WORKLOADS", "PARITY_WORKLOADS", "get_workload", "make_instance",
     "f32_to_bf16_bits", "bf16_bits_to_f32", "storage_to_f64",
     "waterfill_cases", "make_latency_model", "SchedulerCase", "scheduler_case",
+    "MultiChunkWorkload", "MultiChunkInstance", "make_multi_instance", "MULTI_CHUNK_WORKLOADS",
 ]
 
 TENSOR_IDS = {
@@ -493,3 +494,123 @@ def scheduler_case(depth: int, n_ranks: int = 8, seed: int = 0, kv_capacity: int
                          make_latency_model(gamma=2.0 ** -21, gamma0=2.0 ** -15, a_d=2.0 ** -30, a_d0=2.0 ** -16,
                                             a_p=2.0 ** -34, a_p0=2.0 ** -16, a_comm=2.0 ** -24,
                                             a_comm0=2.0 ** -16, n_layers=32))
+
+
+# ---------------------------------------------------------------------------
+# Multi-chunk steps: several prefill requests in one step (sp_degree 1).
+# ---------------------------------------------------------------------------
+
+@dataclass
+class MultiChunkWorkload:
+    """A layer step whose prefill side is a list of chunks [(chunk_len, prior_len)], each
+    a different request with its own cached context, plus a decode population."""
+    name: str
+    seed_id: int
+    dtype: str
+    hidden: int
+    n_q_heads: int
+    n_kv_heads: int
+    head_dim: int
+    ffn_dim: int
+    n_decode: int
+    ctx: tuple
+    chunks: list
+    page_size: int = 16
+    rms_eps: float = 1e-5
+    rope_base: float = 10000.0
+    weight_std: float = 0.02
+    description: str = ""
+
+    @property
+    def n_prefill_rows(self) -> int:
+        return sum(l for l, _ in self.chunks)
+
+    @property
+    def n_rows(self) -> int:
+        return self.n_prefill_rows + self.n_decode
+
+    @property
+    def qkv_dim(self) -> int:
+        return (self.n_q_heads + 2 * self.n_kv_heads) * self.head_dim
+
+
+@dataclass
+class MultiChunkInstance:
+    wl: MultiChunkWorkload
+    x: np.ndarray
+    weights: dict
+    dec_ctx: np.ndarray
+    dec_pages: np.ndarray
+    chunk_pages: list              # per chunk: [Hkv, blocks] int32
+    pool: PagePool
+
+
+def make_multi_instance(wl: MultiChunkWorkload) -> MultiChunkInstance:
+    """Inputs of a multi-chunk step: rows [chunk 0 || chunk 1 || ... || decode].  Every
+    chunk's table covers its prior context and the chunk on all kv heads; slots that hold
+    no cached token (including the ones the step appends to) are NaN."""
+    S, d, H = wl.page_size, wl.head_dim, wl.hidden
+    Hq, Hkv, F = wl.n_q_heads, wl.n_kv_heads, wl.ffn_dim
+    k, dt = wl.seed_id, wl.dtype
+    x = _normal(k, "x", (wl.n_rows, H), 1.0, dt)
+    ws = wl.weight_std
+    weights = {
+        "w_qkv": _normal(k, "w_qkv", (wl.qkv_dim, H), ws, dt),
+        "w_o": _normal(k, "w_o", (H, Hq * d), ws, dt),
+        "w_gate": _normal(k, "w_gate", (F, H), ws, dt),
+        "w_up": _normal(k, "w_up", (F, H), ws, dt),
+        "w_down": _normal(k, "w_down", (H, F), ws, dt),
+    }
+    one = f32_to_bf16_bits(np.ones(H, np.float32)) if dt == "bf16" else np.ones(H, np.float32)
+    weights["g_attn"] = one.copy()
+    weights["g_ffn"] = one.copy()
+    ctx = _draw_ctx(wl)
+    nb_dec = [_cdiv(int(c) + 1, S) for c in ctx]
+    nb_ch = [_cdiv(c + l, S) for l, c in wl.chunks]
+    n_pages = (sum(nb_dec) + sum(nb_ch)) * Hkv
+    perm = _rng(k, "page_perm").permutation(n_pages).astype(np.int32)
+    dec_pages = np.full((wl.n_decode, Hkv, max(max(nb_dec, default=1), 1)), -1, dtype=np.int32)
+    valid = np.full(n_pages, S, dtype=np.int32)
+    it = 0
+    for i, c in enumerate(ctx):
+        for g in range(Hkv):
+            for b in range(nb_dec[i]):
+                p = int(perm[it]); it += 1
+                dec_pages[i, g, b] = p
+                valid[p] = min(max(int(c) - b * S, 0), S)
+    chunk_pages = []
+    for (l, c), nb in zip(wl.chunks, nb_ch):
+        t = np.full((Hkv, nb), -1, dtype=np.int32)
+        for g in range(Hkv):
+            for b in range(nb):
+                p = int(perm[it]); it += 1
+                t[g, b] = p
+                valid[p] = min(max(c - b * S, 0), S)
+        chunk_pages.append(t)
+    arr = _draw_pages(k, "kv", n_pages, (2, S * d), dt)
+    pool = PagePool(n_pages, (2, S * d), dt, valid, S, d, array=arr)
+    ids = pool.poisoned_pages()
+    if len(ids):
+        arr[ids] = pool._poison(arr[ids].copy(), ids)
+    return MultiChunkInstance(wl, x, weights, ctx, dec_pages, chunk_pages, pool)
+
+
+MULTI_CHUNK_WORKLOADS = {
+    # four requests' chunks in one step, bf16, ragged lengths, one starting at position 0
+    "M1": MultiChunkWorkload("M1", 121, "bf16", 512, 8, 2, 128, 1024, n_decode=5, ctx=("uniform", 0, 600),
+                             chunks=[(97, 0), (64, 130), (33, 17), (150, 400)],
+                             description="small bf16 layer, 4 chunks + 5 decodes"),
+    # fp32, with a one-token chunk and no decode shorter than a page
+    "M2": MultiChunkWorkload("M2", 122, "f32", 256, 4, 2, 64, 512, n_decode=3, ctx=("uniform", 20, 90),
+                             chunks=[(20, 5), (1, 0), (40, 100)],
+                             description="tiny fp32 layer, 3 chunks incl. a 1-token chunk"),
+    # prefill only: three chunks, no decode
+    "M3": MultiChunkWorkload("M3", 123, "bf16", 512, 8, 2, 128, 1024, n_decode=0, ctx=("fixed", 0),
+                             chunks=[(70, 33), (16, 0), (129, 250)],
+                             description="small bf16 layer, 3 chunks, no decode"),
+    # the 8B step of the layer benchmark with its 1024 prefill rows from four requests
+    "C2x4": MultiChunkWorkload("C2x4", 24, "bf16", 4096, 32, 8, 128, 14336, n_decode=16, ctx=("fixed", 8192),
+                               chunks=[(256, 0), (256, 2048), (256, 4096), (256, 8192)],
+                               description="Llama-3.1-8B layer: 16 decodes at 8192 + four 256-token chunks "
+                                           "after 0/2048/4096/8192 cached tokens"),
+}

@@ -31,3 +31,15 @@ class ArrayPool:
 
     def __getitem__(self, ids):
         return self.array[np.asarray(ids, dtype=np.int64)]
+
+
+def chunk_oracle_kwargs(inst, **extra):
+    """Keyword arguments of ``oracle.layer.layer_forward_chunks`` for a multi-chunk instance."""
+    wl = inst.wl
+    kw = dict(hidden=wl.hidden, n_q_heads=wl.n_q_heads, n_kv_heads=wl.n_kv_heads,
+              head_dim=wl.head_dim, ffn_dim=wl.ffn_dim, page_size=wl.page_size,
+              rms_eps=wl.rms_eps, rope_base=wl.rope_base, dtype=wl.dtype, x=inst.x,
+              weights=inst.weights, dec_ctx=inst.dec_ctx, dec_pages=inst.dec_pages,
+              chunks=[(l, c, t) for (l, c), t in zip(wl.chunks, inst.chunk_pages)], pool=inst.pool)
+    kw.update(extra)
+    return kw
