@@ -239,6 +239,59 @@ def _mixed_batch(rnd):
     return chunk, prior, dec
 
 
+def multi_chunk_mode(args, X, torch, timer):
+    """Several prefill requests in one step (xp_layer_forward_chunks): the step time in
+    serialized split attention, and each chunk's prefill attention standalone."""
+    from synth import MULTI_CHUNK_WORKLOADS, make_multi_instance
+    from synth.device import make_chunked_step
+    wl = MULTI_CHUNK_WORKLOADS[args.workload]
+    t0 = time.time()
+    inst = make_multi_instance(wl)
+    ctx = X.Ctx(0, 0, 0)
+    step = make_chunked_step(inst, ctx)
+    log(f"[bench] {wl.name}: {wl.description}; rows {wl.n_rows}; inputs ready in {time.time() - t0:.1f} s")
+    t_warm = time.perf_counter()
+    while time.perf_counter() - t_warm < 0.2:
+        step.run()
+        torch.cuda.synchronize()
+    for _ in range(args.warmup):
+        step.run()
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t1 = time.perf_counter()
+    ev0.record()
+    for _ in range(args.steps):
+        step.run()
+    ev1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t1
+    ms = ev0.elapsed_time(ev1) / args.steps
+    assert step.status() == 0
+    lay = step.layout
+    ws = int(step.workspace.data_ptr())
+    hq, d = wl.n_q_heads, wl.head_dim
+    out = torch.empty((max(l for l, _ in wl.chunks), hq * d), dtype=torch.bfloat16, device="cuda")
+    pre, q_off = [], 0
+    for (l, c), t in zip(wl.chunks, step.tables):
+        pws = torch.empty(max(256, X.xp_prefill_workspace_size(hq, wl.n_kv_heads, d, c, l)), dtype=torch.uint8,
+                          device="cuda")
+        tt = timer(lambda: X.xp_prefill_attention(X.XP_BF16, ws + lay.q_pre + q_off, step.pool, inst.pool.n_pages,
+                                                  wl.page_size, t, int(t.shape[1]), hq, wl.n_kv_heads, d, c, l, 0, l,
+                                                  out, hq * d, None, hq * d, pws), args.repeats)
+        fl = 4 * d * hq * (l * c + l * (l + 1) // 2)
+        pre.append({"chunk": l, "prior": c, "us": round(tt * 1e6, 2), "TFLOPs": round(fl / tt / 1e12, 1)})
+        q_off += l * hq * d * 2
+    line = {"metric": METRIC, "value": round(wl.n_rows * args.steps / wall, 1), "unit": "tokens/s", "n_gpus": 1,
+            "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True,
+            "scaling": "weak", "vs_baseline": None, "dtype": wl.dtype, "data": "synthetic (seeded, random-init weights)",
+            "config": {"workload": f"{wl.name}: {wl.description}", "rows": wl.n_rows, "chunks": wl.chunks,
+                       "decodes": wl.n_decode, "split_attention": "serialized"},
+            "kernels": {"prefill_attn_chunks": pre}}
+    log(f"[bench] layer {ms * 1e3:.1f} us/step; prefill chunks {json.dumps(pre)}")
+    print(json.dumps(line), flush=True)
+    ctx.close()
+
+
 def estimator_mode(args, X, torch, timer):
     """Fit the latency model (ConfluxServe §6.2, App. D) from isolated profiles of this
     build's kernels, calibrate alpha and beta on heterogeneous layer steps, then report
@@ -404,6 +457,9 @@ def main():
     torch.cuda.set_stream(torch.cuda.Stream())
     if args.estimator:
         return estimator_mode(args, X, torch, Timer(torch))
+    from synth import MULTI_CHUNK_WORKLOADS
+    if args.workload in MULTI_CHUNK_WORKLOADS:
+        return multi_chunk_mode(args, X, torch, Timer(torch))
     props = torch.cuda.get_device_properties(0)
     n_cus = props.multi_processor_count
     wl = get_workload(args.workload)

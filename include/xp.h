@@ -209,6 +209,34 @@ xp_status xp_layer_forward(xp_ctx* ctx, const xp_layer_shape* shape, const xp_ba
                            const xp_layer_weights* weights, const xp_kv_pages* kv, float* out,
                            void* workspace, size_t workspace_bytes, void* stream);
 
+/* One prefill chunk of a multi-chunk step ([CS] §6.2 Eq. 6 and §6.4: the
+ * scheduled prefills P are a set of chunks, each with its own cached context). */
+typedef struct {
+  int32_t chunk_len;           /* l_j >= 1 tokens at positions prior_len .. prior_len + l_j - 1 */
+  int32_t prior_len;           /* c_j >= 0 tokens of that request already cached               */
+  const int32_t* pre_pages;    /* device [Hkv, pre_max_blocks]: the request's table            */
+  int32_t pre_max_blocks;      /* >= ceil((prior_len + chunk_len) / page_size)                */
+} xp_chunk;
+
+/* Workspace layout of xp_layer_forward_chunks (same fields; q_pre holds the
+ * chunks' [Hq, l_j, d] query blocks one after another). */
+xp_status xp_layer_workspace_layout_chunks(const xp_ctx* ctx, const xp_layer_shape* shape,
+                                           const xp_batch_desc* desc, int32_t n_chunks,
+                                           const xp_chunk* chunks, xp_ws_layout* layout);
+
+/* xp_layer_forward over several prefill chunks at once, sp_degree 1: rows are
+ * [chunk 0 || chunk 1 || ... || decode] (M = sum l_j + n_decode).  `desc`
+ * supplies x, the decodes and sp_degree = 1 with chunk_len = n_prefill_local
+ * = 0; chunk j's rows are rotated at positions c_j + t, appended to every KV
+ * head through its own table, and attend causally over its own c_j + t + 1
+ * keys.  The chunks' prefill attention runs one after another on the prefill
+ * side of the split region; everything else is one co-batched launch per
+ * operator, as in xp_layer_forward.  XP_EUNSUPPORTED for sp_degree > 1. */
+xp_status xp_layer_forward_chunks(xp_ctx* ctx, const xp_layer_shape* shape, const xp_batch_desc* desc,
+                                  int32_t n_chunks, const xp_chunk* chunks, const xp_layer_weights* weights,
+                                  const xp_kv_pages* kv, float* out, void* workspace, size_t workspace_bytes,
+                                  void* stream);
+
 /* Host-side check of a descriptor against host copies of its tables:
  * every table entry a step will touch lies in [0, n_pages) and no page is
  * named twice.  Returns XP_EPAGE / XP_ESHAPE on failure. */

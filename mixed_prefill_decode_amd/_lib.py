@@ -14,8 +14,9 @@ import numpy as np
 
 __all__ = ["XpError", "lib", "XP_F32", "XP_BF16", "XP_EPI_F32", "XP_EPI_ADD_T", "XP_EPI_ADD_F32",
            "XP_EPI_SWIGLU", "XP_DEV_BAD_PAGE", "LayerShape", "LayerWeights", "KvPages", "BatchDesc",
-           "WsLayout", "LatencyModel", "Ctx", "EXPORTED",
+           "WsLayout", "LatencyModel", "Ctx", "EXPORTED", "Chunk", "chunk_array",
            "xp_ctx_create", "xp_layer_workspace_layout", "xp_layer_forward", "xp_validate_batch",
+           "xp_layer_workspace_layout_chunks", "xp_layer_forward_chunks",
            "xp_layer_read_status", "xp_rmsnorm", "xp_gemm_workspace_size", "xp_gemm_tile", "xp_gemm", "xp_kv_append",
            "xp_kv_gather",
            "xp_decode_workspace_size", "xp_decode_attention", "xp_prefill_workspace_size", "xp_prefill_attention",
@@ -36,6 +37,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libxp.so")
 EXPORTED = ["xp_last_error", "xp_build_info", "xp_ctx_create", "xp_ctx_destroy", "xp_ctx_cu_masks",
             "xp_ctx_streams",
             "xp_layer_workspace_layout", "xp_layer_forward", "xp_validate_batch", "xp_layer_read_status",
+            "xp_layer_workspace_layout_chunks", "xp_layer_forward_chunks",
             "xp_rmsnorm", "xp_gemm_workspace_size", "xp_gemm_tile", "xp_gemm", "xp_kv_append", "xp_kv_gather",
             "xp_decode_workspace_size",
             "xp_decode_attention", "xp_prefill_workspace_size", "xp_prefill_attention", "xp_probe_hw_ids",
@@ -71,6 +73,11 @@ class BatchDesc(C.Structure):
                 ("sp_rank", C.c_int32), ("local_row_offset", C.c_int32), ("pre_pages", C.c_void_p),
                 ("pre_max_blocks", C.c_int32), ("peer_qkv_in", C.c_void_p), ("peer_qkv_out", C.c_void_p),
                 ("peer_attn_in", C.c_void_p), ("peer_attn_out", C.c_void_p)]
+
+
+class Chunk(C.Structure):
+    _fields_ = [("chunk_len", C.c_int32), ("prior_len", C.c_int32), ("pre_pages", C.c_void_p),
+                ("pre_max_blocks", C.c_int32)]
 
 
 class WsLayout(C.Structure):
@@ -147,6 +154,10 @@ def _declare(L):
         "xp_layer_workspace_layout": (S, [_vp, C.POINTER(LayerShape), C.POINTER(BatchDesc), C.POINTER(WsLayout)]),
         "xp_layer_forward": (S, [_vp, C.POINTER(LayerShape), C.POINTER(BatchDesc), C.POINTER(LayerWeights),
                                  C.POINTER(KvPages), _vp, _vp, _sz, _vp]),
+        "xp_layer_workspace_layout_chunks": (S, [_vp, C.POINTER(LayerShape), C.POINTER(BatchDesc), _i32,
+                                                 C.POINTER(Chunk), C.POINTER(WsLayout)]),
+        "xp_layer_forward_chunks": (S, [_vp, C.POINTER(LayerShape), C.POINTER(BatchDesc), _i32, C.POINTER(Chunk),
+                                        C.POINTER(LayerWeights), C.POINTER(KvPages), _vp, _vp, _sz, _vp]),
         "xp_validate_batch": (S, [C.POINTER(LayerShape), C.POINTER(BatchDesc), _i32, _vp, _vp, _vp]),
         "xp_layer_read_status": (S, [_vp, C.POINTER(WsLayout), _vp, _vp]),
         "xp_rmsnorm": (S, [_i32, _vp, _i32, _vp, _vp, _i32, _i32, _f32, _vp]),
@@ -272,6 +283,28 @@ def xp_layer_workspace_layout(ctx, shape: LayerShape, desc: BatchDesc) -> WsLayo
 def xp_layer_forward(ctx, shape, desc, weights, kv, out, workspace, workspace_bytes, stream=None):
     _check(lib().xp_layer_forward(ctx.handle, C.byref(shape), C.byref(desc), C.byref(weights), C.byref(kv),
                                   _ptr(out), _ptr(workspace), workspace_bytes, _stream(stream)))
+
+
+def xp_layer_workspace_layout_chunks(ctx, shape, desc, chunks) -> WsLayout:
+    """``chunks``: a ctypes array of Chunk (see chunk_array)."""
+    out = WsLayout()
+    _check(lib().xp_layer_workspace_layout_chunks(ctx.handle if ctx is not None else None, C.byref(shape),
+                                                  C.byref(desc), len(chunks), chunks, C.byref(out)))
+    return out
+
+
+def xp_layer_forward_chunks(ctx, shape, desc, chunks, weights, kv, out, workspace, workspace_bytes, stream=None):
+    _check(lib().xp_layer_forward_chunks(ctx.handle, C.byref(shape), C.byref(desc), len(chunks), chunks,
+                                         C.byref(weights), C.byref(kv), _ptr(out), _ptr(workspace), workspace_bytes,
+                                         _stream(stream)))
+
+
+def chunk_array(chunks):
+    """ctypes array of Chunk from [(chunk_len, prior_len, table tensor [Hkv, blocks])]."""
+    arr = (Chunk * max(1, len(chunks)))()
+    for j, (l, c, t) in enumerate(chunks):
+        arr[j] = Chunk(int(l), int(c), _ptr(t), int(t.shape[-1]))
+    return arr if chunks else (Chunk * 0)()
 
 
 def xp_validate_batch(shape, desc, n_pages, dec_ctx_host, dec_pages_host, pre_pages_host):

@@ -13,6 +13,7 @@
 
 #include <algorithm>
 #include <string>
+#include <vector>
 
 #include "xp_internal.h"
 
@@ -139,12 +140,19 @@ xp_status check_desc(const xp_layer_shape* sh, const xp_batch_desc* d) {
 // concurrent and partitioned steps give bit-identical results)
 int prefill_cus(const xp_ctx* ctx) { return ctx ? ctx->n_cus : device_cus(); }
 
-xp_ws_layout make_layout(const xp_ctx* ctx, const xp_layer_shape* sh, const xp_batch_desc* d) {
+// Prefill side of a step's workspace: the rotated chunk queries and the key-split
+// partials, for one chunk (the descriptor's) or a list of chunks run one after another.
+struct PrefillNeed {
+  size_t q_bytes = 0;     // [Hq/P, rows, d] T per chunk, chunks back to back
+  size_t part_bytes = 0;  // the largest chunk's partials (chunks share them in turn)
+};
+
+xp_ws_layout make_layout_core(const xp_ctx* ctx, const xp_layer_shape* sh, const xp_batch_desc* d, size_t M,
+                              const PrefillNeed& pn) {
   xp_ws_layout L;
   memset(&L, 0, sizeof(L));
   const size_t eb = dtype_bytes(sh->dtype);
-  const size_t M = rows_of(d), H = sh->hidden, F = sh->ffn_dim, Hq = sh->n_q_heads, Hkv = sh->n_kv_heads,
-               D = sh->head_dim;
+  const size_t H = sh->hidden, F = sh->ffn_dim, Hq = sh->n_q_heads, Hkv = sh->n_kv_heads, D = sh->head_dim;
   const int pps = decode_pick_pps(ctx ? ctx->pps : 0, d->n_decode, int(Hkv), d->dec_max_blocks);
   const int splits = d->n_decode > 0 ? decode_splits(d->dec_max_blocks, pps) : 0;
   size_t off = 0;
@@ -157,13 +165,12 @@ xp_ws_layout make_layout(const xp_ctx* ctx, const xp_layer_shape* sh, const xp_b
   L.hn = take(M * H * eb);
   L.qkv = take(M * (Hq + 2 * Hkv) * D * 4);
   L.q_dec = take(size_t(d->n_decode) * Hq * D * eb);
-  L.q_pre = take(size_t(Hq / d->sp_degree) * d->chunk_len * D * eb);
+  L.q_pre = take(pn.q_bytes);
   L.attn = take(M * Hq * D * eb);
   const size_t units = size_t(d->n_decode) * Hq * splits;
   L.dec_ml = take(units * 2 * sizeof(float));
   L.dec_o = take(units * D * sizeof(float));
-  L.pre_part = take(prefill_ws_bytes(int(Hq) / d->sp_degree, int(Hkv) / d->sp_degree, int(D), d->prior_len,
-                                     d->chunk_len, prefill_cus(ctx)));
+  L.pre_part = take(pn.part_bytes);
   {
     const int dt = sh->dtype;
     const size_t g = std::max(std::max(gemm_ws_bytes(dt, XP_EPI_F32, int(M), int((Hq + 2 * Hkv) * D), int(H)),
@@ -178,6 +185,52 @@ xp_ws_layout make_layout(const xp_ctx* ctx, const xp_layer_shape* sh, const xp_b
   L.dec_splits = splits;
   L.dec_pages_per_split = pps;
   return L;
+}
+
+xp_ws_layout make_layout(const xp_ctx* ctx, const xp_layer_shape* sh, const xp_batch_desc* d) {
+  const size_t eb = dtype_bytes(sh->dtype), Hq = sh->n_q_heads, Hkv = sh->n_kv_heads, D = sh->head_dim;
+  PrefillNeed pn;
+  pn.q_bytes = size_t(Hq / d->sp_degree) * d->chunk_len * D * eb;
+  pn.part_bytes = prefill_ws_bytes(int(Hq) / d->sp_degree, int(Hkv) / d->sp_degree, int(D), d->prior_len,
+                                   d->chunk_len, prefill_cus(ctx));
+  return make_layout_core(ctx, sh, d, size_t(rows_of(d)), pn);
+}
+
+// A multi-chunk step: the descriptor carries x, the decodes and sp_degree 1 with no
+// chunk of its own; the chunks' rows come first in x, in list order.
+xp_status check_chunks(const xp_layer_shape* sh, const xp_batch_desc* d, int n_chunks, const xp_chunk* ch) {
+  if (d->sp_degree != 1) return fail(XP_EUNSUPPORTED, "multi-chunk steps need sp_degree 1");
+  if (d->chunk_len != 0 || d->n_prefill_local != 0)
+    return fail(XP_ESHAPE, "multi-chunk steps take their chunks from the list (descriptor chunk_len %d)",
+                d->chunk_len);
+  if (n_chunks < 0 || (n_chunks > 0 && !ch)) return fail(XP_EINVAL, "chunk list");
+  long rows = d->n_decode;
+  for (int j = 0; j < n_chunks; ++j) {
+    const xp_chunk& c = ch[j];
+    if (c.chunk_len < 1 || c.prior_len < 0) return fail(XP_ESHAPE, "chunk %d: length %d, prior %d", j, c.chunk_len, c.prior_len);
+    if (!c.pre_pages) return fail(XP_EINVAL, "chunk %d: null table", j);
+    if (long(c.pre_max_blocks) * sh->page_size < long(c.prior_len) + c.chunk_len)
+      return fail(XP_EPAGE, "chunk %d: table of %d blocks cannot hold %d positions", j, c.pre_max_blocks,
+                  c.prior_len + c.chunk_len);
+    rows += c.chunk_len;
+  }
+  if (rows > INT32_MAX / 2) return fail(XP_ESHAPE, "too many rows");
+  if (rows > 0 && !d->x) return fail(XP_EINVAL, "null x");
+  return XP_OK;
+}
+
+xp_ws_layout make_layout_chunks(const xp_ctx* ctx, const xp_layer_shape* sh, const xp_batch_desc* d, int n_chunks,
+                                const xp_chunk* ch) {
+  const size_t eb = dtype_bytes(sh->dtype), Hq = sh->n_q_heads, Hkv = sh->n_kv_heads, D = sh->head_dim;
+  PrefillNeed pn;
+  size_t rows = 0;
+  for (int j = 0; j < n_chunks; ++j) {
+    rows += size_t(ch[j].chunk_len);
+    pn.part_bytes = std::max(pn.part_bytes, prefill_ws_bytes(int(Hq), int(Hkv), int(D), ch[j].prior_len,
+                                                             ch[j].chunk_len, prefill_cus(ctx)));
+  }
+  pn.q_bytes = Hq * rows * D * eb;
+  return make_layout_core(ctx, sh, d, rows + size_t(d->n_decode), pn);
 }
 
 }  // namespace
@@ -310,27 +363,44 @@ xp_status xp_layer_read_status(const void* ws, const xp_ws_layout* L, uint32_t* 
   return XP_OK;
 }
 
-xp_status xp_layer_forward(xp_ctx* ctx, const xp_layer_shape* sh, const xp_batch_desc* d, const xp_layer_weights* w,
-                           const xp_kv_pages* kv, float* out, void* workspace, size_t workspace_bytes, void* stream) {
-  if (!ctx) return fail(XP_EINVAL, "null ctx");
-  xp_status st = check_shape(sh);
-  if (st) return st;
-  if ((st = check_desc(sh, d))) return st;
+}  // extern "C"
+
+namespace {
+
+// One prefill chunk as the step runs it: chunk rows [off, off + n_local) are the
+// rank's local rows [row0, row0 + n_local) of x; its rotated queries sit q_off bytes
+// into the workspace's q region.
+struct ChunkRun {
+  int len, prior, off, n_local, row0;
+  const int32_t* pages;
+  int max_blocks;
+  const void* peer_qkv_in;
+  void* peer_qkv_out;
+  const void* peer_attn_in;
+  void* peer_attn_out;
+  size_t q_off;
+};
+
+xp_status check_weights(const xp_layer_weights* w, const xp_kv_pages* kv) {
   if (!w || !w->w_qkv || !w->w_o || !w->w_gate || !w->w_up || !w->w_down || !w->g_attn || !w->g_ffn)
     return fail(XP_EINVAL, "null weight");
   if (!kv || !kv->pool || kv->n_pages <= 0) return fail(XP_EINVAL, "null or empty KV pool");
-  const int M = rows_of(d);
-  if (M > 0 && !out) return fail(XP_EINVAL, "null out");
-  const xp_ws_layout L = make_layout(ctx, sh, d);
-  if (!workspace || workspace_bytes < L.total)
-    return fail(XP_EWORKSPACE, "workspace of %zu bytes < %zu required", workspace_bytes, L.total);
+  return XP_OK;
+}
 
-  hipStream_t s = static_cast<hipStream_t>(stream);
+// The step of ConfluxServe §4 (Fig. 7) over rows [chunk rows of every chunk || decode]:
+// co-batched RMSNorm + QKV, RoPE and appends, the split attention region (every chunk's
+// prefill attention in turn on the prefill side), co-batched O projection and FFN.
+xp_status run_layer(xp_ctx* ctx, const xp_layer_shape* sh, const xp_batch_desc* d, const std::vector<ChunkRun>& ch,
+                    int rows_pre, const xp_layer_weights* w, const xp_kv_pages* kv, float* out,
+                    const xp_ws_layout& L, void* workspace, hipStream_t s) {
+  xp_status st;
   const int dt = sh->dtype;
   const size_t eb = dtype_bytes(dt);
   const int H = sh->hidden, Hq = sh->n_q_heads, Hkv = sh->n_kv_heads, D = sh->head_dim, F = sh->ffn_dim;
   const int P = d->sp_degree, r = d->sp_rank, hq_loc = Hq / P, hkv_loc = Hkv / P;
-  const int n_pl = d->n_prefill_local, n_d = d->n_decode;
+  const int n_d = d->n_decode, M = rows_pre + n_d;
+  const int ldq = (Hq + 2 * Hkv) * D;
   char* ws = static_cast<char*>(workspace);
   uint32_t* status = reinterpret_cast<uint32_t*>(ws + L.status);
   char* hn = ws + L.hn;
@@ -340,32 +410,48 @@ xp_status xp_layer_forward(xp_ctx* ctx, const xp_layer_shape* sh, const xp_batch
   char* act = ws + L.act;
   void* gp = ws + L.gemm_part;                  // GEMM K-split partials
   const size_t gpb = L.h1 - L.gemm_part;
+  const size_t attn_row = size_t(Hq) * D * eb;
 
   // shared linear region (1): RMSNorm + QKV over all M rows
   if ((st = launch_rmsnorm(dt, d->x, 0, w->g_attn, hn, M, H, sh->rms_eps, status, s))) return st;
-  if (M > 0 && (st = launch_gemm(dt, XP_EPI_F32, hn, w->w_qkv, nullptr, nullptr, qkv, M, (Hq + 2 * Hkv) * D, H, gp, gpb, s)))
+  if (M > 0 && (st = launch_gemm(dt, XP_EPI_F32, hn, w->w_qkv, nullptr, nullptr, qkv, M, ldq, H, gp, gpb, s)))
     return st;
-  // RoPE + appends (+ the peer stand-ins)
-  PostQkvArgs pa{qkv, n_pl, n_d, Hq, Hkv, D, sh->page_size, sh->rope_base, d->dec_ctx, d->dec_pages,
-                 d->dec_max_blocks, d->prior_len, d->chunk_len, P, r, d->local_row_offset, d->pre_pages,
-                 d->pre_max_blocks, d->peer_qkv_in, d->peer_qkv_out, d->peer_attn_in, kv->pool, kv->n_pages,
-                 ws + L.q_dec, ws + L.q_pre, attn, status};
-  if ((st = launch_post_qkv(dt, pa, s))) return st;
+  // RoPE + appends (+ the peer stand-ins): one launch per chunk, the decodes with the last
+  // (their rows follow it in x) or alone when there is no chunk
+  auto post = [&](const ChunkRun* c, int nd) {
+    const int row0 = c ? c->row0 : rows_pre;
+    PostQkvArgs pa{qkv + size_t(row0) * ldq, c ? c->n_local : 0, nd, Hq, Hkv, D, sh->page_size, sh->rope_base,
+                   d->dec_ctx, d->dec_pages, d->dec_max_blocks, c ? c->prior : 0, c ? c->len : 0, P, r,
+                   c ? c->off : 0, c ? c->pages : nullptr, c ? c->max_blocks : 0, c ? c->peer_qkv_in : nullptr,
+                   c ? c->peer_qkv_out : nullptr, c ? c->peer_attn_in : nullptr, kv->pool, kv->n_pages,
+                   ws + L.q_dec, c ? ws + L.q_pre + c->q_off : nullptr, attn + size_t(row0) * attn_row, status};
+    return launch_post_qkv(dt, pa, s);
+  };
+  if (ch.empty()) {
+    if ((st = post(nullptr, n_d))) return st;
+  } else {
+    for (size_t j = 0; j < ch.size(); ++j)
+      if ((st = post(&ch[j], j + 1 == ch.size() ? n_d : 0))) return st;
+  }
 
   // split attention region
   auto decode = [&](hipStream_t q) {
     return launch_decode(dt, ws + L.q_dec, kv->pool, kv->n_pages, sh->page_size, d->dec_pages, d->dec_max_blocks,
-                         d->dec_ctx, n_d, Hq, Hkv, D, attn + size_t(n_pl) * Hq * D * eb, Hq * D,
+                         d->dec_ctx, n_d, Hq, Hkv, D, attn + size_t(rows_pre) * attn_row, Hq * D,
                          reinterpret_cast<float*>(ws + L.dec_ml), reinterpret_cast<float*>(ws + L.dec_o), L.dec_pages_per_split,
                          status, q);
   };
   auto prefill = [&](hipStream_t q) {
-    return launch_prefill(dt, ws + L.q_pre, kv->pool, kv->n_pages, sh->page_size, d->pre_pages, d->pre_max_blocks,
-                          hq_loc, hkv_loc, D, d->prior_len, d->chunk_len, d->local_row_offset, n_pl,
-                          attn + size_t(r) * hq_loc * D * eb, Hq * D, d->peer_attn_out, hq_loc * D,
-                          ws + L.pre_part, status, prefill_cus(ctx), q);
+    for (const ChunkRun& c : ch) {
+      xp_status e = launch_prefill(dt, ws + L.q_pre + c.q_off, kv->pool, kv->n_pages, sh->page_size, c.pages,
+                                   c.max_blocks, hq_loc, hkv_loc, D, c.prior, c.len, c.off, c.n_local,
+                                   attn + size_t(c.row0) * attn_row + size_t(r) * hq_loc * D * eb, Hq * D,
+                                   c.peer_attn_out, hq_loc * D, ws + L.pre_part, status, prefill_cus(ctx), q);
+      if (e) return e;
+    }
+    return xp_status(XP_OK);
   };
-  const bool concurrent = ctx->s_dec && n_d > 0 && d->chunk_len > 0;
+  const bool concurrent = ctx->s_dec && n_d > 0 && !ch.empty();
   if (!concurrent) {
     if ((st = decode(s))) return st;
     if ((st = prefill(s))) return st;
@@ -388,6 +474,65 @@ xp_status xp_layer_forward(xp_ctx* ctx, const xp_layer_shape* sh, const xp_batch
   if ((st = launch_gemm(dt, XP_EPI_SWIGLU, hn, w->w_gate, w->w_up, nullptr, act, M, F, H, gp, gpb, s))) return st;
   if ((st = launch_gemm(dt, XP_EPI_ADD_F32, act, w->w_down, nullptr, h1, out, M, H, F, gp, gpb, s))) return st;
   return XP_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+xp_status xp_layer_forward(xp_ctx* ctx, const xp_layer_shape* sh, const xp_batch_desc* d, const xp_layer_weights* w,
+                           const xp_kv_pages* kv, float* out, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!ctx) return fail(XP_EINVAL, "null ctx");
+  xp_status st = check_shape(sh);
+  if (st) return st;
+  if ((st = check_desc(sh, d))) return st;
+  if ((st = check_weights(w, kv))) return st;
+  const int M = rows_of(d);
+  if (M > 0 && !out) return fail(XP_EINVAL, "null out");
+  const xp_ws_layout L = make_layout(ctx, sh, d);
+  if (!workspace || workspace_bytes < L.total)
+    return fail(XP_EWORKSPACE, "workspace of %zu bytes < %zu required", workspace_bytes, L.total);
+  std::vector<ChunkRun> ch;
+  if (d->chunk_len > 0)
+    ch.push_back(ChunkRun{d->chunk_len, d->prior_len, d->local_row_offset, d->n_prefill_local, 0, d->pre_pages,
+                          d->pre_max_blocks, d->peer_qkv_in, d->peer_qkv_out, d->peer_attn_in, d->peer_attn_out, 0});
+  return run_layer(ctx, sh, d, ch, d->n_prefill_local, w, kv, out, L, workspace, static_cast<hipStream_t>(stream));
+}
+
+xp_status xp_layer_workspace_layout_chunks(const xp_ctx* ctx, const xp_layer_shape* sh, const xp_batch_desc* d,
+                                           int32_t n_chunks, const xp_chunk* chunks, xp_ws_layout* out) {
+  if (!out) return fail(XP_EINVAL, "null layout out");
+  xp_status st = check_shape(sh);
+  if (st) return st;
+  if ((st = check_desc(sh, d)) || (st = check_chunks(sh, d, n_chunks, chunks))) return st;
+  *out = make_layout_chunks(ctx, sh, d, n_chunks, chunks);
+  return XP_OK;
+}
+
+xp_status xp_layer_forward_chunks(xp_ctx* ctx, const xp_layer_shape* sh, const xp_batch_desc* d, int32_t n_chunks,
+                                  const xp_chunk* chunks, const xp_layer_weights* w, const xp_kv_pages* kv, float* out,
+                                  void* workspace, size_t workspace_bytes, void* stream) {
+  if (!ctx) return fail(XP_EINVAL, "null ctx");
+  xp_status st = check_shape(sh);
+  if (st) return st;
+  if ((st = check_desc(sh, d)) || (st = check_chunks(sh, d, n_chunks, chunks))) return st;
+  if ((st = check_weights(w, kv))) return st;
+  const xp_ws_layout L = make_layout_chunks(ctx, sh, d, n_chunks, chunks);
+  if (!workspace || workspace_bytes < L.total)
+    return fail(XP_EWORKSPACE, "workspace of %zu bytes < %zu required", workspace_bytes, L.total);
+  std::vector<ChunkRun> ch;
+  int rows = 0;
+  size_t q_off = 0;
+  const size_t q_row = size_t(sh->n_q_heads) * sh->head_dim * dtype_bytes(sh->dtype);
+  for (int j = 0; j < n_chunks; ++j) {
+    const xp_chunk& c = chunks[j];
+    ch.push_back(ChunkRun{c.chunk_len, c.prior_len, 0, c.chunk_len, rows, c.pre_pages, c.pre_max_blocks, nullptr,
+                          nullptr, nullptr, nullptr, q_off});
+    rows += c.chunk_len;
+    q_off += size_t(c.chunk_len) * q_row;
+  }
+  if (rows + d->n_decode > 0 && !out) return fail(XP_EINVAL, "null out");
+  return run_layer(ctx, sh, d, ch, rows, w, kv, out, L, workspace, static_cast<hipStream_t>(stream));
 }
 
 // ---- kernel-level entry points ------------------------------------------------

@@ -8,7 +8,7 @@ from __future__ import annotations
 
 from . import _lib as X
 
-__all__ = ["layer_shape", "layer_weights", "batch_desc", "LayerStep"]
+__all__ = ["layer_shape", "layer_weights", "batch_desc", "LayerStep", "ChunkedStep"]
 
 
 def layer_shape(*, hidden, n_q_heads, n_kv_heads, head_dim, ffn_dim, page_size=16, rms_eps=1e-5,
@@ -64,3 +64,29 @@ class LayerStep:
             n *= s
         nbytes = n * torch.empty((), dtype=dtype).element_size()
         return self.workspace[off:off + nbytes].view(dtype).view(*shape)
+
+
+class ChunkedStep:
+    """A multi-chunk batch (xp_layer_forward_chunks): rows [chunk 0 || ... || decode],
+    ``chunks`` = [(chunk_len, prior_len, table tensor [Hkv, blocks])], sp_degree 1."""
+
+    def __init__(self, ctx: X.Ctx, shape: X.LayerShape, desc: X.BatchDesc, chunks, weights: X.LayerWeights,
+                 pool, n_pages: int, keep=()):
+        import torch
+        self.ctx, self.shape, self.desc, self.weights = ctx, shape, desc, weights
+        self.chunks = X.chunk_array(chunks)
+        self.kv = X.KvPages(X._ptr(pool), n_pages)
+        self.layout = X.xp_layer_workspace_layout_chunks(ctx, shape, desc, self.chunks)
+        dev = torch.device("cuda", ctx.device)
+        self.workspace = torch.empty(self.layout.total, dtype=torch.uint8, device=dev)
+        M = sum(int(l) for l, _, _ in chunks) + desc.n_decode
+        self.out = torch.empty((M, shape.hidden), dtype=torch.float32, device=dev)
+        self._keep = (pool,) + tuple(t for _, _, t in chunks) + tuple(keep)
+
+    def run(self, stream=None):
+        X.xp_layer_forward_chunks(self.ctx, self.shape, self.desc, self.chunks, self.weights, self.kv, self.out,
+                                  self.workspace, self.layout.total, stream)
+        return self.out
+
+    def status(self, stream=None) -> int:
+        return X.xp_layer_read_status(self.workspace, self.layout, stream)

@@ -11,7 +11,7 @@ import torch
 
 from .workloads import Instance
 
-__all__ = ["to_device", "upload_pool", "DeviceInstance", "upload"]
+__all__ = ["to_device", "upload_pool", "DeviceInstance", "upload", "make_step", "make_chunked_step"]
 
 
 def to_device(a: np.ndarray, dtype: str, device="cuda") -> torch.Tensor:
@@ -94,3 +94,25 @@ def make_step(inst: Instance, ctx, dev: DeviceInstance | None = None):
     step = LayerStep(ctx, shape, desc, layer_weights(dev.weights), dev.pool, inst.pool.n_pages,
                      keep=(dev,))
     return step, dev
+
+
+def make_chunked_step(inst, ctx):
+    """A ChunkedStep of the package for a multi-chunk instance (device copies only)."""
+    from mixed_prefill_decode_amd import ChunkedStep, batch_desc, layer_shape, layer_weights
+    wl, dt = inst.wl, inst.wl.dtype
+    x = to_device(inst.x, dt)
+    weights = {k: to_device(v, dt) for k, v in inst.weights.items()}
+    dec_ctx = to_device(inst.dec_ctx, "i32")
+    dec_pages = to_device(inst.dec_pages, "i32")
+    tables = [to_device(t, "i32") for t in inst.chunk_pages]
+    pool = to_device(inst.pool.array, dt)
+    shape = layer_shape(hidden=wl.hidden, n_q_heads=wl.n_q_heads, n_kv_heads=wl.n_kv_heads,
+                        head_dim=wl.head_dim, ffn_dim=wl.ffn_dim, page_size=wl.page_size, rms_eps=wl.rms_eps,
+                        rope_base=wl.rope_base, dtype=dt)
+    desc = batch_desc(x=x, n_prefill_local=0, n_decode=wl.n_decode, dec_ctx=dec_ctx,
+                      dec_pages=dec_pages if wl.n_decode else None, chunk_len=0, prior_len=0)
+    chunks = [(l, c, t) for (l, c), t in zip(wl.chunks, tables)]
+    step = ChunkedStep(ctx, shape, desc, chunks, layer_weights(weights), pool, inst.pool.n_pages,
+                       keep=(x, weights, dec_ctx, dec_pages))
+    step.pool, step.x, step.tables, step.dec_ctx, step.dec_pages = pool, x, tables, dec_ctx, dec_pages
+    return step

@@ -350,3 +350,38 @@ def test_fit_rejects_bad_samples():
         X.xp_fit_latency_model(([], []), ([], []), ([], []), ([], []), [], n_layers=0)
     with pytest.raises(X.XpError):
         X.xp_fit_latency_model(([], []), ([], []), ([], []), ([], []), [(1, 1, 1, 1, -1.0)])
+
+
+def test_chunk_list_layout_is_host_only_and_validated():
+    shape = X.layer_shape(hidden=512, n_q_heads=8, n_kv_heads=2, head_dim=128, ffn_dim=1024)
+    x = np.zeros((300, 512), dtype=np.uint16)
+    t1, t2 = np.zeros((2, 7), dtype=np.int32), np.zeros((2, 30), dtype=np.int32)
+
+    class T:  # table stand-in: only the address and the block count reach the library
+        def __init__(self, a):
+            self.a, self.shape = a, a.shape
+
+        def data_ptr(self):
+            return self.a.ctypes.data
+
+        def dim(self):
+            return self.a.ndim
+
+    desc = X.batch_desc(x=x.ctypes.data, n_prefill_local=0, n_decode=0, dec_ctx=None, dec_pages=None,
+                        chunk_len=0, prior_len=0)
+    ok = X.chunk_array([(97, 0, T(t1)), (203, 270, T(t2))])
+    L = X.xp_layer_workspace_layout_chunks(None, shape, desc, ok)
+    L1 = X.xp_layer_workspace_layout(None, shape, X.batch_desc(x=x.ctypes.data, n_prefill_local=300, n_decode=0,
+                                                               dec_ctx=None, dec_pages=None, chunk_len=300,
+                                                               prior_len=0, pre_pages=T(t2)))
+    assert L.q_pre == L1.q_pre and L.attn - L.q_pre == L1.attn - L1.q_pre     # same rows, same query bytes
+    with pytest.raises(X.XpError) as e:                                      # 270 + 203 > 30 blocks * 16
+        X.xp_layer_workspace_layout_chunks(None, shape, desc, X.chunk_array([(203, 280, T(t2))]))
+    assert e.value.status == -3
+    sp2 = X.batch_desc(x=x.ctypes.data, n_prefill_local=0, n_decode=0, dec_ctx=None, dec_pages=None, chunk_len=0,
+                       prior_len=0, sp_degree=2)
+    with pytest.raises(X.XpError) as e:
+        X.xp_layer_workspace_layout_chunks(None, shape, sp2, ok)
+    assert e.value.status == -5
+    with pytest.raises(X.XpError):
+        X.xp_layer_workspace_layout_chunks(None, shape, desc, X.chunk_array([(0, 0, T(t1))]))
