@@ -224,10 +224,10 @@ xp_ws_layout make_layout_chunks(const xp_ctx* ctx, const xp_layer_shape* sh, con
   const size_t eb = dtype_bytes(sh->dtype), Hq = sh->n_q_heads, Hkv = sh->n_kv_heads, D = sh->head_dim;
   PrefillNeed pn;
   size_t rows = 0;
-  for (int j = 0; j < n_chunks; ++j) {
+  for (int j = 0; j < n_chunks; ++j) {  // one launch runs them all: each chunk keeps its own partials
     rows += size_t(ch[j].chunk_len);
-    pn.part_bytes = std::max(pn.part_bytes, prefill_ws_bytes(int(Hq), int(Hkv), int(D), ch[j].prior_len,
-                                                             ch[j].chunk_len, prefill_cus(ctx)));
+    pn.part_bytes += align_up(prefill_ws_bytes(int(Hq), int(Hkv), int(D), ch[j].prior_len, ch[j].chunk_len,
+                                               prefill_cus(ctx)), 256);
   }
   pn.q_bytes = Hq * rows * D * eb;
   return make_layout_core(ctx, sh, d, rows + size_t(d->n_decode), pn);
@@ -442,14 +442,24 @@ xp_status run_layer(xp_ctx* ctx, const xp_layer_shape* sh, const xp_batch_desc* 
                          status, q);
   };
   auto prefill = [&](hipStream_t q) {
-    for (const ChunkRun& c : ch) {
-      xp_status e = launch_prefill(dt, ws + L.q_pre + c.q_off, kv->pool, kv->n_pages, sh->page_size, c.pages,
-                                   c.max_blocks, hq_loc, hkv_loc, D, c.prior, c.len, c.off, c.n_local,
-                                   attn + size_t(c.row0) * attn_row + size_t(r) * hq_loc * D * eb, Hq * D,
-                                   c.peer_attn_out, hq_loc * D, ws + L.pre_part, status, prefill_cus(ctx), q);
-      if (e) return e;
+    if (ch.size() == 1) {
+      const ChunkRun& c = ch[0];
+      return launch_prefill(dt, ws + L.q_pre + c.q_off, kv->pool, kv->n_pages, sh->page_size, c.pages, c.max_blocks,
+                            hq_loc, hkv_loc, D, c.prior, c.len, c.off, c.n_local,
+                            attn + size_t(c.row0) * attn_row + size_t(r) * hq_loc * D * eb, Hq * D, c.peer_attn_out,
+                            hq_loc * D, ws + L.pre_part, status, prefill_cus(ctx), q);
     }
-    return xp_status(XP_OK);
+    // several chunks: one grouped launch, each chunk with its own partials
+    std::vector<PrefillJob> jobs;
+    size_t part = 0;
+    for (const ChunkRun& c : ch) {
+      jobs.push_back(PrefillJob{ws + L.q_pre + c.q_off, c.pages, c.max_blocks, c.prior, c.len, c.off, c.n_local,
+                                attn + size_t(c.row0) * attn_row + size_t(r) * hq_loc * D * eb, Hq * D,
+                                c.peer_attn_out, hq_loc * D, ws + L.pre_part + part});
+      part += align_up(prefill_ws_bytes(hq_loc, hkv_loc, D, c.prior, c.len, prefill_cus(ctx)), 256);
+    }
+    return launch_prefill_group(dt, kv->pool, kv->n_pages, sh->page_size, hq_loc, hkv_loc, D, int(jobs.size()),
+                                jobs.data(), status, prefill_cus(ctx), q);
   };
   const bool concurrent = ctx->s_dec && n_d > 0 && !ch.empty();
   if (!concurrent) {

@@ -32,6 +32,10 @@
 // same slots of the second page -- exactly the k-slots the PV step's P operand
 // supplies, and the V^T operand is then 8 consecutive slots of one dim row.
 #include "gemm_core.h"
+#include <algorithm>
+#include <type_traits>
+#include <vector>
+
 #include "xp_device.h"
 #include "xp_internal.h"
 
@@ -189,7 +193,7 @@ __device__ __forceinline__ void out_row(const PrefillArgs& a, int t, void*& dst,
 }
 
 template <typename T, int D, int NQ, int MAXW>
-__global__ __launch_bounds__(64 * MAXW) void prefill_kernel(PrefillArgs a) {
+__device__ __forceinline__ void prefill_tile(const PrefillArgs& a, int bx, int by) {
   constexpr int EB = St<T>::bytes;
   constexpr int QT = 32 * NQ;                     // queries per tile
   constexpr int PLANE = kPage * D * EB;           // bytes of one K or V plane of a page
@@ -214,11 +218,11 @@ __global__ __launch_bounds__(64 * MAXW) void prefill_kernel(PrefillArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int G = a.hq / a.hkv;
   const int n_qt = (a.chunk + QT - 1) / QT;
-  const int qt = n_qt - 1 - int(blockIdx.x) / a.n_split;   // longest tiles first
-  const int s = int(blockIdx.x) % a.n_split;
+  const int qt = n_qt - 1 - bx / a.n_split;   // longest tiles first
+  const int s = bx % a.n_split;
   const int groups_per_kv = (G + a.wpg - 1) / a.wpg;
-  const int g = int(blockIdx.y) / groups_per_kv;
-  const int h0 = g * G + (int(blockIdx.y) % groups_per_kv) * a.wpg;   // first query head of this workgroup
+  const int g = by / groups_per_kv;
+  const int h0 = g * G + (by % groups_per_kv) * a.wpg;   // first query head of this workgroup
   const int waves = min(a.wpg, g * G + G - h0);
   const int t0 = qt * QT;
   const int q_last = min(t0 + QT - 1, a.chunk - 1);
@@ -453,10 +457,9 @@ constexpr int kMaxSplits = 64;
 constexpr int kMaxQT = 64;          // queries per tile, at most
 
 template <typename T, int D>
-__global__ __launch_bounds__(256) void prefill_combine_kernel(PrefillArgs a) {
+__device__ __forceinline__ void prefill_combine_tile(const PrefillArgs& a, int qt, int h) {
   __shared__ float wts[kMaxSplits][kMaxQT];
   const int QT = a.qt_rows;
-  const int qt = blockIdx.x, h = blockIdx.y;
   const int q_last = min(qt * QT + QT - 1, a.chunk - 1);
   const int nkb = (a.prior + q_last + 1 + 31) / 32;
   const int ns = (nkb + a.bps - 1) / a.bps;
@@ -498,6 +501,63 @@ __global__ __launch_bounds__(256) void prefill_combine_kernel(PrefillArgs a) {
     St<T>::store(dst, o + 2, acc.z);
     St<T>::store(dst, o + 3, acc.w);
   }
+}
+
+template <typename T, int D, int NQ, int MAXW>
+__global__ __launch_bounds__(64 * MAXW) void prefill_kernel(PrefillArgs a) {
+  prefill_tile<T, D, NQ, MAXW>(a, int(blockIdx.x), int(blockIdx.y));
+}
+
+template <typename T, int D>
+__global__ __launch_bounds__(256) void prefill_combine_kernel(PrefillArgs a) {
+  prefill_combine_tile<T, D>(a, int(blockIdx.x), int(blockIdx.y));
+}
+
+// Several chunks' prefill attention in one launch (the scheduled prefills of one
+// step, ConfluxServe §6.2 Eq. 6): member j owns the flat workgroups [start[j],
+// start[j + 1]) and lays them out as its own grid of width gx[j]; its combine owns
+// [cstart[j], cstart[j + 1]) with width cgx[j].  A small chunk alone leaves most CUs
+// idle; in one launch the chunks' tiles share the device.
+constexpr int kMaxGroup = 8;
+struct PrefillGroup {
+  int n;
+  int start[kMaxGroup + 1], gx[kMaxGroup];
+  int cstart[kMaxGroup + 1], cgx[kMaxGroup];
+  PrefillArgs a[kMaxGroup];
+};
+
+// Member of flat workgroup b (uniform): every read of the kernel arguments uses a
+// constant index, so they stay scalar loads of the argument segment.
+__device__ __forceinline__ void group_member(const PrefillGroup& g, int b, bool combine, PrefillArgs& a, int& x,
+                                             int& y) {
+  int j = 0;
+#pragma unroll
+  for (int k = 1; k < kMaxGroup; ++k) j += (k < g.n && b >= (combine ? g.cstart[k] : g.start[k])) ? 1 : 0;
+  int s0 = 0, w = 1;
+  switch (j) {
+#define XP_MEMBER(k) \
+  case k: a = g.a[k]; s0 = combine ? g.cstart[k] : g.start[k]; w = combine ? g.cgx[k] : g.gx[k]; break;
+    XP_MEMBER(0) XP_MEMBER(1) XP_MEMBER(2) XP_MEMBER(3) XP_MEMBER(4) XP_MEMBER(5) XP_MEMBER(6) XP_MEMBER(7)
+#undef XP_MEMBER
+  }
+  x = (b - s0) % w;
+  y = (b - s0) / w;
+}
+
+template <typename T, int D, int NQ, int MAXW>
+__global__ __launch_bounds__(64 * MAXW) void prefill_group_kernel(PrefillGroup g) {
+  PrefillArgs a;
+  int x, y;
+  group_member(g, int(blockIdx.x), false, a, x, y);
+  prefill_tile<T, D, NQ, MAXW>(a, x, y);
+}
+
+template <typename T, int D>
+__global__ __launch_bounds__(256) void prefill_group_combine_kernel(PrefillGroup g) {
+  PrefillArgs a;
+  int x, y;
+  group_member(g, int(blockIdx.x), true, a, x, y);
+  prefill_combine_tile<T, D>(a, x, y);
 }
 
 struct Plan {
@@ -578,56 +638,120 @@ size_t prefill_ws_bytes(int hq, int hkv, int d, int prior, int chunk, int cus) {
   return align_up(units * 2 * sizeof(float), 256) + align_up(units * d * sizeof(float), 256);
 }
 
+namespace {
+
+// One chunk's launch: host checks, its key-split plan, kernel arguments and grids.
+struct Prepared {
+  PrefillArgs a;
+  Plan p;
+  int n_qt, gy;
+};
+
+xp_status prepare(const void* pool, int n_pages, int S, int hq, int hkv, int d, const PrefillJob& j, uint32_t* status,
+                  int cus, Prepared& out) {
+  if (S != kPage) return fail(XP_EUNSUPPORTED, "prefill attention: page_size %d (supported: 16)", S);
+  if (hkv <= 0 || hq % hkv) return fail(XP_ESHAPE, "prefill attention: hq=%d hkv=%d", hq, hkv);
+  if (d != 64 && d != 128) return fail(XP_EUNSUPPORTED, "prefill attention: head_dim %d", d);
+  if (long(j.pre_max_blocks) * kPage < long(j.prior) + j.chunk)
+    return fail(XP_EPAGE, "prefill attention: table of %d blocks < %d keys", j.pre_max_blocks, j.prior + j.chunk);
+  if (j.off < 0 || j.n_local < 0 || j.off + j.n_local > j.chunk) return fail(XP_ESHAPE, "prefill attention: off/n_local");
+  if ((long(j.prior) + j.chunk + 31) / 32 > long(kMaxBps) * kMaxSplits)
+    return fail(XP_EUNSUPPORTED, "prefill attention: %d keys exceed %d", j.prior + j.chunk, 32 * kMaxBps * kMaxSplits);
+  const Plan p = plan(hq, hkv, d, j.prior, j.chunk, cus);
+  const size_t need = prefill_ws_bytes(hq, hkv, d, j.prior, j.chunk, cus);
+  if (need && !j.ws) return fail(XP_EWORKSPACE, "prefill attention: needs %zu bytes of workspace", need);
+  const size_t units = size_t((j.chunk + p.qt - 1) / p.qt) * hq * p.n_split * p.qt;
+  float* ml = static_cast<float*>(j.ws);
+  float* po = j.ws ? reinterpret_cast<float*>(static_cast<char*>(j.ws) + align_up(units * 2 * sizeof(float), 256)) : nullptr;
+  out.a = PrefillArgs{j.q, static_cast<const char*>(pool), n_pages, j.pre_pages, j.pre_max_blocks, hq, hkv, j.prior,
+                      j.chunk, j.off, j.n_local, j.out_local, j.out_local_stride, j.out_peer, j.out_peer_stride,
+                      float(1.4426950408889634 / __builtin_sqrt(double(d))), status, p.bps, p.n_split, p.wpg, p.qt,
+                      ml, po};
+  out.p = p;
+  out.n_qt = (j.chunk + p.qt - 1) / p.qt;
+  const int G = hq / hkv;
+  out.gy = hkv * ((G + p.wpg - 1) / p.wpg);
+  return XP_OK;
+}
+
+template <typename T, int D>
+void launch_one(const Prepared& pr, hipStream_t s) {
+  const dim3 grid(pr.n_qt * pr.p.n_split, pr.gy), block(64 * pr.p.wpg), cgrid(pr.n_qt, pr.a.hq);
+  hipLaunchKernelGGL((prefill_kernel<T, D, XP_PREFILL_NQ, XP_PREFILL_MAXW>), grid, block, 0, s, pr.a);
+  if (pr.p.n_split > 1) hipLaunchKernelGGL((prefill_combine_kernel<T, D>), cgrid, dim3(256), 0, s, pr.a);
+}
+
+template <typename T, int D>
+void launch_group(const Prepared* pr, int n, hipStream_t s) {
+  PrefillGroup g{};
+  g.n = n;
+  bool split = false;
+  for (int k = 0; k < n; ++k) {
+    g.a[k] = pr[k].a;
+    g.gx[k] = pr[k].n_qt * pr[k].p.n_split;
+    g.start[k + 1] = g.start[k] + g.gx[k] * pr[k].gy;
+    const bool sk = pr[k].p.n_split > 1;
+    split = split || sk;
+    g.cgx[k] = pr[k].n_qt;
+    g.cstart[k + 1] = g.cstart[k] + (sk ? pr[k].n_qt * pr[k].a.hq : 0);
+  }
+  hipLaunchKernelGGL((prefill_group_kernel<T, D, XP_PREFILL_NQ, XP_PREFILL_MAXW>), dim3(g.start[n]),
+                     dim3(64 * pr[0].p.wpg), 0, s, g);
+  if (split) hipLaunchKernelGGL((prefill_group_combine_kernel<T, D>), dim3(g.cstart[n]), dim3(256), 0, s, g);
+}
+
+template <typename F>
+xp_status dispatch(int dtype, int d, F&& f) {
+  if (dtype == XP_BF16) {
+    if (d == 128) f(bf16_t{}, std::integral_constant<int, 128>{});
+    else f(bf16_t{}, std::integral_constant<int, 64>{});
+  } else if (dtype == XP_F32) {
+    if (d == 128) f(float{}, std::integral_constant<int, 128>{});
+    else f(float{}, std::integral_constant<int, 64>{});
+  } else {
+    return fail(XP_EINVAL, "prefill attention: dtype %d", dtype);
+  }
+  XP_CHECK_LAUNCH();
+  return XP_OK;
+}
+
+}  // namespace
+
 xp_status launch_prefill(int dtype, const void* q, const void* pool, int n_pages, int S, const int32_t* pre_pages,
                          int pre_max_blocks, int hq, int hkv, int d, int prior, int chunk, int off, int n_local,
                          void* out_local, int out_local_stride, void* out_peer, int out_peer_stride, void* ws,
                          uint32_t* status, int cus, hipStream_t s) {
   if (chunk == 0) return XP_OK;
-  if (S != kPage) return fail(XP_EUNSUPPORTED, "prefill attention: page_size %d (supported: 16)", S);
-  if (hkv <= 0 || hq % hkv) return fail(XP_ESHAPE, "prefill attention: hq=%d hkv=%d", hq, hkv);
-  if (long(pre_max_blocks) * kPage < long(prior) + chunk)
-    return fail(XP_EPAGE, "prefill attention: table of %d blocks < %d keys", pre_max_blocks, prior + chunk);
-  if (off < 0 || n_local < 0 || off + n_local > chunk) return fail(XP_ESHAPE, "prefill attention: off/n_local");
-  if ((long(prior) + chunk + 31) / 32 > long(kMaxBps) * kMaxSplits)
-    return fail(XP_EUNSUPPORTED, "prefill attention: %d keys exceed %d", prior + chunk, 32 * kMaxBps * kMaxSplits);
-  const Plan p = plan(hq, hkv, d, prior, chunk, cus);
-  const size_t need = prefill_ws_bytes(hq, hkv, d, prior, chunk, cus);
-  if (need && !ws) return fail(XP_EWORKSPACE, "prefill attention: needs %zu bytes of workspace", need);
-  const size_t units = size_t((chunk + p.qt - 1) / p.qt) * hq * p.n_split * p.qt;
-  float* ml = static_cast<float*>(ws);
-  float* po = ws ? reinterpret_cast<float*>(static_cast<char*>(ws) + align_up(units * 2 * sizeof(float), 256)) : nullptr;
-  PrefillArgs a{q, static_cast<const char*>(pool), n_pages, pre_pages, pre_max_blocks, hq, hkv, prior, chunk, off,
-                n_local, out_local, out_local_stride, out_peer, out_peer_stride,
-                float(1.4426950408889634 / __builtin_sqrt(double(d))), status, p.bps, p.n_split, p.wpg, p.qt, ml, po};
-  const int n_qt = (chunk + p.qt - 1) / p.qt;
-  const int G = hq / hkv;
-  const dim3 grid(n_qt * p.n_split, hkv * ((G + p.wpg - 1) / p.wpg));
-  const dim3 block(64 * p.wpg);
-  const dim3 cgrid(n_qt, hq);
-  if (dtype == XP_BF16) {
-    if (d == 128) {
-      hipLaunchKernelGGL((prefill_kernel<bf16_t, 128, XP_PREFILL_NQ, XP_PREFILL_MAXW>), grid, block, 0, s, a);
-      if (p.n_split > 1) hipLaunchKernelGGL((prefill_combine_kernel<bf16_t, 128>), cgrid, dim3(256), 0, s, a);
-    } else if (d == 64) {
-      hipLaunchKernelGGL((prefill_kernel<bf16_t, 64, XP_PREFILL_NQ, XP_PREFILL_MAXW>), grid, block, 0, s, a);
-      if (p.n_split > 1) hipLaunchKernelGGL((prefill_combine_kernel<bf16_t, 64>), cgrid, dim3(256), 0, s, a);
-    } else {
-      return fail(XP_EUNSUPPORTED, "prefill attention: head_dim %d", d);
-    }
-  } else if (dtype == XP_F32) {
-    if (d == 128) {
-      hipLaunchKernelGGL((prefill_kernel<float, 128, XP_PREFILL_NQ, XP_PREFILL_MAXW>), grid, block, 0, s, a);
-      if (p.n_split > 1) hipLaunchKernelGGL((prefill_combine_kernel<float, 128>), cgrid, dim3(256), 0, s, a);
-    } else if (d == 64) {
-      hipLaunchKernelGGL((prefill_kernel<float, 64, XP_PREFILL_NQ, XP_PREFILL_MAXW>), grid, block, 0, s, a);
-      if (p.n_split > 1) hipLaunchKernelGGL((prefill_combine_kernel<float, 64>), cgrid, dim3(256), 0, s, a);
-    } else {
-      return fail(XP_EUNSUPPORTED, "prefill attention: head_dim %d", d);
-    }
-  } else {
-    return fail(XP_EINVAL, "prefill attention: dtype %d", dtype);
+  const PrefillJob j{q, pre_pages, pre_max_blocks, prior, chunk, off, n_local, out_local, out_local_stride, out_peer,
+                     out_peer_stride, ws};
+  Prepared pr;
+  xp_status st = prepare(pool, n_pages, S, hq, hkv, d, j, status, cus, pr);
+  if (st) return st;
+  return dispatch(dtype, d, [&](auto t, auto dd) { launch_one<decltype(t), decltype(dd)::value>(pr, s); });
+}
+
+xp_status launch_prefill_group(int dtype, const void* pool, int n_pages, int S, int hq, int hkv, int d, int n,
+                               const PrefillJob* jobs, uint32_t* status, int cus, hipStream_t s) {
+  std::vector<Prepared> pr;
+  for (int k = 0; k < n; ++k) {
+    if (jobs[k].chunk == 0) continue;
+    Prepared one;
+    xp_status st = prepare(pool, n_pages, S, hq, hkv, d, jobs[k], status, cus, one);
+    if (st) return st;
+    pr.push_back(one);
   }
-  XP_CHECK_LAUNCH();
+  // the longest key ranges first, so their tiles start before the short ones
+  std::stable_sort(pr.begin(), pr.end(), [](const Prepared& x, const Prepared& y) {
+    return x.a.prior + x.a.chunk > y.a.prior + y.a.chunk;
+  });
+  for (size_t k0 = 0; k0 < pr.size(); k0 += kMaxGroup) {
+    const int m = int(std::min<size_t>(kMaxGroup, pr.size() - k0));
+    xp_status st = m == 1 ? dispatch(dtype, d, [&](auto t, auto dd) { launch_one<decltype(t), decltype(dd)::value>(pr[k0], s); })
+                          : dispatch(dtype, d, [&](auto t, auto dd) {
+                              launch_group<decltype(t), decltype(dd)::value>(pr.data() + k0, m, s);
+                            });
+    if (st) return st;
+  }
   return XP_OK;
 }
 

@@ -79,6 +79,21 @@ xp_status launch_decode(int dtype, const void* q, const void* pool, int n_pages,
                         float* part_o, int pages_per_split, uint32_t* status, hipStream_t s);
 
 size_t prefill_ws_bytes(int hq, int hkv, int d, int prior, int chunk, int cus);
+// one chunk of a grouped prefill launch; ws holds its own partials (prefill_ws_bytes)
+struct PrefillJob {
+  const void* q;
+  const int32_t* pre_pages;
+  int pre_max_blocks;
+  int prior, chunk, off, n_local;
+  void* out_local;
+  int out_local_stride;
+  void* out_peer;
+  int out_peer_stride;
+  void* ws;
+};
+// Every job's prefill attention, up to eight chunks per launch, longest key range first.
+xp_status launch_prefill_group(int dtype, const void* pool, int n_pages, int S, int hq, int hkv, int d, int n,
+                               const PrefillJob* jobs, uint32_t* status, int cus, hipStream_t s);
 xp_status launch_prefill(int dtype, const void* q, const void* pool, int n_pages, int S,
                          const int32_t* pre_pages, int pre_max_blocks, int hq, int hkv, int d,
                          int prior, int chunk, int off, int n_local, void* out_local,
