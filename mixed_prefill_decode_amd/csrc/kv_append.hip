@@ -33,8 +33,10 @@ __device__ __forceinline__ void put_kv(void* pool, int n_pages, int S, int d, in
   St<T>::store(pool, base + long(S) * d + long(j) * S + slot, vval);
 }
 
-// One workgroup per row task: tasks [0, M) are this rank's rows, tasks
-// [M, M + n_peer) are the chunk's peer rows.
+// One workgroup per row task: tasks [0, M) are this rank's rows; the chunk's peer
+// rows, which are only copied, go kPeerRowsPerTask to a task after them.
+constexpr int kPeerRowsPerTask = 8;
+
 template <typename T>
 __global__ __launch_bounds__(256) void post_qkv_kernel(PostQkvArgs a) {
   extern __shared__ float cs[];  // [d/2] cos, [d/2] sin
@@ -45,22 +47,32 @@ __global__ __launch_bounds__(256) void post_qkv_kernel(PostQkvArgs a) {
   const int q0 = a.r * hq_loc, k0 = a.r * hkv_loc;
   const int ldq = (a.Hq + 2 * a.Hkv) * d;
 
-  if (task >= M) {  // peer chunk row: copy its (already rotated) q | k | v on this rank's heads
-    const int p = task - M;
-    const int t = p < a.off ? p : p + a.n_pl;
-    const int pos = a.prior + t;
-    const int w = (hq_loc + 2 * hkv_loc) * d;
-    const long src = long(p) * w;
-    for (int e = tid; e < hq_loc * d; e += 256) {
-      const int h = e / d, j = e % d;
-      St<T>::store(a.q_pre, (long(h) * a.chunk + t) * d + j, St<T>::load(a.peer_qkv_in, src + e));
-    }
-    for (int e = tid; e < hkv_loc * d; e += 256) {
-      const int g = e / d, j = e % d;
-      const int page = a.pre_pages[long(g) * a.pre_max_blocks + pos / S];
-      put_kv<T>(a.pool, a.n_pages, S, d, page, pos % S, j,
-                St<T>::load(a.peer_qkv_in, src + hq_loc * d + e),
-                St<T>::load(a.peer_qkv_in, src + (hq_loc + hkv_loc) * d + e), a.status);
+  if (task >= M) {  // peer chunk rows: copy their (already rotated) q | k | v on this rank's heads
+    const int n_peer = a.chunk - a.n_pl;
+    const int p1 = min(n_peer, (task - M + 1) * kPeerRowsPerTask);
+    for (int p = (task - M) * kPeerRowsPerTask; p < p1; ++p) {
+      const int t = p < a.off ? p : p + a.n_pl;
+      const int pos = a.prior + t;
+      const int w = (hq_loc + 2 * hkv_loc) * d;
+      const long src = long(p) * w;
+      for (int e0 = tid; e0 < hq_loc * d; e0 += 256 * 8) {
+        float v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) v[u] = e0 + 256 * u < hq_loc * d ? St<T>::load(a.peer_qkv_in, src + e0 + 256 * u) : 0.f;
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const int e = e0 + 256 * u;
+          if (e >= hq_loc * d) break;
+          St<T>::store(a.q_pre, (long(e / d) * a.chunk + t) * d + e % d, v[u]);
+        }
+      }
+      for (int e = tid; e < hkv_loc * d; e += 256) {
+        const int g = e / d, j = e % d;
+        const int page = a.pre_pages[long(g) * a.pre_max_blocks + pos / S];
+        put_kv<T>(a.pool, a.n_pages, S, d, page, pos % S, j,
+                  St<T>::load(a.peer_qkv_in, src + hq_loc * d + e),
+                  St<T>::load(a.peer_qkv_in, src + (hq_loc + hkv_loc) * d + e), a.status);
+      }
     }
     return;
   }
@@ -69,6 +81,7 @@ __global__ __launch_bounds__(256) void post_qkv_kernel(PostQkvArgs a) {
   const int i = task - a.n_pl;          // decode request
   const int t = a.off + task;           // chunk row of a local prefill row
   const int pos = is_dec ? a.dec_ctx[i] : a.prior + t;
+  int* pg = reinterpret_cast<int*>(cs + d);  // [Hkv] page of this row's slot per kv head, -2: not appended here
   if (tid < half) {
     const double theta = pow(a.rope_base, -2.0 * double(tid) / double(d));
     double sn, cn;
@@ -76,64 +89,99 @@ __global__ __launch_bounds__(256) void post_qkv_kernel(PostQkvArgs a) {
     cs[tid] = float(cn);
     cs[half + tid] = float(sn);
   }
+  for (int g = tid; g < a.Hkv; g += 256) {
+    int page = -2;
+    if (is_dec) {
+      page = (pos >= 0 && pos / S < a.dec_max_blocks) ? a.dec_pages[(long(i) * a.Hkv + g) * a.dec_max_blocks + pos / S]
+                                                       : -1;
+    } else if (g >= k0 && g < k0 + hkv_loc) {
+      page = a.pre_pages[long(g - k0) * a.pre_max_blocks + pos / S];
+    }
+    pg[g] = page;
+  }
   __syncthreads();
   const float* row = a.qkv + long(task) * ldq;
   const int oq_w = (a.Hq - hq_loc) * d, ok_w = (a.Hkv - hkv_loc) * d;
   const long pq_out = long(task) * (oq_w + 2 * ok_w);
 
-  // rotated q and k: pairs (j, j + d/2)
-  for (int e = tid; e < (a.Hq + a.Hkv) * half; e += 256) {
-    const int h = e / half, j = e % half;
-    const float x0 = row[h * d + j], x1 = row[h * d + j + half];
-    const float c = cs[j], s = cs[half + j];
-    const float y0 = x0 * c - x1 * s, y1 = x1 * c + x0 * s;
-    if (h < a.Hq) {
-      if (is_dec) {
-        const long o = (long(i) * a.Hq + h) * d;
-        St<T>::store(a.q_dec, o + j, y0);
-        St<T>::store(a.q_dec, o + j + half, y1);
-      } else if (h >= q0 && h < q0 + hq_loc) {
-        const long o = (long(h - q0) * a.chunk + t) * d;
-        St<T>::store(a.q_pre, o + j, y0);
-        St<T>::store(a.q_pre, o + j + half, y1);
-      } else {
-        const long o = pq_out + long(h < q0 ? h : h - hq_loc) * d;
-        St<T>::store(a.peer_qkv_out, o + j, y0);
-        St<T>::store(a.peer_qkv_out, o + j + half, y1);
+  // rotated q and k: pairs (j, j + d/2).  Each thread loads a batch of pairs before
+  // storing any of them: the compiler cannot prove the stores leave the row alone, so
+  // loads interleaved with stores would each wait a full memory round trip.
+  constexpr int kBatch = 8;
+  const int n_pairs = (a.Hq + a.Hkv) * half;
+  for (int e0 = tid; e0 < n_pairs; e0 += 256 * kBatch) {
+    float x0[kBatch], x1[kBatch], v0[kBatch], v1[kBatch];
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      const int e = e0 + 256 * u;
+      x0[u] = x1[u] = v0[u] = v1[u] = 0.f;
+      if (e < n_pairs) {
+        const int h = e / half, j = e % half;
+        x0[u] = row[h * d + j];
+        x1[u] = row[h * d + j + half];
+        if (h >= a.Hq) {  // the value row of kv head h - Hq
+          v0[u] = row[(a.Hkv + h) * d + j];
+          v1[u] = row[(a.Hkv + h) * d + j + half];
+        }
       }
-    } else {
-      const int g = h - a.Hq;
-      const float* vrow = row + (a.Hq + a.Hkv + g) * d;
-      const float v0 = vrow[j], v1 = vrow[j + half];
-      int page = -2;
-      if (is_dec) {
-        page = (pos >= 0 && pos / S < a.dec_max_blocks)
-                   ? a.dec_pages[(long(i) * a.Hkv + g) * a.dec_max_blocks + pos / S]
-                   : -1;
-      } else if (g >= k0 && g < k0 + hkv_loc) {
-        page = a.pre_pages[long(g - k0) * a.pre_max_blocks + pos / S];
-      }
-      if (page != -2) {
-        put_kv<T>(a.pool, a.n_pages, S, d, page, pos % S, j, y0, v0, a.status);
-        put_kv<T>(a.pool, a.n_pages, S, d, page, pos % S, j + half, y1, v1, a.status);
+    }
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      const int e = e0 + 256 * u;
+      if (e >= n_pairs) break;
+      const int h = e / half, j = e % half;
+      const float c = cs[j], s = cs[half + j];
+      const float y0 = x0[u] * c - x1[u] * s, y1 = x1[u] * c + x0[u] * s;
+      if (h < a.Hq) {
+        if (is_dec) {
+          const long o = (long(i) * a.Hq + h) * d;
+          St<T>::store(a.q_dec, o + j, y0);
+          St<T>::store(a.q_dec, o + j + half, y1);
+        } else if (h >= q0 && h < q0 + hq_loc) {
+          const long o = (long(h - q0) * a.chunk + t) * d;
+          St<T>::store(a.q_pre, o + j, y0);
+          St<T>::store(a.q_pre, o + j + half, y1);
+        } else {
+          const long o = pq_out + long(h < q0 ? h : h - hq_loc) * d;
+          St<T>::store(a.peer_qkv_out, o + j, y0);
+          St<T>::store(a.peer_qkv_out, o + j + half, y1);
+        }
       } else {
-        const int gi = g < k0 ? g : g - hkv_loc;
-        const long ok = pq_out + oq_w + long(gi) * d;
-        const long ov = pq_out + oq_w + ok_w + long(gi) * d;
-        St<T>::store(a.peer_qkv_out, ok + j, y0);
-        St<T>::store(a.peer_qkv_out, ok + j + half, y1);
-        St<T>::store(a.peer_qkv_out, ov + j, v0);
-        St<T>::store(a.peer_qkv_out, ov + j + half, v1);
+        const int g = h - a.Hq;
+        const int page = pg[g];
+        if (page != -2) {
+          put_kv<T>(a.pool, a.n_pages, S, d, page, pos % S, j, y0, v0[u], a.status);
+          put_kv<T>(a.pool, a.n_pages, S, d, page, pos % S, j + half, y1, v1[u], a.status);
+        } else {
+          const int gi = g < k0 ? g : g - hkv_loc;
+          const long ok = pq_out + oq_w + long(gi) * d;
+          const long ov = pq_out + oq_w + ok_w + long(gi) * d;
+          St<T>::store(a.peer_qkv_out, ok + j, y0);
+          St<T>::store(a.peer_qkv_out, ok + j + half, y1);
+          St<T>::store(a.peer_qkv_out, ov + j, v0[u]);
+          St<T>::store(a.peer_qkv_out, ov + j + half, v1[u]);
+        }
       }
     }
   }
   // local prefill rows: attention outputs of the heads other ranks own arrive as peer_attn_in
+  // (batched like the pairs above, so the loads do not wait on the stores)
   if (!is_dec && oq_w > 0) {
-    for (int e = tid; e < oq_w; e += 256) {
-      const int hi = e / d, j = e % d;
-      const int h = hi < q0 ? hi : hi + hq_loc;
-      St<T>::store(a.attn, long(task) * a.Hq * d + long(h) * d + j,
-                   St<T>::load(a.peer_attn_in, long(task) * oq_w + e));
+    for (int e0 = tid; e0 < oq_w; e0 += 256 * kBatch) {
+      float v[kBatch];
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) {
+        const int e = e0 + 256 * u;
+        v[u] = e < oq_w ? St<T>::load(a.peer_attn_in, long(task) * oq_w + e) : 0.f;
+      }
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) {
+        const int e = e0 + 256 * u;
+        if (e >= oq_w) break;
+        const int hi = e / d, j = e % d;
+        const int h = hi < q0 ? hi : hi + hq_loc;
+        St<T>::store(a.attn, long(task) * a.Hq * d + long(h) * d + j, v[u]);
+      }
     }
   }
 }
@@ -174,9 +222,9 @@ __global__ __launch_bounds__(256) void kv_gather_kernel(const void* pool, int n_
 }  // namespace
 
 xp_status launch_post_qkv(int dtype, const PostQkvArgs& a, hipStream_t s) {
-  const int tasks = a.n_pl + a.n_d + (a.chunk - a.n_pl);
+  const int tasks = a.n_pl + a.n_d + cdiv(a.chunk - a.n_pl, kPeerRowsPerTask);
   if (tasks == 0) return XP_OK;
-  const size_t shm = size_t(a.d) * sizeof(float);
+  const size_t shm = size_t(a.d) * sizeof(float) + size_t(a.Hkv) * sizeof(int);
   if (dtype == XP_BF16)
     hipLaunchKernelGGL(post_qkv_kernel<bf16_t>, dim3(tasks), dim3(256), shm, s, a);
   else
