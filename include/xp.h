@@ -244,6 +244,14 @@ xp_status xp_validate_batch(const xp_layer_shape* shape, const xp_batch_desc* de
                             const int32_t* dec_ctx_host, const int32_t* dec_pages_host,
                             const int32_t* pre_pages_host);
 
+/* xp_validate_batch for a multi-chunk step: the decode tables as there, and
+ * chunk j's table (positions 0 .. prior_len + chunk_len - 1 on every KV head)
+ * from chunk_pages_host, which holds the chunks' [Hkv, pre_max_blocks] host
+ * tables back to back in list order. */
+xp_status xp_validate_chunks(const xp_layer_shape* shape, const xp_batch_desc* desc, int32_t n_chunks,
+                             const xp_chunk* chunks, int32_t n_pages, const int32_t* dec_ctx_host,
+                             const int32_t* dec_pages_host, const int32_t* chunk_pages_host);
+
 /* Reads the device status word of a workspace (synchronizes `stream`). */
 xp_status xp_layer_read_status(const void* workspace, const xp_ws_layout* layout, uint32_t* status,
                                void* stream);

@@ -16,7 +16,7 @@ __all__ = ["XpError", "lib", "XP_F32", "XP_BF16", "XP_EPI_F32", "XP_EPI_ADD_T", 
            "XP_EPI_SWIGLU", "XP_DEV_BAD_PAGE", "LayerShape", "LayerWeights", "KvPages", "BatchDesc",
            "WsLayout", "LatencyModel", "Ctx", "EXPORTED", "Chunk", "chunk_array",
            "xp_ctx_create", "xp_layer_workspace_layout", "xp_layer_forward", "xp_validate_batch",
-           "xp_layer_workspace_layout_chunks", "xp_layer_forward_chunks",
+           "xp_layer_workspace_layout_chunks", "xp_layer_forward_chunks", "xp_validate_chunks",
            "xp_layer_read_status", "xp_rmsnorm", "xp_gemm_workspace_size", "xp_gemm_tile", "xp_gemm", "xp_kv_append",
            "xp_kv_gather",
            "xp_decode_workspace_size", "xp_decode_attention", "xp_prefill_workspace_size", "xp_prefill_attention",
@@ -37,7 +37,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libxp.so")
 EXPORTED = ["xp_last_error", "xp_build_info", "xp_ctx_create", "xp_ctx_destroy", "xp_ctx_cu_masks",
             "xp_ctx_streams",
             "xp_layer_workspace_layout", "xp_layer_forward", "xp_validate_batch", "xp_layer_read_status",
-            "xp_layer_workspace_layout_chunks", "xp_layer_forward_chunks",
+            "xp_layer_workspace_layout_chunks", "xp_layer_forward_chunks", "xp_validate_chunks",
             "xp_rmsnorm", "xp_gemm_workspace_size", "xp_gemm_tile", "xp_gemm", "xp_kv_append", "xp_kv_gather",
             "xp_decode_workspace_size",
             "xp_decode_attention", "xp_prefill_workspace_size", "xp_prefill_attention", "xp_probe_hw_ids",
@@ -158,6 +158,8 @@ def _declare(L):
                                                  C.POINTER(Chunk), C.POINTER(WsLayout)]),
         "xp_layer_forward_chunks": (S, [_vp, C.POINTER(LayerShape), C.POINTER(BatchDesc), _i32, C.POINTER(Chunk),
                                         C.POINTER(LayerWeights), C.POINTER(KvPages), _vp, _vp, _sz, _vp]),
+        "xp_validate_chunks": (S, [C.POINTER(LayerShape), C.POINTER(BatchDesc), _i32, C.POINTER(Chunk), _i32, _vp,
+                                   _vp, _vp]),
         "xp_validate_batch": (S, [C.POINTER(LayerShape), C.POINTER(BatchDesc), _i32, _vp, _vp, _vp]),
         "xp_layer_read_status": (S, [_vp, C.POINTER(WsLayout), _vp, _vp]),
         "xp_rmsnorm": (S, [_i32, _vp, _i32, _vp, _vp, _i32, _i32, _f32, _vp]),
@@ -305,6 +307,15 @@ def chunk_array(chunks):
     for j, (l, c, t) in enumerate(chunks):
         arr[j] = Chunk(int(l), int(c), _ptr(t), int(t.shape[-1]))
     return arr if chunks else (Chunk * 0)()
+
+
+def xp_validate_chunks(shape, desc, chunks, n_pages, dec_ctx_host, dec_pages_host, chunk_tables_host):
+    """``chunks``: a ctypes Chunk array; ``chunk_tables_host``: the chunks' host tables in list order."""
+    flat = np.ascontiguousarray(np.concatenate([np.asarray(t, dtype=np.int32).reshape(-1) for t in chunk_tables_host])
+                                if len(chunk_tables_host) else np.zeros(1, np.int32), dtype=np.int32)
+    arrs = [None if a is None else np.ascontiguousarray(a, dtype=np.int32) for a in (dec_ctx_host, dec_pages_host)]
+    return lib().xp_validate_chunks(C.byref(shape), C.byref(desc), len(chunks), chunks, n_pages,
+                                    *[_ptr(a) for a in arrs], _ptr(flat))
 
 
 def xp_validate_batch(shape, desc, n_pages, dec_ctx_host, dec_pages_host, pre_pages_host):

@@ -318,38 +318,88 @@ xp_status xp_layer_workspace_layout(const xp_ctx* ctx, const xp_layer_shape* sh,
   return XP_OK;
 }
 
-xp_status xp_validate_batch(const xp_layer_shape* sh, const xp_batch_desc* d, int32_t n_pages,
-                            const int32_t* dec_ctx_h, const int32_t* dec_pages_h, const int32_t* pre_pages_h) {
-  xp_status st = check_shape(sh);
-  if (st) return st;
-  if ((st = check_desc(sh, d))) return st;
-  if (n_pages <= 0) return fail(XP_ESHAPE, "n_pages %d", n_pages);
-  std::string seen(size_t(n_pages), '\0');
-  const int S = sh->page_size, Hkv = sh->n_kv_heads;
-  auto use = [&](int p, const char* what) -> xp_status {
+}  // extern "C"
+
+namespace {
+
+// Marks the pages a step touches; fails on an id outside the pool or named twice.
+struct PageCheck {
+  std::string seen;
+  int n_pages;
+  explicit PageCheck(int n) : seen(size_t(n), '\0'), n_pages(n) {}
+  xp_status use(int p, const char* what) {
     if (p < 0 || p >= n_pages) return fail(XP_EPAGE, "%s page id %d outside [0, %d)", what, p, n_pages);
     if (seen[size_t(p)]) return fail(XP_EPAGE, "%s page id %d named twice", what, p);
     seen[size_t(p)] = 1;
     return XP_OK;
-  };
-  if (d->n_decode > 0) {
+  }
+  xp_status decodes(const xp_layer_shape* sh, const xp_batch_desc* d, const int32_t* dec_ctx_h,
+                    const int32_t* dec_pages_h) {
+    if (d->n_decode == 0) return XP_OK;
     if (!dec_ctx_h || !dec_pages_h) return fail(XP_EINVAL, "null host decode tables");
+    const int S = sh->page_size, Hkv = sh->n_kv_heads;
     for (int i = 0; i < d->n_decode; ++i) {
       const int c = dec_ctx_h[i];
       if (c < 0) return fail(XP_ESHAPE, "decode %d: context %d", i, c);
       const int nb = c / S + 1;
       if (nb > d->dec_max_blocks) return fail(XP_EPAGE, "decode %d: context %d needs %d blocks > %d", i, c, nb, d->dec_max_blocks);
       for (int g = 0; g < Hkv; ++g)
-        for (int b = 0; b < nb; ++b)
-          if ((st = use(dec_pages_h[(long(i) * Hkv + g) * d->dec_max_blocks + b], "decode"))) return st;
+        for (int b = 0; b < nb; ++b) {
+          xp_status st = use(dec_pages_h[(long(i) * Hkv + g) * d->dec_max_blocks + b], "decode");
+          if (st) return st;
+        }
     }
+    return XP_OK;
   }
+  // one prefill table: heads rows of max_blocks, positions [0, prior + len)
+  xp_status chunk(const int32_t* t, int heads, int max_blocks, int prior, int len, int S, const char* what) {
+    const int nb = cdiv(long(prior) + len, S);
+    for (int g = 0; g < heads; ++g)
+      for (int b = 0; b < nb; ++b) {
+        xp_status st = use(t[long(g) * max_blocks + b], what);
+        if (st) return st;
+      }
+    return XP_OK;
+  }
+};
+
+}  // namespace
+
+extern "C" {
+
+xp_status xp_validate_batch(const xp_layer_shape* sh, const xp_batch_desc* d, int32_t n_pages,
+                            const int32_t* dec_ctx_h, const int32_t* dec_pages_h, const int32_t* pre_pages_h) {
+  xp_status st = check_shape(sh);
+  if (st) return st;
+  if ((st = check_desc(sh, d))) return st;
+  if (n_pages <= 0) return fail(XP_ESHAPE, "n_pages %d", n_pages);
+  PageCheck pc(n_pages);
+  if ((st = pc.decodes(sh, d, dec_ctx_h, dec_pages_h))) return st;
   if (d->chunk_len > 0) {
     if (!pre_pages_h) return fail(XP_EINVAL, "null host prefill table");
-    const int nb = cdiv(long(d->prior_len) + d->chunk_len, S);
-    for (int g = 0; g < Hkv / d->sp_degree; ++g)
-      for (int b = 0; b < nb; ++b)
-        if ((st = use(pre_pages_h[long(g) * d->pre_max_blocks + b], "prefill"))) return st;
+    return pc.chunk(pre_pages_h, sh->n_kv_heads / d->sp_degree, d->pre_max_blocks, d->prior_len, d->chunk_len,
+                    sh->page_size, "prefill");
+  }
+  return XP_OK;
+}
+
+xp_status xp_validate_chunks(const xp_layer_shape* sh, const xp_batch_desc* d, int32_t n_chunks, const xp_chunk* chunks,
+                             int32_t n_pages, const int32_t* dec_ctx_h, const int32_t* dec_pages_h,
+                             const int32_t* chunk_pages_h) {
+  xp_status st = check_shape(sh);
+  if (st) return st;
+  if ((st = check_desc(sh, d)) || (st = check_chunks(sh, d, n_chunks, chunks))) return st;
+  if (n_pages <= 0) return fail(XP_ESHAPE, "n_pages %d", n_pages);
+  PageCheck pc(n_pages);
+  if ((st = pc.decodes(sh, d, dec_ctx_h, dec_pages_h))) return st;
+  if (n_chunks > 0 && !chunk_pages_h) return fail(XP_EINVAL, "null host chunk tables");
+  long off = 0;
+  for (int j = 0; j < n_chunks; ++j) {
+    const xp_chunk& c = chunks[j];
+    if ((st = pc.chunk(chunk_pages_h + off, sh->n_kv_heads, c.pre_max_blocks, c.prior_len, c.chunk_len, sh->page_size,
+                       "chunk")))
+      return st;
+    off += long(sh->n_kv_heads) * c.pre_max_blocks;
   }
   return XP_OK;
 }

@@ -608,6 +608,11 @@ MULTI_CHUNK_WORKLOADS = {
     "M3": MultiChunkWorkload("M3", 123, "bf16", 512, 8, 2, 128, 1024, n_decode=0, ctx=("fixed", 0),
                              chunks=[(70, 33), (16, 0), (129, 250)],
                              description="small bf16 layer, 3 chunks, no decode"),
+    # ten chunks: more than one grouped prefill launch (eight chunks per launch)
+    "M4": MultiChunkWorkload("M4", 124, "bf16", 512, 8, 2, 128, 1024, n_decode=2, ctx=("uniform", 10, 300),
+                             chunks=[(17, 0), (40, 3), (5, 60), (64, 16), (33, 200), (1, 7), (90, 0), (12, 500),
+                                     (48, 31), (20, 100)],
+                             description="small bf16 layer, 10 chunks + 2 decodes"),
     # the 8B step of the layer benchmark with its 1024 prefill rows from four requests
     "C2x4": MultiChunkWorkload("C2x4", 24, "bf16", 4096, 32, 8, 128, 14336, n_decode=16, ctx=("fixed", 8192),
                                chunks=[(256, 0), (256, 2048), (256, 4096), (256, 8192)],

@@ -385,3 +385,34 @@ def test_chunk_list_layout_is_host_only_and_validated():
     assert e.value.status == -5
     with pytest.raises(X.XpError):
         X.xp_layer_workspace_layout_chunks(None, shape, desc, X.chunk_array([(0, 0, T(t1))]))
+
+
+def test_chunk_tables_are_validated_on_the_host():
+    from synth import MULTI_CHUNK_WORKLOADS, make_multi_instance
+    inst = make_multi_instance(MULTI_CHUNK_WORKLOADS["M4"])
+    wl = inst.wl
+    shape = X.layer_shape(hidden=wl.hidden, n_q_heads=wl.n_q_heads, n_kv_heads=wl.n_kv_heads, head_dim=wl.head_dim,
+                          ffn_dim=wl.ffn_dim)
+
+    class T:  # host table stand-in: only the address and the block count reach the structs
+        def __init__(self, a):
+            self.a, self.shape = a, a.shape
+
+        def data_ptr(self):
+            return self.a.ctypes.data
+
+        def dim(self):
+            return self.a.ndim
+
+    dec_pages = inst.dec_pages
+    desc = X.batch_desc(x=inst.x.ctypes.data, n_prefill_local=0, n_decode=wl.n_decode, dec_ctx=T(inst.dec_ctx),
+                        dec_pages=T(dec_pages), chunk_len=0, prior_len=0)
+    chunks = X.chunk_array([(l, c, T(t)) for (l, c), t in zip(wl.chunks, inst.chunk_pages)])
+    n = inst.pool.n_pages
+    assert X.xp_validate_chunks(shape, desc, chunks, n, inst.dec_ctx, dec_pages, inst.chunk_pages) == 0
+    bad = [t.copy() for t in inst.chunk_pages]
+    bad[9][1, 0] = n                                                   # outside the pool
+    assert X.xp_validate_chunks(shape, desc, chunks, n, inst.dec_ctx, dec_pages, bad) == -3
+    bad = [t.copy() for t in inst.chunk_pages]
+    bad[3][0, 1] = int(inst.chunk_pages[0][0, 0])                      # named twice
+    assert X.xp_validate_chunks(shape, desc, chunks, n, inst.dec_ctx, dec_pages, bad) == -3

@@ -64,7 +64,7 @@ def _check(inst, step, ref, rows):
     return r
 
 
-@pytest.mark.parametrize("name", ["M1", "M2", "M3"])
+@pytest.mark.parametrize("name", ["M1", "M2", "M3", "M4"])
 def test_chunked_layer_matches_oracle(name):
     inst = make_multi_instance(MULTI_CHUNK_WORKLOADS[name])
     wl, dt = inst.wl, inst.wl.dtype

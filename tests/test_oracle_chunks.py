@@ -27,7 +27,7 @@ def _single(inst, j):
                 peer_qkv_in=inst.x[:0], peer_attn_in=inst.x[:0], pool=inst.pool)
 
 
-@pytest.mark.parametrize("name", ["M1", "M2", "M3"])
+@pytest.mark.parametrize("name", ["M1", "M2", "M3", "M4"])
 def test_each_chunk_equals_its_own_single_chunk_step(name):
     inst = make_multi_instance(MULTI_CHUNK_WORKLOADS[name])
     wl = inst.wl
