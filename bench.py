@@ -384,6 +384,19 @@ def scheduler_timing(X, repeats: int = 100) -> dict:
     import statistics
     from synth import scheduler_case
     out = {"unit": "us", "ranks": 8, "repeats": repeats, "depths": {}}
+    # one dispatch (Algorithm 2) on the same 8-rank state: a 4096-token candidate
+    c = dataclasses.asdict(scheduler_case(10))
+    wf = X.WaterfillCall(tau=c["tau"], n_decode_tokens=c["n_decode_tokens"], decode_ctx_sum=c["decode_ctx_sum"],
+                         candidate=(4096, 0), quantum=c["quantum"], model=c["model"])
+    for _ in range(10):
+        wf.call()
+    ts = []
+    for _ in range(repeats):
+        t0 = time.perf_counter()
+        wf.call()
+        ts.append(time.perf_counter() - t0)
+    out["waterfill_dispatch"] = {"mean": round(statistics.mean(ts) * 1e6, 2), "std": round(statistics.stdev(ts) * 1e6, 2),
+                                 "chunk_len": wf.result()["chunk_len"]}
     for depth in (10, 50, 100, 500):
         c = dataclasses.asdict(scheduler_case(depth))
         c.pop("name")

@@ -22,7 +22,7 @@ __all__ = ["XpError", "lib", "XP_F32", "XP_BF16", "XP_EPI_F32", "XP_EPI_ADD_T", 
            "xp_decode_workspace_size", "xp_decode_attention", "xp_prefill_workspace_size", "xp_prefill_attention",
            "xp_probe_hw_ids",
            "xp_waterfill", "xp_iteration_latency", "xp_admission", "xp_decode_placement", "xp_schedule",
-           "ScheduleCall", "xp_fit_affine", "xp_fit_latency_model", "XP_SCHED_DONE", "XP_SCHED_BUDGET", "XP_SCHED_NO_HOST", "xp_build_info", "xp_last_error"]
+           "ScheduleCall", "WaterfillCall", "xp_fit_affine", "xp_fit_latency_model", "XP_SCHED_DONE", "XP_SCHED_BUDGET", "XP_SCHED_NO_HOST", "xp_build_info", "xp_last_error"]
 
 XP_F32, XP_BF16 = 0, 1
 XP_EPI_F32, XP_EPI_ADD_T, XP_EPI_ADD_F32, XP_EPI_SWIGLU = 0, 1, 2, 3
@@ -396,23 +396,42 @@ def _model(d: dict) -> LatencyModel:
                                                 "a_comm0", "alpha", "beta")], int(d["n_layers"]))
 
 
-def xp_waterfill(*, tau, n_decode_tokens, decode_ctx_sum, existing=None, selected=(), candidate=None,
-                 quantum=1, model, fixed_target=-1, level_hi=0) -> dict:
-    N = len(n_decode_tokens)
-    nd = np.ascontiguousarray(n_decode_tokens, dtype=np.int32)
-    cs = np.ascontiguousarray(decode_ctx_sum, dtype=np.int64)
-    ex = None if existing is None else np.ascontiguousarray(existing, dtype=np.int32)
-    sl = np.ascontiguousarray([s[0] for s in selected] or [0], dtype=np.int32)
-    sc = np.ascontiguousarray([s[1] for s in selected] or [0], dtype=np.int64)
-    m = _model(model)
-    inp = WaterfillIn(N, _ptr(nd), _ptr(cs), _ptr(ex), len(selected), _ptr(sl), _ptr(sc),
-                      1 if candidate is not None else 0, int(candidate[0]) if candidate else 0,
-                      int(candidate[1]) if candidate else 0, int(fixed_target), int(level_hi), int(quantum),
-                      float(tau), C.pointer(m))
-    assign = np.zeros(N, dtype=np.int32)
-    out = WaterfillOut(0, 0, 0, _ptr(assign))
-    _check(lib().xp_waterfill(C.byref(inp), C.byref(out)))
-    return dict(n_target=out.n_target, budget=out.budget, chunk_len=out.chunk_len, assign=assign.tolist())
+class WaterfillCall:
+    """One xp_waterfill call with its arguments marshalled once: ``call()`` runs the
+    dispatcher on them (so a caller can time the native call alone), ``result()``
+    decodes the last call's outputs."""
+
+    def __init__(self, *, tau, n_decode_tokens, decode_ctx_sum, existing=None, selected=(), candidate=None,
+                 quantum=1, model, fixed_target=-1, level_hi=0):
+        N = len(n_decode_tokens)
+        self._arrs = (np.ascontiguousarray(n_decode_tokens, dtype=np.int32),
+                      np.ascontiguousarray(decode_ctx_sum, dtype=np.int64),
+                      None if existing is None else np.ascontiguousarray(existing, dtype=np.int32),
+                      np.ascontiguousarray([s[0] for s in selected] or [0], dtype=np.int32),
+                      np.ascontiguousarray([s[1] for s in selected] or [0], dtype=np.int64))
+        nd, cs, ex, sl, sc = self._arrs
+        self._m = _model(model)
+        self.inp = WaterfillIn(N, _ptr(nd), _ptr(cs), _ptr(ex), len(selected), _ptr(sl), _ptr(sc),
+                               1 if candidate is not None else 0, int(candidate[0]) if candidate else 0,
+                               int(candidate[1]) if candidate else 0, int(fixed_target), int(level_hi), int(quantum),
+                               float(tau), C.pointer(self._m))
+        self.assign = np.zeros(N, dtype=np.int32)
+        self.out = WaterfillOut(0, 0, 0, _ptr(self.assign))
+        self._fn = lib().xp_waterfill
+        self._args = (C.byref(self.inp), C.byref(self.out))
+
+    def call(self):
+        _check(self._fn(*self._args))
+        return self
+
+    def result(self) -> dict:
+        o = self.out
+        return dict(n_target=o.n_target, budget=o.budget, chunk_len=o.chunk_len, assign=self.assign.tolist())
+
+
+def xp_waterfill(**kw) -> dict:
+    """Algorithm 2 (keyword arguments as WaterfillCall)."""
+    return WaterfillCall(**kw).call().result()
 
 
 def xp_iteration_latency(model: dict, n_decode_tokens, decode_ctx_sum, n_prefill_tokens, chunks) -> float:
