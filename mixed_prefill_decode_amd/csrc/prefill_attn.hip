@@ -12,7 +12,9 @@
 // head, as NQ 32-query MFMA column blocks: every K or V fragment it reads from
 // LDS feeds NQ MFMAs, and the NQ accumulation chains are independent.  Blocks
 // (two pages: 8 KB of K rows + 8 KB of V^T rows for d = 128 bf16) are copied
-// straight into a 3-stage LDS ring with buffer_load ... lds.  gfx950's LDS serves
+// straight into an LDS ring of two-block stages with buffer_load ... lds.  A
+// workgroup of a small grid may hold two waves per head (two key sets), each set
+// taking every other block of the split, merged in LDS at the end.  gfx950's LDS serves
 // 16-byte reads 16 lanes at a time over 64 banks (256 bytes), and both planes are
 // XOR-swizzled in 16-byte chunks so those 16 lanes -- 16 keys of a K read, 16 dim
 // rows of a V^T read -- land on distinct banks.  Splitting the key range gives
@@ -57,6 +59,9 @@ constexpr int kPage = 16;
 #define XP_PREFILL_STAGES 2
 #endif
 constexpr int kStages = XP_PREFILL_STAGES;
+#ifndef XP_PREFILL_STAGES_KS2
+#define XP_PREFILL_STAGES_KS2 3
+#endif
 #ifndef XP_PREFILL_SB
 #define XP_PREFILL_SB 2
 #endif
@@ -192,7 +197,7 @@ __device__ __forceinline__ void out_row(const PrefillArgs& a, int t, void*& dst,
   }
 }
 
-template <typename T, int D, int NQ, int MAXW>
+template <typename T, int D, int NQ, int MAXW, int KS>
 __device__ __forceinline__ void prefill_tile(const PrefillArgs& a, int bx, int by) {
   constexpr int EB = St<T>::bytes;
   constexpr int QT = 32 * NQ;                     // queries per tile
@@ -205,17 +210,25 @@ __device__ __forceinline__ void prefill_tile(const PrefillArgs& a, int bx, int b
   constexpr int VROW_CH = kPage * EB / 16;        // 16-byte chunks per V^T row
   // blocks per stage and ring depth, within the LDS budget
   constexpr int kBudget = 144 * 1024;
-  constexpr int SB = kBlocksPerStage * kStages * BLK <= kBudget
+  constexpr int kSt = KS == 2 ? XP_PREFILL_STAGES_KS2 : kStages;
+  constexpr int SB = kBlocksPerStage * 2 * BLK <= kBudget
                          ? kBlocksPerStage
-                         : (kBudget / (kStages * BLK) > 0 ? kBudget / (kStages * BLK) : 1);
-  constexpr int NST = kStages * SB * BLK <= kBudget ? kStages : (kBudget / (SB * BLK) > 2 ? kBudget / (SB * BLK) : 2);
+                         : (kBudget / (2 * BLK) > 0 ? kBudget / (2 * BLK) : 1);
+  constexpr int NST = kSt * SB * BLK <= kBudget ? kSt : (kBudget / (SB * BLK) > 2 ? kBudget / (SB * BLK) : 2);
   constexpr int STAGE = SB * BLK;
   constexpr int INSTR = SB * INSTR_BLK;           // load instructions per stage
   __shared__ uint4 ring[NST][STAGE / 16];
   __shared__ int32_t pids[2 * kMaxBps];
+  // KS key sets: with KS = 2 the workgroup holds two waves per query head; set k
+  // consumes the blocks at odd or even positions of the split's key range, and the
+  // two partial softmax states are merged through LDS at the end.
+  static_assert(KS == 1 || (KS == 2 && SB % 2 == 0 && MAXW * NQ * D * 128 <= NST * STAGE),
+                "two key sets need an even number of blocks per stage and a ring that holds one set's state");
 
   const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wave_all = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int kset = KS == 1 ? 0 : wave_all / a.wpg;
+  const int wave = KS == 1 ? wave_all : wave_all % a.wpg;   // query head of the group
   const int G = a.hq / a.hkv;
   const int n_qt = (a.chunk + QT - 1) / QT;
   const int qt = n_qt - 1 - bx / a.n_split;   // longest tiles first
@@ -259,8 +272,9 @@ __device__ __forceinline__ void prefill_tile(const PrefillArgs& a, int bx, int b
   // instructions have fixed LDS destinations.  Blocks past the split load through
   // empty resources (moving no data), so each wave issues the same number of
   // instructions for every stage and the wait counts below are exact.
+  const int nl = KS * waves, lw = kset * waves + wave;     // loading waves, this wave's index
   int my_blocks = 0;
-  for (int b = wave; b < SB; b += waves) ++my_blocks;
+  for (int b = lw; b < SB; b += nl) ++my_blocks;
   const int my_instr = wave < waves ? my_blocks * INSTR_BLK : 0;   // per stage
   auto issue_block = [&](int sg, int b, int buf) {
     const int kb = kb0 + sg * SB + b;
@@ -317,7 +331,7 @@ __device__ __forceinline__ void prefill_tile(const PrefillArgs& a, int bx, int b
 #pragma unroll
   for (int i = 0; i < NST - 1; ++i)
     if (i < n_sg && wave < waves)
-      for (int b = wave; b < SB; b += waves) issue_block(i, b, i);
+      for (int b = lw; b < SB; b += nl) issue_block(i, b, i);
   const int krow = kappa(ql);
   for (int sg = 0; sg < n_sg; ++sg) {
     // stage sg has landed once no more than the later stages' loads are outstanding
@@ -326,9 +340,9 @@ __device__ __forceinline__ void prefill_tile(const PrefillArgs& a, int bx, int b
     const bool refill = sg + NST - 1 < n_sg;
 #pragma unroll 1
     for (int b = 0; b < SB; ++b) {
-      if (refill && b % waves == wave) issue_block(sg + NST - 1, b, (sg + NST - 1) % NST);
+      if (refill && wave < waves && b % nl == lw) issue_block(sg + NST - 1, b, (sg + NST - 1) % NST);
       const int kb = kb0 + sg * SB + b;
-      if (!active || kb >= kb1) continue;
+      if (!active || kb >= kb1 || (KS == 2 && (b & 1) != kset)) continue;
       const char* st_base = reinterpret_cast<const char*>(ring[sg % NST]) + b * BLK;
       const int key0 = kb * 32;
       // All K fragments of the block are read up front, then the V^T fragments right
@@ -414,7 +428,43 @@ __device__ __forceinline__ void prefill_tile(const PrefillArgs& a, int bx, int b
           for (int j = 0; j < NQ; ++j) mma32x32_k16(o[j][n], vf[u][n], pf[j][u]);
     }
   }
-  if (bad && a.status && lane == 0 && wave == 0) atomicOr(a.status, XP_DEV_BAD_PAGE);
+  if (bad && a.status && lane == 0 && wave_all == 0) atomicOr(a.status, XP_DEV_BAD_PAGE);
+  if constexpr (KS == 2) {
+    // set 1 hands its state to set 0 through the drained ring: o as [head][j][n][r][lane]
+    // floats, (reference, sum) beside it; set 0 rescales both to the larger reference
+    __shared__ float xml[MAXW * NQ * 2 * 64];
+    float* xo = reinterpret_cast<float*>(&ring[0][0]);
+    __syncthreads();
+    if (kset == 1 && active) {
+#pragma unroll
+      for (int j = 0; j < NQ; ++j) {
+#pragma unroll
+        for (int n = 0; n < D / 32; ++n)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) xo[(((wave * NQ + j) * (D / 32) + n) * 16 + r) * 64 + lane] = o[j][n][r];
+        xml[((wave * NQ + j) * 2) * 64 + lane] = ms[j];
+        xml[((wave * NQ + j) * 2 + 1) * 64 + lane] = lsum[j];
+      }
+    }
+    __syncthreads();
+    if (kset == 1) return;
+    if (active) {
+#pragma unroll
+      for (int j = 0; j < NQ; ++j) {
+        const float m1 = xml[((wave * NQ + j) * 2) * 64 + lane], l1 = xml[((wave * NQ + j) * 2 + 1) * 64 + lane];
+        const float mn = fmaxf(ms[j], m1);
+        const float a0 = ms[j] == -__builtin_inff() ? 0.f : fast_exp2(ms[j] - mn);
+        const float a1 = m1 == -__builtin_inff() ? 0.f : fast_exp2(m1 - mn);
+        ms[j] = mn;
+        lsum[j] = lsum[j] * a0 + l1 * a1;
+#pragma unroll
+        for (int n = 0; n < D / 32; ++n)
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            o[j][n][r] = o[j][n][r] * a0 + xo[(((wave * NQ + j) * (D / 32) + n) * 16 + r) * 64 + lane] * a1;
+      }
+    }
+  }
   if (!active) return;
 #pragma unroll
   for (int j = 0; j < NQ; ++j) {
@@ -503,9 +553,9 @@ __device__ __forceinline__ void prefill_combine_tile(const PrefillArgs& a, int q
   }
 }
 
-template <typename T, int D, int NQ, int MAXW>
-__global__ __launch_bounds__(64 * MAXW) void prefill_kernel(PrefillArgs a) {
-  prefill_tile<T, D, NQ, MAXW>(a, int(blockIdx.x), int(blockIdx.y));
+template <typename T, int D, int NQ, int MAXW, int KS>
+__global__ __launch_bounds__(64 * MAXW * KS) void prefill_kernel(PrefillArgs a) {
+  prefill_tile<T, D, NQ, MAXW, KS>(a, int(blockIdx.x), int(blockIdx.y));
 }
 
 template <typename T, int D>
@@ -544,12 +594,12 @@ __device__ __forceinline__ void group_member(const PrefillGroup& g, int b, bool 
   y = (b - s0) / w;
 }
 
-template <typename T, int D, int NQ, int MAXW>
-__global__ __launch_bounds__(64 * MAXW) void prefill_group_kernel(PrefillGroup g) {
+template <typename T, int D, int NQ, int MAXW, int KS>
+__global__ __launch_bounds__(64 * MAXW * KS) void prefill_group_kernel(PrefillGroup g) {
   PrefillArgs a;
   int x, y;
   group_member(g, int(blockIdx.x), false, a, x, y);
-  prefill_tile<T, D, NQ, MAXW>(a, x, y);
+  prefill_tile<T, D, NQ, MAXW, KS>(a, x, y);
 }
 
 template <typename T, int D>
@@ -644,8 +694,21 @@ namespace {
 struct Prepared {
   PrefillArgs a;
   Plan p;
-  int n_qt, gy;
+  int n_qt, gy, cus;
 };
+
+// Two key sets per workgroup (two waves per query head) when the group has at most
+// four heads, the grid has no more workgroups than CUs and the longest work unit
+// spans at least 16 key blocks: each CU then holds one four-wave workgroup, and a
+// second set of waves on the other half of the keys shortens the longest unit
+// (1024-token 8B chunk: 33 -> 29.5 us).  Larger grids already keep two workgroups per
+// CU (a grouped launch of four 256-token chunks runs at the same speed either way);
+// on short units the merge costs more than it saves (a 256-token chunk: 19.4 vs
+// 21.2 us).
+bool two_key_sets(const Prepared& pr, long workgroups) {
+  const int nkb = (pr.a.prior + pr.a.chunk + 31) / 32;
+  return pr.p.wpg <= 4 && workgroups <= pr.cus && std::min(nkb, pr.p.bps) >= 16;
+}
 
 xp_status prepare(const void* pool, int n_pages, int S, int hq, int hkv, int d, const PrefillJob& j, uint32_t* status,
                   int cus, Prepared& out) {
@@ -671,13 +734,17 @@ xp_status prepare(const void* pool, int n_pages, int S, int hq, int hkv, int d, 
   out.n_qt = (j.chunk + p.qt - 1) / p.qt;
   const int G = hq / hkv;
   out.gy = hkv * ((G + p.wpg - 1) / p.wpg);
+  out.cus = cus;
   return XP_OK;
 }
 
 template <typename T, int D>
 void launch_one(const Prepared& pr, hipStream_t s) {
   const dim3 grid(pr.n_qt * pr.p.n_split, pr.gy), block(64 * pr.p.wpg), cgrid(pr.n_qt, pr.a.hq);
-  hipLaunchKernelGGL((prefill_kernel<T, D, XP_PREFILL_NQ, XP_PREFILL_MAXW>), grid, block, 0, s, pr.a);
+  if (two_key_sets(pr, long(grid.x) * grid.y))
+    hipLaunchKernelGGL((prefill_kernel<T, D, XP_PREFILL_NQ, 4, 2>), grid, dim3(2 * block.x), 0, s, pr.a);
+  else
+    hipLaunchKernelGGL((prefill_kernel<T, D, XP_PREFILL_NQ, XP_PREFILL_MAXW, 1>), grid, block, 0, s, pr.a);
   if (pr.p.n_split > 1) hipLaunchKernelGGL((prefill_combine_kernel<T, D>), cgrid, dim3(256), 0, s, pr.a);
 }
 
@@ -695,8 +762,12 @@ void launch_group(const Prepared* pr, int n, hipStream_t s) {
     g.cgx[k] = pr[k].n_qt;
     g.cstart[k + 1] = g.cstart[k] + (sk ? pr[k].n_qt * pr[k].a.hq : 0);
   }
-  hipLaunchKernelGGL((prefill_group_kernel<T, D, XP_PREFILL_NQ, XP_PREFILL_MAXW>), dim3(g.start[n]),
-                     dim3(64 * pr[0].p.wpg), 0, s, g);
+  if (two_key_sets(pr[0], g.start[n]))
+    hipLaunchKernelGGL((prefill_group_kernel<T, D, XP_PREFILL_NQ, 4, 2>), dim3(g.start[n]), dim3(128 * pr[0].p.wpg), 0,
+                       s, g);
+  else
+    hipLaunchKernelGGL((prefill_group_kernel<T, D, XP_PREFILL_NQ, XP_PREFILL_MAXW, 1>), dim3(g.start[n]),
+                       dim3(64 * pr[0].p.wpg), 0, s, g);
   if (split) hipLaunchKernelGGL((prefill_group_combine_kernel<T, D>), dim3(g.cstart[n]), dim3(256), 0, s, g);
 }
 

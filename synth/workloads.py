@@ -367,6 +367,15 @@ PARITY_WORKLOADS = {
     "P4": Workload("P4", 104, "bf16", 1024, 16, 2, 128, 2048, n_decode=2, ctx=("list", [37, 2500]),
                    chunk_len=320, prior_len=2000, sp_degree=2, sp_rank=1,
                    description="small bf16 layer, 2000 prior keys, SP2 rank 1"),
+    # the 8B head layout (G = 4 on 8 kv heads): grids of at most one workgroup per CU
+    # whose work units span 16 or more key blocks, the case where a workgroup holds
+    # two waves per query head; ragged chunk, prior not a multiple of the 32-key block
+    "P5": Workload("P5", 105, "bf16", 512, 32, 8, 128, 1024, n_decode=0, ctx=("fixed", 0),
+                   chunk_len=900, prior_len=300, description="prefill only, 8B heads, 900 after 300"),
+    # the same with the key range split three ways (19-block units: odd, so the two
+    # halves of each unit differ in length) and merged
+    "P6": Workload("P6", 106, "bf16", 512, 32, 8, 128, 1024, n_decode=0, ctx=("fixed", 0),
+                   chunk_len=300, prior_len=1500, description="prefill only, 8B heads, 300 after 1500"),
     # decode only
     "E1": Workload("E1", 111, "bf16", 512, 8, 2, 128, 1024, n_decode=9, ctx=("uniform", 1, 2000),
                    chunk_len=0, prior_len=0, description="decode only"),

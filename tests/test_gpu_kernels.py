@@ -264,7 +264,7 @@ def test_decode_attention(name, pps):
         assert rel_fro(got[i], ref[i]) < 2 * ATTN_TOL[dt], i
 
 
-@pytest.mark.parametrize("name", ["P1", "P2", "P3", "P4", "E2", "C1", "E4"])
+@pytest.mark.parametrize("name", ["P1", "P2", "P3", "P4", "P5", "P6", "E2", "C1", "E4"])
 def test_prefill_attention(name):
     inst = make_instance(get_workload(name))
     wl, dt = inst.wl, inst.wl.dtype

@@ -21,7 +21,7 @@ from tests.helpers import oracle_kwargs, rel_fro
 
 pytestmark = pytest.mark.gpu
 
-SMALL = ["P1", "P2", "P3", "P4", "E1", "E2", "E3", "E4", "C1"]
+SMALL = ["P1", "P2", "P3", "P4", "P5", "P6", "E1", "E2", "E3", "E4", "C1"]
 _CTX = {}
 
 
