@@ -53,6 +53,9 @@ def parse():
                    help="decode CUs of the concurrent split attention the estimator models")
     p.add_argument("--estimator-batches", type=int, default=200)
     p.add_argument("--estimator-out", default=None, help="write every profiled and evaluated batch here (JSON)")
+    p.add_argument("--stack", type=int, default=0,
+                   help="run the workload's batch through this many layers (each with its own weights and KV "
+                        "pool) eagerly and as piecewise graph launches, instead of the layer benchmark")
     p.add_argument("--probe", default=None,
                    help="internal: time one split-attention mode in this fresh process ('rule' = the pages' "
                         "decode-CU calibration, or a decode CU count) and print it as one JSON line")
@@ -292,6 +295,58 @@ def multi_chunk_mode(args, X, torch, timer):
     ctx.close()
 
 
+def stack_mode(args, X, torch):
+    """One batch through a stack of layers (xp_stack_forward), eager and as piecewise graph
+    launches (xp_stack_graph_create: the shared-linear segments in graphs, the attention
+    region eager between them, ConfluxServe §6.1 Fig. 10).  Reports GPU time per step and
+    per layer, and the host time to enqueue a step."""
+    from synth import get_workload, make_stack_instance
+    from synth.device import make_stack_step
+    wl = get_workload(args.workload)
+    t0 = time.time()
+    sinst = make_stack_instance(wl, args.stack)
+    decode_cus = args.decode_cus or 0
+    ctx = X.Ctx(0, decode_cus, 0)
+    step = make_stack_step(sinst, ctx)
+    s = torch.cuda.current_stream()
+    log(f"[bench] {wl.name} x {args.stack} layers: {wl.description}; inputs ready in {time.time() - t0:.1f} s")
+    graph = step.capture(s)
+    res = {}
+    for name, fn in (("eager", lambda: step.run(s)), ("graph", lambda: graph.launch(s))):
+        t_warm = time.perf_counter()
+        while time.perf_counter() - t_warm < 0.2:
+            fn()
+            torch.cuda.synchronize()
+        for _ in range(args.warmup):
+            fn()
+        torch.cuda.synchronize()
+        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t1 = time.perf_counter()
+        ev0.record()
+        for _ in range(args.steps):
+            fn()
+        enq = time.perf_counter() - t1
+        ev1.record()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t1
+        us = ev0.elapsed_time(ev1) / args.steps * 1e3
+        res[name] = {"us_per_step": round(us, 1), "us_per_layer": round(us / args.stack, 1),
+                     "host_enqueue_us_per_step": round(enq / args.steps * 1e6, 1),
+                     "tokens_per_s": round(wl.n_rows * args.steps / wall, 1)}
+        log(f"[bench] {name}: {json.dumps(res[name])}")
+    assert step.status() == 0
+    graph.close()
+    line = {"metric": METRIC, "value": res["graph"]["tokens_per_s"], "unit": "tokens/s", "n_gpus": 1,
+            "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(res["graph"]["us_per_step"] / 1e3, 4),
+            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": wl.dtype,
+            "data": "synthetic (seeded, random-init weights)",
+            "config": {"workload": f"{wl.name}: {wl.description}", "rows": wl.n_rows, "layers": args.stack,
+                       "decode_cus": decode_cus, "timed": "graph launches (eager alongside)"},
+            "stack": res}
+    print(json.dumps(line), flush=True)
+    ctx.close()
+
+
 def estimator_mode(args, X, torch, timer):
     """Fit the latency model (ConfluxServe §6.2, App. D) from isolated profiles of this
     build's kernels, calibrate alpha and beta on heterogeneous layer steps, then report
@@ -470,6 +525,8 @@ def main():
     torch.cuda.set_stream(torch.cuda.Stream())
     if args.estimator:
         return estimator_mode(args, X, torch, Timer(torch))
+    if args.stack > 0:
+        return stack_mode(args, X, torch)
     from synth import MULTI_CHUNK_WORKLOADS
     if args.workload in MULTI_CHUNK_WORKLOADS:
         return multi_chunk_mode(args, X, torch, Timer(torch))

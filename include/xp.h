@@ -237,6 +237,40 @@ xp_status xp_layer_forward_chunks(xp_ctx* ctx, const xp_layer_shape* shape, cons
                                   const xp_kv_pages* kv, float* out, void* workspace, size_t workspace_bytes,
                                   void* stream);
 
+/* A stack of layer steps over one batch ([CS] §4 Fig. 7 layer after layer; §7 and
+ * Fig. 7 on capturing the shared-linear segments in a graph): n_layers >= 1, sp_degree
+ * 1, at most the descriptor's one prefill chunk.  Layer 0 reads desc->x (T); layer
+ * l > 0 reads layer l-1's [M, H] fp32 output, so the residual stream stays fp32
+ * between layers.  weights[l] and kv[l] are layer l's weights and KV pool; the
+ * descriptor's tables, contexts and positions serve every layer (each layer appends
+ * its new K/V to its own pool).  out: device [M, H] fp32; it carries the residual
+ * stream between layers and holds the last layer's output at the end.  The
+ * workspace is one layer's (xp_layer_workspace_layout), reused by every layer.
+ * XP_EUNSUPPORTED for sp_degree > 1; other errors as xp_layer_forward. */
+xp_status xp_stack_forward(xp_ctx* ctx, const xp_layer_shape* shape, const xp_batch_desc* desc, int32_t n_layers,
+                           const xp_layer_weights* weights, const xp_kv_pages* kv, float* out, void* workspace,
+                           size_t workspace_bytes, void* stream);
+
+/* The same stack with its shared-linear segments captured in HIP graphs ([CS] §6.1
+ * "piecewise graph execution", Fig. 10): segment k holds layer k-1's O projection
+ * and FFN and layer k's RMSNorm, QKV projection, RoPE and appends, so n layers give
+ * n + 1 graphs, and xp_graph_launch replays them with each layer's split attention
+ * region launched eagerly in between, in the context's mode (serialized, unmasked
+ * or CU-partitioned).  Capture happens on `stream` (not the null stream) and
+ * launches nothing.  The graphs hold the pointers and launch shapes of this call:
+ * the caller keeps every buffer alive and may change their contents between
+ * launches (x, decode contexts, table entries) but not the batch shape or the table
+ * widths.  Each launch computes what xp_stack_forward computes.  Launches of one
+ * graph, or of graphs sharing buffers, must not overlap.  XP_EINVAL for an empty
+ * batch; other errors as xp_stack_forward. */
+typedef struct xp_graph xp_graph;
+xp_status xp_stack_graph_create(xp_ctx* ctx, const xp_layer_shape* shape, const xp_batch_desc* desc,
+                                int32_t n_layers, const xp_layer_weights* weights, const xp_kv_pages* kv,
+                                float* out, void* workspace, size_t workspace_bytes, void* stream,
+                                xp_graph** graph);
+xp_status xp_graph_launch(xp_graph* graph, void* stream);
+xp_status xp_graph_destroy(xp_graph* graph);
+
 /* Host-side check of a descriptor against host copies of its tables:
  * every table entry a step will touch lies in [0, n_pages) and no page is
  * named twice.  Returns XP_EPAGE / XP_ESHAPE on failure. */

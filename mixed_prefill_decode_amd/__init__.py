@@ -6,4 +6,4 @@ does not load the library; the first call does, and fails loudly if the library
 has not been built.
 """
 from ._lib import *  # noqa: F401,F403
-from .layer import ChunkedStep, LayerStep, batch_desc, layer_shape, layer_weights  # noqa: F401
+from .layer import ChunkedStep, LayerStep, StackStep, batch_desc, layer_shape, layer_weights  # noqa: F401

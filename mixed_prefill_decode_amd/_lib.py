@@ -17,6 +17,8 @@ __all__ = ["XpError", "lib", "XP_F32", "XP_BF16", "XP_EPI_F32", "XP_EPI_ADD_T", 
            "WsLayout", "LatencyModel", "Ctx", "EXPORTED", "Chunk", "chunk_array",
            "xp_ctx_create", "xp_layer_workspace_layout", "xp_layer_forward", "xp_validate_batch",
            "xp_layer_workspace_layout_chunks", "xp_layer_forward_chunks", "xp_validate_chunks",
+           "xp_stack_forward", "xp_stack_graph_create", "xp_graph_launch", "xp_graph_destroy", "Graph",
+           "weights_array", "pools_array",
            "xp_layer_read_status", "xp_rmsnorm", "xp_gemm_workspace_size", "xp_gemm_tile", "xp_gemm", "xp_kv_append",
            "xp_kv_gather",
            "xp_decode_workspace_size", "xp_decode_attention", "xp_prefill_workspace_size", "xp_prefill_attention",
@@ -38,6 +40,7 @@ EXPORTED = ["xp_last_error", "xp_build_info", "xp_ctx_create", "xp_ctx_destroy",
             "xp_ctx_streams",
             "xp_layer_workspace_layout", "xp_layer_forward", "xp_validate_batch", "xp_layer_read_status",
             "xp_layer_workspace_layout_chunks", "xp_layer_forward_chunks", "xp_validate_chunks",
+            "xp_stack_forward", "xp_stack_graph_create", "xp_graph_launch", "xp_graph_destroy",
             "xp_rmsnorm", "xp_gemm_workspace_size", "xp_gemm_tile", "xp_gemm", "xp_kv_append", "xp_kv_gather",
             "xp_decode_workspace_size",
             "xp_decode_attention", "xp_prefill_workspace_size", "xp_prefill_attention", "xp_probe_hw_ids",
@@ -160,6 +163,13 @@ def _declare(L):
                                         C.POINTER(LayerWeights), C.POINTER(KvPages), _vp, _vp, _sz, _vp]),
         "xp_validate_chunks": (S, [C.POINTER(LayerShape), C.POINTER(BatchDesc), _i32, C.POINTER(Chunk), _i32, _vp,
                                    _vp, _vp]),
+        "xp_stack_forward": (S, [_vp, C.POINTER(LayerShape), C.POINTER(BatchDesc), _i32, C.POINTER(LayerWeights),
+                                 C.POINTER(KvPages), _vp, _vp, _sz, _vp]),
+        "xp_stack_graph_create": (S, [_vp, C.POINTER(LayerShape), C.POINTER(BatchDesc), _i32,
+                                      C.POINTER(LayerWeights), C.POINTER(KvPages), _vp, _vp, _sz, _vp,
+                                      C.POINTER(_vp)]),
+        "xp_graph_launch": (S, [_vp, _vp]),
+        "xp_graph_destroy": (S, [_vp]),
         "xp_validate_batch": (S, [C.POINTER(LayerShape), C.POINTER(BatchDesc), _i32, _vp, _vp, _vp]),
         "xp_layer_read_status": (S, [_vp, C.POINTER(WsLayout), _vp, _vp]),
         "xp_rmsnorm": (S, [_i32, _vp, _i32, _vp, _vp, _i32, _i32, _f32, _vp]),
@@ -299,6 +309,68 @@ def xp_layer_forward_chunks(ctx, shape, desc, chunks, weights, kv, out, workspac
     _check(lib().xp_layer_forward_chunks(ctx.handle, C.byref(shape), C.byref(desc), len(chunks), chunks,
                                          C.byref(weights), C.byref(kv), _ptr(out), _ptr(workspace), workspace_bytes,
                                          _stream(stream)))
+
+
+def weights_array(weights):
+    """ctypes array of LayerWeights, one per layer of a stack."""
+    arr = (LayerWeights * len(weights))()
+    for l, w in enumerate(weights):
+        arr[l] = w
+    return arr
+
+
+def pools_array(pools):
+    """ctypes array of KvPages from [(pool tensor, n_pages)], one per layer of a stack."""
+    arr = (KvPages * len(pools))()
+    for l, (p, n) in enumerate(pools):
+        arr[l] = KvPages(_ptr(p), int(n))
+    return arr
+
+
+def xp_stack_forward(ctx, shape, desc, weights, pools, out, workspace, workspace_bytes, stream=None):
+    """``weights``/``pools``: ctypes arrays of one LayerWeights / KvPages per layer."""
+    if len(weights) != len(pools):
+        raise ValueError("one weight set and one pool per layer")
+    _check(lib().xp_stack_forward(ctx.handle, C.byref(shape), C.byref(desc), len(weights), weights, pools,
+                                  _ptr(out), _ptr(workspace), workspace_bytes, _stream(stream)))
+
+
+class Graph:
+    """A captured stack (xp_stack_graph_create); ``launch`` replays it, ``close`` frees it."""
+
+    def __init__(self, handle):
+        self.handle = handle
+
+    def launch(self, stream=None):
+        xp_graph_launch(self, stream)
+
+    def close(self):
+        if self.handle:
+            _check(lib().xp_graph_destroy(self.handle))
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def xp_stack_graph_create(ctx, shape, desc, weights, pools, out, workspace, workspace_bytes, stream) -> Graph:
+    if len(weights) != len(pools):
+        raise ValueError("one weight set and one pool per layer")
+    h = _vp()
+    _check(lib().xp_stack_graph_create(ctx.handle, C.byref(shape), C.byref(desc), len(weights), weights, pools,
+                                       _ptr(out), _ptr(workspace), workspace_bytes, _stream(stream), C.byref(h)))
+    return Graph(h)
+
+
+def xp_graph_launch(graph, stream=None):
+    _check(lib().xp_graph_launch(graph.handle, _stream(stream)))
+
+
+def xp_graph_destroy(graph):
+    graph.close()
 
 
 def chunk_array(chunks):

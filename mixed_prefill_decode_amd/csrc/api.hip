@@ -12,6 +12,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <memory>
 #include <string>
 #include <vector>
 
@@ -438,53 +439,87 @@ xp_status check_weights(const xp_layer_weights* w, const xp_kv_pages* kv) {
   return XP_OK;
 }
 
-// The step of ConfluxServe §4 (Fig. 7) over rows [chunk rows of every chunk || decode]:
-// co-batched RMSNorm + QKV, RoPE and appends, the split attention region (every chunk's
-// prefill attention in turn on the prefill side), co-batched O projection and FFN.
-xp_status run_layer(xp_ctx* ctx, const xp_layer_shape* sh, const xp_batch_desc* d, const std::vector<ChunkRun>& ch,
-                    int rows_pre, const xp_layer_weights* w, const xp_kv_pages* kv, float* out,
-                    const xp_ws_layout& L, void* workspace, hipStream_t s) {
+// The step of ConfluxServe §4 (Fig. 7) over rows [chunk rows of every chunk || decode],
+// in the three pieces a stack runs separately (§6.1, Fig. 10: graph-captured shared-linear
+// segments around an eager attention region):
+//   pre:    co-batched RMSNorm + QKV, RoPE and the appends;
+//   attend: the split attention region (every chunk's prefill attention in turn on the
+//           prefill side; serialized on `s` when split is false or the context is);
+//   post:   co-batched O projection + residual, RMSNorm, gate/up + SwiGLU, down + residual.
+// The layer input is `x`: [M, H] of the workload type, or fp32 when x_f32 (a stack's
+// residual stream); the first RMSNorm and the O projection's residual are its only
+// readers, so `out` may alias an fp32 `x`.  Every member is held by value, so a run
+// outlives the caller's structs (a captured stack keeps its runs for later replays).
+struct LayerRun {
+  xp_ctx* ctx;
+  xp_layer_shape shape;
+  xp_batch_desc desc;
+  std::vector<ChunkRun> ch;
+  int rows_pre;
+  xp_layer_weights weights;
+  xp_kv_pages pool;
+  float* out;
+  xp_ws_layout L;
+  void* workspace;
+  const void* x;
+  bool x_f32;
+
+  xp_status pre(hipStream_t s) const;
+  xp_status attend(hipStream_t s, bool split) const;
+  xp_status post(hipStream_t s) const;
+};
+
+xp_status LayerRun::pre(hipStream_t s) const {
   xp_status st;
-  const int dt = sh->dtype;
-  const size_t eb = dtype_bytes(dt);
-  const int H = sh->hidden, Hq = sh->n_q_heads, Hkv = sh->n_kv_heads, D = sh->head_dim, F = sh->ffn_dim;
-  const int P = d->sp_degree, r = d->sp_rank, hq_loc = Hq / P, hkv_loc = Hkv / P;
-  const int n_d = d->n_decode, M = rows_pre + n_d;
+  const xp_layer_shape* sh = &shape;
+  const xp_batch_desc* d = &desc;
+  const int dt = sh->dtype, H = sh->hidden, Hq = sh->n_q_heads, Hkv = sh->n_kv_heads, D = sh->head_dim;
+  const int P = d->sp_degree, r = d->sp_rank, n_d = d->n_decode, M = rows_pre + n_d;
   const int ldq = (Hq + 2 * Hkv) * D;
   char* ws = static_cast<char*>(workspace);
   uint32_t* status = reinterpret_cast<uint32_t*>(ws + L.status);
-  char* hn = ws + L.hn;
   float* qkv = reinterpret_cast<float*>(ws + L.qkv);
   char* attn = ws + L.attn;
-  float* h1 = reinterpret_cast<float*>(ws + L.h1);
-  char* act = ws + L.act;
-  void* gp = ws + L.gemm_part;                  // GEMM K-split partials
-  const size_t gpb = L.h1 - L.gemm_part;
-  const size_t attn_row = size_t(Hq) * D * eb;
+  const size_t attn_row = size_t(Hq) * D * dtype_bytes(dt);
 
   // shared linear region (1): RMSNorm + QKV over all M rows
-  if ((st = launch_rmsnorm(dt, d->x, 0, w->g_attn, hn, M, H, sh->rms_eps, status, s))) return st;
-  if (M > 0 && (st = launch_gemm(dt, XP_EPI_F32, hn, w->w_qkv, nullptr, nullptr, qkv, M, ldq, H, gp, gpb, s)))
+  if ((st = launch_rmsnorm(dt, x, x_f32 ? 1 : 0, weights.g_attn, ws + L.hn, M, H, sh->rms_eps, status, s))) return st;
+  if (M > 0 && (st = launch_gemm(dt, XP_EPI_F32, ws + L.hn, weights.w_qkv, nullptr, nullptr, qkv, M, ldq, H,
+                                 ws + L.gemm_part, L.h1 - L.gemm_part, s)))
     return st;
   // RoPE + appends (+ the peer stand-ins): one launch per chunk, the decodes with the last
   // (their rows follow it in x) or alone when there is no chunk
-  auto post = [&](const ChunkRun* c, int nd) {
+  auto post_qkv = [&](const ChunkRun* c, int nd) {
     const int row0 = c ? c->row0 : rows_pre;
     PostQkvArgs pa{qkv + size_t(row0) * ldq, c ? c->n_local : 0, nd, Hq, Hkv, D, sh->page_size, sh->rope_base,
                    d->dec_ctx, d->dec_pages, d->dec_max_blocks, c ? c->prior : 0, c ? c->len : 0, P, r,
                    c ? c->off : 0, c ? c->pages : nullptr, c ? c->max_blocks : 0, c ? c->peer_qkv_in : nullptr,
-                   c ? c->peer_qkv_out : nullptr, c ? c->peer_attn_in : nullptr, kv->pool, kv->n_pages,
+                   c ? c->peer_qkv_out : nullptr, c ? c->peer_attn_in : nullptr, pool.pool, pool.n_pages,
                    ws + L.q_dec, c ? ws + L.q_pre + c->q_off : nullptr, attn + size_t(row0) * attn_row, status};
     return launch_post_qkv(dt, pa, s);
   };
   if (ch.empty()) {
-    if ((st = post(nullptr, n_d))) return st;
+    if ((st = post_qkv(nullptr, n_d))) return st;
   } else {
     for (size_t j = 0; j < ch.size(); ++j)
-      if ((st = post(&ch[j], j + 1 == ch.size() ? n_d : 0))) return st;
+      if ((st = post_qkv(&ch[j], j + 1 == ch.size() ? n_d : 0))) return st;
   }
+  return XP_OK;
+}
 
-  // split attention region
+xp_status LayerRun::attend(hipStream_t s, bool split) const {
+  xp_status st;
+  const xp_layer_shape* sh = &shape;
+  const xp_batch_desc* d = &desc;
+  const xp_kv_pages* kv = &pool;
+  const int dt = sh->dtype, Hq = sh->n_q_heads, Hkv = sh->n_kv_heads, D = sh->head_dim;
+  const int P = d->sp_degree, r = d->sp_rank, hq_loc = Hq / P, hkv_loc = Hkv / P, n_d = d->n_decode;
+  const size_t eb = dtype_bytes(dt);
+  char* ws = static_cast<char*>(workspace);
+  uint32_t* status = reinterpret_cast<uint32_t*>(ws + L.status);
+  char* attn = ws + L.attn;
+  const size_t attn_row = size_t(Hq) * D * eb;
+
   auto decode = [&](hipStream_t q) {
     return launch_decode(dt, ws + L.q_dec, kv->pool, kv->n_pages, sh->page_size, d->dec_pages, d->dec_max_blocks,
                          d->dec_ctx, n_d, Hq, Hkv, D, attn + size_t(rows_pre) * attn_row, Hq * D,
@@ -511,7 +546,7 @@ xp_status run_layer(xp_ctx* ctx, const xp_layer_shape* sh, const xp_batch_desc* 
     return launch_prefill_group(dt, kv->pool, kv->n_pages, sh->page_size, hq_loc, hkv_loc, D, int(jobs.size()),
                                 jobs.data(), status, prefill_cus(ctx), q);
   };
-  const bool concurrent = ctx->s_dec && n_d > 0 && !ch.empty();
+  const bool concurrent = split && ctx->s_dec && n_d > 0 && !ch.empty();
   if (!concurrent) {
     if ((st = decode(s))) return st;
     if ((st = prefill(s))) return st;
@@ -526,17 +561,81 @@ xp_status run_layer(xp_ctx* ctx, const xp_layer_shape* sh, const xp_batch_desc* 
     XP_HIP_TRY(hipStreamWaitEvent(s, ctx->e_dec, 0));
     XP_HIP_TRY(hipStreamWaitEvent(s, ctx->e_pre, 0));
   }
-  if (M == 0) return XP_OK;
-
-  // shared linear region (2): O projection + residual, RMSNorm, gate/up + SwiGLU, down + residual
-  if ((st = launch_gemm(dt, XP_EPI_ADD_T, attn, w->w_o, nullptr, d->x, h1, M, H, Hq * D, gp, gpb, s))) return st;
-  if ((st = launch_rmsnorm(dt, h1, 1, w->g_ffn, hn, M, H, sh->rms_eps, nullptr, s))) return st;
-  if ((st = launch_gemm(dt, XP_EPI_SWIGLU, hn, w->w_gate, w->w_up, nullptr, act, M, F, H, gp, gpb, s))) return st;
-  if ((st = launch_gemm(dt, XP_EPI_ADD_F32, act, w->w_down, nullptr, h1, out, M, H, F, gp, gpb, s))) return st;
   return XP_OK;
 }
 
+xp_status LayerRun::post(hipStream_t s) const {
+  xp_status st;
+  const int dt = shape.dtype, H = shape.hidden, HqD = shape.n_q_heads * shape.head_dim, F = shape.ffn_dim;
+  const int M = rows_pre + desc.n_decode;
+  if (M == 0) return XP_OK;
+  char* ws = static_cast<char*>(workspace);
+  float* h1 = reinterpret_cast<float*>(ws + L.h1);
+  void* gp = ws + L.gemm_part;                  // GEMM K-split partials
+  const size_t gpb = L.h1 - L.gemm_part;
+  const xp_layer_weights* w = &weights;
+
+  // shared linear region (2): O projection + residual, RMSNorm, gate/up + SwiGLU, down + residual
+  if ((st = launch_gemm(dt, x_f32 ? XP_EPI_ADD_F32 : XP_EPI_ADD_T, ws + L.attn, w->w_o, nullptr, x, h1, M, H, HqD,
+                        gp, gpb, s)))
+    return st;
+  if ((st = launch_rmsnorm(dt, h1, 1, w->g_ffn, ws + L.hn, M, H, shape.rms_eps, nullptr, s))) return st;
+  if ((st = launch_gemm(dt, XP_EPI_SWIGLU, ws + L.hn, w->w_gate, w->w_up, nullptr, ws + L.act, M, F, H, gp, gpb, s)))
+    return st;
+  if ((st = launch_gemm(dt, XP_EPI_ADD_F32, ws + L.act, w->w_down, nullptr, h1, out, M, H, F, gp, gpb, s))) return st;
+  return XP_OK;
+}
+
+xp_status run_layer(const LayerRun& run, hipStream_t s) {
+  xp_status st;
+  if ((st = run.pre(s)) || (st = run.attend(s, true)) || (st = run.post(s))) return st;
+  return XP_OK;
+}
+
+
+// A layer stack: sp_degree 1, a weight set and a pool per layer.
+xp_status check_stack(const xp_layer_shape* sh, const xp_batch_desc* d, int n_layers, const xp_layer_weights* w,
+                      const xp_kv_pages* kv) {
+  xp_status st = check_shape(sh);
+  if (st) return st;
+  if ((st = check_desc(sh, d))) return st;
+  if (d->sp_degree != 1) return fail(XP_EUNSUPPORTED, "layer stack: sp_degree %d (supported: 1)", d->sp_degree);
+  if (n_layers < 1 || !w || !kv) return fail(XP_EINVAL, "layer stack: %d layers, weights %p, pools %p", n_layers,
+                                             static_cast<const void*>(w), static_cast<const void*>(kv));
+  for (int l = 0; l < n_layers; ++l)
+    if ((st = check_weights(w + l, kv + l))) return st;
+  return XP_OK;
+}
+
+// The runs of a stack, layer after layer over one batch: layer 0 reads desc->x; every
+// layer writes `out`, which the next one reads as its fp32 input (the residual stream).
+std::vector<LayerRun> stack_runs(xp_ctx* ctx, const xp_layer_shape* sh, const xp_batch_desc* d, int n_layers,
+                                 const xp_layer_weights* w, const xp_kv_pages* kv, float* out, const xp_ws_layout& L,
+                                 void* workspace) {
+  std::vector<ChunkRun> ch;
+  if (d->chunk_len > 0)
+    ch.push_back(ChunkRun{d->chunk_len, d->prior_len, 0, d->n_prefill_local, 0, d->pre_pages, d->pre_max_blocks,
+                          nullptr, nullptr, nullptr, nullptr, 0});
+  std::vector<LayerRun> runs;
+  for (int l = 0; l < n_layers; ++l)
+    runs.push_back(LayerRun{ctx, *sh, *d, ch, d->n_prefill_local, w[l], kv[l], out, L, workspace,
+                            l == 0 ? d->x : static_cast<const void*>(out), l > 0});
+  return runs;
+}
+
 }  // namespace
+
+// A captured stack: segment k holds layer k-1's post piece (k > 0) and layer k's pre
+// piece (k < n), so n layers give n + 1 graphs around n eager attention regions.
+struct xp_graph {
+  std::vector<LayerRun> runs;
+  std::vector<hipGraph_t> graphs;
+  std::vector<hipGraphExec_t> execs;
+  ~xp_graph() {
+    for (hipGraphExec_t e : execs) (void)hipGraphExecDestroy(e);
+    for (hipGraph_t g : graphs) (void)hipGraphDestroy(g);
+  }
+};
 
 extern "C" {
 
@@ -556,7 +655,8 @@ xp_status xp_layer_forward(xp_ctx* ctx, const xp_layer_shape* sh, const xp_batch
   if (d->chunk_len > 0)
     ch.push_back(ChunkRun{d->chunk_len, d->prior_len, d->local_row_offset, d->n_prefill_local, 0, d->pre_pages,
                           d->pre_max_blocks, d->peer_qkv_in, d->peer_qkv_out, d->peer_attn_in, d->peer_attn_out, 0});
-  return run_layer(ctx, sh, d, ch, d->n_prefill_local, w, kv, out, L, workspace, static_cast<hipStream_t>(stream));
+  return run_layer(LayerRun{ctx, *sh, *d, ch, d->n_prefill_local, *w, *kv, out, L, workspace, d->x, false},
+                   static_cast<hipStream_t>(stream));
 }
 
 xp_status xp_layer_workspace_layout_chunks(const xp_ctx* ctx, const xp_layer_shape* sh, const xp_batch_desc* d,
@@ -592,7 +692,76 @@ xp_status xp_layer_forward_chunks(xp_ctx* ctx, const xp_layer_shape* sh, const x
     q_off += size_t(c.chunk_len) * q_row;
   }
   if (rows + d->n_decode > 0 && !out) return fail(XP_EINVAL, "null out");
-  return run_layer(ctx, sh, d, ch, rows, w, kv, out, L, workspace, static_cast<hipStream_t>(stream));
+  return run_layer(LayerRun{ctx, *sh, *d, ch, rows, *w, *kv, out, L, workspace, d->x, false},
+                   static_cast<hipStream_t>(stream));
+}
+
+xp_status xp_stack_forward(xp_ctx* ctx, const xp_layer_shape* sh, const xp_batch_desc* d, int32_t n_layers,
+                           const xp_layer_weights* w, const xp_kv_pages* kv, float* out, void* workspace,
+                           size_t workspace_bytes, void* stream) {
+  if (!ctx) return fail(XP_EINVAL, "null ctx");
+  xp_status st = check_stack(sh, d, n_layers, w, kv);
+  if (st) return st;
+  if (rows_of(d) > 0 && !out) return fail(XP_EINVAL, "null out");
+  const xp_ws_layout L = make_layout(ctx, sh, d);
+  if (!workspace || workspace_bytes < L.total)
+    return fail(XP_EWORKSPACE, "workspace of %zu bytes < %zu required", workspace_bytes, L.total);
+  for (const LayerRun& run : stack_runs(ctx, sh, d, n_layers, w, kv, out, L, workspace))
+    if ((st = run_layer(run, static_cast<hipStream_t>(stream)))) return st;
+  return XP_OK;
+}
+
+xp_status xp_stack_graph_create(xp_ctx* ctx, const xp_layer_shape* sh, const xp_batch_desc* d, int32_t n_layers,
+                                const xp_layer_weights* w, const xp_kv_pages* kv, float* out, void* workspace,
+                                size_t workspace_bytes, void* stream, xp_graph** graph) {
+  if (!graph) return fail(XP_EINVAL, "null graph out");
+  *graph = nullptr;
+  if (!ctx) return fail(XP_EINVAL, "null ctx");
+  if (!stream) return fail(XP_EINVAL, "graph capture needs a stream other than the null stream");
+  xp_status st = check_stack(sh, d, n_layers, w, kv);
+  if (st) return st;
+  if (rows_of(d) == 0) return fail(XP_EINVAL, "graph of an empty batch");
+  if (!out) return fail(XP_EINVAL, "null out");
+  const xp_ws_layout L = make_layout(ctx, sh, d);
+  if (!workspace || workspace_bytes < L.total)
+    return fail(XP_EWORKSPACE, "workspace of %zu bytes < %zu required", workspace_bytes, L.total);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  std::unique_ptr<xp_graph> g(new xp_graph);
+  g->runs = stack_runs(ctx, sh, d, n_layers, w, kv, out, L, workspace);
+  for (int k = 0; k <= n_layers; ++k) {
+    XP_HIP_TRY(hipStreamBeginCapture(s, hipStreamCaptureModeThreadLocal));
+    st = k > 0 ? g->runs[k - 1].post(s) : XP_OK;
+    if (!st && k < n_layers) st = g->runs[k].pre(s);
+    hipGraph_t gr = nullptr;
+    const hipError_t e = hipStreamEndCapture(s, &gr);
+    if (gr) g->graphs.push_back(gr);
+    if (st) return st;
+    if (e != hipSuccess || !gr) return fail(XP_EHIP, "hipStreamEndCapture: %s", hipGetErrorString(e));
+    hipGraphExec_t x = nullptr;
+    XP_HIP_TRY(hipGraphInstantiate(&x, gr, nullptr, nullptr, 0));
+    g->execs.push_back(x);
+  }
+  *graph = g.release();
+  return XP_OK;
+}
+
+xp_status xp_graph_launch(xp_graph* graph, void* stream) {
+  if (!graph) return fail(XP_EINVAL, "null graph");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const size_t n = graph->runs.size();
+  for (size_t k = 0; k <= n; ++k) {
+    XP_HIP_TRY(hipGraphLaunch(graph->execs[k], s));
+    if (k < n) {
+      const xp_status st = graph->runs[k].attend(s, true);
+      if (st) return st;
+    }
+  }
+  return XP_OK;
+}
+
+xp_status xp_graph_destroy(xp_graph* graph) {
+  delete graph;
+  return XP_OK;
 }
 
 // ---- kernel-level entry points ------------------------------------------------

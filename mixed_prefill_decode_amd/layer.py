@@ -8,7 +8,7 @@ from __future__ import annotations
 
 from . import _lib as X
 
-__all__ = ["layer_shape", "layer_weights", "batch_desc", "LayerStep", "ChunkedStep"]
+__all__ = ["layer_shape", "layer_weights", "batch_desc", "LayerStep", "ChunkedStep", "StackStep"]
 
 
 def layer_shape(*, hidden, n_q_heads, n_kv_heads, head_dim, ffn_dim, page_size=16, rms_eps=1e-5,
@@ -87,6 +87,37 @@ class ChunkedStep:
         X.xp_layer_forward_chunks(self.ctx, self.shape, self.desc, self.chunks, self.weights, self.kv, self.out,
                                   self.workspace, self.layout.total, stream)
         return self.out
+
+    def status(self, stream=None) -> int:
+        return X.xp_layer_read_status(self.workspace, self.layout, stream)
+
+
+class StackStep:
+    """One batch through a stack of layers (xp_stack_forward): a weight set and a KV pool
+    per layer (``pools`` = [(pool tensor, n_pages)]), one layer's workspace and the fp32
+    output that carries the residual stream between layers.  ``capture`` records the
+    shared-linear segments in HIP graphs (xp_stack_graph_create) for ``Graph.launch``."""
+
+    def __init__(self, ctx: X.Ctx, shape: X.LayerShape, desc: X.BatchDesc, weights, pools, keep=()):
+        import torch
+        self.ctx, self.shape, self.desc = ctx, shape, desc
+        self.weights = X.weights_array(weights)
+        self.pools = X.pools_array(pools)
+        self.layout = X.xp_layer_workspace_layout(ctx, shape, desc)
+        dev = torch.device("cuda", ctx.device)
+        self.workspace = torch.empty(self.layout.total, dtype=torch.uint8, device=dev)
+        M = desc.n_prefill_local + desc.n_decode
+        self.out = torch.empty((M, shape.hidden), dtype=torch.float32, device=dev)
+        self._keep = tuple(p for p, _ in pools) + tuple(keep)
+
+    def run(self, stream=None):
+        X.xp_stack_forward(self.ctx, self.shape, self.desc, self.weights, self.pools, self.out, self.workspace,
+                           self.layout.total, stream)
+        return self.out
+
+    def capture(self, stream) -> X.Graph:
+        return X.xp_stack_graph_create(self.ctx, self.shape, self.desc, self.weights, self.pools, self.out,
+                                       self.workspace, self.layout.total, stream)
 
     def status(self, stream=None) -> int:
         return X.xp_layer_read_status(self.workspace, self.layout, stream)

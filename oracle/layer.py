@@ -35,7 +35,7 @@ from .numerics import encode, round_f64, to_f64
 
 __all__ = [
     "rmsnorm", "rope", "silu", "attend", "PagedKV", "decode_attention",
-    "prefill_attention", "layer_forward", "layer_forward_chunks", "causal_pair_count",
+    "prefill_attention", "layer_forward", "layer_forward_chunks", "stack_forward", "causal_pair_count",
 ]
 
 
@@ -183,7 +183,7 @@ def prefill_attention(q: np.ndarray, kv: PagedKV, pre_pages: np.ndarray, prior_l
 def layer_forward(*, hidden, n_q_heads, n_kv_heads, head_dim, ffn_dim, page_size, rms_eps,
                   rope_base, dtype, x, weights, dec_ctx, dec_pages, chunk_len, prior_len,
                   sp_degree, sp_rank, n_prefill_local, local_row_offset, pre_pages,
-                  peer_qkv_in, peer_attn_in, pool, rows=None, peer_rows=None) -> dict:
+                  peer_qkv_in, peer_attn_in, pool, rows=None, peer_rows=None, x_dtype=None) -> dict:
     """One layer step on one GPU, rows ordered [prefill-local || decode].
 
     Steps (ConfluxServe §4, Fig. 7: co-batched QKV, split attention, co-batched O-proj and
@@ -196,7 +196,8 @@ def layer_forward(*, hidden, n_q_heads, n_kv_heads, head_dim, ffn_dim, page_size
       5. h1 = x + attn W_o^T;  a = silu(RMSNorm(h1) W_gate^T) * (RMSNorm(h1) W_up^T)
       6. out = h1 + a W_down^T
     ``rows`` limits steps 3-6 to a subset of output rows; ``peer_rows`` limits the exported
-    peer attention rows.  Everything else is computed in full.
+    peer attention rows.  Everything else is computed in full.  ``x`` is in the workload's
+    storage format, or in ``x_dtype``'s ("f32": a stack's residual stream).
     """
     H, Hq, Hkv, d, S = hidden, n_q_heads, n_kv_heads, head_dim, page_size
     G = Hq // Hkv
@@ -206,7 +207,7 @@ def layer_forward(*, hidden, n_q_heads, n_kv_heads, head_dim, ffn_dim, page_size
     n_d = len(dec_ctx)
     M = n_pl + n_d
     W = {k: to_f64(v, dtype) for k, v in weights.items()}
-    x64 = to_f64(x, dtype).reshape(M, H)
+    x64 = to_f64(x, x_dtype or dtype).reshape(M, H)
     kv = PagedKV(pool, dtype, S, d)
 
     # 1. norm + co-batched QKV projection over all M rows
@@ -350,6 +351,23 @@ def layer_forward_chunks(*, hidden, n_q_heads, n_kv_heads, head_dim, ffn_dim, pa
         act[rows] = silu(hn2 @ W["w_gate"].T) * (hn2 @ W["w_up"].T)
         out[rows] = h1[rows] + act[rows] @ W["w_down"].T
     return dict(out=out, h1=h1, act=act, attn=attn, q=q, k=k, v=v, positions=pos, kv=kv, rows=rows)
+
+
+def stack_forward(*, layers, x, dtype, **step) -> dict:
+    """A stack of layer steps over one batch (ConfluxServe §4 Fig. 7 layer after layer),
+    sp_degree 1.  ``layers``: per layer {"weights", "pool"}; every other argument is
+    layer_forward's and serves every layer (tables, contexts, positions).  Layer 0 reads
+    ``x`` in the workload's format; layer l > 0 reads layer l-1's output stored as
+    float32 (the residual stream between layers is kept in fp32), so the only rounding
+    between layers is that store.  Returns the last layer's output and every layer's
+    result."""
+    results = []
+    cur, cur_dtype = x, None
+    for layer in layers:
+        r = layer_forward(x=cur, dtype=dtype, weights=layer["weights"], pool=layer["pool"], x_dtype=cur_dtype, **step)
+        results.append(r)
+        cur, cur_dtype = r["out"].astype(np.float32), "f32"
+    return dict(out=results[-1]["out"], layers=results)
 
 
 def _peer_index(t: int, off: int, n_pl: int) -> int:

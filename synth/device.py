@@ -116,3 +116,27 @@ def make_chunked_step(inst, ctx):
                        keep=(x, weights, dec_ctx, dec_pages))
     step.pool, step.x, step.tables, step.dec_ctx, step.dec_pages = pool, x, tables, dec_ctx, dec_pages
     return step
+
+
+def make_stack_step(sinst, ctx):
+    """A StackStep of the package for a layer-stack instance (device copies only)."""
+    import types
+    from mixed_prefill_decode_amd import StackStep, batch_desc, layer_shape, layer_weights
+    base, wl, dt = sinst.base, sinst.wl, sinst.wl.dtype
+    x = to_device(base.x, dt)
+    dec_ctx = to_device(base.dec_ctx, "i32")
+    dec_pages = to_device(base.dec_pages, "i32")
+    pre_pages = to_device(base.pre_pages, "i32")
+    weights = [{k: to_device(v, dt) for k, v in layer["weights"].items()} for layer in sinst.layers]
+    pools = [upload_pool(types.SimpleNamespace(pool=layer["pool"], wl=wl)) for layer in sinst.layers]
+    shape = layer_shape(hidden=wl.hidden, n_q_heads=wl.n_q_heads, n_kv_heads=wl.n_kv_heads,
+                        head_dim=wl.head_dim, ffn_dim=wl.ffn_dim, page_size=wl.page_size, rms_eps=wl.rms_eps,
+                        rope_base=wl.rope_base, dtype=dt)
+    desc = batch_desc(x=x, n_prefill_local=wl.n_prefill_local, n_decode=wl.n_decode, dec_ctx=dec_ctx,
+                      dec_pages=dec_pages if wl.n_decode else None, chunk_len=wl.chunk_len,
+                      prior_len=wl.prior_len, pre_pages=pre_pages if wl.chunk_len else None)
+    step = StackStep(ctx, shape, desc, [layer_weights(w) for w in weights],
+                     [(p, layer["pool"].n_pages) for p, layer in zip(pools, sinst.layers)],
+                     keep=(x, dec_ctx, dec_pages, pre_pages, weights))
+    step.x, step.pool_tensors = x, pools
+    return step

@@ -37,6 +37,7 @@ __all__ = [
     "f32_to_bf16_bits", "bf16_bits_to_f32", "storage_to_f64",
     "waterfill_cases", "make_latency_model", "SchedulerCase", "scheduler_case",
     "MultiChunkWorkload", "MultiChunkInstance", "make_multi_instance", "MULTI_CHUNK_WORKLOADS",
+    "StackInstance", "make_stack_instance",
 ]
 
 TENSOR_IDS = {
@@ -49,8 +50,11 @@ TENSOR_IDS = {
 _KV_DRAW_PAGES = 1024
 
 
-def _rng(seed_id: int, tensor: str) -> np.random.Generator:
-    return np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed_id, TENSOR_IDS[tensor]])))
+def _rng(seed_id: int, tensor: str, layer: int = 0) -> np.random.Generator:
+    """Generator of one tensor; layer l > 0 of a stack draws its own (layer 0 is the
+    single-layer draw)."""
+    key = [seed_id, TENSOR_IDS[tensor]] + ([layer] if layer else [])
+    return np.random.Generator(np.random.PCG64(np.random.SeedSequence(key)))
 
 
 def f32_to_bf16_bits(a: np.ndarray) -> np.ndarray:
@@ -75,8 +79,8 @@ def storage_to_f64(a: np.ndarray, dtype: str) -> np.ndarray:
     return np.asarray(a, dtype=np.float32).astype(np.float64)
 
 
-def _normal(seed_id: int, tensor: str, shape, scale: float, dtype: str) -> np.ndarray:
-    v = _rng(seed_id, tensor).standard_normal(size=int(np.prod(shape)), dtype=np.float32)
+def _normal(seed_id: int, tensor: str, shape, scale: float, dtype: str, layer: int = 0) -> np.ndarray:
+    v = _rng(seed_id, tensor, layer).standard_normal(size=int(np.prod(shape)), dtype=np.float32)
     if scale != 1.0:
         v *= np.float32(scale)
     v = v.reshape(shape)
@@ -303,8 +307,8 @@ def make_instance(wl: Workload, materialize_limit_bytes: int = 4 << 30) -> Insta
     return Instance(wl, x, weights, ctx, dec_pages, pre_pages, pool, peer_qkv_in, peer_attn_in)
 
 
-def _draw_pages(seed_id, tensor, n_pages, row_shape, dt):
-    r = _rng(seed_id, tensor)
+def _draw_pages(seed_id, tensor, n_pages, row_shape, dt, layer=0):
+    r = _rng(seed_id, tensor, layer)
     per = int(np.prod(row_shape))
     out = np.empty((n_pages,) + tuple(row_shape), dtype=np.uint16 if dt == "bf16" else np.float32)
     flat = out.reshape(n_pages, per)
@@ -340,6 +344,9 @@ WORKLOADS = {
     "C4": Workload("C4", 4, "bf16", 4096, 32, 8, 128, 14336, n_decode=128, ctx=("fixed", 32768),
                    chunk_len=0, prior_len=0, kv_bank_pages=16384,
                    description="decode-heavy Llama-3.1-8B layer: 128 decodes at 32768, no prefill"),
+    "D1": Workload("D1", 6, "bf16", 4096, 32, 8, 128, 14336, n_decode=16, ctx=("fixed", 1024),
+                   chunk_len=0, prior_len=0,
+                   description="small Llama-3.1-8B decode step: 16 decodes at 1024, no prefill"),
     "C5": Workload("C5", 5, "bf16", 5120, 64, 8, 128, 25600, n_decode=32,
                    ctx=("lognormal", _LN_MU, _LN_SIGMA, 1, 65536),
                    chunk_len=4096, prior_len=12288, sp_degree=8, sp_rank=0,
@@ -628,3 +635,52 @@ MULTI_CHUNK_WORKLOADS = {
                                description="Llama-3.1-8B layer: 16 decodes at 8192 + four 256-token chunks "
                                            "after 0/2048/4096/8192 cached tokens"),
 }
+
+
+# ---------------------------------------------------------------------------
+# Layer stacks: one batch (x, decode contexts, page tables) through n layers, each
+# with its own weights and its own KV pool laid out by the same tables.
+# ---------------------------------------------------------------------------
+
+@dataclass
+class StackInstance:
+    base: Instance                 # the batch and layer 0 (the single-layer draw)
+    layers: list                   # per layer: {"weights": dict, "pool": PagePool}
+
+    @property
+    def wl(self) -> Workload:
+        return self.base.wl
+
+
+def make_stack_instance(wl: Workload, n_layers: int) -> StackInstance:
+    """Layer 0 is make_instance(wl); layer l > 0 draws its weights and its pool pages
+    from its own generators, with the same valid slots (NaN past each page's cached
+    tokens) and, for banked pools, the same bank indices."""
+    assert wl.sp_degree == 1 and n_layers >= 1
+    base = make_instance(wl)
+    k, dt = wl.seed_id, wl.dtype
+    H, d, F, S = wl.hidden, wl.head_dim, wl.ffn_dim, wl.page_size
+    layers = [{"weights": base.weights, "pool": base.pool}]
+    for l in range(1, n_layers):
+        ws = wl.weight_std
+        w = {
+            "w_qkv": _normal(k, "w_qkv", (wl.qkv_dim, H), ws, dt, l),
+            "w_o": _normal(k, "w_o", (H, wl.n_q_heads * d), ws, dt, l),
+            "w_gate": _normal(k, "w_gate", (F, H), ws, dt, l),
+            "w_up": _normal(k, "w_up", (F, H), ws, dt, l),
+            "w_down": _normal(k, "w_down", (H, F), ws, dt, l),
+            "g_attn": base.weights["g_attn"].copy(),
+            "g_ffn": base.weights["g_ffn"].copy(),
+        }
+        bp = base.pool
+        if bp.bank is not None:
+            bank = _draw_pages(k, "kv", bp.bank.shape[0], bp.row_shape, dt, l)
+            pool = PagePool(bp.n_pages, bp.row_shape, dt, bp.valid_slots, S, d, bank=bank, bank_idx=bp.bank_idx)
+        else:
+            arr = _draw_pages(k, "kv", bp.n_pages, bp.row_shape, dt, l)
+            pool = PagePool(bp.n_pages, bp.row_shape, dt, bp.valid_slots, S, d, array=arr)
+            ids = pool.poisoned_pages()
+            if len(ids):
+                arr[ids] = pool._poison(arr[ids].copy(), ids)
+        layers.append({"weights": w, "pool": pool})
+    return StackInstance(base, layers)

@@ -43,3 +43,13 @@ def chunk_oracle_kwargs(inst, **extra):
               chunks=[(l, c, t) for (l, c), t in zip(wl.chunks, inst.chunk_pages)], pool=inst.pool)
     kw.update(extra)
     return kw
+
+
+def stack_oracle_kwargs(sinst, **extra):
+    """Keyword arguments of ``oracle.layer.stack_forward`` for a drawn stack instance."""
+    kw = oracle_kwargs(sinst.base)
+    for k in ("weights", "pool"):
+        kw.pop(k)
+    kw["layers"] = sinst.layers
+    kw.update(extra)
+    return kw
