@@ -258,9 +258,10 @@ xp_status xp_stack_forward(xp_ctx* ctx, const xp_layer_shape* shape, const xp_ba
  * region launched eagerly in between, in the context's mode (serialized, unmasked
  * or CU-partitioned).  Capture happens on `stream` (not the null stream) and
  * launches nothing.  The graphs hold the pointers and launch shapes of this call:
- * the caller keeps every buffer alive and may change their contents between
- * launches (x, decode contexts, table entries) but not the batch shape or the table
- * widths.  Each launch computes what xp_stack_forward computes.  Launches of one
+ * the caller keeps the context and every buffer alive until xp_graph_destroy, and
+ * may change the buffers' contents between launches (x, decode contexts, table
+ * entries) but not the batch shape or the table widths.  Each launch computes what
+ * xp_stack_forward computes.  Launches of one
  * graph, or of graphs sharing buffers, must not overlap.  XP_EINVAL for an empty
  * batch; other errors as xp_stack_forward. */
 typedef struct xp_graph xp_graph;
