@@ -671,6 +671,18 @@ def main():
         kern["prefill_attn"] = {"us": round(t * 1e6, 2), "TFLOPs": round(fl / t / 1e12, 1),
                                 "mfma_frac": round(fl / t / 1e12 / PEAK_BF16_TFLOPS, 4), "flops": fl}
 
+    if "serialized_layer_us" in seg:
+        # the attention segment alone: decode then prefill each on the whole GPU
+        # (standalone kernel times above), the contention-free bound max(T_D, T_P), and
+        # the overlapped modes' segment time, i.e. their layer time less the layer's
+        # non-attention part (serialized layer time - T_D - T_P)
+        td, tp = kern["decode_attn"]["us"], kern["prefill_attn"]["us"]
+        rest = seg["serialized_layer_us"] - (td + tp)
+        seg["attention_segment_us"] = {
+            "serialized": round(td + tp, 1), "bound": round(max(td, tp), 1),
+            "unmasked": round(seg["unmasked_layer_us"] - rest, 1),
+            "partitions": {kk: round(v - rest, 1) for kk, v in seg["partition_layer_us"].items()}}
+
     dom = "gate_up"
     traffic = recorded_traffic(wl.name)
     m_, n_, k_ = gl[dom]
