@@ -658,8 +658,16 @@ def main():
                                                 wl.n_q_heads, wl.n_kv_heads, wl.head_dim, dout,
                                                 wl.n_q_heads * wl.head_dim, dws, lay.dec_pages_per_split), args.repeats)
         nb = decode_bytes(inst)
+        # measured streaming-read ceiling: one read of 2 GiB (8x the Infinity Cache)
+        big = torch.empty(1 << 31, dtype=torch.uint8, device="cuda")
+        sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+        t_rd = timer(lambda: X.xp_probe_read(big, big.numel(), sink), 5)
+        ceiling = big.numel() / t_rd / 1e9
+        del big
         kern["decode_attn"] = {"us": round(t * 1e6, 2), "GBs": round(nb / t / 1e9, 1),
-                               "hbm_frac": round(nb / t / 1e9 / PEAK_HBM_GBS, 4), "bytes": nb}
+                               "hbm_frac": round(nb / t / 1e9 / PEAK_HBM_GBS, 4), "bytes": nb,
+                               "read_ceiling_GBs": round(ceiling, 1),
+                               "ceiling_frac": round(nb / t / 1e9 / ceiling, 4)}
     if wl.chunk_len:
         hq, d = wl.hq_loc, wl.head_dim
         pout = torch.empty((wl.chunk_len, hq * d), dtype=torch.bfloat16, device="cuda")

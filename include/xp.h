@@ -385,6 +385,12 @@ xp_status xp_prefill_attention(int32_t dtype, const void* q, const void* pool, i
  * XCC id, SE id and CU id it ran on: out [n_blocks, 4] int32 (device). */
 xp_status xp_probe_hw_ids(int32_t n_blocks, int32_t* out, void* stream);
 
+/* Reads every byte of src (device, `bytes` a positive multiple of 16) once with wide
+ * loads on `stream`, for measuring the streaming-read ceiling that HBM-bound kernels
+ * are compared with.  sink: one device uint32 the kernel may write.  Nothing else is
+ * written.  XP_EINVAL on a null pointer or a bad size. */
+xp_status xp_probe_read(const void* src, size_t bytes, uint32_t* sink, void* stream);
+
 /* ------------------------------------------------------------------------ */
 /* Waterfill dispatch (host only, thread-safe)                              */
 /* ------------------------------------------------------------------------ */

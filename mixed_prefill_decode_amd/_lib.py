@@ -22,7 +22,7 @@ __all__ = ["XpError", "lib", "XP_F32", "XP_BF16", "XP_EPI_F32", "XP_EPI_ADD_T", 
            "xp_layer_read_status", "xp_rmsnorm", "xp_gemm_workspace_size", "xp_gemm_tile", "xp_gemm", "xp_kv_append",
            "xp_kv_gather",
            "xp_decode_workspace_size", "xp_decode_attention", "xp_prefill_workspace_size", "xp_prefill_attention",
-           "xp_probe_hw_ids",
+           "xp_probe_hw_ids", "xp_probe_read",
            "xp_waterfill", "xp_iteration_latency", "xp_admission", "xp_decode_placement", "xp_schedule",
            "ScheduleCall", "WaterfillCall", "xp_fit_affine", "xp_fit_latency_model", "XP_SCHED_DONE", "XP_SCHED_BUDGET", "XP_SCHED_NO_HOST", "xp_build_info", "xp_last_error"]
 
@@ -44,7 +44,8 @@ EXPORTED = ["xp_last_error", "xp_build_info", "xp_ctx_create", "xp_ctx_destroy",
             "xp_rmsnorm", "xp_gemm_workspace_size", "xp_gemm_tile", "xp_gemm", "xp_kv_append", "xp_kv_gather",
             "xp_decode_workspace_size",
             "xp_decode_attention", "xp_prefill_workspace_size", "xp_prefill_attention", "xp_probe_hw_ids",
-            "xp_waterfill",
+            "xp_probe_read",
+            "xp_probe_read", "xp_waterfill",
             "xp_iteration_latency", "xp_fit_affine", "xp_fit_latency_model", "xp_admission",
             "xp_decode_placement", "xp_schedule"]
 
@@ -185,6 +186,7 @@ def _declare(L):
         "xp_prefill_attention": (S, [_i32, _vp, _vp, _i32, _i32, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
                                      _i32, _vp, _i32, _vp, _i32, _vp, _vp, _vp]),
         "xp_probe_hw_ids": (S, [_i32, _vp, _vp]),
+        "xp_probe_read": (S, [_vp, _sz, _vp, _vp]),
         "xp_waterfill": (S, [C.POINTER(WaterfillIn), C.POINTER(WaterfillOut)]),
         "xp_iteration_latency": (S, [C.POINTER(LatencyModel), _i32, _vp, _vp, _vp, _i32, _vp, _vp,
                                      C.POINTER(_f64)]),
@@ -461,6 +463,10 @@ def xp_prefill_attention(dtype, q, pool, n_pages, page_size, pre_pages, pre_max_
 
 def xp_probe_hw_ids(n_blocks, out, stream=None):
     _check(lib().xp_probe_hw_ids(n_blocks, _ptr(out), _stream(stream)))
+
+
+def xp_probe_read(src, nbytes, sink, stream=None):
+    _check(lib().xp_probe_read(_ptr(src), nbytes, _ptr(sink), _stream(stream)))
 
 
 def _model(d: dict) -> LatencyModel:

@@ -30,6 +30,12 @@ constexpr int kPage = 16;
 constexpr int kDepth = 1;
 // pages are read through plain pointers (true) or per-page buffer resources
 constexpr bool kPtrLoads = false;
+// Cache policy of the page loads: non-temporal (the buffer instructions' nt bit).
+// Every K/V byte is read once per step, so keeping it out of the caches' recency
+// costs nothing; measured on MI355X it raises the decode stream from 5.16 to 5.79
+// TB/s on the 8B batch (6.03 on the 32K-context one) and shortens the 8B layer step
+// by 4%, the following GEMMs finding more of their operands cached.
+constexpr int kLoadAux = 2;
 // log2-domain margin by which a head's maximum may exceed the softmax reference
 // before O and l are rescaled
 constexpr float kLazy = 8.0f;
@@ -77,17 +83,17 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t page_rsrc(const char* page, in
 }
 
 __device__ __forceinline__ void bload(Frag8<bf16_t>& f, __amdgpu_buffer_rsrc_t r, int off) {
-  f.v = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+  f.v = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kLoadAux));
 }
 __device__ __forceinline__ void bload(Frag8<float>& f, __amdgpu_buffer_rsrc_t r, int off) {
-  f.lo = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
-  f.hi = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(r, off + 16, 0, 0));
+  f.lo = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kLoadAux));
+  f.hi = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(r, off + 16, 0, kLoadAux));
 }
 __device__ __forceinline__ void bload(Frag4<bf16_t>& f, __amdgpu_buffer_rsrc_t r, int off) {
-  f.v = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0));
+  f.v = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, kLoadAux));
 }
 __device__ __forceinline__ void bload(Frag4<float>& f, __amdgpu_buffer_rsrc_t r, int off) {
-  f.v = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+  f.v = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kLoadAux));
 }
 
 // K plane token-major [16][D]: lane l reads key l%16, dims [32*st + 8*(l/16), +8).

@@ -335,3 +335,21 @@ def test_decode_token_matches_prefill_row_on_gpu():
         a = to_f64(to_host_bits(out_d), dt)
         b = to_f64(to_host_bits(out_l), dt)[rows][:, g * G * d:(g + 1) * G * d]
         assert rel_fro(a, b) < 5e-3
+
+
+def test_read_probe_reads_every_piece():
+    # a thread writes the sink only when the XOR of the words it read equals 0x9e3779b9;
+    # here each 16-byte piece is one thread's
+    buf = torch.zeros(4096, dtype=torch.int32, device="cuda")
+    buf[4093] = int(np.int32(np.uint32(0x9E3779B9).view(np.int32)))   # the last 16-byte piece
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    X.xp_probe_read(buf, buf.numel() * 4, sink)
+    torch.cuda.synchronize()
+    assert int(np.int32(sink.item()).view(np.uint32)) == 0x9E3779B9
+    buf[4092] = 1                                                      # that piece's XOR changes
+    sink.zero_()
+    X.xp_probe_read(buf, buf.numel() * 4, sink)
+    torch.cuda.synchronize()
+    assert sink.item() == 0
+    with pytest.raises(X.XpError):
+        X.xp_probe_read(buf, 10, sink)
