@@ -25,24 +25,19 @@ __global__ void probe_kernel(int32_t* out) {
   }
 }
 
-#ifndef XP_PROBE_U
-#define XP_PROBE_U 4
-#endif
-#ifndef XP_PROBE_NT
-#define XP_PROBE_NT 0
-#endif
-// Each thread reads U independent 16-byte pieces per iteration of a grid-stride loop;
-// the XOR of everything a thread read reaches memory only if it equals a value that
-// random data essentially never gives, which keeps the loads without adding traffic.
+// Each thread reads U = 4 independent 16-byte pieces per iteration of a grid-stride
+// loop, non-temporal (measured on MI355X: 6.05 TB/s, against 5.55 with plain loads and
+// 5.3-5.4 with 8 or 16 pieces); the XOR of everything a thread read reaches memory only
+// if it equals a value that random data essentially never gives, which keeps the
+// loads without adding traffic.
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ uint32_t fold16(const uint4* p) {
-  const u32x4* q = reinterpret_cast<const u32x4*>(p);
-  const u32x4 a = XP_PROBE_NT ? __builtin_nontemporal_load(q) : *q;
+  const u32x4 a = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
   return a.x ^ a.y ^ a.z ^ a.w;
 }
 __global__ __launch_bounds__(256) void read_probe_kernel(const uint4* __restrict__ src, long n16,
                                                          uint32_t* __restrict__ sink) {
-  constexpr int U = XP_PROBE_U;
+  constexpr int U = 4;
   const long stride = long(gridDim.x) * 256;
   uint32_t acc = 0;
   long i = long(blockIdx.x) * 256 + threadIdx.x;
