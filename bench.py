@@ -18,7 +18,9 @@ import hashlib
 import json
 import math
 import os
+import shutil
 import sys
+import tempfile
 import time
 
 import numpy as np
@@ -37,14 +39,21 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=5)
-    p.add_argument("--workload", default="C2")
+    p.add_argument("--workload", default="C5")
     p.add_argument("--decode-cus", type=int, default=None,
                    help="CUs for decode attention (default: the fastest of serialized, unmasked and a sweep of "
                         "partitions that includes the pages' 90%% rule; 0 = serialized, -1 = unmasked)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-budget-s", type=float, default=25.0)
-    p.add_argument("--kernel-only", choices=["none", "swiglu", "decode", "prefill", "copy"], default="none",
+    p.add_argument("--kernel-only", choices=["none", "qkv", "o", "gate_up", "down", "decode_attn", "prefill_attn",
+                                             "copy"], default="none",
                    help="only launch one kernel repeatedly (for counter runs)")
+    p.add_argument("--extra-decode", default="C4",
+                   help="also time this workload's decode attention alone (its KV pool is built on the device); "
+                        "'none' to skip")
+    p.add_argument("--no-split-sweep", action="store_true",
+                   help="time the step serialized only (no split-attention probes)")
+    p.add_argument("--instance-cache", default=None, help="internal: directory of a saved input instance")
     p.add_argument("--repeats", type=int, default=20, help="launches per kernel timing")
     p.add_argument("--estimator", action="store_true",
                    help="fit the iteration-latency estimator on this GPU from isolated profiles and report its "
@@ -106,29 +115,54 @@ def gemm_list(wl):
             "gate_up": (M, 2 * F, H), "down": (M, H, F)}
 
 
-TRAFFIC_PROFILE = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles",
-                               "gate_up_swiglu_gemm_c2_traffic.md")
-GEMM_SOURCES = ("mixed_prefill_decode_amd/csrc/gemm_core.h", "mixed_prefill_decode_amd/csrc/gemm.hip",
-                "mixed_prefill_decode_amd/csrc/xp_device.h")
+PROFILES = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles")
+# the sources each measured kernel is built from: a traffic record counts only while they
+# hash to the value recorded with it
+KERNEL_SOURCES = {
+    "gemm": ("mixed_prefill_decode_amd/csrc/gemm_core.h", "mixed_prefill_decode_amd/csrc/gemm.hip",
+             "mixed_prefill_decode_amd/csrc/xp_device.h"),
+    "decode_attn": ("mixed_prefill_decode_amd/csrc/decode_attn.hip", "mixed_prefill_decode_amd/csrc/xp_device.h"),
+    "prefill_attn": ("mixed_prefill_decode_amd/csrc/prefill_attn.hip", "mixed_prefill_decode_amd/csrc/gemm_core.h",
+                     "mixed_prefill_decode_amd/csrc/xp_device.h"),
+}
+KERNEL_NAMES = {
+    "qkv": "gemm_kernel<bf16,F32> (QKV projection)", "o": "gemm_kernel<bf16,AddT> (O projection + residual)",
+    "gate_up": "gemm_kernel<bf16,SwiGLU> (gate/up projection)",
+    "down": "gemm_kernel<bf16,AddF32> (down projection + residual)",
+    "decode_attn": "decode_split_kernel + decode_combine_kernel (paged GQA decode attention)",
+    "prefill_attn": "prefill_kernel (+ prefill_combine_kernel) (causal chunked-prefill attention)",
+}
 
 
-def recorded_traffic(workload: str):
-    """HBM bytes per launch of the dominant kernel from the committed counter summary
-    (FETCH_SIZE and WRITE_SIZE scaled by a copy kernel's readings), or None when the
-    summary is for another workload or the GEMM sources changed since it was taken."""
+def sources_hash(kernel: str) -> str:
+    key = "gemm" if kernel in ("qkv", "o", "gate_up", "down") else kernel
+    h = hashlib.sha256()
+    root = os.path.dirname(os.path.abspath(__file__))
+    for f in KERNEL_SOURCES[key]:
+        with open(os.path.join(root, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def recorded_traffic(workload: str, kernel: str):
+    """HBM bytes per launch of `kernel` on `workload` from a committed counter summary
+    (profiles/*_traffic.md: FETCH_SIZE and WRITE_SIZE scaled by what the same counters
+    read for a copy kernel), or None when there is none for this pair or the kernel's
+    sources changed since it was taken."""
+    import glob
     try:
-        text = open(TRAFFIC_PROFILE).read()
-        rec = json.loads(text[text.index("```json") + 7:text.rindex("```")])
-        h = hashlib.sha256()
-        root = os.path.dirname(os.path.abspath(__file__))
-        for f in GEMM_SOURCES:
-            with open(os.path.join(root, f), "rb") as fh:
-                h.update(fh.read())
-    except (OSError, ValueError):
+        want = sources_hash(kernel)
+    except OSError:
         return None
-    if rec.get("workload") != workload or rec.get("src_sha256_16") != h.hexdigest()[:16]:
-        return None
-    return rec["traffic_bytes"]
+    for path in sorted(glob.glob(os.path.join(PROFILES, "*_traffic.md"))):
+        try:
+            text = open(path).read()
+            rec = json.loads(text[text.index("```json") + 7:text.index("```", text.index("```json") + 7)])
+        except (OSError, ValueError):
+            continue
+        if rec.get("workload") == workload and rec.get("kernel") == kernel and rec.get("src_sha256_16") == want:
+            return rec["traffic_bytes"]
+    return None
 
 
 def cpu_baseline(inst, budget_s: float) -> dict:
@@ -470,11 +504,10 @@ def scheduler_timing(X, repeats: int = 100) -> dict:
     return out
 
 
-def calibrate_decode_cus(X, torch, step, inst, dev, timer, n_cus, repeats) -> tuple[int, dict]:
-    """Fewest CUs whose standalone decode-attention bandwidth is >= 90% of the all-CU figure
-    (the decode CU-allocation rule of the pages).  Candidates are multiples of 32: the mask
-    spreads CUs evenly over the 8 XCDs, and bandwidth only grows when every shader engine
-    (4 per XCD) gains a CU."""
+def calibrate_decode_cus(X, torch, step, inst, dev, n_cus, repeats) -> tuple[int, dict]:
+    """The pages' decode-CU rule, measured by the library (xp_calibrate_decode_cus): the
+    fewest CUs, in steps of 32 (every shader engine of the 8 XCDs gains one), whose
+    standalone decode-attention bandwidth is >= 90% of the all-CU figure."""
     wl = inst.wl
     lay = step.layout
     q = int(step.workspace.data_ptr()) + lay.q_dec
@@ -482,28 +515,150 @@ def calibrate_decode_cus(X, torch, step, inst, dev, timer, n_cus, repeats) -> tu
                                                  lay.dec_pages_per_split), dtype=torch.uint8, device="cuda")
     out = torch.empty((wl.n_decode, wl.n_q_heads * wl.head_dim), dtype=torch.bfloat16, device="cuda")
     nbytes = decode_bytes(inst)
+    k, curve = X.xp_calibrate_decode_cus(0, X.XP_BF16, q, dev.pool, inst.pool.n_pages, wl.page_size, dev.dec_pages,
+                                         inst.dec_max_blocks, dev.dec_ctx, wl.n_decode, wl.n_q_heads,
+                                         wl.n_kv_heads, wl.head_dim, out, wl.n_q_heads * wl.head_dim, dws,
+                                         lay.dec_pages_per_split, keep_fraction=0.9, cu_step=32, repeats=repeats,
+                                         stop_at_rule=False)
+    torch.cuda.synchronize()
+    gbs = {c: round(nbytes / (us * 1e-6) / 1e9, 1) for c, us in curve["points"].items()}
+    return k, {"full_GBs": round(nbytes / (curve["us_all"] * 1e-6) / 1e9, 1), "curve_GBs": gbs}
 
-    def run_on(stream):
-        return lambda: X.xp_decode_attention(X.XP_BF16, q, dev.pool, inst.pool.n_pages, wl.page_size,
-                                             dev.dec_pages, inst.dec_max_blocks, dev.dec_ctx, wl.n_decode,
-                                             wl.n_q_heads, wl.n_kv_heads, wl.head_dim, out,
-                                             wl.n_q_heads * wl.head_dim, dws, lay.dec_pages_per_split, stream)
 
-    full = nbytes / timer(run_on(None), repeats)
-    curve = {}
-    chosen = n_cus - 32
-    for k in range(32, n_cus, 32):
-        ctx = X.Ctx(0, k, lay.dec_pages_per_split)
-        s_dec, _ = ctx.streams()
-        ts = torch.cuda.ExternalStream(s_dec)
-        with torch.cuda.stream(ts):
-            bw = nbytes / timer(run_on(s_dec), repeats)
-        curve[k] = round(bw / 1e9, 1)
-        ctx.close()
-        if bw >= 0.9 * full:
-            chosen = k
-            break
-    return chosen, {"full_GBs": round(full / 1e9, 1), "curve_GBs": curve}
+def read_curve(X, torch, repeats) -> dict:
+    """The streaming-read probe's bandwidth against the CUs it may use (xp_probe_read_curve
+    over 2 GiB, 8x the Infinity Cache): the most HBM bandwidth a partition of k CUs can
+    reach, the ceiling of the decode side of a CU partition."""
+    big = torch.empty(1 << 31, dtype=torch.uint8, device="cuda")
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    c = X.xp_probe_read_curve(0, big, big.numel(), sink, cu_step=32, repeats=repeats)
+    torch.cuda.synchronize()
+    del big
+    gb = (1 << 31) / 1e9
+    return {"full_GBs": round(gb / (c["us_all"] * 1e-6), 1),
+            "curve_GBs": {k: round(gb / (us * 1e-6), 1) for k, us in c["points"].items()}}
+
+
+def kernel_calls(X, torch, inst, step, dev):
+    """Launchers of the step's kernels on their own, through the C ABI, on the step's
+    workspace (torch's current stream): name -> (call, algorithmic work, unit)."""
+    wl = inst.wl
+    lay, ws, w = step.layout, int(step.workspace.data_ptr()), dev.weights
+    M, H, F = wl.n_rows, wl.hidden, wl.ffn_dim
+    gl = gemm_list(wl)
+    gp, gpb = ws + lay.gemm_part, lay.h1 - lay.gemm_part     # the layer's GEMM split partials
+    calls = {
+        "qkv": lambda: X.xp_gemm(X.XP_BF16, X.XP_EPI_F32, ws + lay.hn, w["w_qkv"], None, None, ws + lay.qkv,
+                                 M, gl["qkv"][1], H, gp, gpb),
+        "o": lambda: X.xp_gemm(X.XP_BF16, X.XP_EPI_ADD_T, ws + lay.attn, w["w_o"], None, dev.x, ws + lay.h1,
+                               M, H, gl["o"][2], gp, gpb),
+        "gate_up": lambda: X.xp_gemm(X.XP_BF16, X.XP_EPI_SWIGLU, ws + lay.hn, w["w_gate"], w["w_up"], None,
+                                     ws + lay.act, M, F, H, gp, gpb),
+        "down": lambda: X.xp_gemm(X.XP_BF16, X.XP_EPI_ADD_F32, ws + lay.act, w["w_down"], None, ws + lay.h1,
+                                  step.out, M, H, F, gp, gpb),
+    }
+    out = {k: (fn, 2.0 * gl[k][0] * gl[k][1] * gl[k][2], "flop") for k, fn in calls.items()}
+    if wl.n_decode:
+        dws = torch.empty(X.xp_decode_workspace_size(wl.n_decode, wl.n_q_heads, wl.n_kv_heads, wl.head_dim,
+                                                     inst.dec_max_blocks, lay.dec_pages_per_split),
+                          dtype=torch.uint8, device="cuda")
+        dout = torch.empty((wl.n_decode, wl.n_q_heads * wl.head_dim), dtype=torch.bfloat16, device="cuda")
+
+        def dec(stream=None):
+            X.xp_decode_attention(X.XP_BF16, ws + lay.q_dec, dev.pool, inst.pool.n_pages, wl.page_size,
+                                  dev.dec_pages, inst.dec_max_blocks, dev.dec_ctx, wl.n_decode, wl.n_q_heads,
+                                  wl.n_kv_heads, wl.head_dim, dout, wl.n_q_heads * wl.head_dim, dws,
+                                  lay.dec_pages_per_split, stream)
+        dec._keep = (dws, dout)
+        out["decode_attn"] = (dec, float(decode_bytes(inst)), "byte")
+    if wl.chunk_len:
+        hq, d = wl.hq_loc, wl.head_dim
+        pout = torch.empty((wl.chunk_len, hq * d), dtype=torch.bfloat16, device="cuda")
+
+        def pre(stream=None):
+            X.xp_prefill_attention(X.XP_BF16, ws + lay.q_pre, dev.pool, inst.pool.n_pages, wl.page_size,
+                                   dev.pre_pages, inst.pre_max_blocks, hq, wl.hkv_loc, d, wl.prior_len,
+                                   wl.chunk_len, 0, wl.chunk_len, pout, hq * d, None, hq * d, ws + lay.pre_part,
+                                   None, stream)
+        pre._keep = (pout,)
+        out["prefill_attn"] = (pre, float(prefill_flops(wl)), "flop")
+    return out
+
+
+def kernel_figures(name, seconds, work, unit) -> dict:
+    r = {"us": round(seconds * 1e6, 2)}
+    if unit == "byte":
+        r.update(GBs=round(work / seconds / 1e9, 1), hbm_frac=round(work / seconds / 1e9 / PEAK_HBM_GBS, 4),
+                 bytes=int(work))
+    else:
+        r.update(TFLOPs=round(work / seconds / 1e12, 1),
+                 mfma_frac=round(work / seconds / 1e12 / PEAK_BF16_TFLOPS, 4), flops=work)
+    return r
+
+
+def window_times(X, torch, inst, step, dev, ctx, repeats) -> dict:
+    """Decode and prefill attention inside the split region of a CU-partitioned (or
+    unmasked) context: both launched between a fork and a join as the layer step
+    launches them, each timed with events on its own stream (the figures the pages'
+    overlap rule is about: decode's bandwidth and prefill's MFMA rate while the other
+    one runs)."""
+    calls = kernel_calls(X, torch, inst, step, dev)
+    dec, dbytes, _ = calls["decode_attn"]
+    pre, pflops, _ = calls["prefill_attn"]
+    s_dec, s_pre = ctx.streams()
+    ts_dec, ts_pre = torch.cuda.ExternalStream(s_dec), torch.cuda.ExternalStream(s_pre)
+    main = torch.cuda.current_stream()
+    E = lambda: torch.cuda.Event(enable_timing=True)
+    rec = []
+    for it in range(2 * repeats):
+        fork, d0, d1, p0, p1, join = E(), E(), E(), E(), E(), E()
+        fork.record(main)
+        ts_dec.wait_event(fork)
+        ts_pre.wait_event(fork)
+        d0.record(ts_dec)
+        dec(s_dec)
+        d1.record(ts_dec)
+        p0.record(ts_pre)
+        pre(s_pre)
+        p1.record(ts_pre)
+        main.wait_stream(ts_dec)
+        main.wait_stream(ts_pre)
+        join.record(main)
+        if it >= repeats:
+            rec.append((fork, d0, d1, p0, p1, join))
+    torch.cuda.synchronize()
+    n = len(rec)
+    td = sum(a[1].elapsed_time(a[2]) for a in rec) / n * 1e-3
+    tp = sum(a[3].elapsed_time(a[4]) for a in rec) / n * 1e-3
+    tw = sum(a[0].elapsed_time(a[5]) for a in rec) / n * 1e-3
+    return {"window_us": round(tw * 1e6, 1), "decode_us": round(td * 1e6, 1),
+            "decode_GBs": round(dbytes / td / 1e9, 1), "decode_hbm_frac": round(dbytes / td / 1e9 / PEAK_HBM_GBS, 4),
+            "prefill_us": round(tp * 1e6, 1), "prefill_TFLOPs": round(pflops / tp / 1e12, 1),
+            "prefill_mfma_frac": round(pflops / tp / 1e12 / PEAK_BF16_TFLOPS, 4)}
+
+
+def extra_decode(X, torch, name, timer, repeats) -> dict:
+    """Decode attention of another workload alone (its KV pool built on the device), for
+    the HBM-bound figure on a decode-heavy batch."""
+    from synth import get_workload, make_instance
+    from synth.device import to_device, upload_pool
+    wl = get_workload(name)
+    inst = make_instance(wl)
+    pool = upload_pool(inst)
+    dec_pages, dec_ctx = to_device(inst.dec_pages, "i32"), to_device(inst.dec_ctx, "i32")
+    q = (torch.randn((wl.n_decode, wl.n_q_heads * wl.head_dim), device="cuda")).to(torch.bfloat16)
+    out = torch.empty_like(q)
+    ws = torch.empty(X.xp_decode_workspace_size(wl.n_decode, wl.n_q_heads, wl.n_kv_heads, wl.head_dim,
+                                                inst.dec_max_blocks, 0), dtype=torch.uint8, device="cuda")
+    fn = lambda: X.xp_decode_attention(X.XP_BF16, q, pool, inst.pool.n_pages, wl.page_size, dec_pages,
+                                       inst.dec_max_blocks, dec_ctx, wl.n_decode, wl.n_q_heads, wl.n_kv_heads,
+                                       wl.head_dim, out, wl.n_q_heads * wl.head_dim, ws, 0)
+    t = timer(fn, repeats)
+    r = kernel_figures("decode_attn", t, float(decode_bytes(inst)), "byte")
+    r["workload"] = f"{wl.name}: {wl.description}"
+    del pool
+    torch.cuda.empty_cache()
+    return r
 
 
 def main():
@@ -515,7 +670,7 @@ def main():
     import torch
 
     import mixed_prefill_decode_amd as X
-    from synth import get_workload, make_instance
+    from synth import get_workload, load_instance, make_instance, save_instance
     from synth.device import make_step, upload
 
     torch.cuda.init()
@@ -534,7 +689,7 @@ def main():
     n_cus = props.multi_processor_count
     wl = get_workload(args.workload)
     t0 = time.time()
-    inst = make_instance(wl)
+    inst = load_instance(args.instance_cache) if args.instance_cache else make_instance(wl)
     dev = upload(inst)
     log(f"[bench] {wl.name}: {wl.description}; rows {wl.n_rows}; pool {inst.pool.nbytes / 2**30:.2f} GiB; "
         f"inputs ready in {time.time() - t0:.1f} s on {props.name} ({n_cus} CUs)")
@@ -559,44 +714,54 @@ def main():
     step0.run()
     torch.cuda.synchronize()
     # Split-attention mode.  The pages size the decode partition by their rule (the
-    # fewest CUs that keep 90% of decode's standalone bandwidth); on MI355X decode
-    # bandwidth grows almost linearly with CUs, so that rule hands decode most of the
-    # chip and starves prefill.  The step is therefore also timed serialized, with the
-    # two attention kernels concurrent on all CUs (no masks), and on a sweep of
-    # partitions; the timed steps use the fastest and every figure is reported.
-    # Each mode is timed in a fresh process whose first streams are that context's:
-    # a context created after others in one process can be slowed as a whole (its
-    # queues may share a hardware pipe with the main stream's), so this process
-    # creates no masked context before the chosen one.
+    # fewest CUs that keep 90% of decode's standalone bandwidth).  The step is timed
+    # serialized, with the two attention kernels concurrent on all CUs (no masks), on
+    # a sweep of partitions and on the rule's; the timed steps use the fastest and
+    # every figure is reported.  Each mode is timed in a fresh process whose first
+    # streams are that context's (a context created after others in one process can
+    # be slowed as a whole: its queues may share a hardware pipe with the main
+    # stream's), so this process creates no masked context before the chosen one;
+    # the probes map this process's inputs instead of drawing them again.
     seg = {}
     step, k, timed_mode = step0, 0, "serialized"
-    if args.decode_cus is not None:
-        k = args.decode_cus
-        if k != 0:
-            step, _ = make_step(inst, X.Ctx(0, k, 0), dev)
-            timed_mode = "unmasked" if k < 0 else "partitioned"
-    elif wl.n_decode and wl.chunk_len:
-        rule = run_probe(args, "rule")
-        k_rule = rule["rule_decode_cus"]
-        seg["rule_decode_cus"] = k_rule
-        seg["calibration"] = rule["calibration"]
-        seg["serialized_layer_us"] = round(timer(step0.run, args.repeats) * 1e6, 1)
-        sweep = {}
-        best = (seg["serialized_layer_us"], 0)
-        for kk in sorted({-1, 64, 96, 128, 160, k_rule}):
-            t = run_probe(args, str(kk))["layer_us"]
-            sweep["unmasked" if kk < 0 else kk] = t
-            if t < best[0]:
-                best = (t, kk)
-        seg["rule_layer_us"] = sweep[k_rule]
-        seg["unmasked_layer_us"] = sweep["unmasked"]
-        seg["partition_layer_us"] = {kk: v for kk, v in sweep.items() if kk != "unmasked"}
-        k = best[1]
-        if k != 0:
-            step, _ = make_step(inst, X.Ctx(0, k, 0), dev)
-        timed_mode = "serialized" if k == 0 else "unmasked" if k < 0 else "partitioned"
-        seg["decode_cus"] = k
-        seg["timed_mode"] = timed_mode
+    cache = None
+    try:
+        if args.decode_cus is not None:
+            k = args.decode_cus
+            if k != 0:
+                step, _ = make_step(inst, X.Ctx(0, k, 0), dev)
+                timed_mode = "unmasked" if k < 0 else "partitioned"
+        elif wl.n_decode and wl.chunk_len and not args.no_split_sweep:
+            cache = tempfile.mkdtemp(prefix="xp_bench_", dir="/dev/shm" if os.path.isdir("/dev/shm") else None)
+            save_instance(inst, cache)
+            rule = run_probe(args, "rule", cache)
+            k_rule = rule["rule_decode_cus"]
+            seg["rule_decode_cus"] = k_rule
+            seg["calibration"] = rule["calibration"]
+            seg["read_probe_curve"] = rule["read_curve"]
+            seg["serialized_layer_us"] = round(timer(step0.run, args.repeats) * 1e6, 1)
+            sweep, windows = {}, {}
+            best = (seg["serialized_layer_us"], 0)
+            for kk in sorted({-1, 64, 96, 128, 160, k_rule}):
+                r = run_probe(args, str(kk), cache)
+                t = r["layer_us"]
+                sweep["unmasked" if kk < 0 else kk] = t
+                windows["unmasked" if kk < 0 else kk] = r["window"]
+                if t < best[0]:
+                    best = (t, kk)
+            seg["rule_layer_us"] = sweep[k_rule]
+            seg["unmasked_layer_us"] = sweep["unmasked"]
+            seg["partition_layer_us"] = {kk: v for kk, v in sweep.items() if kk != "unmasked"}
+            seg["window"] = windows
+            k = best[1]
+            if k != 0:
+                step, _ = make_step(inst, X.Ctx(0, k, 0), dev)
+            timed_mode = "serialized" if k == 0 else "unmasked" if k < 0 else "partitioned"
+            seg["decode_cus"] = k
+            seg["timed_mode"] = timed_mode
+    finally:
+        if cache:
+            shutil.rmtree(cache, ignore_errors=True)
 
     def one_step():
         r = X.xp_waterfill(**wf_args)
@@ -623,61 +788,22 @@ def main():
     tokens_per_s = wl.n_rows * args.steps / wall
     assert step.status() == 0
 
-    # per-kernel measurements (standalone, all CUs, caller stream)
-    lay = step0.layout
-    ws = int(step0.workspace.data_ptr())
-    w = dev.weights
-    M, H, F = wl.n_rows, wl.hidden, wl.ffn_dim
+    # per-kernel measurements (standalone, all CUs, HIP events on the launch stream)
     kern = {}
-    gl = gemm_list(wl)
-    gp, gpb = ws + lay.gemm_part, lay.h1 - lay.gemm_part     # the layer's GEMM split partials
-    gemm_calls = {
-        "qkv": lambda: X.xp_gemm(X.XP_BF16, X.XP_EPI_F32, ws + lay.hn, w["w_qkv"], None, None, ws + lay.qkv,
-                                 M, gl["qkv"][1], H, gp, gpb),
-        "o": lambda: X.xp_gemm(X.XP_BF16, X.XP_EPI_ADD_T, ws + lay.attn, w["w_o"], None, dev.x, ws + lay.h1,
-                               M, H, gl["o"][2], gp, gpb),
-        "gate_up": lambda: X.xp_gemm(X.XP_BF16, X.XP_EPI_SWIGLU, ws + lay.hn, w["w_gate"], w["w_up"], None,
-                                     ws + lay.act, M, F, H, gp, gpb),
-        "down": lambda: X.xp_gemm(X.XP_BF16, X.XP_EPI_ADD_F32, ws + lay.act, w["w_down"], None, ws + lay.h1,
-                                  step0.out, M, H, F, gp, gpb),
-    }
-    for name, fn in gemm_calls.items():
-        m_, n_, k_ = gl[name]
-        t = timer(fn, args.repeats)
-        fl = 2.0 * m_ * n_ * k_
-        wbytes = n_ * k_ * 2
-        kern[name] = {"us": round(t * 1e6, 2), "TFLOPs": round(fl / t / 1e12, 1),
-                      "mfma_frac": round(fl / t / 1e12 / PEAK_BF16_TFLOPS, 4),
-                      "weight_GBs": round(wbytes / t / 1e9, 1)}
-    dws = torch.empty(X.xp_decode_workspace_size(wl.n_decode, wl.n_q_heads, wl.n_kv_heads, wl.head_dim, max(inst.dec_max_blocks, 1),
-                                                 lay.dec_pages_per_split) or 256, dtype=torch.uint8, device="cuda")
-    if wl.n_decode:
-        dout = torch.empty((wl.n_decode, wl.n_q_heads * wl.head_dim), dtype=torch.bfloat16, device="cuda")
-        t = timer(lambda: X.xp_decode_attention(X.XP_BF16, ws + lay.q_dec, dev.pool, inst.pool.n_pages, 16,
-                                                dev.dec_pages, inst.dec_max_blocks, dev.dec_ctx, wl.n_decode,
-                                                wl.n_q_heads, wl.n_kv_heads, wl.head_dim, dout,
-                                                wl.n_q_heads * wl.head_dim, dws, lay.dec_pages_per_split), args.repeats)
-        nb = decode_bytes(inst)
+    calls = kernel_calls(X, torch, inst, step0, dev)
+    for name, (fn, work, unit) in calls.items():
+        kern[name] = kernel_figures(name, timer(fn, args.repeats), work, unit)
+        if name in ("qkv", "o", "gate_up", "down"):
+            m_, n_, k_ = gemm_list(wl)[name]
+            kern[name]["weight_GBs"] = round(n_ * k_ * 2 / (kern[name]["us"] * 1e-6) / 1e9, 1)
+    if "decode_attn" in kern:
         # measured streaming-read ceiling: one read of 2 GiB (8x the Infinity Cache)
         big = torch.empty(1 << 31, dtype=torch.uint8, device="cuda")
         sink = torch.zeros(1, dtype=torch.int32, device="cuda")
-        t_rd = timer(lambda: X.xp_probe_read(big, big.numel(), sink), 5)
-        ceiling = big.numel() / t_rd / 1e9
+        ceiling = big.numel() / timer(lambda: X.xp_probe_read(big, big.numel(), sink), 5) / 1e9
         del big
-        kern["decode_attn"] = {"us": round(t * 1e6, 2), "GBs": round(nb / t / 1e9, 1),
-                               "hbm_frac": round(nb / t / 1e9 / PEAK_HBM_GBS, 4), "bytes": nb,
-                               "read_ceiling_GBs": round(ceiling, 1),
-                               "ceiling_frac": round(nb / t / 1e9 / ceiling, 4)}
-    if wl.chunk_len:
-        hq, d = wl.hq_loc, wl.head_dim
-        pout = torch.empty((wl.chunk_len, hq * d), dtype=torch.bfloat16, device="cuda")
-        t = timer(lambda: X.xp_prefill_attention(X.XP_BF16, ws + lay.q_pre, dev.pool, inst.pool.n_pages, 16,
-                                                 dev.pre_pages, inst.pre_max_blocks, hq, wl.hkv_loc, d,
-                                                 wl.prior_len, wl.chunk_len, 0, wl.chunk_len, pout, hq * d,
-                                                 None, hq * d, ws + lay.pre_part), args.repeats)
-        fl = prefill_flops(wl)
-        kern["prefill_attn"] = {"us": round(t * 1e6, 2), "TFLOPs": round(fl / t / 1e12, 1),
-                                "mfma_frac": round(fl / t / 1e12 / PEAK_BF16_TFLOPS, 4), "flops": fl}
+        kern["decode_attn"]["read_ceiling_GBs"] = round(ceiling, 1)
+        kern["decode_attn"]["ceiling_frac"] = round(kern["decode_attn"]["GBs"] / ceiling, 4)
 
     if "serialized_layer_us" in seg:
         # the attention segment alone: decode then prefill each on the whole GPU
@@ -691,16 +817,26 @@ def main():
             "unmasked": round(seg["unmasked_layer_us"] - rest, 1),
             "partitions": {kk: round(v - rest, 1) for kk, v in seg["partition_layer_us"].items()}}
 
-    dom = "gate_up"
-    traffic = recorded_traffic(wl.name)
-    m_, n_, k_ = gl[dom]
-    fl = 2.0 * m_ * n_ * k_
+    # the roofline of the kernel that takes the most time in this workload's step
+    dom = max(kern, key=lambda n: kern[n]["us"])
+    fn, work, unit = calls[dom]
     t_dom = kern[dom]["us"] * 1e-6
-    roofline = {"bound": "mfma", "achieved": round(fl / t_dom / 1e12, 2), "peak": PEAK_BF16_TFLOPS,
-                "unit": "TFLOP/s", "frac": round(fl / t_dom / 1e12 / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
-                "kernel": "gemm_kernel<bf16,SwiGLU> (gate/up projection)", "flops_per_launch": fl}
+    traffic = recorded_traffic(wl.name, dom)
+    if unit == "byte":
+        roofline = {"bound": "hbm", "achieved": round(work / t_dom / 1e9, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                    "frac": round(work / t_dom / 1e9 / PEAK_HBM_GBS, 4), "traffic": traffic,
+                    "kernel": KERNEL_NAMES[dom], "bytes_per_launch": work}
+    else:
+        roofline = {"bound": "mfma", "achieved": round(work / t_dom / 1e12, 2), "peak": PEAK_BF16_TFLOPS,
+                    "unit": "TFLOP/s", "frac": round(work / t_dom / 1e12 / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
+                    "kernel": KERNEL_NAMES[dom], "flops_per_launch": work}
     log(f"[bench] layer {ms * 1e3:.1f} us/step, {tokens_per_s:.0f} tokens/s; kernels {json.dumps(kern)}")
     log(f"[bench] split attention {json.dumps(seg)}")
+
+    extra = None
+    if args.extra_decode != "none" and args.extra_decode != wl.name:
+        extra = extra_decode(X, torch, args.extra_decode, timer, args.repeats)
+        log(f"[bench] extra decode {json.dumps(extra)}")
 
     sched = scheduler_timing(X)
     log(f"[bench] scheduler {json.dumps(sched)}")
@@ -719,17 +855,18 @@ def main():
                    "chunk": wl.chunk_len, "prior": wl.prior_len, "sp_degree": wl.sp_degree,
                    "decode_cus": k, "split_attention": timed_mode if wl.n_decode and wl.chunk_len else None,
                    "page_size": wl.page_size},
-        "roofline": roofline, "cpu_baseline": cpu, "kernels": kern, "split_attention": seg,
-        "scheduler": sched,
+        "roofline": roofline, "cpu_baseline": cpu, "kernels": kern, "extra_decode": extra,
+        "split_attention": seg, "scheduler": sched,
     }
     print(json.dumps(line), flush=True)
 
 
-def run_probe(args, what: str) -> dict:
-    """Runs this script with --probe in a child process and returns its JSON line."""
+def run_probe(args, what: str, cache: str) -> dict:
+    """Runs this script with --probe in a child process (on the saved inputs) and
+    returns its JSON line."""
     import subprocess
     cmd = [sys.executable, os.path.abspath(__file__), "--workload", args.workload, "--repeats", str(args.repeats),
-           "--probe", what]
+           "--probe", what, "--instance-cache", cache]
     r = subprocess.run(cmd, capture_output=True, text=True, timeout=600)
     if r.returncode != 0:
         raise RuntimeError(f"probe {what} failed ({r.returncode}):\n{r.stderr[-2000:]}")
@@ -746,55 +883,43 @@ def probe_mode(args, X, torch, inst, dev, timer, n_cus):
         step0, _ = make_step(inst, ctx0, dev)
         step0.run()
         torch.cuda.synchronize()
-        k_rule, calib = calibrate_decode_cus(X, torch, step0, inst, dev, timer, n_cus, args.repeats)
-        print(json.dumps({"rule_decode_cus": k_rule, "calibration": calib}), flush=True)
+        k_rule, calib = calibrate_decode_cus(X, torch, step0, inst, dev, n_cus, args.repeats)
+        rc = read_curve(X, torch, 5)
+        print(json.dumps({"rule_decode_cus": k_rule, "calibration": calib, "read_curve": rc}), flush=True)
+        ctx0.close()
         return
     k = int(args.probe)
-    step, _ = make_step(inst, X.Ctx(0, k, 0), dev)
+    ctx = X.Ctx(0, k, 0)
+    step, _ = make_step(inst, ctx, dev)
     for _ in range(3):
         step.run()
     torch.cuda.synchronize()
     t = timer(step.run, args.repeats)
     assert step.status() == 0
-    print(json.dumps({"decode_cus": k, "layer_us": round(t * 1e6, 1)}), flush=True)
+    win = window_times(X, torch, inst, step, dev, ctx, args.repeats)
+    print(json.dumps({"decode_cus": k, "layer_us": round(t * 1e6, 1), "window": win}), flush=True)
+    ctx.close()
 
 
 def kernel_only(args, X, torch, inst, step, dev, timer):
     """Launch only one kernel repeatedly (input of counter-collection runs)."""
-    wl = inst.wl
     step.run()
     torch.cuda.synchronize()
-    lay, ws, w = step.layout, int(step.workspace.data_ptr()), dev.weights
-    if args.kernel_only == "swiglu":
-        fn = lambda: X.xp_gemm(X.XP_BF16, X.XP_EPI_SWIGLU, ws + lay.hn, w["w_gate"], w["w_up"], None, ws + lay.act,
-                               wl.n_rows, wl.ffn_dim, wl.hidden, ws + lay.gemm_part, lay.h1 - lay.gemm_part)
-    elif args.kernel_only == "prefill":
-        hq, d = wl.hq_loc, wl.head_dim
-        pout = torch.empty((wl.chunk_len, hq * d), dtype=torch.bfloat16, device="cuda")
-        fn = lambda: X.xp_prefill_attention(X.XP_BF16, ws + lay.q_pre, dev.pool, inst.pool.n_pages, wl.page_size,
-                                            dev.pre_pages, inst.pre_max_blocks, hq, wl.hkv_loc, d, wl.prior_len,
-                                            wl.chunk_len, 0, wl.chunk_len, pout, hq * d, None, hq * d,
-                                            ws + lay.pre_part)
-    elif args.kernel_only == "decode":
-        dws = torch.empty(X.xp_decode_workspace_size(wl.n_decode, wl.n_q_heads, wl.n_kv_heads, wl.head_dim,
-                                                     inst.dec_max_blocks, lay.dec_pages_per_split),
-                          dtype=torch.uint8, device="cuda")
-        dout = torch.empty((wl.n_decode, wl.n_q_heads * wl.head_dim), dtype=torch.bfloat16, device="cuda")
-        fn = lambda: X.xp_decode_attention(X.XP_BF16, ws + lay.q_dec, dev.pool, inst.pool.n_pages, wl.page_size,
-                                           dev.dec_pages, inst.dec_max_blocks, dev.dec_ctx, wl.n_decode,
-                                           wl.n_q_heads, wl.n_kv_heads, wl.head_dim, dout,
-                                           wl.n_q_heads * wl.head_dim, dws, lay.dec_pages_per_split)
-    elif args.kernel_only == "copy":
+    if args.kernel_only == "copy":
         src = torch.empty(1 << 28, dtype=torch.float32, device="cuda").fill_(1.0)   # 1 GiB
         dst = torch.empty_like(src)
         fn = lambda: dst.copy_(src)
         log("[bench] copy kernel: 1 GiB read + 1 GiB written per launch")
     else:
-        raise SystemExit(f"--kernel-only {args.kernel_only}: not wired")
+        calls = kernel_calls(X, torch, inst, step, dev)
+        if args.kernel_only not in calls:
+            raise SystemExit(f"--kernel-only {args.kernel_only}: not part of {inst.wl.name}")
+        fn = calls[args.kernel_only][0]
     t = timer(fn, args.repeats)
     torch.cuda.synchronize()
     log(f"[bench] {args.kernel_only}: {t * 1e6:.2f} us per launch over {args.repeats} launches")
-    print(json.dumps({"kernel_only": args.kernel_only, "us": round(t * 1e6, 3), "repeats": args.repeats}))
+    print(json.dumps({"kernel_only": args.kernel_only, "us": round(t * 1e6, 3), "repeats": args.repeats,
+                      "src_sha256_16": sources_hash(args.kernel_only) if args.kernel_only != "copy" else None}))
 
 
 if __name__ == "__main__":

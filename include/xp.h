@@ -141,6 +141,20 @@ typedef struct {
   void* peer_qkv_out;
   const void* peer_attn_in;
   void* peer_attn_out;
+  /* Optional host copies of the device tables above, for validation before launch
+   * (NULL: not given).  When any is given, every one the step reads must be
+   * (dec_ctx_host [n_decode] and dec_pages_host [n_decode, Hkv, dec_max_blocks] when
+   * n_decode > 0, pre_pages_host [Hkv/P, pre_max_blocks] when chunk_len > 0, else
+   * XP_EINVAL), and the step checks on the host, before anything is launched, that
+   * every decode context fits its table and every table entry the step touches lies
+   * in [0, n_pages) and names a page no other entry names (XP_EPAGE / XP_ESHAPE).
+   * Without them the page ids are checked on the device: an id outside the pool is
+   * never dereferenced, the rows that depend on it are written as NaN and
+   * XP_DEV_BAD_PAGE is raised in the status word (xp_layer_read_status).  The copies
+   * must match the device tables; they are read during the call only. */
+  const int32_t* dec_ctx_host;
+  const int32_t* dec_pages_host;
+  const int32_t* pre_pages_host;
 } xp_batch_desc;
 
 /* Offsets (bytes from the workspace base) of the intermediates a layer step
@@ -164,16 +178,18 @@ typedef struct {
 } xp_ws_layout;
 
 typedef struct xp_ctx xp_ctx;
+#define XP_SPLIT_SERIALIZED 0
+#define XP_SPLIT_UNMASKED (-1)
 
 /* Create a context on `device`: it owns two HIP streams and four events used
  * for the split attention region ([CS] §6.1 "coordinated attention overlap").
  * decode_cus:
- *    0  -> serialized: decode then prefill attention on the caller's stream;
- *   -1  -> concurrent on two unmasked streams;
+ *   XP_SPLIT_SERIALIZED (0) -> decode then prefill attention on the caller's stream;
+ *   XP_SPLIT_UNMASKED (-1)  -> concurrent on two unmasked streams;
  *   k in [1, nCU-1] -> concurrent on CU-masked streams, k CUs for decode and
  *         the rest for prefill ([CS] §6.1: decode gets the fewest CUs that keep
- *         90% of its standalone HBM bandwidth).  The k CUs are spread evenly
- *         over the XCDs.
+ *         90% of its standalone HBM bandwidth: xp_calibrate_decode_cus gives that k
+ *         for a batch).  The k CUs are spread evenly over the XCDs.
  * decode_pages_per_split: KV pages per decode split-K partition, 1..64, or 0
  *   to choose per batch from the decode shape (about 1600 split waves, 8..64
  *   pages each; the layout's dec_pages_per_split reports the choice).
@@ -216,6 +232,7 @@ typedef struct {
   int32_t prior_len;           /* c_j >= 0 tokens of that request already cached               */
   const int32_t* pre_pages;    /* device [Hkv, pre_max_blocks]: the request's table            */
   int32_t pre_max_blocks;      /* >= ceil((prior_len + chunk_len) / page_size)                */
+  const int32_t* pre_pages_host;  /* optional host copy of pre_pages (see xp_batch_desc)      */
 } xp_chunk;
 
 /* Workspace layout of xp_layer_forward_chunks (same fields; q_pre holds the
@@ -295,8 +312,12 @@ xp_status xp_layer_read_status(const void* workspace, const xp_ws_layout* layout
 /* Kernel-level entry points (the same device code the layer step runs)     */
 /* ------------------------------------------------------------------------ */
 
-/* y[M, H] (T) = x / sqrt(mean(x^2) + eps) * gamma; x is T (x_is_f32 = 0) or
- * fp32 (x_is_f32 = 1). */
+/* The layer's RMSNorm ([TKNP] §4.3: normalization around attention and the MLP of
+ * each layer; [CS] §4 Fig. 7 pre-norm block): y[M, H] (T) = x / sqrt(mean(x^2) +
+ * eps) * gamma, the mean and sum of squares in fp32.  x is device [M, H] of T
+ * (x_is_f32 = 0) or fp32 (x_is_f32 = 1); gamma device [H] of T; y device [M, H] of T
+ * (caller-owned, may not alias x).  XP_EINVAL on a null pointer or bad dtype,
+ * XP_ESHAPE unless H is a positive multiple of 8; M = 0 launches nothing. */
 xp_status xp_rmsnorm(int32_t dtype, const void* x, int32_t x_is_f32, const void* gamma, void* y,
                      int32_t M, int32_t H, float eps, void* stream);
 
@@ -328,15 +349,27 @@ xp_status xp_gemm(int32_t dtype, int32_t epilogue, const void* A, const void* B,
                   const void* R, void* C, int32_t M, int32_t N, int32_t K, void* workspace,
                   size_t workspace_bytes, void* stream);
 
-/* Append n token rows of K/V (T, [n, d] each) at device positions pos[n]
- * through table rows: token t uses table + seq[t] * table_stride (seq: device
- * [n] row index into the table).  Exact copy; bit-exact with a host scatter. */
+/* The KV append of a step ([TKNP] §4.3: after the rotary embedding the new keys and
+ * values are appended to the local cache, then attention runs; [CS] §7 "KV-cache
+ * aliasing": one pool addressed through block tables).  Appends n token rows of K/V
+ * (device [n, d] of T each) at device positions pos[n] through table rows: token t
+ * uses the device table row table + seq[t] * table_stride (seq: device [n] row
+ * index), block pos/page_size, slot pos % page_size, in the pool layout above.
+ * Exact copy, bit-exact with a host scatter; writes only the slots named.  A page id
+ * outside [0, n_pages) is not written (host arguments are checked: XP_EINVAL /
+ * XP_ESHAPE; n = 0 launches nothing). */
 xp_status xp_kv_append(int32_t dtype, void* pool, int32_t n_pages, int32_t page_size, int32_t head_dim,
                        const int32_t* table, int32_t table_stride, const int32_t* seq,
                        const int32_t* pos, const void* k, const void* v, int32_t n, void* stream);
 
-/* Gather positions [0, len[s]) of n_seq table rows into contiguous K/V
- * [n_seq, max_len, d] (T); positions >= len[s] are left untouched. */
+/* Reads a sequence's K/V back through its block table ([CS] §7 "KV-cache aliasing":
+ * the decode and prefill views are tables over one physical pool).  Gathers positions
+ * [0, len[s]) of the n_seq device table rows (row s at table + s * table_stride) into
+ * caller-owned contiguous device K/V [n_seq, max_len, d] of T (K row-major, V
+ * row-major as well: the pool's dim-major V plane is transposed back); positions
+ * >= len[s] are left untouched and a page id outside [0, n_pages) is never read (the
+ * positions it covers are written as NaN).  Exact copy.  XP_EINVAL / XP_ESHAPE on bad host
+ * arguments. */
 xp_status xp_kv_gather(int32_t dtype, const void* pool, int32_t n_pages, int32_t page_size,
                        int32_t head_dim, const int32_t* table, int32_t table_stride,
                        const int32_t* len, int32_t n_seq, int32_t max_len, void* k_out, void* v_out,
@@ -380,6 +413,46 @@ xp_status xp_prefill_attention(int32_t dtype, const void* q, const void* pool, i
                                int32_t prior_len, int32_t chunk_len, int32_t off, int32_t n_local,
                                void* out_local, int32_t out_local_stride, void* out_peer,
                                int32_t out_peer_stride, void* workspace, uint32_t* status, void* stream);
+
+/* ------------------------------------------------------------------------ */
+/* Decode CU partition: the pages' sizing rule                              */
+/* ------------------------------------------------------------------------ */
+
+/* A kernel's time per launch against the number of CUs its stream may use. */
+#define XP_CU_CURVE_MAX 64
+typedef struct {
+  int32_t n_cus;                  /* CUs of the device                                  */
+  double us_all;                  /* microseconds per launch on every CU (no mask)      */
+  int32_t n_points;               /* entries of cus / us                                */
+  int32_t cus[XP_CU_CURVE_MAX];   /* CU counts tried, ascending multiples of cu_step    */
+  double us[XP_CU_CURVE_MAX];     /* microseconds per launch with that many CUs         */
+} xp_cu_curve;
+
+/* The decode CU count of the split attention region ([CS] §6.1 "coordinated
+ * attention overlap"; [PD]: decode is given the fewest SMs that still keep 90% of its
+ * standalone HBM bandwidth, the rest go to prefill).  Times the decode attention of
+ * the given batch (arguments as xp_decode_attention) standalone on every CU, then on
+ * CU-masked streams of k = cu_step, 2 cu_step, ... < n_cus CUs (spread over the XCDs
+ * as xp_ctx_create spreads them), `repeats` launches each after as many untimed ones,
+ * and returns in *decode_cus the smallest k whose bandwidth, us_all / us(k), is at
+ * least keep_fraction (0.9 on the pages), or the largest k tried when none is; with
+ * stop_at_rule != 0 the sweep ends at that k.  Pass the result to xp_ctx_create.  A
+ * cu_step of 32 keeps every shader engine (4 per XCD) equally loaded.
+ * Synchronous: blocks the calling thread; it creates and destroys its own streams and
+ * events on `device` and writes `out` and `workspace` (as xp_decode_attention) many
+ * times.  XP_EINVAL on bad sizes or a null pointer; errors of xp_decode_attention. */
+xp_status xp_calibrate_decode_cus(int32_t device, int32_t dtype, const void* q, const void* pool, int32_t n_pages,
+                                  int32_t page_size, const int32_t* dec_pages, int32_t dec_max_blocks,
+                                  const int32_t* dec_ctx, int32_t n_decode, int32_t n_q_heads, int32_t n_kv_heads,
+                                  int32_t head_dim, void* out, int32_t out_stride, void* workspace,
+                                  int32_t pages_per_split, double keep_fraction, int32_t cu_step, int32_t repeats,
+                                  int32_t stop_at_rule, int32_t* decode_cus, xp_cu_curve* curve);
+
+/* The same sweep for the streaming-read probe (xp_probe_read over `bytes` of src):
+ * how much HBM bandwidth the chip itself delivers from k CUs, the ceiling the rule
+ * above can reach on a partition of k CUs.  Synchronous, like the calibration. */
+xp_status xp_probe_read_curve(int32_t device, const void* src, size_t bytes, uint32_t* sink, int32_t cu_step,
+                              int32_t repeats, xp_cu_curve* curve);
 
 /* Records, per workgroup of a `n_blocks` launch on `stream`, the hardware
  * XCC id, SE id and CU id it ran on: out [n_blocks, 4] int32 (device). */

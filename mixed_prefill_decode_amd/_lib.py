@@ -7,12 +7,14 @@ no fallback path.
 """
 from __future__ import annotations
 
+import atexit
 import ctypes as C
 import os
+import weakref
 
 import numpy as np
 
-__all__ = ["XpError", "lib", "XP_F32", "XP_BF16", "XP_EPI_F32", "XP_EPI_ADD_T", "XP_EPI_ADD_F32",
+__all__ = ["XpError", "lib", "close_all", "XP_F32", "XP_BF16", "XP_EPI_F32", "XP_EPI_ADD_T", "XP_EPI_ADD_F32",
            "XP_EPI_SWIGLU", "XP_DEV_BAD_PAGE", "LayerShape", "LayerWeights", "KvPages", "BatchDesc",
            "WsLayout", "LatencyModel", "Ctx", "EXPORTED", "Chunk", "chunk_array",
            "xp_ctx_create", "xp_layer_workspace_layout", "xp_layer_forward", "xp_validate_batch",
@@ -22,13 +24,15 @@ __all__ = ["XpError", "lib", "XP_F32", "XP_BF16", "XP_EPI_F32", "XP_EPI_ADD_T", 
            "xp_layer_read_status", "xp_rmsnorm", "xp_gemm_workspace_size", "xp_gemm_tile", "xp_gemm", "xp_kv_append",
            "xp_kv_gather",
            "xp_decode_workspace_size", "xp_decode_attention", "xp_prefill_workspace_size", "xp_prefill_attention",
-           "xp_probe_hw_ids", "xp_probe_read",
+           "xp_probe_hw_ids", "xp_probe_read", "xp_calibrate_decode_cus", "xp_probe_read_curve", "CuCurve",
+           "XP_SPLIT_SERIALIZED", "XP_SPLIT_UNMASKED",
            "xp_waterfill", "xp_iteration_latency", "xp_admission", "xp_decode_placement", "xp_schedule",
            "ScheduleCall", "WaterfillCall", "xp_fit_affine", "xp_fit_latency_model", "XP_SCHED_DONE", "XP_SCHED_BUDGET", "XP_SCHED_NO_HOST", "xp_build_info", "xp_last_error"]
 
 XP_F32, XP_BF16 = 0, 1
 XP_EPI_F32, XP_EPI_ADD_T, XP_EPI_ADD_F32, XP_EPI_SWIGLU = 0, 1, 2, 3
 XP_DEV_BAD_PAGE = 1
+XP_SPLIT_SERIALIZED, XP_SPLIT_UNMASKED = 0, -1
 XP_SCHED_DONE, XP_SCHED_BUDGET, XP_SCHED_NO_HOST = 0, 1, 2
 STATUS_NAMES = {0: "XP_OK", -1: "XP_EINVAL", -2: "XP_ESHAPE", -3: "XP_EPAGE", -4: "XP_EHIP",
                 -5: "XP_EUNSUPPORTED", -6: "XP_EWORKSPACE"}
@@ -44,8 +48,7 @@ EXPORTED = ["xp_last_error", "xp_build_info", "xp_ctx_create", "xp_ctx_destroy",
             "xp_rmsnorm", "xp_gemm_workspace_size", "xp_gemm_tile", "xp_gemm", "xp_kv_append", "xp_kv_gather",
             "xp_decode_workspace_size",
             "xp_decode_attention", "xp_prefill_workspace_size", "xp_prefill_attention", "xp_probe_hw_ids",
-            "xp_probe_read",
-            "xp_probe_read", "xp_waterfill",
+            "xp_probe_read", "xp_calibrate_decode_cus", "xp_probe_read_curve", "xp_waterfill",
             "xp_iteration_latency", "xp_fit_affine", "xp_fit_latency_model", "xp_admission",
             "xp_decode_placement", "xp_schedule"]
 
@@ -76,12 +79,13 @@ class BatchDesc(C.Structure):
                 ("chunk_len", C.c_int32), ("prior_len", C.c_int32), ("sp_degree", C.c_int32),
                 ("sp_rank", C.c_int32), ("local_row_offset", C.c_int32), ("pre_pages", C.c_void_p),
                 ("pre_max_blocks", C.c_int32), ("peer_qkv_in", C.c_void_p), ("peer_qkv_out", C.c_void_p),
-                ("peer_attn_in", C.c_void_p), ("peer_attn_out", C.c_void_p)]
+                ("peer_attn_in", C.c_void_p), ("peer_attn_out", C.c_void_p), ("dec_ctx_host", C.c_void_p),
+                ("dec_pages_host", C.c_void_p), ("pre_pages_host", C.c_void_p)]
 
 
 class Chunk(C.Structure):
     _fields_ = [("chunk_len", C.c_int32), ("prior_len", C.c_int32), ("pre_pages", C.c_void_p),
-                ("pre_max_blocks", C.c_int32)]
+                ("pre_max_blocks", C.c_int32), ("pre_pages_host", C.c_void_p)]
 
 
 class WsLayout(C.Structure):
@@ -91,6 +95,18 @@ class WsLayout(C.Structure):
 
     def as_dict(self):
         return {f: getattr(self, f) for f, _ in self._fields_}
+
+
+XP_CU_CURVE_MAX = 64
+
+
+class CuCurve(C.Structure):
+    _fields_ = [("n_cus", C.c_int32), ("us_all", C.c_double), ("n_points", C.c_int32),
+                ("cus", C.c_int32 * XP_CU_CURVE_MAX), ("us", C.c_double * XP_CU_CURVE_MAX)]
+
+    def as_dict(self):
+        return {"n_cus": self.n_cus, "us_all": self.us_all,
+                "points": {int(self.cus[i]): float(self.us[i]) for i in range(self.n_points)}}
 
 
 class LatencyModel(C.Structure):
@@ -187,6 +203,10 @@ def _declare(L):
                                      _i32, _vp, _i32, _vp, _i32, _vp, _vp, _vp]),
         "xp_probe_hw_ids": (S, [_i32, _vp, _vp]),
         "xp_probe_read": (S, [_vp, _sz, _vp, _vp]),
+        "xp_calibrate_decode_cus": (S, [_i32, _i32, _vp, _vp, _i32, _i32, _vp, _i32, _vp, _i32, _i32, _i32, _i32,
+                                        _vp, _i32, _vp, _i32, _f64, _i32, _i32, _i32, C.POINTER(_i32),
+                                        C.POINTER(CuCurve)]),
+        "xp_probe_read_curve": (S, [_i32, _vp, _sz, _vp, _i32, _i32, C.POINTER(CuCurve)]),
         "xp_waterfill": (S, [C.POINTER(WaterfillIn), C.POINTER(WaterfillOut)]),
         "xp_iteration_latency": (S, [C.POINTER(LatencyModel), _i32, _vp, _vp, _vp, _i32, _vp, _vp,
                                      C.POINTER(_f64)]),
@@ -204,6 +224,29 @@ def _declare(L):
         fn.argtypes = args
 
 
+# Contexts and captured graphs still open.  They own HIP streams, events and graphs,
+# which are destroyed at interpreter exit by an atexit hook (registered when the
+# library is loaded, so it runs while the HIP runtime is still up) rather than left
+# to garbage collection during interpreter teardown or to the runtime's own
+# finalizers: graphs first, then the contexts whose streams they were captured on.
+_LIVE_GRAPHS = weakref.WeakSet()
+_LIVE_CTXS = weakref.WeakSet()
+
+
+def close_all():
+    """Destroys every open Graph, then every open Ctx (safe to call more than once)."""
+    for g in list(_LIVE_GRAPHS):
+        try:
+            g.close()
+        except Exception:
+            pass
+    for c in list(_LIVE_CTXS):
+        try:
+            c.close()
+        except Exception:
+            pass
+
+
 def lib():
     """The loaded library (raises if it has not been built)."""
     global _LIB
@@ -213,6 +256,7 @@ def lib():
         L = C.CDLL(LIB_PATH)
         _declare(L)
         _LIB = L
+        atexit.register(close_all)
     return _LIB
 
 
@@ -258,6 +302,7 @@ class Ctx:
         _check(lib().xp_ctx_create(C.byref(h), device, decode_cus, pages_per_split))
         self.handle = h
         self.device, self.decode_cus = device, decode_cus
+        _LIVE_CTXS.add(self)
 
     def cu_masks(self):
         dec = (C.c_uint32 * 8)()
@@ -274,8 +319,9 @@ class Ctx:
 
     def close(self):
         if getattr(self, "handle", None):
-            lib().xp_ctx_destroy(self.handle)
-            self.handle = None
+            h, self.handle = self.handle, None
+            _LIVE_CTXS.discard(self)
+            lib().xp_ctx_destroy(h)
 
     def __del__(self):
         try:
@@ -342,14 +388,16 @@ class Graph:
 
     def __init__(self, handle):
         self.handle = handle
+        _LIVE_GRAPHS.add(self)
 
     def launch(self, stream=None):
         xp_graph_launch(self, stream)
 
     def close(self):
-        if self.handle:
-            _check(lib().xp_graph_destroy(self.handle))
-            self.handle = None
+        if getattr(self, "handle", None):
+            h, self.handle = self.handle, None
+            _LIVE_GRAPHS.discard(self)
+            _check(lib().xp_graph_destroy(h))
 
     def __del__(self):
         try:
@@ -375,12 +423,20 @@ def xp_graph_destroy(graph):
     graph.close()
 
 
-def chunk_array(chunks):
-    """ctypes array of Chunk from [(chunk_len, prior_len, table tensor [Hkv, blocks])]."""
+def chunk_array(chunks, host_tables=None):
+    """ctypes array of Chunk from [(chunk_len, prior_len, table tensor [Hkv, blocks])];
+    ``host_tables``: optional host copies of the tables (validated before launch)."""
     arr = (Chunk * max(1, len(chunks)))()
+    keep = []
     for j, (l, c, t) in enumerate(chunks):
-        arr[j] = Chunk(int(l), int(c), _ptr(t), int(t.shape[-1]))
-    return arr if chunks else (Chunk * 0)()
+        h = None
+        if host_tables is not None:
+            h = np.ascontiguousarray(host_tables[j], dtype=np.int32)
+            keep.append(h)
+        arr[j] = Chunk(int(l), int(c), _ptr(t), int(t.shape[-1]), _ptr(h))
+    out = arr if chunks else (Chunk * 0)()
+    out._host = keep          # the host copies live as long as the array
+    return out
 
 
 def xp_validate_chunks(shape, desc, chunks, n_pages, dec_ctx_host, dec_pages_host, chunk_tables_host):
@@ -467,6 +523,26 @@ def xp_probe_hw_ids(n_blocks, out, stream=None):
 
 def xp_probe_read(src, nbytes, sink, stream=None):
     _check(lib().xp_probe_read(_ptr(src), nbytes, _ptr(sink), _stream(stream)))
+
+
+def xp_calibrate_decode_cus(device, dtype, q, pool, n_pages, page_size, dec_pages, dec_max_blocks, dec_ctx,
+                            n_decode, n_q_heads, n_kv_heads, head_dim, out, out_stride, workspace,
+                            pages_per_split=0, keep_fraction=0.9, cu_step=32, repeats=10, stop_at_rule=True):
+    """(decode_cus, curve dict): the pages' decode-CU rule measured on this device."""
+    k = _i32()
+    cv = CuCurve()
+    _check(lib().xp_calibrate_decode_cus(device, dtype, _ptr(q), _ptr(pool), n_pages, page_size, _ptr(dec_pages),
+                                         dec_max_blocks, _ptr(dec_ctx), n_decode, n_q_heads, n_kv_heads, head_dim,
+                                         _ptr(out), out_stride, _ptr(workspace), pages_per_split,
+                                         float(keep_fraction), cu_step, repeats, int(bool(stop_at_rule)),
+                                         C.byref(k), C.byref(cv)))
+    return k.value, cv.as_dict()
+
+
+def xp_probe_read_curve(device, src, nbytes, sink, cu_step=32, repeats=5) -> dict:
+    cv = CuCurve()
+    _check(lib().xp_probe_read_curve(device, _ptr(src), nbytes, _ptr(sink), cu_step, repeats, C.byref(cv)))
+    return cv.as_dict()
 
 
 def _model(d: dict) -> LatencyModel:

@@ -253,8 +253,9 @@ xp_status xp_ctx_create(xp_ctx** out, int32_t device, int32_t decode_cus, int32_
   c->n_cus = prop.multiProcessorCount;
   c->pps = pages_per_split;  // 0: chosen per batch
   if (decode_cus < -1 || decode_cus >= c->n_cus) {
+    const int n_cus = c->n_cus;
     delete c;
-    return fail(XP_EINVAL, "decode_cus %d (valid: -1, 0, 1..%d)", decode_cus, c->n_cus - 1);
+    return fail(XP_EINVAL, "decode_cus %d (valid: -1, 0, 1..%d)", decode_cus, n_cus - 1);
   }
   c->decode_cus = decode_cus;
   hipError_t e = hipSuccess;
@@ -418,6 +419,34 @@ xp_status xp_layer_read_status(const void* ws, const xp_ws_layout* L, uint32_t* 
 
 namespace {
 
+// The optional host copies of a step's tables (xp_batch_desc, xp_chunk): none given
+// leaves the page ids to the device-side check; otherwise every table the step reads
+// must have its copy, and the copies are checked like xp_validate_batch /
+// xp_validate_chunks before anything is launched.
+xp_status check_host_tables(const xp_layer_shape* sh, const xp_batch_desc* d, int n_pages, int n_chunks,
+                            const xp_chunk* ch) {
+  bool given = d->dec_ctx_host || d->dec_pages_host || d->pre_pages_host;
+  for (int j = 0; j < n_chunks; ++j) given = given || ch[j].pre_pages_host;
+  if (!given) return XP_OK;
+  if (d->n_decode > 0 && (!d->dec_ctx_host || !d->dec_pages_host))
+    return fail(XP_EINVAL, "host table copies: dec_ctx_host and dec_pages_host are both needed");
+  if (d->chunk_len > 0 && !d->pre_pages_host) return fail(XP_EINVAL, "host table copies: pre_pages_host is needed");
+  for (int j = 0; j < n_chunks; ++j)
+    if (!ch[j].pre_pages_host) return fail(XP_EINVAL, "host table copies: chunk %d has no pre_pages_host", j);
+  PageCheck pc(n_pages);
+  xp_status st = pc.decodes(sh, d, d->dec_ctx_host, d->dec_pages_host);
+  if (st) return st;
+  if (d->chunk_len > 0 &&
+      (st = pc.chunk(d->pre_pages_host, sh->n_kv_heads / d->sp_degree, d->pre_max_blocks, d->prior_len,
+                     d->chunk_len, sh->page_size, "prefill")))
+    return st;
+  for (int j = 0; j < n_chunks; ++j)
+    if ((st = pc.chunk(ch[j].pre_pages_host, sh->n_kv_heads, ch[j].pre_max_blocks, ch[j].prior_len, ch[j].chunk_len,
+                       sh->page_size, "chunk")))
+      return st;
+  return XP_OK;
+}
+
 // One prefill chunk as the step runs it: chunk rows [off, off + n_local) are the
 // rank's local rows [row0, row0 + n_local) of x; its rotated queries sit q_off bytes
 // into the workspace's q region.
@@ -463,6 +492,7 @@ struct LayerRun {
   void* workspace;
   const void* x;
   bool x_f32;
+  bool clear_status;  // the first layer of a call resets the device status word
 
   xp_status pre(hipStream_t s) const;
   xp_status attend(hipStream_t s, bool split) const;
@@ -483,7 +513,9 @@ xp_status LayerRun::pre(hipStream_t s) const {
   const size_t attn_row = size_t(Hq) * D * dtype_bytes(dt);
 
   // shared linear region (1): RMSNorm + QKV over all M rows
-  if ((st = launch_rmsnorm(dt, x, x_f32 ? 1 : 0, weights.g_attn, ws + L.hn, M, H, sh->rms_eps, status, s))) return st;
+  if ((st = launch_rmsnorm(dt, x, x_f32 ? 1 : 0, weights.g_attn, ws + L.hn, M, H, sh->rms_eps,
+                           clear_status ? status : nullptr, s)))
+    return st;
   if (M > 0 && (st = launch_gemm(dt, XP_EPI_F32, ws + L.hn, weights.w_qkv, nullptr, nullptr, qkv, M, ldq, H,
                                  ws + L.gemm_part, L.h1 - L.gemm_part, s)))
     return st;
@@ -602,9 +634,13 @@ xp_status check_stack(const xp_layer_shape* sh, const xp_batch_desc* d, int n_la
   if (d->sp_degree != 1) return fail(XP_EUNSUPPORTED, "layer stack: sp_degree %d (supported: 1)", d->sp_degree);
   if (n_layers < 1 || !w || !kv) return fail(XP_EINVAL, "layer stack: %d layers, weights %p, pools %p", n_layers,
                                              static_cast<const void*>(w), static_cast<const void*>(kv));
-  for (int l = 0; l < n_layers; ++l)
+  int n_pages = INT32_MAX;
+  for (int l = 0; l < n_layers; ++l) {
     if ((st = check_weights(w + l, kv + l))) return st;
-  return XP_OK;
+    n_pages = std::min(n_pages, int(kv[l].n_pages));
+  }
+  // every layer reads the same tables: a page id must lie inside every layer's pool
+  return check_host_tables(sh, d, n_pages, 0, nullptr);
 }
 
 // The runs of a stack, layer after layer over one batch: layer 0 reads desc->x; every
@@ -619,7 +655,7 @@ std::vector<LayerRun> stack_runs(xp_ctx* ctx, const xp_layer_shape* sh, const xp
   std::vector<LayerRun> runs;
   for (int l = 0; l < n_layers; ++l)
     runs.push_back(LayerRun{ctx, *sh, *d, ch, d->n_prefill_local, w[l], kv[l], out, L, workspace,
-                            l == 0 ? d->x : static_cast<const void*>(out), l > 0});
+                            l == 0 ? d->x : static_cast<const void*>(out), l > 0, l == 0});
   return runs;
 }
 
@@ -646,6 +682,7 @@ xp_status xp_layer_forward(xp_ctx* ctx, const xp_layer_shape* sh, const xp_batch
   if (st) return st;
   if ((st = check_desc(sh, d))) return st;
   if ((st = check_weights(w, kv))) return st;
+  if ((st = check_host_tables(sh, d, kv->n_pages, 0, nullptr))) return st;
   const int M = rows_of(d);
   if (M > 0 && !out) return fail(XP_EINVAL, "null out");
   const xp_ws_layout L = make_layout(ctx, sh, d);
@@ -655,7 +692,7 @@ xp_status xp_layer_forward(xp_ctx* ctx, const xp_layer_shape* sh, const xp_batch
   if (d->chunk_len > 0)
     ch.push_back(ChunkRun{d->chunk_len, d->prior_len, d->local_row_offset, d->n_prefill_local, 0, d->pre_pages,
                           d->pre_max_blocks, d->peer_qkv_in, d->peer_qkv_out, d->peer_attn_in, d->peer_attn_out, 0});
-  return run_layer(LayerRun{ctx, *sh, *d, ch, d->n_prefill_local, *w, *kv, out, L, workspace, d->x, false},
+  return run_layer(LayerRun{ctx, *sh, *d, ch, d->n_prefill_local, *w, *kv, out, L, workspace, d->x, false, true},
                    static_cast<hipStream_t>(stream));
 }
 
@@ -677,6 +714,7 @@ xp_status xp_layer_forward_chunks(xp_ctx* ctx, const xp_layer_shape* sh, const x
   if (st) return st;
   if ((st = check_desc(sh, d)) || (st = check_chunks(sh, d, n_chunks, chunks))) return st;
   if ((st = check_weights(w, kv))) return st;
+  if ((st = check_host_tables(sh, d, kv->n_pages, n_chunks, chunks))) return st;
   const xp_ws_layout L = make_layout_chunks(ctx, sh, d, n_chunks, chunks);
   if (!workspace || workspace_bytes < L.total)
     return fail(XP_EWORKSPACE, "workspace of %zu bytes < %zu required", workspace_bytes, L.total);
@@ -692,7 +730,7 @@ xp_status xp_layer_forward_chunks(xp_ctx* ctx, const xp_layer_shape* sh, const x
     q_off += size_t(c.chunk_len) * q_row;
   }
   if (rows + d->n_decode > 0 && !out) return fail(XP_EINVAL, "null out");
-  return run_layer(LayerRun{ctx, *sh, *d, ch, rows, *w, *kv, out, L, workspace, d->x, false},
+  return run_layer(LayerRun{ctx, *sh, *d, ch, rows, *w, *kv, out, L, workspace, d->x, false, true},
                    static_cast<hipStream_t>(stream));
 }
 
@@ -840,6 +878,127 @@ xp_status xp_decode_attention(int32_t dtype, const void* q, const void* pool, in
   float* po = reinterpret_cast<float*>(static_cast<char*>(workspace) + ml_bytes);
   return launch_decode(dtype, q, pool, n_pages, S, dec_pages, max_blocks, dec_ctx, n_d, Hq, Hkv, d, out, out_stride,
                        ml, po, pps, nullptr, static_cast<hipStream_t>(stream));
+}
+
+}  // extern "C"
+
+namespace {
+
+// Times `launch` (enqueued on the given stream) on every CU, then on CU-masked streams
+// of cu_step, 2 cu_step, ... CUs: `repeats` untimed launches, then `repeats` timed
+// between two events.  `stop(us_all, us_k)` ends the sweep early.  Every stream and
+// event made here is destroyed before returning.
+template <typename Launch, typename Stop>
+xp_status cu_sweep(int device, int cu_step, int repeats, Launch&& launch, Stop&& stop, xp_cu_curve* curve) {
+  ScopedDevice sd(device);
+  hipDeviceProp_t prop;
+  XP_HIP_TRY(hipGetDeviceProperties(&prop, device));
+  const int n_cus = prop.multiProcessorCount;
+  memset(curve, 0, sizeof(*curve));
+  curve->n_cus = n_cus;
+  hipEvent_t e0 = nullptr, e1 = nullptr;
+  hipStream_t s = nullptr;
+  auto cleanup = [&]() {
+    if (s) (void)hipStreamDestroy(s);
+    if (e0) (void)hipEventDestroy(e0);
+    if (e1) (void)hipEventDestroy(e1);
+    s = nullptr;
+  };
+  auto time_on = [&](double* us) -> xp_status {
+    for (int i = 0; i < repeats; ++i) {
+      xp_status st = launch(s);
+      if (st) return st;
+    }
+    XP_HIP_TRY(hipEventRecord(e0, s));
+    for (int i = 0; i < repeats; ++i) {
+      xp_status st = launch(s);
+      if (st) return st;
+    }
+    XP_HIP_TRY(hipEventRecord(e1, s));
+    XP_HIP_TRY(hipEventSynchronize(e1));
+    float ms = 0.f;
+    XP_HIP_TRY(hipEventElapsedTime(&ms, e0, e1));
+    *us = 1e3 * double(ms) / repeats;
+    return XP_OK;
+  };
+  xp_status st = XP_OK;
+  hipError_t e = hipEventCreate(&e0);
+  if (e == hipSuccess) e = hipEventCreate(&e1);
+  if (e == hipSuccess) e = hipStreamCreateWithFlags(&s, hipStreamNonBlocking);
+  if (e != hipSuccess) {
+    cleanup();
+    return fail(XP_EHIP, "CU sweep set-up: %s", hipGetErrorString(e));
+  }
+  st = time_on(&curve->us_all);
+  (void)hipStreamDestroy(s);
+  s = nullptr;
+  for (int k = cu_step; !st && k < n_cus && curve->n_points < XP_CU_CURVE_MAX; k += cu_step) {
+    uint32_t dec[8], pre[8];
+    spread_mask(n_cus, k, dec, pre);
+    e = hipExtStreamCreateWithCUMask(&s, 8, dec);
+    if (e != hipSuccess) {
+      st = fail(XP_EHIP, "hipExtStreamCreateWithCUMask(%d CUs): %s", k, hipGetErrorString(e));
+      break;
+    }
+    double us = 0.0;
+    st = time_on(&us);
+    (void)hipStreamSynchronize(s);
+    (void)hipStreamDestroy(s);
+    s = nullptr;
+    if (st) break;
+    curve->cus[curve->n_points] = k;
+    curve->us[curve->n_points] = us;
+    ++curve->n_points;
+    if (stop(curve->us_all, us)) break;
+  }
+  cleanup();
+  return st;
+}
+
+}  // namespace
+
+extern "C" {
+
+xp_status xp_calibrate_decode_cus(int32_t device, int32_t dtype, const void* q, const void* pool, int32_t n_pages,
+                                  int32_t S, const int32_t* dec_pages, int32_t max_blocks, const int32_t* dec_ctx,
+                                  int32_t n_d, int32_t Hq, int32_t Hkv, int32_t d, void* out, int32_t out_stride,
+                                  void* workspace, int32_t pps, double keep_fraction, int32_t cu_step,
+                                  int32_t repeats, int32_t stop_at_rule, int32_t* decode_cus, xp_cu_curve* curve) {
+  if (!decode_cus || !curve) return fail(XP_EINVAL, "xp_calibrate_decode_cus: null output");
+  if (!(keep_fraction > 0.0 && keep_fraction <= 1.0) || cu_step < 1 || repeats < 1)
+    return fail(XP_EINVAL, "xp_calibrate_decode_cus: keep_fraction %g, cu_step %d, repeats %d", keep_fraction,
+                cu_step, repeats);
+  if (n_d < 1) return fail(XP_ESHAPE, "xp_calibrate_decode_cus: no decode requests");
+  int n_dev = 0;
+  XP_HIP_TRY(hipGetDeviceCount(&n_dev));
+  if (device < 0 || device >= n_dev) return fail(XP_EINVAL, "xp_calibrate_decode_cus: device %d of %d", device, n_dev);
+  auto launch = [&](hipStream_t s) {
+    return xp_decode_attention(dtype, q, pool, n_pages, S, dec_pages, max_blocks, dec_ctx, n_d, Hq, Hkv, d, out,
+                               out_stride, workspace, pps, s);
+  };
+  auto meets = [&](double us_all, double us) { return us_all >= keep_fraction * us; };
+  xp_status st = cu_sweep(device, cu_step, repeats, launch,
+                          [&](double a, double u) { return stop_at_rule != 0 && meets(a, u); }, curve);
+  if (st) return st;
+  if (curve->n_points == 0) return fail(XP_EINVAL, "xp_calibrate_decode_cus: cu_step %d leaves no partition", cu_step);
+  *decode_cus = curve->cus[curve->n_points - 1];
+  for (int i = 0; i < curve->n_points; ++i)
+    if (meets(curve->us_all, curve->us[i])) {
+      *decode_cus = curve->cus[i];
+      break;
+    }
+  return XP_OK;
+}
+
+xp_status xp_probe_read_curve(int32_t device, const void* src, size_t bytes, uint32_t* sink, int32_t cu_step,
+                              int32_t repeats, xp_cu_curve* curve) {
+  if (!curve || !src || !sink || cu_step < 1 || repeats < 1 || bytes == 0 || bytes % 16)
+    return fail(XP_EINVAL, "xp_probe_read_curve: bad argument");
+  int n_dev = 0;
+  XP_HIP_TRY(hipGetDeviceCount(&n_dev));
+  if (device < 0 || device >= n_dev) return fail(XP_EINVAL, "xp_probe_read_curve: device %d of %d", device, n_dev);
+  return cu_sweep(device, cu_step, repeats, [&](hipStream_t s) { return xp_probe_read(src, bytes, sink, s); },
+                  [](double, double) { return false; }, curve);
 }
 
 size_t xp_prefill_workspace_size(int32_t hq, int32_t hkv, int32_t d, int32_t prior, int32_t chunk) {

@@ -374,10 +374,7 @@ int decode_splits(int dec_max_blocks, int pps) { return std::max(1, cdiv(dec_max
 // 8B, 14B and 32B decode batches: as fast as one workgroup per split for uniform
 // contexts, and 1.26x faster for the lognormal 32B batch, whose short requests no
 // longer leave most of a table-wide grid empty.
-#ifndef XP_DECODE_GRID_WAVES
-#define XP_DECODE_GRID_WAVES 16384
-#endif
-constexpr long kGridWaves = XP_DECODE_GRID_WAVES;
+constexpr long kGridWaves = 16384;
 int decode_grid(int n_d, int Hkv, int n_splits) {
   const long units = long(n_d) * Hkv * n_splits;   // when every request fills its table
   const long per = (units + kGridWaves - 1) / kGridWaves;
@@ -388,10 +385,7 @@ int decode_grid(int n_d, int Hkv, int n_splits) {
 // waves over the batch's (request, KV head) pairs at their table width, i.e.
 // some six resident waves per CU, and between 8 and 64 pages per wave.  Fewer,
 // longer splits write fewer partials; more splits keep more pages in flight.
-#ifndef XP_DECODE_TARGET_UNITS
-#define XP_DECODE_TARGET_UNITS 1600
-#endif
-constexpr long kTargetWaves = XP_DECODE_TARGET_UNITS;
+constexpr long kTargetWaves = 1600;
 int decode_pick_pps(int requested, int n_d, int Hkv, int dec_max_blocks) {
   if (requested > 0) return requested;
   const long work = long(n_d) * Hkv * dec_max_blocks;

@@ -46,26 +46,11 @@ namespace xp {
 namespace {
 
 constexpr int kPage = 16;
-#ifndef XP_PREFILL_NQ
-#define XP_PREFILL_NQ 1
-#endif
-#ifndef XP_PREFILL_TARGET_WAVES
-#define XP_PREFILL_TARGET_WAVES 8192
-#endif
-#ifndef XP_PREFILL_MAXW
-#define XP_PREFILL_MAXW 8
-#endif
-#ifndef XP_PREFILL_STAGES
-#define XP_PREFILL_STAGES 2
-#endif
-constexpr int kStages = XP_PREFILL_STAGES;
-#ifndef XP_PREFILL_STAGES_KS2
-#define XP_PREFILL_STAGES_KS2 3
-#endif
-#ifndef XP_PREFILL_SB
-#define XP_PREFILL_SB 2
-#endif
-constexpr int kBlocksPerStage = XP_PREFILL_SB;
+constexpr int kNQ = 1;               // 32-query column blocks per wave
+constexpr int kMaxW = 8;             // waves (query heads) per workgroup
+constexpr int kStages = 2;           // LDS ring stages, one key set
+constexpr int kStagesKS2 = 3;        // LDS ring stages, two key sets
+constexpr int kBlocksPerStage = 2;   // 32-key blocks per stage
 constexpr int kMaxBps = 256;   // key blocks per split (its page ids are staged in LDS)
 
 __device__ __forceinline__ int kappa(int i) { return (i & ~12) | ((i & 4) << 1) | ((i & 8) >> 1); }
@@ -210,7 +195,7 @@ __device__ __forceinline__ void prefill_tile(const PrefillArgs& a, int bx, int b
   constexpr int VROW_CH = kPage * EB / 16;        // 16-byte chunks per V^T row
   // blocks per stage and ring depth, within the LDS budget
   constexpr int kBudget = 144 * 1024;
-  constexpr int kSt = KS == 2 ? XP_PREFILL_STAGES_KS2 : kStages;
+  constexpr int kSt = KS == 2 ? kStagesKS2 : kStages;
   constexpr int SB = kBlocksPerStage * 2 * BLK <= kBudget
                          ? kBlocksPerStage
                          : (kBudget / (2 * BLK) > 0 ? kBudget / (2 * BLK) : 1);
@@ -621,7 +606,7 @@ struct Shape {
 Shape pick_shape(int d, int G) {
   (void)d;
   (void)G;
-  return {XP_PREFILL_NQ, XP_PREFILL_MAXW};
+  return {kNQ, kMaxW};
 }
 
 // Key blocks per split (planned for the whole device in every split-attention mode, so
@@ -742,9 +727,9 @@ template <typename T, int D>
 void launch_one(const Prepared& pr, hipStream_t s) {
   const dim3 grid(pr.n_qt * pr.p.n_split, pr.gy), block(64 * pr.p.wpg), cgrid(pr.n_qt, pr.a.hq);
   if (two_key_sets(pr, long(grid.x) * grid.y))
-    hipLaunchKernelGGL((prefill_kernel<T, D, XP_PREFILL_NQ, 4, 2>), grid, dim3(2 * block.x), 0, s, pr.a);
+    hipLaunchKernelGGL((prefill_kernel<T, D, kNQ, 4, 2>), grid, dim3(2 * block.x), 0, s, pr.a);
   else
-    hipLaunchKernelGGL((prefill_kernel<T, D, XP_PREFILL_NQ, XP_PREFILL_MAXW, 1>), grid, block, 0, s, pr.a);
+    hipLaunchKernelGGL((prefill_kernel<T, D, kNQ, kMaxW, 1>), grid, block, 0, s, pr.a);
   if (pr.p.n_split > 1) hipLaunchKernelGGL((prefill_combine_kernel<T, D>), cgrid, dim3(256), 0, s, pr.a);
 }
 
@@ -763,10 +748,10 @@ void launch_group(const Prepared* pr, int n, hipStream_t s) {
     g.cstart[k + 1] = g.cstart[k] + (sk ? pr[k].n_qt * pr[k].a.hq : 0);
   }
   if (two_key_sets(pr[0], g.start[n]))
-    hipLaunchKernelGGL((prefill_group_kernel<T, D, XP_PREFILL_NQ, 4, 2>), dim3(g.start[n]), dim3(128 * pr[0].p.wpg), 0,
+    hipLaunchKernelGGL((prefill_group_kernel<T, D, kNQ, 4, 2>), dim3(g.start[n]), dim3(128 * pr[0].p.wpg), 0,
                        s, g);
   else
-    hipLaunchKernelGGL((prefill_group_kernel<T, D, XP_PREFILL_NQ, XP_PREFILL_MAXW, 1>), dim3(g.start[n]),
+    hipLaunchKernelGGL((prefill_group_kernel<T, D, kNQ, kMaxW, 1>), dim3(g.start[n]),
                        dim3(64 * pr[0].p.wpg), 0, s, g);
   if (split) hipLaunchKernelGGL((prefill_group_combine_kernel<T, D>), dim3(g.cstart[n]), dim3(256), 0, s, g);
 }

@@ -23,13 +23,21 @@ def layer_weights(w: dict) -> X.LayerWeights:
 
 def batch_desc(*, x, n_prefill_local, n_decode, dec_ctx, dec_pages, chunk_len, prior_len, sp_degree=1,
                sp_rank=0, local_row_offset=0, pre_pages=None, peer_qkv_in=None, peer_qkv_out=None,
-               peer_attn_in=None, peer_attn_out=None) -> X.BatchDesc:
+               peer_attn_in=None, peer_attn_out=None, dec_ctx_host=None, dec_pages_host=None,
+               pre_pages_host=None) -> X.BatchDesc:
+    """The descriptor struct; the optional ``*_host`` numpy copies of the tables make the
+    step validate every page id on the host before it launches anything."""
+    import numpy as np
     dmb = int(dec_pages.shape[-1]) if (dec_pages is not None and dec_pages.dim() == 3) else 0
     pmb = int(pre_pages.shape[-1]) if (pre_pages is not None and pre_pages.dim() == 2) else 0
     P = X._ptr
-    return X.BatchDesc(P(x), n_prefill_local, n_decode, P(dec_ctx), P(dec_pages), dmb, chunk_len, prior_len,
-                       sp_degree, sp_rank, local_row_offset, P(pre_pages), pmb, P(peer_qkv_in), P(peer_qkv_out),
-                       P(peer_attn_in), P(peer_attn_out))
+    host = [None if a is None else np.ascontiguousarray(a, dtype=np.int32)
+            for a in (dec_ctx_host, dec_pages_host, pre_pages_host)]
+    d = X.BatchDesc(P(x), n_prefill_local, n_decode, P(dec_ctx), P(dec_pages), dmb, chunk_len, prior_len,
+                    sp_degree, sp_rank, local_row_offset, P(pre_pages), pmb, P(peer_qkv_in), P(peer_qkv_out),
+                    P(peer_attn_in), P(peer_attn_out), *[P(a) for a in host])
+    d._host = host            # the host copies live as long as the struct
+    return d
 
 
 class LayerStep:

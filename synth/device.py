@@ -77,8 +77,10 @@ def upload(inst: Instance, device="cuda") -> DeviceInstance:
     return DeviceInstance(inst, device)
 
 
-def make_step(inst: Instance, ctx, dev: DeviceInstance | None = None):
-    """A LayerStep of the package for this instance (imports the HIP binding)."""
+def make_step(inst: Instance, ctx, dev: DeviceInstance | None = None, host_tables: bool = False):
+    """A LayerStep of the package for this instance (imports the HIP binding).  With
+    ``host_tables`` the descriptor also carries host copies of the page tables, so the
+    step checks every page id on the host before it launches."""
     from mixed_prefill_decode_amd import LayerStep, batch_desc, layer_shape, layer_weights
     wl = inst.wl
     dev = dev or upload(inst)
@@ -90,7 +92,10 @@ def make_step(inst: Instance, ctx, dev: DeviceInstance | None = None):
                       prior_len=wl.prior_len, sp_degree=wl.sp_degree, sp_rank=wl.sp_rank,
                       local_row_offset=wl.local_row_offset, pre_pages=dev.pre_pages if wl.chunk_len else None,
                       peer_qkv_in=dev.peer_qkv_in, peer_qkv_out=dev.peer_qkv_out,
-                      peer_attn_in=dev.peer_attn_in, peer_attn_out=dev.peer_attn_out)
+                      peer_attn_in=dev.peer_attn_in, peer_attn_out=dev.peer_attn_out,
+                      dec_ctx_host=inst.dec_ctx if host_tables else None,
+                      dec_pages_host=inst.dec_pages if host_tables else None,
+                      pre_pages_host=inst.pre_pages if host_tables else None)
     step = LayerStep(ctx, shape, desc, layer_weights(dev.weights), dev.pool, inst.pool.n_pages,
                      keep=(dev,))
     return step, dev

@@ -37,7 +37,7 @@ __all__ = [
     "f32_to_bf16_bits", "bf16_bits_to_f32", "storage_to_f64",
     "waterfill_cases", "make_latency_model", "SchedulerCase", "scheduler_case",
     "MultiChunkWorkload", "MultiChunkInstance", "make_multi_instance", "MULTI_CHUNK_WORKLOADS",
-    "StackInstance", "make_stack_instance",
+    "StackInstance", "make_stack_instance", "save_instance", "load_instance",
 ]
 
 TENSOR_IDS = {
@@ -383,6 +383,11 @@ PARITY_WORKLOADS = {
     # halves of each unit differ in length) and merged
     "P6": Workload("P6", 106, "bf16", 512, 32, 8, 128, 1024, n_decode=0, ctx=("fixed", 0),
                    chunk_len=300, prior_len=1500, description="prefill only, 8B heads, 300 after 1500"),
+    # long decode contexts on the 32B head layout (64 q / 8 kv heads): the shortest and
+    # longest requests of the 32B decode batch (502 and 48957 cached tokens) and the 8K and
+    # 32K contexts of the 8B batches, for decode-attention parity on identical inputs
+    "L1": Workload("L1", 121, "bf16", 1024, 64, 8, 128, 2048, n_decode=4, ctx=("list", [502, 8192, 32768, 48957]),
+                   chunk_len=0, prior_len=0, description="decode only, 32B heads, 502 / 8K / 32K / 49K contexts"),
     # decode only
     "E1": Workload("E1", 111, "bf16", 512, 8, 2, 128, 1024, n_decode=9, ctx=("uniform", 1, 2000),
                    chunk_len=0, prior_len=0, description="decode only"),
@@ -684,3 +689,46 @@ def make_stack_instance(wl: Workload, n_layers: int) -> StackInstance:
                 arr[ids] = pool._poison(arr[ids].copy(), ids)
         layers.append({"weights": w, "pool": pool})
     return StackInstance(base, layers)
+
+
+# ---------------------------------------------------------------------------
+# A drawn instance stored as plain .npy arrays plus a JSON description (no
+# pickling), so another process can map the same inputs instead of drawing them
+# again.
+# ---------------------------------------------------------------------------
+
+def save_instance(inst: Instance, path: str) -> None:
+    import json
+    import os
+    os.makedirs(path, exist_ok=True)
+    arrays = {"x": inst.x, "dec_ctx": inst.dec_ctx, "dec_pages": inst.dec_pages, "pre_pages": inst.pre_pages,
+              "peer_qkv_in": inst.peer_qkv_in, "peer_attn_in": inst.peer_attn_in,
+              "valid_slots": inst.pool.valid_slots}
+    arrays.update({"w." + k: v for k, v in inst.weights.items()})
+    pool = inst.pool
+    if pool.array is not None:
+        arrays["pool"] = pool.array
+    else:
+        arrays["bank"], arrays["bank_idx"] = pool.bank, pool.bank_idx
+    for k, v in arrays.items():
+        np.save(os.path.join(path, k + ".npy"), np.ascontiguousarray(v), allow_pickle=False)
+    meta = {"workload": inst.wl.name, "n_pages": pool.n_pages, "row_shape": list(pool.row_shape),
+            "dtype": pool.dtype, "page_size": pool.page_size, "head_dim": pool.head_dim,
+            "weights": sorted(inst.weights), "arrays": sorted(arrays)}
+    with open(os.path.join(path, "instance.json"), "w") as f:
+        json.dump(meta, f)
+
+
+def load_instance(path: str) -> Instance:
+    """The instance save_instance stored (arrays memory-mapped read-only)."""
+    import json
+    import os
+    meta = json.load(open(os.path.join(path, "instance.json")))
+    a = {k: np.load(os.path.join(path, k + ".npy"), mmap_mode="r", allow_pickle=False) for k in meta["arrays"]}
+    pool = PagePool(meta["n_pages"], tuple(meta["row_shape"]), meta["dtype"], np.asarray(a["valid_slots"]),
+                    meta["page_size"], meta["head_dim"], array=a.get("pool"), bank=a.get("bank"),
+                    bank_idx=a.get("bank_idx"))
+    weights = {k: a["w." + k] for k in meta["weights"]}
+    return Instance(get_workload(meta["workload"]), a["x"], weights, np.asarray(a["dec_ctx"]),
+                    np.asarray(a["dec_pages"]), np.asarray(a["pre_pages"]), pool, a["peer_qkv_in"],
+                    a["peer_attn_in"])

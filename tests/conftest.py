@@ -25,3 +25,8 @@ def pytest_collection_modifyitems(config, items):
     for it in items:
         if "gpu" in it.keywords:
             it.add_marker(skip)
+
+
+def pytest_sessionfinish(session, exitstatus):
+    from tests.helpers import close_shared_ctxs
+    close_shared_ctxs()

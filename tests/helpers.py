@@ -53,3 +53,22 @@ def stack_oracle_kwargs(sinst, **extra):
     kw["layers"] = sinst.layers
     kw.update(extra)
     return kw
+
+
+# Contexts shared by the GPU test modules, keyed by decode CU count; closed at the end
+# of the session (conftest.pytest_sessionfinish), before interpreter exit.
+_CTXS = {}
+
+
+def shared_ctx(decode_cus=0):
+    import mixed_prefill_decode_amd as X
+    c = _CTXS.get(decode_cus)
+    if c is None or c.handle is None:
+        c = _CTXS[decode_cus] = X.Ctx(0, decode_cus, 0)
+    return c
+
+
+def close_shared_ctxs():
+    for c in _CTXS.values():
+        c.close()
+    _CTXS.clear()

@@ -416,3 +416,19 @@ def test_chunk_tables_are_validated_on_the_host():
     bad = [t.copy() for t in inst.chunk_pages]
     bad[3][0, 1] = int(inst.chunk_pages[0][0, 0])                      # named twice
     assert X.xp_validate_chunks(shape, desc, chunks, n, inst.dec_ctx, dec_pages, bad) == -3
+
+
+def test_calibration_entry_points_check_their_arguments_on_the_host():
+    # every check below fails before the library touches a device
+    L = X.lib()
+    import ctypes as C
+    cv = X.CuCurve()
+    kk = C.c_int32()
+    args = [0, X.XP_BF16, 1, 1, 10, 16, 1, 4, 1, 2, 8, 2, 128, 1, 1024, 1, 0]
+    assert L.xp_calibrate_decode_cus(*args, 0.9, 32, 5, 1, None, C.byref(cv)) == -1       # null output
+    assert L.xp_calibrate_decode_cus(*args, 1.5, 32, 5, 1, C.byref(kk), C.byref(cv)) == -1  # fraction > 1
+    assert L.xp_calibrate_decode_cus(*args, 0.9, 0, 5, 1, C.byref(kk), C.byref(cv)) == -1   # cu_step 0
+    assert L.xp_calibrate_decode_cus(*args, 0.9, 32, 0, 1, C.byref(kk), C.byref(cv)) == -1  # no repeats
+    assert L.xp_probe_read_curve(0, 1, 15, 1, 32, 5, C.byref(cv)) == -1                     # bytes % 16
+    assert L.xp_probe_read_curve(0, None, 16, 1, 32, 5, C.byref(cv)) == -1
+    assert "xp_probe_read_curve" in X.xp_last_error()

@@ -14,17 +14,11 @@ from oracle import layer as L
 from oracle.numerics import to_f64
 from synth import MULTI_CHUNK_WORKLOADS, make_multi_instance
 from synth.device import make_chunked_step, to_host_bits
-from tests.helpers import chunk_oracle_kwargs, rel_fro
+from tests.helpers import chunk_oracle_kwargs, rel_fro, shared_ctx
 
 pytestmark = pytest.mark.gpu
 
-_CTX = {}
-
-
-def ctx(decode_cus=0):
-    if decode_cus not in _CTX:
-        _CTX[decode_cus] = X.Ctx(0, decode_cus, 0)
-    return _CTX[decode_cus]
+ctx = shared_ctx
 
 
 def _tdt(dt):

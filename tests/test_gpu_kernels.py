@@ -264,6 +264,38 @@ def test_decode_attention(name, pps):
         assert rel_fro(got[i], ref[i]) < 2 * ATTN_TOL[dt], i
 
 
+def test_decode_attention_long_contexts():
+    """Identical inputs at 502, 8K, 32K and 49K cached tokens on the 32B head layout (the
+    longest decode of the 32B batch takes the most key splits): each request within the
+    attention bar on its own, in the split size the layer picks and in single-page splits."""
+    inst = make_instance(get_workload("L1"))
+    wl, dt = inst.wl, inst.wl.dtype
+    rng = np.random.default_rng(8)
+    dpool = upload_pool(inst)
+    kv = L.PagedKV(inst.pool, dt, wl.page_size, wl.head_dim)
+    _append_decode_tokens(inst, dpool, rng, kv)
+    q = _rand(rng, (wl.n_decode, wl.n_q_heads, wl.head_dim), dt)
+    ref = L.decode_attention(to_f64(q, dt), kv, inst.dec_pages, inst.dec_ctx, wl.n_kv_heads)
+    errs = {}
+    for pps in (0, 1):
+        out = torch.full((wl.n_decode, wl.n_q_heads * wl.head_dim), float("nan"), dtype=torch.bfloat16,
+                         device="cuda")
+        ws = torch.empty(X.xp_decode_workspace_size(wl.n_decode, wl.n_q_heads, wl.n_kv_heads, wl.head_dim,
+                                                    inst.dec_max_blocks, pps), dtype=torch.uint8, device="cuda")
+        X.xp_decode_attention(DT[dt], to_device(q, dt), dpool, inst.pool.n_pages, wl.page_size,
+                              to_device(inst.dec_pages, "i32"), inst.dec_max_blocks,
+                              to_device(inst.dec_ctx, "i32"), wl.n_decode, wl.n_q_heads, wl.n_kv_heads,
+                              wl.head_dim, out, wl.n_q_heads * wl.head_dim, ws, pps)
+        _sync()
+        got = to_f64(to_host_bits(out), dt).reshape(ref.shape)
+        assert np.isfinite(got).all()
+        errs[pps] = [rel_fro(got[i], ref[i]) for i in range(wl.n_decode)]
+    print(f"[decode long] per-request rel-Frobenius {dict(zip(inst.dec_ctx.tolist(), errs[0]))} "
+          f"(single-page splits {errs[1]})", flush=True)
+    for pps, e in errs.items():
+        assert max(e) < ATTN_TOL[dt], (pps, e)
+
+
 @pytest.mark.parametrize("name", ["P1", "P2", "P3", "P4", "P5", "P6", "E2", "C1", "E4"])
 def test_prefill_attention(name):
     inst = make_instance(get_workload(name))

@@ -17,18 +17,12 @@ from oracle import layer as L
 from oracle.numerics import to_f64
 from synth import get_workload, make_instance
 from synth.device import make_step, to_host_bits, upload
-from tests.helpers import oracle_kwargs, rel_fro
+from tests.helpers import oracle_kwargs, rel_fro, shared_ctx
 
 pytestmark = pytest.mark.gpu
 
 SMALL = ["P1", "P2", "P3", "P4", "P5", "P6", "E1", "E2", "E3", "E4", "C1"]
-_CTX = {}
-
-
-def ctx(decode_cus=0):
-    if decode_cus not in _CTX:
-        _CTX[decode_cus] = X.Ctx(0, decode_cus, 0)
-    return _CTX[decode_cus]
+ctx = shared_ctx
 
 
 def _bits(a):
@@ -191,3 +185,105 @@ def test_cu_masks_partition_the_chip():
     bits_p = sum(bin(w).count("1") for w in pre)
     assert bits_d == 64 and bits_d + bits_p == n
     assert all((a & b) == 0 for a, b in zip(dec, pre))
+
+
+def test_host_table_copies_validate_before_launch():
+    """With host copies of its tables the step checks every page id on the host and
+    launches nothing on a bad one (XP_EPAGE); without them the device check flags it."""
+    inst = make_instance(get_workload("P1"))
+    ref_step, dev = make_step(inst, ctx(0))
+    ref = ref_step.run().clone()
+    torch.cuda.synchronize()
+    step, _ = make_step(inst, ctx(0), dev, host_tables=True)
+    got = step.run()
+    torch.cuda.synchronize()
+    assert step.status() == 0
+    assert torch.equal(got, ref)                       # valid copies: the same step
+    wl = inst.wl
+    for what in ("range", "twice", "short"):
+        dec_pages, pre_pages, dec_ctx = inst.dec_pages.copy(), inst.pre_pages.copy(), inst.dec_ctx.copy()
+        if what == "range":
+            dec_pages[1, 0, 0] = inst.pool.n_pages
+        elif what == "twice":
+            pre_pages[0, 1] = pre_pages[0, 0]
+        else:
+            dec_ctx[0] = inst.dec_max_blocks * wl.page_size
+        desc = X.batch_desc(x=dev.x, n_prefill_local=wl.n_prefill_local, n_decode=wl.n_decode,
+                            dec_ctx=dev.dec_ctx, dec_pages=dev.dec_pages, chunk_len=wl.chunk_len,
+                            prior_len=wl.prior_len, sp_degree=wl.sp_degree, sp_rank=wl.sp_rank,
+                            local_row_offset=wl.local_row_offset, pre_pages=dev.pre_pages,
+                            peer_qkv_in=dev.peer_qkv_in, peer_qkv_out=dev.peer_qkv_out,
+                            peer_attn_in=dev.peer_attn_in, peer_attn_out=dev.peer_attn_out,
+                            dec_ctx_host=dec_ctx, dec_pages_host=dec_pages, pre_pages_host=pre_pages)
+        pool0 = dev.pool.clone()
+        step.out.fill_(7.0)
+        torch.cuda.synchronize()
+        with pytest.raises(X.XpError) as e:
+            X.xp_layer_forward(step.ctx, step.shape, desc, step.weights, step.kv, step.out, step.workspace,
+                               step.layout.total)
+        torch.cuda.synchronize()
+        assert e.value.status == -3, what
+        assert bool((step.out == 7.0).all()), what           # nothing was launched
+        assert torch.equal(dev.pool.view(torch.int16), pool0.view(torch.int16)), what
+    # copies of only some of the tables the step reads
+    part = X.batch_desc(x=dev.x, n_prefill_local=wl.n_prefill_local, n_decode=wl.n_decode, dec_ctx=dev.dec_ctx,
+                        dec_pages=dev.dec_pages, chunk_len=wl.chunk_len, prior_len=wl.prior_len,
+                        pre_pages=dev.pre_pages, dec_ctx_host=inst.dec_ctx, dec_pages_host=inst.dec_pages)
+    with pytest.raises(X.XpError) as e:
+        X.xp_layer_forward(step.ctx, step.shape, part, step.weights, step.kv, step.out, step.workspace,
+                           step.layout.total)
+    assert e.value.status == -1
+
+
+def test_ctx_create_rejects_out_of_range_decode_cus():
+    n = ctx(0).cu_masks()[2]
+    for k in (n, n + 5, -2):
+        with pytest.raises(X.XpError) as e:
+            X.Ctx(0, k, 0)
+        assert e.value.status == -1
+        assert str(n - 1) in str(e.value)
+
+
+def test_calibrate_decode_cus_through_the_abi():
+    """The pages' rule measured by the library: the chosen k is the first CU count whose
+    decode time is within 1/0.9 of the all-CU time (or the largest tried), and the
+    calibration's launches compute what a plain decode-attention call computes."""
+    inst = make_instance(get_workload("E1"))
+    step, dev = make_step(inst, ctx(0))
+    step.run()
+    torch.cuda.synchronize()
+    wl, lay = inst.wl, step.layout
+    q = int(step.workspace.data_ptr()) + lay.q_dec
+    dws = torch.empty(X.xp_decode_workspace_size(wl.n_decode, wl.n_q_heads, wl.n_kv_heads, wl.head_dim,
+                                                 inst.dec_max_blocks, 0), dtype=torch.uint8, device="cuda")
+    tdt = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
+    dt = X.XP_BF16 if wl.dtype == "bf16" else X.XP_F32
+    ref = torch.empty((wl.n_decode, wl.n_q_heads * wl.head_dim), dtype=tdt, device="cuda")
+    X.xp_decode_attention(dt, q, dev.pool, inst.pool.n_pages, wl.page_size, dev.dec_pages, inst.dec_max_blocks,
+                          dev.dec_ctx, wl.n_decode, wl.n_q_heads, wl.n_kv_heads, wl.head_dim, ref,
+                          wl.n_q_heads * wl.head_dim, dws, 0)
+    torch.cuda.synchronize()
+    out = torch.full_like(ref, float("nan"))
+    k, curve = X.xp_calibrate_decode_cus(0, dt, q, dev.pool, inst.pool.n_pages, wl.page_size, dev.dec_pages,
+                                         inst.dec_max_blocks, dev.dec_ctx, wl.n_decode, wl.n_q_heads,
+                                         wl.n_kv_heads, wl.head_dim, out, wl.n_q_heads * wl.head_dim, dws,
+                                         keep_fraction=0.9, cu_step=64, repeats=3, stop_at_rule=False)
+    torch.cuda.synchronize()
+    assert torch.equal(out, ref)
+    pts = curve["points"]
+    assert sorted(pts) == list(range(64, curve["n_cus"], 64))
+    ok = [c for c in sorted(pts) if curve["us_all"] >= 0.9 * pts[c]]
+    assert k == (ok[0] if ok else max(pts))
+    assert all(t > 0 for t in pts.values()) and curve["us_all"] > 0
+    with pytest.raises(X.XpError):
+        X.xp_calibrate_decode_cus(0, dt, q, dev.pool, inst.pool.n_pages, wl.page_size, dev.dec_pages,
+                                  inst.dec_max_blocks, dev.dec_ctx, wl.n_decode, wl.n_q_heads, wl.n_kv_heads,
+                                  wl.head_dim, out, wl.n_q_heads * wl.head_dim, dws, keep_fraction=1.5)
+
+
+def test_probe_read_curve_through_the_abi():
+    buf = torch.zeros(1 << 26, dtype=torch.uint8, device="cuda")
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    curve = X.xp_probe_read_curve(0, buf, buf.numel(), sink, cu_step=128, repeats=2)
+    assert sorted(curve["points"]) == list(range(128, curve["n_cus"], 128))
+    assert int(sink.item()) == 0                       # zeros never reach the sink

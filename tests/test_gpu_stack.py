@@ -17,17 +17,11 @@ from oracle import layer as L
 from oracle.numerics import to_f64
 from synth import get_workload, make_stack_instance
 from synth.device import make_stack_step, to_host_bits
-from tests.helpers import rel_fro, stack_oracle_kwargs
+from tests.helpers import rel_fro, stack_oracle_kwargs, shared_ctx
 
 pytestmark = pytest.mark.gpu
 
-_CTX = {}
-
-
-def ctx(decode_cus=0):
-    if decode_cus not in _CTX:
-        _CTX[decode_cus] = X.Ctx(0, decode_cus, 0)
-    return _CTX[decode_cus]
+ctx = shared_ctx
 
 
 def _bits(a):
@@ -139,3 +133,23 @@ def test_stack_arguments_are_checked_before_launch():
     with pytest.raises(ValueError):
         X.xp_stack_forward(step.ctx, step.shape, step.desc, step.weights, X.pools_array([]), step.out,
                            step.workspace, step.layout.total)
+
+
+def test_stack_status_keeps_a_bad_page_of_any_layer():
+    """The device status word is cleared once per stack call: a page id that only layer
+    0's pool lacks is still reported after the last layer."""
+    sinst = make_stack_instance(get_workload("P2"), 2)
+    step = make_stack_step(sinst, ctx(0))
+    base = sinst.base
+    used = np.concatenate([base.dec_pages.reshape(-1), base.pre_pages.reshape(-1)])
+    top = int(used[used >= 0].max())
+    pools = [(step.pool_tensors[0], top)] + [(p, l["pool"].n_pages) for p, l in
+                                             zip(step.pool_tensors[1:], sinst.layers[1:])]
+    step.pools = X.pools_array(pools)              # layer 0's pool ends below the largest id
+    step.run()
+    torch.cuda.synchronize()
+    assert step.status() & X.XP_DEV_BAD_PAGE
+    ok = make_stack_step(sinst, ctx(0))
+    ok.run()
+    torch.cuda.synchronize()
+    assert ok.status() == 0

@@ -67,3 +67,17 @@ def test_workload_shapes_are_consistent():
     assert WORKLOADS["C2"].n_rows == 1040 and WORKLOADS["C3"].n_rows == 536
     assert WORKLOADS["C4"].n_rows == 128 and WORKLOADS["C5"].n_rows == 544
     assert len(waterfill_cases()) >= 3
+
+
+def test_saved_instance_maps_back_identically(tmp_path):
+    from synth import load_instance, save_instance
+    inst = make_instance(get_workload("P1"))
+    save_instance(inst, str(tmp_path))
+    back = load_instance(str(tmp_path))
+    assert back.wl == inst.wl
+    for a, b in ((back.x, inst.x), (back.dec_ctx, inst.dec_ctx), (back.dec_pages, inst.dec_pages),
+                 (back.pre_pages, inst.pre_pages), (back.peer_qkv_in, inst.peer_qkv_in),
+                 (back.peer_attn_in, inst.peer_attn_in), (back.pool.array, inst.pool.array),
+                 (back.pool.valid_slots, inst.pool.valid_slots)):
+        assert np.array_equal(np.asarray(a), np.asarray(b))
+    assert all(np.array_equal(back.weights[k], inst.weights[k]) for k in inst.weights)
