@@ -539,9 +539,11 @@ def read_curve(X, torch, repeats) -> dict:
             "curve_GBs": {k: round(gb / (us * 1e-6), 1) for k, us in c["points"].items()}}
 
 
-def kernel_calls(X, torch, inst, step, dev):
+def kernel_calls(X, torch, inst, step, dev, plan_cus=0):
     """Launchers of the step's kernels on their own, through the C ABI, on the step's
-    workspace (torch's current stream): name -> (call, algorithmic work, unit)."""
+    workspace (torch's current stream): name -> (call, algorithmic work, unit).  The
+    prefill attention plans its key splits for plan_cus CUs (0: all of them), as the
+    step's context does."""
     wl = inst.wl
     lay, ws, w = step.layout, int(step.workspace.data_ptr()), dev.weights
     M, H, F = wl.n_rows, wl.hidden, wl.ffn_dim
@@ -579,7 +581,7 @@ def kernel_calls(X, torch, inst, step, dev):
             X.xp_prefill_attention(X.XP_BF16, ws + lay.q_pre, dev.pool, inst.pool.n_pages, wl.page_size,
                                    dev.pre_pages, inst.pre_max_blocks, hq, wl.hkv_loc, d, wl.prior_len,
                                    wl.chunk_len, 0, wl.chunk_len, pout, hq * d, None, hq * d, ws + lay.pre_part,
-                                   None, stream)
+                                   None, stream, plan_cus=plan_cus)
         pre._keep = (pout,)
         out["prefill_attn"] = (pre, float(prefill_flops(wl)), "flop")
     return out
@@ -602,7 +604,8 @@ def window_times(X, torch, inst, step, dev, ctx, repeats) -> dict:
     launches them, each timed with events on its own stream (the figures the pages'
     overlap rule is about: decode's bandwidth and prefill's MFMA rate while the other
     one runs)."""
-    calls = kernel_calls(X, torch, inst, step, dev)
+    k = ctx.decode_cus
+    calls = kernel_calls(X, torch, inst, step, dev, plan_cus=ctx.cu_masks()[2] - k if k > 0 else 0)
     dec, dbytes, _ = calls["decode_attn"]
     pre, pflops, _ = calls["prefill_attn"]
     s_dec, s_pre = ctx.streams()
@@ -742,7 +745,7 @@ def main():
             seg["serialized_layer_us"] = round(timer(step0.run, args.repeats) * 1e6, 1)
             sweep, windows = {}, {}
             best = (seg["serialized_layer_us"], 0)
-            for kk in sorted({-1, 64, 96, 128, 160, k_rule}):
+            for kk in sorted({-1, 64, 80, 96, 112, 128, 160, k_rule}):
                 r = run_probe(args, str(kk), cache)
                 t = r["layer_us"]
                 sweep["unmasked" if kk < 0 else kk] = t

@@ -198,9 +198,9 @@ def _declare(L):
         "xp_decode_workspace_size": (_sz, [_i32, _i32, _i32, _i32, _i32, _i32]),
         "xp_decode_attention": (S, [_i32, _vp, _vp, _i32, _i32, _vp, _i32, _vp, _i32, _i32, _i32, _i32, _vp,
                                     _i32, _vp, _i32, _vp]),
-        "xp_prefill_workspace_size": (_sz, [_i32, _i32, _i32, _i32, _i32]),
+        "xp_prefill_workspace_size": (_sz, [_i32, _i32, _i32, _i32, _i32, _i32]),
         "xp_prefill_attention": (S, [_i32, _vp, _vp, _i32, _i32, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
-                                     _i32, _vp, _i32, _vp, _i32, _vp, _vp, _vp]),
+                                     _i32, _vp, _i32, _vp, _i32, _vp, _i32, _vp, _vp]),
         "xp_probe_hw_ids": (S, [_i32, _vp, _vp]),
         "xp_probe_read": (S, [_vp, _sz, _vp, _vp]),
         "xp_calibrate_decode_cus": (S, [_i32, _i32, _vp, _vp, _i32, _i32, _vp, _i32, _vp, _i32, _i32, _i32, _i32,
@@ -504,17 +504,17 @@ def xp_decode_attention(dtype, q, pool, n_pages, page_size, dec_pages, dec_max_b
                                      _ptr(out), out_stride, _ptr(workspace), pages_per_split, _stream(stream)))
 
 
-def xp_prefill_workspace_size(hq, hkv, head_dim, prior_len, chunk_len) -> int:
-    return int(lib().xp_prefill_workspace_size(hq, hkv, head_dim, prior_len, chunk_len))
+def xp_prefill_workspace_size(hq, hkv, head_dim, prior_len, chunk_len, plan_cus=0) -> int:
+    return int(lib().xp_prefill_workspace_size(hq, hkv, head_dim, prior_len, chunk_len, plan_cus))
 
 
 def xp_prefill_attention(dtype, q, pool, n_pages, page_size, pre_pages, pre_max_blocks, hq, hkv, head_dim,
                          prior_len, chunk_len, off, n_local, out_local, out_local_stride, out_peer,
-                         out_peer_stride, workspace=None, status=None, stream=None):
+                         out_peer_stride, workspace=None, status=None, stream=None, plan_cus=0):
     _check(lib().xp_prefill_attention(dtype, _ptr(q), _ptr(pool), n_pages, page_size, _ptr(pre_pages),
                                       pre_max_blocks, hq, hkv, head_dim, prior_len, chunk_len, off, n_local,
                                       _ptr(out_local), out_local_stride, _ptr(out_peer), out_peer_stride,
-                                      _ptr(workspace), _ptr(status), _stream(stream)))
+                                      _ptr(workspace), plan_cus, _ptr(status), _stream(stream)))
 
 
 def xp_probe_hw_ids(n_blocks, out, stream=None):

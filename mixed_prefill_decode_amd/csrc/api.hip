@@ -136,10 +136,17 @@ xp_status check_desc(const xp_layer_shape* sh, const xp_batch_desc* d) {
   return XP_OK;
 }
 
-// CUs the prefill key-split plan assumes: the whole device in every split-attention
-// mode, so that the mode never changes which partials are summed (serialized,
-// concurrent and partitioned steps give bit-identical results)
-int prefill_cus(const xp_ctx* ctx) { return ctx ? ctx->n_cus : device_cus(); }
+// CUs the prefill key-split plan assumes: the CUs the prefill attention runs on (the
+// whole device when serialized or unmasked, the prefill side of a CU partition
+// otherwise), so that its work units fill them in few rounds.  The split points, and
+// so the order in which a row's partial sums are merged, follow from that count: a
+// CU-partitioned step can differ from a serialized one in the last bits of the
+// prefill rows (each is within the attention tolerance of the oracle).
+int prefill_cus(const xp_ctx* ctx) {
+  if (!ctx) return device_cus();
+  return ctx->decode_cus > 0 ? ctx->n_cus - ctx->decode_cus : ctx->n_cus;
+}
+int plan_cus_or_device(int plan_cus) { return plan_cus > 0 ? plan_cus : device_cus(); }
 
 // Prefill side of a step's workspace: the rotated chunk queries and the key-split
 // partials, for one chunk (the descriptor's) or a list of chunks run one after another.
@@ -1001,23 +1008,26 @@ xp_status xp_probe_read_curve(int32_t device, const void* src, size_t bytes, uin
                   [](double, double) { return false; }, curve);
 }
 
-size_t xp_prefill_workspace_size(int32_t hq, int32_t hkv, int32_t d, int32_t prior, int32_t chunk) {
-  if (hq <= 0 || hkv <= 0 || hq % hkv || d <= 0 || prior < 0 || chunk <= 0) return 0;
-  return prefill_ws_bytes(hq, hkv, d, prior, chunk, device_cus());
+size_t xp_prefill_workspace_size(int32_t hq, int32_t hkv, int32_t d, int32_t prior, int32_t chunk,
+                                 int32_t plan_cus) {
+  if (hq <= 0 || hkv <= 0 || hq % hkv || d <= 0 || prior < 0 || chunk <= 0 || plan_cus < 0) return 0;
+  return prefill_ws_bytes(hq, hkv, d, prior, chunk, plan_cus_or_device(plan_cus));
 }
 
 xp_status xp_prefill_attention(int32_t dtype, const void* q, const void* pool, int32_t n_pages, int32_t S,
                                const int32_t* pre_pages, int32_t pre_max_blocks, int32_t hq, int32_t hkv, int32_t d,
                                int32_t prior, int32_t chunk, int32_t off, int32_t n_local, void* out_local,
                                int32_t out_local_stride, void* out_peer, int32_t out_peer_stride, void* workspace,
-                               uint32_t* status, void* stream) {
+                               int32_t plan_cus, uint32_t* status, void* stream) {
   if (chunk < 0 || prior < 0) return fail(XP_ESHAPE, "xp_prefill_attention: chunk/prior");
+  if (plan_cus < 0) return fail(XP_EINVAL, "xp_prefill_attention: plan_cus %d", plan_cus);
   if (chunk == 0) return XP_OK;
   if (!q || !pool || !pre_pages) return fail(XP_EINVAL, "xp_prefill_attention: null pointer");
   if (n_local > 0 && (!out_local || out_local_stride < hq * d)) return fail(XP_EINVAL, "xp_prefill_attention: out_local");
   if (chunk - n_local > 0 && (!out_peer || out_peer_stride < hq * d)) return fail(XP_EINVAL, "xp_prefill_attention: out_peer");
   return launch_prefill(dtype, q, pool, n_pages, S, pre_pages, pre_max_blocks, hq, hkv, d, prior, chunk, off, n_local,
-                        out_local, out_local_stride, out_peer, out_peer_stride, workspace, status, device_cus(),
+                        out_local, out_local_stride, out_peer, out_peer_stride, workspace, status,
+                        plan_cus_or_device(plan_cus),
                         static_cast<hipStream_t>(stream));
 }
 

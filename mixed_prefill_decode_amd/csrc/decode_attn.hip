@@ -96,14 +96,38 @@ __device__ __forceinline__ void bload(Frag4<float>& f, __amdgpu_buffer_rsrc_t r,
   f.v = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kLoadAux));
 }
 
-// K plane token-major [16][D]: lane l reads key l%16, dims [32*st + 8*(l/16), +8).
+// byte offset of slot `key`, dim j inside a page's K plane (chunk-major, k_elem)
+template <typename T>
+__device__ __forceinline__ int k_byte(int key, int j) {
+  return int(k_elem<T>(key, j, kPage)) * St<T>::bytes;
+}
+
+// K fragment of one key: dims [j0, j0 + 8) (one 16-byte chunk for bf16, two for fp32)
+__device__ __forceinline__ void bload_k(Frag8<bf16_t>& f, __amdgpu_buffer_rsrc_t r, int key, int j0) {
+  f.v = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, k_byte<bf16_t>(key, j0), 0, kLoadAux));
+}
+__device__ __forceinline__ void bload_k(Frag8<float>& f, __amdgpu_buffer_rsrc_t r, int key, int j0) {
+  f.lo = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(r, k_byte<float>(key, j0), 0, kLoadAux));
+  f.hi = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(r, k_byte<float>(key, j0 + 4), 0, kLoadAux));
+}
+__device__ __forceinline__ void pload_k(Frag8<bf16_t>& f, const char* page, int key, int j0) {
+  f.v = *reinterpret_cast<const uint4*>(page + k_byte<bf16_t>(key, j0));
+}
+__device__ __forceinline__ void pload_k(Frag8<float>& f, const char* page, int key, int j0) {
+  f.lo = *reinterpret_cast<const float4*>(page + k_byte<float>(key, j0));
+  f.hi = *reinterpret_cast<const float4*>(page + k_byte<float>(key, j0 + 4));
+}
+
+// K plane chunk-major (k_elem): lane l reads key l%16, dims [32*st + 8*(l/16), +8); for
+// bf16 the 64 lanes of fragment st read the plane's bytes [1024 st, 1024 (st + 1))
+// in lane order, one contiguous run per load instruction.
 // V plane dim-major [D][16]: lane l reads dim 16*n + l%16, keys [4*(l/16), +4).
 template <typename T, int D>
 __device__ __forceinline__ void load_page(PageFrags<T, D>& f, __amdgpu_buffer_rsrc_t r, int lane) {
   constexpr int EB = St<T>::bytes;
   const int key = lane & 15, grp = lane >> 4;
 #pragma unroll
-  for (int st = 0; st < D / 32; ++st) bload(f.k[st], r, (key * D + 32 * st + 8 * grp) * EB);
+  for (int st = 0; st < D / 32; ++st) bload_k(f.k[st], r, key, 32 * st + 8 * grp);
 #pragma unroll
   for (int n = 0; n < D / 16; ++n) bload(f.v[n], r, (kPage * D + (16 * n + key) * kPage + 4 * grp) * EB);
 }
@@ -114,7 +138,7 @@ __device__ __forceinline__ void load_page(PageFrags<T, D>& f, const char* page, 
   constexpr int EB = St<T>::bytes;
   const int key = lane & 15, grp = lane >> 4;
 #pragma unroll
-  for (int st = 0; st < D / 32; ++st) load_frag8(f.k[st], page + (key * D + 32 * st + 8 * grp) * EB);
+  for (int st = 0; st < D / 32; ++st) pload_k(f.k[st], page, key, 32 * st + 8 * grp);
 #pragma unroll
   for (int n = 0; n < D / 16; ++n) load_frag4(f.v[n], page + (kPage * D + (16 * n + key) * kPage + 4 * grp) * EB);
 }

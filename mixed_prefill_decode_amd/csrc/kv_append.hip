@@ -7,9 +7,9 @@
 // to this rank's KV heads only, for all chunk rows (local rows from this rank's
 // projection, peer rows from the All-to-All stand-in buffer).
 //
-// Pool layout: page = [K plane: page_size x d token-major | V plane: d x
-// page_size dim-major]; position p of a table row is slot p % page_size of page
-// table[p / page_size].
+// Pool layout: page = [K plane: 16-byte chunks of dims, chunk-major over the slots
+// (k_elem) | V plane: d x page_size dim-major]; position p of a table row is slot
+// p % page_size of page table[p / page_size].
 //
 // RoPE angles pos * base^(-2i/d) are formed and reduced in fp64 once per row
 // (positions reach 65536, where an fp32 product would already be off by
@@ -29,7 +29,7 @@ __device__ __forceinline__ void put_kv(void* pool, int n_pages, int S, int d, in
     return;
   }
   const long base = long(page) * 2 * S * d;
-  St<T>::store(pool, base + long(slot) * d + j, kval);
+  St<T>::store(pool, base + k_elem<T>(slot, j, S), kval);
   St<T>::store(pool, base + long(S) * d + long(j) * S + slot, vval);
 }
 
@@ -215,7 +215,7 @@ __global__ __launch_bounds__(256) void kv_gather_kernel(const void* pool, int n_
     return;
   }
   const long base = long(page) * 2 * S * d;
-  St<T>::store(k_out, o, St<T>::load(pool, base + long(p % S) * d + j));
+  St<T>::store(k_out, o, St<T>::load(pool, base + k_elem<T>(p % S, j, S)));
   St<T>::store(v_out, o, St<T>::load(pool, base + long(S) * d + long(j) * S + p % S));
 }
 

@@ -15,9 +15,10 @@
 // straight into an LDS ring of two-block stages with buffer_load ... lds.  A
 // workgroup of a small grid may hold two waves per head (two key sets), each set
 // taking every other block of the split, merged in LDS at the end.  gfx950's LDS serves
-// 16-byte reads 16 lanes at a time over 64 banks (256 bytes), and both planes are
-// XOR-swizzled in 16-byte chunks so those 16 lanes -- 16 keys of a K read, 16 dim
-// rows of a V^T read -- land on distinct banks.  Splitting the key range gives
+// 16-byte reads 16 lanes at a time over 64 banks (256 bytes): the K plane's chunk-major
+// page layout already puts one dim chunk of 16 keys in 256 consecutive bytes, and the
+// V^T plane is XOR-swizzled in 16-byte chunks so 16 dim rows of a read land on
+// distinct banks.  Splitting the key range gives
 // long prior contexts enough workgroups; a tile whose keys fit in one split
 // writes its output directly, the others write fp32 (max, sum, output) partials
 // that `prefill_combine_kernel` merges (the log-sum-exp merge of Decode Token
@@ -94,34 +95,26 @@ __device__ __forceinline__ float pack_and_sum(Frag8<float>& f, const float* p) {
   return ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
 }
 
-// LDS plane swizzles (16-byte chunks).  K plane: rows of KROW_CH chunks, one per
-// key; key k's chunk c sits at c ^ kswz(k), where keys that share a 256-byte
-// bank line (two for 128-byte rows) get the same value and the next 16 keys
-// distinct ones.  V^T plane: rows of VROW_CH chunks, one per dim; dim row r's
-// chunk c sits at c ^ vswz(r), which alternates every 256 bytes of rows.
-template <int KROW_CH>
-__device__ __forceinline__ int kswz(int k) {
-  constexpr int ROWS256 = KROW_CH >= 16 ? 1 : 16 / KROW_CH;   // K rows per 256-byte bank line
-  return (k / ROWS256) & (KROW_CH - 1);
-}
+// LDS planes.  K: the page's K plane copied as it is stored, 16-byte chunks of dims
+// chunk-major over the page's 16 slots (chunk c of key k at (c * 16 + k) * 16), so a
+// 16-lane group reading one chunk of 16 keys reads 256 consecutive bytes: all 64
+// banks once.  V^T: rows of VROW_CH chunks, one per dim; dim row r's chunk c sits at
+// c ^ vswz(r), which alternates every 256 bytes of rows.
 template <int VROW_CH>
 __device__ __forceinline__ int vswz(int r) {
   constexpr int ROWS256 = 16 / VROW_CH;                       // V^T rows per 256-byte bank line
   return (r / ROWS256) & (VROW_CH - 1);
 }
-template <int KROW_CH>
-__device__ __forceinline__ const uint4* kchunk(const char* plane, int k, int c, int row_bytes) {
-  return reinterpret_cast<const uint4*>(plane + k * row_bytes + (c ^ kswz<KROW_CH>(k)) * 16);
+__device__ __forceinline__ const uint4* kchunk(const char* plane, int k, int c) {
+  return reinterpret_cast<const uint4*>(plane + (c * kPage + k) * 16);
 }
-template <int KROW_CH>
-__device__ __forceinline__ void kfrag(Frag8<bf16_t>& f, const char* plane, int k, int elem0, int row_bytes) {
-  f.v = *kchunk<KROW_CH>(plane, k, elem0 * 2 / 16, row_bytes);
+// K fragment of key k: dims [elem0, elem0 + 8)
+__device__ __forceinline__ void kfrag(Frag8<bf16_t>& f, const char* plane, int k, int elem0) {
+  f.v = *kchunk(plane, k, elem0 / 8);
 }
-template <int KROW_CH>
-__device__ __forceinline__ void kfrag(Frag8<float>& f, const char* plane, int k, int elem0, int row_bytes) {
-  const int c = elem0 * 4 / 16;
-  f.lo = __builtin_bit_cast(float4, *kchunk<KROW_CH>(plane, k, c, row_bytes));
-  f.hi = __builtin_bit_cast(float4, *kchunk<KROW_CH>(plane, k, c + 1, row_bytes));
+__device__ __forceinline__ void kfrag(Frag8<float>& f, const char* plane, int k, int elem0) {
+  f.lo = __builtin_bit_cast(float4, *kchunk(plane, k, elem0 / 4));
+  f.hi = __builtin_bit_cast(float4, *kchunk(plane, k, elem0 / 4 + 1));
 }
 // V^T fragment: 8 consecutive key slots [8*hf, 8*hf + 8) of dim row r
 template <int VROW_CH>
@@ -191,7 +184,6 @@ __device__ __forceinline__ void prefill_tile(const PrefillArgs& a, int bx, int b
   constexpr int BLK = 4 * PLANE;                  // one 32-key block: K_A | K_B | V_A | V_B
   constexpr int CH_PER_PLANE = PLANE / 16;        // 16-byte chunks per plane
   constexpr int INSTR_BLK = 4 * CH_PER_PLANE / 64;  // 64-lane load instructions per block
-  constexpr int KROW_CH = D * EB / 16;            // 16-byte chunks per K row
   constexpr int VROW_CH = kPage * EB / 16;        // 16-byte chunks per V^T row
   // blocks per stage and ring depth, within the LDS budget
   constexpr int kBudget = 144 * 1024;
@@ -275,8 +267,7 @@ __device__ __forceinline__ void prefill_tile(const PrefillArgs& a, int bx, int b
       const int p = (i % (CH_PER_PLANE / 64)) * 64 + lane;  // chunk position inside the plane
       int src;
       if (region < 2) {
-        const int row = p / KROW_CH, c = (p % KROW_CH) ^ kswz<KROW_CH>(row);
-        src = row * (D * EB) + c * 16;
+        src = p * 16;                 // the K plane as stored
       } else {
         const int row = p / VROW_CH, c = (p % VROW_CH) ^ vswz<VROW_CH>(row);
         src = PLANE + (row * VROW_CH + c) * 16;
@@ -337,7 +328,7 @@ __device__ __forceinline__ void prefill_tile(const PrefillArgs& a, int bx, int b
       const int kr = krow & 15;
       Frag8<T> kf[D / 16];
 #pragma unroll
-      for (int st = 0; st < D / 16; ++st) kfrag<KROW_CH>(kf[st], kplane, kr, 16 * st + 8 * hf, D * EB);
+      for (int st = 0; st < D / 16; ++st) kfrag(kf[st], kplane, kr, 16 * st + 8 * hf);
       // S^T = K . Q^T; K operand row ql holds key kappa(ql) of the block
       f32x16 sacc[NQ];
 #pragma unroll

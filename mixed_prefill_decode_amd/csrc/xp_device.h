@@ -84,6 +84,16 @@ template <> struct St4<float> {
   }
 };
 
+// Element offset of slot s, dim j inside a page's K plane.  The plane is stored
+// 16-byte-chunk-major: chunk c holds dims [c E, (c + 1) E) of one slot (E = 16 bytes
+// of T), and the chunks of one dim range are consecutive over the page's S slots
+// ([d / E][S][E]).  An MFMA operand fragment of 16 keys then reads one contiguous run.
+template <typename T>
+__device__ __forceinline__ long k_elem(int s, int j, int S) {
+  constexpr int E = 16 / St<T>::bytes;
+  return (long(j / E) * S + s) * E + (j % E);
+}
+
 // value after a round trip through the storage type
 template <typename T> __device__ __forceinline__ float round_st(float v);
 template <> __device__ __forceinline__ float round_st<bf16_t>(float v) { return bf2f(f2bf(v)); }

@@ -54,7 +54,8 @@ def _matvec(W, x):
 
 def _read_page_slot(pool, page, slot, S, d, dtype):
     row = pool[[page]][0]
-    k = [read_stored(row[0][slot * d + j], dtype) for j in range(d)]
+    E = 8 if dtype == "bf16" else 4          # elements per 16-byte chunk of the K plane
+    k = [read_stored(row[0][((j // E) * S + slot) * E + j % E], dtype) for j in range(d)]
     v = [read_stored(row[1][j * S + slot], dtype) for j in range(d)]
     return k, v
 

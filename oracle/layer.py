@@ -84,16 +84,24 @@ def causal_pair_count(chunk_len: int, prior_len: int) -> int:
     return int(np.sum(prior_len + t + 1))
 
 
+def _k_chunk(dtype: str) -> int:
+    """Elements of the storage type in one 16-byte chunk of the stored K plane."""
+    return 8 if dtype == "bf16" else 4
+
+
 class PagedKV:
     """Logical K/V view of the paged pool (ConfluxServe §4 KV residency; §7 KV-cache aliasing:
     one physical pool, a decode-local table and a head-sharded prefill table).
 
-    ``pool[ids]`` returns stored rows [n, 2, S*d]: plane 0 is K token-major [S, d], plane 1
-    is V dim-major [d, S].  Writes (the appends of this step) are rounded to the storage
+    ``pool[ids]`` returns stored rows [n, 2, S*d] in the C ABI's page format: plane 0 is K
+    in 16-byte chunks of consecutive dims, chunk-major over the S slots ([d/E, S, E] with E
+    the elements of 16 bytes: 8 bf16 or 4 fp32), plane 1 is V dim-major [d, S].  Writes (the appends of this step) are rounded to the storage
     type and kept in an overlay; the base pool is never modified.
     """
 
     def __init__(self, pool, dtype: str, page_size: int, head_dim: int):
+        if head_dim % _k_chunk(dtype):
+            raise ValueError(f"head_dim {head_dim} is not a whole number of 16-byte K chunks")
         self.pool = pool
         self.dtype = dtype
         self.S = page_size
@@ -103,7 +111,8 @@ class PagedKV:
     def _load(self, ids: np.ndarray):
         S, d = self.S, self.d
         rows = to_f64(self.pool[np.asarray(ids, dtype=np.int64)], self.dtype)
-        K = rows[:, 0].reshape(len(ids), S, d).copy()
+        E = _k_chunk(self.dtype)
+        K = rows[:, 0].reshape(len(ids), d // E, S, E).transpose(0, 2, 1, 3).reshape(len(ids), S, d).copy()
         V = rows[:, 1].reshape(len(ids), d, S).transpose(0, 2, 1).copy()
         for k, p in enumerate(ids):
             ov = self.overlay.get(int(p))
@@ -137,7 +146,9 @@ class PagedKV:
         if int(p) not in self.overlay:
             return np.asarray(self.pool[np.array([p])])[0]
         K, V = self.overlay[int(p)]
-        return np.stack([encode(K.reshape(-1), self.dtype), encode(V.T.reshape(-1), self.dtype)])
+        E = _k_chunk(self.dtype)
+        k_plane = K.reshape(self.S, self.d // E, E).transpose(1, 0, 2).reshape(-1)
+        return np.stack([encode(k_plane, self.dtype), encode(V.T.reshape(-1), self.dtype)])
 
 
 def decode_attention(q: np.ndarray, kv: PagedKV, dec_pages: np.ndarray, dec_ctx: np.ndarray,

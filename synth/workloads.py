@@ -10,9 +10,11 @@ Storage formats (these are the formats the C ABI consumes):
 
 * activations / weights: row-major; weights are ``[out_features, in_features]``
   so a projection is ``y = x @ W.T``.
-* KV pool: ``[n_pages, 2, page_size * head_dim]``.  Plane 0 holds K token-major
-  (element ``s * d + j`` is slot ``s``, dim ``j``); plane 1 holds V dim-major
-  (element ``j * page_size + s``).  One page holds one KV head of one request.
+* KV pool: ``[n_pages, 2, page_size * head_dim]``.  Plane 0 holds K in 16-byte
+  chunks of consecutive dims, chunk-major over the slots (with ``E`` elements per
+  chunk, 8 for bf16 and 4 for float32, element ``((j // E) * page_size + s) * E +
+  j % E`` is slot ``s``, dim ``j``); plane 1 holds V dim-major (element
+  ``j * page_size + s``).  One page holds one KV head of one request.
 * decode page table ``[n_decode, n_kv_heads, dec_max_blocks]`` int32 and prefill
   page table ``[n_kv_heads / sp_degree, pre_max_blocks]`` int32; block ``b``
   covers positions ``[b * page_size, (b + 1) * page_size)``; unused entries -1.
@@ -179,7 +181,8 @@ class PagePool:
         for k, p in enumerate(ids):
             v = int(self.valid_slots[p])
             if v < S:
-                rows[k, 0].reshape(S, d)[v:, :] = nan
+                E = 8 if self.dtype == "bf16" else 4
+                rows[k, 0].reshape(d // E, S, E)[:, v:, :] = nan
                 rows[k, 1].reshape(d, S)[:, v:] = nan
         return rows
 

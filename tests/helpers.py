@@ -72,3 +72,23 @@ def close_shared_ctxs():
     for c in _CTXS.values():
         c.close()
     _CTXS.clear()
+
+
+class DevicePages:
+    """``pool[ids]`` over a device pool tensor: copies just those pages to the host in the
+    storage format (for oracle checks on pools too large to copy whole)."""
+
+    def __init__(self, tensor):
+        self.tensor = tensor
+
+    def __getitem__(self, ids):
+        import torch
+        from synth.device import to_host_bits
+        idx = torch.as_tensor(np.asarray(ids, dtype=np.int64), device=self.tensor.device)
+        return to_host_bits(self.tensor[idx])
+
+
+def k_slots(plane, page_size, head_dim, dtype):
+    """A stored K plane (flat, the ABI's chunk-major page format) as [slot, dim]."""
+    E = 8 if dtype == "bf16" else 4
+    return np.asarray(plane).reshape(head_dim // E, page_size, E).transpose(1, 0, 2).reshape(page_size, head_dim)

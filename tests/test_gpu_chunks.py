@@ -14,7 +14,7 @@ from oracle import layer as L
 from oracle.numerics import to_f64
 from synth import MULTI_CHUNK_WORKLOADS, make_multi_instance
 from synth.device import make_chunked_step, to_host_bits
-from tests.helpers import chunk_oracle_kwargs, rel_fro, shared_ctx
+from tests.helpers import chunk_oracle_kwargs, rel_fro, shared_ctx, k_slots
 
 pytestmark = pytest.mark.gpu
 
@@ -77,8 +77,8 @@ def test_chunked_layer_matches_oracle(name):
             assert pool[p].tobytes() == inst.pool[[p]][0].tobytes(), p
             continue
         want = kv.stored_page(p)
-        gk, gv = pool[p, 0].reshape(S, dd), pool[p, 1].reshape(dd, S).T
-        wk, wv = want[0].reshape(S, dd), want[1].reshape(dd, S).T
+        gk, gv = k_slots(pool[p, 0], S, dd, dt), pool[p, 1].reshape(dd, S).T
+        wk, wv = k_slots(want[0], S, dd, dt), want[1].reshape(dd, S).T
         same = np.all(_bits(gk) == _bits(wk), axis=1) & np.all(_bits(gv) == _bits(wv), axis=1)
         for s in np.nonzero(~same)[0]:
             a = np.concatenate([to_f64(gk[s], dt), to_f64(gv[s], dt)])
@@ -112,15 +112,19 @@ def test_chunked_step_equals_single_chunk_steps():
     assert torch.equal(full[starts[-1]:], got)
 
 
-def test_chunked_split_attention_modes_give_identical_results():
+def test_chunked_split_attention_modes_agree():
     inst = make_multi_instance(MULTI_CHUNK_WORKLOADS["M1"])
     outs = []
     for mode in (0, -1, 64):
         step = make_chunked_step(inst, ctx(mode))
         outs.append(step.run().clone())
         torch.cuda.synchronize()
+    # decode rows bit-identical; chunk rows within merge-order rounding (a partition's
+    # prefill plans its key splits for the CUs it has)
+    n_pre = inst.wl.n_prefill_rows
     for o in outs[1:]:
-        assert torch.equal(o, outs[0])
+        assert torch.equal(o[n_pre:], outs[0][n_pre:])
+        assert rel_fro(o.cpu().numpy(), outs[0].cpu().numpy()) < 1e-3
 
 
 def test_chunked_8b_step_on_sampled_rows():

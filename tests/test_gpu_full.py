@@ -9,9 +9,18 @@ and 32-row tile edges (the rows whose key range ends at a block or key-split bou
 and the diagonal blocks' first and last queries) and seeded interior rows.  Attention
 errors are taken per row over the heads this rank computes (decode rows: all heads;
 local prefill rows: the rank's own heads, not the peer_attn_in copies; peer rows: the
-exported heads).  Bars: attention rel-Frobenius <= 5e-3 pooled over the checked rows
-of each kind, and <= 1e-2 for any single row; layer output rel-Frobenius <= 5e-3 and
-teacher-forced max-abs <= 2e-2 (the small-workload layer tests' bars).
+exported heads).
+
+Attention is checked two ways.  Teacher-forced (identical inputs): the oracle attends
+with the GPU's own rotated queries (the step's workspace) over the GPU's pool after the
+step's appends; every checked row within rel-Frobenius 5e-3.  End to end (against the
+oracle's fp64 queries): the queries are bf16 MFMA operands rotated from a projection of
+the bf16-rounded RMSNorm output, and an exact emulation of just those two roundings
+gives up to 1.0e-2 per row (5.7e-3 pooled) on the 8B chunk's rows and up to 1.96e-2 per
+row (median 6.5e-3) on the 32B chunk's local rows, so the end-to-end bars are 1.5x the
+worst emulated floor: 1.5e-2 pooled and 3e-2 per row, with the figures recorded.  Layer output:
+rel-Frobenius <= 5e-3 and teacher-forced max-abs <= 2e-2 (the small-workload layer
+tests' bars).
 """
 import json
 import os
@@ -24,7 +33,7 @@ from oracle import layer as L
 from oracle.numerics import to_f64
 from synth import get_workload, make_instance
 from synth.device import make_step, to_host_bits, upload
-from tests.helpers import oracle_kwargs, rel_fro, shared_ctx
+from tests.helpers import DevicePages, oracle_kwargs, rel_fro, shared_ctx
 
 pytestmark = pytest.mark.gpu
 
@@ -71,6 +80,60 @@ def _per_row(got, want):
     return np.array([rel_fro(g, w) for g, w in zip(got, want)])
 
 
+def _check_mode(inst, mode, step, out_t, peer_t, ref, tfref, rows3):
+    """Metrics of one launch configuration against the oracle (end to end) and against
+    the teacher-forced reference (the oracle's attention on the GPU's queries and pool)."""
+    wl, dt = inst.wl, inst.wl.dtype
+    pre_rows, dec_rows, peer_rows = rows3
+    rows = pre_rows + dec_rows
+    M, H, Hq, d, F = wl.n_rows, wl.hidden, wl.n_q_heads, wl.head_dim, wl.ffn_dim
+    tdt = torch.bfloat16 if dt == "bf16" else torch.float32
+    out = out_t.cpu().numpy().astype(np.float64)
+    attn = to_f64(to_host_bits(step.ws_view("attn", (M, Hq * d), tdt)), dt)
+    h1 = step.ws_view("h1", (M, H), torch.float32).cpu().numpy().astype(np.float64)
+    act = to_f64(to_host_bits(step.ws_view("act", (M, F), tdt)), dt)
+    own = slice(wl.sp_rank * wl.hq_loc * d, (wl.sp_rank + 1) * wl.hq_loc * d)   # the rank's own heads
+    peer = to_f64(to_host_bits(peer_t), dt)[peer_rows] if peer_rows else None
+    r, e2e, tf = {"mode": mode}, {}, {}
+    if dec_rows:
+        e2e["decode"] = _per_row(attn[dec_rows], ref["attn"][dec_rows])
+        r["attn_decode"] = rel_fro(attn[dec_rows], ref["attn"][dec_rows])
+        ctxs = inst.dec_ctx[np.asarray(dec_rows) - wl.n_prefill_local]
+        r["decode_by_ctx"] = {int(c): round(float(x), 6) for c, x in zip(ctxs, e2e["decode"])}
+        tf["decode"] = _per_row(attn[dec_rows], tfref["decode"])
+    if pre_rows:
+        e2e["prefill"] = _per_row(attn[pre_rows][:, own], ref["attn"][pre_rows][:, own])
+        r["attn_prefill"] = rel_fro(attn[pre_rows][:, own], ref["attn"][pre_rows][:, own])
+        tf["prefill"] = _per_row(attn[pre_rows][:, own], tfref["prefill"])
+        other = np.ones(Hq * d, bool)
+        other[own] = False
+        # the other heads' columns are the peer_attn_in rows, copied bit for bit
+        assert np.array_equal(attn[pre_rows][:, other], ref["attn"][pre_rows][:, other])
+    if peer_rows:
+        e2e["peer"] = _per_row(peer, ref["peer_attn_out"][peer_rows])
+        r["attn_peer"] = rel_fro(peer, ref["peer_attn_out"][peer_rows])
+        tf["peer"] = _per_row(peer, tfref["peer"])
+    r["tf_attn_row_max"] = {k: float(v.max()) for k, v in tf.items()}
+    r["tf_attn_row_median"] = {k: float(np.median(v)) for k, v in tf.items()}
+    r["out"] = rel_fro(out[rows], ref["out"][rows])
+    r["out_maxabs"] = float(np.abs(out[rows] - ref["out"][rows]).max())
+    r["tf_maxabs"] = float(np.abs(out[rows] - (h1[rows] + act[rows] @ to_f64(inst.weights["w_down"], dt).T)).max())
+    r["row_max"] = {k: float(v.max()) for k, v in e2e.items()}
+    r["row_median"] = {k: float(np.median(v)) for k, v in e2e.items()}
+    print(f"[full] {wl.name} mode {mode}: {json.dumps(r)}", flush=True)
+    record(wl.name, r)
+    assert np.isfinite(out).all()
+    for k, v in tf.items():
+        assert v.max() < 5e-3, ("teacher-forced", mode, k, int(np.argmax(v)), float(v.max()))
+    for k in ("attn_decode", "attn_prefill", "attn_peer"):
+        if k in r:
+            assert r[k] < 1.5e-2, (mode, k, r[k])
+    for k, v in e2e.items():
+        assert v.max() < 3e-2, (mode, k, int(np.argmax(v)), float(v.max()))
+    assert r["tf_maxabs"] < 2e-2, r
+    assert r["out"] < 5e-3, r
+
+
 @pytest.mark.parametrize("name", ["C2", "C3", "C4", "C5", "C3-full", "C5-full"])
 def test_full_size_layer_on_sampled_rows(name):
     wl = get_workload(name)
@@ -87,53 +150,35 @@ def test_full_size_layer_on_sampled_rows(name):
         torch.cuda.synchronize()
         assert step.status() == 0
         outs[mode] = (step, step.out.clone(), dev.peer_attn_out.clone())
-    assert torch.equal(outs[0][1], outs[128][1])
-    assert torch.equal(outs[0][2], outs[128][2])
-    step = outs[0][0]
+    # decode rows do not depend on the split-attention mode (batch-invariant dense path,
+    # decode splits fixed by the batch)
+    n_pl = wl.n_prefill_local
+    assert torch.equal(outs[0][1][n_pl:], outs[128][1][n_pl:])
     print(f"[full] {name}: oracle on {len(pre_rows)} prefill, {len(dec_rows)} decode and "
           f"{len(peer_rows or [])} peer rows", flush=True)
     ref = L.layer_forward(**oracle_kwargs(inst, rows=rows, peer_rows=peer_rows))
-    dt = wl.dtype
-    M, H, Hq, d, F = wl.n_rows, wl.hidden, wl.n_q_heads, wl.head_dim, wl.ffn_dim
+    dt, d, Hq = wl.dtype, wl.head_dim, wl.n_q_heads
     tdt = torch.bfloat16 if dt == "bf16" else torch.float32
-    out = outs[0][1].cpu().numpy().astype(np.float64)
-    attn = to_f64(to_host_bits(step.ws_view("attn", (M, Hq * d), tdt)), dt)
-    h1 = step.ws_view("h1", (M, H), torch.float32).cpu().numpy().astype(np.float64)
-    act = to_f64(to_host_bits(step.ws_view("act", (M, F), tdt)), dt)
-    own = slice(wl.sp_rank * wl.hq_loc * d, (wl.sp_rank + 1) * wl.hq_loc * d)   # the rank's own heads
-    r = {}
-    per_row = {}
+    # teacher-forced reference: the oracle's attention on the GPU's own rotated queries (the
+    # same in both modes: the projection is batch invariant) over the pool after the step's
+    # appends (the same appends in both modes)
+    step0 = outs[0][0]
+    kv = L.PagedKV(DevicePages(dev.pool), dt, wl.page_size, d)
+    tfref = {}
     if dec_rows:
-        e = _per_row(attn[dec_rows], ref["attn"][dec_rows])
-        per_row["decode"] = e
-        r["attn_decode"] = rel_fro(attn[dec_rows], ref["attn"][dec_rows])
-        ctxs = inst.dec_ctx[np.asarray(dec_rows) - wl.n_prefill_local]
-        r["decode_by_ctx"] = {int(c): round(float(x), 6) for c, x in zip(ctxs, e)}
-    if pre_rows:
-        e = _per_row(attn[pre_rows][:, own], ref["attn"][pre_rows][:, own])
-        per_row["prefill"] = e
-        r["attn_prefill"] = rel_fro(attn[pre_rows][:, own], ref["attn"][pre_rows][:, own])
-        other = np.ones(Hq * d, bool)
-        other[own] = False
-        # the other heads' columns are the peer_attn_in rows, copied bit for bit
-        assert np.array_equal(attn[pre_rows][:, other], ref["attn"][pre_rows][:, other])
-    if peer_rows:
-        got = to_f64(to_host_bits(outs[0][2]), dt)[peer_rows]
-        e = _per_row(got, ref["peer_attn_out"][peer_rows])
-        per_row["peer"] = e
-        r["attn_peer"] = rel_fro(got, ref["peer_attn_out"][peer_rows])
-    r["out"] = rel_fro(out[rows], ref["out"][rows])
-    r["out_maxabs"] = float(np.abs(out[rows] - ref["out"][rows]).max())
-    r["tf_maxabs"] = float(np.abs(out[rows] - (h1[rows] + act[rows] @ to_f64(inst.weights["w_down"], dt).T)).max())
-    r["row_max"] = {k: float(v.max()) for k, v in per_row.items()}
-    r["row_median"] = {k: float(np.median(v)) for k, v in per_row.items()}
-    print(f"[full] {name}: {json.dumps(r)}", flush=True)
-    record(name, r)
-    assert np.isfinite(out).all()
-    for k in ("attn_decode", "attn_prefill", "attn_peer"):
-        if k in r:
-            assert r[k] < 5e-3, (k, r[k])
-    for k, v in per_row.items():
-        assert v.max() < 1e-2, (k, int(np.argmax(v)), float(v.max()))
-    assert r["tf_maxabs"] < 2e-2, r
-    assert r["out"] < 5e-3, r
+        req = [t - n_pl for t in dec_rows]
+        qd = to_f64(to_host_bits(step0.ws_view("q_dec", (wl.n_decode, Hq, d), tdt)), dt)
+        o = L.decode_attention(qd, kv, inst.dec_pages, inst.dec_ctx, wl.n_kv_heads, requests=req)[req]
+        tfref["decode"] = o.reshape(len(req), Hq * d)
+    if wl.chunk_len:
+        off = wl.local_row_offset
+        qp = to_f64(to_host_bits(step0.ws_view("q_pre", (wl.hq_loc, wl.chunk_len, d), tdt)), dt).transpose(1, 0, 2)
+        pos_loc = [off + t for t in pre_rows]
+        pos_peer = [p if p < off else p + n_pl for p in (peer_rows or [])]
+        o = L.prefill_attention(qp, kv, inst.pre_pages, wl.prior_len, wl.group, rows=pos_loc + pos_peer)
+        if pos_loc:
+            tfref["prefill"] = o[pos_loc].reshape(len(pos_loc), -1)
+        if pos_peer:
+            tfref["peer"] = o[pos_peer].reshape(len(pos_peer), -1)
+    for mode, (step, out_t, peer_t) in outs.items():
+        _check_mode(inst, mode, step, out_t, peer_t, ref, tfref, (pre_rows, dec_rows, peer_rows))

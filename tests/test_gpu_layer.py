@@ -17,7 +17,7 @@ from oracle import layer as L
 from oracle.numerics import to_f64
 from synth import get_workload, make_instance
 from synth.device import make_step, to_host_bits, upload
-from tests.helpers import oracle_kwargs, rel_fro, shared_ctx
+from tests.helpers import oracle_kwargs, rel_fro, shared_ctx, k_slots
 
 pytestmark = pytest.mark.gpu
 
@@ -92,8 +92,8 @@ def test_layer_matches_oracle(name):
         if p not in kv.overlay:
             assert pool[p].tobytes() == inst.pool[[p]][0].tobytes(), p
             continue
-        gk, gv = pool[p, 0].reshape(S, dd), pool[p, 1].reshape(dd, S).T
-        wk, wv = want[0].reshape(S, dd), want[1].reshape(dd, S).T
+        gk, gv = k_slots(pool[p, 0], S, dd, dt), pool[p, 1].reshape(dd, S).T
+        wk, wv = k_slots(want[0], S, dd, dt), want[1].reshape(dd, S).T
         same = np.all(_bits(gk) == _bits(wk), axis=1) & np.all(_bits(gv) == _bits(wv), axis=1)
         for s in np.nonzero(~same)[0]:      # appended slots: values within bf16 rounding of the oracle's
             a = np.concatenate([to_f64(gk[s], dt), to_f64(gv[s], dt)])
@@ -101,16 +101,24 @@ def test_layer_matches_oracle(name):
             assert np.isfinite(a).all() and rel_fro(a, b) < 1e-2, (p, s)
 
 
-def test_split_attention_modes_give_identical_results():
+def test_split_attention_modes_agree():
+    """Serialized, unmasked and CU-partitioned steps: decode rows bit-identical (the
+    dense path is batch invariant and decode's splits do not depend on the mode); the
+    prefill rows and the exported peer rows within merge-order rounding (a partition's
+    prefill plans its key splits for the CUs it has)."""
     inst = make_instance(get_workload("P1"))
+    n_pl = inst.wl.n_prefill_local
     outs = []
     for mode in (0, -1, 64):
         step, dev = make_step(inst, ctx(mode))
         step.run()
         torch.cuda.synchronize()
+        assert step.status() == 0
         outs.append((step.out.clone(), dev.peer_attn_out.clone()))
     for o, p in outs[1:]:
-        assert torch.equal(o, outs[0][0]) and torch.equal(p, outs[0][1])
+        assert torch.equal(o[n_pl:], outs[0][0][n_pl:])
+        assert rel_fro(o.cpu().numpy(), outs[0][0].cpu().numpy()) < 1e-3
+        assert rel_fro(p.float().cpu().numpy(), outs[0][1].float().cpu().numpy()) < 1e-3
 
 
 def test_repeat_calls_are_deterministic_and_idempotent():
@@ -228,7 +236,10 @@ def test_host_table_copies_validate_before_launch():
     # copies of only some of the tables the step reads
     part = X.batch_desc(x=dev.x, n_prefill_local=wl.n_prefill_local, n_decode=wl.n_decode, dec_ctx=dev.dec_ctx,
                         dec_pages=dev.dec_pages, chunk_len=wl.chunk_len, prior_len=wl.prior_len,
-                        pre_pages=dev.pre_pages, dec_ctx_host=inst.dec_ctx, dec_pages_host=inst.dec_pages)
+                        sp_degree=wl.sp_degree, sp_rank=wl.sp_rank, local_row_offset=wl.local_row_offset,
+                        pre_pages=dev.pre_pages, peer_qkv_in=dev.peer_qkv_in, peer_qkv_out=dev.peer_qkv_out,
+                        peer_attn_in=dev.peer_attn_in, peer_attn_out=dev.peer_attn_out,
+                        dec_ctx_host=inst.dec_ctx, dec_pages_host=inst.dec_pages)
     with pytest.raises(X.XpError) as e:
         X.xp_layer_forward(step.ctx, step.shape, part, step.weights, step.kv, step.out, step.workspace,
                            step.layout.total)

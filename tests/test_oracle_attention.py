@@ -6,7 +6,7 @@ import torch
 from oracle import brute
 from oracle import layer as L
 from oracle.numerics import encode
-from tests.helpers import ArrayPool
+from tests.helpers import ArrayPool, k_slots
 
 
 def _rng(s):
@@ -49,7 +49,8 @@ def test_attend_against_torch_sdpa_causal():
 
 def _build_pool(K_seq, V_seq, S, dtype, rnd, extra_pages=3):
     """Write contiguous per-head K/V [n, d] sequences into a shuffled pool with the ABI layout
-    (plane 0 token-major K, plane 1 dim-major V); unused slots NaN."""
+    (plane 0 K in 16-byte chunks chunk-major over the slots: 4 fp32 per chunk here; plane 1
+    dim-major V); unused slots NaN."""
     n_heads = len(K_seq)
     n, d = K_seq[0].shape
     nb = -(-n // S)
@@ -65,7 +66,8 @@ def _build_pool(K_seq, V_seq, S, dtype, rnd, extra_pages=3):
             for s in range(S):
                 pos = b * S + s
                 if pos < n:
-                    pool[p, 0, s * d:(s + 1) * d] = K_seq[h][pos]
+                    for j in range(d):
+                        pool[p, 0, ((j // 4) * S + s) * 4 + j % 4] = K_seq[h][pos][j]
                     pool[p, 1, np.arange(d) * S + s] = V_seq[h][pos]
     return ArrayPool(pool), table
 
@@ -141,10 +143,10 @@ def test_visible_pairs_equal_the_pages_workload_count():
     S = 16
     for c, l in ((0, 1), (0, 19), (13, 7), (32, 16)):
         n = c + l
-        d = n
+        d = -(-n // 4) * 4          # whole 16-byte chunks of fp32 in the stored K plane
         r = _rng(c * 100 + l)
         Ks = [r.standard_normal((n, d)) * 0.1]
-        Vs = [np.eye(n)]
+        Vs = [np.eye(n, d)]         # key j's V row is the indicator of column j
         pool, table = _build_pool(Ks, Vs, S, "f32", r)
         kv = L.PagedKV(pool, "f32", S, d)
         q = r.standard_normal((l, 1, d)) * 0.1
@@ -183,7 +185,7 @@ def test_append_rounds_to_storage_and_roundtrips():
     k = r.standard_normal(d); v = r.standard_normal(d)
     kv.write(table, 17, k, v)
     page = kv.stored_page(0)
-    K = page[0].reshape(S, d); V = page[1].reshape(d, S)
+    K = k_slots(page[0], S, d, "bf16"); V = page[1].reshape(d, S)
     ref_k = torch.from_numpy(k).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
     ref_v = torch.from_numpy(v).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
     assert np.array_equal(K[1], ref_k) and np.array_equal(V[:, 1], ref_v)

@@ -13,7 +13,7 @@ import torch
 from oracle import brute
 from oracle import layer as L
 from synth import Workload, make_instance
-from tests.helpers import ArrayPool, oracle_kwargs
+from tests.helpers import ArrayPool, oracle_kwargs, k_slots
 
 TINY = Workload("tiny", 901, "f32", 16, 4, 2, 4, 24, n_decode=3, ctx=("list", [0, 6, 9]),
                 chunk_len=5, prior_len=7, page_size=4, spare_pages=2)
@@ -39,7 +39,8 @@ def test_appends_land_in_the_right_slots_and_nothing_else_changes():
         for g in range(TINY.n_kv_heads):
             p = int(inst.dec_pages[i, g, c // S]); touched.add(p)
             page = kv.stored_page(p)
-            assert np.array_equal(page[0].reshape(S, d)[c % S], res["k"][TINY.n_prefill_local + i, g].astype(np.float32))
+            assert np.array_equal(k_slots(page[0], S, d, TINY.dtype)[c % S],
+                                  res["k"][TINY.n_prefill_local + i, g].astype(np.float32))
     for t in range(TINY.chunk_len):
         pos = TINY.prior_len + t
         for g in range(TINY.n_kv_heads):
@@ -126,7 +127,7 @@ def test_layer_matches_library_llama_layer_run_per_request():
             table_row[b] = next(it)
         for pos in range(n):
             p, s = table_row[pos // S], pos % S
-            pool[p, 0, s * d:(s + 1) * d] = K[pos]
+            pool[p, 0, ((np.arange(d) // 4) * S + s) * 4 + np.arange(d) % 4] = K[pos]   # chunk-major K, fp32
             pool[p, 1, np.arange(d) * S + s] = V[pos]
 
     for g in range(Hkv):

@@ -1,6 +1,7 @@
 """The seeded input generators: determinism, table validity, NaN poisoning -- CPU only."""
 import numpy as np
 
+from tests.helpers import k_slots
 from synth import (PARITY_WORKLOADS, WORKLOADS, bf16_bits_to_f32, f32_to_bf16_bits, get_workload,
                    make_instance, waterfill_cases)
 
@@ -38,7 +39,7 @@ def test_unwritten_slots_are_nan_and_cached_slots_finite():
         for g in range(inst.wl.n_kv_heads):
             for pos in range(-(-(int(c) + 1) // S) * S):
                 row = inst.pool[[inst.dec_pages[i, g, pos // S]]][0]
-                k = bf16_bits_to_f32(row[0].reshape(S, d)[pos % S])
+                k = bf16_bits_to_f32(k_slots(row[0], S, d, "bf16")[pos % S])
                 v = bf16_bits_to_f32(row[1].reshape(d, S)[:, pos % S])
                 assert np.isfinite(k).all() == (pos < c) and np.isfinite(v).all() == (pos < c)
 
