@@ -395,6 +395,25 @@ xp_status xp_decode_attention(int32_t dtype, const void* q, const void* pool, in
                               int32_t n_kv_heads, int32_t head_dim, void* out, int32_t out_stride,
                               void* workspace, int32_t pages_per_split, void* stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc): xp_decode_attention with its split
+ * partials in a static device buffer the library holds, XP_DECODE_STATIC_SCRATCH_BYTES
+ * (64 MiB) on each GPU it runs on, until the process ends, instead of a caller
+ * workspace.  Same arguments, kernels and results as xp_decode_attention (bit for bit
+ * at the same pages_per_split), minus the workspace.  The call allocates nothing
+ * (no hipMalloc, hipFree or allocating library routine); the buffer's device address
+ * is looked up on the first call on each device.  XP_EWORKSPACE when the batch's
+ * partials (xp_decode_workspace_size) exceed the buffer; other errors as
+ * xp_decode_attention.  Every call on one GPU uses the same buffer: calls that
+ * overlap on one GPU (concurrent streams, or host threads) race and must be
+ * serialized by the caller; nothing in the buffer needs to start at zero. */
+#define XP_DECODE_STATIC_SCRATCH_BYTES (64u << 20)
+xp_status xp_decode_attention_static(int32_t dtype, const void* q, const void* pool, int32_t n_pages,
+                                     int32_t page_size, const int32_t* dec_pages, int32_t dec_max_blocks,
+                                     const int32_t* dec_ctx, int32_t n_decode, int32_t n_q_heads,
+                                     int32_t n_kv_heads, int32_t head_dim, void* out, int32_t out_stride,
+                                     int32_t pages_per_split, void* stream);
+
 /* Bytes of device workspace xp_prefill_attention needs for these sizes and plan_cus
  * (0 when no query tile's keys are split). */
 size_t xp_prefill_workspace_size(int32_t n_q_heads_loc, int32_t n_kv_heads_loc, int32_t head_dim,

@@ -23,7 +23,8 @@ __all__ = ["XpError", "lib", "close_all", "XP_F32", "XP_BF16", "XP_EPI_F32", "XP
            "weights_array", "pools_array",
            "xp_layer_read_status", "xp_rmsnorm", "xp_gemm_workspace_size", "xp_gemm_tile", "xp_gemm", "xp_kv_append",
            "xp_kv_gather",
-           "xp_decode_workspace_size", "xp_decode_attention", "xp_prefill_workspace_size", "xp_prefill_attention",
+           "xp_decode_workspace_size", "xp_decode_attention", "xp_decode_attention_static", "XP_DECODE_STATIC_SCRATCH_BYTES",
+           "xp_prefill_workspace_size", "xp_prefill_attention",
            "xp_probe_hw_ids", "xp_probe_read", "xp_calibrate_decode_cus", "xp_probe_read_curve", "CuCurve",
            "XP_SPLIT_SERIALIZED", "XP_SPLIT_UNMASKED",
            "xp_waterfill", "xp_iteration_latency", "xp_admission", "xp_decode_placement", "xp_schedule",
@@ -47,7 +48,7 @@ EXPORTED = ["xp_last_error", "xp_build_info", "xp_ctx_create", "xp_ctx_destroy",
             "xp_stack_forward", "xp_stack_graph_create", "xp_graph_launch", "xp_graph_destroy",
             "xp_rmsnorm", "xp_gemm_workspace_size", "xp_gemm_tile", "xp_gemm", "xp_kv_append", "xp_kv_gather",
             "xp_decode_workspace_size",
-            "xp_decode_attention", "xp_prefill_workspace_size", "xp_prefill_attention", "xp_probe_hw_ids",
+            "xp_decode_attention", "xp_decode_attention_static", "xp_prefill_workspace_size", "xp_prefill_attention", "xp_probe_hw_ids",
             "xp_probe_read", "xp_calibrate_decode_cus", "xp_probe_read_curve", "xp_waterfill",
             "xp_iteration_latency", "xp_fit_affine", "xp_fit_latency_model", "xp_admission",
             "xp_decode_placement", "xp_schedule"]
@@ -198,6 +199,8 @@ def _declare(L):
         "xp_decode_workspace_size": (_sz, [_i32, _i32, _i32, _i32, _i32, _i32]),
         "xp_decode_attention": (S, [_i32, _vp, _vp, _i32, _i32, _vp, _i32, _vp, _i32, _i32, _i32, _i32, _vp,
                                     _i32, _vp, _i32, _vp]),
+        "xp_decode_attention_static": (S, [_i32, _vp, _vp, _i32, _i32, _vp, _i32, _vp, _i32, _i32, _i32, _i32, _vp,
+                                           _i32, _i32, _vp]),
         "xp_prefill_workspace_size": (_sz, [_i32, _i32, _i32, _i32, _i32, _i32]),
         "xp_prefill_attention": (S, [_i32, _vp, _vp, _i32, _i32, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
                                      _i32, _vp, _i32, _vp, _i32, _vp, _i32, _vp, _vp]),
@@ -502,6 +505,16 @@ def xp_decode_attention(dtype, q, pool, n_pages, page_size, dec_pages, dec_max_b
     _check(lib().xp_decode_attention(dtype, _ptr(q), _ptr(pool), n_pages, page_size, _ptr(dec_pages),
                                      dec_max_blocks, _ptr(dec_ctx), n_decode, n_q_heads, n_kv_heads, head_dim,
                                      _ptr(out), out_stride, _ptr(workspace), pages_per_split, _stream(stream)))
+
+
+def xp_decode_attention_static(dtype, q, pool, n_pages, page_size, dec_pages, dec_max_blocks, dec_ctx, n_decode,
+                               n_q_heads, n_kv_heads, head_dim, out, out_stride, pages_per_split, stream=None):
+    _check(lib().xp_decode_attention_static(dtype, _ptr(q), _ptr(pool), n_pages, page_size, _ptr(dec_pages),
+                                            dec_max_blocks, _ptr(dec_ctx), n_decode, n_q_heads, n_kv_heads,
+                                            head_dim, _ptr(out), out_stride, pages_per_split, _stream(stream)))
+
+
+XP_DECODE_STATIC_SCRATCH_BYTES = 64 << 20
 
 
 def xp_prefill_workspace_size(hq, hkv, head_dim, prior_len, chunk_len, plan_cus=0) -> int:

@@ -18,6 +18,8 @@
 // of one dim row (8 contiguous bytes for bf16).  Scores are kept in the exp2
 // domain (scale * log2(e) folded in).  Each wave keeps a few pages of K/V
 // fragments in flight ahead of the page it consumes.
+#include <mutex>
+
 #include "xp_device.h"
 #include "xp_internal.h"
 
@@ -440,3 +442,68 @@ xp_status launch_decode(int dtype, const void* q, const void* pool, int n_pages,
 }
 
 }  // namespace xp
+
+namespace xp {
+
+// ---- the entry point that allocates nothing ----------------------------------------
+//
+// The split partials of xp_decode_attention_static live in this file-scope device
+// array, one copy per GPU the library runs on, held until the process ends.  Host code
+// never passes the array's name to a kernel (on the host it is a stand-in symbol, not a
+// device address): the device address of each GPU's copy is looked up once per device,
+// with that device current, and kept in g_scratch_ptr.
+static __device__ __align__(256) char scratch[XP_DECODE_STATIC_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+void* g_scratch_ptr[kMaxDevices] = {};
+std::mutex g_scratch_mu;
+
+// The current device's copy of `scratch` (looked up on the device's first call).
+xp_status scratch_of_current_device(char** out) {
+  int dev = -1;
+  XP_HIP_TRY(hipGetDevice(&dev));
+  if (dev < 0 || dev >= kMaxDevices) return fail(XP_EUNSUPPORTED, "xp_decode_attention_static: device %d", dev);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return fail(XP_EHIP, "xp_decode_attention_static: hipGetSymbolAddress(scratch): %s", hipGetErrorString(e));
+    g_scratch_ptr[dev] = p;
+  }
+  *out = static_cast<char*>(g_scratch_ptr[dev]);
+  return XP_OK;
+}
+}  // namespace
+
+}  // namespace xp
+
+extern "C" xp_status xp_decode_attention_static(int32_t dtype, const void* q, const void* pool, int32_t n_pages,
+                                                int32_t S, const int32_t* dec_pages, int32_t max_blocks,
+                                                const int32_t* dec_ctx, int32_t n_d, int32_t Hq, int32_t Hkv,
+                                                int32_t d, void* out, int32_t out_stride, int32_t pps,
+                                                void* stream) {
+  using namespace xp;
+  if (n_d < 0) return fail(XP_ESHAPE, "xp_decode_attention_static: n_decode %d", n_d);
+  if (n_d == 0) return XP_OK;
+  if (!q || !pool || !dec_pages || !dec_ctx || !out) return fail(XP_EINVAL, "xp_decode_attention_static: null pointer");
+  if (out_stride < Hq * d) return fail(XP_ESHAPE, "xp_decode_attention_static: out_stride %d < Hq*d", out_stride);
+  if (pps < 0) return fail(XP_EINVAL, "xp_decode_attention_static: pages_per_split %d", pps);
+  if (Hq <= 0 || Hkv <= 0 || d <= 0 || max_blocks <= 0)
+    return fail(XP_ESHAPE, "xp_decode_attention_static: Hq %d Hkv %d d %d max_blocks %d", Hq, Hkv, d, max_blocks);
+  pps = decode_pick_pps(pps, n_d, Hkv, max_blocks);
+  const int splits = decode_splits(max_blocks, pps);
+  const size_t need = decode_ws_bytes(n_d, Hq, d, splits);
+  if (need > size_t(XP_DECODE_STATIC_SCRATCH_BYTES))
+    return fail(XP_EWORKSPACE, "xp_decode_attention_static: the split partials need %zu bytes, more than the %zu "
+                "of its static scratch (use xp_decode_attention with a workspace)", need,
+                size_t(XP_DECODE_STATIC_SCRATCH_BYTES));
+  char* ws = nullptr;
+  xp_status st = scratch_of_current_device(&ws);
+  if (st) return st;
+  const size_t ml_bytes = align_up(size_t(n_d) * Hq * splits * 2 * sizeof(float), 256);
+  return launch_decode(dtype, q, pool, n_pages, S, dec_pages, max_blocks, dec_ctx, n_d, Hq, Hkv, d, out, out_stride,
+                       reinterpret_cast<float*>(ws), reinterpret_cast<float*>(ws + ml_bytes), pps, nullptr,
+                       static_cast<hipStream_t>(stream));
+}
