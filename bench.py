@@ -45,7 +45,7 @@ def parse():
                         "partitions that includes the pages' 90%% rule; 0 = serialized, -1 = unmasked)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-budget-s", type=float, default=25.0)
-    p.add_argument("--kernel-only", choices=["none", "qkv", "o", "gate_up", "down", "decode_attn", "prefill_attn",
+    p.add_argument("--kernel-only", choices=["none", "qkv", "o", "gate_up", "down", "decode_attn", "prefill_attn", "read",
                                              "copy"], default="none",
                    help="only launch one kernel repeatedly (for counter runs)")
     p.add_argument("--extra-decode", default="C4",
@@ -909,10 +909,17 @@ def kernel_only(args, X, torch, inst, step, dev, timer):
     step.run()
     torch.cuda.synchronize()
     if args.kernel_only == "copy":
+        # a plain elementwise kernel (16-byte loads and stores per lane), not the runtime's
+        # blit, whose counter readings differ from one runtime to the next
         src = torch.empty(1 << 28, dtype=torch.float32, device="cuda").fill_(1.0)   # 1 GiB
         dst = torch.empty_like(src)
-        fn = lambda: dst.copy_(src)
+        fn = lambda: torch.mul(src, 1.0, out=dst)
         log("[bench] copy kernel: 1 GiB read + 1 GiB written per launch")
+    elif args.kernel_only == "read":
+        src = torch.empty(1 << 28, dtype=torch.float32, device="cuda").fill_(1.0)   # 1 GiB
+        sink = torch.empty(1 << 16, dtype=torch.float32, device="cuda")
+        fn = lambda: X.xp_probe_read(src, src.numel() * 4, sink)
+        log("[bench] read probe: 1 GiB read per launch")
     else:
         calls = kernel_calls(X, torch, inst, step, dev)
         if args.kernel_only not in calls:
@@ -922,7 +929,7 @@ def kernel_only(args, X, torch, inst, step, dev, timer):
     torch.cuda.synchronize()
     log(f"[bench] {args.kernel_only}: {t * 1e6:.2f} us per launch over {args.repeats} launches")
     print(json.dumps({"kernel_only": args.kernel_only, "us": round(t * 1e6, 3), "repeats": args.repeats,
-                      "src_sha256_16": sources_hash(args.kernel_only) if args.kernel_only != "copy" else None}))
+                      "src_sha256_16": sources_hash(args.kernel_only) if args.kernel_only not in ("copy", "read") else None}))
 
 
 if __name__ == "__main__":
