@@ -13,7 +13,10 @@
 //
 // RoPE angles pos * base^(-2i/d) are formed and reduced in fp64 once per row
 // (positions reach 65536, where an fp32 product would already be off by
-// several milliradians) and the rotation itself runs in fp32.
+// several milliradians; the frequencies base^(-2i/d) come from the host, also in
+// fp64) and the rotation itself runs in fp32.
+#include <cmath>
+
 #include "xp_device.h"
 #include "xp_internal.h"
 
@@ -33,8 +36,49 @@ __device__ __forceinline__ void put_kv(void* pool, int n_pages, int S, int d, in
   St<T>::store(pool, base + long(S) * d + long(j) * S + slot, vval);
 }
 
+// dims j .. j + 3 (j a multiple of 4) of one slot: the four K values are consecutive
+// inside one 16-byte chunk of the K plane, the V values are S apart
+template <typename T>
+__device__ __forceinline__ void put_kv4(void* pool, int n_pages, int S, int d, int page, int slot, int j, float4 k,
+                                        float4 v, uint32_t* status) {
+  if (page < 0 || page >= n_pages) {
+    if (status) atomicOr(status, XP_DEV_BAD_PAGE);
+    return;
+  }
+  const long base = long(page) * 2 * S * d;
+  St4<T>::store(pool, base + k_elem<T>(slot, j, S), k);
+  const long vb = base + long(S) * d + long(j) * S + slot;
+  St<T>::store(pool, vb, v.x);
+  St<T>::store(pool, vb + S, v.y);
+  St<T>::store(pool, vb + 2 * S, v.z);
+  St<T>::store(pool, vb + 3 * S, v.w);
+}
+
+// copies elements [si, si + 8) of src to [di, di + 8) of dst unchanged (16 or 32 bytes)
+template <typename T>
+__device__ __forceinline__ void copy8(void* dst, long di, const void* src, long si) {
+  const uint4* s4 = reinterpret_cast<const uint4*>(static_cast<const T*>(src) + si);
+  uint4* d4 = reinterpret_cast<uint4*>(static_cast<T*>(dst) + di);
+  d4[0] = s4[0];
+  if constexpr (sizeof(T) == 4) d4[1] = s4[1];
+}
+
+// sin and cos of x (radians, |x| < 2^40) in fp64.  x is first reduced modulo 2 pi by
+// Cody and Waite's two-constant method (2 pi = P1 + P2, P1 the double nearest 2 pi; for
+// these magnitudes k P1 is exact inside the fma and the remainder is good to a few
+// units in the last place), so the library's sincos only ever sees |r| <= pi.
+__device__ __forceinline__ void sincos_2pi(double x, double* sn, double* cn) {
+  constexpr double P1 = 6.283185307179586;        // 0x1.921fb54442d18p+2
+  constexpr double P2 = 2.4492935982947064e-16;   // 2 pi - P1
+  const double k = rint(x * (1.0 / P1));
+  const double r = fma(-k, P2, fma(-k, P1, x));
+  sincos(r, sn, cn);
+}
+
 // One workgroup per row task: tasks [0, M) are this rank's rows; the chunk's peer
-// rows, which are only copied, go kPeerRowsPerTask to a task after them.
+// rows, which are only copied, go kPeerRowsPerTask to a task after them.  Every
+// thread moves 4 consecutive dims of a head (and their rotation partners d/2 away) or
+// 8 consecutive elements of a copy per access.
 constexpr int kPeerRowsPerTask = 8;
 
 template <typename T>
@@ -48,30 +92,62 @@ __global__ __launch_bounds__(256) void post_qkv_kernel(PostQkvArgs a) {
   const int ldq = (a.Hq + 2 * a.Hkv) * d;
 
   if (task >= M) {  // peer chunk rows: copy their (already rotated) q | k | v on this rank's heads
+    // the task's rows flattened: q items of 8 elements, then K/V items of 4 dims; every
+    // thread loads all its items before it stores any
     const int n_peer = a.chunk - a.n_pl;
-    const int p1 = min(n_peer, (task - M + 1) * kPeerRowsPerTask);
-    for (int p = (task - M) * kPeerRowsPerTask; p < p1; ++p) {
-      const int t = p < a.off ? p : p + a.n_pl;
-      const int pos = a.prior + t;
-      const int w = (hq_loc + 2 * hkv_loc) * d;
-      const long src = long(p) * w;
-      for (int e0 = tid; e0 < hq_loc * d; e0 += 256 * 8) {
-        float v[8];
+    const int pr0 = (task - M) * kPeerRowsPerTask, nr = min(n_peer - pr0, kPeerRowsPerTask);
+    const int w = (hq_loc + 2 * hkv_loc) * d;
+    const int qi = hq_loc * d / 8, ki = hkv_loc * d / 4;   // items per row
+    constexpr int kQ = 4, kK = 2;
+    uint4 qv[kQ][sizeof(T) / 2];
+    float4 kv[kK], vv[kK];
 #pragma unroll
-        for (int u = 0; u < 8; ++u) v[u] = e0 + 256 * u < hq_loc * d ? St<T>::load(a.peer_qkv_in, src + e0 + 256 * u) : 0.f;
+    for (int u = 0; u < kQ; ++u) {
+      const int e = tid + 256 * u;
+      if (e < nr * qi) {
+        const uint4* src = reinterpret_cast<const uint4*>(static_cast<const T*>(a.peer_qkv_in) +
+                                                          long(pr0 + e / qi) * w + 8 * (e % qi));
 #pragma unroll
-        for (int u = 0; u < 8; ++u) {
-          const int e = e0 + 256 * u;
-          if (e >= hq_loc * d) break;
-          St<T>::store(a.q_pre, (long(e / d) * a.chunk + t) * d + e % d, v[u]);
-        }
+        for (int c = 0; c < int(sizeof(T) / 2); ++c) qv[u][c] = src[c];
       }
-      for (int e = tid; e < hkv_loc * d; e += 256) {
-        const int g = e / d, j = e % d;
-        const int page = a.pre_pages[long(g) * a.pre_max_blocks + pos / S];
-        put_kv<T>(a.pool, a.n_pages, S, d, page, pos % S, j,
-                  St<T>::load(a.peer_qkv_in, src + hq_loc * d + e),
-                  St<T>::load(a.peer_qkv_in, src + (hq_loc + hkv_loc) * d + e), a.status);
+    }
+#pragma unroll
+    for (int u = 0; u < kK; ++u) {
+      const int e = tid + 256 * u;
+      if (e < nr * ki) {
+        const long src = long(pr0 + e / ki) * w + 4 * (e % ki);
+        kv[u] = St4<T>::load(a.peer_qkv_in, src + hq_loc * d);
+        vv[u] = St4<T>::load(a.peer_qkv_in, src + (hq_loc + hkv_loc) * d);
+      }
+    }
+    // items past the unrolled batches (shapes larger than the 32B layer's), one at a time
+    for (int e = tid + 256 * kQ; e < nr * qi; e += 256) {
+      const int p = pr0 + e / qi, t = p < a.off ? p : p + a.n_pl, f = 8 * (e % qi);
+      copy8<T>(a.q_pre, (long(f / d) * a.chunk + t) * d + f % d, a.peer_qkv_in, long(p) * w + f);
+    }
+    for (int e = tid + 256 * kK; e < nr * ki; e += 256) {
+      const int p = pr0 + e / ki, t = p < a.off ? p : p + a.n_pl, pos = a.prior + t, f = 4 * (e % ki);
+      const int g = f / d, page = a.pre_pages[long(g) * a.pre_max_blocks + pos / S];
+      put_kv4<T>(a.pool, a.n_pages, S, d, page, pos % S, f % d, St4<T>::load(a.peer_qkv_in, long(p) * w + hq_loc * d + f),
+                 St4<T>::load(a.peer_qkv_in, long(p) * w + (hq_loc + hkv_loc) * d + f), a.status);
+    }
+#pragma unroll
+    for (int u = 0; u < kQ; ++u) {
+      const int e = tid + 256 * u;
+      if (e < nr * qi) {
+        const int p = pr0 + e / qi, t = p < a.off ? p : p + a.n_pl, f = 8 * (e % qi);
+        uint4* dst = reinterpret_cast<uint4*>(static_cast<T*>(a.q_pre) + (long(f / d) * a.chunk + t) * d + f % d);
+#pragma unroll
+        for (int c = 0; c < int(sizeof(T) / 2); ++c) dst[c] = qv[u][c];
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kK; ++u) {
+      const int e = tid + 256 * u;
+      if (e < nr * ki) {
+        const int p = pr0 + e / ki, t = p < a.off ? p : p + a.n_pl, pos = a.prior + t, f = 4 * (e % ki);
+        const int g = f / d, page = a.pre_pages[long(g) * a.pre_max_blocks + pos / S];
+        put_kv4<T>(a.pool, a.n_pages, S, d, page, pos % S, f % d, kv[u], vv[u], a.status);
       }
     }
     return;
@@ -82,10 +158,38 @@ __global__ __launch_bounds__(256) void post_qkv_kernel(PostQkvArgs a) {
   const int t = a.off + task;           // chunk row of a local prefill row
   const int pos = is_dec ? a.dec_ctx[i] : a.prior + t;
   int* pg = reinterpret_cast<int*>(cs + d);  // [Hkv] page of this row's slot per kv head, -2: not appended here
+  const float* row = a.qkv + long(task) * ldq;
+  const int oq_w = (a.Hq - hq_loc) * d, ok_w = (a.Hkv - hkv_loc) * d;
+  const long pq_out = long(task) * (oq_w + 2 * ok_w);
+
+  // rotated q and k: item (head h, dims j .. j + 3 < d/2) with partners j + d/2.  Each
+  // thread loads a batch of items before storing any of them (the compiler cannot prove
+  // the stores leave the row alone, so loads interleaved with stores would each wait a
+  // full memory round trip); the first batch goes out before the angles are formed.
+  constexpr int kBatch = 5;
+  const int quads = half / 4;
+  const int n_items = (a.Hq + a.Hkv) * quads;
+  float4 x0[kBatch], x1[kBatch], v0[kBatch], v1[kBatch];
+  auto load_batch = [&](int e0) {
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      const int e = e0 + 256 * u;
+      x0[u] = x1[u] = v0[u] = v1[u] = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (e < n_items) {
+        const int h = e / quads, j = 4 * (e % quads);
+        x0[u] = *reinterpret_cast<const float4*>(row + h * d + j);
+        x1[u] = *reinterpret_cast<const float4*>(row + h * d + j + half);
+        if (h >= a.Hq) {  // the value row of kv head h - Hq
+          v0[u] = *reinterpret_cast<const float4*>(row + (a.Hkv + h) * d + j);
+          v1[u] = *reinterpret_cast<const float4*>(row + (a.Hkv + h) * d + j + half);
+        }
+      }
+    }
+  };
+  load_batch(tid);
   if (tid < half) {
-    const double theta = pow(a.rope_base, -2.0 * double(tid) / double(d));
     double sn, cn;
-    sincos(double(pos) * theta, &sn, &cn);
+    sincos_2pi(double(pos) * a.inv_freq[tid], &sn, &cn);
     cs[tid] = float(cn);
     cs[half + tid] = float(sn);
   }
@@ -100,88 +204,58 @@ __global__ __launch_bounds__(256) void post_qkv_kernel(PostQkvArgs a) {
     pg[g] = page;
   }
   __syncthreads();
-  const float* row = a.qkv + long(task) * ldq;
-  const int oq_w = (a.Hq - hq_loc) * d, ok_w = (a.Hkv - hkv_loc) * d;
-  const long pq_out = long(task) * (oq_w + 2 * ok_w);
-
-  // rotated q and k: pairs (j, j + d/2).  Each thread loads a batch of pairs before
-  // storing any of them: the compiler cannot prove the stores leave the row alone, so
-  // loads interleaved with stores would each wait a full memory round trip.
-  constexpr int kBatch = 8;
-  const int n_pairs = (a.Hq + a.Hkv) * half;
-  for (int e0 = tid; e0 < n_pairs; e0 += 256 * kBatch) {
-    float x0[kBatch], x1[kBatch], v0[kBatch], v1[kBatch];
+  for (int e0 = tid; e0 < n_items; e0 += 256 * kBatch) {
+    if (e0 != tid) load_batch(e0);
 #pragma unroll
     for (int u = 0; u < kBatch; ++u) {
       const int e = e0 + 256 * u;
-      x0[u] = x1[u] = v0[u] = v1[u] = 0.f;
-      if (e < n_pairs) {
-        const int h = e / half, j = e % half;
-        x0[u] = row[h * d + j];
-        x1[u] = row[h * d + j + half];
-        if (h >= a.Hq) {  // the value row of kv head h - Hq
-          v0[u] = row[(a.Hkv + h) * d + j];
-          v1[u] = row[(a.Hkv + h) * d + j + half];
-        }
-      }
-    }
-#pragma unroll
-    for (int u = 0; u < kBatch; ++u) {
-      const int e = e0 + 256 * u;
-      if (e >= n_pairs) break;
-      const int h = e / half, j = e % half;
-      const float c = cs[j], s = cs[half + j];
-      const float y0 = x0[u] * c - x1[u] * s, y1 = x1[u] * c + x0[u] * s;
+      if (e >= n_items) break;
+      const int h = e / quads, j = 4 * (e % quads);
+      const float4 c = *reinterpret_cast<const float4*>(cs + j), sn = *reinterpret_cast<const float4*>(cs + half + j);
+      float4 y0, y1;
+      y0.x = x0[u].x * c.x - x1[u].x * sn.x, y1.x = x1[u].x * c.x + x0[u].x * sn.x;
+      y0.y = x0[u].y * c.y - x1[u].y * sn.y, y1.y = x1[u].y * c.y + x0[u].y * sn.y;
+      y0.z = x0[u].z * c.z - x1[u].z * sn.z, y1.z = x1[u].z * c.z + x0[u].z * sn.z;
+      y0.w = x0[u].w * c.w - x1[u].w * sn.w, y1.w = x1[u].w * c.w + x0[u].w * sn.w;
       if (h < a.Hq) {
+        long o;
+        void* dst;
         if (is_dec) {
-          const long o = (long(i) * a.Hq + h) * d;
-          St<T>::store(a.q_dec, o + j, y0);
-          St<T>::store(a.q_dec, o + j + half, y1);
+          dst = a.q_dec;
+          o = (long(i) * a.Hq + h) * d;
         } else if (h >= q0 && h < q0 + hq_loc) {
-          const long o = (long(h - q0) * a.chunk + t) * d;
-          St<T>::store(a.q_pre, o + j, y0);
-          St<T>::store(a.q_pre, o + j + half, y1);
+          dst = a.q_pre;
+          o = (long(h - q0) * a.chunk + t) * d;
         } else {
-          const long o = pq_out + long(h < q0 ? h : h - hq_loc) * d;
-          St<T>::store(a.peer_qkv_out, o + j, y0);
-          St<T>::store(a.peer_qkv_out, o + j + half, y1);
+          dst = a.peer_qkv_out;
+          o = pq_out + long(h < q0 ? h : h - hq_loc) * d;
         }
+        St4<T>::store(dst, o + j, y0);
+        St4<T>::store(dst, o + j + half, y1);
       } else {
         const int g = h - a.Hq;
         const int page = pg[g];
         if (page != -2) {
-          put_kv<T>(a.pool, a.n_pages, S, d, page, pos % S, j, y0, v0[u], a.status);
-          put_kv<T>(a.pool, a.n_pages, S, d, page, pos % S, j + half, y1, v1[u], a.status);
+          put_kv4<T>(a.pool, a.n_pages, S, d, page, pos % S, j, y0, v0[u], a.status);
+          put_kv4<T>(a.pool, a.n_pages, S, d, page, pos % S, j + half, y1, v1[u], a.status);
         } else {
           const int gi = g < k0 ? g : g - hkv_loc;
           const long ok = pq_out + oq_w + long(gi) * d;
           const long ov = pq_out + oq_w + ok_w + long(gi) * d;
-          St<T>::store(a.peer_qkv_out, ok + j, y0);
-          St<T>::store(a.peer_qkv_out, ok + j + half, y1);
-          St<T>::store(a.peer_qkv_out, ov + j, v0[u]);
-          St<T>::store(a.peer_qkv_out, ov + j + half, v1[u]);
+          St4<T>::store(a.peer_qkv_out, ok + j, y0);
+          St4<T>::store(a.peer_qkv_out, ok + j + half, y1);
+          St4<T>::store(a.peer_qkv_out, ov + j, v0[u]);
+          St4<T>::store(a.peer_qkv_out, ov + j + half, v1[u]);
         }
       }
     }
   }
   // local prefill rows: attention outputs of the heads other ranks own arrive as peer_attn_in
-  // (batched like the pairs above, so the loads do not wait on the stores)
   if (!is_dec && oq_w > 0) {
-    for (int e0 = tid; e0 < oq_w; e0 += 256 * kBatch) {
-      float v[kBatch];
-#pragma unroll
-      for (int u = 0; u < kBatch; ++u) {
-        const int e = e0 + 256 * u;
-        v[u] = e < oq_w ? St<T>::load(a.peer_attn_in, long(task) * oq_w + e) : 0.f;
-      }
-#pragma unroll
-      for (int u = 0; u < kBatch; ++u) {
-        const int e = e0 + 256 * u;
-        if (e >= oq_w) break;
-        const int hi = e / d, j = e % d;
-        const int h = hi < q0 ? hi : hi + hq_loc;
-        St<T>::store(a.attn, long(task) * a.Hq * d + long(h) * d + j, v[u]);
-      }
+    for (int e = 8 * tid; e < oq_w; e += 256 * 8) {
+      const int hi = e / d, j = e % d;
+      const int h = hi < q0 ? hi : hi + hq_loc;
+      copy8<T>(a.attn, long(task) * a.Hq * d + long(h) * d + j, a.peer_attn_in, long(task) * oq_w + e);
     }
   }
 }
@@ -221,9 +295,13 @@ __global__ __launch_bounds__(256) void kv_gather_kernel(const void* pool, int n_
 
 }  // namespace
 
-xp_status launch_post_qkv(int dtype, const PostQkvArgs& a, hipStream_t s) {
-  const int tasks = a.n_pl + a.n_d + cdiv(a.chunk - a.n_pl, kPeerRowsPerTask);
+xp_status launch_post_qkv(int dtype, const PostQkvArgs& args, hipStream_t s) {
+  const int tasks = args.n_pl + args.n_d + cdiv(args.chunk - args.n_pl, kPeerRowsPerTask);
   if (tasks == 0) return XP_OK;
+  if (args.d % 8 || args.d / 2 > 64) return fail(XP_EUNSUPPORTED, "RoPE: head_dim %d", args.d);
+  // the rotation frequencies base^(-2i/d), formed once in fp64 on the host
+  PostQkvArgs a = args;
+  for (int i = 0; i < a.d / 2; ++i) a.inv_freq[i] = std::pow(a.rope_base, -2.0 * double(i) / double(a.d));
   const size_t shm = size_t(a.d) * sizeof(float) + size_t(a.Hkv) * sizeof(int);
   if (dtype == XP_BF16)
     hipLaunchKernelGGL(post_qkv_kernel<bf16_t>, dim3(tasks), dim3(256), shm, s, a);

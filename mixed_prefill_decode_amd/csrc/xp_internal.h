@@ -59,6 +59,7 @@ struct PostQkvArgs {
   void* q_pre;
   void* attn;
   uint32_t* status;
+  double inv_freq[64];   // base^(-2i/d), i < d/2: filled by launch_post_qkv
 };
 xp_status launch_post_qkv(int dtype, const PostQkvArgs& a, hipStream_t s);
 
