@@ -8,6 +8,9 @@ region eager between them).  Checked: the last layer's output and every layer's 
 against the oracle; graph launches bit-identical to the eager stack, launch after
 launch with other work in between, in serialized and CU-partitioned contexts.
 """
+import json
+import os
+
 import numpy as np
 import pytest
 import torch
@@ -68,8 +71,13 @@ def test_stack_matches_oracle(name, n_layers):
     assert np.isfinite(out).all()
     err = rel_fro(out, ref["out"])
     print(f"[stack] {name}: rel err {err:.2e}", flush=True)
-    # each layer within the single-layer bound (5e-3), compounded over the stack
-    assert err < 5e-3 * n_layers, err
+    path = os.environ.get("XP_METRICS_OUT")
+    if path:
+        with open(path, "a") as f:
+            f.write(json.dumps({"case": f"stack {name} x{n_layers}", "out": err}) + "\n")
+    # the single-layer bar of the dtype, not one that grows with depth: the residual
+    # stream between layers is fp32 on both sides, so a layer adds its own rounding only
+    assert err < (5e-3 if sinst.wl.dtype == "bf16" else 1e-5), err
     for l in range(n_layers):
         _check_pool(sinst, l, step.pool_tensors[l], ref["layers"][l]["kv"])
 
