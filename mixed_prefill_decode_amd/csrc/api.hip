@@ -519,30 +519,50 @@ xp_status LayerRun::pre(hipStream_t s) const {
   char* attn = ws + L.attn;
   const size_t attn_row = size_t(Hq) * D * dtype_bytes(dt);
 
-  // shared linear region (1): RMSNorm + QKV over all M rows
-  if ((st = launch_rmsnorm(dt, x, x_f32 ? 1 : 0, weights.g_attn, ws + L.hn, M, H, sh->rms_eps,
-                           clear_status ? status : nullptr, s)))
-    return st;
-  if (M > 0 && (st = launch_gemm(dt, XP_EPI_F32, ws + L.hn, weights.w_qkv, nullptr, nullptr, qkv, M, ldq, H,
-                                 ws + L.gemm_part, L.h1 - L.gemm_part, s)))
-    return st;
-  // RoPE + appends (+ the peer stand-ins): one launch per chunk, the decodes with the last
-  // (their rows follow it in x) or alone when there is no chunk
-  auto post_qkv = [&](const ChunkRun* c, int nd) {
+  // RoPE + appends (+ the peer stand-ins) of one chunk's rows, the decodes with the last
+  // chunk (their rows follow it in x) or alone when there is no chunk
+  auto args_of = [&](const ChunkRun* c, int nd, bool rope_done) {
     const int row0 = c ? c->row0 : rows_pre;
     PostQkvArgs pa{qkv + size_t(row0) * ldq, c ? c->n_local : 0, nd, Hq, Hkv, D, sh->page_size, sh->rope_base,
                    d->dec_ctx, d->dec_pages, d->dec_max_blocks, c ? c->prior : 0, c ? c->len : 0, P, r,
                    c ? c->off : 0, c ? c->pages : nullptr, c ? c->max_blocks : 0, c ? c->peer_qkv_in : nullptr,
                    c ? c->peer_qkv_out : nullptr, c ? c->peer_attn_in : nullptr, pool.pool, pool.n_pages,
                    ws + L.q_dec, c ? ws + L.q_pre + c->q_off : nullptr, attn + size_t(row0) * attn_row, status};
-    return launch_post_qkv(dt, pa, s);
+    pa.rope_done = rope_done ? 1 : 0;
+    return pa;
   };
-  if (ch.empty()) {
-    if ((st = post_qkv(nullptr, n_d))) return st;
-  } else {
-    for (size_t j = 0; j < ch.size(); ++j)
-      if ((st = post_qkv(&ch[j], j + 1 == ch.size() ? n_d : 0))) return st;
+
+  // shared linear region (1): RMSNorm + QKV over all M rows.  With at most one chunk the
+  // QKV projection rotates and appends in its epilogue (the RMSNorm forms each row's
+  // RoPE table in the qkv region, which then holds no projection); several chunks rotate
+  // per chunk afterwards.
+  const ChunkRun* c0 = ch.empty() ? nullptr : &ch[0];
+  const bool fused = ch.size() <= 1 && gemm_rope_supported(dt, D);
+  RopeTab rt{};
+  if (fused) {
+    rt.tab = reinterpret_cast<float2*>(qkv);
+    rt.half = D / 2;
+    rt.n_pl = c0 ? c0->n_local : 0;
+    rt.pos0 = c0 ? c0->prior + c0->off : 0;
+    rt.dec_ctx = d->dec_ctx;
+    rope_frequencies(sh->rope_base, D, rt.inv_freq);
   }
+  if ((st = launch_rmsnorm(dt, x, x_f32 ? 1 : 0, weights.g_attn, ws + L.hn, M, H, sh->rms_eps,
+                           clear_status ? status : nullptr, s, fused ? &rt : nullptr)))
+    return st;
+  if (fused) {
+    PostQkvArgs pa = args_of(c0, n_d, false);
+    pa.rope_tab = rt.tab;
+    if (M > 0 && (st = launch_gemm_rope(dt, ws + L.hn, weights.w_qkv, M, ldq, H, pa, s))) return st;
+    // what is left: the chunk's peer rows and the peer_attn_in copies (sequence parallel)
+    return launch_post_qkv(dt, args_of(c0, n_d, true), s);
+  }
+  if (M > 0 && (st = launch_gemm(dt, XP_EPI_F32, ws + L.hn, weights.w_qkv, nullptr, nullptr, qkv, M, ldq, H,
+                                 ws + L.gemm_part, L.h1 - L.gemm_part, s)))
+    return st;
+  if (ch.empty()) return launch_post_qkv(dt, args_of(nullptr, n_d, false), s);
+  for (size_t j = 0; j < ch.size(); ++j)
+    if ((st = launch_post_qkv(dt, args_of(&ch[j], j + 1 == ch.size() ? n_d : 0, false), s))) return st;
   return XP_OK;
 }
 

@@ -19,14 +19,16 @@ using gemm::gemm_kernel;
 
 template <typename T, int BM, int BN, int WGM, int WGN, int EPI, int ST, bool FOLD = false>
 xp_status launch_cfg(const void* A, const void* B, const void* B2, const void* R, void* C, int M, int N, int K,
-                     int splits, int chunks, float* part, hipStream_t s) {
+                     int splits, int chunks, float* part, hipStream_t s,
+                     const typename gemm::EpiArg<EPI>::type& ea = {}) {
   const int tm = cdiv(M, BM), tn = cdiv(N, BN);
   const int stages = K / gemm::Cfg<T, BM, BN, WGM, WGN, EPI>::BK;
   const int per = cdiv(stages, chunks);     // stages per K chunk
   hipLaunchKernelGGL((gemm_kernel<T, BM, BN, WGM, WGN, EPI, ST, 128, FOLD>), dim3(tm * tn * splits),
                      dim3(64 * WGM * WGN), 0, s, static_cast<const char*>(A), static_cast<const char*>(B),
-                     static_cast<const char*>(B2), R, C, M, N, K, tm, tn, splits, per, part);
+                     static_cast<const char*>(B2), R, C, M, N, K, tm, tn, splits, per, part, ea);
   XP_CHECK_LAUNCH();
+  if constexpr (EPI == gemm::kEpiRope) return XP_OK;   // one unit per tile, no partials
   if (splits > 1) {
     const long mn = long(M) * N;
     const int blocks = int(std::min<long>((mn + 255) / 256, 4096));
@@ -61,6 +63,14 @@ constexpr Candidate kSingle[] = {
 // Unsplit units that fold K chunks hold a second set of accumulators: the tiles
 // that keep it in registers.
 constexpr Candidate kSingleFold[] = {
+    {0, 64, 128, 1, 4.59},
+    {1, 96, 128, 1, 5.50},
+    {2, 128, 256, 1, 6.65},
+    {3, 192, 128, 1, 7.03},
+};
+// The fused RoPE epilogue stages a tile of whole heads in the ring: tiles whose width
+// is a multiple of 128 (so of d = 64 and 128) and whose [BM][BN + 4] fp32 image fits.
+constexpr Candidate kSingleRope[] = {
     {0, 64, 128, 1, 4.59},
     {1, 96, 128, 1, 5.50},
     {2, 128, 256, 1, 6.65},
@@ -137,7 +147,38 @@ xp_status launch_type(int epi, const void* A, const void* B, const void* B2, con
   return fail(XP_EINVAL, "xp_gemm: unknown epilogue %d", epi);
 }
 
+template <typename T>
+xp_status launch_rope_type(const void* A, const void* B, int M, int N, int K, const PostQkvArgs& ra, hipStream_t s) {
+  constexpr int E = gemm::kEpiRope;
+#define XP_ROPE_ARGS A, B, nullptr, nullptr, nullptr, M, N, K, 1, 1, nullptr, s, ra
+  switch (pick(kSingleRope, M, N, K, device_cus(), 1, 1)) {
+    case 1: return launch_cfg<T, 96, 128, 1, 4, E, 4>(XP_ROPE_ARGS);
+    case 2: return launch_cfg<T, 128, 256, 2, 4, E, 3>(XP_ROPE_ARGS);
+    case 3: return launch_cfg<T, 192, 128, 2, 4, E, 4>(XP_ROPE_ARGS);
+    default: return launch_cfg<T, 64, 128, 1, 4, E, 4>(XP_ROPE_ARGS);
+  }
+#undef XP_ROPE_ARGS
+}
+
 }  // namespace
+
+bool gemm_rope_supported(int dtype, int d) {
+  return (dtype == XP_BF16 || dtype == XP_F32) && (d == 64 || d == 128);
+}
+
+xp_status launch_gemm_rope(int dtype, const void* A, const void* B, int M, int N, int K, const PostQkvArgs& ra,
+                           hipStream_t s) {
+  if (!gemm_rope_supported(dtype, ra.d)) return fail(XP_EUNSUPPORTED, "fused RoPE epilogue: head_dim %d", ra.d);
+  if (M < 0 || N != (ra.Hq + 2 * ra.Hkv) * ra.d || K <= 0) return fail(XP_ESHAPE, "fused RoPE epilogue: M=%d N=%d", M, N);
+  const int bk = 128 / dtype_bytes(dtype);
+  if (K % bk || 256L * K * dtype_bytes(dtype) >= (1L << 31)) return fail(XP_EUNSUPPORTED, "fused RoPE epilogue: K=%d", K);
+  if (!A || !B || !ra.rope_tab) return fail(XP_EINVAL, "fused RoPE epilogue: null operand");
+  if (M == 0) return XP_OK;
+  // the rotation frequencies are not needed here (the table holds cos and sin)
+  xp_status st = dtype == XP_BF16 ? launch_rope_type<bf16_t>(A, B, M, N, K, ra, s)
+                                  : launch_rope_type<float>(A, B, M, N, K, ra, s);
+  return st;
+}
 
 int device_cus() {
   static int cached[64] = {};

@@ -25,6 +25,7 @@
 // tile shape, so a row's result does not depend on which other rows are co-batched
 // with it.
 #pragma once
+#include "rope.h"
 #include "xp_device.h"
 #include "../../include/xp.h"
 
@@ -55,6 +56,13 @@ __device__ __forceinline__ void lds_frag(Frag8<T>& f, const uint4* buf, int row,
     f.hi = __builtin_bit_cast(float4, b);
   }
 }
+
+// Internal epilogue of the QKV projection: RoPE and the step's appends (rope.h) instead
+// of an fp32 store; its kernel argument is the step's PostQkvArgs.
+constexpr int kEpiRope = 16;
+struct NoEpiArg {};
+template <int EPI> struct EpiArg { using type = NoEpiArg; };
+template <> struct EpiArg<kEpiRope> { using type = PostQkvArgs; };
 
 template <typename T, int BM, int BN, int WGM, int WGN, int EPI, int RB = 128>
 struct Cfg {
@@ -146,7 +154,8 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(const char* __rest
                                                                  const char* __restrict__ B2, const void* __restrict__ R,
                                                                  void* __restrict__ C, int M, int N, int K, int tiles_m,
                                                                  int tiles_n, int splits, int kt_per_split,
-                                                                 float* __restrict__ part) {
+                                                                 float* __restrict__ part,
+                                                                 typename EpiArg<EPI>::type ea) {
   using G = Cfg<T, BM, BN, WGM, WGN, EPI, RB>;
   using Rw = Rows<RB>;
   constexpr int NB = G::NB, FM = G::FM, FN = G::FN, CPK = G::CPK;
@@ -176,6 +185,41 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(const char* __rest
   const auto rb = rsrc_rows(B + n0 * kbytes, min(BN, N - n0), kbytes);
   const auto rb2 = rsrc_rows((NB == 2 ? B2 : B) + n0 * kbytes, min(BN, N - n0), kbytes);
   const int lrow = lane / CH;
+
+  // The RoPE epilogue's lookups (each row's position and page ids, each item's cos/sin
+  // pairs) depend only on the tile, so they are issued here and land during the K loop.
+  [[maybe_unused]] constexpr int RHPT = BN / 64;                      // heads per tile, at most
+  [[maybe_unused]] constexpr int RIPT = (BM * BN / 8 + G::THREADS - 1) / G::THREADS;   // items per thread
+  [[maybe_unused]] int rope_pos_r = 0, rope_page_r[RHPT > 0 ? RHPT : 1] = {};
+  [[maybe_unused]] constexpr bool RPRE = RIPT <= 6;                   // cos/sin prefetched (register budget)
+  [[maybe_unused]] float4 rope_c[RPRE ? RIPT : 1][2];
+  if constexpr (EPI == kEpiRope) {
+    const PostQkvArgs& ra = ea;
+    const int d = ra.d, half = d / 2, pq = d / 8, hpt = BN / d, head0 = n0 / d, n_heads = ra.Hq + 2 * ra.Hkv;
+    static_assert(BM <= G::THREADS, "one thread per tile row");
+    const int rr = threadIdx.x;
+    if (rr < BM && m0 + rr < M) {
+      const int row = m0 + rr;
+      rope_pos_r = rope_pos(ra, row);
+#pragma unroll
+      for (int hl = 0; hl < RHPT; ++hl) {
+        const int h = head0 + hl;
+        const int g = h >= ra.Hq + ra.Hkv ? h - ra.Hq - ra.Hkv : h - ra.Hq;
+        if (hl < hpt && h >= ra.Hq && h < n_heads) rope_page_r[hl] = rope_page(ra, row, g, rope_pos_r);
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < (RPRE ? RIPT : 0); ++k) {
+      const int e = threadIdx.x + k * G::THREADS;
+      const int er = e / (hpt * pq), hl = (e / pq) % hpt, j = 4 * (e % pq);
+      const int row = m0 + er, h = head0 + hl;
+      rope_c[k][0] = rope_c[k][1] = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (e < BM * hpt * pq && row < M && h < ra.Hq + ra.Hkv) {
+        rope_c[k][0] = *reinterpret_cast<const float4*>(ra.rope_tab + long(row) * half + j);
+        rope_c[k][1] = *reinterpret_cast<const float4*>(ra.rope_tab + long(row) * half + j + 2);
+      }
+    }
+  }
 
   // Load instruction i of a wave fills LDS rows (i * W + wave) * LR .. + LR - 1 of a
   // stage.  W * LR divides BM and BN, so whether instruction i reads A, B or B2 depends
@@ -345,6 +389,71 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(const char* __rest
   // opposite halves of the 64 banks, and each 16-lane group of a read takes rows r and
   // r + 4 as well.  The arithmetic per element is unchanged.
   barrier();
+  if constexpr (EPI == kEpiRope) {
+    // RoPE + appends of the QKV projection.  The tile goes through the drained ring as
+    // [BM][BN + 8] fp32 (rows 8 floats apart put the two half-waves of an MFMA-layout
+    // store on disjoint banks), so a rotation pair (dims j and j + d/2 of one head, held
+    // by different waves) is in one place; BN is a multiple of d, so a tile holds whole
+    // heads.  Each row's position and, per key/value head of the tile, the page of its
+    // slot are looked up once into LDS beside the tile.  Items are (row, head, dims
+    // j .. j + 3 < d/2 and their partners j + d/2): query and key pairs are rotated,
+    // value pieces stored as they are.
+    const PostQkvArgs& ra = ea;
+    constexpr int TP = BN + 8;
+    constexpr int HPT_MAX = BN / 64;                         // heads per tile, at most (d >= 64)
+    static_assert(BM * TP * 4 + BM * (1 + HPT_MAX) * 4 <= STAGES * SLOT, "the staged tile fits in the ring");
+    float* tile = reinterpret_cast<float*>(&lds[0][0]);
+    int* rpos = reinterpret_cast<int*>(tile + BM * TP);      // [BM] positions
+    int* rpage = rpos + BM;                                  // [BM][HPT_MAX] pages
+    const int d = ra.d, half = d / 2, pq = d / 8, hpt = BN / d, head0 = n0 / d;
+    const int n_heads = ra.Hq + 2 * ra.Hkv;
+    if (live) {
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            tile[(wm * WM + i * 32 + 8 * (r >> 2) + 4 * kg + (r & 3)) * TP + wn * WN + j * 32 + lr] = acc[0][i][j][r];
+    }
+    if (threadIdx.x < BM) {
+      rpos[threadIdx.x] = rope_pos_r;
+#pragma unroll
+      for (int hl = 0; hl < RHPT; ++hl) rpage[threadIdx.x * HPT_MAX + hl] = rope_page_r[hl];
+    }
+    barrier();
+#pragma unroll
+    for (int k = 0; k < RIPT; ++k) {
+      const int e = threadIdx.x + k * G::THREADS;
+      if (e >= BM * hpt * pq) break;
+      const int rr = e / (hpt * pq), hl = (e / pq) % hpt, j = 4 * (e % pq);
+      const int row = m0 + rr, h = head0 + hl;
+      if (row >= M || h >= n_heads) continue;
+      const int pos = rpos[rr], page = rpage[rr * HPT_MAX + hl];
+      const float* src = tile + rr * TP + hl * d;
+      const float4 x0 = *reinterpret_cast<const float4*>(src + j), x1 = *reinterpret_cast<const float4*>(src + j + half);
+      if (h >= ra.Hq + ra.Hkv) {
+        rope_store4<T>(ra, row, h, j, x0, pos, page);
+        rope_store4<T>(ra, row, h, j + half, x1, pos, page);
+      } else {
+        float4 c01, c23;
+        if constexpr (RPRE) {
+          c01 = rope_c[k][0];
+          c23 = rope_c[k][1];
+        } else {
+          c01 = *reinterpret_cast<const float4*>(ra.rope_tab + long(row) * half + j);
+          c23 = *reinterpret_cast<const float4*>(ra.rope_tab + long(row) * half + j + 2);
+        }
+        const float2 cs[4] = {make_float2(c01.x, c01.y), make_float2(c01.z, c01.w), make_float2(c23.x, c23.y),
+                              make_float2(c23.z, c23.w)};
+        float4 y0, y1;
+        rope_pair4(x0, x1, cs, y0, y1);
+        rope_store4<T>(ra, row, h, j, y0, pos, page);
+        rope_store4<T>(ra, row, h, j + half, y1, pos, page);
+      }
+    }
+    return;
+  }
   if (!live) return;
   constexpr int PS = 40;                                   // patch row stride (floats)
   float* patch = reinterpret_cast<float*>(&lds[0][0]) + wave * (32 * PS);

@@ -5,7 +5,10 @@
 // §4 (KV residency, Fig. 8): decode requests extend their rank-local cache on
 // every KV head, while the prefill chunk appends to its head-sharded cache, i.e.
 // to this rank's KV heads only, for all chunk rows (local rows from this rank's
-// projection, peer rows from the All-to-All stand-in buffer).
+// projection, peer rows from the All-to-All stand-in buffer).  A step with at most one
+// chunk rotates and appends its local rows in the QKV projection's epilogue
+// (gemm_core.h); this kernel then only copies the peer rows and the peer_attn_in rows.
+// The rotation and routing helpers are shared (rope.h).
 //
 // Pool layout: page = [K plane: 16-byte chunks of dims, chunk-major over the slots
 // (k_elem) | V plane: d x page_size dim-major]; position p of a table row is slot
@@ -17,6 +20,7 @@
 // fp64) and the rotation itself runs in fp32.
 #include <cmath>
 
+#include "rope.h"
 #include "xp_device.h"
 #include "xp_internal.h"
 
@@ -61,18 +65,6 @@ __device__ __forceinline__ void copy8(void* dst, long di, const void* src, long 
   uint4* d4 = reinterpret_cast<uint4*>(static_cast<T*>(dst) + di);
   d4[0] = s4[0];
   if constexpr (sizeof(T) == 4) d4[1] = s4[1];
-}
-
-// sin and cos of x (radians, |x| < 2^40) in fp64.  x is first reduced modulo 2 pi by
-// Cody and Waite's two-constant method (2 pi = P1 + P2, P1 the double nearest 2 pi; for
-// these magnitudes k P1 is exact inside the fma and the remainder is good to a few
-// units in the last place), so the library's sincos only ever sees |r| <= pi.
-__device__ __forceinline__ void sincos_2pi(double x, double* sn, double* cn) {
-  constexpr double P1 = 6.283185307179586;        // 0x1.921fb54442d18p+2
-  constexpr double P2 = 2.4492935982947064e-16;   // 2 pi - P1
-  const double k = rint(x * (1.0 / P1));
-  const double r = fma(-k, P2, fma(-k, P1, x));
-  sincos(r, sn, cn);
 }
 
 // One workgroup per row task: tasks [0, M) are this rank's rows; the chunk's peer
@@ -154,13 +146,25 @@ __global__ __launch_bounds__(256) void post_qkv_kernel(PostQkvArgs a) {
   }
 
   const bool is_dec = task >= a.n_pl;
-  const int i = task - a.n_pl;          // decode request
-  const int t = a.off + task;           // chunk row of a local prefill row
-  const int pos = is_dec ? a.dec_ctx[i] : a.prior + t;
-  int* pg = reinterpret_cast<int*>(cs + d);  // [Hkv] page of this row's slot per kv head, -2: not appended here
-  const float* row = a.qkv + long(task) * ldq;
-  const int oq_w = (a.Hq - hq_loc) * d, ok_w = (a.Hkv - hkv_loc) * d;
-  const long pq_out = long(task) * (oq_w + 2 * ok_w);
+  const int row = task;                 // local row: the chunk's local rows, then the decodes
+  const int oq_w = (a.Hq - hq_loc) * d;
+  // local prefill rows: attention outputs of the heads other ranks own arrive as peer_attn_in
+  auto copy_peer_attn = [&] {
+    if (is_dec || oq_w == 0) return;
+    for (int e = 8 * tid; e < oq_w; e += 256 * 8) {
+      const int hi = e / d, j = e % d;
+      const int h = hi < q0 ? hi : hi + hq_loc;
+      copy8<T>(a.attn, long(task) * a.Hq * d + long(h) * d + j, a.peer_attn_in, long(task) * oq_w + e);
+    }
+  };
+  if (a.rope_done) {   // the QKV projection's epilogue rotated and appended this row
+    copy_peer_attn();
+    return;
+  }
+  const int pos = rope_pos(a, row);
+  float2* cs2 = reinterpret_cast<float2*>(cs);   // [d/2] (cos, sin)
+  int* pg = reinterpret_cast<int*>(cs + d);      // [Hkv] page of this row's slot per kv head (rope_page)
+  const float* qrow = a.qkv + long(task) * ldq;
 
   // rotated q and k: item (head h, dims j .. j + 3 < d/2) with partners j + d/2.  Each
   // thread loads a batch of items before storing any of them (the compiler cannot prove
@@ -177,32 +181,18 @@ __global__ __launch_bounds__(256) void post_qkv_kernel(PostQkvArgs a) {
       x0[u] = x1[u] = v0[u] = v1[u] = make_float4(0.f, 0.f, 0.f, 0.f);
       if (e < n_items) {
         const int h = e / quads, j = 4 * (e % quads);
-        x0[u] = *reinterpret_cast<const float4*>(row + h * d + j);
-        x1[u] = *reinterpret_cast<const float4*>(row + h * d + j + half);
+        x0[u] = *reinterpret_cast<const float4*>(qrow + h * d + j);
+        x1[u] = *reinterpret_cast<const float4*>(qrow + h * d + j + half);
         if (h >= a.Hq) {  // the value row of kv head h - Hq
-          v0[u] = *reinterpret_cast<const float4*>(row + (a.Hkv + h) * d + j);
-          v1[u] = *reinterpret_cast<const float4*>(row + (a.Hkv + h) * d + j + half);
+          v0[u] = *reinterpret_cast<const float4*>(qrow + (a.Hkv + h) * d + j);
+          v1[u] = *reinterpret_cast<const float4*>(qrow + (a.Hkv + h) * d + j + half);
         }
       }
     }
   };
   load_batch(tid);
-  if (tid < half) {
-    double sn, cn;
-    sincos_2pi(double(pos) * a.inv_freq[tid], &sn, &cn);
-    cs[tid] = float(cn);
-    cs[half + tid] = float(sn);
-  }
-  for (int g = tid; g < a.Hkv; g += 256) {
-    int page = -2;
-    if (is_dec) {
-      page = (pos >= 0 && pos / S < a.dec_max_blocks) ? a.dec_pages[(long(i) * a.Hkv + g) * a.dec_max_blocks + pos / S]
-                                                       : -1;
-    } else if (g >= k0 && g < k0 + hkv_loc) {
-      page = a.pre_pages[long(g - k0) * a.pre_max_blocks + pos / S];
-    }
-    pg[g] = page;
-  }
+  if (tid < half) cs2[tid] = rope_cs(pos, a.inv_freq[tid]);
+  for (int g = tid; g < a.Hkv; g += 256) pg[g] = rope_page(a, row, g, pos);
   __syncthreads();
   for (int e0 = tid; e0 < n_items; e0 += 256 * kBatch) {
     if (e0 != tid) load_batch(e0);
@@ -211,53 +201,19 @@ __global__ __launch_bounds__(256) void post_qkv_kernel(PostQkvArgs a) {
       const int e = e0 + 256 * u;
       if (e >= n_items) break;
       const int h = e / quads, j = 4 * (e % quads);
-      const float4 c = *reinterpret_cast<const float4*>(cs + j), sn = *reinterpret_cast<const float4*>(cs + half + j);
+      const float2 c4[4] = {cs2[j], cs2[j + 1], cs2[j + 2], cs2[j + 3]};
       float4 y0, y1;
-      y0.x = x0[u].x * c.x - x1[u].x * sn.x, y1.x = x1[u].x * c.x + x0[u].x * sn.x;
-      y0.y = x0[u].y * c.y - x1[u].y * sn.y, y1.y = x1[u].y * c.y + x0[u].y * sn.y;
-      y0.z = x0[u].z * c.z - x1[u].z * sn.z, y1.z = x1[u].z * c.z + x0[u].z * sn.z;
-      y0.w = x0[u].w * c.w - x1[u].w * sn.w, y1.w = x1[u].w * c.w + x0[u].w * sn.w;
-      if (h < a.Hq) {
-        long o;
-        void* dst;
-        if (is_dec) {
-          dst = a.q_dec;
-          o = (long(i) * a.Hq + h) * d;
-        } else if (h >= q0 && h < q0 + hq_loc) {
-          dst = a.q_pre;
-          o = (long(h - q0) * a.chunk + t) * d;
-        } else {
-          dst = a.peer_qkv_out;
-          o = pq_out + long(h < q0 ? h : h - hq_loc) * d;
-        }
-        St4<T>::store(dst, o + j, y0);
-        St4<T>::store(dst, o + j + half, y1);
-      } else {
-        const int g = h - a.Hq;
-        const int page = pg[g];
-        if (page != -2) {
-          put_kv4<T>(a.pool, a.n_pages, S, d, page, pos % S, j, y0, v0[u], a.status);
-          put_kv4<T>(a.pool, a.n_pages, S, d, page, pos % S, j + half, y1, v1[u], a.status);
-        } else {
-          const int gi = g < k0 ? g : g - hkv_loc;
-          const long ok = pq_out + oq_w + long(gi) * d;
-          const long ov = pq_out + oq_w + ok_w + long(gi) * d;
-          St4<T>::store(a.peer_qkv_out, ok + j, y0);
-          St4<T>::store(a.peer_qkv_out, ok + j + half, y1);
-          St4<T>::store(a.peer_qkv_out, ov + j, v0[u]);
-          St4<T>::store(a.peer_qkv_out, ov + j + half, v1[u]);
-        }
+      rope_pair4(x0[u], x1[u], c4, y0, y1);
+      const int page = h >= a.Hq ? pg[h - a.Hq] : 0;
+      rope_store4<T>(a, row, h, j, y0, pos, page);
+      rope_store4<T>(a, row, h, j + half, y1, pos, page);
+      if (h >= a.Hq) {
+        rope_store4<T>(a, row, h + a.Hkv, j, v0[u], pos, page);
+        rope_store4<T>(a, row, h + a.Hkv, j + half, v1[u], pos, page);
       }
     }
   }
-  // local prefill rows: attention outputs of the heads other ranks own arrive as peer_attn_in
-  if (!is_dec && oq_w > 0) {
-    for (int e = 8 * tid; e < oq_w; e += 256 * 8) {
-      const int hi = e / d, j = e % d;
-      const int h = hi < q0 ? hi : hi + hq_loc;
-      copy8<T>(a.attn, long(task) * a.Hq * d + long(h) * d + j, a.peer_attn_in, long(task) * oq_w + e);
-    }
-  }
+  copy_peer_attn();
 }
 
 template <typename T>
@@ -295,13 +251,21 @@ __global__ __launch_bounds__(256) void kv_gather_kernel(const void* pool, int n_
 
 }  // namespace
 
+void rope_frequencies(double base, int d, double* inv_freq) {
+  for (int i = 0; i < d / 2 && i < 64; ++i) inv_freq[i] = std::pow(base, -2.0 * double(i) / double(d));
+}
+
 xp_status launch_post_qkv(int dtype, const PostQkvArgs& args, hipStream_t s) {
-  const int tasks = args.n_pl + args.n_d + cdiv(args.chunk - args.n_pl, kPeerRowsPerTask);
+  const int n_peer_tasks = cdiv(args.chunk - args.n_pl, kPeerRowsPerTask);
+  int tasks = args.n_pl + args.n_d + n_peer_tasks;
+  // with the rotation done by the QKV epilogue only the peer rows and the peer_attn_in
+  // copies remain (none without sequence parallelism)
+  if (args.rope_done && n_peer_tasks == 0 && args.Hq / args.P == args.Hq) tasks = 0;
   if (tasks == 0) return XP_OK;
   if (args.d % 8 || args.d / 2 > 64) return fail(XP_EUNSUPPORTED, "RoPE: head_dim %d", args.d);
   // the rotation frequencies base^(-2i/d), formed once in fp64 on the host
   PostQkvArgs a = args;
-  for (int i = 0; i < a.d / 2; ++i) a.inv_freq[i] = std::pow(a.rope_base, -2.0 * double(i) / double(a.d));
+  rope_frequencies(a.rope_base, a.d, a.inv_freq);
   const size_t shm = size_t(a.d) * sizeof(float) + size_t(a.Hkv) * sizeof(int);
   if (dtype == XP_BF16)
     hipLaunchKernelGGL(post_qkv_kernel<bf16_t>, dim3(tasks), dim3(256), shm, s, a);

@@ -28,8 +28,17 @@ inline int cdiv(long a, long b) { return int((a + b - 1) / b); }
 inline int dtype_bytes(int dtype) { return dtype == XP_BF16 ? 2 : 4; }
 
 // ---- launchers (each validates its own arguments) ------------------------------
+struct RopeTab;
+struct PostQkvArgs;
+// `rope` (optional): also form each row's RoPE table (see RopeTab)
 xp_status launch_rmsnorm(int dtype, const void* x, int x_is_f32, const void* gamma, void* y, int M,
-                         int H, float eps, uint32_t* status_clear, hipStream_t s);
+                         int H, float eps, uint32_t* status_clear, hipStream_t s, const RopeTab* rope = nullptr);
+// The QKV projection with RoPE and the appends fused into its epilogue (no qkv output):
+// rows [0, M) are the step's local rows as PostQkvArgs describes them.  XP_EUNSUPPORTED
+// when the head dimension does not divide the candidate tiles' widths.
+bool gemm_rope_supported(int dtype, int d);
+xp_status launch_gemm_rope(int dtype, const void* A, const void* B, int M, int N, int K, const PostQkvArgs& ra,
+                           hipStream_t s);
 
 int device_cus();   // CUs of the current device (256 when none is visible)
 int gemm_chunks(int dtype, int epi, int N, int K);
@@ -59,8 +68,21 @@ struct PostQkvArgs {
   void* q_pre;
   void* attn;
   uint32_t* status;
-  double inv_freq[64];   // base^(-2i/d), i < d/2: filled by launch_post_qkv
+  double inv_freq[64];       // base^(-2i/d), i < d/2: filled by launch_post_qkv
+  const float2* rope_tab;    // [rows][d/2] (cos, sin) of each local row's position (fused epilogue)
+  int rope_done;             // the QKV GEMM's epilogue already rotated and appended the local rows
 };
+
+// Each row's RoPE (cos, sin) pairs, formed by the first RMSNorm launch of a step for the
+// QKV GEMM's fused epilogue: tab[row][i] for i < half, at position pos0 + row for
+// rows < n_pl (the chunk's local rows) and dec_ctx[row - n_pl] after them.
+struct RopeTab {
+  float2* tab;
+  int half, n_pl, pos0;
+  const int32_t* dec_ctx;
+  double inv_freq[64];
+};
+void rope_frequencies(double base, int d, double* inv_freq);
 xp_status launch_post_qkv(int dtype, const PostQkvArgs& a, hipStream_t s);
 
 xp_status launch_kv_append(int dtype, void* pool, int n_pages, int S, int d, const int32_t* table,
