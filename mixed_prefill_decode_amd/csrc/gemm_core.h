@@ -395,9 +395,9 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(const char* __rest
     // store on disjoint banks), so a rotation pair (dims j and j + d/2 of one head, held
     // by different waves) is in one place; BN is a multiple of d, so a tile holds whole
     // heads.  Each row's position and, per key/value head of the tile, the page of its
-    // slot are looked up once into LDS beside the tile.  Items are (row, head, dims
-    // j .. j + 3 < d/2 and their partners j + d/2): query and key pairs are rotated,
-    // value pieces stored as they are.
+    // slot (looked up before the K loop) go to LDS beside the tile.  Items of the first
+    // pass are (row, head, dims j .. j + 3 < d/2 and their partners j + d/2) of query and
+    // key heads, rotated and stored; value heads, stored as they are, take a second pass.
     const PostQkvArgs& ra = ea;
     constexpr int TP = BN + 8;
     constexpr int HPT_MAX = BN / 64;                         // heads per tile, at most (d >= 64)
@@ -428,28 +428,59 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(const char* __rest
       if (e >= BM * hpt * pq) break;
       const int rr = e / (hpt * pq), hl = (e / pq) % hpt, j = 4 * (e % pq);
       const int row = m0 + rr, h = head0 + hl;
-      if (row >= M || h >= n_heads) continue;
+      if (row >= M || h >= ra.Hq + ra.Hkv) continue;       // value heads: the pass below
       const int pos = rpos[rr], page = rpage[rr * HPT_MAX + hl];
       const float* src = tile + rr * TP + hl * d;
       const float4 x0 = *reinterpret_cast<const float4*>(src + j), x1 = *reinterpret_cast<const float4*>(src + j + half);
-      if (h >= ra.Hq + ra.Hkv) {
-        rope_store4<T>(ra, row, h, j, x0, pos, page);
-        rope_store4<T>(ra, row, h, j + half, x1, pos, page);
+      float4 c01, c23;
+      if constexpr (RPRE) {
+        c01 = rope_c[k][0];
+        c23 = rope_c[k][1];
       } else {
-        float4 c01, c23;
-        if constexpr (RPRE) {
-          c01 = rope_c[k][0];
-          c23 = rope_c[k][1];
-        } else {
-          c01 = *reinterpret_cast<const float4*>(ra.rope_tab + long(row) * half + j);
-          c23 = *reinterpret_cast<const float4*>(ra.rope_tab + long(row) * half + j + 2);
+        c01 = *reinterpret_cast<const float4*>(ra.rope_tab + long(row) * half + j);
+        c23 = *reinterpret_cast<const float4*>(ra.rope_tab + long(row) * half + j + 2);
+      }
+      const float2 cs[4] = {make_float2(c01.x, c01.y), make_float2(c01.z, c01.w), make_float2(c23.x, c23.y),
+                            make_float2(c23.z, c23.w)};
+      float4 y0, y1;
+      rope_pair4(x0, x1, cs, y0, y1);
+      rope_store4<T>(ra, row, h, j, y0, pos, page);
+      rope_store4<T>(ra, row, h, j + half, y1, pos, page);
+    }
+    // Value heads, whose page plane is dim-major: an item is 4 rows x 4 dims, so that
+    // rows on consecutive slots of one page leave as one 4-slot store per dim.  Lanes
+    // take the four row quads of 16 rows first, then the dim quads.
+    static_assert(BM % 16 == 0, "value pass walks 16-row groups");
+    if (head0 + hpt > ra.Hq + ra.Hkv) {
+      const int n_items = BM / 4 * hpt * (d / 4);
+      for (int e = threadIdx.x; e < n_items; e += G::THREADS) {
+        const int qd = e & 3, g = (e >> 2) % (d / 4), rest = e / d;
+        const int rr0 = (rest % (BM / 16)) * 16 + qd * 4, hl = rest / (BM / 16);
+        const int row0 = m0 + rr0, h = head0 + hl;
+        if (row0 >= M || h < ra.Hq + ra.Hkv || h >= n_heads) continue;
+        float4 x[4];
+        int pos[4], page[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          x[i] = *reinterpret_cast<const float4*>(tile + (rr0 + i) * TP + hl * d + 4 * g);
+          pos[i] = rpos[rr0 + i];
+          page[i] = rpage[(rr0 + i) * HPT_MAX + hl];
         }
-        const float2 cs[4] = {make_float2(c01.x, c01.y), make_float2(c01.z, c01.w), make_float2(c23.x, c23.y),
-                              make_float2(c23.z, c23.w)};
-        float4 y0, y1;
-        rope_pair4(x0, x1, cs, y0, y1);
-        rope_store4<T>(ra, row, h, j, y0, pos, page);
-        rope_store4<T>(ra, row, h, j + half, y1, pos, page);
+        const bool run = row0 + 3 < M && (ra.S & 3) == 0 && (pos[0] & 3) == 0 && page[0] >= 0 &&
+                         page[0] < ra.n_pages && page[1] == page[0] && page[2] == page[0] && page[3] == page[0] &&
+                         pos[1] == pos[0] + 1 && pos[2] == pos[0] + 2 && pos[3] == pos[0] + 3;
+        if (run) {
+          const int S = ra.S;
+          const long vb = long(page[0]) * 2 * S * d + long(S) * d + long(4 * g) * S + pos[0] % S;
+          St4<T>::store(ra.pool, vb, make_float4(x[0].x, x[1].x, x[2].x, x[3].x));
+          St4<T>::store(ra.pool, vb + S, make_float4(x[0].y, x[1].y, x[2].y, x[3].y));
+          St4<T>::store(ra.pool, vb + 2 * S, make_float4(x[0].z, x[1].z, x[2].z, x[3].z));
+          St4<T>::store(ra.pool, vb + 3 * S, make_float4(x[0].w, x[1].w, x[2].w, x[3].w));
+        } else {
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            if (row0 + i < M) rope_store4<T>(ra, row0 + i, h, 4 * g, x[i], pos[i], page[i]);
+        }
       }
     }
     return;
