@@ -7,9 +7,11 @@ RMSNorm + QKV GEMM, RoPE + paged K/V append, decode attention || prefill
 attention on a CU partition, O-proj, RMSNorm, gate/up + SwiGLU, down), inputs
 resident in HBM.  Prints one JSON line (metric, value, roofline of the dominant
 kernel, the fp64 oracle timed on the host as a baseline) on stdout; details go
-to stderr.
+to stderr.  The dominant kernel is the one with the longest launches inside the
+step, timed by the library's stage events over a second pass of the same steps
+(`stages_us`); standalone loops of each kernel are reported beside it (`kernels`).
 
-    python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--workload C2]
+    python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--workload C5]
 """
 from __future__ import annotations
 
@@ -48,6 +50,9 @@ def parse():
     p.add_argument("--kernel-only", choices=["none", "qkv", "o", "gate_up", "down", "decode_attn", "prefill_attn", "read",
                                              "copy"], default="none",
                    help="only launch one kernel repeatedly (for counter runs)")
+    p.add_argument("--no-kernel-loops", action="store_true",
+                   help="skip the standalone per-kernel timing loops (a kernel trace then holds only the "
+                        "step's own launches)")
     p.add_argument("--extra-decode", default="C4",
                    help="also time this workload's decode attention alone (its KV pool is built on the device); "
                         "'none' to skip")
@@ -126,12 +131,15 @@ KERNEL_SOURCES = {
                      "mixed_prefill_decode_amd/csrc/xp_device.h"),
 }
 KERNEL_NAMES = {
-    "qkv": "gemm_kernel<bf16,F32> (QKV projection)", "o": "gemm_kernel<bf16,AddT> (O projection + residual)",
+    "qkv": "gemm_kernel<bf16,F32 or RoPE/append epilogue> (QKV projection)", "o": "gemm_kernel<bf16,AddT> (O projection + residual)",
     "gate_up": "gemm_kernel<bf16,SwiGLU> (gate/up projection)",
     "down": "gemm_kernel<bf16,AddF32> (down projection + residual)",
     "decode_attn": "decode_split_kernel + decode_combine_kernel (paged GQA decode attention)",
     "prefill_attn": "prefill_kernel (+ prefill_combine_kernel) (causal chunked-prefill attention)",
 }
+# layer stages (xp_ctx_stage_timing) -> the kernel figures above they time inside the step
+STAGE_KERNELS = {"qkv": "qkv", "o": "o", "gate_up": "gate_up", "down": "down", "decode": "decode_attn",
+                 "prefill": "prefill_attn"}
 
 
 def sources_hash(kernel: str) -> str:
@@ -790,11 +798,25 @@ def main():
     ms = ev0.elapsed_time(ev1) / args.steps
     tokens_per_s = wl.n_rows * args.steps / wall
     assert step.status() == 0
+    # The same steps again with the library's stage events (xp_ctx_stage_timing: HIP
+    # events around each stage on the stream it runs on): the per-launch durations of the
+    # kernels inside the step.  The events add a few microseconds between kernels (about
+    # 5% of a C5 step), so this pass is not the one the step rate comes from.
+    step.ctx.stage_timing(args.steps)
+    ev2, ev3 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev2.record()
+    for _ in range(args.steps):
+        one_step()
+    ev3.record()
+    torch.cuda.synchronize()
+    stages = {name: round(t / n * 1e3, 2) for name, (n, t) in step.ctx.stage_times().items() if n}
+    stages["step_with_events"] = round(ev2.elapsed_time(ev3) / args.steps * 1e3, 2)
+    step.ctx.stage_timing(0)
 
     # per-kernel measurements (standalone, all CUs, HIP events on the launch stream)
     kern = {}
     calls = kernel_calls(X, torch, inst, step0, dev)
-    for name, (fn, work, unit) in calls.items():
+    for name, (fn, work, unit) in ([] if args.no_kernel_loops else calls.items()):
         kern[name] = kernel_figures(name, timer(fn, args.repeats), work, unit)
         if name in ("qkv", "o", "gate_up", "down"):
             m_, n_, k_ = gemm_list(wl)[name]
@@ -808,7 +830,7 @@ def main():
         kern["decode_attn"]["read_ceiling_GBs"] = round(ceiling, 1)
         kern["decode_attn"]["ceiling_frac"] = round(kern["decode_attn"]["GBs"] / ceiling, 4)
 
-    if "serialized_layer_us" in seg:
+    if "serialized_layer_us" in seg and "decode_attn" in kern:
         # the attention segment alone: decode then prefill each on the whole GPU
         # (standalone kernel times above), the contention-free bound max(T_D, T_P), and
         # the overlapped modes' segment time, i.e. their layer time less the layer's
@@ -820,19 +842,24 @@ def main():
             "unmasked": round(seg["unmasked_layer_us"] - rest, 1),
             "partitions": {kk: round(v - rest, 1) for kk, v in seg["partition_layer_us"].items()}}
 
-    # the roofline of the kernel that takes the most time in this workload's step
-    dom = max(kern, key=lambda n: kern[n]["us"])
+    # the roofline of the kernel that takes the most time in this workload's timed steps,
+    # from its launches inside them (the stage events); the standalone loops above are
+    # reported beside it
+    in_step = {kn: stages[sn] for sn, kn in STAGE_KERNELS.items() if sn in stages and kn in calls}
+    if not in_step:
+        in_step = {kn: kern[kn]["us"] for kn in kern}
+    dom = max(in_step, key=in_step.get)
     fn, work, unit = calls[dom]
-    t_dom = kern[dom]["us"] * 1e-6
+    t_dom = in_step[dom] * 1e-6
     traffic = recorded_traffic(wl.name, dom)
     if unit == "byte":
         roofline = {"bound": "hbm", "achieved": round(work / t_dom / 1e9, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                     "frac": round(work / t_dom / 1e9 / PEAK_HBM_GBS, 4), "traffic": traffic,
-                    "kernel": KERNEL_NAMES[dom], "bytes_per_launch": work}
+                    "kernel": KERNEL_NAMES[dom], "bytes_per_launch": work, "launch_us": round(t_dom * 1e6, 2)}
     else:
         roofline = {"bound": "mfma", "achieved": round(work / t_dom / 1e12, 2), "peak": PEAK_BF16_TFLOPS,
                     "unit": "TFLOP/s", "frac": round(work / t_dom / 1e12 / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
-                    "kernel": KERNEL_NAMES[dom], "flops_per_launch": work}
+                    "kernel": KERNEL_NAMES[dom], "flops_per_launch": work, "launch_us": round(t_dom * 1e6, 2)}
     log(f"[bench] layer {ms * 1e3:.1f} us/step, {tokens_per_s:.0f} tokens/s; kernels {json.dumps(kern)}")
     log(f"[bench] split attention {json.dumps(seg)}")
 
@@ -858,7 +885,7 @@ def main():
                    "chunk": wl.chunk_len, "prior": wl.prior_len, "sp_degree": wl.sp_degree,
                    "decode_cus": k, "split_attention": timed_mode if wl.n_decode and wl.chunk_len else None,
                    "page_size": wl.page_size},
-        "roofline": roofline, "cpu_baseline": cpu, "kernels": kern, "extra_decode": extra,
+        "roofline": roofline, "cpu_baseline": cpu, "stages_us": stages, "kernels": kern, "extra_decode": extra,
         "split_attention": seg, "scheduler": sched,
     }
     print(json.dumps(line), flush=True)

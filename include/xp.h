@@ -211,6 +211,31 @@ xp_status xp_ctx_cu_masks(const xp_ctx* ctx, uint32_t* decode_mask8, uint32_t* p
  * kernel-level entry point on the same CU partition the layer step uses. */
 xp_status xp_ctx_streams(const xp_ctx* ctx, void** decode_stream, void** prefill_stream);
 
+/* Per-stage GPU time of the layer steps a context runs, a measurement aid for the
+ * stages of [CS] §6.1 Fig. 10 (the shared-linear segments and the two attention
+ * kernels).  xp_ctx_stage_timing(ctx, capacity > 0) brackets each of the next
+ * `capacity` eager runs of every stage (xp_layer_forward, xp_layer_forward_chunks,
+ * xp_stack_forward; graph launches are not timed) with two timing events recorded on
+ * the stream that stage runs on, so a stage's time is its kernels' time (plus the few
+ * microseconds between two events); runs past the capacity go untimed.  A new call
+ * restarts the count; capacity 0 frees the events.  Capacity is at most 4096.
+ * xp_ctx_stage_time waits for the recorded runs of one stage and returns their count
+ * and summed duration in milliseconds (0 and 0 when none).  A stage that launches
+ * nothing in a run (e.g. RoPE/append when the QKV epilogue did it all) still counts,
+ * with its near-zero time. */
+#define XP_STAGE_NORM1 0        /* RMSNorm-1 (+ the rows' RoPE table for the fused QKV) */
+#define XP_STAGE_QKV 1          /* QKV projection (with RoPE + appends when fused)   */
+#define XP_STAGE_ROPE_APPEND 2  /* stand-alone RoPE/append and stand-in copies       */
+#define XP_STAGE_DECODE 3       /* decode attention + split combine                  */
+#define XP_STAGE_PREFILL 4      /* prefill attention + split combine                 */
+#define XP_STAGE_O 5            /* O projection + residual                           */
+#define XP_STAGE_NORM2 6        /* RMSNorm-2                                         */
+#define XP_STAGE_GATE_UP 7      /* gate/up projection + SwiGLU                       */
+#define XP_STAGE_DOWN 8         /* down projection + residual                        */
+#define XP_STAGE_COUNT 9
+xp_status xp_ctx_stage_timing(xp_ctx* ctx, int32_t capacity);
+xp_status xp_ctx_stage_time(xp_ctx* ctx, int32_t stage, int32_t* count, double* total_ms);
+
 xp_status xp_layer_workspace_layout(const xp_ctx* ctx, const xp_layer_shape* shape,
                                     const xp_batch_desc* desc, xp_ws_layout* layout);
 

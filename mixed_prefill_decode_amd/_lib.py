@@ -26,7 +26,7 @@ __all__ = ["XpError", "lib", "close_all", "XP_F32", "XP_BF16", "XP_EPI_F32", "XP
            "xp_decode_workspace_size", "xp_decode_attention", "xp_decode_attention_static", "XP_DECODE_STATIC_SCRATCH_BYTES",
            "xp_prefill_workspace_size", "xp_prefill_attention",
            "xp_probe_hw_ids", "xp_probe_read", "xp_calibrate_decode_cus", "xp_probe_read_curve", "CuCurve",
-           "XP_SPLIT_SERIALIZED", "XP_SPLIT_UNMASKED",
+           "XP_SPLIT_SERIALIZED", "XP_SPLIT_UNMASKED", "STAGES", "XP_STAGE_COUNT",
            "xp_waterfill", "xp_iteration_latency", "xp_admission", "xp_decode_placement", "xp_schedule",
            "ScheduleCall", "WaterfillCall", "xp_fit_affine", "xp_fit_latency_model", "XP_SCHED_DONE", "XP_SCHED_BUDGET", "XP_SCHED_NO_HOST", "xp_build_info", "xp_last_error"]
 
@@ -35,6 +35,9 @@ XP_EPI_F32, XP_EPI_ADD_T, XP_EPI_ADD_F32, XP_EPI_SWIGLU = 0, 1, 2, 3
 XP_DEV_BAD_PAGE = 1
 XP_SPLIT_SERIALIZED, XP_SPLIT_UNMASKED = 0, -1
 XP_SCHED_DONE, XP_SCHED_BUDGET, XP_SCHED_NO_HOST = 0, 1, 2
+# layer stages of xp_ctx_stage_timing, in XP_STAGE_* order
+STAGES = ("norm1", "qkv", "rope_append", "decode", "prefill", "o", "norm2", "gate_up", "down")
+XP_STAGE_COUNT = len(STAGES)
 STATUS_NAMES = {0: "XP_OK", -1: "XP_EINVAL", -2: "XP_ESHAPE", -3: "XP_EPAGE", -4: "XP_EHIP",
                 -5: "XP_EUNSUPPORTED", -6: "XP_EWORKSPACE"}
 
@@ -42,7 +45,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libxp.so")
 
 # every symbol include/xp.h declares
 EXPORTED = ["xp_last_error", "xp_build_info", "xp_ctx_create", "xp_ctx_destroy", "xp_ctx_cu_masks",
-            "xp_ctx_streams",
+            "xp_ctx_streams", "xp_ctx_stage_timing", "xp_ctx_stage_time",
             "xp_layer_workspace_layout", "xp_layer_forward", "xp_validate_batch", "xp_layer_read_status",
             "xp_layer_workspace_layout_chunks", "xp_layer_forward_chunks", "xp_validate_chunks",
             "xp_stack_forward", "xp_stack_graph_create", "xp_graph_launch", "xp_graph_destroy",
@@ -172,6 +175,8 @@ def _declare(L):
         "xp_ctx_destroy": (S, [_vp]),
         "xp_ctx_cu_masks": (S, [_vp, _vp, _vp, _vp]),
         "xp_ctx_streams": (S, [_vp, C.POINTER(_vp), C.POINTER(_vp)]),
+        "xp_ctx_stage_timing": (S, [_vp, _i32]),
+        "xp_ctx_stage_time": (S, [_vp, _i32, C.POINTER(_i32), C.POINTER(C.c_double)]),
         "xp_layer_workspace_layout": (S, [_vp, C.POINTER(LayerShape), C.POINTER(BatchDesc), C.POINTER(WsLayout)]),
         "xp_layer_forward": (S, [_vp, C.POINTER(LayerShape), C.POINTER(BatchDesc), C.POINTER(LayerWeights),
                                  C.POINTER(KvPages), _vp, _vp, _sz, _vp]),
@@ -319,6 +324,19 @@ class Ctx:
         d, p = _vp(), _vp()
         _check(lib().xp_ctx_streams(self.handle, C.byref(d), C.byref(p)))
         return d.value or 0, p.value or 0
+
+    def stage_timing(self, capacity: int):
+        """Times the next `capacity` eager runs of every layer stage (0 stops)."""
+        _check(lib().xp_ctx_stage_timing(self.handle, capacity))
+
+    def stage_times(self) -> dict:
+        """{stage name: (runs, total milliseconds)} of the runs timed so far (waits for them)."""
+        out = {}
+        for k, name in enumerate(STAGES):
+            n, ms = _i32(), C.c_double()
+            _check(lib().xp_ctx_stage_time(self.handle, k, C.byref(n), C.byref(ms)))
+            out[name] = (n.value, ms.value)
+        return out
 
     def close(self):
         if getattr(self, "handle", None):

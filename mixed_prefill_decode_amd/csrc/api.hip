@@ -36,6 +36,15 @@ xp_status fail(xp_status code, const char* fmt, ...) {
 
 using namespace xp;
 
+// Timing events of the layer stages (xp_ctx_stage_timing): per stage, `cap` pairs of
+// (begin, end) events, of which the first n[stage] hold recorded runs.
+struct StageTimer {
+  int cap = 0;
+  int n[XP_STAGE_COUNT] = {};
+  std::vector<hipEvent_t> ev;   // [stage][cap][2]
+  hipEvent_t* pair(int stage, int i) { return &ev[(size_t(stage) * cap + i) * 2]; }
+};
+
 struct xp_ctx {
   int device = 0;
   int n_cus = 0;
@@ -44,6 +53,7 @@ struct xp_ctx {
   hipStream_t s_dec = nullptr, s_pre = nullptr;
   hipEvent_t e_fork = nullptr, e_dec = nullptr, e_pre = nullptr;
   uint32_t mask_dec[8] = {}, mask_pre[8] = {};
+  StageTimer timer;
 };
 
 extern "C" {
@@ -291,6 +301,7 @@ xp_status xp_ctx_create(xp_ctx** out, int32_t device, int32_t decode_cus, int32_
 xp_status xp_ctx_destroy(xp_ctx* c) {
   if (!c) return XP_OK;
   ScopedDevice sd(c->device);
+  for (hipEvent_t e : c->timer.ev) (void)hipEventDestroy(e);
   if (c->s_dec) (void)hipStreamDestroy(c->s_dec);
   if (c->s_pre) (void)hipStreamDestroy(c->s_pre);
   if (c->e_fork) (void)hipEventDestroy(c->e_fork);
@@ -314,6 +325,48 @@ xp_status xp_ctx_streams(const xp_ctx* c, void** dec, void** pre) {
   if (!c) return fail(XP_EINVAL, "null ctx");
   if (dec) *dec = c->s_dec;
   if (pre) *pre = c->s_pre;
+  return XP_OK;
+}
+
+xp_status xp_ctx_stage_timing(xp_ctx* c, int32_t capacity) {
+  if (!c) return fail(XP_EINVAL, "null ctx");
+  if (capacity < 0 || capacity > 4096) return fail(XP_EINVAL, "stage timing capacity %d (0..4096)", capacity);
+  ScopedDevice sd(c->device);
+  StageTimer& t = c->timer;
+  for (int k = 0; k < XP_STAGE_COUNT; ++k) t.n[k] = 0;
+  if (capacity == t.cap) return XP_OK;
+  for (hipEvent_t e : t.ev) (void)hipEventDestroy(e);
+  t.ev.clear();
+  t.cap = 0;
+  std::vector<hipEvent_t> ev(size_t(XP_STAGE_COUNT) * capacity * 2, nullptr);
+  for (hipEvent_t& e : ev) {
+    const hipError_t r = hipEventCreateWithFlags(&e, hipEventReleaseToDevice);
+    if (r != hipSuccess) {
+      for (hipEvent_t x : ev)
+        if (x) (void)hipEventDestroy(x);
+      return fail(XP_EHIP, "hipEventCreate: %s", hipGetErrorString(r));
+    }
+  }
+  t.ev.swap(ev);
+  t.cap = capacity;
+  return XP_OK;
+}
+
+xp_status xp_ctx_stage_time(xp_ctx* c, int32_t stage, int32_t* count, double* total_ms) {
+  if (!c || !count || !total_ms) return fail(XP_EINVAL, "null argument");
+  if (stage < 0 || stage >= XP_STAGE_COUNT) return fail(XP_EINVAL, "stage %d (0..%d)", stage, XP_STAGE_COUNT - 1);
+  ScopedDevice sd(c->device);
+  StageTimer& t = c->timer;
+  double sum = 0;
+  for (int i = 0; i < t.n[stage]; ++i) {
+    hipEvent_t* e = t.pair(stage, i);
+    XP_HIP_TRY(hipEventSynchronize(e[1]));
+    float ms = 0.f;
+    XP_HIP_TRY(hipEventElapsedTime(&ms, e[0], e[1]));
+    sum += ms;
+  }
+  *count = t.n[stage];
+  *total_ms = sum;
   return XP_OK;
 }
 
@@ -500,6 +553,20 @@ struct LayerRun {
   const void* x;
   bool x_f32;
   bool clear_status;  // the first layer of a call resets the device status word
+  bool timed = true;  // eager runs record the context's stage events (graph captures do not)
+
+  // runs f() (launches on stream s) between the stage's timing events when the
+  // context times stages and the stage has room left
+  template <typename F>
+  xp_status stage(int id, hipStream_t s, F&& f) const {
+    StageTimer& t = ctx->timer;
+    if (!timed || t.n[id] >= t.cap) return f();
+    hipEvent_t* e = t.pair(id, t.n[id]++);
+    XP_HIP_TRY(hipEventRecord(e[0], s));
+    const xp_status st = f();
+    XP_HIP_TRY(hipEventRecord(e[1], s));
+    return st;
+  }
 
   xp_status pre(hipStream_t s) const;
   xp_status attend(hipStream_t s, bool split) const;
@@ -547,23 +614,32 @@ xp_status LayerRun::pre(hipStream_t s) const {
     rt.dec_ctx = d->dec_ctx;
     rope_frequencies(sh->rope_base, D, rt.inv_freq);
   }
-  if ((st = launch_rmsnorm(dt, x, x_f32 ? 1 : 0, weights.g_attn, ws + L.hn, M, H, sh->rms_eps,
-                           clear_status ? status : nullptr, s, fused ? &rt : nullptr)))
+  if ((st = stage(XP_STAGE_NORM1, s, [&] {
+         return launch_rmsnorm(dt, x, x_f32 ? 1 : 0, weights.g_attn, ws + L.hn, M, H, sh->rms_eps,
+                               clear_status ? status : nullptr, s, fused ? &rt : nullptr);
+       })))
     return st;
   if (fused) {
     PostQkvArgs pa = args_of(c0, n_d, false);
     pa.rope_tab = rt.tab;
-    if (M > 0 && (st = launch_gemm_rope(dt, ws + L.hn, weights.w_qkv, M, ldq, H, pa, s))) return st;
+    if (M > 0 && (st = stage(XP_STAGE_QKV, s, [&] { return launch_gemm_rope(dt, ws + L.hn, weights.w_qkv, M, ldq, H, pa, s); })))
+      return st;
     // what is left: the chunk's peer rows and the peer_attn_in copies (sequence parallel)
-    return launch_post_qkv(dt, args_of(c0, n_d, true), s);
+    return stage(XP_STAGE_ROPE_APPEND, s, [&] { return launch_post_qkv(dt, args_of(c0, n_d, true), s); });
   }
-  if (M > 0 && (st = launch_gemm(dt, XP_EPI_F32, ws + L.hn, weights.w_qkv, nullptr, nullptr, qkv, M, ldq, H,
-                                 ws + L.gemm_part, L.h1 - L.gemm_part, s)))
+  if (M > 0 && (st = stage(XP_STAGE_QKV, s, [&] {
+                  return launch_gemm(dt, XP_EPI_F32, ws + L.hn, weights.w_qkv, nullptr, nullptr, qkv, M, ldq, H,
+                                     ws + L.gemm_part, L.h1 - L.gemm_part, s);
+                })))
     return st;
-  if (ch.empty()) return launch_post_qkv(dt, args_of(nullptr, n_d, false), s);
-  for (size_t j = 0; j < ch.size(); ++j)
-    if ((st = launch_post_qkv(dt, args_of(&ch[j], j + 1 == ch.size() ? n_d : 0, false), s))) return st;
-  return XP_OK;
+  return stage(XP_STAGE_ROPE_APPEND, s, [&] {
+    if (ch.empty()) return launch_post_qkv(dt, args_of(nullptr, n_d, false), s);
+    for (size_t j = 0; j < ch.size(); ++j) {
+      const xp_status e = launch_post_qkv(dt, args_of(&ch[j], j + 1 == ch.size() ? n_d : 0, false), s);
+      if (e) return e;
+    }
+    return xp_status(XP_OK);
+  });
 }
 
 xp_status LayerRun::attend(hipStream_t s, bool split) const {
@@ -607,15 +683,15 @@ xp_status LayerRun::attend(hipStream_t s, bool split) const {
   };
   const bool concurrent = split && ctx->s_dec && n_d > 0 && !ch.empty();
   if (!concurrent) {
-    if ((st = decode(s))) return st;
-    if ((st = prefill(s))) return st;
+    if ((st = stage(XP_STAGE_DECODE, s, [&] { return decode(s); }))) return st;
+    if ((st = stage(XP_STAGE_PREFILL, s, [&] { return prefill(s); }))) return st;
   } else {
     XP_HIP_TRY(hipEventRecord(ctx->e_fork, s));
     XP_HIP_TRY(hipStreamWaitEvent(ctx->s_dec, ctx->e_fork, 0));
     XP_HIP_TRY(hipStreamWaitEvent(ctx->s_pre, ctx->e_fork, 0));
-    if ((st = decode(ctx->s_dec))) return st;
+    if ((st = stage(XP_STAGE_DECODE, ctx->s_dec, [&] { return decode(ctx->s_dec); }))) return st;
     XP_HIP_TRY(hipEventRecord(ctx->e_dec, ctx->s_dec));
-    if ((st = prefill(ctx->s_pre))) return st;
+    if ((st = stage(XP_STAGE_PREFILL, ctx->s_pre, [&] { return prefill(ctx->s_pre); }))) return st;
     XP_HIP_TRY(hipEventRecord(ctx->e_pre, ctx->s_pre));
     XP_HIP_TRY(hipStreamWaitEvent(s, ctx->e_dec, 0));
     XP_HIP_TRY(hipStreamWaitEvent(s, ctx->e_pre, 0));
@@ -635,14 +711,21 @@ xp_status LayerRun::post(hipStream_t s) const {
   const xp_layer_weights* w = &weights;
 
   // shared linear region (2): O projection + residual, RMSNorm, gate/up + SwiGLU, down + residual
-  if ((st = launch_gemm(dt, x_f32 ? XP_EPI_ADD_F32 : XP_EPI_ADD_T, ws + L.attn, w->w_o, nullptr, x, h1, M, H, HqD,
-                        gp, gpb, s)))
+  if ((st = stage(XP_STAGE_O, s, [&] {
+         return launch_gemm(dt, x_f32 ? XP_EPI_ADD_F32 : XP_EPI_ADD_T, ws + L.attn, w->w_o, nullptr, x, h1, M, H, HqD,
+                            gp, gpb, s);
+       })))
     return st;
-  if ((st = launch_rmsnorm(dt, h1, 1, w->g_ffn, ws + L.hn, M, H, shape.rms_eps, nullptr, s))) return st;
-  if ((st = launch_gemm(dt, XP_EPI_SWIGLU, ws + L.hn, w->w_gate, w->w_up, nullptr, ws + L.act, M, F, H, gp, gpb, s)))
+  if ((st = stage(XP_STAGE_NORM2, s,
+                  [&] { return launch_rmsnorm(dt, h1, 1, w->g_ffn, ws + L.hn, M, H, shape.rms_eps, nullptr, s); })))
     return st;
-  if ((st = launch_gemm(dt, XP_EPI_ADD_F32, ws + L.act, w->w_down, nullptr, h1, out, M, H, F, gp, gpb, s))) return st;
-  return XP_OK;
+  if ((st = stage(XP_STAGE_GATE_UP, s, [&] {
+         return launch_gemm(dt, XP_EPI_SWIGLU, ws + L.hn, w->w_gate, w->w_up, nullptr, ws + L.act, M, F, H, gp, gpb, s);
+       })))
+    return st;
+  return stage(XP_STAGE_DOWN, s, [&] {
+    return launch_gemm(dt, XP_EPI_ADD_F32, ws + L.act, w->w_down, nullptr, h1, out, M, H, F, gp, gpb, s);
+  });
 }
 
 xp_status run_layer(const LayerRun& run, hipStream_t s) {
@@ -793,6 +876,7 @@ xp_status xp_stack_graph_create(xp_ctx* ctx, const xp_layer_shape* sh, const xp_
   hipStream_t s = static_cast<hipStream_t>(stream);
   std::unique_ptr<xp_graph> g(new xp_graph);
   g->runs = stack_runs(ctx, sh, d, n_layers, w, kv, out, L, workspace);
+  for (LayerRun& r : g->runs) r.timed = false;
   for (int k = 0; k <= n_layers; ++k) {
     XP_HIP_TRY(hipStreamBeginCapture(s, hipStreamCaptureModeThreadLocal));
     st = k > 0 ? g->runs[k - 1].post(s) : XP_OK;

@@ -23,6 +23,13 @@ def test_library_exports_every_declared_symbol():
     assert "gfx950" in X.xp_build_info()
 
 
+def test_stage_names_follow_the_header():
+    # the binding's stage names are indexed by the header's XP_STAGE_* values
+    defs = dict((m, int(v)) for m, v in re.findall(r"^#define XP_STAGE_(\w+) (\d+)", open(HEADER).read(), re.M))
+    assert defs.pop("COUNT") == X.XP_STAGE_COUNT == len(X.STAGES)
+    assert {X.STAGES[v]: v for v in defs.values()} == {m.lower(): v for m, v in defs.items()}
+
+
 def test_waterfill_worked_example():
     import json
     g = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "waterfill_worked_example.json")))

@@ -121,6 +121,37 @@ def test_split_attention_modes_agree():
         assert rel_fro(p.float().cpu().numpy(), outs[0][1].float().cpu().numpy()) < 1e-3
 
 
+def test_stage_timing_counts_and_leaves_results_unchanged():
+    """xp_ctx_stage_timing: the first `capacity` runs of every stage are timed (on the
+    attention streams too in a partitioned context), later runs are not, and timing
+    changes no bit of the step's output."""
+    inst = make_instance(get_workload("P1"))
+    for mode in (0, 64):
+        c = X.Ctx(0, mode, 0)
+        try:
+            step, dev = make_step(inst, c)
+            ref = step.run().clone()
+            c.stage_timing(3)
+            for _ in range(4):
+                out = step.run()
+            torch.cuda.synchronize()
+            assert torch.equal(out, ref)
+            t = c.stage_times()
+            assert set(t) == set(X.STAGES)
+            for name, (n, ms) in t.items():
+                assert n == 3 and ms >= 0, (mode, name, n, ms)
+            for name in ("norm1", "qkv", "rope_append", "decode", "prefill", "o", "norm2", "gate_up", "down"):
+                assert t[name][1] > 0, (mode, name)
+            c.stage_timing(0)
+            step.run()
+            torch.cuda.synchronize()
+            assert all(n == 0 for n, _ in c.stage_times().values())
+            with pytest.raises(X.XpError):
+                c.stage_timing(-1)
+        finally:
+            c.close()
+
+
 def test_repeat_calls_are_deterministic_and_idempotent():
     inst = make_instance(get_workload("P3"))
     step, dev = make_step(inst, ctx(0))
