@@ -1,5 +1,27 @@
-"""Marshalling helpers shared by the tests (no layer arithmetic here)."""
+"""Marshalling helpers shared by the tests, and the teacher-forced check of the last stage."""
 import numpy as np
+
+# Teacher-forced last stage: out = h1 + act W_down^T from the GPU's own h1 and act.  The
+# kernel multiplies bf16 (or fp32) operands and accumulates in fp32, so its error against
+# the fp64 value is a few fp32 roundings of the partial sums.  The bar compares it with the
+# same arithmetic done by an independent fp32 accumulation (numpy's float32 product of the
+# same operands, another summation order): the kernel's worst row error may be at most
+# TF_FACTOR times the fp32 product's, with one fp32 rounding of the largest output as a
+# floor.  Accumulating in a narrower type, or dropping or repeating a term, fails it.
+TF_FACTOR = 4.0
+U32 = 2.0 ** -24
+
+
+def down_stage_errors(out, h1, act, wd):
+    """(the GPU's max-abs error, the fp32 product's max-abs error, the bar) of the last
+    stage on the given rows, all against fp64; `out`, `h1`, `act` are the rows' values as
+    the GPU holds them (act already rounded to its dtype), `wd` the stored down weight."""
+    out, h1, act, wd = (np.asarray(a, dtype=np.float64) for a in (out, h1, act, wd))
+    exact = h1 + act @ wd.T
+    f32 = h1.astype(np.float32) + act.astype(np.float32) @ wd.astype(np.float32).T
+    e_gpu = float(np.abs(out - exact).max())
+    e_f32 = float(np.abs(f32.astype(np.float64) - exact).max())
+    return e_gpu, e_f32, TF_FACTOR * max(e_f32, U32 * float(np.abs(exact).max()))
 
 
 def oracle_kwargs(inst, **extra):

@@ -19,8 +19,8 @@ the bf16-rounded RMSNorm output, and an exact emulation of just those two roundi
 gives up to 1.0e-2 per row (5.7e-3 pooled) on the 8B chunk's rows and up to 1.96e-2 per
 row (median 6.5e-3) on the 32B chunk's local rows, so the end-to-end bars are 1.5x the
 worst emulated floor: 1.5e-2 pooled and 3e-2 per row, with the figures recorded.  Layer output:
-rel-Frobenius <= 5e-3 and teacher-forced max-abs <= 2e-2 (the small-workload layer
-tests' bars).
+rel-Frobenius <= 5e-3 and the last stage within TF_FACTOR of an independent fp32 product
+(the small-workload layer tests' bars).
 """
 import json
 import os
@@ -33,7 +33,7 @@ from oracle import layer as L
 from oracle.numerics import to_f64
 from synth import get_workload, make_instance
 from synth.device import make_step, to_host_bits, upload
-from tests.helpers import DevicePages, oracle_kwargs, rel_fro, shared_ctx
+from tests.helpers import DevicePages, down_stage_errors, oracle_kwargs, rel_fro, shared_ctx
 
 pytestmark = pytest.mark.gpu
 
@@ -117,7 +117,8 @@ def _check_mode(inst, mode, step, out_t, peer_t, ref, tfref, rows3):
     r["tf_attn_row_median"] = {k: float(np.median(v)) for k, v in tf.items()}
     r["out"] = rel_fro(out[rows], ref["out"][rows])
     r["out_maxabs"] = float(np.abs(out[rows] - ref["out"][rows]).max())
-    r["tf_maxabs"] = float(np.abs(out[rows] - (h1[rows] + act[rows] @ to_f64(inst.weights["w_down"], dt).T)).max())
+    r["tf_maxabs"], r["tf_f32_maxabs"], tf_bar = down_stage_errors(out[rows], h1[rows], act[rows],
+                                                                   to_f64(inst.weights["w_down"], dt))
     r["row_max"] = {k: float(v.max()) for k, v in e2e.items()}
     r["row_median"] = {k: float(np.median(v)) for k, v in e2e.items()}
     print(f"[full] {wl.name} mode {mode}: {json.dumps(r)}", flush=True)
@@ -130,7 +131,7 @@ def _check_mode(inst, mode, step, out_t, peer_t, ref, tfref, rows3):
             assert r[k] < 1.5e-2, (mode, k, r[k])
     for k, v in e2e.items():
         assert v.max() < 3e-2, (mode, k, int(np.argmax(v)), float(v.max()))
-    assert r["tf_maxabs"] < 2e-2, r
+    assert r["tf_maxabs"] <= tf_bar, r
     assert r["out"] < 5e-3, r
 
 

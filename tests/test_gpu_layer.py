@@ -1,9 +1,10 @@
 """Layer-step parity of the HIP path against the fp64 oracle, through the C ABI.
 
 Bars: attention rows and exported peer buffers rel-Frobenius <= 5e-3; bf16 layer outputs
-(fp32 residual stream) rel-Frobenius <= 5e-3 end to end, and max-abs <= 2e-2 teacher-forced
-on the last stage (out = h1 + act W_down^T recomputed in fp64 from the GPU's own h1 and act);
-fp32 layer outputs max-abs <= 2e-2 end to end.  Pages no append touches stay bit-identical.
+(fp32 residual stream) rel-Frobenius <= 5e-3 end to end, and on the last stage (out =
+h1 + act W_down^T from the GPU's own h1 and act) a max-abs error at most TF_FACTOR times that
+of an independent fp32 product of the same operands (tests.helpers.down_stage_errors); fp32
+layer outputs max-abs <= 2e-2 end to end.  Pages no append touches stay bit-identical.
 """
 import json
 import os
@@ -17,7 +18,7 @@ from oracle import layer as L
 from oracle.numerics import to_f64
 from synth import get_workload, make_instance
 from synth.device import make_step, to_host_bits, upload
-from tests.helpers import oracle_kwargs, rel_fro, shared_ctx, k_slots
+from tests.helpers import down_stage_errors, oracle_kwargs, rel_fro, shared_ctx, k_slots
 
 pytestmark = pytest.mark.gpu
 
@@ -54,11 +55,10 @@ def check_layer(inst, step, ref, rows=None):
     r = dict(attn=rel_fro(attn[rows], ref["attn"][rows]), out=rel_fro(out[rows], ref["out"][rows]),
              out_maxabs=float(np.abs(out[rows] - ref["out"][rows]).max()))
     # teacher-forced last stage
-    wd = to_f64(inst.weights["w_down"], dt)
-    tf = h1[rows] + act[rows] @ wd.T
-    r["tf_maxabs"] = float(np.abs(out[rows] - tf).max())
+    r["tf_maxabs"], r["tf_f32_maxabs"], tf_bar = down_stage_errors(out[rows], h1[rows], act[rows],
+                                                                   to_f64(inst.weights["w_down"], dt))
     assert r["attn"] < 5e-3, r
-    assert r["tf_maxabs"] < 2e-2, r
+    assert r["tf_maxabs"] <= tf_bar, r
     if dt == "f32":
         assert r["out_maxabs"] < 2e-2, r
     else:
