@@ -87,10 +87,15 @@ def test_chunked_layer_matches_oracle(name):
 
 
 def test_chunked_step_equals_single_chunk_steps():
+    """Each chunk's rows, and the decode rows, equal their own steps bit for bit; and the
+    single-chunk steps (RoPE and appends in the QKV GEMM's epilogue) rewrite every page of
+    the pool with the bits the multi-chunk step (the stand-alone RoPE/append kernel) wrote."""
     inst = make_multi_instance(MULTI_CHUNK_WORKLOADS["M1"])
     wl = inst.wl
     step = make_chunked_step(inst, ctx(0))
     full = step.run().clone()
+    torch.cuda.synchronize()
+    pool0 = step.pool.clone().view(torch.uint8)          # bits (unused slots hold NaN)
     starts = np.cumsum([0] + [l for l, _ in wl.chunks])
     x = step.x
     for j, (l, c) in enumerate(wl.chunks):
@@ -110,6 +115,7 @@ def test_chunked_step_equals_single_chunk_steps():
     got = dec.run().clone()
     torch.cuda.synchronize()
     assert torch.equal(full[starts[-1]:], got)
+    assert torch.equal(step.pool.view(torch.uint8), pool0)
 
 
 def test_chunked_split_attention_modes_agree():
