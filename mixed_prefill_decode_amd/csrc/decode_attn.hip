@@ -233,8 +233,10 @@ __device__ __forceinline__ void decode_unit(const void* __restrict__ q, const ch
           for (int n = 0; n < D / 16; ++n) zero_tail(cur.v[n], n_keys - k0);
         }
         float mb = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
-        mb = fmaxf(mb, shfl_xor(mb, 16));
-        mb = fmaxf(mb, shfl_xor(mb, 32)) * scale_log2;   // finite: every visited page holds a key
+        float x0, x1;
+        halves_xor16(mb, x0, x1);                         // register lane swaps, not the LDS queue
+        halves_xor32(fmaxf(x0, x1), x0, x1);
+        mb = fmaxf(x0, x1) * scale_log2;                  // finite: every visited page holds a key
         // Lazily moved softmax reference (exp2 domain): O and l are rescaled only when
         // some head's maximum exceeds the reference by more than kLazy, so the
         // weights stay below 2^kLazy; the result is the same function of the scores.

@@ -370,7 +370,9 @@ __device__ __forceinline__ void prefill_tile(const PrefillArgs& a, int bx, int b
         float mb = fmaxf(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])), fmaxf(fmaxf(sv[4], sv[5]), fmaxf(sv[6], sv[7])));
         mb = fmaxf(mb, fmaxf(fmaxf(fmaxf(sv[8], sv[9]), fmaxf(sv[10], sv[11])),
                              fmaxf(fmaxf(sv[12], sv[13]), fmaxf(sv[14], sv[15]))));
-        mb = fmaxf(mb, shfl_xor(mb, 32)) * a.scale_log2;
+        float m0, m1;
+        halves_xor32(mb, m0, m1);
+        mb = fmaxf(m0, m1) * a.scale_log2;
         if (__builtin_amdgcn_ballot_w64(mb > ms[j] + kLazy) != 0) {
           const float mn = fmaxf(ms[j], mb);
           const float alpha = ms[j] == -__builtin_inff() ? 0.f : fast_exp2(ms[j] - mn);

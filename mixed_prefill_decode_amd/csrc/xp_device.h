@@ -202,6 +202,22 @@ __device__ __forceinline__ void mma16x16_k16(f32x4& acc, const Frag4<float>& a, 
 // ---- wave-level helpers ------------------------------------------------------
 __device__ __forceinline__ float shfl_xor(float v, int m) { return __shfl_xor(v, m, 64); }
 
+// v of this lane and of lane l ^ 32, through gfx950's register lane swap between the two
+// halves of the wave.  Unlike a bpermute it does not go through the LDS queue, so it does
+// not wait behind the LDS reads in flight.  Each lane gets its own value in one of the
+// two results and its partner's in the other.
+__device__ __forceinline__ void halves_xor32(float v, float& a, float& b) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  a = __uint_as_float(r[0]);
+  b = __uint_as_float(r[1]);
+}
+// the same for lanes l and l ^ 16 (the swap between neighbouring 16-lane rows)
+__device__ __forceinline__ void halves_xor16(float v, float& a, float& b) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  a = __uint_as_float(r[0]);
+  b = __uint_as_float(r[1]);
+}
+
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 }  // namespace xp
