@@ -608,41 +608,26 @@ def kernel_figures(name, seconds, work, unit) -> dict:
 
 def window_times(X, torch, inst, step, dev, ctx, repeats) -> dict:
     """Decode and prefill attention inside the split region of a CU-partitioned (or
-    unmasked) context: both launched between a fork and a join as the layer step
-    launches them, each timed with events on its own stream (the figures the pages'
+    unmasked) context, from the layer step itself: the library's stage events time each
+    of the two on its own stream while the other one runs (the figures the pages'
     overlap rule is about: decode's bandwidth and prefill's MFMA rate while the other
-    one runs)."""
-    k = ctx.decode_cus
-    calls = kernel_calls(X, torch, inst, step, dev, plan_cus=ctx.cu_masks()[2] - k if k > 0 else 0)
-    dec, dbytes, _ = calls["decode_attn"]
-    pre, pflops, _ = calls["prefill_attn"]
-    s_dec, s_pre = ctx.streams()
-    ts_dec, ts_pre = torch.cuda.ExternalStream(s_dec), torch.cuda.ExternalStream(s_pre)
-    main = torch.cuda.current_stream()
-    E = lambda: torch.cuda.Event(enable_timing=True)
-    rec = []
-    for it in range(2 * repeats):
-        fork, d0, d1, p0, p1, join = E(), E(), E(), E(), E(), E()
-        fork.record(main)
-        ts_dec.wait_event(fork)
-        ts_pre.wait_event(fork)
-        d0.record(ts_dec)
-        dec(s_dec)
-        d1.record(ts_dec)
-        p0.record(ts_pre)
-        pre(s_pre)
-        p1.record(ts_pre)
-        main.wait_stream(ts_dec)
-        main.wait_stream(ts_pre)
-        join.record(main)
-        if it >= repeats:
-            rec.append((fork, d0, d1, p0, p1, join))
+    runs).  Both start at the step's fork, so the region lasts as long as the longer."""
+    wl = inst.wl
+    calls = kernel_calls(X, torch, inst, step, dev)
+    _, dbytes, _ = calls["decode_attn"]
+    _, pflops, _ = calls["prefill_attn"]
+    for _ in range(repeats):
+        step.run()
     torch.cuda.synchronize()
-    n = len(rec)
-    td = sum(a[1].elapsed_time(a[2]) for a in rec) / n * 1e-3
-    tp = sum(a[3].elapsed_time(a[4]) for a in rec) / n * 1e-3
-    tw = sum(a[0].elapsed_time(a[5]) for a in rec) / n * 1e-3
-    return {"window_us": round(tw * 1e6, 1), "decode_us": round(td * 1e6, 1),
+    ctx.stage_timing(repeats)
+    for _ in range(repeats):
+        step.run()
+    torch.cuda.synchronize()
+    st = ctx.stage_times()
+    ctx.stage_timing(0)
+    td = st["decode"][1] / max(st["decode"][0], 1) * 1e-3
+    tp = st["prefill"][1] / max(st["prefill"][0], 1) * 1e-3
+    return {"window_us": round(max(td, tp) * 1e6, 1), "decode_us": round(td * 1e6, 1),
             "decode_GBs": round(dbytes / td / 1e9, 1), "decode_hbm_frac": round(dbytes / td / 1e9 / PEAK_HBM_GBS, 4),
             "prefill_us": round(tp * 1e6, 1), "prefill_TFLOPs": round(pflops / tp / 1e12, 1),
             "prefill_mfma_frac": round(pflops / tp / 1e12 / PEAK_BF16_TFLOPS, 4)}

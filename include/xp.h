@@ -188,7 +188,11 @@ typedef struct xp_ctx xp_ctx;
  * for the split attention region ([CS] §6.1 "coordinated attention overlap").
  * decode_cus:
  *   XP_SPLIT_SERIALIZED (0) -> decode then prefill attention on the caller's stream;
- *   XP_SPLIT_UNMASKED (-1)  -> concurrent on two unmasked streams;
+ *   XP_SPLIT_UNMASKED (-1)  -> concurrent on two unmasked streams, sharing every CU:
+ *         in bf16 both kernels take co-resident forms (decode in four-wave
+ *         workgroups that reserve LDS so a CU holds at most one of them, both
+ *         kernels within 168 registers per wave), so each CU runs one prefill
+ *         workgroup and four decode waves at once; same results, bit for bit;
  *   k in [1, nCU-1] -> concurrent on CU-masked streams, k CUs for decode and
  *         the rest for prefill ([CS] §6.1: decode gets the fewest CUs that keep
  *         90% of its standalone HBM bandwidth: xp_calibrate_decode_cus gives that k

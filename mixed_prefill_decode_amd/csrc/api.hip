@@ -655,11 +655,17 @@ xp_status LayerRun::attend(hipStream_t s, bool split) const {
   char* attn = ws + L.attn;
   const size_t attn_row = size_t(Hq) * D * eb;
 
+  // Concurrent on unmasked streams, the two kernels share every CU: in bf16 both take
+  // their co-resident forms, whose register and LDS budgets leave each CU room for one
+  // prefill workgroup and four decode waves at once (same arithmetic, same bits; the
+  // fp32 kernels do not fit those budgets).
+  const bool concurrent = split && ctx->s_dec && n_d > 0 && !ch.empty();
+  const bool cores = concurrent && ctx->decode_cus == XP_SPLIT_UNMASKED && dt == XP_BF16;
   auto decode = [&](hipStream_t q) {
     return launch_decode(dt, ws + L.q_dec, kv->pool, kv->n_pages, sh->page_size, d->dec_pages, d->dec_max_blocks,
                          d->dec_ctx, n_d, Hq, Hkv, D, attn + size_t(rows_pre) * attn_row, Hq * D,
                          reinterpret_cast<float*>(ws + L.dec_ml), reinterpret_cast<float*>(ws + L.dec_o), L.dec_pages_per_split,
-                         status, q);
+                         status, q, cores);
   };
   auto prefill = [&](hipStream_t q) {
     if (ch.size() == 1) {
@@ -667,7 +673,7 @@ xp_status LayerRun::attend(hipStream_t s, bool split) const {
       return launch_prefill(dt, ws + L.q_pre + c.q_off, kv->pool, kv->n_pages, sh->page_size, c.pages, c.max_blocks,
                             hq_loc, hkv_loc, D, c.prior, c.len, c.off, c.n_local,
                             attn + size_t(c.row0) * attn_row + size_t(r) * hq_loc * D * eb, Hq * D, c.peer_attn_out,
-                            hq_loc * D, ws + L.pre_part, status, prefill_cus(ctx), q);
+                            hq_loc * D, ws + L.pre_part, status, prefill_cus(ctx), q, cores);
     }
     // several chunks: one grouped launch, each chunk with its own partials
     std::vector<PrefillJob> jobs;
@@ -679,9 +685,8 @@ xp_status LayerRun::attend(hipStream_t s, bool split) const {
       part += align_up(prefill_ws_bytes(hq_loc, hkv_loc, D, c.prior, c.len, prefill_cus(ctx)), 256);
     }
     return launch_prefill_group(dt, kv->pool, kv->n_pages, sh->page_size, hq_loc, hkv_loc, D, int(jobs.size()),
-                                jobs.data(), status, prefill_cus(ctx), q);
+                                jobs.data(), status, prefill_cus(ctx), q, cores);
   };
-  const bool concurrent = split && ctx->s_dec && n_d > 0 && !ch.empty();
   if (!concurrent) {
     if ((st = stage(XP_STAGE_DECODE, s, [&] { return decode(s); }))) return st;
     if ((st = stage(XP_STAGE_PREFILL, s, [&] { return prefill(s); }))) return st;

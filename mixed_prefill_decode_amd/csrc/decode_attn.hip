@@ -157,7 +157,7 @@ __device__ __forceinline__ void decode_unit(const void* __restrict__ q, const ch
   constexpr int EB = St<T>::bytes;
   constexpr int PAGE_BYTES = 2 * kPage * D * EB;
   constexpr int NB = DEPTH + 1;
-  const int lane = threadIdx.x;
+  const int lane = threadIdx.x & 63;
   const int G = Hq / Hkv;
   const int b0 = s * pps;
   // the table slice is read before anything that depends on the context length
@@ -283,15 +283,17 @@ __device__ __forceinline__ void decode_unit(const void* __restrict__ q, const ch
 // units w, w + W, w + 2W, ... of the W workgroups launched.  Short requests then
 // cost nothing and the splits of long ones spread over the whole grid; the
 // partials keep their (i, h, s) layout for the combine.
+// A workgroup holds one wave (its own unit list position) or, in the co-resident form,
+// four independent waves: wave w of workgroup b then takes list position 4 b + w.
 template <typename T, int D, int DEPTH, bool PTR>
-__global__ __launch_bounds__(64) void decode_split_kernel(const void* __restrict__ q, const char* __restrict__ pool,
-                                                          int n_pages, const int32_t* __restrict__ dec_pages,
-                                                          int max_blocks, const int32_t* __restrict__ dec_ctx, int n_d,
-                                                          int Hq, int Hkv, int pps, int n_splits,
-                                                          float* __restrict__ part_ml, float* __restrict__ part_o,
-                                                          float scale_log2, uint32_t* __restrict__ status) {
-  const int W = int(gridDim.x);
-  int u = int(blockIdx.x);
+__device__ __forceinline__ void decode_units(const void* __restrict__ q, const char* __restrict__ pool, int n_pages,
+                                             const int32_t* __restrict__ dec_pages, int max_blocks,
+                                             const int32_t* __restrict__ dec_ctx, int n_d, int Hq, int Hkv, int pps,
+                                             int n_splits, float* __restrict__ part_ml, float* __restrict__ part_o,
+                                             float scale_log2, uint32_t* __restrict__ status) {
+  const int wpb = int(blockDim.x) >> 6;
+  const int W = int(gridDim.x) * wpb;
+  int u = int(blockIdx.x) * wpb + __builtin_amdgcn_readfirstlane(int(threadIdx.x) >> 6);
   int base = 0;
   for (int i = 0; i < n_d; ++i) {
     const int nb_need = (dec_ctx[i] + kPage) / kPage;               // pages of ctx + 1 keys
@@ -304,6 +306,34 @@ __global__ __launch_bounds__(64) void decode_split_kernel(const void* __restrict
     }
     base += cnt;
   }
+}
+
+template <typename T, int D, int DEPTH, bool PTR>
+__global__ __launch_bounds__(64) void decode_split_kernel(const void* __restrict__ q, const char* __restrict__ pool,
+                                                          int n_pages, const int32_t* __restrict__ dec_pages,
+                                                          int max_blocks, const int32_t* __restrict__ dec_ctx, int n_d,
+                                                          int Hq, int Hkv, int pps, int n_splits,
+                                                          float* __restrict__ part_ml, float* __restrict__ part_o,
+                                                          float scale_log2, uint32_t* __restrict__ status) {
+  decode_units<T, D, DEPTH, PTR>(q, pool, n_pages, dec_pages, max_blocks, dec_ctx, n_d, Hq, Hkv, pps, n_splits,
+                                 part_ml, part_o, scale_log2, status);
+}
+
+// The co-resident form, for decode running beside prefill attention on the same CUs:
+// four-wave workgroups of at most 168 registers per wave (three waves per SIMD), each
+// launched with kCoresLds bytes of LDS it does not use, so that a CU holds at most one
+// of them (four decode waves, one per SIMD) next to one prefill workgroup (two waves
+// per SIMD of at most 168 registers, 68 KB of LDS).  The units and their arithmetic are
+// those of decode_split_kernel: the results are the same bits.
+constexpr int kCoresWaves = 4;
+constexpr size_t kCoresLds = 84 * 1024;
+template <typename T, int D, int DEPTH, bool PTR>
+__global__ __launch_bounds__(64 * kCoresWaves) __attribute__((amdgpu_waves_per_eu(3))) void decode_split_cores_kernel(
+    const void* __restrict__ q, const char* __restrict__ pool, int n_pages, const int32_t* __restrict__ dec_pages,
+    int max_blocks, const int32_t* __restrict__ dec_ctx, int n_d, int Hq, int Hkv, int pps, int n_splits,
+    float* __restrict__ part_ml, float* __restrict__ part_o, float scale_log2, uint32_t* __restrict__ status) {
+  decode_units<T, D, DEPTH, PTR>(q, pool, n_pages, dec_pages, max_blocks, dec_ctx, n_d, Hq, Hkv, pps, n_splits,
+                                 part_ml, part_o, scale_log2, status);
 }
 
 // out[i, h*D + j] = sum_s 2^(m_s - m*) o_s[j] / sum_s 2^(m_s - m*) l_s
@@ -378,12 +408,18 @@ __global__ __launch_bounds__(kCombineThreads) void decode_combine_kernel(const f
 template <typename T, int D>
 xp_status launch_dec_t(const void* q, const void* pool, int n_pages, const int32_t* dec_pages, int max_blocks,
                        const int32_t* dec_ctx, int n_d, int Hq, int Hkv, void* out, int out_stride, float* part_ml,
-                       float* part_o, int pps, uint32_t* status, hipStream_t s) {
+                       float* part_o, int pps, uint32_t* status, bool cores, hipStream_t s) {
   const int n_splits = decode_splits(max_blocks, pps);
   const float scale_log2 = float(1.4426950408889634 / __builtin_sqrt(double(D)));
-  hipLaunchKernelGGL((decode_split_kernel<T, D, kDepth, kPtrLoads>), dim3(decode_grid(n_d, Hkv, n_splits)), dim3(64), 0,
-                     s, q, static_cast<const char*>(pool), n_pages, dec_pages, max_blocks, dec_ctx, n_d, Hq, Hkv, pps,
-                     n_splits, part_ml, part_o, scale_log2, status);
+  const int waves = decode_grid(n_d, Hkv, n_splits);
+  if (cores)
+    hipLaunchKernelGGL((decode_split_cores_kernel<T, D, kDepth, kPtrLoads>), dim3(cdiv(waves, kCoresWaves)),
+                       dim3(64 * kCoresWaves), kCoresLds, s, q, static_cast<const char*>(pool), n_pages, dec_pages,
+                       max_blocks, dec_ctx, n_d, Hq, Hkv, pps, n_splits, part_ml, part_o, scale_log2, status);
+  else
+    hipLaunchKernelGGL((decode_split_kernel<T, D, kDepth, kPtrLoads>), dim3(waves), dim3(64), 0, s, q,
+                       static_cast<const char*>(pool), n_pages, dec_pages, max_blocks, dec_ctx, n_d, Hq, Hkv, pps,
+                       n_splits, part_ml, part_o, scale_log2, status);
   XP_CHECK_LAUNCH();
   hipLaunchKernelGGL((decode_combine_kernel<T, D>), dim3(Hq, n_d), dim3(kCombineThreads), 0, s, part_ml, part_o, dec_ctx, Hq, pps,
                      n_splits, out, out_stride);
@@ -427,18 +463,19 @@ size_t decode_ws_bytes(int n_d, int Hq, int d, int n_splits) {
 
 xp_status launch_decode(int dtype, const void* q, const void* pool, int n_pages, int S, const int32_t* dec_pages,
                         int dec_max_blocks, const int32_t* dec_ctx, int n_d, int Hq, int Hkv, int d, void* out,
-                        int out_stride, float* part_ml, float* part_o, int pps, uint32_t* status, hipStream_t s) {
+                        int out_stride, float* part_ml, float* part_o, int pps, uint32_t* status, hipStream_t s,
+                        bool cores) {
   if (n_d == 0) return XP_OK;
   if (S != kPage) return fail(XP_EUNSUPPORTED, "decode attention: page_size %d (supported: 16)", S);
   if (Hkv <= 0 || Hq % Hkv || Hq / Hkv > 16) return fail(XP_EUNSUPPORTED, "decode attention: Hq=%d Hkv=%d", Hq, Hkv);
   if (pps < 1 || pps > 64) return fail(XP_EINVAL, "decode attention: pages_per_split %d (1..64)", pps);
   if (dec_max_blocks < 1) return fail(XP_ESHAPE, "decode attention: dec_max_blocks %d", dec_max_blocks);
   if (dtype == XP_BF16) {
-    if (d == 128) return launch_dec_t<bf16_t, 128>(q, pool, n_pages, dec_pages, dec_max_blocks, dec_ctx, n_d, Hq, Hkv, out, out_stride, part_ml, part_o, pps, status, s);
-    if (d == 64) return launch_dec_t<bf16_t, 64>(q, pool, n_pages, dec_pages, dec_max_blocks, dec_ctx, n_d, Hq, Hkv, out, out_stride, part_ml, part_o, pps, status, s);
+    if (d == 128) return launch_dec_t<bf16_t, 128>(q, pool, n_pages, dec_pages, dec_max_blocks, dec_ctx, n_d, Hq, Hkv, out, out_stride, part_ml, part_o, pps, status, cores, s);
+    if (d == 64) return launch_dec_t<bf16_t, 64>(q, pool, n_pages, dec_pages, dec_max_blocks, dec_ctx, n_d, Hq, Hkv, out, out_stride, part_ml, part_o, pps, status, cores, s);
   } else if (dtype == XP_F32) {
-    if (d == 128) return launch_dec_t<float, 128>(q, pool, n_pages, dec_pages, dec_max_blocks, dec_ctx, n_d, Hq, Hkv, out, out_stride, part_ml, part_o, pps, status, s);
-    if (d == 64) return launch_dec_t<float, 64>(q, pool, n_pages, dec_pages, dec_max_blocks, dec_ctx, n_d, Hq, Hkv, out, out_stride, part_ml, part_o, pps, status, s);
+    if (d == 128) return launch_dec_t<float, 128>(q, pool, n_pages, dec_pages, dec_max_blocks, dec_ctx, n_d, Hq, Hkv, out, out_stride, part_ml, part_o, pps, status, cores, s);
+    if (d == 64) return launch_dec_t<float, 64>(q, pool, n_pages, dec_pages, dec_max_blocks, dec_ctx, n_d, Hq, Hkv, out, out_stride, part_ml, part_o, pps, status, cores, s);
   }
   return fail(XP_EUNSUPPORTED, "decode attention: dtype %d head_dim %d", dtype, d);
 }

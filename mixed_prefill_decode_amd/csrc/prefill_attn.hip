@@ -536,6 +536,15 @@ __global__ __launch_bounds__(64 * MAXW * KS) void prefill_kernel(PrefillArgs a) 
   prefill_tile<T, D, NQ, MAXW, KS>(a, int(blockIdx.x), int(blockIdx.y));
 }
 
+// The co-resident form, for prefill running beside decode attention on the same CUs:
+// the same tiles within 168 registers per wave, so that a SIMD holds two prefill waves
+// and one of decode's co-resident waves.
+template <typename T, int D, int NQ, int MAXW, int KS>
+__global__ __launch_bounds__(64 * MAXW * KS) __attribute__((amdgpu_waves_per_eu(3))) void prefill_cores_kernel(
+    PrefillArgs a) {
+  prefill_tile<T, D, NQ, MAXW, KS>(a, int(blockIdx.x), int(blockIdx.y));
+}
+
 template <typename T, int D>
 __global__ __launch_bounds__(256) void prefill_combine_kernel(PrefillArgs a) {
   prefill_combine_tile<T, D>(a, int(blockIdx.x), int(blockIdx.y));
@@ -574,6 +583,15 @@ __device__ __forceinline__ void group_member(const PrefillGroup& g, int b, bool 
 
 template <typename T, int D, int NQ, int MAXW, int KS>
 __global__ __launch_bounds__(64 * MAXW * KS) void prefill_group_kernel(PrefillGroup g) {
+  PrefillArgs a;
+  int x, y;
+  group_member(g, int(blockIdx.x), false, a, x, y);
+  prefill_tile<T, D, NQ, MAXW, KS>(a, x, y);
+}
+
+template <typename T, int D, int NQ, int MAXW, int KS>
+__global__ __launch_bounds__(64 * MAXW * KS) __attribute__((amdgpu_waves_per_eu(3))) void prefill_group_cores_kernel(
+    PrefillGroup g) {
   PrefillArgs a;
   int x, y;
   group_member(g, int(blockIdx.x), false, a, x, y);
@@ -716,10 +734,14 @@ xp_status prepare(const void* pool, int n_pages, int S, int hq, int hkv, int d, 
   return XP_OK;
 }
 
+// `cores`: decode runs beside this launch on the same CUs (its co-resident form), so
+// the tiles take the co-resident kernel and one key set
 template <typename T, int D>
-void launch_one(const Prepared& pr, hipStream_t s) {
+void launch_one(const Prepared& pr, bool cores, hipStream_t s) {
   const dim3 grid(pr.n_qt * pr.p.n_split, pr.gy), block(64 * pr.p.wpg), cgrid(pr.n_qt, pr.a.hq);
-  if (two_key_sets(pr, long(grid.x) * grid.y))
+  if (cores)
+    hipLaunchKernelGGL((prefill_cores_kernel<T, D, kNQ, kMaxW, 1>), grid, block, 0, s, pr.a);
+  else if (two_key_sets(pr, long(grid.x) * grid.y))
     hipLaunchKernelGGL((prefill_kernel<T, D, kNQ, 4, 2>), grid, dim3(2 * block.x), 0, s, pr.a);
   else
     hipLaunchKernelGGL((prefill_kernel<T, D, kNQ, kMaxW, 1>), grid, block, 0, s, pr.a);
@@ -727,7 +749,7 @@ void launch_one(const Prepared& pr, hipStream_t s) {
 }
 
 template <typename T, int D>
-void launch_group(const Prepared* pr, int n, hipStream_t s) {
+void launch_group(const Prepared* pr, int n, bool cores, hipStream_t s) {
   PrefillGroup g{};
   g.n = n;
   bool split = false;
@@ -740,7 +762,10 @@ void launch_group(const Prepared* pr, int n, hipStream_t s) {
     g.cgx[k] = pr[k].n_qt;
     g.cstart[k + 1] = g.cstart[k] + (sk ? pr[k].n_qt * pr[k].a.hq : 0);
   }
-  if (two_key_sets(pr[0], g.start[n]))
+  if (cores)
+    hipLaunchKernelGGL((prefill_group_cores_kernel<T, D, kNQ, kMaxW, 1>), dim3(g.start[n]), dim3(64 * pr[0].p.wpg),
+                       0, s, g);
+  else if (two_key_sets(pr[0], g.start[n]))
     hipLaunchKernelGGL((prefill_group_kernel<T, D, kNQ, 4, 2>), dim3(g.start[n]), dim3(128 * pr[0].p.wpg), 0,
                        s, g);
   else
@@ -769,18 +794,18 @@ xp_status dispatch(int dtype, int d, F&& f) {
 xp_status launch_prefill(int dtype, const void* q, const void* pool, int n_pages, int S, const int32_t* pre_pages,
                          int pre_max_blocks, int hq, int hkv, int d, int prior, int chunk, int off, int n_local,
                          void* out_local, int out_local_stride, void* out_peer, int out_peer_stride, void* ws,
-                         uint32_t* status, int cus, hipStream_t s) {
+                         uint32_t* status, int cus, hipStream_t s, bool cores) {
   if (chunk == 0) return XP_OK;
   const PrefillJob j{q, pre_pages, pre_max_blocks, prior, chunk, off, n_local, out_local, out_local_stride, out_peer,
                      out_peer_stride, ws};
   Prepared pr;
   xp_status st = prepare(pool, n_pages, S, hq, hkv, d, j, status, cus, pr);
   if (st) return st;
-  return dispatch(dtype, d, [&](auto t, auto dd) { launch_one<decltype(t), decltype(dd)::value>(pr, s); });
+  return dispatch(dtype, d, [&](auto t, auto dd) { launch_one<decltype(t), decltype(dd)::value>(pr, cores, s); });
 }
 
 xp_status launch_prefill_group(int dtype, const void* pool, int n_pages, int S, int hq, int hkv, int d, int n,
-                               const PrefillJob* jobs, uint32_t* status, int cus, hipStream_t s) {
+                               const PrefillJob* jobs, uint32_t* status, int cus, hipStream_t s, bool cores) {
   std::vector<Prepared> pr;
   for (int k = 0; k < n; ++k) {
     if (jobs[k].chunk == 0) continue;
@@ -795,9 +820,11 @@ xp_status launch_prefill_group(int dtype, const void* pool, int n_pages, int S, 
   });
   for (size_t k0 = 0; k0 < pr.size(); k0 += kMaxGroup) {
     const int m = int(std::min<size_t>(kMaxGroup, pr.size() - k0));
-    xp_status st = m == 1 ? dispatch(dtype, d, [&](auto t, auto dd) { launch_one<decltype(t), decltype(dd)::value>(pr[k0], s); })
+    xp_status st = m == 1 ? dispatch(dtype, d, [&](auto t, auto dd) {
+                              launch_one<decltype(t), decltype(dd)::value>(pr[k0], cores, s);
+                            })
                           : dispatch(dtype, d, [&](auto t, auto dd) {
-                              launch_group<decltype(t), decltype(dd)::value>(pr.data() + k0, m, s);
+                              launch_group<decltype(t), decltype(dd)::value>(pr.data() + k0, m, cores, s);
                             });
     if (st) return st;
   }

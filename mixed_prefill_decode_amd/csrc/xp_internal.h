@@ -96,10 +96,12 @@ int decode_splits(int dec_max_blocks, int pages_per_split);
 int decode_grid(int n_d, int Hkv, int n_splits);
 int decode_pick_pps(int requested, int n_d, int Hkv, int dec_max_blocks);
 size_t decode_ws_bytes(int n_d, int Hq, int d, int n_splits);
+// `cores`: the co-resident form (four-wave workgroups that leave each CU room for one
+// prefill workgroup beside them), for decode running concurrently with prefill attention
 xp_status launch_decode(int dtype, const void* q, const void* pool, int n_pages, int S,
                         const int32_t* dec_pages, int dec_max_blocks, const int32_t* dec_ctx, int n_d,
                         int Hq, int Hkv, int d, void* out, int out_stride, float* part_ml,
-                        float* part_o, int pages_per_split, uint32_t* status, hipStream_t s);
+                        float* part_o, int pages_per_split, uint32_t* status, hipStream_t s, bool cores = false);
 
 size_t prefill_ws_bytes(int hq, int hkv, int d, int prior, int chunk, int cus);
 // one chunk of a grouped prefill launch; ws holds its own partials (prefill_ws_bytes)
@@ -115,12 +117,15 @@ struct PrefillJob {
   void* ws;
 };
 // Every job's prefill attention, up to eight chunks per launch, longest key range first.
+// `cores`: the co-resident form (within 168 registers per wave, one key set), for prefill
+// running concurrently with decode's co-resident form on the same CUs.
 xp_status launch_prefill_group(int dtype, const void* pool, int n_pages, int S, int hq, int hkv, int d, int n,
-                               const PrefillJob* jobs, uint32_t* status, int cus, hipStream_t s);
+                               const PrefillJob* jobs, uint32_t* status, int cus, hipStream_t s,
+                               bool cores = false);
 xp_status launch_prefill(int dtype, const void* q, const void* pool, int n_pages, int S,
                          const int32_t* pre_pages, int pre_max_blocks, int hq, int hkv, int d,
                          int prior, int chunk, int off, int n_local, void* out_local,
                          int out_local_stride, void* out_peer, int out_peer_stride, void* ws,
-                         uint32_t* status, int cus, hipStream_t s);
+                         uint32_t* status, int cus, hipStream_t s, bool cores = false);
 
 }  // namespace xp

@@ -1,7 +1,8 @@
 """GPU parity at the measured workloads' full sizes (C2, C3, C4, C5 and the whole-prompt
 readings C3-full, C5-full), in the launch configurations bench.py times: the layer step
-serialized and with the split attention on a 128-CU decode partition (bit-identical to
-each other), checked against the oracle on rows the oracle computes one by one.
+serialized, with the split attention on a 128-CU decode partition, and with both attention
+kernels concurrent on every CU in their co-resident forms (decode rows bit-identical across
+the three), checked against the oracle on rows the oracle computes one by one.
 
 Rows checked: every decode row (C4: 32 of its 128 requests, spread over the batch);
 at least 64 local prefill rows and 64 exported peer rows at the chunk's ends, at page
@@ -144,7 +145,7 @@ def test_full_size_layer_on_sampled_rows(name):
     pre_rows, dec_rows, peer_rows = _sample(wl)
     rows = pre_rows + dec_rows
     outs = {}
-    for mode in (0, 128):
+    for mode in (0, 128, -1):
         step, _ = make_step(inst, ctx(mode), dev)
         print(f"[full] {name}: layer step, decode_cus {mode}", flush=True)
         step.run()
@@ -155,6 +156,7 @@ def test_full_size_layer_on_sampled_rows(name):
     # decode splits fixed by the batch)
     n_pl = wl.n_prefill_local
     assert torch.equal(outs[0][1][n_pl:], outs[128][1][n_pl:])
+    assert torch.equal(outs[0][1][n_pl:], outs[-1][1][n_pl:])
     print(f"[full] {name}: oracle on {len(pre_rows)} prefill, {len(dec_rows)} decode and "
           f"{len(peer_rows or [])} peer rows", flush=True)
     ref = L.layer_forward(**oracle_kwargs(inst, rows=rows, peer_rows=peer_rows))
