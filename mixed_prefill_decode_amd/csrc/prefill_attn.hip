@@ -53,6 +53,7 @@ constexpr int kStages = 2;           // LDS ring stages, one key set
 constexpr int kStagesKS2 = 3;        // LDS ring stages, two key sets
 constexpr int kBlocksPerStage = 2;   // 32-key blocks per stage
 constexpr int kMaxBps = 256;   // key blocks per split (its page ids are staged in LDS)
+constexpr int kXcds = 8;       // XCDs the hardware deals consecutive workgroups to, in turn
 
 __device__ __forceinline__ int kappa(int i) { return (i & ~12) | ((i & 4) << 1) | ((i & 8) >> 1); }
 
@@ -208,8 +209,15 @@ __device__ __forceinline__ void prefill_tile(const PrefillArgs& a, int bx, int b
   const int wave = KS == 1 ? wave_all : wave_all % a.wpg;   // query head of the group
   const int G = a.hq / a.hkv;
   const int n_qt = (a.chunk + QT - 1) / QT;
-  const int qt = n_qt - 1 - bx / a.n_split;   // longest tiles first
-  const int s = bx % a.n_split;
+  // Work units (query tile, key split), longest tiles first, in groups of kXcds adjacent
+  // tiles with the tile fastest: the hardware deals consecutive workgroups to the XCDs
+  // in turn, so each XCD takes one tile of every group with all of its splits.  (With
+  // the split fastest, split s would always land on XCD s mod kXcds, and the later
+  // splits of short causal tiles hold no keys: the first XCDs would get most of the work.)
+  const int grp = bx / (kXcds * a.n_split), rem = bx % (kXcds * a.n_split);
+  const int s = rem / kXcds;
+  const int qt = n_qt - 1 - (grp * kXcds + rem % kXcds);
+  if (qt < 0) return;                                       // padding of the last group
   const int groups_per_kv = (G + a.wpg - 1) / a.wpg;
   const int g = by / groups_per_kv;
   const int h0 = g * G + (by % groups_per_kv) * a.wpg;   // first query head of this workgroup
@@ -706,6 +714,9 @@ struct Prepared {
 // CU (a grouped launch of four 256-token chunks runs at the same speed either way);
 // on short units the merge costs more than it saves (a 256-token chunk: 19.4 vs
 // 21.2 us).
+// Workgroups along x of one chunk's launch: whole groups of kXcds tiles, every split
+int unit_grid(const Prepared& pr) { return cdiv(pr.n_qt, kXcds) * kXcds * pr.p.n_split; }
+
 bool two_key_sets(const Prepared& pr, long workgroups) {
   const int nkb = (pr.a.prior + pr.a.chunk + 31) / 32;
   return pr.p.wpg <= 4 && workgroups <= pr.cus && std::min(nkb, pr.p.bps) >= 16;
@@ -743,7 +754,7 @@ xp_status prepare(const void* pool, int n_pages, int S, int hq, int hkv, int d, 
 // the tiles take the co-resident kernel and one key set
 template <typename T, int D>
 void launch_one(const Prepared& pr, bool cores, hipStream_t s) {
-  const dim3 grid(pr.n_qt * pr.p.n_split, pr.gy), block(64 * pr.p.wpg), cgrid(pr.n_qt, pr.a.hq);
+  const dim3 grid(unit_grid(pr), pr.gy), block(64 * pr.p.wpg), cgrid(pr.n_qt, pr.a.hq);
   if (cores)
     hipLaunchKernelGGL((prefill_cores_kernel<T, D, kNQ, kMaxW, 1>), grid, block, 0, s, pr.a);
   else if (two_key_sets(pr, long(grid.x) * grid.y))
@@ -760,7 +771,7 @@ void launch_group(const Prepared* pr, int n, bool cores, hipStream_t s) {
   bool split = false;
   for (int k = 0; k < n; ++k) {
     g.a[k] = pr[k].a;
-    g.gx[k] = pr[k].n_qt * pr[k].p.n_split;
+    g.gx[k] = unit_grid(pr[k]);
     g.start[k + 1] = g.start[k] + g.gx[k] * pr[k].gy;
     const bool sk = pr[k].p.n_split > 1;
     split = split || sk;
