@@ -51,6 +51,7 @@ constexpr int kNQ = 1;               // 32-query column blocks per wave
 constexpr int kMaxW = 8;             // waves (query heads) per workgroup
 constexpr int kStages = 2;           // LDS ring stages, one key set
 constexpr int kStagesKS2 = 3;        // LDS ring stages, two key sets
+constexpr int kStagesPipe = 3;       // LDS ring stages, the block-pipelined loop
 constexpr int kBlocksPerStage = 2;   // 32-key blocks per stage
 constexpr int kMaxBps = 256;   // key blocks per split (its page ids are staged in LDS)
 constexpr int kXcds = 8;       // XCDs the hardware deals consecutive workgroups to, in turn
@@ -176,7 +177,9 @@ __device__ __forceinline__ void out_row(const PrefillArgs& a, int t, void*& dst,
   }
 }
 
-template <typename T, int D, int NQ, int MAXW, int KS>
+// PIPE: the block-pipelined loop (one key set, one query column block, 16-bit
+// operands; below).
+template <typename T, int D, int NQ, int MAXW, int KS, bool PIPE = false>
 __device__ __forceinline__ void prefill_tile(const PrefillArgs& a, int bx, int by) {
   constexpr int EB = St<T>::bytes;
   constexpr int QT = 32 * NQ;                     // queries per tile
@@ -188,7 +191,8 @@ __device__ __forceinline__ void prefill_tile(const PrefillArgs& a, int bx, int b
   constexpr int VROW_CH = kPage * EB / 16;        // 16-byte chunks per V^T row
   // blocks per stage and ring depth, within the LDS budget
   constexpr int kBudget = 144 * 1024;
-  constexpr int kSt = KS == 2 ? kStagesKS2 : kStages;
+  static_assert(!PIPE || (KS == 1 && NQ == 1 && sizeof(T) == 2), "the pipelined loop: one key set, NQ = 1, bf16");
+  constexpr int kSt = KS == 2 ? kStagesKS2 : (PIPE ? kStagesPipe : kStages);
   constexpr int SB = kBlocksPerStage * 2 * BLK <= kBudget
                          ? kBlocksPerStage
                          : (kBudget / (2 * BLK) > 0 ? kBudget / (2 * BLK) : 1);
@@ -308,6 +312,136 @@ __device__ __forceinline__ void prefill_tile(const PrefillArgs& a, int bx, int b
     lsum[j] = 0.f;
   }
 
+  const int krow = kappa(ql);
+  if constexpr (PIPE) {
+    // Block-pipelined loop.  Each step issues the PV MFMAs of the previous block
+    // between the masking and maximum of this block's scores, and the QK MFMAs of the
+    // next block between this block's exponentials and packing, so a wave keeps its
+    // matrix pipe fed through its own softmax instead of leaving that to the other
+    // wave of its SIMD.  The rescale of block i still precedes block i's PV product
+    // and every sum runs in the plain loop's order: both loops give the same bits.
+    // The last block of a stage has its V^T fragments read after the barrier that
+    // opens the next stage, so that barrier refills the slot of the stage before
+    // (a three-slot ring), with the next stage's loads issued as it opens.
+    constexpr int NM = D / 16;                    // MFMAs of each product per block
+    const int n = kb1 - kb0;
+    const int n_sg = (n + SB - 1) / SB;
+    auto open_stage = [&](int sg) {
+      gemm::wait_vmcnt<0>();                      // this wave's loads of stage sg landed
+      __builtin_amdgcn_s_barrier();
+      if (sg + 1 < n_sg && wave < waves)
+        for (int b = lw; b < SB; b += nl) issue_block(sg + 1, b, (sg + 1) % NST);
+    };
+    if (wave < waves)
+      for (int b = lw; b < SB; b += nl) issue_block(0, b, 0);
+    if (!active) {
+      for (int sg = 0; sg < n_sg; ++sg) open_stage(sg);
+    } else {
+      open_stage(0);
+      auto blk = [&](int i) { return reinterpret_cast<const char*>(ring[(i / SB) % NST]) + (i % SB) * BLK; };
+      const int kofs = krow < kPage ? 0 : PLANE, kr = krow & 15;
+      Frag8<T> kf[NM], vf[2][D / 32], pf[2];
+      // the first step's PV product adds zeros
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        pf[u].v = make_uint4(0u, 0u, 0u, 0u);
+#pragma unroll
+        for (int nn = 0; nn < D / 32; ++nn) vf[u][nn].v = make_uint4(0u, 0u, 0u, 0u);
+      }
+#pragma unroll
+      for (int st = 0; st < NM; ++st) kfrag(kf[st], blk(0) + kofs, kr, 16 * st + 8 * hf);
+      f32x16 sc = f32x16{};
+#pragma unroll
+      for (int st = 0; st < NM; ++st) mma32x32_k16(sc, kf[st], qf[0][st]);
+      for (int sg = 0; sg < n_sg; ++sg) {
+#pragma unroll
+        for (int b = 0; b < SB; ++b) {
+          const int i = sg * SB + b;
+          if (i >= n) break;
+          const int key0 = (kb0 + i) * 32;
+          // causal mask (blocks that cross the diagonal)
+          if (key0 + 31 > a.prior + t0) {
+            const int lim = a.prior + min(t0 + ql, a.chunk - 1) - (key0 + 8 * hf);
+#pragma unroll
+            for (int r = 0; r < 16; ++r) sc[r] = (16 * (r >> 3) + (r & 7) > lim) ? -__builtin_inff() : sc[r];
+          }
+          // PV of block i - 1 | K fragments of block i + 1 (same stage) | block maximum
+#pragma unroll
+          for (int u = 0; u < 2; ++u)
+#pragma unroll
+            for (int nn = 0; nn < D / 32; ++nn) mma32x32_k16(o[0][nn], vf[u][nn], pf[u]);
+          if (b + 1 < SB) {
+#pragma unroll
+            for (int st = 0; st < NM; ++st) kfrag(kf[st], blk(i + 1) + kofs, kr, 16 * st + 8 * hf);
+          }
+          float mb = fmaxf(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])), fmaxf(fmaxf(sc[4], sc[5]), fmaxf(sc[6], sc[7])));
+          mb = fmaxf(mb, fmaxf(fmaxf(fmaxf(sc[8], sc[9]), fmaxf(sc[10], sc[11])),
+                               fmaxf(fmaxf(sc[12], sc[13]), fmaxf(sc[14], sc[15]))));
+          float m0, m1;
+          halves_xor32(mb, m0, m1);
+          mb = fmaxf(m0, m1) * a.scale_log2;
+#pragma unroll
+          for (int k = 0; k < NM; ++k) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);
+          }
+          if (__builtin_amdgcn_ballot_w64(mb > ms[0] + kLazy) != 0) {
+            const float mn = fmaxf(ms[0], mb);
+            const float alpha = ms[0] == -__builtin_inff() ? 0.f : fast_exp2(ms[0] - mn);
+            ms[0] = mn;
+            lsum[0] *= alpha;
+#pragma unroll
+            for (int nn = 0; nn < D / 32; ++nn) o[0][nn] *= alpha;
+          }
+          const float mref = ms[0] == -__builtin_inff() ? 0.f : ms[0];
+          if (b + 1 == SB && sg + 1 < n_sg) open_stage(sg + 1);
+          // QK of block i + 1 | weights of block i | V^T fragments of block i.  Past the
+          // last block the K fragments are stale and that product goes unused.
+          if (b + 1 == SB) {
+#pragma unroll
+            for (int st = 0; st < NM; ++st) kfrag(kf[st], blk(i + 1) + kofs, kr, 16 * st + 8 * hf);
+          }
+          f32x16 sn = f32x16{};
+#pragma unroll
+          for (int st = 0; st < NM; ++st) mma32x32_k16(sn, kf[st], qf[0][st]);
+#pragma unroll
+          for (int u = 0; u < 2; ++u) {
+            float pu[8];
+#pragma unroll
+            for (int r = 0; r < 8; ++r) pu[r] = fast_exp2(__builtin_fmaf(sc[8 * u + r], a.scale_log2, -mref));
+            lsum[0] += pack_and_sum(pf[u], pu);
+          }
+#pragma unroll
+          for (int u = 0; u < 2; ++u)
+#pragma unroll
+            for (int nn = 0; nn < D / 32; ++nn) vfrag<VROW_CH>(vf[u][nn], blk(i) + (2 + u) * PLANE, 32 * nn + ql, hf);
+          if (b + 1 == SB) __builtin_amdgcn_sched_group_barrier(0x100, NM, 0);
+#pragma unroll
+          for (int k = 0; k < NM; ++k) {
+            __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+          }
+          sc = sn;
+        }
+      }
+      // slots at or past the table end hold no key (their V^T columns may hold
+      // anything, including NaN): only the table's last block has them, and it can
+      // only be the last block of a split
+      const int key_last = (kb1 - 1) * 32;
+      if (key_last + 32 > n_keys) {
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
+#pragma unroll
+          for (int nn = 0; nn < D / 32; ++nn) zero_from(vf[u][nn], n_keys - (key_last + 16 * u + 8 * hf));
+      }
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int nn = 0; nn < D / 32; ++nn) mma32x32_k16(o[0][nn], vf[u][nn], pf[u]);
+    }
+  } else {
   // stages 0 .. NST - 2 in flight before the first one is consumed; stage
   // sg + NST - 1 is then issued block by block while stage sg is consumed, into the
   // ring slot every wave finished reading before the barrier that opened stage sg
@@ -316,7 +450,6 @@ __device__ __forceinline__ void prefill_tile(const PrefillArgs& a, int bx, int b
   for (int i = 0; i < NST - 1; ++i)
     if (i < n_sg && wave < waves)
       for (int b = lw; b < SB; b += nl) issue_block(i, b, i);
-  const int krow = kappa(ql);
   for (int sg = 0; sg < n_sg; ++sg) {
     // stage sg has landed once no more than the later stages' loads are outstanding
     wait_vm_le(min(NST - 2, n_sg - 1 - sg) * my_instr);
@@ -413,6 +546,7 @@ __device__ __forceinline__ void prefill_tile(const PrefillArgs& a, int bx, int b
 #pragma unroll
           for (int j = 0; j < NQ; ++j) mma32x32_k16(o[j][n], vf[u][n], pf[j][u]);
     }
+  }
   }
   if (bad && a.status && lane == 0 && wave_all == 0) atomicOr(a.status, XP_DEV_BAD_PAGE);
   if constexpr (KS == 2) {
@@ -539,9 +673,9 @@ __device__ __forceinline__ void prefill_combine_tile(const PrefillArgs& a, int q
   }
 }
 
-template <typename T, int D, int NQ, int MAXW, int KS>
+template <typename T, int D, int NQ, int MAXW, int KS, bool PIPE = false>
 __global__ __launch_bounds__(64 * MAXW * KS) void prefill_kernel(PrefillArgs a) {
-  prefill_tile<T, D, NQ, MAXW, KS>(a, int(blockIdx.x), int(blockIdx.y));
+  prefill_tile<T, D, NQ, MAXW, KS, PIPE>(a, int(blockIdx.x), int(blockIdx.y));
 }
 
 // The co-resident form, for prefill running beside decode attention on the same CUs:
@@ -593,12 +727,12 @@ __device__ __forceinline__ void group_member(const PrefillGroup& g, int b, bool 
   y = (b - s0) / w;
 }
 
-template <typename T, int D, int NQ, int MAXW, int KS>
+template <typename T, int D, int NQ, int MAXW, int KS, bool PIPE = false>
 __global__ __launch_bounds__(64 * MAXW * KS) void prefill_group_kernel(PrefillGroup g) {
   PrefillArgs a;
   int x, y;
   group_member(g, int(blockIdx.x), false, a, x, y);
-  prefill_tile<T, D, NQ, MAXW, KS>(a, x, y);
+  prefill_tile<T, D, NQ, MAXW, KS, PIPE>(a, x, y);
 }
 
 template <typename T, int D, int NQ, int MAXW, int KS>
@@ -760,7 +894,7 @@ void launch_one(const Prepared& pr, bool cores, hipStream_t s) {
   else if (two_key_sets(pr, long(grid.x) * grid.y))
     hipLaunchKernelGGL((prefill_kernel<T, D, kNQ, 4, 2>), grid, dim3(2 * block.x), 0, s, pr.a);
   else
-    hipLaunchKernelGGL((prefill_kernel<T, D, kNQ, kMaxW, 1>), grid, block, 0, s, pr.a);
+    hipLaunchKernelGGL((prefill_kernel<T, D, kNQ, kMaxW, 1, sizeof(T) == 2>), grid, block, 0, s, pr.a);
   if (pr.p.n_split > 1) hipLaunchKernelGGL((prefill_combine_kernel<T, D>), cgrid, dim3(256), 0, s, pr.a);
 }
 
@@ -785,7 +919,7 @@ void launch_group(const Prepared* pr, int n, bool cores, hipStream_t s) {
     hipLaunchKernelGGL((prefill_group_kernel<T, D, kNQ, 4, 2>), dim3(g.start[n]), dim3(128 * pr[0].p.wpg), 0,
                        s, g);
   else
-    hipLaunchKernelGGL((prefill_group_kernel<T, D, kNQ, kMaxW, 1>), dim3(g.start[n]),
+    hipLaunchKernelGGL((prefill_group_kernel<T, D, kNQ, kMaxW, 1, sizeof(T) == 2>), dim3(g.start[n]),
                        dim3(64 * pr[0].p.wpg), 0, s, g);
   if (split) hipLaunchKernelGGL((prefill_group_combine_kernel<T, D>), dim3(g.cstart[n]), dim3(256), 0, s, g);
 }
