@@ -53,6 +53,7 @@ constexpr int kStages = 2;           // LDS ring stages, one key set
 constexpr int kStagesKS2 = 3;        // LDS ring stages, two key sets
 constexpr int kStagesPipe = 3;       // LDS ring stages, the block-pipelined loop
 constexpr int kBlocksPerStage = 2;   // 32-key blocks per stage
+constexpr int kBlocksPerStagePipe = 3;   // 32-key blocks per stage, the block-pipelined loop
 constexpr int kMaxBps = 256;   // key blocks per split (its page ids are staged in LDS)
 constexpr int kXcds = 8;       // XCDs the hardware deals consecutive workgroups to, in turn
 
@@ -74,6 +75,28 @@ __device__ __forceinline__ void zero_from(Frag8<float>& f, int nvalid) {
   if (nvalid <= 5) f.hi.y = 0.f;
   if (nvalid <= 6) f.hi.z = 0.f;
   if (nvalid <= 7) f.hi.w = 0.f;
+}
+
+// Maximum of two scores as one v_med3 (the median of a, b and +inf).  fmaxf costs an
+// extra quieting instruction per operand produced by an MFMA; scores are never
+// signalling NaNs (slots past the table end are replaced by -inf before any maximum),
+// so the median gives the same value.  The +inf comes from a scalar register the
+// compiler cannot see through (with a literal +inf it turns the median back into
+// fmaxf).
+__device__ __forceinline__ float opaque_inf() {
+  float v;
+  asm("s_mov_b32 %0, 0x7f800000" : "=s"(v));
+  return v;
+}
+__device__ __forceinline__ float smax(float a, float b, float inf) { return __builtin_amdgcn_fmed3f(a, b, inf); }
+// the maximum of 16 scores
+template <typename V>
+__device__ __forceinline__ float max16(const V& v, float inf) {
+  const float lo = smax(smax(smax(v[0], v[1], inf), smax(v[2], v[3], inf), inf),
+                        smax(smax(v[4], v[5], inf), smax(v[6], v[7], inf), inf), inf);
+  const float hi = smax(smax(smax(v[8], v[9], inf), smax(v[10], v[11], inf), inf),
+                        smax(smax(v[12], v[13], inf), smax(v[14], v[15], inf), inf), inf);
+  return smax(lo, hi, inf);
 }
 
 // log2-domain margin by which a row maximum may exceed the softmax reference
@@ -193,7 +216,9 @@ __device__ __forceinline__ void prefill_tile(const PrefillArgs& a, int bx, int b
   constexpr int kBudget = 144 * 1024;
   static_assert(!PIPE || (KS == 1 && NQ == 1 && sizeof(T) == 2), "the pipelined loop: one key set, NQ = 1, bf16");
   constexpr int kSt = KS == 2 ? kStagesKS2 : (PIPE ? kStagesPipe : kStages);
-  constexpr int SB = kBlocksPerStage * 2 * BLK <= kBudget
+  constexpr int kBps = PIPE ? kBlocksPerStagePipe : kBlocksPerStage;
+  constexpr int SB = kBps * kSt * BLK <= kBudget ? kBps
+                     : kBlocksPerStage * 2 * BLK <= kBudget
                          ? kBlocksPerStage
                          : (kBudget / (2 * BLK) > 0 ? kBudget / (2 * BLK) : 1);
   constexpr int NST = kSt * SB * BLK <= kBudget ? kSt : (kBudget / (SB * BLK) > 2 ? kBudget / (SB * BLK) : 2);
@@ -374,12 +399,11 @@ __device__ __forceinline__ void prefill_tile(const PrefillArgs& a, int bx, int b
 #pragma unroll
             for (int st = 0; st < NM; ++st) kfrag(kf[st], blk(i + 1) + kofs, kr, 16 * st + 8 * hf);
           }
-          float mb = fmaxf(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])), fmaxf(fmaxf(sc[4], sc[5]), fmaxf(sc[6], sc[7])));
-          mb = fmaxf(mb, fmaxf(fmaxf(fmaxf(sc[8], sc[9]), fmaxf(sc[10], sc[11])),
-                               fmaxf(fmaxf(sc[12], sc[13]), fmaxf(sc[14], sc[15]))));
+          const float inf = opaque_inf();
+          float mb = max16(sc, inf);
           float m0, m1;
           halves_xor32(mb, m0, m1);
-          mb = fmaxf(m0, m1) * a.scale_log2;
+          mb = smax(m0, m1, inf) * a.scale_log2;
 #pragma unroll
           for (int k = 0; k < NM; ++k) {
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
@@ -508,12 +532,11 @@ __device__ __forceinline__ void prefill_tile(const PrefillArgs& a, int bx, int b
 #pragma unroll
           for (int r = 0; r < 16; ++r) sv[r] = (16 * (r >> 3) + (r & 7) > lim) ? -__builtin_inff() : sv[r];
         }
-        float mb = fmaxf(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])), fmaxf(fmaxf(sv[4], sv[5]), fmaxf(sv[6], sv[7])));
-        mb = fmaxf(mb, fmaxf(fmaxf(fmaxf(sv[8], sv[9]), fmaxf(sv[10], sv[11])),
-                             fmaxf(fmaxf(sv[12], sv[13]), fmaxf(sv[14], sv[15]))));
+        const float inf = opaque_inf();
+        float mb = max16(sv, inf);
         float m0, m1;
         halves_xor32(mb, m0, m1);
-        mb = fmaxf(m0, m1) * a.scale_log2;
+        mb = smax(m0, m1, inf) * a.scale_log2;
         if (__builtin_amdgcn_ballot_w64(mb > ms[j] + kLazy) != 0) {
           const float mn = fmaxf(ms[j], mb);
           const float alpha = ms[j] == -__builtin_inff() ? 0.f : fast_exp2(ms[j] - mn);
