@@ -863,17 +863,18 @@ struct Prepared {
   int n_qt, gy, cus;
 };
 
-// Two key sets per workgroup (two waves per query head) when the group has at most
-// four heads, the grid has no more workgroups than CUs and the longest work unit
-// spans at least 16 key blocks: each CU then holds one four-wave workgroup, and a
-// second set of waves on the other half of the keys shortens the longest unit
-// (1024-token 8B chunk: 33 -> 29.5 us).  Larger grids already keep two workgroups per
-// CU (a grouped launch of four 256-token chunks runs at the same speed either way);
-// on short units the merge costs more than it saves (a 256-token chunk: 19.4 vs
-// 21.2 us).
 // Workgroups along x of one chunk's launch: whole groups of kXcds tiles, every split
 int unit_grid(const Prepared& pr) { return cdiv(pr.n_qt, kXcds) * kXcds * pr.p.n_split; }
 
+// Two key sets per workgroup (two waves per query head), for 32-bit operands, when the
+// group has at most four heads, the grid has no more workgroups than CUs and the
+// longest work unit spans at least 16 key blocks: each CU then holds one four-wave
+// workgroup, and a second set of waves on the other half of the keys shortens the
+// longest unit (1024-token 8B chunk, plain loop: 33 -> 29.5 us).  Larger grids already
+// keep two workgroups per CU, and on short units the merge costs more than it saves
+// (a 256-token chunk: 19.4 vs 21.2 us).  16-bit operands always take the pipelined
+// loop with one key set, which overlaps a wave's own softmax with its MFMAs (the 8B
+// chunk: 30.2 us against 31.2 with two key sets).
 bool two_key_sets(const Prepared& pr, long workgroups) {
   const int nkb = (pr.a.prior + pr.a.chunk + 31) / 32;
   return pr.p.wpg <= 4 && workgroups <= pr.cus && std::min(nkb, pr.p.bps) >= 16;
@@ -914,7 +915,7 @@ void launch_one(const Prepared& pr, bool cores, hipStream_t s) {
   const dim3 grid(unit_grid(pr), pr.gy), block(64 * pr.p.wpg), cgrid(pr.n_qt, pr.a.hq);
   if (cores)
     hipLaunchKernelGGL((prefill_cores_kernel<T, D, kNQ, kMaxW, 1>), grid, block, 0, s, pr.a);
-  else if (two_key_sets(pr, long(grid.x) * grid.y))
+  else if (sizeof(T) != 2 && two_key_sets(pr, long(grid.x) * grid.y))
     hipLaunchKernelGGL((prefill_kernel<T, D, kNQ, 4, 2>), grid, dim3(2 * block.x), 0, s, pr.a);
   else
     hipLaunchKernelGGL((prefill_kernel<T, D, kNQ, kMaxW, 1, sizeof(T) == 2>), grid, block, 0, s, pr.a);
@@ -938,7 +939,7 @@ void launch_group(const Prepared* pr, int n, bool cores, hipStream_t s) {
   if (cores)
     hipLaunchKernelGGL((prefill_group_cores_kernel<T, D, kNQ, kMaxW, 1>), dim3(g.start[n]), dim3(64 * pr[0].p.wpg),
                        0, s, g);
-  else if (two_key_sets(pr[0], g.start[n]))
+  else if (sizeof(T) != 2 && two_key_sets(pr[0], g.start[n]))
     hipLaunchKernelGGL((prefill_group_kernel<T, D, kNQ, 4, 2>), dim3(g.start[n]), dim3(128 * pr[0].p.wpg), 0,
                        s, g);
   else

@@ -378,12 +378,12 @@ PARITY_WORKLOADS = {
                    chunk_len=320, prior_len=2000, sp_degree=2, sp_rank=1,
                    description="small bf16 layer, 2000 prior keys, SP2 rank 1"),
     # the 8B head layout (G = 4 on 8 kv heads): grids of at most one workgroup per CU
-    # whose work units span 16 or more key blocks, the case where a workgroup holds
-    # two waves per query head; ragged chunk, prior not a multiple of the 32-key block
+    # whose work units span 16 or more key blocks (one wave per SIMD); ragged chunk,
+    # prior not a multiple of the 32-key block
     "P5": Workload("P5", 105, "bf16", 512, 32, 8, 128, 1024, n_decode=0, ctx=("fixed", 0),
                    chunk_len=900, prior_len=300, description="prefill only, 8B heads, 900 after 300"),
-    # the same with the key range split three ways (19-block units: odd, so the two
-    # halves of each unit differ in length) and merged
+    # the same with the key range split three ways (19-block units, not a multiple of
+    # the pipelined loop's three-block stages) and merged
     "P6": Workload("P6", 106, "bf16", 512, 32, 8, 128, 1024, n_decode=0, ctx=("fixed", 0),
                    chunk_len=300, prior_len=1500, description="prefill only, 8B heads, 300 after 1500"),
     # long decode contexts on the 32B head layout (64 q / 8 kv heads): the shortest and
@@ -400,6 +400,14 @@ PARITY_WORKLOADS = {
     # single decode row, fp32
     "E3": Workload("E3", 113, "f32", 256, 4, 2, 64, 512, n_decode=1, ctx=("fixed", 40),
                    chunk_len=0, prior_len=0, description="one fp32 decode row"),
+    # bf16 with d = 64 and three query heads per kv head: the pipelined prefill loop's
+    # d = 64 form, ragged chunk and prior
+    "P7": Workload("P7", 107, "bf16", 512, 12, 4, 64, 1024, n_decode=0, ctx=("fixed", 0),
+                   chunk_len=150, prior_len=90, description="prefill only, bf16, d = 64, G = 3"),
+    # fp32 on the 8B head layout at d = 64 (P5's grid): a workgroup holds two waves per
+    # query head (two key sets, 32-bit operands only)
+    "E5": Workload("E5", 115, "f32", 512, 32, 8, 64, 1024, n_decode=0, ctx=("fixed", 0),
+                   chunk_len=900, prior_len=300, description="prefill only, fp32, two key sets"),
     # fp32 with SP2
     "E4": Workload("E4", 114, "f32", 256, 4, 2, 64, 512, n_decode=3, ctx=("uniform", 0, 100),
                    chunk_len=34, prior_len=17, sp_degree=2, sp_rank=1, description="fp32, SP2 rank 1"),
