@@ -226,7 +226,9 @@ xp_status xp_ctx_streams(const xp_ctx* ctx, void** decode_stream, void** prefill
  * xp_ctx_stage_time waits for the recorded runs of one stage and returns their count
  * and summed duration in milliseconds (0 and 0 when none).  A stage that launches
  * nothing in a run (e.g. RoPE/append when the QKV epilogue did it all) still counts,
- * with its near-zero time. */
+ * with its near-zero time.  When the QKV epilogue rotates and appends, the copies of
+ * peer_attn_in (which only the O projection reads) run on decode attention's stream
+ * right after it, outside every stage. */
 #define XP_STAGE_NORM1 0        /* RMSNorm-1 (+ the rows' RoPE table for the fused QKV) */
 #define XP_STAGE_QKV 1          /* QKV projection (with RoPE + appends when fused)   */
 #define XP_STAGE_ROPE_APPEND 2  /* stand-alone RoPE/append and stand-in copies       */

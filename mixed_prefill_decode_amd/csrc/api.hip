@@ -571,40 +571,50 @@ struct LayerRun {
   xp_status pre(hipStream_t s) const;
   xp_status attend(hipStream_t s, bool split) const;
   xp_status post(hipStream_t s) const;
+  // RoPE + appends (+ the peer stand-ins) of one chunk's rows, the decodes with the last
+  // chunk (their rows follow it in x) or alone when there is no chunk
+  PostQkvArgs post_args(const ChunkRun* c, int nd, bool rope_done) const;
+  // with at most one chunk the QKV projection rotates and appends in its epilogue
+  bool fused_qkv() const { return ch.size() <= 1 && gemm_rope_supported(shape.dtype, shape.head_dim); }
 };
+
+PostQkvArgs LayerRun::post_args(const ChunkRun* c, int nd, bool rope_done) const {
+  const xp_layer_shape* sh = &shape;
+  const xp_batch_desc* d = &desc;
+  const int Hq = sh->n_q_heads, Hkv = sh->n_kv_heads, D = sh->head_dim;
+  const int ldq = (Hq + 2 * Hkv) * D;
+  char* ws = static_cast<char*>(workspace);
+  float* qkv = reinterpret_cast<float*>(ws + L.qkv);
+  const size_t attn_row = size_t(Hq) * D * dtype_bytes(sh->dtype);
+  const int row0 = c ? c->row0 : rows_pre;
+  PostQkvArgs pa{qkv + size_t(row0) * ldq, c ? c->n_local : 0, nd, Hq, Hkv, D, sh->page_size, sh->rope_base,
+                 d->dec_ctx, d->dec_pages, d->dec_max_blocks, c ? c->prior : 0, c ? c->len : 0, d->sp_degree,
+                 d->sp_rank, c ? c->off : 0, c ? c->pages : nullptr, c ? c->max_blocks : 0,
+                 c ? c->peer_qkv_in : nullptr, c ? c->peer_qkv_out : nullptr, c ? c->peer_attn_in : nullptr,
+                 pool.pool, pool.n_pages, ws + L.q_dec, c ? ws + L.q_pre + c->q_off : nullptr,
+                 ws + L.attn + size_t(row0) * attn_row, reinterpret_cast<uint32_t*>(ws + L.status)};
+  pa.rope_done = rope_done ? 1 : 0;
+  return pa;
+}
 
 xp_status LayerRun::pre(hipStream_t s) const {
   xp_status st;
   const xp_layer_shape* sh = &shape;
   const xp_batch_desc* d = &desc;
   const int dt = sh->dtype, H = sh->hidden, Hq = sh->n_q_heads, Hkv = sh->n_kv_heads, D = sh->head_dim;
-  const int P = d->sp_degree, r = d->sp_rank, n_d = d->n_decode, M = rows_pre + n_d;
+  const int n_d = d->n_decode, M = rows_pre + n_d;
   const int ldq = (Hq + 2 * Hkv) * D;
   char* ws = static_cast<char*>(workspace);
   uint32_t* status = reinterpret_cast<uint32_t*>(ws + L.status);
   float* qkv = reinterpret_cast<float*>(ws + L.qkv);
-  char* attn = ws + L.attn;
-  const size_t attn_row = size_t(Hq) * D * dtype_bytes(dt);
-
-  // RoPE + appends (+ the peer stand-ins) of one chunk's rows, the decodes with the last
-  // chunk (their rows follow it in x) or alone when there is no chunk
-  auto args_of = [&](const ChunkRun* c, int nd, bool rope_done) {
-    const int row0 = c ? c->row0 : rows_pre;
-    PostQkvArgs pa{qkv + size_t(row0) * ldq, c ? c->n_local : 0, nd, Hq, Hkv, D, sh->page_size, sh->rope_base,
-                   d->dec_ctx, d->dec_pages, d->dec_max_blocks, c ? c->prior : 0, c ? c->len : 0, P, r,
-                   c ? c->off : 0, c ? c->pages : nullptr, c ? c->max_blocks : 0, c ? c->peer_qkv_in : nullptr,
-                   c ? c->peer_qkv_out : nullptr, c ? c->peer_attn_in : nullptr, pool.pool, pool.n_pages,
-                   ws + L.q_dec, c ? ws + L.q_pre + c->q_off : nullptr, attn + size_t(row0) * attn_row, status};
-    pa.rope_done = rope_done ? 1 : 0;
-    return pa;
-  };
+  auto args_of = [&](const ChunkRun* c, int nd, bool rope_done) { return post_args(c, nd, rope_done); };
 
   // shared linear region (1): RMSNorm + QKV over all M rows.  With at most one chunk the
   // QKV projection rotates and appends in its epilogue (the RMSNorm forms each row's
   // RoPE table in the qkv region, which then holds no projection); several chunks rotate
   // per chunk afterwards.
   const ChunkRun* c0 = ch.empty() ? nullptr : &ch[0];
-  const bool fused = ch.size() <= 1 && gemm_rope_supported(dt, D);
+  const bool fused = fused_qkv();
   RopeTab rt{};
   if (fused) {
     rt.tab = reinterpret_cast<float2*>(qkv);
@@ -624,8 +634,11 @@ xp_status LayerRun::pre(hipStream_t s) const {
     pa.rope_tab = rt.tab;
     if (M > 0 && (st = stage(XP_STAGE_QKV, s, [&] { return launch_gemm_rope(dt, ws + L.hn, weights.w_qkv, M, ldq, H, pa, s); })))
       return st;
-    // what is left: the chunk's peer rows and the peer_attn_in copies (sequence parallel)
-    return stage(XP_STAGE_ROPE_APPEND, s, [&] { return launch_post_qkv(dt, args_of(c0, n_d, true), s); });
+    // what is left before attention: the chunk's peer rows (sequence parallel); the
+    // peer_attn_in copies follow decode attention (attend)
+    PostQkvArgs pp = args_of(c0, n_d, true);
+    pp.only = 2;
+    return stage(XP_STAGE_ROPE_APPEND, s, [&] { return launch_post_qkv(dt, pp, s); });
   }
   if (M > 0 && (st = stage(XP_STAGE_QKV, s, [&] {
                   return launch_gemm(dt, XP_EPI_F32, ws + L.hn, weights.w_qkv, nullptr, nullptr, qkv, M, ldq, H,
@@ -664,8 +677,18 @@ xp_status LayerRun::attend(hipStream_t s, bool split) const {
   auto decode = [&](hipStream_t q) {
     return launch_decode(dt, ws + L.q_dec, kv->pool, kv->n_pages, sh->page_size, d->dec_pages, d->dec_max_blocks,
                          d->dec_ctx, n_d, Hq, Hkv, D, attn + size_t(rows_pre) * attn_row, Hq * D,
-                         reinterpret_cast<float*>(ws + L.dec_ml), reinterpret_cast<float*>(ws + L.dec_o), L.dec_pages_per_split,
-                         status, q, cores);
+                         reinterpret_cast<float*>(ws + L.dec_ml), reinterpret_cast<float*>(ws + L.dec_o),
+                         L.dec_pages_per_split, status, q, cores);
+  };
+  // the other ranks' heads of the local prefill rows (peer_attn_in), which only the O
+  // projection reads: copied on decode's stream after decode (in the concurrent modes
+  // decode ends before prefill, so the copy leaves the path to attention; outside the
+  // decode stage's events)
+  auto peer_heads = [&](hipStream_t q) {
+    if (!fused_qkv()) return xp_status(XP_OK);
+    PostQkvArgs pc = post_args(ch.empty() ? nullptr : &ch[0], n_d, true);
+    pc.only = 1;
+    return launch_post_qkv(dt, pc, q);
   };
   auto prefill = [&](hipStream_t q) {
     if (ch.size() == 1) {
@@ -689,12 +712,14 @@ xp_status LayerRun::attend(hipStream_t s, bool split) const {
   };
   if (!concurrent) {
     if ((st = stage(XP_STAGE_DECODE, s, [&] { return decode(s); }))) return st;
+    if ((st = peer_heads(s))) return st;
     if ((st = stage(XP_STAGE_PREFILL, s, [&] { return prefill(s); }))) return st;
   } else {
     XP_HIP_TRY(hipEventRecord(ctx->e_fork, s));
     XP_HIP_TRY(hipStreamWaitEvent(ctx->s_dec, ctx->e_fork, 0));
     XP_HIP_TRY(hipStreamWaitEvent(ctx->s_pre, ctx->e_fork, 0));
     if ((st = stage(XP_STAGE_DECODE, ctx->s_dec, [&] { return decode(ctx->s_dec); }))) return st;
+    if ((st = peer_heads(ctx->s_dec))) return st;
     XP_HIP_TRY(hipEventRecord(ctx->e_dec, ctx->s_dec));
     if ((st = stage(XP_STAGE_PREFILL, ctx->s_pre, [&] { return prefill(ctx->s_pre); }))) return st;
     XP_HIP_TRY(hipEventRecord(ctx->e_pre, ctx->s_pre));

@@ -31,8 +31,15 @@ xp_status launch_cfg(const void* A, const void* B, const void* B2, const void* R
   if constexpr (EPI == gemm::kEpiRope) return XP_OK;   // one unit per tile, no partials
   if (splits > 1) {
     const long mn = long(M) * N;
-    const int blocks = int(std::min<long>((mn + 255) / 256, 4096));
-    hipLaunchKernelGGL((gemm::gemm_reduce_kernel<T, EPI>), dim3(blocks), dim3(256), 0, s, part, R, C, mn, splits);
+    if (mn % 4 == 0) {
+      const int blocks = int(std::min<long>((mn / 4 + 255) / 256, 4096));
+      hipLaunchKernelGGL((gemm::gemm_reduce_kernel<T, EPI, true>), dim3(blocks), dim3(256), 0, s, part, R, C, mn,
+                         splits);
+    } else {
+      const int blocks = int(std::min<long>((mn + 255) / 256, 4096));
+      hipLaunchKernelGGL((gemm::gemm_reduce_kernel<T, EPI, false>), dim3(blocks), dim3(256), 0, s, part, R, C, mn,
+                         splits);
+    }
     XP_CHECK_LAUNCH();
   }
   return XP_OK;

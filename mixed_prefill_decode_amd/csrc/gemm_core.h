@@ -575,23 +575,47 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(const char* __rest
 
 // Sums the K-split partials of gemm_kernel in split order and applies the epilogue:
 // C = epi(sum_s part[s][0]) (SwiGLU: silu(sum_s part[s][0]) * sum_s part[s][1]).
-template <typename T, int EPI>
+// V4: four consecutive elements per thread (MN a multiple of 4), the same sums.
+template <typename T, int EPI, bool V4>
 __global__ __launch_bounds__(256) void gemm_reduce_kernel(const float* __restrict__ part, const void* __restrict__ R,
                                                           void* __restrict__ C, long MN, int splits) {
   constexpr int NB = (EPI == XP_EPI_SWIGLU) ? 2 : 1;
-  for (long idx = long(blockIdx.x) * 256 + threadIdx.x; idx < MN; idx += long(gridDim.x) * 256) {
-    float v = part[idx];
-    for (int s = 1; s < splits; ++s) v += part[long(s) * NB * MN + idx];
-    if constexpr (EPI == XP_EPI_F32) {
-      reinterpret_cast<float*>(C)[idx] = v;
-    } else if constexpr (EPI == XP_EPI_ADD_T) {
-      reinterpret_cast<float*>(C)[idx] = St<T>::load(R, idx) + v;
-    } else if constexpr (EPI == XP_EPI_ADD_F32) {
-      reinterpret_cast<float*>(C)[idx] = reinterpret_cast<const float*>(R)[idx] + v;
-    } else {
-      float u = part[MN + idx];
-      for (int s = 1; s < splits; ++s) u += part[(long(s) * NB + 1) * MN + idx];
-      St<T>::store(C, idx, v / (1.0f + __expf(-v)) * u);
+  if constexpr (V4) {
+    const float4* p4 = reinterpret_cast<const float4*>(part);
+    const long MN4 = MN / 4;
+    auto add = [](float4 a, float4 b) { return make_float4(a.x + b.x, a.y + b.y, a.z + b.z, a.w + b.w); };
+    for (long i = long(blockIdx.x) * 256 + threadIdx.x; i < MN4; i += long(gridDim.x) * 256) {
+      float4 v = p4[i];
+      for (int s = 1; s < splits; ++s) v = add(v, p4[long(s) * NB * MN4 + i]);
+      if constexpr (EPI == XP_EPI_F32) {
+        reinterpret_cast<float4*>(C)[i] = v;
+      } else if constexpr (EPI == XP_EPI_ADD_T) {
+        reinterpret_cast<float4*>(C)[i] = add(St4<T>::load(R, 4 * i), v);
+      } else if constexpr (EPI == XP_EPI_ADD_F32) {
+        reinterpret_cast<float4*>(C)[i] = add(reinterpret_cast<const float4*>(R)[i], v);
+      } else {
+        float4 u = p4[MN4 + i];
+        for (int s = 1; s < splits; ++s) u = add(u, p4[(long(s) * NB + 1) * MN4 + i]);
+        St4<T>::store(C, 4 * i,
+                      make_float4(v.x / (1.0f + __expf(-v.x)) * u.x, v.y / (1.0f + __expf(-v.y)) * u.y,
+                                  v.z / (1.0f + __expf(-v.z)) * u.z, v.w / (1.0f + __expf(-v.w)) * u.w));
+      }
+    }
+  } else {
+    for (long idx = long(blockIdx.x) * 256 + threadIdx.x; idx < MN; idx += long(gridDim.x) * 256) {
+      float v = part[idx];
+      for (int s = 1; s < splits; ++s) v += part[long(s) * NB * MN + idx];
+      if constexpr (EPI == XP_EPI_F32) {
+        reinterpret_cast<float*>(C)[idx] = v;
+      } else if constexpr (EPI == XP_EPI_ADD_T) {
+        reinterpret_cast<float*>(C)[idx] = St<T>::load(R, idx) + v;
+      } else if constexpr (EPI == XP_EPI_ADD_F32) {
+        reinterpret_cast<float*>(C)[idx] = reinterpret_cast<const float*>(R)[idx] + v;
+      } else {
+        float u = part[MN + idx];
+        for (int s = 1; s < splits; ++s) u += part[(long(s) * NB + 1) * MN + idx];
+        St<T>::store(C, idx, v / (1.0f + __expf(-v)) * u);
+      }
     }
   }
 }

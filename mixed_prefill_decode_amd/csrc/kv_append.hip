@@ -18,6 +18,7 @@
 // (positions reach 65536, where an fp32 product would already be off by
 // several milliradians; the frequencies base^(-2i/d) come from the host, also in
 // fp64) and the rotation itself runs in fp32.
+#include <algorithm>
 #include <cmath>
 
 #include "rope.h"
@@ -76,7 +77,7 @@ constexpr int kPeerRowsPerTask = 8;
 template <typename T>
 __global__ __launch_bounds__(256) void post_qkv_kernel(PostQkvArgs a) {
   extern __shared__ float cs[];  // [d/2] cos, [d/2] sin
-  const int task = blockIdx.x, tid = threadIdx.x;
+  const int task = int(blockIdx.x) + a.task0, tid = threadIdx.x;
   const int M = a.n_pl + a.n_d;
   const int d = a.d, half = d / 2, S = a.S;
   const int hq_loc = a.Hq / a.P, hkv_loc = a.Hkv / a.P;
@@ -257,14 +258,18 @@ void rope_frequencies(double base, int d, double* inv_freq) {
 
 xp_status launch_post_qkv(int dtype, const PostQkvArgs& args, hipStream_t s) {
   const int n_peer_tasks = cdiv(args.chunk - args.n_pl, kPeerRowsPerTask);
-  int tasks = args.n_pl + args.n_d + n_peer_tasks;
-  // with the rotation done by the QKV epilogue only the peer rows and the peer_attn_in
-  // copies remain (none without sequence parallelism)
-  if (args.rope_done && n_peer_tasks == 0 && args.Hq / args.P == args.Hq) tasks = 0;
-  if (tasks == 0) return XP_OK;
+  const int M = args.n_pl + args.n_d;
+  int lo = args.only == 2 ? M : 0, hi = args.only == 1 ? M : M + n_peer_tasks;
+  // with the rotation done by the QKV epilogue a local row's task only copies its
+  // peer_attn_in heads (none without sequence parallelism)
+  if (args.rope_done && args.P == 1) lo = std::max(lo, M);
+  if (args.rope_done && args.only == 1) hi = std::min(hi, args.n_pl);   // decode rows have no peer heads
+  if (hi <= lo) return XP_OK;
   if (args.d % 8 || args.d / 2 > 64) return fail(XP_EUNSUPPORTED, "RoPE: head_dim %d", args.d);
   // the rotation frequencies base^(-2i/d), formed once in fp64 on the host
   PostQkvArgs a = args;
+  a.task0 = lo;
+  const int tasks = hi - lo;
   rope_frequencies(a.rope_base, a.d, a.inv_freq);
   const size_t shm = size_t(a.d) * sizeof(float) + size_t(a.Hkv) * sizeof(int);
   if (dtype == XP_BF16)

@@ -71,6 +71,8 @@ struct PostQkvArgs {
   double inv_freq[64];       // base^(-2i/d), i < d/2: filled by launch_post_qkv
   const float2* rope_tab;    // [rows][d/2] (cos, sin) of each local row's position (fused epilogue)
   int rope_done;             // the QKV GEMM's epilogue already rotated and appended the local rows
+  int only;                  // 0: every task; 1: the local rows' tasks; 2: the chunk's peer rows
+  int task0;                 // first task of the launch (set by launch_post_qkv)
 };
 
 // Each row's RoPE (cos, sin) pairs, formed by the first RMSNorm launch of a step for the
