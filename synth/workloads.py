@@ -404,6 +404,10 @@ PARITY_WORKLOADS = {
     # d = 64 form, ragged chunk and prior
     "P7": Workload("P7", 107, "bf16", 512, 12, 4, 64, 1024, n_decode=0, ctx=("fixed", 0),
                    chunk_len=150, prior_len=90, description="prefill only, bf16, d = 64, G = 3"),
+    # twelve query heads per kv head: each kv head takes two workgroups of eight waves,
+    # the second with four heads, so four of its waves only take the stage barriers
+    "P8": Workload("P8", 108, "bf16", 512, 24, 2, 128, 1024, n_decode=0, ctx=("fixed", 0),
+                   chunk_len=100, prior_len=300, description="prefill only, bf16, G = 12"),
     # fp32 on the 8B head layout at d = 64 (P5's grid): a workgroup holds two waves per
     # query head (two key sets, 32-bit operands only)
     "E5": Workload("E5", 115, "f32", 512, 32, 8, 64, 1024, n_decode=0, ctx=("fixed", 0),
