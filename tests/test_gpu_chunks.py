@@ -126,11 +126,13 @@ def test_chunked_split_attention_modes_agree():
         outs.append(step.run().clone())
         torch.cuda.synchronize()
     # decode rows bit-identical; chunk rows within merge-order rounding (a partition's
-    # prefill plans its key splits for the CUs it has)
+    # prefill plans its key splits for the CUs it has); the co-resident step plans for
+    # every CU, like the serialized one, and its kernels sum in the same order
     n_pre = inst.wl.n_prefill_rows
     for o in outs[1:]:
         assert torch.equal(o[n_pre:], outs[0][n_pre:])
         assert rel_fro(o.cpu().numpy(), outs[0].cpu().numpy()) < 1e-3
+    assert torch.equal(outs[1], outs[0])
 
 
 def test_chunked_8b_step_on_sampled_rows():

@@ -2,7 +2,8 @@
 readings C3-full, C5-full), in the launch configurations bench.py times: the layer step
 serialized, with the split attention on a 128-CU decode partition, and with both attention
 kernels concurrent on every CU in their co-resident forms (decode rows bit-identical across
-the three), checked against the oracle on rows the oracle computes one by one.
+the three, every row between the serialized and co-resident steps), checked against the
+oracle on rows the oracle computes one by one.
 
 Rows checked: every decode row (C4: 32 of its 128 requests, spread over the batch);
 at least 64 local prefill rows and 64 exported peer rows at the chunk's ends, at page
@@ -157,6 +158,11 @@ def test_full_size_layer_on_sampled_rows(name):
     n_pl = wl.n_prefill_local
     assert torch.equal(outs[0][1][n_pl:], outs[128][1][n_pl:])
     assert torch.equal(outs[0][1][n_pl:], outs[-1][1][n_pl:])
+    # serialized and co-resident steps plan prefill for the same CUs, and the stand-alone
+    # kernel's block-pipelined loop sums in the co-resident kernel's order: every row
+    # and every exported peer row is the same
+    assert torch.equal(outs[0][1], outs[-1][1])
+    assert torch.equal(outs[0][2], outs[-1][2])
     print(f"[full] {name}: oracle on {len(pre_rows)} prefill, {len(dec_rows)} decode and "
           f"{len(peer_rows or [])} peer rows", flush=True)
     ref = L.layer_forward(**oracle_kwargs(inst, rows=rows, peer_rows=peer_rows))
