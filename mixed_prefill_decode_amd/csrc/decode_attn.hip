@@ -30,8 +30,6 @@ namespace {
 constexpr int kPage = 16;
 // pages in flight per wave while one is consumed
 constexpr int kDepth = 1;
-// pages are read through plain pointers (true) or per-page buffer resources
-constexpr bool kPtrLoads = false;
 // Cache policy of the page loads: non-temporal (the buffer instructions' nt bit).
 // Every K/V byte is read once per step, so keeping it out of the caches' recency
 // costs nothing; measured on MI355X it raises the decode stream from 5.16 to 5.79
@@ -84,13 +82,6 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t page_rsrc(const char* page, in
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(page), (short)0, nbytes, 0x00020000);
 }
 
-__device__ __forceinline__ void bload(Frag8<bf16_t>& f, __amdgpu_buffer_rsrc_t r, int off) {
-  f.v = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kLoadAux));
-}
-__device__ __forceinline__ void bload(Frag8<float>& f, __amdgpu_buffer_rsrc_t r, int off) {
-  f.lo = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kLoadAux));
-  f.hi = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(r, off + 16, 0, kLoadAux));
-}
 __device__ __forceinline__ void bload(Frag4<bf16_t>& f, __amdgpu_buffer_rsrc_t r, int off) {
   f.v = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, kLoadAux));
 }
@@ -112,13 +103,6 @@ __device__ __forceinline__ void bload_k(Frag8<float>& f, __amdgpu_buffer_rsrc_t 
   f.lo = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(r, k_byte<float>(key, j0), 0, kLoadAux));
   f.hi = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(r, k_byte<float>(key, j0 + 4), 0, kLoadAux));
 }
-__device__ __forceinline__ void pload_k(Frag8<bf16_t>& f, const char* page, int key, int j0) {
-  f.v = *reinterpret_cast<const uint4*>(page + k_byte<bf16_t>(key, j0));
-}
-__device__ __forceinline__ void pload_k(Frag8<float>& f, const char* page, int key, int j0) {
-  f.lo = *reinterpret_cast<const float4*>(page + k_byte<float>(key, j0));
-  f.hi = *reinterpret_cast<const float4*>(page + k_byte<float>(key, j0 + 4));
-}
 
 // K plane chunk-major (k_elem): lane l reads key l%16, dims [32*st + 8*(l/16), +8); for
 // bf16 the 64 lanes of fragment st read the plane's bytes [1024 st, 1024 (st + 1))
@@ -134,21 +118,10 @@ __device__ __forceinline__ void load_page(PageFrags<T, D>& f, __amdgpu_buffer_rs
   for (int n = 0; n < D / 16; ++n) bload(f.v[n], r, (kPage * D + (16 * n + key) * kPage + 4 * grp) * EB);
 }
 
-// the same fragments through a plain pointer to the page
-template <typename T, int D>
-__device__ __forceinline__ void load_page(PageFrags<T, D>& f, const char* page, int lane) {
-  constexpr int EB = St<T>::bytes;
-  const int key = lane & 15, grp = lane >> 4;
-#pragma unroll
-  for (int st = 0; st < D / 32; ++st) pload_k(f.k[st], page, key, 32 * st + 8 * grp);
-#pragma unroll
-  for (int n = 0; n < D / 16; ++n) load_frag4(f.v[n], page + (kPage * D + (16 * n + key) * kPage + 4 * grp) * EB);
-}
-
 // One unit of work: split s of request i's context on KV head g.  DEPTH pages
 // are in flight while one is consumed; the register ring has DEPTH + 1 page
 // buffers and the loop is unrolled over the ring so every buffer index is static.
-template <typename T, int D, int DEPTH, bool PTR>
+template <typename T, int D, int DEPTH>
 __device__ __forceinline__ void decode_unit(const void* __restrict__ q, const char* __restrict__ pool, int n_pages,
                                             const int32_t* __restrict__ dec_pages, int max_blocks,
                                             const int32_t* __restrict__ dec_ctx, int Hq, int Hkv, int pps,
@@ -187,15 +160,6 @@ __device__ __forceinline__ void decode_unit(const void* __restrict__ q, const ch
     bad |= in && !ok;
     return page_rsrc(pool + (ok ? long(pid) : 0L) * PAGE_BYTES, ok ? PAGE_BYTES : 0);
   };
-  // pointer form: a page outside the split or the pool reads page 0 instead (never
-  // consumed, or consumed only by a split whose output is flagged)
-  auto page_of = [&](int b) {
-    const bool in = b < b1;
-    const int pid = __builtin_amdgcn_readlane(my_pid, in ? b - b0 : 0);
-    const bool ok = in && pid >= 0 && pid < n_pages;
-    bad |= in && !ok;
-    return pool + (ok ? long(pid) : 0L) * PAGE_BYTES;
-  };
 
   f32x4 o[D / 16];
 #pragma unroll
@@ -205,8 +169,7 @@ __device__ __forceinline__ void decode_unit(const void* __restrict__ q, const ch
   PageFrags<T, D> buf[NB];
 #pragma unroll
   for (int j = 0; j < DEPTH; ++j) {
-    if constexpr (PTR) load_page<T, D>(buf[j], page_of(b0 + j), lane);
-    else load_page<T, D>(buf[j], rsrc_of(b0 + j), lane);
+    load_page<T, D>(buf[j], rsrc_of(b0 + j), lane);
     // keep the pages' loads in issue order: the waits below count on it
     __builtin_amdgcn_sched_barrier(0);
   }
@@ -214,8 +177,7 @@ __device__ __forceinline__ void decode_unit(const void* __restrict__ q, const ch
 #pragma unroll
     for (int u = 0; u < NB; ++u) {
       const int b = bb + u;
-      if constexpr (PTR) load_page<T, D>(buf[(u + DEPTH) % NB], page_of(b + DEPTH), lane);
-      else load_page<T, D>(buf[(u + DEPTH) % NB], rsrc_of(b + DEPTH), lane);
+      load_page<T, D>(buf[(u + DEPTH) % NB], rsrc_of(b + DEPTH), lane);
       __builtin_amdgcn_sched_barrier(0);
       if (b < b1) {
         PageFrags<T, D>& cur = buf[u];
@@ -285,7 +247,7 @@ __device__ __forceinline__ void decode_unit(const void* __restrict__ q, const ch
 // partials keep their (i, h, s) layout for the combine.
 // A workgroup holds one wave (its own unit list position) or, in the co-resident form,
 // four independent waves: wave w of workgroup b then takes list position 4 b + w.
-template <typename T, int D, int DEPTH, bool PTR>
+template <typename T, int D, int DEPTH>
 __device__ __forceinline__ void decode_units(const void* __restrict__ q, const char* __restrict__ pool, int n_pages,
                                              const int32_t* __restrict__ dec_pages, int max_blocks,
                                              const int32_t* __restrict__ dec_ctx, int n_d, int Hq, int Hkv, int pps,
@@ -301,21 +263,21 @@ __device__ __forceinline__ void decode_units(const void* __restrict__ q, const c
     const int cnt = ns * Hkv;
     for (; u < base + cnt; u += W) {
       const int r = u - base;
-      decode_unit<T, D, DEPTH, PTR>(q, pool, n_pages, dec_pages, max_blocks, dec_ctx, Hq, Hkv, pps, n_splits,
+      decode_unit<T, D, DEPTH>(q, pool, n_pages, dec_pages, max_blocks, dec_ctx, Hq, Hkv, pps, n_splits,
                                     part_ml, part_o, scale_log2, status, i, r % Hkv, r / Hkv);
     }
     base += cnt;
   }
 }
 
-template <typename T, int D, int DEPTH, bool PTR>
+template <typename T, int D, int DEPTH>
 __global__ __launch_bounds__(64) void decode_split_kernel(const void* __restrict__ q, const char* __restrict__ pool,
                                                           int n_pages, const int32_t* __restrict__ dec_pages,
                                                           int max_blocks, const int32_t* __restrict__ dec_ctx, int n_d,
                                                           int Hq, int Hkv, int pps, int n_splits,
                                                           float* __restrict__ part_ml, float* __restrict__ part_o,
                                                           float scale_log2, uint32_t* __restrict__ status) {
-  decode_units<T, D, DEPTH, PTR>(q, pool, n_pages, dec_pages, max_blocks, dec_ctx, n_d, Hq, Hkv, pps, n_splits,
+  decode_units<T, D, DEPTH>(q, pool, n_pages, dec_pages, max_blocks, dec_ctx, n_d, Hq, Hkv, pps, n_splits,
                                  part_ml, part_o, scale_log2, status);
 }
 
@@ -327,12 +289,12 @@ __global__ __launch_bounds__(64) void decode_split_kernel(const void* __restrict
 // those of decode_split_kernel: the results are the same bits.
 constexpr int kCoresWaves = 4;
 constexpr size_t kCoresLds = 84 * 1024;
-template <typename T, int D, int DEPTH, bool PTR>
+template <typename T, int D, int DEPTH>
 __global__ __launch_bounds__(64 * kCoresWaves) __attribute__((amdgpu_waves_per_eu(3))) void decode_split_cores_kernel(
     const void* __restrict__ q, const char* __restrict__ pool, int n_pages, const int32_t* __restrict__ dec_pages,
     int max_blocks, const int32_t* __restrict__ dec_ctx, int n_d, int Hq, int Hkv, int pps, int n_splits,
     float* __restrict__ part_ml, float* __restrict__ part_o, float scale_log2, uint32_t* __restrict__ status) {
-  decode_units<T, D, DEPTH, PTR>(q, pool, n_pages, dec_pages, max_blocks, dec_ctx, n_d, Hq, Hkv, pps, n_splits,
+  decode_units<T, D, DEPTH>(q, pool, n_pages, dec_pages, max_blocks, dec_ctx, n_d, Hq, Hkv, pps, n_splits,
                                  part_ml, part_o, scale_log2, status);
 }
 
@@ -413,11 +375,11 @@ xp_status launch_dec_t(const void* q, const void* pool, int n_pages, const int32
   const float scale_log2 = float(1.4426950408889634 / __builtin_sqrt(double(D)));
   const int waves = decode_grid(n_d, Hkv, n_splits);
   if (cores)
-    hipLaunchKernelGGL((decode_split_cores_kernel<T, D, kDepth, kPtrLoads>), dim3(cdiv(waves, kCoresWaves)),
+    hipLaunchKernelGGL((decode_split_cores_kernel<T, D, kDepth>), dim3(cdiv(waves, kCoresWaves)),
                        dim3(64 * kCoresWaves), kCoresLds, s, q, static_cast<const char*>(pool), n_pages, dec_pages,
                        max_blocks, dec_ctx, n_d, Hq, Hkv, pps, n_splits, part_ml, part_o, scale_log2, status);
   else
-    hipLaunchKernelGGL((decode_split_kernel<T, D, kDepth, kPtrLoads>), dim3(waves), dim3(64), 0, s, q,
+    hipLaunchKernelGGL((decode_split_kernel<T, D, kDepth>), dim3(waves), dim3(64), 0, s, q,
                        static_cast<const char*>(pool), n_pages, dec_pages, max_blocks, dec_ctx, n_d, Hq, Hkv, pps,
                        n_splits, part_ml, part_o, scale_log2, status);
   XP_CHECK_LAUNCH();

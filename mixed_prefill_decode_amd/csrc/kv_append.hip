@@ -81,7 +81,7 @@ __global__ __launch_bounds__(256) void post_qkv_kernel(PostQkvArgs a) {
   const int M = a.n_pl + a.n_d;
   const int d = a.d, half = d / 2, S = a.S;
   const int hq_loc = a.Hq / a.P, hkv_loc = a.Hkv / a.P;
-  const int q0 = a.r * hq_loc, k0 = a.r * hkv_loc;
+  const int q0 = a.r * hq_loc;
   const int ldq = (a.Hq + 2 * a.Hkv) * d;
 
   if (task >= M) {  // peer chunk rows: copy their (already rotated) q | k | v on this rank's heads

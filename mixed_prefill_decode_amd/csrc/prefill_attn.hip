@@ -223,7 +223,6 @@ __device__ __forceinline__ void prefill_tile(const PrefillArgs& a, int bx, int b
                          : (kBudget / (2 * BLK) > 0 ? kBudget / (2 * BLK) : 1);
   constexpr int NST = kSt * SB * BLK <= kBudget ? kSt : (kBudget / (SB * BLK) > 2 ? kBudget / (SB * BLK) : 2);
   constexpr int STAGE = SB * BLK;
-  constexpr int INSTR = SB * INSTR_BLK;           // load instructions per stage
   __shared__ uint4 ring[NST][STAGE / 16];
   __shared__ int32_t pids[2 * kMaxBps];
   // KS key sets: with KS = 2 the workgroup holds two waves per query head; set k
@@ -658,7 +657,7 @@ __device__ __forceinline__ void prefill_combine_tile(const PrefillArgs& a, int q
   const int ns = (nkb + a.bps - 1) / a.bps;
   if (ns <= 1) return;
   const long u0 = ((long(qt) * a.hq + h) * a.n_split) * QT;   // unit of (split 0, query 0)
-  if (threadIdx.x < QT) {
+  if (int(threadIdx.x) < QT) {
     const int ql = threadIdx.x;
     float mx = -__builtin_inff();
     for (int s = 0; s < ns; ++s) mx = fmaxf(mx, a.part_ml[2 * (u0 + s * QT + ql)]);
@@ -913,9 +912,10 @@ xp_status prepare(const void* pool, int n_pages, int S, int hq, int hkv, int d, 
 template <typename T, int D>
 void launch_one(const Prepared& pr, bool cores, hipStream_t s) {
   const dim3 grid(unit_grid(pr), pr.gy), block(64 * pr.p.wpg), cgrid(pr.n_qt, pr.a.hq);
-  if (cores)
-    hipLaunchKernelGGL((prefill_cores_kernel<T, D, kNQ, kMaxW, 1>), grid, block, 0, s, pr.a);
-  else if (sizeof(T) != 2 && two_key_sets(pr, long(grid.x) * grid.y))
+  if (cores && sizeof(T) == 2) {
+    // the co-resident form exists for 16-bit operands only (the step never asks for others)
+    if constexpr (sizeof(T) == 2) hipLaunchKernelGGL((prefill_cores_kernel<T, D, kNQ, kMaxW, 1>), grid, block, 0, s, pr.a);
+  } else if (sizeof(T) != 2 && two_key_sets(pr, long(grid.x) * grid.y))
     hipLaunchKernelGGL((prefill_kernel<T, D, kNQ, 4, 2>), grid, dim3(2 * block.x), 0, s, pr.a);
   else
     hipLaunchKernelGGL((prefill_kernel<T, D, kNQ, kMaxW, 1, sizeof(T) == 2>), grid, block, 0, s, pr.a);
@@ -936,10 +936,11 @@ void launch_group(const Prepared* pr, int n, bool cores, hipStream_t s) {
     g.cgx[k] = pr[k].n_qt;
     g.cstart[k + 1] = g.cstart[k] + (sk ? pr[k].n_qt * pr[k].a.hq : 0);
   }
-  if (cores)
-    hipLaunchKernelGGL((prefill_group_cores_kernel<T, D, kNQ, kMaxW, 1>), dim3(g.start[n]), dim3(64 * pr[0].p.wpg),
-                       0, s, g);
-  else if (sizeof(T) != 2 && two_key_sets(pr[0], g.start[n]))
+  if (cores && sizeof(T) == 2) {
+    if constexpr (sizeof(T) == 2)
+      hipLaunchKernelGGL((prefill_group_cores_kernel<T, D, kNQ, kMaxW, 1>), dim3(g.start[n]),
+                         dim3(64 * pr[0].p.wpg), 0, s, g);
+  } else if (sizeof(T) != 2 && two_key_sets(pr[0], g.start[n]))
     hipLaunchKernelGGL((prefill_group_kernel<T, D, kNQ, 4, 2>), dim3(g.start[n]), dim3(128 * pr[0].p.wpg), 0,
                        s, g);
   else
