@@ -335,6 +335,44 @@ def test_prefill_attention(name):
         assert rel_fro(full[t], ref[t]) < 2 * ATTN_TOL[dt], t
 
 
+def test_prefill_out_of_range_page_is_flagged_not_dereferenced():
+    """A page id outside the pool in one KV head's chunk table: the status bit is set, the
+    query tiles whose staged key range covers that page come out as NaN on that head's query
+    heads, and every other row (the earlier tile, the other KV head) is the oracle's."""
+    inst = make_instance(get_workload("E2"))      # bf16, 8 q heads on 2 kv heads, 130 after 33
+    wl, dt = inst.wl, inst.wl.dtype
+    rng = np.random.default_rng(11)
+    dpool = upload_pool(inst)
+    kv = L.PagedKV(inst.pool, dt, wl.page_size, wl.head_dim)
+    _append_chunk_tokens(inst, dpool, rng, kv)
+    l, hq, hkv, d = wl.chunk_len, wl.hq_loc, wl.hkv_loc, wl.head_dim
+    q = _rand(rng, (hq, l, d), dt)
+    ref = L.prefill_attention(to_f64(q, dt).transpose(1, 0, 2), kv, inst.pre_pages, wl.prior_len, wl.group)
+    ref = ref.reshape(l, hq * d)
+    bad_pages = inst.pre_pages.copy()
+    bad_pages[1, 7] = inst.pool.n_pages + 5       # kv head 1, keys 112..127
+    tdt = torch.bfloat16
+    out = torch.full((l, hq * d), 7.0, dtype=tdt, device="cuda")
+    peer = torch.empty((1, hq * d), dtype=tdt, device="cuda")
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    ws = torch.empty(max(X.xp_prefill_workspace_size(hq, hkv, d, wl.prior_len, l), 1), dtype=torch.uint8,
+                     device="cuda")
+    pool0 = dpool.clone()
+    X.xp_prefill_attention(DT[dt], to_device(q, dt), dpool, inst.pool.n_pages, wl.page_size,
+                           to_device(bad_pages, "i32"), inst.pre_max_blocks, hq, hkv, d, wl.prior_len, l, 0, l,
+                           out, hq * d, peer, hq * d, ws, status)
+    _sync()
+    assert int(status.item()) & X.XP_DEV_BAD_PAGE
+    assert torch.equal(dpool.view(torch.int16), pool0.view(torch.int16))
+    got = to_f64(to_host_bits(out), dt)
+    g = wl.group
+    head1 = slice(g * d, 2 * g * d)                # the query heads of kv head 1
+    # tile 0 (queries 0..31) stages keys below 96 only; every later tile's range reaches 127
+    assert np.isnan(got[32:, head1]).all()
+    assert np.isfinite(got[:32, head1]).all() and rel_fro(got[:32, head1], ref[:32, head1]) < ATTN_TOL[dt]
+    assert np.isfinite(got[:, :g * d]).all() and rel_fro(got[:, :g * d], ref[:, :g * d]) < ATTN_TOL[dt]
+
+
 def test_decode_token_matches_prefill_row_on_gpu():
     # decode attention of a query at position c+t over the chunk's own table equals prefill row t
     inst = make_instance(get_workload("E2"))
