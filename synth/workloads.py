@@ -408,6 +408,10 @@ PARITY_WORKLOADS = {
     # the second with four heads, so four of its waves only take the stage barriers
     "P8": Workload("P8", 108, "bf16", 512, 24, 2, 128, 1024, n_decode=0, ctx=("fixed", 0),
                    chunk_len=100, prior_len=300, description="prefill only, bf16, G = 12"),
+    # a three-token chunk after 1000 cached tokens: one mostly empty query tile whose key
+    # range is cut into splits, merged by the combine
+    "P9": Workload("P9", 109, "bf16", 512, 16, 2, 128, 1024, n_decode=0, ctx=("fixed", 0),
+                   chunk_len=3, prior_len=1000, description="prefill only, bf16, 3 after 1000"),
     # fp32 on the 8B head layout at d = 64 (P5's grid): a workgroup holds two waves per
     # query head (two key sets, 32-bit operands only)
     "E5": Workload("E5", 115, "f32", 512, 32, 8, 64, 1024, n_decode=0, ctx=("fixed", 0),

@@ -296,7 +296,7 @@ def test_decode_attention_long_contexts():
         assert max(e) < ATTN_TOL[dt], (pps, e)
 
 
-@pytest.mark.parametrize("name", ["P1", "P2", "P3", "P4", "P5", "P6", "P7", "P8", "E2", "C1", "E4", "E5"])
+@pytest.mark.parametrize("name", ["P1", "P2", "P3", "P4", "P5", "P6", "P7", "P8", "P9", "E2", "C1", "E4", "E5"])
 def test_prefill_attention(name):
     inst = make_instance(get_workload(name))
     wl, dt = inst.wl, inst.wl.dtype
@@ -331,7 +331,7 @@ def test_prefill_attention(name):
     # every row, including the first chunk rows that see only a few keys
     full = np.zeros_like(ref)
     full[loc], full[peer] = got_l, got_p
-    for t in (0, 1, l // 2, l - 1):
+    for t in sorted({0, min(1, l - 1), l // 2, l - 1}):
         assert rel_fro(full[t], ref[t]) < 2 * ATTN_TOL[dt], t
 
 
