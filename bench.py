@@ -137,6 +137,12 @@ KERNEL_NAMES = {
     "decode_attn": "decode_split_kernel + decode_combine_kernel (paged GQA decode attention)",
     "prefill_attn": "prefill_kernel (+ prefill_combine_kernel) (causal chunked-prefill attention)",
 }
+# the attention kernels' co-resident forms, which the step runs when decode and prefill
+# attention share every CU
+CORES_KERNEL_NAMES = {
+    "decode_attn": "decode_split_cores_kernel + decode_combine_kernel (paged GQA decode attention, co-resident form)",
+    "prefill_attn": "prefill_cores_kernel (+ prefill_combine_kernel) (causal chunked-prefill attention, co-resident form)",
+}
 # layer stages (xp_ctx_stage_timing) -> the kernel figures above they time inside the step
 STAGE_KERNELS = {"qkv": "qkv", "o": "o", "gate_up": "gate_up", "down": "down", "decode": "decode_attn",
                  "prefill": "prefill_attn"}
@@ -837,14 +843,15 @@ def main():
     fn, work, unit = calls[dom]
     t_dom = in_step[dom] * 1e-6
     traffic = recorded_traffic(wl.name, dom)
+    kname = CORES_KERNEL_NAMES.get(dom, KERNEL_NAMES[dom]) if timed_mode == "unmasked" else KERNEL_NAMES[dom]
     if unit == "byte":
         roofline = {"bound": "hbm", "achieved": round(work / t_dom / 1e9, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                     "frac": round(work / t_dom / 1e9 / PEAK_HBM_GBS, 4), "traffic": traffic,
-                    "kernel": KERNEL_NAMES[dom], "bytes_per_launch": work, "launch_us": round(t_dom * 1e6, 2)}
+                    "kernel": kname, "bytes_per_launch": work, "launch_us": round(t_dom * 1e6, 2)}
     else:
         roofline = {"bound": "mfma", "achieved": round(work / t_dom / 1e12, 2), "peak": PEAK_BF16_TFLOPS,
                     "unit": "TFLOP/s", "frac": round(work / t_dom / 1e12 / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
-                    "kernel": KERNEL_NAMES[dom], "flops_per_launch": work, "launch_us": round(t_dom * 1e6, 2)}
+                    "kernel": kname, "flops_per_launch": work, "launch_us": round(t_dom * 1e6, 2)}
     log(f"[bench] layer {ms * 1e3:.1f} us/step, {tokens_per_s:.0f} tokens/s; kernels {json.dumps(kern)}")
     log(f"[bench] split attention {json.dumps(seg)}")
 
