@@ -5,7 +5,7 @@ function is affine in its workload metric, fitted from isolated profiles; the
 contention factors alpha, beta >= 1 of Eq. 4 are calibrated on heterogeneous
 iterations.  fp64 NumPy; ``numpy.linalg.lstsq`` is the least-squares step.
 
-Readings (also listed in the design doc):
+Readings of points the pages leave open:
 
 * The pages name no loss; their accuracy figure is a mean absolute percentage error
   (§8.5, Table 4), so each fit minimizes the squared relative error

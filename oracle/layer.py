@@ -10,7 +10,7 @@ causal attention).  So this module is that definition written out, in fp64,
 with rounding only where the layer stores state in the workload's type: the
 K/V it appends to the paged pool.
 
-Readings of points the pages leave open (each also listed in the design doc):
+Readings of points the pages leave open:
 
 * Block structure: two RMSNorms, two residual adds, no biases, SwiGLU FFN
   down(silu(gate) * up); no QK-norm.  Gains are inputs; eps is an input.

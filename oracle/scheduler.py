@@ -5,7 +5,7 @@ ConfluxServe §6.4 (Algorithm 1), §6.3 "Decode: dual-mode placement" with App. 
 for token counts and capacities, Python floats (fp64) for times.  The dispatcher
 calls go to ``oracle.waterfill.dispatch`` (Algorithm 2).
 
-Readings (also listed in the design doc):
+Readings of points the pages leave open:
 
 * App. G's capacity before the deadline is K_i = max(0, floor((d_i - t) / tau)) * B0:
   the whole iterations left before d_i times the per-iteration budget (the printed

@@ -3,7 +3,7 @@
 ConfluxServe §6.2 (Eq. 2-6), App. D (Eq. 7-12), §6.3 and App. E (Algorithm 2).
 Python integers for token counts, Python floats (fp64) for latencies.
 
-Readings (also listed in the design doc):
+Readings of points the pages leave open:
 
 * Eq. 6 is read as T_P = f_comm(max_r n_p^r) + f_P((1/N) * sum_{i in P} l_i (c_i + (l_i + 1)/2)),
   with P the selected chunks plus the candidate's chunk when it is non-empty.
