@@ -412,8 +412,11 @@ PARITY_WORKLOADS = {
     # range is cut into splits, merged by the combine
     "P9": Workload("P9", 109, "bf16", 512, 16, 2, 128, 1024, n_decode=0, ctx=("fixed", 0),
                    chunk_len=3, prior_len=1000, description="prefill only, bf16, 3 after 1000"),
-    # fp32 on the 8B head layout at d = 64 (P5's grid): a workgroup holds two waves per
-    # query head (two key sets, 32-bit operands only)
+    # d = 64 on the 8B head layout (P5's grid): in bf16 the block-pipelined loop with
+    # units of up to 38 key blocks; in fp32 a workgroup holds two waves per query head
+    # (two key sets, 32-bit operands only)
+    "P10": Workload("P10", 110, "bf16", 512, 32, 8, 64, 1024, n_decode=0, ctx=("fixed", 0),
+                    chunk_len=900, prior_len=300, description="prefill only, bf16, d = 64, long units"),
     "E5": Workload("E5", 115, "f32", 512, 32, 8, 64, 1024, n_decode=0, ctx=("fixed", 0),
                    chunk_len=900, prior_len=300, description="prefill only, fp32, two key sets"),
     # fp32 with SP2

@@ -296,7 +296,7 @@ def test_decode_attention_long_contexts():
         assert max(e) < ATTN_TOL[dt], (pps, e)
 
 
-@pytest.mark.parametrize("name", ["P1", "P2", "P3", "P4", "P5", "P6", "P7", "P8", "P9", "E2", "C1", "E4", "E5"])
+@pytest.mark.parametrize("name", ["P1", "P2", "P3", "P4", "P5", "P6", "P7", "P8", "P9", "P10", "E2", "C1", "E4", "E5"])
 def test_prefill_attention(name):
     inst = make_instance(get_workload(name))
     wl, dt = inst.wl, inst.wl.dtype
